@@ -1,0 +1,269 @@
+"""CSA2 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Python marshalling around the plain C oracle in ``csa2_oracle.c``.  Only the
+test-suite, the smoke check and the benchmark's CPU-baseline leg may import
+this package; the HIP library never does, and this package never imports the
+HIP library.  Inputs come from ``csa2_synth`` (seeded, shared by both sides);
+no input or expected value here is ever produced by the GPU path.
+
+Parity status of each function (what pins it) is listed in the tests under
+``tests/test_oracle_*.py``.  The one part with no independent pin is the
+end-to-end value of the attention output on random inputs: beyond the
+identities those tests check (sink identity against a library SDPA, the t=0
+closed form, MQA symmetry, the value bound), its parity is unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libcsa2oracle.so")
+
+D, ROPE_LO, WINDOW, HI, DI, TOPK = 512, 448, 128, 32, 128, 512
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", *CFLAGS, os.path.join(_HERE, "csa2_oracle.c"), "-o", _SO + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.orc_e2m1_value.argtypes = [i32]
+        L.orc_e2m1_value.restype = f32
+        L.orc_e2m1_encode.argtypes = [f32]
+        L.orc_e4m3_value.argtypes = [i32]
+        L.orc_e4m3_value.restype = f32
+        L.orc_e4m3_encode.argtypes = [f32]
+        L.orc_exp.argtypes = [f32]
+        L.orc_exp.restype = f32
+        L.orc_fp4_encode.argtypes = [vp, i32, vp, vp]
+        L.orc_fp4_value.argtypes = [vp, vp, i32]
+        L.orc_fp4_value.restype = ctypes.c_double
+        L.orc_fp8_encode_row.argtypes = [vp, i32, vp, vp]
+        L.orc_rmsnorm.argtypes = [vp, vp, i32, vp]
+        L.orc_compress_entry.argtypes = [vp] * 16
+        L.orc_compress.argtypes = [i32, i32, i32] + [vp] * 12 + [i64]
+        L.orc_window_encode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp]
+        L.orc_fp4_encode_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_fp8_encode_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_index_scores.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+        L.orc_topk.argtypes = [vp, i64, i32, vp]
+        L.orc_topk.restype = i32
+        L.orc_quant_index_query.argtypes = [vp, vp, vp]
+        L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.orc_query_rows.argtypes = [i32, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32,
+                                     vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def P(a):
+    """pointer of a C-contiguous numpy array (or None)"""
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need C-contiguous numpy"
+    return a.ctypes.data
+
+
+def c(a, dt):
+    return None if a is None else np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------- formats
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(code)
+
+
+def e2m1_encode(y: float) -> int:
+    return lib().orc_e2m1_encode(y)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(code)
+
+
+def e4m3_encode(y: float) -> int:
+    return lib().orc_e4m3_encode(y)
+
+
+def fp4_encode(x: np.ndarray):
+    """x [rows, n] fp32 -> codes [rows, n/2] u8, scales [rows, n/32] u8"""
+    x = c(x, np.float32)
+    rows, n = x.shape
+    codes = np.zeros((rows, n // 2), np.uint8)
+    scales = np.zeros((rows, n // 32), np.uint8)
+    for r in range(rows):
+        lib().orc_fp4_encode(P(x[r]), n, P(codes[r]), P(scales[r]))
+    return codes, scales
+
+
+def fp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """exact values (double) of FP4 rows"""
+    codes = c(codes, np.uint8)
+    scales = c(scales, np.uint8)
+    rows = codes.shape[0]
+    n = codes.shape[1] * 2
+    out = np.empty((rows, n), np.float64)
+    for r in range(rows):
+        for k in range(n):
+            out[r, k] = lib().orc_fp4_value(P(codes[r]), P(scales[r]), k)
+    return out
+
+
+def fp8_encode_row(x: np.ndarray):
+    x = c(x, np.float32)
+    codes = np.zeros(x.shape[0], np.uint8)
+    s = np.zeros(1, np.float32)
+    lib().orc_fp8_encode_row(P(x), x.shape[0], P(codes), P(s))
+    return codes, float(s[0])
+
+
+def fp4_encode_rows_bf16(x: np.ndarray):
+    x = c(x, np.uint16)
+    rows, n = x.shape
+    codes = np.zeros((rows, n // 2), np.uint8)
+    scales = np.zeros((rows, n // 32), np.uint8)
+    lib().orc_fp4_encode_rows(P(x), rows, n, P(codes), P(scales))
+    return codes, scales
+
+
+def fp8_encode_rows_bf16(x: np.ndarray):
+    x = c(x, np.uint16)
+    rows, n = x.shape
+    codes = np.zeros((rows, n), np.uint8)
+    sc = np.zeros(rows, np.float32)
+    lib().orc_fp8_encode_rows(P(x), rows, n, P(codes), P(sc))
+    return codes, sc
+
+
+def exp32(x: float) -> float:
+    return lib().orc_exp(x)
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    x = c(x, np.float32)
+    g = c(gamma, np.float32)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(P(x), P(g), x.shape[0], P(y))
+    return y
+
+
+# ---------------------------------------------------------------- steps
+def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn):
+    """one entry; returns (z_codes, z_scales, ki_codes, ki_scales, z_pre, ki_pre)"""
+    zc = np.zeros(256, np.uint8)
+    zs = np.zeros(16, np.uint8)
+    kc_ = np.zeros(64, np.uint8)
+    ks = np.zeros(4, np.uint8)
+    zp = np.zeros(512, np.float32)
+    kp = np.zeros(128, np.float32)
+    args = [c(kc0, np.uint16), c(kc1, np.uint16), c(gc0, np.uint16), c(gc1, np.uint16),
+            c(gamma_c, np.float32), None if w_ik is None else c(w_ik, np.uint16),
+            c(gamma_ik, np.float32), None if ki_given is None else c(ki_given, np.uint16),
+            c(cs, np.float32), c(sn, np.float32)]
+    lib().orc_compress_entry(*[P(a) for a in args], P(zc), P(zs), P(kc_), P(ks), P(zp), P(kp))
+    return zc, zs, kc_, ks, zp, kp
+
+
+def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stride, pos0=0):
+    """kc, gc [B,T,512] bf16 -> caches [B, entry_stride, ...] (entries pos0/2 .. (pos0+T)/2-1)"""
+    kc = c(kc, np.uint16)
+    gc = c(gc, np.uint16)
+    B, T, _ = kc.shape
+    z_codes = np.zeros((B, entry_stride, 256), np.uint8)
+    z_scales = np.zeros((B, entry_stride, 16), np.uint8)
+    ki_codes = np.zeros((B, entry_stride, 64), np.uint8)
+    ki_scales = np.zeros((B, entry_stride, 4), np.uint8)
+    lib().orc_compress(B, T, pos0, P(kc), P(gc), P(c(gamma_c, np.float32)),
+                       P(None if w_ik is None else c(w_ik, np.uint16)), P(c(gamma_ik, np.float32)),
+                       P(None if ki_given is None else c(ki_given, np.uint16)),
+                       P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
+                       P(z_codes), P(z_scales), P(ki_codes), P(ki_scales), entry_stride)
+    return z_codes, z_scales, ki_codes, ki_scales
+
+
+def window_encode(wn, cos_t, sin_t, cap, pos0=0, w_codes=None, w_scale=None):
+    """wn [B,T,512] bf16 at positions pos0.. -> ring [B,cap,512] codes, [B,cap] scales"""
+    wn = c(wn, np.uint16)
+    B, T, _ = wn.shape
+    if w_codes is None:
+        w_codes = np.zeros((B, cap, 512), np.uint8)
+        w_scale = np.zeros((B, cap), np.float32)
+    lib().orc_window_encode(B, T, pos0, P(wn), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
+                            cap, P(w_codes), P(w_scale))
+    return w_codes, w_scale
+
+
+def quant_index_query(q):
+    q = c(q, np.uint16)
+    q8 = np.zeros((32, 128), np.uint8)
+    sq = np.zeros(32, np.float32)
+    lib().orc_quant_index_query(P(q), P(q8), P(sq))
+    return q8, sq
+
+
+def index_scores(q8, sq, w, ki_codes, ki_scales, n):
+    S = np.zeros(max(n, 1), np.float32)
+    lib().orc_index_scores(P(c(q8, np.uint8)), P(c(sq, np.float32)), P(c(w, np.float32)),
+                           P(c(ki_codes, np.uint8)), P(c(ki_scales, np.uint8)), n, P(S))
+    return S[:n]
+
+
+def topk(S, n, k=TOPK):
+    idx = np.zeros(k, np.int32)
+    cnt = lib().orc_topk(P(c(S, np.float32)), n, k, P(idx))
+    return idx, cnt
+
+
+def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t):
+    """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512]"""
+    Q = c(Q, np.uint16)
+    H = Q.shape[0]
+    O = np.zeros((H, 512), np.float64)
+    lse = np.zeros(H, np.float64)
+    Ob = np.zeros((H, 512), np.uint16)
+    lib().orc_attend(P(Q), H, p, P(c(w_codes, np.uint8)), P(c(w_scale, np.float32)), cap,
+                     P(c(z_codes, np.uint8)), P(c(z_scales, np.uint8)), P(c(idx, np.int32)), cnt,
+                     P(c(sink, np.float32)), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
+                     P(O), P(lse), P(Ob))
+    return O, lse, Ob
+
+
+def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales, w_codes,
+               w_scale, cap, sink, cos_t, sin_t, k=TOPK, want_scores=False, want_O=True):
+    """Selection and attention for query tokens of ONE request (caches of that request)."""
+    pos = c(pos, np.int64)
+    nq = pos.shape[0]
+    H = Q.shape[1] if Q is not None else 0
+    idx = np.zeros((nq, k), np.int32)
+    cnt = np.zeros(nq, np.int32)
+    O = np.zeros((nq, H, 512), np.float64) if (Q is not None and want_O) else None
+    Ob = np.zeros((nq, H, 512), np.uint16) if Q is not None else None
+    lse = np.zeros((nq, H), np.float64) if Q is not None else None
+    S = np.zeros((nq, max(n_entries, 1)), np.float32) if want_scores else None
+    lib().orc_query_rows(nq, P(pos), n_entries, P(c(qI, np.uint16)), P(c(wI, np.float32)),
+                         P(None if Q is None else c(Q, np.uint16)), H,
+                         P(c(ki_codes, np.uint8)), P(c(ki_scales, np.uint8)),
+                         P(c(z_codes, np.uint8)), P(c(z_scales, np.uint8)),
+                         P(c(w_codes, np.uint8)), P(c(w_scale, np.float32)), cap,
+                         P(c(sink, np.float32)), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
+                         k, P(idx), P(cnt), P(O), P(Ob), P(lse), P(S))
+    return dict(idx=idx, cnt=cnt, O=O, O_bf16=Ob, lse=lse, S=S)
