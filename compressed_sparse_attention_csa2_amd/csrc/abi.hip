@@ -1,0 +1,424 @@
+// C ABI of the CSA2 layer: argument validation, workspace layout and kernel
+// launches on the caller's stream.  Declarations and the contract of every
+// entry point are in include/csa2.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "csa2.h"
+#include "csa2_device.h"
+
+namespace csa2 {
+__global__ void k_compress(int, int, const int32_t*, const uint16_t*, const uint16_t*,
+                           const float*, const uint16_t*, const float*, const uint16_t*,
+                           const float*, const float*, int64_t, uint8_t*, uint8_t*, uint8_t*,
+                           uint8_t*, int64_t);
+__global__ void k_window_encode(int, int, const int32_t*, const uint16_t*, const float*,
+                                const float*, int64_t, uint8_t*, float*, int);
+__global__ void k_encode_fp4_rows(const uint16_t*, int64_t, int, uint8_t*, uint8_t*);
+__global__ void k_encode_fp8_rows(const uint16_t*, int64_t, int, uint8_t*, float*);
+__global__ void k_decode_fp4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
+__global__ void k_decode_fp8_rows(const uint8_t*, int64_t, int, uint16_t*);
+__global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*);
+__global__ void k_quant_index_query(const uint16_t*, const float*, int64_t, uint8_t*, float*);
+template <int TOK>
+__global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                               const float*, const uint8_t*, const uint8_t*, int64_t, float*, int,
+                               int);
+__global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int32_t*,
+                       int32_t*);
+template <int NW>
+__global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
+                       const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
+                       const int32_t*, const float*, const float*, const float*, int64_t,
+                       uint16_t*, float*, int, int, float*, float*);
+__global__ void k_attn_combine(int, int, int, const int32_t*, const float*, const float*,
+                               const float*, int64_t, int, const float*, const float*, uint16_t*,
+                               float*);
+}  // namespace csa2
+
+using namespace csa2;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa2_status fail(csa2_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+csa2_status ok() {
+    g_err[0] = 0;
+    return CSA2_OK;
+}
+
+csa2_status check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return CSA2_OK;
+}
+
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int IDX_CHUNK_H = 1024;   // must equal the indexer's chunk
+constexpr int MAX_ROWS = WINDOW + TOPK;
+
+int index_tok(int Tq) { return Tq == 1 ? 1 : (Tq <= 8 ? 8 : 4); }
+
+// split of the 640 attention rows across blocks for small token counts
+void attn_split(int64_t tokens, int* nsplit, int* rows_per) {
+    int ns = 1;
+    if (tokens < 1024) {
+        ns = (int)cdiv(2048, tokens > 0 ? tokens : 1);
+        if (ns > MAX_ROWS / 32) ns = MAX_ROWS / 32;
+    }
+    int rp = (int)cdiv(cdiv(MAX_ROWS, ns), 32) * 32;
+    *rows_per = rp;
+    *nsplit = (int)cdiv(MAX_ROWS, rp);
+}
+
+struct IndexWs {
+    size_t q8, wq, S, total;
+};
+IndexWs index_ws(int B, int Tq, int64_t stride) {
+    IndexWs w;
+    const size_t rows = (size_t)B * Tq;
+    w.q8 = 0;
+    w.wq = align256(rows * HI * DI);
+    w.S = w.wq + align256(rows * HI * sizeof(float));
+    w.total = w.S + align256(rows * (size_t)stride * sizeof(float));
+    return w;
+}
+
+struct AttnWs {
+    int nsplit, rows_per;
+    size_t pO, pml, total;
+};
+AttnWs attn_ws(int B, int Tq, int H) {
+    AttnWs w;
+    attn_split((int64_t)B * Tq, &w.nsplit, &w.rows_per);
+    w.pO = 0;
+    w.pml = 0;
+    w.total = 0;
+    if (w.nsplit > 1) {
+        const size_t n = (size_t)B * Tq * w.nsplit * H;
+        w.pml = align256(n * D * sizeof(float));
+        w.total = w.pml + align256(n * 2 * sizeof(float));
+    }
+    return w;
+}
+
+bool bad_sizes(int B, int Tq, int64_t stride) {
+    return B < 1 || Tq < 0 || stride < 1 || (int64_t)B * Tq > (int64_t)0x7FFFFFFF;
+}
+
+void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                   const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                   const uint8_t* ki_scales, int64_t stride, float* Sc, void* ws, hipStream_t st) {
+    const IndexWs L = index_ws(B, Tq, stride);
+    uint8_t* base = (uint8_t*)ws;
+    uint8_t* q8 = base + L.q8;
+    float* wq = (float*)(base + L.wq);
+    const int64_t qrows = (int64_t)B * Tq * HI;
+    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 4)), dim3(256), 0, st, qI,
+                       wI, qrows, q8, wq);
+    const int tok = index_tok(Tq);
+    const int n_tg = (int)cdiv(Tq, tok);
+    const int n_ch = (int)cdiv(stride, IDX_CHUNK_H);
+    const int64_t items = (int64_t)B * n_tg * n_ch;
+    const dim3 grid((unsigned)cdiv(items, 4));
+    if (tok == 1)
+        hipLaunchKernelGGL(k_index_scores<1>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
+                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+    else if (tok == 8)
+        hipLaunchKernelGGL(k_index_scores<8>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
+                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+    else
+        hipLaunchKernelGGL(k_index_scores<4>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
+                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+}
+
+csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                         const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                         const uint8_t* ki_scales, int64_t stride, int32_t* idx, int32_t* cnt,
+                         void* ws, hipStream_t st) {
+    if (Tq == 0) return CSA2_OK;
+    const IndexWs L = index_ws(B, Tq, stride);
+    float* Sc = (float*)((uint8_t*)ws + L.S);
+    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, ws, st);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)((int64_t)B * Tq)), dim3(256), 0, st, B, Tq, q_pos0,
+                       n_entries, Sc, stride, idx, cnt);
+    return check_launch("csa2_index_topk");
+}
+
+csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
+                        const uint8_t* w_codes, const float* w_scale, int cap,
+                        const uint8_t* z_codes, const uint8_t* z_scales, int64_t stride,
+                        const int32_t* idx, const int32_t* cnt, const float* sink,
+                        const float* rc, const float* rs, int64_t rope_rows, uint16_t* O,
+                        float* lse, void* ws, hipStream_t st) {
+    if (Tq == 0) return CSA2_OK;
+    const AttnWs L = attn_ws(B, Tq, H);
+    float* pO = (float*)((uint8_t*)ws + L.pO);
+    float* pml = (float*)((uint8_t*)ws + L.pml);
+    const dim3 grid((unsigned)((int64_t)B * Tq), (unsigned)L.nsplit);
+    const int nw = H / 16;
+#define CSA2_ATTN(NWV)                                                                        \
+    hipLaunchKernelGGL(k_attn<NWV>, grid, dim3(NWV * 64), 0, st, B, Tq, H, q_pos0, Q, w_codes, \
+                       w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
+                       rope_rows, O, lse, L.nsplit, L.rows_per, pO, pml)
+    switch (nw) {
+        case 1: CSA2_ATTN(1); break;
+        case 2: CSA2_ATTN(2); break;
+        case 3: CSA2_ATTN(3); break;
+        default: CSA2_ATTN(4); break;
+    }
+#undef CSA2_ATTN
+    if (L.nsplit > 1) {
+        const int64_t items = (int64_t)B * Tq * H;
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st, B,
+                           Tq, H, q_pos0, sink, rc, rs, rope_rows, L.nsplit, pO, pml, O, lse);
+    }
+    return check_launch("csa2_sparse_attn");
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_last_error(void) { return g_err; }
+
+const char* csa2_status_string(csa2_status s) {
+    switch (s) {
+        case CSA2_OK: return "ok";
+        case CSA2_ERR_NULL: return "null pointer";
+        case CSA2_ERR_SHAPE: return "bad shape";
+        case CSA2_ERR_UNSUPPORTED: return "unsupported size";
+        case CSA2_ERR_RANGE: return "buffer too small";
+        case CSA2_ERR_WORKSPACE: return "workspace too small";
+        case CSA2_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride) {
+    if (bad_sizes(B, Tq, entry_stride)) return 0;
+    if (op == CSA2_OP_INDEX_TOPK) return index_ws(B, Tq, entry_stride).total;
+    if (op == CSA2_OP_INDEX_SCORES) return index_ws(B, Tq, entry_stride).S;
+    if (H < 16 || H > 64 || H % 16) return 0;
+    if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H).total;
+    if (op == CSA2_OP_FORWARD) {
+        size_t a = index_ws(B, Tq, entry_stride).total, c = attn_ws(B, Tq, H).total;
+        return (a > c ? a : c) + align256((size_t)B * sizeof(int32_t));
+    }
+    return 0;
+}
+
+csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
+                          const uint16_t* gc, const float* gamma_c, const uint16_t* w_ik,
+                          const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
+                          const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
+                          uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
+                          int64_t entry_stride, void* stream) {
+    if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "compress: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
+    if (!pos0 || !kc || !gc || !gamma_c || !rope_cos || !rope_sin || !z_codes || !z_scales ||
+        !ki_codes || !ki_scales)
+        return fail(CSA2_ERR_NULL, "compress: a required pointer is NULL");
+    if (w_ik ? !gamma_ik : !ki_given)
+        return fail(CSA2_ERR_NULL, "compress: need w_ik+gamma_ik (derive) or ki_given (given)");
+    if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "compress: empty rotary table");
+    const int64_t items = (int64_t)B * (T / 2);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, S(stream), B, T,
+                       pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
+                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride);
+    csa2_status s = check_launch("csa2_compress");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t* wn,
+                               const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                               uint8_t* w_codes, float* w_scale, int cap, void* stream) {
+    if (bad_sizes(B, T, 1) || cap < 1) return fail(CSA2_ERR_SHAPE, "encode_window: B=%d T=%d cap=%d", B, T, cap);
+    if (!pos0 || !wn || !rope_cos || !rope_sin || !w_codes || !w_scale)
+        return fail(CSA2_ERR_NULL, "encode_window: a required pointer is NULL");
+    if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "encode_window: empty rotary table");
+    const int64_t items = (int64_t)B * T;
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_window_encode, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, S(stream),
+                       B, T, pos0, wn, rope_cos, rope_sin, rope_rows, w_codes, w_scale, cap);
+    csa2_status s = check_launch("csa2_encode_window");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                            const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
+                            int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
+        return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
+    const size_t need = index_ws(B, Tq, entry_stride).total;
+    if (Tq > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
+    csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
+                                 entry_stride, idx, cnt, ws, S(stream));
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                              const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                              const uint8_t* ki_scales, int64_t entry_stride, float* scores,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_scores: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !scores)
+        return fail(CSA2_ERR_NULL, "index_scores: a required pointer is NULL");
+    const size_t need = index_ws(B, Tq, entry_stride).S;
+    if (Tq > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_ERR_WORKSPACE, "index_scores: workspace %zu < %zu bytes", ws_bytes, need);
+    if (Tq == 0) return ok();
+    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, scores, ws,
+                  S(stream));
+    csa2_status s = check_launch("csa2_index_scores");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
+                             const uint8_t* w_codes, const float* w_scale, int cap,
+                             const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
+                             const int32_t* idx, const int32_t* cnt, const float* sink,
+                             const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                             uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "sparse_attn: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: H=%d (need 16, 32, 48 or 64)", H);
+    if (!q_pos0 || !Q || !w_codes || !w_scale || !z_codes || !z_scales || !idx || !cnt || !sink ||
+        !rope_cos || !rope_sin || !O)
+        return fail(CSA2_ERR_NULL, "sparse_attn: a required pointer is NULL");
+    if ((int64_t)cap < (int64_t)Tq + WINDOW - 1)
+        return fail(CSA2_ERR_RANGE, "sparse_attn: window ring cap=%d < Tq+127=%lld", cap, (long long)Tq + WINDOW - 1);
+    if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "sparse_attn: empty rotary table");
+    const size_t need = attn_ws(B, Tq, H).total;
+    if (Tq > 0 && need > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_ERR_WORKSPACE, "sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
+    csa2_status s = launch_attn(B, Tq, H, q_pos0, Q, w_codes, w_scale, cap, z_codes, z_scales,
+                                entry_stride, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O,
+                                lse, ws, S(stream));
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_t* kc,
+                         const uint16_t* gc, const uint16_t* wn, const float* gamma_c,
+                         const uint16_t* w_ik, const float* gamma_ik, const uint16_t* ki_given,
+                         const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
+                         const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                         uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
+                         uint8_t* ki_scales, int64_t entry_stride, const int32_t* n_entries,
+                         uint8_t* w_codes, float* w_scale, int cap, int32_t* idx, int32_t* cnt,
+                         uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "forward: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
+    if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "forward: H=%d (need 16, 32, 48 or 64)", H);
+    const bool prefill = kc != nullptr;
+    if (!pos0 || !Q || !qI || !wI || !sink || !rope_cos || !rope_sin || !z_codes || !z_scales ||
+        !ki_codes || !ki_scales || !w_codes || !w_scale || !idx || !cnt || !O)
+        return fail(CSA2_ERR_NULL, "forward: a required pointer is NULL");
+    if (prefill && (!gc || !wn || !gamma_c || (w_ik ? !gamma_ik : !ki_given)))
+        return fail(CSA2_ERR_NULL, "forward: prefill needs gc, wn, gamma_c and w_ik+gamma_ik or ki_given");
+    if (!prefill && !n_entries) return fail(CSA2_ERR_NULL, "forward: decode needs n_entries");
+    if ((int64_t)cap < (int64_t)T + WINDOW - 1)
+        return fail(CSA2_ERR_RANGE, "forward: window ring cap=%d < T+127=%lld", cap, (long long)T + WINDOW - 1);
+    if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "forward: empty rotary table");
+    const size_t need = csa2_workspace_size(CSA2_OP_FORWARD, B, T, H, entry_stride);
+    if (!ws || ws_bytes < need)
+        return fail(CSA2_ERR_WORKSPACE, "forward: workspace %zu < %zu bytes", ws_bytes, need);
+    if (T == 0) return ok();
+    hipStream_t st = S(stream);
+    const size_t ne_off = need - align256((size_t)B * sizeof(int32_t));
+    int32_t* ne = (int32_t*)((uint8_t*)ws + ne_off);
+    if (wn) {
+        hipLaunchKernelGGL(k_window_encode, dim3((unsigned)cdiv((int64_t)B * T, 4)), dim3(256), 0,
+                           st, B, T, pos0, wn, rope_cos, rope_sin, rope_rows, w_codes, w_scale,
+                           cap);
+    }
+    if (prefill) {
+        const int64_t items = (int64_t)B * (T / 2);
+        if (items > 0)
+            hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st, B, T,
+                               pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
+                               rope_sin, rope_rows, z_codes, z_scales, ki_codes, ki_scales,
+                               entry_stride);
+        if (!n_entries) {
+            hipLaunchKernelGGL(k_prefill_entries, dim3((unsigned)cdiv(B, 256)), dim3(256), 0, st,
+                               B, T, pos0, entry_stride, ne);
+            n_entries = ne;
+        }
+    }
+    csa2_status s = check_launch("csa2_forward (encode)");
+    if (s != CSA2_OK) return s;
+    s = launch_index(B, T, pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, idx, cnt,
+                     ws, st);
+    if (s != CSA2_OK) return s;
+    s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride, idx,
+                    cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, ws, st);
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                 uint8_t* scales, void* stream) {
+    if (rows < 0 || cols < 32 || cols % 32) return fail(CSA2_ERR_SHAPE, "encode_fp4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!x || !codes || !scales) return fail(CSA2_ERR_NULL, "encode_fp4_rows: NULL pointer");
+    const int64_t items = rows * (cols / 32);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_encode_fp4_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
+                       S(stream), x, rows, cols, codes, scales);
+    csa2_status s = check_launch("csa2_encode_fp4_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                 float* scale, void* stream) {
+    if (rows < 0 || cols < 1 || cols > 1024) return fail(CSA2_ERR_SHAPE, "encode_fp8_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!x || !codes || !scale) return fail(CSA2_ERR_NULL, "encode_fp8_rows: NULL pointer");
+    if (rows == 0) return ok();
+    hipLaunchKernelGGL(k_encode_fp8_rows, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, S(stream),
+                       x, rows, cols, codes, scale);
+    csa2_status s = check_launch("csa2_encode_fp8_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int cols, uint16_t* out, void* stream) {
+    if (rows < 0 || cols < 32 || cols % 32) return fail(CSA2_ERR_SHAPE, "decode_fp4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!codes || !scales || !out) return fail(CSA2_ERR_NULL, "decode_fp4_rows: NULL pointer");
+    const int64_t items = rows * (cols / 8);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_decode_fp4_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
+                       S(stream), codes, scales, rows, cols, out);
+    csa2_status s = check_launch("csa2_decode_fp4_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_decode_fp8_rows(const uint8_t* codes, int64_t rows, int cols, uint16_t* out,
+                                 void* stream) {
+    if (rows < 0 || cols < 8 || cols % 8) return fail(CSA2_ERR_SHAPE, "decode_fp8_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!codes || !out) return fail(CSA2_ERR_NULL, "decode_fp8_rows: NULL pointer");
+    const int64_t items = rows * (cols / 8);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_decode_fp8_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
+                       S(stream), codes, rows, cols, out);
+    csa2_status s = check_launch("csa2_decode_fp8_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+}  // extern "C"

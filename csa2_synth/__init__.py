@@ -159,9 +159,10 @@ class Workload:
 
     def wn_rows(self, b: int, pos) -> np.ndarray:
         """Window vectors of request b at absolute positions pos (in the ring)."""
-        idx = (b * self.win_rows + (np.asarray(pos, np.int64) - self.win_pos0)).astype(np.int64)
+        idx = np.ascontiguousarray(b * self.win_rows + (np.asarray(pos, np.int64) - self.win_pos0),
+                                   dtype=np.int64)
         out = np.empty((len(idx), D), np.uint16)
-        lib().synth_normal_rows(self.seed, ID_WN, _ptr(np.ascontiguousarray(idx)), len(idx), D,
+        lib().synth_normal_rows(self.seed, ID_WN, _ptr(idx), len(idx), D,
                                 1.0, 0.0, 1, _ptr(out))
         return out
 
@@ -171,9 +172,10 @@ class Workload:
     def Q_rows(self, b: int, t) -> np.ndarray:
         """Q[b, :, t, :] for local query indices t -> [len(t), H, 512]."""
         t = np.asarray(t, np.int64)
-        rows = ((b * self.H + np.arange(self.H)[None, :]) * self.Tq + t[:, None]).reshape(-1)
+        rows = np.ascontiguousarray(
+            ((b * self.H + np.arange(self.H)[None, :]) * self.Tq + t[:, None]).reshape(-1), np.int64)
         out = np.empty((len(t) * self.H, D), np.uint16)
-        lib().synth_normal_rows(self.seed, ID_Q, _ptr(np.ascontiguousarray(rows)), len(rows), D,
+        lib().synth_normal_rows(self.seed, ID_Q, _ptr(rows), len(rows), D,
                                 1.0, 0.0, 1, _ptr(out))
         return out.reshape(len(t), self.H, D)
 
@@ -182,9 +184,10 @@ class Workload:
 
     def qI_rows(self, b: int, t) -> np.ndarray:
         t = np.asarray(t, np.int64)
-        rows = ((b * self.Tq + t[:, None]) * HI + np.arange(HI)[None, :]).reshape(-1)
+        rows = np.ascontiguousarray(
+            ((b * self.Tq + t[:, None]) * HI + np.arange(HI)[None, :]).reshape(-1), np.int64)
         out = np.empty((len(rows), DI), np.uint16)
-        lib().synth_normal_rows(self.seed, ID_QI, _ptr(np.ascontiguousarray(rows)), len(rows), DI,
+        lib().synth_normal_rows(self.seed, ID_QI, _ptr(rows), len(rows), DI,
                                 1.0, 0.0, 1, _ptr(out))
         return out.reshape(len(t), HI, DI)
 

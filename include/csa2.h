@@ -1,0 +1,211 @@
+/*
+ * csa2.h -- C ABI of the CSA2 attention layer for MI355X (gfx950).
+ *
+ * One attention layer of Compressed Sparse Attention 2 on one GPU: pair-pooled
+ * FP4 compressed keys, a 32-head lightning indexer choosing 512 entries per
+ * query, a 128-token FP8 window, and 64-head shared-latent attention with a
+ * per-head sink.  Every step runs in the library's own HIP kernels.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees them and allocates no device memory.  Scratch memory comes
+ *    from the caller's workspace (see csa2_workspace_size).
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Layouts are row-major
+ *    in the bracketed order.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; no call synchronises.
+ *  - Positions are absolute token positions.  Compressed entry j pools the
+ *    tokens at positions 2j and 2j+1 and is rotated at position 2j.
+ *  - Caches (per request b, `entry_stride` entries apart):
+ *      z_codes  [B][entry_stride][256]  E2M1 pairs, element 2i in the low nibble of byte i
+ *      z_scales [B][entry_stride][16]   E8M0 bytes, one per 32 channels (2^(byte-127))
+ *      ki_codes [B][entry_stride][64], ki_scales [B][entry_stride][4]   same format, 128 wide
+ *      w_codes  [B][cap][512] E4M3FN, w_scale [B][cap] fp32: window ring, the
+ *               row of position p lives in slot p mod cap.
+ *  - Rotary table: rope_cos, rope_sin fp32 [rope_rows][32]; row p holds the
+ *    cos/sin of the 32 angles of position p (pairs (lo+2i, lo+2i+1)).
+ *  - Device-resident integers (positions, entry counts, indices) cannot be
+ *    checked without a synchronisation.  Kernels clamp every one of them into
+ *    its buffer, so a wrong value gives wrong numbers but never an access out
+ *    of bounds.  Host-visible sizes are validated before anything is launched:
+ *    on failure the call returns a status, launches nothing, writes nothing
+ *    and records a message for csa2_last_error().
+ *  - No C++ exception crosses this boundary.  Calls are thread-safe.
+ *
+ * Citations name the page and the passage that defines each operation:
+ *  [atlas]  "DeepSeek V4.1 -- Pooled group -> Source layer, pairs pooled"
+ *           (equations of compressed sparse attention; cache note "between
+ *           forward calls").
+ *  [norm]   "DeepSeek V4.1 -- Window layer -> Attention RMSNorm".
+ *  [blog]   "Inside DeepSeek V4.1", sections "Attention that looks at 640
+ *           places" and "890 bytes".
+ *  [zharf]  "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache",
+ *           sections "Deriving the 890 bytes per token" and "FP4 is a storage
+ *           choice".
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
+    CSA2_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
+    CSA2_ERR_UNSUPPORTED = 3, /* a size the kernels do not implement (e.g. heads not a multiple of 16) */
+    CSA2_ERR_RANGE = 4,       /* a buffer is too small for the stated sizes (ring, rotary table, cache) */
+    CSA2_ERR_WORKSPACE = 5,   /* workspace missing or smaller than csa2_workspace_size() */
+    CSA2_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} csa2_status;
+
+/* workspace query ops */
+#define CSA2_OP_INDEX_TOPK 1
+#define CSA2_OP_SPARSE_ATTN 2
+#define CSA2_OP_FORWARD 3
+#define CSA2_OP_INDEX_SCORES 4
+
+/*
+ * Compression of new positions into the compressed cache and the index-key
+ * cache [atlas: k^p = sum_i softmax_i(g^c_i) (.) k^c_i over i in {2j, 2j+1};
+ * c = gamma_C (.) k^p / sqrt(mean(k^p^2) + eps) with eps = 1e-20 [norm];
+ * Z_{j,448:} <- R_{2j} c_{j,448:}; Z <- FP4(Z); k^i = c W_IK; k^n = RMSNorm;
+ * K^I_{j,64:} <- R_{2j} k^n_{j,64:}; K^I <- FP4(K^I)].
+ *
+ *  B, T      requests, new positions per request (T >= 0; floor(T/2) entries
+ *            are written; an odd last position is left for the caller).
+ *  pos0      [B] int32 device: absolute position of each request's first new
+ *            token; must be even.  Entry j = pos0/2 + i is written at cache
+ *            row j (rows >= entry_stride are skipped).
+ *  kc, gc    [B][T][512] bf16: pooled keys and gate logits of the new tokens.
+ *  gamma_c   [512] fp32 RMSNorm gain of the compressed rows.
+ *  w_ik      [512][128] bf16 index-key projection, or NULL for given mode.
+ *  gamma_ik  [128] fp32 gain of the index-key norm (derive mode only).
+ *  ki_given  [B][T/2][128] bf16 given index keys (already normalised and
+ *            rotated; only encoded), used when w_ik == NULL.
+ *  rope_*    rotary table, rope_rows >= 1.
+ *  outputs   z_codes, z_scales, ki_codes, ki_scales as described above.
+ */
+csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
+                          const uint16_t* gc, const float* gamma_c, const uint16_t* w_ik,
+                          const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
+                          const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
+                          uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
+                          int64_t entry_stride, void* stream);
+
+/*
+ * Window rows [atlas: W_{t,448:} <- R_t w^n_{t,448:}; W <- FP8(W); blog: the
+ * window is stored in FP8].  Row i of request b is the window vector of
+ * position pos0[b] + i; it is rotated at that position and written to ring
+ * slot (position mod cap) as E4M3FN codes with one fp32 scale (max|x|/448).
+ *  wn  [B][T][512] bf16.   cap >= 1.
+ */
+csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t* wn,
+                               const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                               uint8_t* w_codes, float* w_scale, int cap, void* stream);
+
+/*
+ * Lightning indexer and causal top-512 [atlas: S^I_{t,j} = sum_h w^I_{t,h}
+ * ReLU(Q^I_{h,t} . K^I_j); I_t = top_512(S^I_{t,j} : j < floor((t+1)/2));
+ * blog: 32 heads of 128, one key per entry].
+ *  Tq        query tokens per request, at positions q_pos0[b] + i.
+ *  q_pos0    [B] int32 device.   n_entries [B] int32 device: valid cache rows.
+ *  qI        [B][Tq][32][128] bf16 index queries (already rotated); each
+ *            (token, head) row is quantised to E4M3FN with scale max|x|/448.
+ *  wI        [B][Tq][32] fp32 head weights (the 1/sqrt(128*32) already applied).
+ *  idx       [B][Tq][512] int32 out: chosen entries in ascending order,
+ *            padded with -1.  Ties: larger score, then smaller entry.
+ *  cnt       [B][Tq] int32 out: min(512, min(floor((p+1)/2), n_entries)).
+ *  ws        workspace of at least csa2_workspace_size(CSA2_OP_INDEX_TOPK, ...).
+ */
+csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                            const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
+                            int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The indexer's raw scores without selection [atlas: S^I_{t,j} = sum_h
+ * w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j)], same queries and keys as
+ * csa2_index_topk.  scores [B][Tq][entry_stride] fp32: for query i of request
+ * b only entries j < min(floor((p+1)/2), n_entries[b]) are written.
+ *  ws  at least csa2_workspace_size(CSA2_OP_INDEX_SCORES, ...) bytes.
+ */
+csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                              const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                              const uint8_t* ki_scales, int64_t entry_stride, float* scores,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse shared-latent attention with a sink [atlas: J^w_t = {max(0,t-127)..t};
+ * Y = [W; Z]; J = [J^w; I + |W|]; G_t = Y[J_t]; S = Q . G / sqrt(512);
+ * A = exp S / (exp s_h + sum exp S); O = sum A G; O_{448:} <- R_t^{-1} O_{448:};
+ * blog: one key-value vector per place shared by all heads, per-head sink].
+ *  H         query heads, a multiple of 16 in 16..64.
+ *  Q         [B][H][Tq][512] bf16, already rotated.
+ *  cap       window ring capacity, >= Tq + 127.
+ *  idx, cnt  as produced by csa2_index_topk.
+ *  sink      [H] fp32.
+ *  O         [B][H][Tq][512] bf16 out.   lse [B][H][Tq] fp32 out or NULL
+ *            (natural log of the full softmax denominator, sink included).
+ */
+csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
+                             const uint8_t* w_codes, const float* w_scale, int cap,
+                             const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
+                             const int32_t* idx, const int32_t* cnt, const float* sink,
+                             const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                             uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer for one call.
+ *  Prefill (kc != NULL): compress the T new positions, write their window
+ *  rows, then select and attend for every new position; n_entries may be NULL
+ *  (then floor((pos0+T)/2) per request).
+ *  Decode (kc == NULL): caches are given.  If wn != NULL the new tokens'
+ *  window rows are written first.  n_entries is required.
+ *  Arguments as in the calls above; T is the number of query tokens.
+ */
+csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_t* kc,
+                         const uint16_t* gc, const uint16_t* wn, const float* gamma_c,
+                         const uint16_t* w_ik, const float* gamma_ik, const uint16_t* ki_given,
+                         const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
+                         const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                         uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
+                         uint8_t* ki_scales, int64_t entry_stride, const int32_t* n_entries,
+                         uint8_t* w_codes, float* w_scale, int cap, int32_t* idx, int32_t* cnt,
+                         uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace an op needs for these sizes (0 on invalid sizes). */
+size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride);
+
+/*
+ * Storage encoders used to fill caches from given values [zharf: E2M1 with
+ * block scales; blog: FP8 window].  x [rows][cols] bf16.
+ *  fp4: cols a multiple of 32; codes [rows][cols/2], scales [rows][cols/32].
+ *  fp8: cols in 1..1024; codes [rows][cols], scale [rows] (max|x|/448, 1 if 0).
+ */
+csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                 uint8_t* scales, void* stream);
+csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                 float* scale, void* stream);
+
+/* Dequantisation as the attention kernel performs it, to bf16 (exact for these formats). */
+csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int cols, uint16_t* out, void* stream);
+csa2_status csa2_decode_fp8_rows(const uint8_t* codes, int64_t rows, int cols, uint16_t* out,
+                                 void* stream);
+
+const char* csa2_status_string(csa2_status s);
+const char* csa2_last_error(void);
+int csa2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

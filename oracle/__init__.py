@@ -75,12 +75,20 @@ def lib():
     return _lib
 
 
-def P(a):
-    """pointer of a C-contiguous numpy array (or None)"""
-    if a is None:
-        return None
-    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need C-contiguous numpy"
-    return a.ctypes.data
+class _Args:
+    """Pointer marshalling that keeps every converted array alive until the
+    owning function returns (a temporary's address must not outlive it)."""
+
+    def __init__(self):
+        self.keep = []
+
+    def __call__(self, a, dt=None):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dt) if dt is not None else a
+        assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need C-contiguous numpy"
+        self.keep.append(a)
+        return a.ctypes.data
 
 
 def c(a, dt):
@@ -106,17 +114,19 @@ def e4m3_encode(y: float) -> int:
 
 def fp4_encode(x: np.ndarray):
     """x [rows, n] fp32 -> codes [rows, n/2] u8, scales [rows, n/32] u8"""
+    A = _Args()
     x = c(x, np.float32)
     rows, n = x.shape
     codes = np.zeros((rows, n // 2), np.uint8)
     scales = np.zeros((rows, n // 32), np.uint8)
     for r in range(rows):
-        lib().orc_fp4_encode(P(x[r]), n, P(codes[r]), P(scales[r]))
+        lib().orc_fp4_encode(A(x[r]), n, A(codes[r]), A(scales[r]))
     return codes, scales
 
 
 def fp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """exact values (double) of FP4 rows"""
+    A = _Args()
     codes = c(codes, np.uint8)
     scales = c(scales, np.uint8)
     rows = codes.shape[0]
@@ -124,33 +134,36 @@ def fp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty((rows, n), np.float64)
     for r in range(rows):
         for k in range(n):
-            out[r, k] = lib().orc_fp4_value(P(codes[r]), P(scales[r]), k)
+            out[r, k] = lib().orc_fp4_value(A(codes[r]), A(scales[r]), k)
     return out
 
 
 def fp8_encode_row(x: np.ndarray):
+    A = _Args()
     x = c(x, np.float32)
     codes = np.zeros(x.shape[0], np.uint8)
     s = np.zeros(1, np.float32)
-    lib().orc_fp8_encode_row(P(x), x.shape[0], P(codes), P(s))
+    lib().orc_fp8_encode_row(A(x), x.shape[0], A(codes), A(s))
     return codes, float(s[0])
 
 
 def fp4_encode_rows_bf16(x: np.ndarray):
+    A = _Args()
     x = c(x, np.uint16)
     rows, n = x.shape
     codes = np.zeros((rows, n // 2), np.uint8)
     scales = np.zeros((rows, n // 32), np.uint8)
-    lib().orc_fp4_encode_rows(P(x), rows, n, P(codes), P(scales))
+    lib().orc_fp4_encode_rows(A(x), rows, n, A(codes), A(scales))
     return codes, scales
 
 
 def fp8_encode_rows_bf16(x: np.ndarray):
+    A = _Args()
     x = c(x, np.uint16)
     rows, n = x.shape
     codes = np.zeros((rows, n), np.uint8)
     sc = np.zeros(rows, np.float32)
-    lib().orc_fp8_encode_rows(P(x), rows, n, P(codes), P(sc))
+    lib().orc_fp8_encode_rows(A(x), rows, n, A(codes), A(sc))
     return codes, sc
 
 
@@ -159,16 +172,18 @@ def exp32(x: float) -> float:
 
 
 def rmsnorm(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    A = _Args()
     x = c(x, np.float32)
     g = c(gamma, np.float32)
     y = np.empty_like(x)
-    lib().orc_rmsnorm(P(x), P(g), x.shape[0], P(y))
+    lib().orc_rmsnorm(A(x), A(g), x.shape[0], A(y))
     return y
 
 
 # ---------------------------------------------------------------- steps
 def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn):
     """one entry; returns (z_codes, z_scales, ki_codes, ki_scales, z_pre, ki_pre)"""
+    A = _Args()
     zc = np.zeros(256, np.uint8)
     zs = np.zeros(16, np.uint8)
     kc_ = np.zeros(64, np.uint8)
@@ -179,12 +194,13 @@ def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn
             c(gamma_c, np.float32), None if w_ik is None else c(w_ik, np.uint16),
             c(gamma_ik, np.float32), None if ki_given is None else c(ki_given, np.uint16),
             c(cs, np.float32), c(sn, np.float32)]
-    lib().orc_compress_entry(*[P(a) for a in args], P(zc), P(zs), P(kc_), P(ks), P(zp), P(kp))
+    lib().orc_compress_entry(*[A(a) for a in args], A(zc), A(zs), A(kc_), A(ks), A(zp), A(kp))
     return zc, zs, kc_, ks, zp, kp
 
 
 def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stride, pos0=0):
     """kc, gc [B,T,512] bf16 -> caches [B, entry_stride, ...] (entries pos0/2 .. (pos0+T)/2-1)"""
+    A = _Args()
     kc = c(kc, np.uint16)
     gc = c(gc, np.uint16)
     B, T, _ = kc.shape
@@ -192,64 +208,70 @@ def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stri
     z_scales = np.zeros((B, entry_stride, 16), np.uint8)
     ki_codes = np.zeros((B, entry_stride, 64), np.uint8)
     ki_scales = np.zeros((B, entry_stride, 4), np.uint8)
-    lib().orc_compress(B, T, pos0, P(kc), P(gc), P(c(gamma_c, np.float32)),
-                       P(None if w_ik is None else c(w_ik, np.uint16)), P(c(gamma_ik, np.float32)),
-                       P(None if ki_given is None else c(ki_given, np.uint16)),
-                       P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
-                       P(z_codes), P(z_scales), P(ki_codes), P(ki_scales), entry_stride)
+    lib().orc_compress(B, T, pos0, A(kc), A(gc), A(gamma_c, np.float32),
+                       A(None if w_ik is None else c(w_ik, np.uint16)), A(gamma_ik, np.float32),
+                       A(None if ki_given is None else c(ki_given, np.uint16)),
+                       A(cos_t, np.float32), A(sin_t, np.float32),
+                       A(z_codes), A(z_scales), A(ki_codes), A(ki_scales), entry_stride)
     return z_codes, z_scales, ki_codes, ki_scales
 
 
 def window_encode(wn, cos_t, sin_t, cap, pos0=0, w_codes=None, w_scale=None):
     """wn [B,T,512] bf16 at positions pos0.. -> ring [B,cap,512] codes, [B,cap] scales"""
+    A = _Args()
     wn = c(wn, np.uint16)
     B, T, _ = wn.shape
     if w_codes is None:
         w_codes = np.zeros((B, cap, 512), np.uint8)
         w_scale = np.zeros((B, cap), np.float32)
-    lib().orc_window_encode(B, T, pos0, P(wn), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
-                            cap, P(w_codes), P(w_scale))
+    lib().orc_window_encode(B, T, pos0, A(wn), A(cos_t, np.float32), A(sin_t, np.float32),
+                            cap, A(w_codes), A(w_scale))
     return w_codes, w_scale
 
 
 def quant_index_query(q):
+    A = _Args()
     q = c(q, np.uint16)
     q8 = np.zeros((32, 128), np.uint8)
     sq = np.zeros(32, np.float32)
-    lib().orc_quant_index_query(P(q), P(q8), P(sq))
+    lib().orc_quant_index_query(A(q), A(q8), A(sq))
     return q8, sq
 
 
 def index_scores(q8, sq, w, ki_codes, ki_scales, n):
+    A = _Args()
     S = np.zeros(max(n, 1), np.float32)
-    lib().orc_index_scores(P(c(q8, np.uint8)), P(c(sq, np.float32)), P(c(w, np.float32)),
-                           P(c(ki_codes, np.uint8)), P(c(ki_scales, np.uint8)), n, P(S))
+    lib().orc_index_scores(A(q8, np.uint8), A(sq, np.float32), A(w, np.float32),
+                           A(ki_codes, np.uint8), A(ki_scales, np.uint8), n, A(S))
     return S[:n]
 
 
 def topk(S, n, k=TOPK):
+    A = _Args()
     idx = np.zeros(k, np.int32)
-    cnt = lib().orc_topk(P(c(S, np.float32)), n, k, P(idx))
+    cnt = lib().orc_topk(A(S, np.float32), n, k, A(idx))
     return idx, cnt
 
 
 def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t):
     """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512]"""
+    A = _Args()
     Q = c(Q, np.uint16)
     H = Q.shape[0]
     O = np.zeros((H, 512), np.float64)
     lse = np.zeros(H, np.float64)
     Ob = np.zeros((H, 512), np.uint16)
-    lib().orc_attend(P(Q), H, p, P(c(w_codes, np.uint8)), P(c(w_scale, np.float32)), cap,
-                     P(c(z_codes, np.uint8)), P(c(z_scales, np.uint8)), P(c(idx, np.int32)), cnt,
-                     P(c(sink, np.float32)), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
-                     P(O), P(lse), P(Ob))
+    lib().orc_attend(A(Q), H, p, A(w_codes, np.uint8), A(w_scale, np.float32), cap,
+                     A(z_codes, np.uint8), A(z_scales, np.uint8), A(idx, np.int32), cnt,
+                     A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
+                     A(O), A(lse), A(Ob))
     return O, lse, Ob
 
 
 def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales, w_codes,
                w_scale, cap, sink, cos_t, sin_t, k=TOPK, want_scores=False, want_O=True):
     """Selection and attention for query tokens of ONE request (caches of that request)."""
+    A = _Args()
     pos = c(pos, np.int64)
     nq = pos.shape[0]
     H = Q.shape[1] if Q is not None else 0
@@ -259,11 +281,11 @@ def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales
     Ob = np.zeros((nq, H, 512), np.uint16) if Q is not None else None
     lse = np.zeros((nq, H), np.float64) if Q is not None else None
     S = np.zeros((nq, max(n_entries, 1)), np.float32) if want_scores else None
-    lib().orc_query_rows(nq, P(pos), n_entries, P(c(qI, np.uint16)), P(c(wI, np.float32)),
-                         P(None if Q is None else c(Q, np.uint16)), H,
-                         P(c(ki_codes, np.uint8)), P(c(ki_scales, np.uint8)),
-                         P(c(z_codes, np.uint8)), P(c(z_scales, np.uint8)),
-                         P(c(w_codes, np.uint8)), P(c(w_scale, np.float32)), cap,
-                         P(c(sink, np.float32)), P(c(cos_t, np.float32)), P(c(sin_t, np.float32)),
-                         k, P(idx), P(cnt), P(O), P(Ob), P(lse), P(S))
+    lib().orc_query_rows(nq, A(pos), n_entries, A(qI, np.uint16), A(wI, np.float32),
+                         A(None if Q is None else c(Q, np.uint16)), H,
+                         A(ki_codes, np.uint8), A(ki_scales, np.uint8),
+                         A(z_codes, np.uint8), A(z_scales, np.uint8),
+                         A(w_codes, np.uint8), A(w_scale, np.float32), cap,
+                         A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
+                         k, A(idx), A(cnt), A(O), A(Ob), A(lse), A(S))
     return dict(idx=idx, cnt=cnt, O=O, O_bf16=Ob, lse=lse, S=S)

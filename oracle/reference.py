@@ -95,10 +95,9 @@ class DecodeReference:
         js = js[~self._z_done[js]]
         if len(js) == 0:
             return
-        rows = self.b * self.wl.n_entries + js
+        rows = np.ascontiguousarray(self.b * self.wl.n_entries + js.astype(np.int64))
         raw = np.empty((len(js), 512), np.uint16)
-        synth.lib().synth_normal_rows(self.wl.seed, synth.ID_ZROW,
-                                      synth._ptr(np.ascontiguousarray(rows, np.int64)), len(js),
+        synth.lib().synth_normal_rows(self.wl.seed, synth.ID_ZROW, synth._ptr(rows), len(js),
                                       512, 1.0, 0.0, 1, synth._ptr(raw))
         cc, ss = fp4_encode_rows_bf16(raw)
         self.z_codes[js] = cc

@@ -1,0 +1,110 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, sizes its
+workspace, and rejects bad arguments before launching anything (no GPU needed:
+every call here fails validation, so no HIP work is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import compressed_sparse_attention_csa2_amd as csa2
+    return csa2.lib()
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:csa2_status|size_t|const char\*|int)\s+(csa2_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.csa2_abi_version() == 1
+    for s in range(7):
+        assert L.csa2_status_string(s)
+
+
+def test_workspace_sizes(L):
+    import compressed_sparse_attention_csa2_amd as csa2
+    ws = csa2.workspace_size
+    assert ws(csa2.OP_INDEX_TOPK, 1, 65536, 64, 32768) >= 65536 * 32768 * 4
+    assert ws(csa2.OP_FORWARD, 1, 256, 16, 128) > 0
+    assert ws(csa2.OP_FORWARD, 1, 256, 17, 128) == 0          # heads not a multiple of 16
+    assert ws(csa2.OP_FORWARD, 0, 256, 16, 128) == 0
+    assert ws(csa2.OP_SPARSE_ATTN, 1, 65536, 64, 32768) == 0  # one split: no partials
+    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) > 0     # decode splits the rows
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def test_rejects_before_launch(L):
+    import compressed_sparse_attention_csa2_amd as csa2
+    n = None
+    # compress: NULL kc
+    s = L.csa2_compress(1, 4, FAKE, n, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                        FAKE, 8, n)
+    assert s == 1 and b"NULL" in L.csa2_last_error()
+    # compress: negative T
+    s = L.csa2_compress(1, -2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE,
+                        FAKE, FAKE, 8, n)
+    assert s == 2
+    # compress: neither projection nor given keys
+    s = L.csa2_compress(1, 4, FAKE, FAKE, FAKE, FAKE, n, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                        FAKE, 8, n)
+    assert s == 1
+    # window: cap 0
+    assert L.csa2_encode_window(1, 4, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, n) == 2
+    # index: workspace too small
+    s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 16, n)
+    assert s == 5 and b"workspace" in L.csa2_last_error()
+    # attention: unsupported heads, small ring, missing workspace
+    args = [FAKE] * 4 + [200, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, FAKE]
+    assert L.csa2_sparse_attn(1, 8, 24, *args, 1 << 30, n) == 3
+    args_ring = [FAKE] * 4 + [100, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, FAKE]
+    assert L.csa2_sparse_attn(1, 8, 64, *args_ring, 1 << 30, n) == 4
+    assert L.csa2_sparse_attn(4, 1, 64, *args, 0, n) == 5
+    # forward: decode without n_entries
+    s = L.csa2_forward(1, 1, 64, FAKE, n, n, n, n, n, n, n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                       FAKE, FAKE, FAKE, FAKE, 64, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n, FAKE,
+                       1 << 30, n)
+    assert s == 1 and b"n_entries" in L.csa2_last_error()
+    # forward: ring smaller than T + 127
+    s = L.csa2_forward(1, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, FAKE,
+                       FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, n, FAKE, FAKE, 100, FAKE, FAKE,
+                       FAKE, n, FAKE, 1 << 30, n)
+    assert s == 4
+    # encoders: bad widths
+    assert L.csa2_encode_fp4_rows(FAKE, 4, 48, FAKE, FAKE, n) == 2
+    assert L.csa2_encode_fp8_rows(FAKE, 4, 2048, FAKE, FAKE, n) == 2
+    assert L.csa2_decode_fp8_rows(FAKE, 4, 12, FAKE, n) == 2
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(csa2.CSA2Error, match="GPU"):
+        csa2.csa2_encode_fp4_rows(x, torch.zeros(4, 16, dtype=torch.uint8),
+                                  torch.zeros(4, 1, dtype=torch.uint8))
+
+
+def test_product_path_has_no_oracle_import():
+    """the library package never imports the oracle"""
+    pkg = os.path.join(ROOT, "compressed_sparse_attention_csa2_amd")
+    for dp, _, fs in os.walk(pkg):
+        for f in fs:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dp, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "csa2_oracle" not in txt, f

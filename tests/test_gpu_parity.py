@@ -1,0 +1,282 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small sizes are compared in full (several tiles and a ragged tail); the five
+measured workloads run at full size in the benchmark's launch configuration
+and are compared on sampled rows.
+"""
+import numpy as np
+import pytest
+
+from tests.parity import check_attention, check_selection, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print("[gpu]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_csa2_amd as csa2
+    csa2.lib()
+    return "cuda"
+
+
+def _up(a):
+    import csa2_harness
+    return csa2_harness.up(a)
+
+
+def _down(t):
+    import csa2_harness
+    return csa2_harness.down(t)
+
+
+# ---------------------------------------------------------------- formats
+def test_fp4_decode_matches_oracle_values(dev, orc):
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    log("csa2_decode_fp4_rows: 256 code bytes x scale bytes")
+    sbytes = np.array([1, 60, 100, 117, 120, 125, 127, 128, 130, 140, 180, 250], np.uint8)
+    rows = len(sbytes)
+    codes = np.tile(np.arange(256, dtype=np.uint8)[None, :16 * 16], (rows, 1))  # 256 bytes = 512 elems
+    scales = np.repeat(sbytes[:, None], 16, axis=1)
+    out = torch.zeros(rows, 512, dtype=torch.bfloat16, device=dev)
+    csa2.csa2_decode_fp4_rows(_up(codes), _up(scales), out)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(_down(out))
+    ref = orc.fp4_decode(codes, scales)
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_decode_matches_oracle_values(dev, orc):
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    log("csa2_decode_fp8_rows: all 254 finite codes")
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0, 0x80        # NaN codes are never stored
+    out = torch.zeros(1, 256, dtype=torch.bfloat16, device=dev)
+    csa2.csa2_decode_fp8_rows(_up(codes[None]), out)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(_down(out))[0]
+    ref = np.array([orc.e4m3_value(int(c)) for c in codes])
+    assert np.array_equal(got, ref)
+
+
+def _edge_rows(rng, cols):
+    x = rng.standard_normal((64, cols)).astype(np.float32)
+    x[1] *= 1e-3
+    x[2] *= 300.0
+    x[3] = 0.0
+    x[4, ::7] = 0.0
+    x[5] = np.ldexp(np.round(rng.standard_normal(cols) * 4) / 4, rng.integers(-3, 3, cols))  # ties
+    x[6] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0], cols) * rng.choice([-1, 1], cols)
+    x[7] = np.exp(rng.standard_normal(cols) * 3) * rng.choice([-1, 1], cols)
+    import tests.test_oracle_compress as tc
+    return tc.bf16(x)
+
+
+def test_encoders_bit_exact(dev, orc):
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    rng = np.random.default_rng(5)
+    for cols in (512, 128):
+        x = _edge_rows(rng, cols)
+        log(f"csa2_encode_fp4_rows / fp8_rows: rows={len(x)} cols={cols}")
+        c4 = torch.zeros(len(x), cols // 2, dtype=torch.uint8, device=dev)
+        s4 = torch.zeros(len(x), cols // 32, dtype=torch.uint8, device=dev)
+        c8 = torch.zeros(len(x), cols, dtype=torch.uint8, device=dev)
+        s8 = torch.zeros(len(x), dtype=torch.float32, device=dev)
+        xd = _up(x)
+        csa2.csa2_encode_fp4_rows(xd, c4, s4)
+        csa2.csa2_encode_fp8_rows(xd, c8, s8)
+        torch.cuda.synchronize()
+        oc4, os4 = orc.fp4_encode_rows_bf16(x)
+        oc8, os8 = orc.fp8_encode_rows_bf16(x)
+        assert np.array_equal(_down(c4), oc4) and np.array_equal(_down(s4), os4)
+        assert np.array_equal(_down(c8), oc8) and np.array_equal(_down(s8), os8)
+
+
+# ---------------------------------------------------------------- prefill
+def _prefill(wl):
+    import torch
+    import csa2_harness
+    log(f"csa2_forward prefill: {wl.name} seed={wl.seed:#x}")
+    run = csa2_harness.PrefillRun(wl)
+    run.forward()
+    torch.cuda.synchronize()
+    return run
+
+
+def _check_prefill_rows(wl, out, ref, rows, attn=True):
+    r = ref.rows(rows, want_scores=True, want_attn=attn)
+    swaps = 0
+    for i, t in enumerate(rows):
+        swaps += check_selection(out["idx"][0, t], out["cnt"][0, t], r["idx"][i], r["cnt"][i],
+                                 r["S"][i])
+    if attn:
+        import oracle
+        got = out["O"][0][:, rows, :].transpose(1, 0, 2)
+        exp = r["O"]
+        # where a boundary swap changed the row set, evaluate the oracle on the GPU's selection
+        for i, t in enumerate(rows):
+            if not np.array_equal(out["idx"][0, t], r["idx"][i]):
+                O, _, _ = oracle.attend(wl.Q_rows(0, [t])[0], int(t), ref.w_codes[0],
+                                        ref.w_scale[0], ref.cap, ref.z_codes[0], ref.z_scales[0],
+                                        out["idx"][0, t], int(out["cnt"][0, t]), ref.sink,
+                                        ref.cos, ref.sin)
+                exp = exp.copy()
+                exp[i] = O
+        mx, rel = check_attention(got, exp, wl.name)
+        log(f"  rows={len(rows)} swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
+    return swaps
+
+
+@pytest.mark.parametrize("T,H", [(256, 16), (257, 16), (130, 32)])
+def test_prefill_derived_keys_full(dev, synth, T, H):
+    """T=256 is the small measured workload; odd T leaves the last position pending."""
+    from oracle.reference import PrefillReference
+    wl = synth.workload(0, T=T, H=H)
+    out = _prefill(wl).fetch()
+    ref = PrefillReference(wl)
+    w_codes, w_scale = ref.window_full()
+    n = T // 2
+    assert np.array_equal(out["z_codes"][0, :n], ref.z_codes[0, :n])
+    assert np.array_equal(out["z_scales"][0, :n], ref.z_scales[0, :n])
+    assert np.array_equal(out["ki_codes"][0, :n], ref.ki_codes[0, :n])
+    assert np.array_equal(out["ki_scales"][0, :n], ref.ki_scales[0, :n])
+    assert np.array_equal(out["w_codes"][0, :T], w_codes[:T])
+    assert np.array_equal(out["w_scale"][0, :T], w_scale[:T])
+    _check_prefill_rows(wl, out, ref, np.arange(T))
+
+
+def test_prefill_clustered_keys_ragged(dev, synth):
+    """given-mode keys, 2 index chunks + a ragged tail, selection active for t >= 1023"""
+    from oracle.reference import PrefillReference
+    wl = synth.workload(1, T=2600, H=16)
+    out = _prefill(wl).fetch()
+    ref = PrefillReference(wl)
+    n = wl.Tq // 2
+    assert np.array_equal(out["z_codes"][0, :n], ref.z_codes[0, :n])
+    assert np.array_equal(out["ki_codes"][0, :n], ref.ki_codes[0, :n])
+    assert np.array_equal(out["ki_scales"][0, :n], ref.ki_scales[0, :n])
+    rows = np.unique(np.concatenate([np.arange(0, 8), [1021, 1022, 1023, 1024, 2047, 2048],
+                                     np.arange(wl.Tq - 6, wl.Tq),
+                                     np.random.default_rng(3).integers(0, wl.Tq, 30)]))
+    _check_prefill_rows(wl, out, ref, rows)
+
+
+def test_prefill_deterministic(dev, synth):
+    import torch
+    import csa2_harness
+    wl = synth.workload(1, T=1500, H=32)
+    log(f"determinism: {wl.name}")
+    run = csa2_harness.PrefillRun(wl)
+    run.forward()
+    a = run.fetch()
+    run.idx.fill_(-5)
+    run.O.zero_()
+    run.forward()
+    torch.cuda.synchronize()
+    b = run.fetch()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_sparse_attn_given_oracle_selection(dev, synth):
+    """attention alone, fed the oracle's caches and selections"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    from oracle.reference import PrefillReference
+    wl = synth.workload(1, T=1400, H=64)
+    ref = PrefillReference(wl)
+    w_codes, w_scale = ref.window_full()
+    rows = np.arange(wl.Tq)
+    sel = ref.rows(rows, want_attn=False)
+    log(f"csa2_sparse_attn with oracle selection: {wl.name}")
+    O = torch.zeros(1, wl.H, wl.Tq, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(1, wl.H, wl.Tq, dtype=torch.float32, device=dev)
+    cos_t, sin_t = synth.rope_table(wl.rope_rows)
+    ws = csa2.workspace(csa2.OP_SPARSE_ATTN, 1, wl.Tq, wl.H, wl.Tq // 2)
+    csa2.csa2_sparse_attn(_up(np.zeros(1, np.int32)), _up(wl.Q()), _up(w_codes[None]),
+                          _up(w_scale[None]), _up(ref.z_codes), _up(ref.z_scales),
+                          _up(sel["idx"][None]), _up(sel["cnt"][None]), _up(ref.sink),
+                          _up(cos_t), _up(sin_t), O, lse, ws)
+    torch.cuda.synchronize()
+    sample = np.random.default_rng(9).choice(wl.Tq, 40, replace=False)
+    r = ref.rows(sample)
+    got = _down(O)[0][:, sample, :].transpose(1, 0, 2)
+    mx, rel = check_attention(got, r["O"], "sparse_attn")
+    lse_g = _down(lse)[0][:, sample].T
+    assert np.max(np.abs(lse_g - r["lse"])) < 1e-3
+    log(f"  max|dO|={mx:.2e} rel={rel:.2e}")
+
+
+# ---------------------------------------------------------------- decode
+@pytest.mark.parametrize("Tq,N,keys", [(1, 3000, "flat"), (6, 2600, "lognormal_dup")])
+def test_decode_small(dev, synth, Tq, N, keys):
+    import torch
+    import csa2_harness
+    from oracle.reference import DecodeReference
+    wl = synth.decode_workload(B=3, Tq=Tq, n_entries=N, H=64, keys=keys)
+    log(f"csa2_forward decode: {wl.name} keys={keys}")
+    run = csa2_harness.DecodeRun(wl)
+    run.forward()
+    torch.cuda.synchronize()
+    out = run.fetch()
+    import oracle
+    for b in range(wl.B):
+        ref = DecodeReference(wl, b)
+        r = ref.rows(np.arange(Tq), want_scores=True)
+        swaps = 0
+        for i in range(Tq):
+            swaps += check_selection(out["idx"][b, i], out["cnt"][b, i], r["idx"][i], r["cnt"][i],
+                                     r["S"][i])
+        exp = r["O"].copy()
+        for i in range(Tq):     # a boundary swap: judge attention on the GPU's selection
+            if not np.array_equal(out["idx"][b, i], r["idx"][i]):
+                ref._ensure_z(out["idx"][b, i])
+                exp[i] = oracle.attend(wl.Q()[b][:, i, :], wl.q_pos0 + i, ref.w_codes, ref.w_scale,
+                                       wl.cap, ref.z_codes, ref.z_scales, out["idx"][b, i],
+                                       int(out["cnt"][b, i]), ref.sink, ref.cos, ref.sin)[0]
+        mx, rel = check_attention(out["O"][b].transpose(1, 0, 2), exp, wl.name)
+        log(f"  request {b}: swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
+
+
+def test_index_scores_match_oracle(dev, orc):
+    """raw indexer scores against the oracle's (fp32 accumulation vs exact), ragged chunks"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import tests.test_oracle_compress as tc
+    rng = np.random.default_rng(17)
+    N, Tq = 2100, 12
+    kpre = tc.bf16(rng.standard_normal((N, 128)).astype(np.float32))
+    kc_, ks_ = orc.fp4_encode_rows_bf16(kpre)
+    qI = tc.bf16(rng.standard_normal((1, Tq, 32, 128)).astype(np.float32))
+    wI = (rng.standard_normal((1, Tq, 32)) / 64).astype(np.float32)
+    q0 = 2 * N - Tq - 300            # last queries see every entry
+    log(f"csa2_index_scores: N={N} Tq={Tq}")
+    S = torch.full((1, Tq, N), float("nan"), dtype=torch.float32, device=dev)
+    ws = csa2.workspace(csa2.OP_INDEX_SCORES, 1, Tq, 64, N)
+    csa2.csa2_index_scores(_up(np.array([q0], np.int32)), _up(np.array([N], np.int32)), _up(qI),
+                           _up(wI), _up(kc_[None]), _up(ks_[None]), S, ws)
+    torch.cuda.synchronize()
+    g = _down(S)[0]
+    e4 = np.array([orc.e4m3_value(c) for c in range(256)])
+    Kabs = np.abs(orc.fp4_decode(kc_, ks_))
+    u = 2.0 ** -24
+    for i in range(Tq):
+        n = min((q0 + i + 1) // 2, N)
+        q8, sq = orc.quant_index_query(qI[0, i])
+        ref = orc.index_scores(q8, sq, wI[0, i], kc_, ks_, n)
+        assert np.all(np.isfinite(g[i, :n]))
+        err = np.abs(g[i, :n].astype(np.float64) - ref)
+        # fp32 recursive-summation bound: 128-term dot products (<= 127u), the weight
+        # product, the 32-term head sum and the final rounding, with a factor-2 margin
+        mass = (Kabs[:n] @ (np.abs(e4[q8]).T * (np.abs(wI[0, i]) * sq)[None, :])).sum(1)
+        bound = 2 * (128 + 32 + 2) * u * mass + u * np.abs(ref)
+        assert np.all(err <= bound), (i, err.max(), (err / bound).max())

@@ -1,0 +1,96 @@
+"""The five measured workloads at full size, in the launch configuration the
+benchmark times (one csa2_forward), compared with the oracle on sampled rows.
+Storage codes are compared in full where the oracle can produce them quickly."""
+import numpy as np
+import pytest
+
+from tests.parity import check_attention, check_selection
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print("[gpu]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return "cuda"
+
+
+def _attn_expected(wl, ref, b, rows_local, positions, g_idx, g_cnt, r, Qrows):
+    """oracle attention on the GPU's selection where a boundary swap changed it"""
+    import oracle
+    exp = r["O"].copy()
+    for i in range(len(rows_local)):
+        if not np.array_equal(g_idx[i], r["idx"][i]):
+            O, _, _ = oracle.attend(Qrows[i], int(positions[i]), ref.w_codes if ref.w_codes.ndim == 2 else ref.w_codes[0],
+                                    ref.w_scale if ref.w_scale.ndim == 1 else ref.w_scale[0], wl.cap,
+                                    ref.z_codes if ref.z_codes.ndim == 2 else ref.z_codes[0],
+                                    ref.z_scales if ref.z_scales.ndim == 2 else ref.z_scales[0],
+                                    g_idx[i], int(g_cnt[i]), ref.sink, ref.cos, ref.sin)
+            exp[i] = O
+    return exp
+
+
+@pytest.mark.parametrize("cid,nrows", [(1, 48), (2, 12)])
+def test_prefill_workload(dev, synth, cid, nrows):
+    import torch
+    import csa2_harness
+    from oracle.reference import PrefillReference
+    wl = synth.workload(cid)
+    log(f"workload {cid}: {wl.name}")
+    run = csa2_harness.PrefillRun(wl)
+    run.forward()
+    torch.cuda.synchronize()
+    T = wl.Tq
+    rng = np.random.default_rng(100 + cid)
+    rows = np.unique(np.concatenate([[0, 1, 2, 1022, 1023, T - 1],
+                                     rng.integers(T // 2, T, nrows - 6)]))
+    ti = torch.from_numpy(rows).cuda()
+    g_idx = run.idx[0, ti].cpu().numpy()
+    g_cnt = run.cnt[0, ti].cpu().numpy()
+    g_O = csa2_harness.down(run.O[0][:, ti, :].contiguous()).transpose(1, 0, 2)
+    zc, zs = csa2_harness.down(run.z_codes), csa2_harness.down(run.z_scales)
+    kc, ks = csa2_harness.down(run.ki_codes), csa2_harness.down(run.ki_scales)
+    del run
+    torch.cuda.empty_cache()
+    ref = PrefillReference(wl)
+    assert np.array_equal(zc, ref.z_codes) and np.array_equal(zs, ref.z_scales)
+    assert np.array_equal(kc, ref.ki_codes) and np.array_equal(ks, ref.ki_scales)
+    r = ref.rows(rows, want_scores=True)
+    swaps = sum(check_selection(g_idx[i], g_cnt[i], r["idx"][i], r["cnt"][i], r["S"][i])
+                for i in range(len(rows)))
+    exp = _attn_expected(wl, ref, 0, rows, rows, g_idx, g_cnt, r, wl.Q_rows(0, rows))
+    mx, rel = check_attention(g_O, exp, wl.name)
+    log(f"  rows={len(rows)} swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
+
+
+@pytest.mark.parametrize("cid,reqs,qrows", [(3, (0, 77, 127), (0,)), (4, (5,), (0, 5))])
+def test_decode_workload(dev, synth, cid, reqs, qrows):
+    import torch
+    import csa2_harness
+    from oracle.reference import DecodeReference
+    wl = synth.workload(cid)
+    log(f"workload {cid}: {wl.name}")
+    run = csa2_harness.DecodeRun(wl)
+    run.forward()
+    torch.cuda.synchronize()
+    out = run.fetch()
+    del run
+    torch.cuda.empty_cache()
+    for b in reqs:
+        ref = DecodeReference(wl, b)
+        q = np.array(qrows)
+        r = ref.rows(q, want_scores=True)
+        swaps = sum(check_selection(out["idx"][b, i], out["cnt"][b, i], r["idx"][k], r["cnt"][k],
+                                    r["S"][k]) for k, i in enumerate(q))
+        ref._ensure_z(out["idx"][b, q].reshape(-1))
+        Qr = wl.Q()[b][:, q, :].transpose(1, 0, 2)
+        exp = _attn_expected(wl, ref, b, q, wl.q_pos0 + q, out["idx"][b, q], out["cnt"][b, q], r, Qr)
+        got = out["O"][b][:, q, :].transpose(1, 0, 2)
+        mx, rel = check_attention(got, exp, f"{wl.name} request {b}")
+        log(f"  request {b}: swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
