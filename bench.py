@@ -1,0 +1,240 @@
+"""Benchmark of the CSA2 attention layer on one MI355X.
+
+A step is one csa2_forward over one batch of synthetic inputs: compression of
+the new positions, window rows, lightning indexer + top-512, and the sparse
+attention.  Default workload: prefill B=1, T=65536, 64 heads (32768
+compressed entries).  A second object reports the batched decode workload
+(128 requests x 1 query at 131072 context).  Inputs are seeded synthetic
+tensors already resident in device memory when timing starts.
+
+Prints ONE JSON line.  Roofline figures use algorithmic work only:
+  indexer scores  8192 FLOP per (query, candidate entry) pair (32 heads x 128 x 2)
+  attention       4 * 512 * H FLOP per (query, attended row) (QK^T and PV)
+  decode bytes    68 B per scanned index key + gathered rows + Q/O/window
+and are divided by the kernel's average duration measured here with HIP
+events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8 = 5.0e15       # dense FP8 MFMA, FLOP/s
+PEAK_BF16 = 2.5e15      # dense BF16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # HBM3E, B/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def prefill_work(T: int, H: int):
+    """algorithmic FLOPs of the indexer scores and of attention for a T-token prefill"""
+    idx_pairs = sum((t + 1) // 2 for t in range(T))
+    rows = sum(min(t + 1, 128) + min((t + 1) // 2, 512) for t in range(T))
+    return 8192.0 * idx_pairs, 4.0 * 512 * H * rows
+
+
+def decode_bytes(B: int, Tq: int, N: int, H: int) -> float:
+    """minimum HBM bytes of one decode step (per request: the index-key scan,
+    gathered compressed rows, window rows, queries, outputs, indexer queries)"""
+    per_req = (68.0 * N + Tq * 512 * 272 + (127 + Tq) * 516 + Tq * (2 * H * 512 * 2)
+               + Tq * (32 * 128 * 2 + 32 * 4))
+    return B * per_req
+
+
+def time_events(fn, steps: int, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / steps      # ms per call
+
+
+def stage_times(run, steps: int, stream):
+    """per-stage ms (each stage is one ABI call) measured with events on the launch stream"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    ws_i = run.ws
+    out = {}
+    if hasattr(run, "kc"):
+        out["compress"] = time_events(lambda: csa2.csa2_compress(
+            run.pos0, run.kc, run.gc, run.gamma_c, run.w_ik, run.gamma_ik, run.ki_given,
+            run.rope_cos, run.rope_sin, run.z_codes, run.z_scales, run.ki_codes, run.ki_scales),
+            steps, stream)
+        out["window"] = time_events(lambda: csa2.csa2_encode_window(
+            run.pos0, run.wn, run.rope_cos, run.rope_sin, run.w_codes, run.w_scale), steps, stream)
+        q_pos0 = run.pos0
+        n_ent = torch.full_like(run.pos0, run.stride)
+    else:
+        q_pos0, n_ent = run.q_pos0, run.n_entries
+    scores = torch.empty(run.idx.shape[0], run.idx.shape[1], run.stride, dtype=torch.float32,
+                         device="cuda")
+    out["index_scores"] = time_events(lambda: csa2.csa2_index_scores(
+        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, scores, ws_i), steps, stream)
+    del scores
+    out["index_topk"] = time_events(lambda: csa2.csa2_index_topk(
+        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, run.idx, run.cnt, ws_i),
+        steps, stream)
+    out["sparse_attn"] = time_events(lambda: csa2.csa2_sparse_attn(
+        q_pos0, run.Q, run.w_codes, run.w_scale, run.z_codes, run.z_scales, run.idx, run.cnt,
+        run.sink, run.rope_cos, run.rope_sin, run.O, run.lse, run.ws), steps, stream)
+    return out
+
+
+def cpu_baseline_prefill(wl, n_rows: int):
+    """the oracle on a bounded sample: all compression + n_rows query rows spread over T"""
+    import numpy as np
+    from oracle.reference import PrefillReference
+    t0 = time.perf_counter()
+    ref = PrefillReference(wl)
+    t_compress = time.perf_counter() - t0
+    rows = np.linspace(0, wl.Tq - 1, n_rows).astype(np.int64)
+    t1 = time.perf_counter()
+    for t in rows:
+        ref.rows([t])
+    t_rows = time.perf_counter() - t1
+    per_token = t_compress / wl.Tq + t_rows / n_rows
+    return {"value": 1.0 / per_token, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full compression of {wl.Tq} positions ({t_compress:.1f} s) + {n_rows} "
+                      f"query rows evenly spaced over t=0..{wl.Tq - 1} ({t_rows:.1f} s), "
+                      f"single-threaded C oracle, rate = 1 / (compress s/token + row s/row)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time a single workload (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs the layer on one GPU; multi-GPU sharding is "
+                                   "described in DESIGN.md but not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import csa2_harness
+    import csa2_synth as synth
+    import compressed_sparse_attention_csa2_amd as csa2
+    csa2.lib()
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    stream = torch.cuda.current_stream()
+
+    result = {}
+    wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
+    if args.only == "decode":
+        args.no_cpu = True
+        run_decode(args, result, stream)
+        print(json.dumps(result), flush=True)
+        return
+    # ---------------------------------------------------------------- prefill
+    log(f"generating inputs: {wl.name}")
+    t0 = time.time()
+    run = csa2_harness.PrefillRun(wl)
+    torch.cuda.synchronize()
+    log(f"inputs resident ({time.time() - t0:.1f} s); warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run.forward()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_start = time.perf_counter()
+    ms = time_events(run.forward, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) / args.steps * 1e3
+    log(f"prefill: {ms:.3f} ms/step (wall {wall:.3f})")
+    stages = stage_times(run, args.steps, stream)
+    log(f"stages (ms): {json.dumps({k: round(v, 4) for k, v in stages.items()})}")
+    flop_idx, flop_att = prefill_work(wl.Tq, wl.H)
+    t_att = stages["sparse_attn"] * 1e-3
+    t_idx = stages["index_scores"] * 1e-3
+    if t_att >= t_idx:
+        dom = {"kernel": "k_attn (csa2_sparse_attn: gather, dequant, bf16 MFMA QK^T/PV, sink "
+                         "softmax, inverse rotation)", "bound": "mfma", "achieved":
+               flop_att / t_att / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+               "flop_per_launch": flop_att}
+    else:
+        dom = {"kernel": "k_index_scores (csa2_index_scores: q^I FP8 pre-pass + FP8xFP4 MFMA "
+                         "scores)", "bound": "mfma", "achieved": flop_idx / t_idx / 1e12,
+               "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s", "flop_per_launch": flop_idx}
+    dom["frac"] = dom["achieved"] / dom["peak"]
+    dom["traffic"] = None
+    value = wl.Tq / (ms * 1e-3)
+    mixed_time = flop_idx / PEAK_FP8 + flop_att / PEAK_BF16
+    result.update({
+        "metric": "CSA2 query-tokens/s (prefill T=64K; decode B=128@128K) + % of MFMA/HBM roofline",
+        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8xfp4 indexer + bf16 attention",
+        "data": "synthetic (seeded; shapes and distributions of the workload description)",
+        "config": {"workload": f"CSA2 prefill B=1 T={wl.Tq} H={wl.H} d=512 window 128 "
+                               f"top-512, {wl.Tq // 2} compressed entries, clustered index keys",
+                   "global_batch": 1, "seq_len": wl.Tq, "parallelism": "none (1 GPU)"},
+        "roofline": dom,
+        "stages_ms": stages,
+        "mixed_roofline_frac": mixed_time / (ms * 1e-3),
+        "fp8_peak_frac_literal": (flop_idx + flop_att) / (ms * 1e-3) / PEAK_FP8,
+    })
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_decode and args.only is None:
+        run_decode(args, result, stream)
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu:
+        log(f"timing the CPU oracle on {args.cpu_rows} rows")
+        result["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def run_decode(args, result, stream):
+    import torch
+    import csa2_harness
+    import csa2_synth as synth
+    if True:
+        dwl = synth.workload(3)
+        log(f"generating caches: {dwl.name}")
+        t0 = time.time()
+        drun = csa2_harness.DecodeRun(dwl)
+        log(f"caches resident ({time.time() - t0:.1f} s)")
+        for _ in range(args.warmup):
+            drun.forward()
+        torch.cuda.synchronize()
+        dms = time_events(drun.forward, args.steps, stream)
+        dstages = stage_times(drun, args.steps, stream)
+        log(f"decode: {dms:.4f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in dstages.items()})}")
+        nbytes = decode_bytes(dwl.B, dwl.Tq, dwl.n_entries, dwl.H)
+        scan_bytes = 68.0 * dwl.n_entries * dwl.B
+        result["decode"] = {
+            "workload": "CSA2 batched decode B=128 x 1 query, 131072 context (65536 FP4 entries "
+                        "+ 128 FP8 window rows), H=64, top-512",
+            "value": dwl.B * dwl.Tq / (dms * 1e-3), "unit": "query-tokens/s", "ms_per_step": dms,
+            "stages_ms": dstages,
+            "hbm_frac_step": nbytes / (dms * 1e-3) / PEAK_HBM,
+            "roofline": {"kernel": "k_index_scores (index-key scan)", "bound": "hbm",
+                         "achieved": scan_bytes / (dstages["index_scores"] * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": scan_bytes / (dstages["index_scores"] * 1e-3) / PEAK_HBM,
+                         "bytes_per_launch": scan_bytes, "traffic": None},
+        }
+        del drun
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()
