@@ -29,7 +29,7 @@ __global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const u
                                int);
 __global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int32_t*,
                        int32_t*);
-template <int NW>
+template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
                        const int32_t*, const float*, const float*, const float*, int64_t,
@@ -172,9 +172,9 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     float* pO = (float*)((uint8_t*)ws + L.pO);
     float* pml = (float*)((uint8_t*)ws + L.pml);
     const dim3 grid((unsigned)((int64_t)B * Tq), (unsigned)L.nsplit);
-    const int nw = H / 16;
-#define CSA2_ATTN(NWV)                                                                        \
-    hipLaunchKernelGGL(k_attn<NWV>, grid, dim3(NWV * 64), 0, st, B, Tq, H, q_pos0, Q, w_codes, \
+    const int nw = H / 16;   // head groups; two waves each
+#define CSA2_ATTN(NWV)                                                                         \
+    hipLaunchKernelGGL(k_attn<NWV>, grid, dim3(NWV * 128), 0, st, B, Tq, H, q_pos0, Q, w_codes, \
                        w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
                        rope_rows, O, lse, L.nsplit, L.rows_per, pO, pml)
     switch (nw) {
