@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (no accumulator-register copies in the epilogues)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
 ]
 

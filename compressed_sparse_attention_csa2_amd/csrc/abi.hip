@@ -27,8 +27,10 @@ template <int TOK>
 __global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                const float*, const uint8_t*, const uint8_t*, int64_t, float*, int,
                                int);
-__global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int32_t*,
-                       int32_t*);
+__global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int,
+                       int32_t*, int32_t*, int32_t*, float*, int32_t*);
+__global__ void k_topk_merge(int, int, int, const int32_t*, const float*, const int32_t*,
+                             int32_t*, int32_t*);
 template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
@@ -70,7 +72,6 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int IDX_CHUNK_H = 1024;   // must equal the indexer's chunk
 constexpr int MAX_ROWS = WINDOW + TOPK;
 
 int index_tok(int Tq) { return Tq == 1 ? 1 : (Tq <= 8 ? 8 : 4); }
@@ -87,16 +88,25 @@ void attn_split(int64_t tokens, int* nsplit, int* rows_per) {
     *nsplit = (int)cdiv(MAX_ROWS, rp);
 }
 
+constexpr int TOPK_SEG_H = 32768;   // list length one selection block handles
+
+int topk_segments(int64_t stride) { return (int)cdiv(stride, TOPK_SEG_H); }
+
 struct IndexWs {
-    size_t q8, wq, S, total;
+    size_t q8, wq, S, seg_j, seg_s, seg_n, total;
 };
 IndexWs index_ws(int B, int Tq, int64_t stride) {
     IndexWs w;
     const size_t rows = (size_t)B * Tq;
+    const int nseg = topk_segments(stride);
     w.q8 = 0;
     w.wq = align256(rows * HI * DI);
     w.S = w.wq + align256(rows * HI * sizeof(float));
-    w.total = w.S + align256(rows * (size_t)stride * sizeof(float));
+    w.seg_j = w.S + align256(rows * (size_t)stride * sizeof(float));
+    const size_t segc = nseg > 1 ? rows * nseg * TOPK : 0;
+    w.seg_s = w.seg_j + align256(segc * sizeof(int32_t));
+    w.seg_n = w.seg_s + align256(segc * sizeof(float));
+    w.total = w.seg_n + align256((nseg > 1 ? rows * nseg : 0) * sizeof(int32_t));
     return w;
 }
 
@@ -134,7 +144,7 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
                        wI, qrows, q8, wq);
     const int tok = index_tok(Tq);
     const int n_tg = (int)cdiv(Tq, tok);
-    const int n_ch = (int)cdiv(stride, IDX_CHUNK_H);
+    const int n_ch = (int)cdiv(stride, IDX_CHUNK);
     const int64_t items = (int64_t)B * n_tg * n_ch;
     const dim3 grid((unsigned)cdiv(items, 4));
     if (tok == 1)
@@ -156,8 +166,16 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     const IndexWs L = index_ws(B, Tq, stride);
     float* Sc = (float*)((uint8_t*)ws + L.S);
     launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, ws, st);
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)((int64_t)B * Tq)), dim3(256), 0, st, B, Tq, q_pos0,
-                       n_entries, Sc, stride, idx, cnt);
+    const int nseg = topk_segments(stride);
+    int32_t* seg_j = (int32_t*)((uint8_t*)ws + L.seg_j);
+    float* seg_s = (float*)((uint8_t*)ws + L.seg_s);
+    int32_t* seg_n = (int32_t*)((uint8_t*)ws + L.seg_n);
+    const unsigned rows = (unsigned)((int64_t)B * Tq);
+    hipLaunchKernelGGL(k_topk, dim3(rows, (unsigned)nseg), dim3(256), 0, st, B, Tq, q_pos0,
+                       n_entries, Sc, stride, nseg, idx, cnt, seg_j, seg_s, seg_n);
+    if (nseg > 1)
+        hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(256), 0, st, B, Tq, nseg, seg_j, seg_s,
+                           seg_n, idx, cnt);
     return check_launch("csa2_index_topk");
 }
 
@@ -270,6 +288,8 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
+    if (topk_segments(entry_stride) > 64)
+        return fail(CSA2_ERR_UNSUPPORTED, "index_topk: entry_stride %lld > 2097152", (long long)entry_stride);
     const size_t need = index_ws(B, Tq, entry_stride).total;
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
@@ -339,6 +359,8 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
     if ((int64_t)cap < (int64_t)T + WINDOW - 1)
         return fail(CSA2_ERR_RANGE, "forward: window ring cap=%d < T+127=%lld", cap, (long long)T + WINDOW - 1);
     if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "forward: empty rotary table");
+    if (topk_segments(entry_stride) > 64)
+        return fail(CSA2_ERR_UNSUPPORTED, "forward: entry_stride %lld > 2097152", (long long)entry_stride);
     const size_t need = csa2_workspace_size(CSA2_OP_FORWARD, B, T, H, entry_stride);
     if (!ws || ws_bytes < need)
         return fail(CSA2_ERR_WORKSPACE, "forward: workspace %zu < %zu bytes", ws_bytes, need);

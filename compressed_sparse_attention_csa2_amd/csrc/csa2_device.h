@@ -21,6 +21,7 @@ constexpr int HI = 32;          // indexer heads
 constexpr int DI = 128;         // indexer width
 constexpr int KI_ROPE_LO = 64;  // rotated channels of an index key: 64..127
 constexpr int TOPK = 512;
+constexpr int IDX_CHUNK = 2048;  // index entries scanned by one wave of the score kernel
 
 typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(4))) float f4;
