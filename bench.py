@@ -29,6 +29,35 @@ PEAK_FP8 = 5.0e15       # dense FP8 MFMA, FLOP/s
 PEAK_BF16 = 2.5e15      # dense BF16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # HBM3E, B/s
 
+# HBM bytes per launch counted by rocprofv3 (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, factors from
+# a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
+# for the kernel sources it was taken on: reported as null once any listed file has changed.
+TRAFFIC = {
+    ("k_attn", "prefill", 65536): (1.352e10, {
+        "attention.hip": "89d1af482a00c98ad02d3dd4af06b5601f4d8c5e5025c092bb9fe27455d685c1",
+        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
+    ("k_index_scores", "prefill", 65536): (5.321e9, {
+        "indexer.hip": "f7dc91f1199930d3221211c44fcb891ffd4c4bed9ad1117010a4c1a6043030d3",
+        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
+    ("k_index_scores", "decode", 131072): (6.085e8, {
+        "indexer.hip": "f7dc91f1199930d3221211c44fcb891ffd4c4bed9ad1117010a4c1a6043030d3",
+        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
+}
+
+
+def measured_traffic(kernel: str, mode: str, size: int):
+    """counter-measured HBM bytes per launch, or None if not measured on the current sources"""
+    import hashlib
+    ent = TRAFFIC.get((kernel, mode, size))
+    if ent is None:
+        return None
+    csrc = os.path.join(ROOT, "compressed_sparse_attention_csa2_amd", "csrc")
+    for name, digest in ent[1].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return ent[0]
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -118,8 +147,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time a single workload (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="time a single workload (for profiling runs); 'copy' runs a plain "
+                         "1 GiB device copy, the calibration kernel for the HBM byte counters")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
     args = ap.parse_args()
@@ -137,6 +167,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     result = {}
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.warmup, 1)):
+            dst.copy_(src)
+        ms = time_events(lambda: dst.copy_(src), args.steps, stream)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                          "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+        return
     wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
     if args.only == "decode":
         args.no_cpu = True
@@ -173,7 +213,8 @@ def main():
                          "scores)", "bound": "mfma", "achieved": flop_idx / t_idx / 1e12,
                "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s", "flop_per_launch": flop_idx}
     dom["frac"] = dom["achieved"] / dom["peak"]
-    dom["traffic"] = None
+    dom["traffic"] = measured_traffic("k_attn" if t_att >= t_idx else "k_index_scores", "prefill",
+                                      wl.Tq)
     value = wl.Tq / (ms * 1e-3)
     mixed_time = flop_idx / PEAK_FP8 + flop_att / PEAK_BF16
     result.update({
@@ -230,7 +271,9 @@ def run_decode(args, result, stream):
                          "achieved": scan_bytes / (dstages["index_scores"] * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": scan_bytes / (dstages["index_scores"] * 1e-3) / PEAK_HBM,
-                         "bytes_per_launch": scan_bytes, "traffic": None},
+                         "bytes_per_launch": scan_bytes,
+                         "traffic": measured_traffic("k_index_scores", "decode",
+                                                     dwl.q_pos0 + 1)},
         }
         del drun
         torch.cuda.empty_cache()

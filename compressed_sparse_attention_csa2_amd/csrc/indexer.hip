@@ -3,8 +3,8 @@
 // "DeepSeek V4.1 -- Pooled group -> Source layer, pairs pooled", indexer
 // equations: S^I_{t,j} = sum_h w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j) over 32 heads
 // of 128 channels, and I_t = top_512(S^I_{t,j} : j < floor((t+1)/2)).
-// "Inside DeepSeek V4.1", section "Attention that looks at 640 places": the
-// indexer scores every entry and keeps the top 512.
+// "Inside DeepSeek V4.1", section "Attention that looks at 640 places": all
+// compressed entries are scored; 512 of them go on to the main attention.
 //
 // Queries are quantised per (token, head) row to E4M3FN (scale max|x|/448);
 // keys stay in their FP4 storage.  The dot products run on gfx950's block-
