@@ -35,7 +35,7 @@ template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
                        const int32_t*, const float*, const float*, const float*, int64_t,
-                       uint16_t*, float*, int, int, float*, float*);
+                       uint16_t*, float*, int, float*, float*);
 __global__ void k_attn_combine(int, int, int, const int32_t*, const float*, const float*,
                                const float*, int64_t, int, const float*, const float*, uint16_t*,
                                float*);
@@ -76,16 +76,12 @@ constexpr int MAX_ROWS = WINDOW + TOPK;
 
 int index_tok(int Tq) { return Tq == 1 ? 1 : (Tq <= 8 ? 8 : 4); }
 
-// split of the 640 attention rows across blocks for small token counts
-void attn_split(int64_t tokens, int* nsplit, int* rows_per) {
-    int ns = 1;
-    if (tokens < 1024) {
-        ns = (int)cdiv(2048, tokens > 0 ? tokens : 1);
-        if (ns > MAX_ROWS / 32) ns = MAX_ROWS / 32;
-    }
-    int rp = (int)cdiv(cdiv(MAX_ROWS, ns), 32) * 32;
-    *rows_per = rp;
-    *nsplit = (int)cdiv(MAX_ROWS, rp);
+// split of a token's attention rows (20 chunks of 32 at full size) across
+// blocks when there are too few tokens to fill the chip
+int attn_split(int64_t tokens) {
+    if (tokens >= 256) return 1;
+    const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
+    return ns > 8 ? 8 : ns;
 }
 
 constexpr int TOPK_SEG_H = 32768;   // list length one selection block handles
@@ -111,12 +107,12 @@ IndexWs index_ws(int B, int Tq, int64_t stride) {
 }
 
 struct AttnWs {
-    int nsplit, rows_per;
+    int nsplit;
     size_t pO, pml, total;
 };
 AttnWs attn_ws(int B, int Tq, int H) {
     AttnWs w;
-    attn_split((int64_t)B * Tq, &w.nsplit, &w.rows_per);
+    w.nsplit = attn_split((int64_t)B * Tq);
     w.pO = 0;
     w.pml = 0;
     w.total = 0;
@@ -190,12 +186,12 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     float* pO = (float*)((uint8_t*)ws + L.pO);
     float* pml = (float*)((uint8_t*)ws + L.pml);
     const dim3 grid((unsigned)((int64_t)B * Tq), (unsigned)L.nsplit);
-    const int nw = H / 16;   // head groups; two waves each
-#define CSA2_ATTN(NWV)                                                                         \
-    hipLaunchKernelGGL(k_attn<NWV>, grid, dim3(NWV * 128), 0, st, B, Tq, H, q_pos0, Q, w_codes, \
+    const int ht = H / 16;   // head tiles of 16
+#define CSA2_ATTN(HTV)                                                                         \
+    hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(512), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
                        w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
-                       rope_rows, O, lse, L.nsplit, L.rows_per, pO, pml)
-    switch (nw) {
+                       rope_rows, O, lse, L.nsplit, pO, pml)
+    switch (ht) {
         case 1: CSA2_ATTN(1); break;
         case 2: CSA2_ATTN(2); break;
         case 3: CSA2_ATTN(3); break;

@@ -8,84 +8,136 @@
 // that looks at 640 places": 64 query heads share one key-value vector per
 // place, and each head has a sink.
 //
-// One block per (query token, split of its rows); wave w owns heads
-// 16w..16w+15.  Rows are processed 32 at a time: the block gathers the rows
-// (FP8 window rows from the ring, FP4 entries picked by the indexer),
-// dequantises them exactly to bf16 into LDS twice -- row-major for
-// S^T = G Q^T (contraction over the 512 channels) and transposed for
-// O^T = G^T P^T (contraction over rows) -- and runs bf16 MFMA 16x16x32.
-// Window rows enter as their E4M3 codes; their fp32 row scale multiplies the
-// logit and is folded into P before the PV product.  The softmax is online in
-// fp32; the sink enters the denominator only.  Splits of the row range write
-// (m, l, unnormalised O) partials that a combine kernel merges.
+// One block of 8 waves per (query token, split of its rows).  The rows are
+// taken 32 at a time ("chunks"; window rows and compressed rows never share a
+// chunk).  Per chunk:
+//   staging  the chunk's raw codes (FP8 window rows or FP4 entries with their
+//            E8M0 block scales) are loaded one chunk ahead into registers and
+//            stored to LDS (double-buffered), swizzled by 16-byte unit;
+//   QK       wave (g4 = w/2, half = w%2) computes S for 16 heads x 16 rows
+//            with the block-scaled MFMA 16x16x128: A = the raw row codes (FP4
+//            with their own block scales, or FP8), B = the query split into
+//            two E4M3 terms hi + lo (each with an E8M0 scale per 128 channels),
+//            which together reproduce the bf16 query exactly up to the
+//            smallest elements of a block.  The same wave dequantises one
+//            quarter of its rows' channels to bf16 for the PV product;
+//   softmax  online, in log2 units, with a lazy maximum: the running maximum
+//            of a head only moves when the chunk exceeds it by more than
+//            2^8, so rescales are rare.  P (bf16) goes to LDS as [head][row];
+//   PV       wave w owns channels 64w..64w+63 for every head: O^T += G^T P^T
+//            with bf16 MFMA 16x16x32; G^T is read with the transposing LDS
+//            load (ds_read_b64_tr_b16), so each bf16 row is stored once.
+// Window rows enter as E4M3 codes; their fp32 row scale multiplies the logit
+// and is folded into P.  Splits of the chunk range write (m, l, unnormalised
+// O) partials that k_attn_combine merges.
 #include "csa2_device.h"
 
 namespace csa2 {
 
-constexpr int ATT_ROWS = 32;          // rows per chunk
-
-__device__ __forceinline__ float fast_exp(float x) { return expf(x); }
-constexpr int GT_LD = ATT_ROWS + 4;   // transposed LDS stride (bf16): 18 dwords
-
-// Row-major copy: row r holds its 64 chunks of 8 channels; chunk c is stored at
-// position c ^ (r & 15).  The 64 lanes writing one row and the 16 lanes reading
-// one chunk of 16 rows both touch distinct banks.
-__device__ __forceinline__ int grm_index(int r, int chunk) {
-    return r * D + ((chunk ^ (r & 15)) << 3);
-}
-
-// Transposed copy: channel d holds its 32 rows in 8 units of 4 rows (8 bytes);
-// unit u is stored at position u ^ ((d >> 5) & 7).  Writers (64 lanes on 64
-// consecutive 8-channel groups, one row pair) hit distinct banks, and readers
-// (16 consecutive channels, one unit) still read 8 contiguous bytes.
-__device__ __forceinline__ int gt_index(int d, int r) {
-    return d * GT_LD + ((((r >> 2) ^ (d >> 5)) & 7) << 2) + (r & 3);
-}
-
-// Raw codes of one 8-channel segment of a row, in flight from global memory.
-struct RowSeg {
-    uint2 code;     // 8 FP8 codes, or 8 FP4 codes in .x
-    float scale;    // FP4 block scale as an fp32 power of two (unused for FP8 rows)
-};
-
+constexpr int CH = 32;                 // rows per chunk
+constexpr int ATT_THREADS = 512;       // 8 waves
+constexpr float LAZY_TAU = 8.0f;       // log2 headroom before the running max is moved
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <int HG>
-__global__ void __launch_bounds__(HG * 128, 2) k_attn(
+typedef __attribute__((ext_vector_type(4))) short s4;
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// Raw codes of one thread's share of a chunk (thread = row tid/16, unit tid%16).
+struct Stage {
+    uint4 c0, c1;   // 16-byte units u and u+16 of a window row; unit u of an FP4 entry
+    uint32_t sc;    // units 0..3 of an entry: scale bytes 4u..4u+3; unit 0 of a window row: its scale
+};
+
+// bf16 copy of a chunk, [row][512]: 16-byte unit u of row r sits at u ^ gb_swz(r).
+// Conflict-free for the transposing reads (16 rows x 32 bytes per read, two
+// half-waves of 8 rows) and for the dequantising writes (16 rows, one unit).
+__device__ __forceinline__ int gb_swz(int r) {
+    return (((r & 3) | ((r >> 1) & 4)) << 1) | ((r >> 2) & 1);
+}
+// P [head][32 rows] bf16, 64 bytes per head: unit u at u ^ ((h >> 2) & 3)
+__device__ __forceinline__ int pb_off(int h, int u) { return h * 64 + ((u ^ ((h >> 2) & 3)) << 4); }
+
+// Chunk k of a token: window chunks first (rows [32k, ..) of the window), then
+// compressed chunks.  Returns the valid row count; *win and *base describe it.
+__device__ __forceinline__ int chunk_rows(int k, int nwch, int nwin, int ncmp, bool* win,
+                                          int* base) {
+    if (k < nwch) {
+        *win = true;
+        *base = k * CH;
+        const int n = nwin - k * CH;
+        return n < CH ? n : CH;
+    }
+    *win = false;
+    *base = (k - nwch) * CH;
+    const int n = ncmp - (k - nwch) * CH;
+    return n < CH ? n : CH;
+}
+
+// One MFMA step of S for channel block M (128 channels): A = raw row codes, B = query hi and lo.
+// Scale registers carry the block exponent in their low byte (byte M of the packed words).
+template <int M, bool WIN>
+__device__ __forceinline__ f4 qk_step(const uint8_t* rrow, int r15, int g, uint32_t zsc,
+                                      const i8 (&qh)[4], const i8 (&ql)[4], uint32_t qsh,
+                                      uint32_t qsl, f4 acc, i8* keep) {
+    const int sh = (int)((qsh >> (8 * M)) & 0xFFu), sl = (int)((qsl >> (8 * M)) & 0xFFu);
+    i8 a;
+    if constexpr (WIN) {
+        const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * M + g) ^ r15));
+        const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * M + 4 + g) ^ r15));
+        a = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], acc, 0, 0, 0, 127, 0, sh);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], acc, 0, 0, 0, 127, 0, sl);
+    } else {
+        const int sa = (int)((zsc >> (8 * M)) & 0xFFu);
+        const uint4 x = *(const uint4*)(rrow + 16 * ((4 * M + g) ^ r15));
+        a = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], acc, 4, 0, 0, sa, 0, sh);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], acc, 4, 0, 0, sa, 0, sl);
+    }
+    if (keep) *keep = a;
+    return acc;
+}
+
+template <int HT>
+__global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     int B, int Tq, int H, const int32_t* __restrict__ q_pos0, const uint16_t* __restrict__ Q,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scale, int cap,
     const uint8_t* __restrict__ z_codes, const uint8_t* __restrict__ z_scales,
     int64_t entry_stride, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     const float* __restrict__ sink, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint16_t* __restrict__ O,
-    float* __restrict__ lse, int nsplit, int rows_per_split, float* __restrict__ part_O,
+    float* __restrict__ lse, int nsplit, float* __restrict__ part_O,
     float* __restrict__ part_ml) {
-    constexpr int NT = HG * 128;                  // threads (2 waves per head group)
-    constexpr int NWAVE = NT / 64;
-    constexpr int RPW = ATT_ROWS / NWAVE;         // rows gathered per wave per chunk
-    __shared__ __attribute__((aligned(16))) uint16_t Grm[ATT_ROWS * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Gt[D * GT_LD];
-    __shared__ float Sx[HG * 2 * 4 * 64];
-    __shared__ float rsc[ATT_ROWS];
+    __shared__ __attribute__((aligned(16))) uint8_t rawc[2][CH * 512];
+    __shared__ __attribute__((aligned(16))) uint32_t zsc[2][CH][4];
+    __shared__ float rscl[2][CH];
+    __shared__ __attribute__((aligned(16))) uint16_t Gb[2][CH * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Pb[64 * CH];
+    __shared__ float mxb[2][64];
+    __shared__ float cor[64];
+    __shared__ float mfin[64], lfin[2][64];
     __shared__ int32_t sidx[TOPK];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, grp = lane >> 4;
-    const int hg = wave >> 1, half = wave & 1;
-    const int row = blockIdx.x;                // b * Tq + t
+    const int n16 = lane & 15, g = lane >> 4;
+    const int g4 = wave >> 1, half = wave & 1;     // QK role: head group, row half
+    const bool qk = g4 < HT;
+    const int row = blockIdx.x;                    // b * Tq + t
     const int split = blockIdx.y;
     const int b = row / Tq, t = row - b * Tq;
     int64_t p = (int64_t)q_pos0[b] + t;
     if (p < 0) p = 0;
     const int64_t w0 = p - (WINDOW - 1) > 0 ? p - (WINDOW - 1) : 0;
     const int nwin = (int)(p - w0 + 1);
-    const int slot0 = (int)(w0 % cap);         // ring slot of the first window row
-    int c = cnt[row];
-    c = c < 0 ? 0 : (c > TOPK ? TOPK : c);
-    const int nr = nwin + c;
-    const int r_begin = split * rows_per_split;
-    const int r_end = (r_begin + rows_per_split < nr) ? r_begin + rows_per_split : nr;
+    const int slot0 = (int)(w0 % cap);
+    int ncmp = cnt[row];
+    ncmp = ncmp < 0 ? 0 : (ncmp > TOPK ? TOPK : ncmp);
+    const int nwch = (nwin + CH - 1) / CH;
+    const int nch = nwch + (ncmp + CH - 1) / CH;
+    const int cps = (nch + nsplit - 1) / nsplit;
+    const int k_begin = split * cps;
+    const int k_end = (k_begin + cps < nch) ? k_begin + cps : nch;
     const uint8_t* wrow0 = w_codes + (int64_t)b * cap * D;
     const float* wsc = w_scale + (int64_t)b * cap;
     const uint8_t* zc0 = z_codes + (int64_t)b * entry_stride * 256;
@@ -94,197 +146,325 @@ __global__ void __launch_bounds__(HG * 128, 2) k_attn(
     {   // the row's selected entries, clamped into the cache
         const int32_t* irow = idx + (int64_t)row * TOPK;
         const int emax = entry_stride < 0x7FFFFFFF ? (int)entry_stride - 1 : 0x7FFFFFFE;
-        for (int i = tid; i < c; i += NT) {
+        for (int i = tid; i < ncmp; i += ATT_THREADS) {
             const int e = irow[i];
             sidx[i] = e < 0 ? 0 : (e > emax ? emax : e);
         }
     }
 
-    const int h = hg * 16 + col;   // this lane's head (column of S^T and O^T)
-    bf8 Qb[16];                    // Q^T operand: lane holds Q[h][32kk + 8grp .. +7]
-    {
-        const uint16_t* qrow = Q + (((int64_t)b * H + h) * Tq + t) * D + 8 * grp;
+    // ---- query of this wave's 16 heads as two E4M3 terms (QK waves) ---------
+    // Lane (head 16*g4 + n16, group g) holds, for channel block M, channels
+    // 128M + 16g..+15 and 128M + 64 + 16g..+15 (the FP8 operand layout).
+    i8 qh[4], ql[4];
+    uint32_t qsh = 0x7F7F7F7Fu, qsl = 0x7F7F7F7Fu;
+    if (qk) {
+        const uint16_t* qrow = Q + (((int64_t)b * H + 16 * g4 + n16) * Tq + t) * D;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) Qb[kk] = *(const bf8*)(qrow + 32 * kk);
-    }
-    f4 oacc[16];                   // O^T for channels 256*half + 16*dt + 4*grp + i
+        for (int m = 0; m < 4; ++m) {
+            float x[32];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;       // running max (log2 units) and sum
-    const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
-    __syncthreads();                              // sidx ready
-
-    // Wave `wave` gathers rows wave + NWAVE*k of each chunk; lane owns channels 8*lane..+7.
-    auto fetch = [&](int rb, RowSeg (&seg)[RPW], float (&wsr)[RPW]) {
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint16_t* src = qrow + 128 * m + 64 * s2 + 16 * g;
+                const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 8);
+                const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-        for (int k = 0; k < RPW; ++k) {
-            const int gr = rb + wave + NWAVE * k;          // wave-uniform
-            seg[k].code = make_uint2(0, 0);
-            seg[k].scale = 0.0f;
-            wsr[k] = 0.0f;
-            if (gr < r_end) {
-                if (gr < nwin) {
-                    int slot = slot0 + gr;
-                    if (slot >= cap) slot -= cap;
-                    seg[k].code = *(const uint2*)(wrow0 + (int64_t)slot * D + 8 * lane);
-                    wsr[k] = wsc[slot];
-                } else {
-                    const int e = __builtin_amdgcn_readfirstlane(sidx[gr - nwin]);
-                    seg[k].code.x = *(const uint32_t*)(zc0 + (int64_t)e * 256 + 4 * lane);
-                    seg[k].scale = e8m0_to_f32(zs0[(int64_t)e * 16 + (lane >> 2)]);
-                    wsr[k] = 1.0f;
+                for (int j = 0; j < 8; ++j) {
+                    x[16 * s2 + 2 * j] = __uint_as_float(w8[j] << 16);
+                    x[16 * s2 + 2 * j + 1] = __uint_as_float(w8[j] & 0xFFFF0000u);
                 }
             }
+            // one exponent per (head, 128 channels): an FP8 operand's scale bytes are
+            // attached to K blocks, not to the lane holding the bytes, so all four
+            // lane groups of a head use the same scale
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            int sh = amax > 0.0f ? floor_log2(amax) - 7 : 0;     // |x| / 2^sh < 256
+            sh = sh < -120 ? -120 : sh;
+            const float inv = __uint_as_float((uint32_t)(127 - sh) << 23);
+            int hw[8], lw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float a0 = x[4 * j] * inv, a1 = x[4 * j + 1] * inv;
+                const float a2 = x[4 * j + 2] * inv, a3 = x[4 * j + 3] * inv;
+                int hcode = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+                hcode = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, hcode, true);
+                const f2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hcode, false);
+                const f2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hcode, true);
+                int lcode = __builtin_amdgcn_cvt_pk_fp8_f32((a0 - h01[0]) * 16.0f,
+                                                            (a1 - h01[1]) * 16.0f, 0, false);
+                lcode = __builtin_amdgcn_cvt_pk_fp8_f32((a2 - h23[0]) * 16.0f,
+                                                        (a3 - h23[1]) * 16.0f, lcode, true);
+                hw[j] = hcode;
+                lw[j] = lcode;
+            }
+            qh[m] = i8{hw[0], hw[1], hw[2], hw[3], hw[4], hw[5], hw[6], hw[7]};
+            ql[m] = i8{lw[0], lw[1], lw[2], lw[3], lw[4], lw[5], lw[6], lw[7]};
+            const uint32_t bh = (uint32_t)(sh + 127), bl = (uint32_t)(sh - 4 + 127);
+            qsh = (qsh & ~(0xFFu << (8 * m))) | (bh << (8 * m));
+            qsl = (qsl & ~(0xFFu << (8 * m))) | (bl << (8 * m));
+        }
+    }
+    __syncthreads();   // sidx ready
+
+    // ---- staging: thread -> (row tid/16, unit tid%16) ------------------------
+    const int st_row = tid >> 4, st_u = tid & 15;
+    auto stage_load = [&](int k, Stage& s) {
+        s.c0 = make_uint4(0, 0, 0, 0);
+        s.c1 = make_uint4(0, 0, 0, 0);
+        s.sc = 0;
+        if (k >= k_end) return;
+        bool win;
+        int base;
+        const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
+        if (st_row >= nv) return;
+        if (win) {
+            int slot = slot0 + base + st_row;
+            if (slot >= cap) slot -= cap;
+            const uint8_t* src = wrow0 + (int64_t)slot * D + 16 * st_u;
+            s.c0 = *(const uint4*)src;
+            s.c1 = *(const uint4*)(src + 256);
+            if (st_u == 0) s.sc = __float_as_uint(wsc[slot]);
+        } else {
+            const int e = sidx[base + st_row];
+            s.c0 = *(const uint4*)(zc0 + (int64_t)e * 256 + 16 * st_u);
+            if (st_u < 4) s.sc = *(const uint32_t*)(zs0 + (int64_t)e * 16 + 4 * st_u);
+        }
+    };
+    auto stage_store = [&](int k, const Stage& s) {
+        if (k >= k_end) return;
+        bool win;
+        int base;
+        chunk_rows(k, nwch, nwin, ncmp, &win, &base);
+        const int buf = k & 1;
+        uint8_t* rr = &rawc[buf][st_row * 512];
+        const int x = st_row & 15;
+        *(uint4*)(rr + 16 * (st_u ^ x)) = s.c0;
+        if (win) {
+            *(uint4*)(rr + 16 * ((st_u + 16) ^ x)) = s.c1;
+            if (st_u == 0) rscl[buf][st_row] = __uint_as_float(s.sc);
+        } else if (st_u < 4) {
+            zsc[buf][st_row][st_u] = s.sc;   // the entry's 16 scale bytes, in order
         }
     };
 
-    RowSeg seg[RPW];
-    float wsr[RPW];
-    if (r_begin < r_end) fetch(r_begin, seg, wsr);
-
-    for (int rb = r_begin; rb < r_end; rb += ATT_ROWS) {
-        __syncthreads();   // previous chunk's readers are done with Grm, Gt, rsc, Sx
-        // ---- dequantise this wave's rows into both LDS layouts -------------
+    f4 oacc[4][HT];                       // O^T tiles: [channel tile][head tile]
 #pragma unroll
-        for (int k = 0; k < RPW; ++k) {
-            const int r = wave + NWAVE * k;
-            const int gr = rb + r;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (gr < r_end) {
-                if (gr < nwin) {
-                    v.x = fp8x2_to_bf16x2<false>(seg[k].code.x);
-                    v.y = fp8x2_to_bf16x2<true>(seg[k].code.x);
-                    v.z = fp8x2_to_bf16x2<false>(seg[k].code.y);
-                    v.w = fp8x2_to_bf16x2<true>(seg[k].code.y);
-                } else {
-                    const uint32_t w = seg[k].code.x;
-                    const float sc = seg[k].scale;
-                    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
-                    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
-                    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
-                    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
-                }
-            }
-            *(uint4*)(Grm + grm_index(r, lane)) = v;
-            // transposed copy: channel 8*lane + i, row r (16-bit stores)
-            uint16_t* gt = Gt + gt_index(8 * lane, r);
-            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) gt[i * GT_LD] = (uint16_t)(vw[i >> 1] >> ((i & 1) * 16));
-            if (lane == 0) rsc[r] = wsr[k];
-        }
-        __syncthreads();
-        // ---- next chunk's codes are loaded while this one is computed ------
-        if (rb + ATT_ROWS < r_end) fetch(rb + ATT_ROWS, seg, wsr);
+        for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_used = -INFINITY, l_part = 0.0f;      // QK waves: head 16*g4 + n16
+    const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
 
-        // ---- S^T for this wave's 16 rows: rows 16*half + 4*grp + i ----------
+    Stage SA;
+    stage_load(k_begin, SA);
+    stage_store(k_begin, SA);
+    stage_load(k_begin + 1, SA);
+    __syncthreads();
+
+    // One chunk.  `nxt` holds the raw codes of chunk k+1 (stored here) and is
+    // then refilled with chunk k+2.
+    auto chunk = [&](int k, Stage& nxt) {
+        bool win;
+        int base;
+        const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
+        const int buf = k & 1;
+        // ---- QK + dequantisation of channel block g4 of rows 16*half.. --------
+        const int r = 16 * half + n16;
+        const int r15 = r & 15;
+        const uint8_t* rrow = &rawc[buf][r * 512];
+        uint16_t* grow = &Gb[buf][r * D];
+        const int gsw = gb_swz(r);
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-        {
-            const int r = half * 16 + col;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const bf8 a = *(const bf8*)(Grm + grm_index(r, 4 * kk + grp));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[kk], acc, 0, 0, 0);
+        i8 mine;
+        if (win) {
+            if (qk) {
+                acc = qk_step<0, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 0 ? &mine : nullptr);
+                acc = qk_step<1, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 1 ? &mine : nullptr);
+                acc = qk_step<2, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 2 ? &mine : nullptr);
+                acc = qk_step<3, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 3 ? &mine : nullptr);
+            } else {
+                const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * g4 + g) ^ r15));
+                const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * g4 + 4 + g) ^ r15));
+                mine = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
             }
-        }
-        float* sx = Sx + ((hg * 2 + half) * 4) * 64;
+            // bf16 of channels 128*g4 + 16g..+15 (units 16g4 + 2g, +1) and +64 (units +8)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = half * 16 + 4 * grp + i;
-            sx[i * 64 + lane] = (rb + r < r_end) ? acc[i] * (rsc[r] * lscale) : -INFINITY;
-        }
-        __syncthreads();
-        // logits (log2 units) of all 32 rows, identical in both waves of the pair
-        float pr[8];
-        {
-            const float* s0 = Sx + ((hg * 2 + 0) * 4) * 64;
-            const float* s1 = Sx + ((hg * 2 + 1) * 4) * 64;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pr[i] = s0[i * 64 + lane];
-                pr[4 + i] = s1[i * 64 + lane];
-            }
-        }
-        float mx = fmaxf(fmaxf(fmaxf(pr[0], pr[1]), fmaxf(pr[2], pr[3])),
-                         fmaxf(fmaxf(pr[4], pr[5]), fmaxf(pr[6], pr[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        float corr = 1.0f, lsum = 0.0f;
-        if (m_new != -INFINITY) {
-            corr = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                pr[k] = __builtin_amdgcn_exp2f(pr[k] - m_new);
-                lsum += pr[k];
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint32_t w0 = (uint32_t)mine[4 * s2], w1 = (uint32_t)mine[4 * s2 + 1];
+                const uint32_t w2 = (uint32_t)mine[4 * s2 + 2], w3 = (uint32_t)mine[4 * s2 + 3];
+                const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                                            fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+                const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(w2), fp8x2_to_bf16x2<true>(w2),
+                                            fp8x2_to_bf16x2<false>(w3), fp8x2_to_bf16x2<true>(w3));
+                const int u = 16 * g4 + 8 * s2 + 2 * g;
+                *(uint4*)(grow + 8 * (u ^ gsw)) = lo;
+                *(uint4*)(grow + 8 * ((u + 1) ^ gsw)) = hi;
             }
         } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) pr[k] = 0.0f;
-        }
-        lsum += __shfl_xor(lsum, 16, 64);
-        lsum += __shfl_xor(lsum, 32, 64);
-        l_run = l_run * corr + lsum;
-        m_run = m_new;
-        if (__any(corr != 1.0f)) {
-#pragma unroll
-            for (int dt = 0; dt < 16; ++dt) oacc[dt] *= corr;
-        }
-        // P^T operand: K slot 8grp+j <-> row (j<4 ? 4grp+j : 16+4grp+j-4); window scale folded in
-        bf8 pb;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int r = (k < 4) ? 4 * grp + k : 16 + 4 * grp + (k - 4);
-            pb[k] = (__bf16)(pr[k] * rsc[r]);
-        }
-        // ---- O^T[d][h] += G^T[d][r] P^T[r][h] for this wave's 256 channels ---
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-            const int d = (half * 16 + dt) * 16 + col;
-            const uint2 lo = *(const uint2*)(Gt + gt_index(d, 4 * grp));
-            const uint2 hi = *(const uint2*)(Gt + gt_index(d, 16 + 4 * grp));
-            const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, av), pb,
-                                                             oacc[dt], 0, 0, 0);
-        }
-    }
-
-    if (nsplit == 1) {
-        const float sh = sink[h] * LOG2E;
-        const float M = fmaxf(m_run, sh);
-        const float em = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-        const float den = l_run * em + __builtin_amdgcn_exp2f(sh - M);
-        const float f = em / den;
-        const int64_t prow = p < rope_rows ? p : rope_rows - 1;
-        uint16_t* orow = O + (((int64_t)b * H + h) * Tq + t) * D;
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-            float o[4] = {oacc[dt][0] * f, oacc[dt][1] * f, oacc[dt][2] * f, oacc[dt][3] * f};
-            const int d0 = (half * 16 + dt) * 16 + 4 * grp;
-            if (d0 >= ROPE_LO) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int pi = (d0 - ROPE_LO) / 2 + q;
-                    const float co = rcos[prow * PAIRS + pi], si = rsin[prow * PAIRS + pi];
-                    const float x0 = o[2 * q], x1 = o[2 * q + 1];
-                    o[2 * q] = x0 * co + x1 * si;
-                    o[2 * q + 1] = x1 * co - x0 * si;
-                }
+            // the row's scale bytes regrouped for lane group g: byte m = block 4m + g
+            const uint4 z4 = *(const uint4*)&zsc[buf][r][0];
+            const uint32_t sel = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
+            const uint32_t zs = __builtin_amdgcn_perm(__builtin_amdgcn_perm(z4.w, z4.z, sel),
+                                                      __builtin_amdgcn_perm(z4.y, z4.x, sel),
+                                                      0x05040100u);
+            if (qk) {
+                acc = qk_step<0, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 0 ? &mine : nullptr);
+                acc = qk_step<1, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 1 ? &mine : nullptr);
+                acc = qk_step<2, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 2 ? &mine : nullptr);
+                acc = qk_step<3, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 3 ? &mine : nullptr);
+            } else {
+                const uint4 x = *(const uint4*)(rrow + 16 * ((4 * g4 + g) ^ r15));
+                mine = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
             }
-            const uint32_t w0v = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-            const uint32_t w1v = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
-            *(uint2*)(orow + d0) = make_uint2(w0v, w1v);
-        }
-        if (lse && half == 0 && grp == 0)
-            lse[((int64_t)b * H + h) * Tq + t] = (M + log2f(den)) * 0.6931471805599453f;
-    } else {
-        const int64_t pbase = ((int64_t)row * nsplit + split) * H + h;
-        float* po = part_O + pbase * D;
+            // bf16 of channels 128*g4 + 32g..+31 (units 16g4 + 4g .. +3)
+            const float sc = e8m0_to_f32((zs >> (8 * g4)) & 0xFFu);
 #pragma unroll
-        for (int dt = 0; dt < 16; ++dt) *(f4*)(po + (half * 16 + dt) * 16 + 4 * grp) = oacc[dt];
-        if (half == 0 && grp == 0) {
-            part_ml[pbase * 2] = m_run;          // log2 units
-            part_ml[pbase * 2 + 1] = l_run;
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const uint32_t w = (uint32_t)mine[k2];
+                const uint4 v = make_uint4(
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+                *(uint4*)(grow + 8 * ((16 * g4 + 4 * g + k2) ^ gsw)) = v;
+            }
+        }
+        // ---- logits of rows 16*half + 4g + i, head 16*g4 + n16 ---------------
+        float s[4], lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * half + 4 * g + i;
+            float v = acc[i] * (win ? lscale * rscl[buf][rr] : lscale);
+            v = rr < nv ? v : -INFINITY;
+            s[i] = v;
+            lm = fmaxf(lm, v);
+        }
+        lm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
+        if (qk && g == 0) mxb[half][16 * g4 + n16] = lm;
+        __syncthreads();   // A: S maxima, bf16 rows of chunk k written; raw[k+1 & 1] free
+
+        if (qk) {
+            const float cm = fmaxf(lm, mxb[half ^ 1][16 * g4 + n16]);
+            float corr = 1.0f;
+            if (cm > m_used + LAZY_TAU) {
+                corr = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - cm);
+                m_used = cm;
+            }
+            float ps = 0.0f, pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * half + 4 * g + i;
+                const float e = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_used);
+                ps += e;
+                pv[i] = win ? e * rscl[buf][rr] : e;
+            }
+            ps += __shfl_xor(ps, 16, 64);
+            ps += __shfl_xor(ps, 32, 64);
+            l_part = l_part * corr + ps;
+            const int h = 16 * g4 + n16;
+            const uint32_t p01 = (uint32_t)f2bf(pv[0]) | ((uint32_t)f2bf(pv[1]) << 16);
+            const uint32_t p23 = (uint32_t)f2bf(pv[2]) | ((uint32_t)f2bf(pv[3]) << 16);
+            const int rr0 = 16 * half + 4 * g;
+            *(uint2*)((uint8_t*)Pb + pb_off(h, rr0 >> 3) + 2 * (rr0 & 7)) = make_uint2(p01, p23);
+            if (half == 0 && g == 0) cor[h] = corr;
+        }
+        stage_store(k + 1, nxt);
+        stage_load(k + 2, nxt);
+        __syncthreads();   // B: P, corrections and raw[k+1] visible
+
+        // ---- PV: O^T[64w + 16ct + .., heads] += G^T P^T over the 32 rows -------
+        float cr[HT];
+        bool resc = false;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            cr[ht] = cor[16 * ht + n16];
+            resc |= cr[ht] != 1.0f;
+        }
+        if (__any(resc)) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] *= cr[ht];
+        }
+        bf8 pb[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+            pb[ht] = *(const bf8*)((const uint8_t*)Pb + pb_off(16 * ht + n16, g));
+        const int sr = n16 >> 2, sq = n16 & 3;        // transposing-read source: row, 4-channel group
+        const int ra = 8 * g + sr, rb2 = ra + 4;
+        const uint16_t* gba = &Gb[buf][ra * D];
+        const uint16_t* gbb = &Gb[buf][rb2 * D];
+        const int swa = gb_swz(ra), swb = gb_swz(rb2);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int c0 = 64 * wave + 16 * ct;
+            const int u = (c0 >> 3) + (sq >> 1);
+            const int off = 4 * (sq & 1);
+            const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gba + 8 * (u ^ swa) + off));
+            const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gbb + 8 * (u ^ swb) + off));
+            const bf8 a = __builtin_bit_cast(bf8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+                oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht], oacc[ct][ht], 0, 0, 0);
+        }
+    };
+
+    for (int k = k_begin; k < k_end; ++k) chunk(k, SA);
+
+    // ---- final per-head state ----------------------------------------------
+    if (qk && g == 0) {
+        const int h = 16 * g4 + n16;
+        if (half == 0) mfin[h] = m_used;
+        lfin[half][h] = l_part;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = 16 * ht + n16;
+        const float m = mfin[h], l = lfin[0][h] + lfin[1][h];
+        if (nsplit == 1) {
+            const float shv = sink[h] * LOG2E;
+            const float M = fmaxf(m, shv);
+            const float em = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            const float den = l * em + __builtin_amdgcn_exp2f(shv - M);
+            const float f = em / den;
+            const int64_t prow = p < rope_rows ? p : rope_rows - 1;
+            uint16_t* orow = O + (((int64_t)b * H + h) * Tq + t) * D;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int d0 = 64 * wave + 16 * ct + 4 * g;
+                float o[4] = {oacc[ct][ht][0] * f, oacc[ct][ht][1] * f, oacc[ct][ht][2] * f,
+                              oacc[ct][ht][3] * f};
+                if (d0 >= ROPE_LO) {
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const int pi = (d0 - ROPE_LO) / 2 + q2;
+                        const float co = rcos[prow * PAIRS + pi], si = rsin[prow * PAIRS + pi];
+                        const float x0 = o[2 * q2], x1 = o[2 * q2 + 1];
+                        o[2 * q2] = x0 * co + x1 * si;
+                        o[2 * q2 + 1] = x1 * co - x0 * si;
+                    }
+                }
+                const uint32_t w0v = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+                const uint32_t w1v = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+                *(uint2*)(orow + d0) = make_uint2(w0v, w1v);
+            }
+            if (lse && wave == 0 && g == 0)
+                lse[((int64_t)b * H + h) * Tq + t] = (M + log2f(den)) * 0.6931471805599453f;
+        } else {
+            const int64_t pbase = ((int64_t)row * nsplit + split) * H + h;
+            float* po = part_O + pbase * D;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) *(f4*)(po + 64 * wave + 16 * ct + 4 * g) = oacc[ct][ht];
+            if (wave == 0 && g == 0) {
+                part_ml[pbase * 2] = m;          // log2 units
+                part_ml[pbase * 2 + 1] = l;
+            }
         }
     }
 }
@@ -343,25 +523,17 @@ __global__ void __launch_bounds__(256) k_attn_combine(
     if (lse && lane == 0) lse[((int64_t)b * H + h) * Tq + t] = (M + log2f(den)) * 0.6931471805599453f;
 }
 
-template __global__ void k_attn<1>(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
-                                   const float*, int, const uint8_t*, const uint8_t*, int64_t,
-                                   const int32_t*, const int32_t*, const float*, const float*,
-                                   const float*, int64_t, uint16_t*, float*, int, int, float*,
-                                   float*);
-template __global__ void k_attn<2>(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
-                                   const float*, int, const uint8_t*, const uint8_t*, int64_t,
-                                   const int32_t*, const int32_t*, const float*, const float*,
-                                   const float*, int64_t, uint16_t*, float*, int, int, float*,
-                                   float*);
-template __global__ void k_attn<3>(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
-                                   const float*, int, const uint8_t*, const uint8_t*, int64_t,
-                                   const int32_t*, const int32_t*, const float*, const float*,
-                                   const float*, int64_t, uint16_t*, float*, int, int, float*,
-                                   float*);
-template __global__ void k_attn<4>(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
-                                   const float*, int, const uint8_t*, const uint8_t*, int64_t,
-                                   const int32_t*, const int32_t*, const float*, const float*,
-                                   const float*, int64_t, uint16_t*, float*, int, int, float*,
-                                   float*);
+#define CSA2_ATTN_INST(HTV)                                                                    \
+    template __global__ void k_attn<HTV>(int, int, int, const int32_t*, const uint16_t*,       \
+                                         const uint8_t*, const float*, int, const uint8_t*,    \
+                                         const uint8_t*, int64_t, const int32_t*,              \
+                                         const int32_t*, const float*, const float*,           \
+                                         const float*, int64_t, uint16_t*, float*, int, float*, \
+                                         float*);
+CSA2_ATTN_INST(1)
+CSA2_ATTN_INST(2)
+CSA2_ATTN_INST(3)
+CSA2_ATTN_INST(4)
+#undef CSA2_ATTN_INST
 
 }  // namespace csa2
