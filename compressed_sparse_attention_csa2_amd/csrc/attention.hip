@@ -41,12 +41,46 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(4))) short s4;
 typedef __attribute__((address_space(3))) s4 lds_s4;
+typedef __attribute__((ext_vector_type(2))) short s2v;
 
-// Raw codes of one thread's share of a chunk (thread = row tid/16, unit tid%16).
-struct Stage {
-    uint4 c0, c1;   // 16-byte units u and u+16 of a window row; unit u of an FP4 entry
-    uint32_t sc;    // units 0..3 of an entry: scale bytes 4u..4u+3; unit 0 of a window row: its scale
-};
+constexpr int NRAW = 3;                // raw staging buffers (chunks in flight)
+
+// Direct-to-LDS copies: every active lane copies 16 (4) bytes from its own
+// global address to lds + 16 (4) * lane; lds is wave-uniform and goes to M0.
+// The kernel uses M0 for nothing else.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds) : "memory");
+}
+// Workgroup barrier after this wave's LDS operations and all but its N most
+// recent direct-to-LDS copies have completed.
+template <int N>
+__device__ __forceinline__ void barrier_vm() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+// max / sum over the four lanes l, l^16, l^32, l^48 (the 16-lane rows)
+__device__ __forceinline__ float rows_max(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 
 // bf16 copy of a chunk, [row][512]: 16-byte unit u of row r sits at u ^ gb_swz(r).
 // Conflict-free for the transposing reads (16 rows x 32 bytes per read, two
@@ -73,29 +107,29 @@ __device__ __forceinline__ int chunk_rows(int k, int nwch, int nwin, int ncmp, b
     return n < CH ? n : CH;
 }
 
-// One MFMA step of S for channel block M (128 channels): A = raw row codes, B = query hi and lo.
-// Scale registers carry the block exponent in their low byte (byte M of the packed words).
+// One MFMA step of S for channel block M (128 channels): A = raw row codes, B =
+// query hi (into ah) and lo (into al).  Scale registers carry the block
+// exponent in their low byte (byte M of the packed words).
 template <int M, bool WIN>
-__device__ __forceinline__ f4 qk_step(const uint8_t* rrow, int r15, int g, uint32_t zsc,
-                                      const i8 (&qh)[4], const i8 (&ql)[4], uint32_t qsh,
-                                      uint32_t qsl, f4 acc, i8* keep) {
+__device__ __forceinline__ void qk_step(const uint8_t* rrow, int r15, int g, uint32_t zsc,
+                                        const i8 (&qh)[4], const i8 (&ql)[4], uint32_t qsh,
+                                        uint32_t qsl, f4& ah, f4& al, i8* keep) {
     const int sh = (int)((qsh >> (8 * M)) & 0xFFu), sl = (int)((qsl >> (8 * M)) & 0xFFu);
     i8 a;
     if constexpr (WIN) {
         const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * M + g) ^ r15));
         const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * M + 4 + g) ^ r15));
         a = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], acc, 0, 0, 0, 127, 0, sh);
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], acc, 0, 0, 0, 127, 0, sl);
+        ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], ah, 0, 0, 0, 127, 0, sh);
+        al = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], al, 0, 0, 0, 127, 0, sl);
     } else {
         const int sa = (int)((zsc >> (8 * M)) & 0xFFu);
         const uint4 x = *(const uint4*)(rrow + 16 * ((4 * M + g) ^ r15));
         a = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], acc, 4, 0, 0, sa, 0, sh);
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], acc, 4, 0, 0, sa, 0, sl);
+        ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], ah, 4, 0, 0, sa, 0, sh);
+        al = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], al, 4, 0, 0, sa, 0, sl);
     }
     if (keep) *keep = a;
-    return acc;
 }
 
 template <int HT>
@@ -108,9 +142,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const float* __restrict__ rsin, int64_t rope_rows, uint16_t* __restrict__ O,
     float* __restrict__ lse, int nsplit, float* __restrict__ part_O,
     float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) uint8_t rawc[2][CH * 512];
-    __shared__ __attribute__((aligned(16))) uint32_t zsc[2][CH][4];
-    __shared__ float rscl[2][CH];
+    __shared__ __attribute__((aligned(16))) uint8_t rawc[NRAW][CH * 512];
+    __shared__ __attribute__((aligned(16))) uint32_t zsc[NRAW][CH][4];
+    __shared__ __attribute__((aligned(16))) float rscl[NRAW][CH];
     __shared__ __attribute__((aligned(16))) uint16_t Gb[2][CH * D];
     __shared__ __attribute__((aligned(16))) uint16_t Pb[64 * CH];
     __shared__ float mxb[2][64];
@@ -154,99 +188,112 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
 
     // ---- query of this wave's 16 heads as two E4M3 terms (QK waves) ---------
     // Lane (head 16*g4 + n16, group g) holds, for channel block M, channels
-    // 128M + 16g..+15 and 128M + 64 + 16g..+15 (the FP8 operand layout).
+    // 128M + 16g..+15 and 128M + 64 + 16g..+15 (the FP8 operand layout).  One
+    // exponent s per (head, 128 channels): an FP8 operand's scale bytes attach
+    // to K blocks, not to the lane holding the bytes, so the four lane groups of
+    // a head share it.  hi = E4M3(q / 2^s) (|q| / 2^s < 256), lo = E4M3((q - hi
+    // 2^s) / 2^(s-4)); hi + lo reproduces the bf16 query up to the block's
+    // smallest elements.  Wave (g4, half) converts blocks 2 half and 2 half + 1
+    // and swaps them with its partner through LDS (the bf16 row buffers and P,
+    // unused until the first chunk).
     i8 qh[4], ql[4];
     uint32_t qsh = 0x7F7F7F7Fu, qsl = 0x7F7F7F7Fu;
+    uint4* qx = (uint4*)&Gb[0][0];                 // [g4][m][4 quads][64 lanes]
+    uint32_t* qxs = (uint32_t*)&Pb[0];               // [g4][m][64 lanes] exponents (4 KB)
     if (qk) {
         const uint16_t* qrow = Q + (((int64_t)b * H + 16 * g4 + n16) * Tq + t) * D;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float x[32];
+        for (int mm = 0; mm < 2; ++mm) {
+            const int m = 2 * half + mm;
+            uint32_t w[16];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const uint16_t* src = qrow + 128 * m + 64 * s2 + 16 * g;
                 const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 8);
-                const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    x[16 * s2 + 2 * j] = __uint_as_float(w8[j] << 16);
-                    x[16 * s2 + 2 * j + 1] = __uint_as_float(w8[j] & 0xFFFF0000u);
-                }
+                w[8 * s2 + 0] = u0.x; w[8 * s2 + 1] = u0.y; w[8 * s2 + 2] = u0.z; w[8 * s2 + 3] = u0.w;
+                w[8 * s2 + 4] = u1.x; w[8 * s2 + 5] = u1.y; w[8 * s2 + 6] = u1.z; w[8 * s2 + 7] = u1.w;
             }
-            // one exponent per (head, 128 channels): an FP8 operand's scale bytes are
-            // attached to K blocks, not to the lane holding the bytes, so all four
-            // lane groups of a head use the same scale
-            float amax = 0.0f;
+            uint32_t mx = 0;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-            int sh = amax > 0.0f ? floor_log2(amax) - 7 : 0;     // |x| / 2^sh < 256
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t a = w[j] & 0x7FFF7FFFu;
+                mx = max(mx, max(a & 0xFFFFu, a >> 16));
+            }
+            const float amax = rows_max(__uint_as_float(mx << 16));
+            int sh = amax > 0.0f ? floor_log2(amax) - 7 : 0;
             sh = sh < -120 ? -120 : sh;
-            const float inv = __uint_as_float((uint32_t)(127 - sh) << 23);
-            int hw[8], lw[8];
+            const float sc_hi = __uint_as_float((uint32_t)(sh + 127) << 23);
+            const float sc_lo = __uint_as_float((uint32_t)(sh - 4 + 127) << 23);
+            uint32_t hw[8], lw[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float a0 = x[4 * j] * inv, a1 = x[4 * j + 1] * inv;
-                const float a2 = x[4 * j + 2] * inv, a3 = x[4 * j + 3] * inv;
-                int hcode = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-                hcode = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, hcode, true);
-                const f2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hcode, false);
-                const f2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hcode, true);
-                int lcode = __builtin_amdgcn_cvt_pk_fp8_f32((a0 - h01[0]) * 16.0f,
-                                                            (a1 - h01[1]) * 16.0f, 0, false);
-                lcode = __builtin_amdgcn_cvt_pk_fp8_f32((a2 - h23[0]) * 16.0f,
-                                                        (a3 - h23[1]) * 16.0f, lcode, true);
-                hw[j] = hcode;
-                lw[j] = lcode;
+                s2v hc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s2v{0, 0}, __builtin_bit_cast(bf2, w[2 * j]), sc_hi, false);
+                hc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hc, __builtin_bit_cast(bf2, w[2 * j + 1]), sc_hi, true);
+                const uint32_t hcu = __builtin_bit_cast(uint32_t, hc);
+                const f2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hcu, sc_hi, false);
+                const f2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hcu, sc_hi, true);
+                const float x0 = __uint_as_float(w[2 * j] << 16), x1 = __uint_as_float(w[2 * j] & 0xFFFF0000u);
+                const float x2 = __uint_as_float(w[2 * j + 1] << 16), x3 = __uint_as_float(w[2 * j + 1] & 0xFFFF0000u);
+                s2v lc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s2v{0, 0}, x0 - h01[0], x1 - h01[1], sc_lo, false);
+                lc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lc, x2 - h23[0], x3 - h23[1], sc_lo, true);
+                hw[j] = hcu;
+                lw[j] = __builtin_bit_cast(uint32_t, lc);
             }
-            qh[m] = i8{hw[0], hw[1], hw[2], hw[3], hw[4], hw[5], hw[6], hw[7]};
-            ql[m] = i8{lw[0], lw[1], lw[2], lw[3], lw[4], lw[5], lw[6], lw[7]};
+            uint4* dst = qx + ((g4 * 4 + m) * 4) * 64 + lane;
+            dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            dst[64] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+            dst[128] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            dst[192] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+            qxs[(g4 * 4 + m) * 64 + lane] = (uint32_t)sh;
+        }
+    }
+    __syncthreads();   // sidx ready, both halves of the query converted
+    if (qk) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint4* srcq = qx + ((g4 * 4 + m) * 4) * 64 + lane;
+            const uint4 a0 = srcq[0], a1 = srcq[64], c0 = srcq[128], c1 = srcq[192];
+            qh[m] = i8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            ql[m] = i8{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+            const int sh = (int)qxs[(g4 * 4 + m) * 64 + lane];
             const uint32_t bh = (uint32_t)(sh + 127), bl = (uint32_t)(sh - 4 + 127);
             qsh = (qsh & ~(0xFFu << (8 * m))) | (bh << (8 * m));
             qsl = (qsl & ~(0xFFu << (8 * m))) | (bl << (8 * m));
         }
     }
-    __syncthreads();   // sidx ready
 
-    // ---- staging: thread -> (row tid/16, unit tid%16) ------------------------
-    const int st_row = tid >> 4, st_u = tid & 15;
-    auto stage_load = [&](int k, Stage& s) {
-        s.c0 = make_uint4(0, 0, 0, 0);
-        s.c1 = make_uint4(0, 0, 0, 0);
-        s.sc = 0;
+    // ---- staging: direct-to-LDS copies of chunk k into raw buffer k % NRAW ----
+    // Rows past the chunk's end copy the chunk's first row (finite values; their
+    // logits are masked).  Compressed rows are 256 bytes apart, window rows 512.
+    auto dma_chunk = [&](int k) {
         if (k >= k_end) return;
         bool win;
         int base;
         const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
-        if (st_row >= nv) return;
+        const int buf = k % NRAW;
         if (win) {
-            int slot = slot0 + base + st_row;
-            if (slot >= cap) slot -= cap;
-            const uint8_t* src = wrow0 + (int64_t)slot * D + 16 * st_u;
-            s.c0 = *(const uint4*)src;
-            s.c1 = *(const uint4*)(src + 256);
-            if (st_u == 0) s.sc = __float_as_uint(wsc[slot]);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rr = 4 * wave + 2 * h2 + (lane >> 5), q = lane & 31;
+                int slot = slot0 + base + (rr < nv ? rr : 0);
+                if (slot >= cap) slot -= cap;
+                dma16(wrow0 + (int64_t)slot * D + 16 * (q ^ (rr & 15)),
+                      lds_addr(&rawc[buf][(4 * wave + 2 * h2) * 512]));
+            }
+            if (wave == 0 && lane < CH) {
+                int slot = slot0 + base + (lane < nv ? lane : 0);
+                if (slot >= cap) slot -= cap;
+                dma4(wsc + slot, lds_addr(&rscl[buf][0]));
+            }
         } else {
-            const int e = sidx[base + st_row];
-            s.c0 = *(const uint4*)(zc0 + (int64_t)e * 256 + 16 * st_u);
-            if (st_u < 4) s.sc = *(const uint32_t*)(zs0 + (int64_t)e * 16 + 4 * st_u);
-        }
-    };
-    auto stage_store = [&](int k, const Stage& s) {
-        if (k >= k_end) return;
-        bool win;
-        int base;
-        chunk_rows(k, nwch, nwin, ncmp, &win, &base);
-        const int buf = k & 1;
-        uint8_t* rr = &rawc[buf][st_row * 512];
-        const int x = st_row & 15;
-        *(uint4*)(rr + 16 * (st_u ^ x)) = s.c0;
-        if (win) {
-            *(uint4*)(rr + 16 * ((st_u + 16) ^ x)) = s.c1;
-            if (st_u == 0) rscl[buf][st_row] = __uint_as_float(s.sc);
-        } else if (st_u < 4) {
-            zsc[buf][st_row][st_u] = s.sc;   // the entry's 16 scale bytes, in order
+            const int rr = 4 * wave + (lane >> 4), q = lane & 15;
+            const int e = sidx[base + (rr < nv ? rr : 0)];
+            dma16(zc0 + (int64_t)e * 256 + 16 * (q ^ (rr & 15)),
+                  lds_addr(&rawc[buf][4 * wave * 256]));
+            if (wave == 0 && lane < CH) {
+                const int e2 = sidx[base + (lane < nv ? lane : 0)];
+                dma16(zs0 + (int64_t)e2 * 16, lds_addr(&zsc[buf][0][0]));
+            }
         }
     };
 
@@ -258,33 +305,33 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     float m_used = -INFINITY, l_part = 0.0f;      // QK waves: head 16*g4 + n16
     const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
 
-    Stage SA;
-    stage_load(k_begin, SA);
-    stage_store(k_begin, SA);
-    stage_load(k_begin + 1, SA);
-    __syncthreads();
+    dma_chunk(k_begin);
+    dma_chunk(k_begin + 1);
+    dma_chunk(k_begin + 2);
+    // chunk k_begin staged: every staged chunk is at least one copy per wave, so
+    // two later chunks in flight allow two outstanding copies
+    if (k_begin + 2 < k_end) barrier_vm<2>();
+    else barrier_vm<0>();
 
-    // One chunk.  `nxt` holds the raw codes of chunk k+1 (stored here) and is
-    // then refilled with chunk k+2.
-    auto chunk = [&](int k, Stage& nxt) {
+    auto chunk = [&](int k) {
         bool win;
         int base;
         const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
-        const int buf = k & 1;
+        const int buf = k & 1, rbuf = k % NRAW;
         // ---- QK + dequantisation of channel block g4 of rows 16*half.. --------
         const int r = 16 * half + n16;
         const int r15 = r & 15;
-        const uint8_t* rrow = &rawc[buf][r * 512];
+        const uint8_t* rrow = &rawc[rbuf][r * (win ? 512 : 256)];
         uint16_t* grow = &Gb[buf][r * D];
         const int gsw = gb_swz(r);
-        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+        f4 ah = f4{0.f, 0.f, 0.f, 0.f}, al = f4{0.f, 0.f, 0.f, 0.f};
         i8 mine;
         if (win) {
             if (qk) {
-                acc = qk_step<0, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 0 ? &mine : nullptr);
-                acc = qk_step<1, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 1 ? &mine : nullptr);
-                acc = qk_step<2, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 2 ? &mine : nullptr);
-                acc = qk_step<3, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, acc, g4 == 3 ? &mine : nullptr);
+                qk_step<0, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 0 ? &mine : nullptr);
+                qk_step<1, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 1 ? &mine : nullptr);
+                qk_step<2, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 2 ? &mine : nullptr);
+                qk_step<3, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 3 ? &mine : nullptr);
             } else {
                 const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * g4 + g) ^ r15));
                 const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * g4 + 4 + g) ^ r15));
@@ -306,16 +353,16 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             }
         } else {
             // the row's scale bytes regrouped for lane group g: byte m = block 4m + g
-            const uint4 z4 = *(const uint4*)&zsc[buf][r][0];
+            const uint4 z4 = *(const uint4*)&zsc[rbuf][r][0];
             const uint32_t sel = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
             const uint32_t zs = __builtin_amdgcn_perm(__builtin_amdgcn_perm(z4.w, z4.z, sel),
                                                       __builtin_amdgcn_perm(z4.y, z4.x, sel),
                                                       0x05040100u);
             if (qk) {
-                acc = qk_step<0, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 0 ? &mine : nullptr);
-                acc = qk_step<1, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 1 ? &mine : nullptr);
-                acc = qk_step<2, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 2 ? &mine : nullptr);
-                acc = qk_step<3, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, acc, g4 == 3 ? &mine : nullptr);
+                qk_step<0, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 0 ? &mine : nullptr);
+                qk_step<1, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 1 ? &mine : nullptr);
+                qk_step<2, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 2 ? &mine : nullptr);
+                qk_step<3, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 3 ? &mine : nullptr);
             } else {
                 const uint4 x = *(const uint4*)(rrow + 16 * ((4 * g4 + g) ^ r15));
                 mine = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
@@ -334,19 +381,21 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             }
         }
         // ---- logits of rows 16*half + 4g + i, head 16*g4 + n16 ---------------
-        float s[4], lm = -INFINITY;
+        const f4 acc = ah + al;
+        float s[4], rs[4], lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * half + 4 * g + i;
-            float v = acc[i] * (win ? lscale * rscl[buf][rr] : lscale);
+            rs[i] = win ? rscl[rbuf][rr] : 1.0f;
+            float v = acc[i] * (lscale * rs[i]);
             v = rr < nv ? v : -INFINITY;
             s[i] = v;
             lm = fmaxf(lm, v);
         }
-        lm = fmaxf(lm, __shfl_xor(lm, 16, 64));
-        lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
+        lm = rows_max(lm);
         if (qk && g == 0) mxb[half][16 * g4 + n16] = lm;
-        __syncthreads();   // A: S maxima, bf16 rows of chunk k written; raw[k+1 & 1] free
+        barrier_lds();     // A: maxima and bf16 rows of chunk k written; raw buffer k free
+        dma_chunk(k + NRAW);
 
         if (qk) {
             const float cm = fmaxf(lm, mxb[half ^ 1][16 * g4 + n16]);
@@ -361,21 +410,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const int rr = 16 * half + 4 * g + i;
                 const float e = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_used);
                 ps += e;
-                pv[i] = win ? e * rscl[buf][rr] : e;
+                pv[i] = e * rs[i];
             }
-            ps += __shfl_xor(ps, 16, 64);
-            ps += __shfl_xor(ps, 32, 64);
-            l_part = l_part * corr + ps;
+            l_part = l_part * corr + rows_sum(ps);
             const int h = 16 * g4 + n16;
-            const uint32_t p01 = (uint32_t)f2bf(pv[0]) | ((uint32_t)f2bf(pv[1]) << 16);
-            const uint32_t p23 = (uint32_t)f2bf(pv[2]) | ((uint32_t)f2bf(pv[3]) << 16);
+            const uint32_t p01 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[0], (__bf16)pv[1]});
+            const uint32_t p23 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[2], (__bf16)pv[3]});
             const int rr0 = 16 * half + 4 * g;
             *(uint2*)((uint8_t*)Pb + pb_off(h, rr0 >> 3) + 2 * (rr0 & 7)) = make_uint2(p01, p23);
             if (half == 0 && g == 0) cor[h] = corr;
         }
-        stage_store(k + 1, nxt);
-        stage_load(k + 2, nxt);
-        __syncthreads();   // B: P, corrections and raw[k+1] visible
+        // B: P and corrections visible; chunk k+1 staged (chunks k+2, k+3 may be in flight)
+        if (k + NRAW < k_end) barrier_vm<2>();
+        else barrier_vm<0>();
 
         // ---- PV: O^T[64w + 16ct + .., heads] += G^T P^T over the 32 rows -------
         float cr[HT];
@@ -414,7 +461,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         }
     };
 
-    for (int k = k_begin; k < k_end; ++k) chunk(k, SA);
+    for (int k = k_begin; k < k_end; ++k) chunk(k);
 
     // ---- final per-head state ----------------------------------------------
     if (qk && g == 0) {
@@ -450,8 +497,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         o[2 * q2 + 1] = x1 * co - x0 * si;
                     }
                 }
-                const uint32_t w0v = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-                const uint32_t w1v = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+                const uint32_t w0v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[0], (__bf16)o[1]});
+                const uint32_t w1v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[2], (__bf16)o[3]});
                 *(uint2*)(orow + d0) = make_uint2(w0v, w1v);
             }
             if (lse && wave == 0 && g == 0)
