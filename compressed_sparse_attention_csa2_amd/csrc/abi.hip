@@ -25,12 +25,12 @@ __global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*);
 __global__ void k_quant_index_query(const uint16_t*, const float*, int64_t, uint8_t*, float*);
 template <int TOK>
 __global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
-                               const float*, const uint8_t*, const uint8_t*, int64_t, float*, int,
-                               int);
-__global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int,
-                       int32_t*, int32_t*, int32_t*, float*, int32_t*);
-__global__ void k_topk_merge(int, int, int, const int32_t*, const float*, const int32_t*,
-                             int32_t*, int32_t*);
+                               const float*, const uint8_t*, const uint8_t*, int64_t, float*,
+                               int64_t, int, int);
+__global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int64_t,
+                       int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*, uint32_t*);
+__global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const int32_t*,
+                             const uint32_t*, int32_t*, int32_t*);
 template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
@@ -84,25 +84,34 @@ int attn_split(int64_t tokens) {
     return ns > 8 ? 8 : ns;
 }
 
-constexpr int TOPK_SEG_H = 32768;   // list length one selection block handles
-
-int topk_segments(int64_t stride) { return (int)cdiv(stride, TOPK_SEG_H); }
+// Segments per query row for the selection: enough lists (one wave each) to
+// fill the chip when rows are few, at most 16 segments of at least 4096 entries.
+int topk_segments(int64_t rows, int64_t stride) {
+    int64_t ns = cdiv(4096, rows > 0 ? rows : 1);
+    if (ns > 16) ns = 16;
+    const int64_t by_len = stride / 4096;
+    if (ns > by_len) ns = by_len;
+    return ns < 1 ? 1 : (int)ns;
+}
+int topk_seg_len(int64_t stride, int nseg) { return (int)(cdiv(cdiv(stride, nseg), 256) * 256); }
+int64_t score_pitch(int64_t stride) { return cdiv(stride, 64) * 64; }   // floats between score rows
 
 struct IndexWs {
-    size_t q8, wq, S, seg_j, seg_s, seg_n, total;
+    size_t q8, wq, S, seg_key, seg_j, seg_n, seg_kth, total;
 };
 IndexWs index_ws(int B, int Tq, int64_t stride) {
     IndexWs w;
     const size_t rows = (size_t)B * Tq;
-    const int nseg = topk_segments(stride);
+    const int nseg = topk_segments((int64_t)rows, stride);
     w.q8 = 0;
     w.wq = align256(rows * HI * DI);
     w.S = w.wq + align256(rows * HI * sizeof(float));
-    w.seg_j = w.S + align256(rows * (size_t)stride * sizeof(float));
+    w.seg_key = w.S + align256(rows * (size_t)score_pitch(stride) * sizeof(float));
     const size_t segc = nseg > 1 ? rows * nseg * TOPK : 0;
-    w.seg_s = w.seg_j + align256(segc * sizeof(int32_t));
-    w.seg_n = w.seg_s + align256(segc * sizeof(float));
-    w.total = w.seg_n + align256((nseg > 1 ? rows * nseg : 0) * sizeof(int32_t));
+    w.seg_j = w.seg_key + align256(segc * sizeof(uint32_t));
+    w.seg_n = w.seg_j + align256(segc * sizeof(int32_t));
+    w.seg_kth = w.seg_n + align256((nseg > 1 ? rows * nseg : 0) * sizeof(int32_t));
+    w.total = w.seg_kth + align256((nseg > 1 ? rows * nseg : 0) * sizeof(uint32_t));
     return w;
 }
 
@@ -130,7 +139,8 @@ bool bad_sizes(int B, int Tq, int64_t stride) {
 
 void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                    const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                   const uint8_t* ki_scales, int64_t stride, float* Sc, void* ws, hipStream_t st) {
+                   const uint8_t* ki_scales, int64_t stride, float* Sc, int64_t s_stride, void* ws,
+                   hipStream_t st) {
     const IndexWs L = index_ws(B, Tq, stride);
     uint8_t* base = (uint8_t*)ws;
     uint8_t* q8 = base + L.q8;
@@ -145,13 +155,13 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
     const dim3 grid((unsigned)cdiv(items, 4));
     if (tok == 1)
         hipLaunchKernelGGL(k_index_scores<1>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
     else if (tok == 8)
         hipLaunchKernelGGL(k_index_scores<8>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
     else
         hipLaunchKernelGGL(k_index_scores<4>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
 }
 
 csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
@@ -161,17 +171,21 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     if (Tq == 0) return CSA2_OK;
     const IndexWs L = index_ws(B, Tq, stride);
     float* Sc = (float*)((uint8_t*)ws + L.S);
-    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, ws, st);
-    const int nseg = topk_segments(stride);
+    const int64_t pitch = score_pitch(stride);
+    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, pitch, ws, st);
+    const int64_t rows = (int64_t)B * Tq;
+    const int nseg = topk_segments(rows, stride);
+    const int seg_len = topk_seg_len(stride, nseg);
+    uint32_t* seg_key = (uint32_t*)((uint8_t*)ws + L.seg_key);
     int32_t* seg_j = (int32_t*)((uint8_t*)ws + L.seg_j);
-    float* seg_s = (float*)((uint8_t*)ws + L.seg_s);
     int32_t* seg_n = (int32_t*)((uint8_t*)ws + L.seg_n);
-    const unsigned rows = (unsigned)((int64_t)B * Tq);
-    hipLaunchKernelGGL(k_topk, dim3(rows, (unsigned)nseg), dim3(256), 0, st, B, Tq, q_pos0,
-                       n_entries, Sc, stride, nseg, idx, cnt, seg_j, seg_s, seg_n);
+    uint32_t* seg_kth = (uint32_t*)((uint8_t*)ws + L.seg_kth);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)cdiv(rows * nseg, 4)), dim3(256), 0, st, B, Tq,
+                       q_pos0, n_entries, Sc, pitch, stride, nseg, seg_len, idx, cnt, seg_key,
+                       seg_j, seg_n, seg_kth);
     if (nseg > 1)
-        hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(256), 0, st, B, Tq, nseg, seg_j, seg_s,
-                           seg_n, idx, cnt);
+        hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
+                           (int)rows, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
     return check_launch("csa2_index_topk");
 }
 
@@ -284,8 +298,6 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
-    if (topk_segments(entry_stride) > 64)
-        return fail(CSA2_ERR_UNSUPPORTED, "index_topk: entry_stride %lld > 2097152", (long long)entry_stride);
     const size_t need = index_ws(B, Tq, entry_stride).total;
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
@@ -305,7 +317,8 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_scores: workspace %zu < %zu bytes", ws_bytes, need);
     if (Tq == 0) return ok();
-    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, scores, ws,
+    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, scores,
+                  entry_stride, ws,
                   S(stream));
     csa2_status s = check_launch("csa2_index_scores");
     return s == CSA2_OK ? ok() : s;
@@ -355,8 +368,6 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
     if ((int64_t)cap < (int64_t)T + WINDOW - 1)
         return fail(CSA2_ERR_RANGE, "forward: window ring cap=%d < T+127=%lld", cap, (long long)T + WINDOW - 1);
     if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "forward: empty rotary table");
-    if (topk_segments(entry_stride) > 64)
-        return fail(CSA2_ERR_UNSUPPORTED, "forward: entry_stride %lld > 2097152", (long long)entry_stride);
     const size_t need = csa2_workspace_size(CSA2_OP_FORWARD, B, T, H, entry_stride);
     if (!ws || ws_bytes < need)
         return fail(CSA2_ERR_WORKSPACE, "forward: workspace %zu < %zu bytes", ws_bytes, need);

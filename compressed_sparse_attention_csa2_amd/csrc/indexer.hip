@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const uint8_t* __restrict__ q8, const float* __restrict__ wq,
     const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
-    int64_t entry_stride, float* __restrict__ S, int n_tg, int n_ch) {
+    int64_t entry_stride, float* __restrict__ S, int64_t s_stride, int n_tg, int n_ch) {
     static_assert(TOK == 1 || TOK % 4 == 0, "token slots per wave");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     }
     const uint8_t* kbase = ki_codes + ((int64_t)b * entry_stride + j_begin) * 64 + 16 * grp;
     const uint8_t* sbase = ki_scales + ((int64_t)b * entry_stride + j_begin) * 4;
-    float* Sbase = S + ((int64_t)b * Tq + t0) * entry_stride + j_begin;
+    float* Sbase = S + ((int64_t)b * Tq + t0) * s_stride + j_begin;
 
     auto load = [&](int jt, uint4& kc, uint32_t& sw) {
         int j = jt + col;
@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
 #pragma unroll
                 for (int g = 1; g < 4; ++g)
                     if (grp == g) nc = ncand[k4 + g < TOK ? k4 + g : k4];
-                if (j < nc) Sbase[(int64_t)(k4 + grp) * entry_stride + j] = tot;
+                if (j < nc) Sbase[(int64_t)(k4 + grp) * s_stride + j] = tot;
             }
         }
     }
@@ -184,25 +184,23 @@ __global__ void __launch_bounds__(256) k_index_scores(
 
 // ---------------------------------------------------------------------------
 // Top-512 selection.  Keys are the scores mapped to order-preserving u32 (-0
-// first turned into +0 so equal scores compare equal).  Ties: larger score,
-// then smaller entry index; output in ascending entry order, padded with -1.
+// first turned into +0 so equal scores compare equal; 0 never occurs for a
+// finite score and marks "no element").  Ties: larger score, then smaller
+// entry index; output in ascending entry order, padded with -1.
 //
-// One block of 256 threads per list (a query row, or the merged candidates of
-// a long row's segments):
-//  1. theta = the 512th largest key of a strided sample (at most SAMPLE keys)
-//     of the list -- a lower bound of the list's 512th largest key;
-//  2. one pass compacts every element with key >= theta, in list order, into
-//     LDS (at most CAND);
-//  3. radix select of the 512th largest key among those, then an ordered
-//     compaction of the winners.
-// When more than CAND elements reach theta (large exact ties) the block falls
-// back to radix passes over the list in global memory.  Lists longer than
-// TOPK_SEG are cut into segments whose top-512 are merged by a second launch.
+// One wave per list (a query row, a segment of a long row, or the merged
+// candidates of a row's segments), no block barriers.  The list is streamed
+// once, in order, 256 elements per step (lane l holds elements 4l..4l+3), and
+// every element whose key exceeds the wave's threshold is appended to a
+// per-wave LDS buffer (ballot compaction keeps list order).  When the buffer
+// would overflow, a wave-local radix select finds its 512th largest key K
+// (and how many copies of K belong to the top 512); the buffer is compacted
+// to exactly those 512 and the threshold becomes K, now strict: a later
+// element equal to K ranks below the 512 kept ones (all earlier in the list).
+// At the end the same select trims the buffer to 512.
 // ---------------------------------------------------------------------------
-constexpr int TK_THREADS = 256;
-constexpr int TK_SAMPLE = 8192;
-constexpr int TK_CAND = 4096;
-constexpr int TOPK_SEG = 32768;
+constexpr int WS_CAP = 1024;          // per-wave candidate buffer
+constexpr int WS_WAVES = 4;           // lists per block
 
 __device__ __forceinline__ uint32_t score_key(float f) {
     f = f + 0.0f;   // -0 -> +0 so equal scores compare equal
@@ -210,267 +208,340 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// exclusive block scan of one value per thread; returns prefix, total in *tot
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds4, uint32_t* tot) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const uint32_t o = __shfl_up(inc, s, 64);
-        if (lane >= s) inc += o;
-    }
-    if (lane == 63) lds4[wave] = inc;
-    __syncthreads();
-    uint32_t base = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < TK_THREADS / 64; ++w) {
-        const uint32_t x = lds4[w];
-        if (w < wave) base += x;
-        all += x;
-    }
-    __syncthreads();
-    *tot = all;
-    return base + inc - v;
-}
-
-struct TopkShared {
+struct WaveSel {
+    uint32_t key[WS_CAP];
+    int32_t j[WS_CAP];
     uint32_t hist[256];
-    uint32_t lds4[TK_THREADS / 64];
-    uint32_t sel_digit, sel_above;
-    uint32_t keys[TK_SAMPLE];       // sample keys, then candidate keys
-    int32_t cj[TK_CAND];            // candidate list positions
 };
 
-// After histogramming the current digit, pick the digit holding the k-th largest.
-__device__ __forceinline__ void pick_digit(TopkShared& sh, uint32_t krem) {
-    const int tid = threadIdx.x;
-    if (tid < 64) {
+// Wave-wide inclusive prefix sum with DPP row shifts and row broadcasts (no LDS).
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+// Wave-wide min / max of u32 values (DPP; lanes outside a row keep the identity),
+// returned in every lane.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
+    return min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)v, CTRL, RMASK, 0xf, false));
+}
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RMASK, 0xf, false));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+    v = dpp_min<0x111, 0xf>(v);
+    v = dpp_min<0x112, 0xf>(v);
+    v = dpp_min<0x114, 0xf>(v);
+    v = dpp_min<0x118, 0xf>(v);
+    v = dpp_min<0x142, 0xa>(v);
+    v = dpp_min<0x143, 0xc>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = dpp_max<0x111, 0xf>(v);
+    v = dpp_max<0x112, 0xf>(v);
+    v = dpp_max<0x114, 0xf>(v);
+    v = dpp_max<0x118, 0xf>(v);
+    v = dpp_max<0x142, 0xa>(v);
+    v = dpp_max<0x143, 0xc>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Radix threshold over the buffer's keys, held in registers (lane l: elements
+// l + 64r, r < 16; 0 past nc).  Returns theta with at least k keys >= theta.
+// exact: theta is the k-th largest key and *krem the number of its copies in
+// the top k.  Otherwise refinement stops as soon as at most `limit` keys are
+// >= theta (*krem is then "all copies"); if equal keys keep the count above the
+// limit to the last bit, the exact answer is returned.  The bits common to all
+// keys are skipped; 8 bits per pass.
+__device__ uint32_t wave_threshold(WaveSel& ws, const uint32_t (&kr)[16], uint32_t k,
+                                   uint32_t limit, bool exact, uint32_t* krem_out) {
+    const int lane = threadIdx.x & 63;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (kr[r] != 0u) lo = min(lo, kr[r]);
+        hi = max(hi, kr[r]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lo >= hi) {                 // all keys equal
+        *krem_out = exact ? k : 0xFFFFFFFFu;
+        return hi;
+    }
+    int hib = 31 - __clz((int)(lo ^ hi));
+    uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
+    uint32_t prefix = lo & pmask, krem = k, above_all = 0;
+    while (hib >= 0) {
+        const int lob = hib - 7 > 0 ? hib - 7 : 0;
+        const uint32_t dmask = (2u << (hib - lob)) - 1u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ws.hist[4 * lane + q] = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (kr[r] != 0u && (kr[r] & pmask) == prefix) atomicAdd(&ws.hist[(kr[r] >> lob) & dmask], 1u);
+        // digit holding the krem-th largest: bins in descending order, 4 per lane
         uint32_t h[4], loc = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { h[q] = sh.hist[255 - 4 * tid - q]; loc += h[q]; }
-        uint32_t inc = loc;
-#pragma unroll
-        for (int sft = 1; sft < 64; sft <<= 1) {
-            const uint32_t o = __shfl_up(inc, sft, 64);
-            if (tid >= sft) inc += o;
-        }
-        uint32_t above = inc - loc;
+        for (int q = 0; q < 4; ++q) { h[q] = ws.hist[255 - 4 * lane - q]; loc += h[q]; }
+        const uint32_t inc = wave_scan_add(loc);
+        uint32_t above = inc - loc, dsel = 0, asel = 0, hsel = 0;
+        bool found = false;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (above < krem && krem <= above + h[q]) {
-                sh.sel_digit = 255 - 4 * tid - q;
-                sh.sel_above = above;
+                dsel = 255u - 4u * lane - q;
+                asel = above;
+                hsel = h[q];
+                found = true;
             }
             above += h[q];
         }
-    }
-}
-
-// k-th largest key (1-based k <= n) of n keys given by get(i); returns the key,
-// *krem = how many elements equal to it belong to the top k.
-template <typename Get>
-__device__ uint32_t radix_kth(TopkShared& sh, int n, uint32_t k, Get get, uint32_t* krem_out) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0, krem = k;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        sh.hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += TK_THREADS) {
-            const uint32_t key = get(i);
-            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        const int src = __ffsll((long long)__ballot(found)) - 1;
+        dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
+        asel = (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
+        hsel = (uint32_t)__builtin_amdgcn_readlane((int)hsel, src);
+        prefix |= dsel << lob;
+        pmask |= dmask << lob;
+        krem -= asel;
+        above_all += asel;
+        hib = lob - 1;
+        if (!exact && above_all + hsel <= limit) {   // keys >= prefix (low bits 0) fit
+            *krem_out = 0xFFFFFFFFu;
+            return prefix;
         }
-        __syncthreads();
-        pick_digit(sh, krem);
-        __syncthreads();
-        prefix |= sh.sel_digit << shift;
-        pmask |= 255u << shift;
-        krem -= sh.sel_above;
-        __syncthreads();
     }
+    // every bit resolved: the k-th largest itself, and its copies in the top k
+    // (also when a non-exact search could not get under the limit: many equal keys)
     *krem_out = krem;
     return prefix;
 }
 
-// Winners among n elements in list order: keys above kth, and the first krem equal
-// to it.  pos_of(i) gives the output value for element i.
-template <typename Get, typename Pos>
-__device__ void ordered_winners(TopkShared& sh, int n, uint32_t kth, uint32_t krem, Get get,
-                                Pos pos_of, int32_t* out) {
-    const int tid = threadIdx.x;
-    uint32_t eq_base = 0, sel_base = 0;
-    for (int i0 = 0; i0 < n; i0 += TK_THREADS * 4) {
-        uint32_t keys[4], neq = 0;
+// Keep, in order, the buffered elements above theta and the first krem equal to it.
+__device__ int wave_keep(WaveSel& ws, int nc, const uint32_t (&kr)[16], uint32_t theta,
+                         uint32_t krem) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int32_t jr[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = i0 + 4 * tid + q;
-            keys[q] = i < n ? get(i) : 0u;
-            neq += (i < n && keys[q] == kth) ? 1u : 0u;
-        }
-        uint32_t eq_tot;
-        uint32_t eq_rank = eq_base + block_excl_scan(neq, sh.lds4, &eq_tot);
-        uint32_t take[4], nsel = 0;
+    for (int r = 0; r < 16; ++r) jr[r] = 64 * r + lane < nc ? ws.j[64 * r + lane] : 0;
+    uint32_t kept = 0, eq = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = i0 + 4 * tid + q;
-            bool tk = false;
-            if (i < n) {
-                if (keys[q] > kth) tk = true;
-                else if (keys[q] == kth) { tk = eq_rank < krem; ++eq_rank; }
-            }
-            take[q] = tk;
-            nsel += tk;
+    for (int r = 0; r < 16; ++r) {
+        if (64 * r >= nc) break;
+        const bool valid = 64 * r + lane < nc;
+        const uint64_t meq = __ballot(valid && kr[r] == theta);
+        const bool keep = valid && (kr[r] > theta ||
+                                    (kr[r] == theta && eq + (uint32_t)__popcll(meq & below) < krem));
+        const uint64_t mk = __ballot(keep);
+        if (keep) {
+            const uint32_t pos = kept + (uint32_t)__popcll(mk & below);
+            ws.key[pos] = kr[r];
+            ws.j[pos] = jr[r];
         }
-        uint32_t sel_tot;
-        uint32_t pos = sel_base + block_excl_scan(nsel, sh.lds4, &sel_tot);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (take[q] && pos < TOPK) out[pos] = pos_of(i0 + 4 * tid + q);
-            pos += take[q];
-        }
-        eq_base += eq_tot;
-        sel_base += sel_tot;
+        kept += (uint32_t)__popcll(mk);
+        eq += (uint32_t)__popcll(meq);
     }
+    return (int)kept;
 }
 
-// Top-512 of a list of n scores (list element i: score sc(i), entry index jj(i));
-// writes TOPK entry indices (ascending, -1 padded) and returns the count.
-template <typename Sc, typename Jj>
-__device__ int select_list(TopkShared& sh, int n, Sc sc, Jj jj, int32_t* out) {
-    const int tid = threadIdx.x;
-    if (n <= TOPK) {
-        for (int i = tid; i < TOPK; i += TK_THREADS) out[i] = i < n ? jj(i) : -1;
-        return n;
-    }
-    // 1. sampled lower bound of the 512th largest key
-    const int stride = (n + TK_SAMPLE - 1) / TK_SAMPLE;
-    const int m = (n + stride - 1) / stride;
-    for (int i = tid; i < m; i += TK_THREADS) sh.keys[i] = score_key(sc(i * stride));
-    __syncthreads();
-    uint32_t krem;
-    const uint32_t theta = radix_kth(sh, m, TOPK, [&](int i) { return sh.keys[i]; }, &krem);
-    if (stride == 1) {   // the sample is the whole list: theta is the exact 512th key
-        ordered_winners(sh, n, theta, krem, [&](int i) { return sh.keys[i]; },
-                        [&](int i) { return jj(i); }, out);
-        return TOPK;
-    }
-    // 2. ordered compaction of keys >= theta
-    uint32_t base = 0;
-    for (int i0 = 0; i0 < n; i0 += TK_THREADS * 4) {
-        uint32_t keys[4], nge = 0;
+__device__ __forceinline__ void load_keys(const WaveSel& ws, int nc, uint32_t (&kr)[16]) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = i0 + 4 * tid + q;
-            keys[q] = i < n ? score_key(sc(i)) : 0u;
-            nge += (i < n && keys[q] >= theta) ? 1u : 0u;
+    for (int r = 0; r < 16; ++r) kr[r] = 64 * r + lane < nc ? ws.key[64 * r + lane] : 0u;
+}
+
+struct WaveTopk {
+    WaveSel& ws;
+    int nc;
+    uint32_t thr;     // elements with key > thr are appended (0: every element)
+
+    // four elements per lane, in list order (lane, then q); key 0 = no element
+    __device__ void push(const uint32_t (&k)[4], const int32_t (&jj)[4]) {
+        const int lane = threadIdx.x & 63;
+        const uint64_t below = (1ull << lane) - 1ull;
+        uint64_t m[4];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { m[q] = __ballot(k[q] > thr); cnt += (uint32_t)__popcll(m[q]); }
+        if (nc + (int)cnt > WS_CAP) {
+            // keep every key >= theta, where at least 512 are >= theta: a later key
+            // equal to theta ranks below all of them
+            uint32_t kr[16], krem;
+            load_keys(ws, nc, kr);
+            const uint32_t theta = wave_threshold(ws, kr, TOPK, WS_CAP - 256, false, &krem);
+            nc = wave_keep(ws, nc, kr, theta, krem);
+            thr = theta;
+            cnt = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { m[q] = __ballot(k[q] > thr); cnt += (uint32_t)__popcll(m[q]); }
         }
-        uint32_t tot;
-        uint32_t pos = base + block_excl_scan(nge, sh.lds4, &tot);
+        uint32_t pos = (uint32_t)nc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pos += (uint32_t)__popcll(m[q] & below);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int i = i0 + 4 * tid + q;
-            if (i < n && keys[q] >= theta) {
-                if (pos < TK_CAND) { sh.keys[pos] = keys[q]; sh.cj[pos] = jj(i); }
+            if (k[q] > thr) {
+                ws.key[pos] = k[q];
+                ws.j[pos] = jj[q];
                 ++pos;
             }
         }
-        base += tot;
+        nc += (int)cnt;
     }
-    __syncthreads();
-    if (base <= (uint32_t)TK_CAND) {
-        // 3. exact selection among the candidates (held in list order)
-        const int nc = (int)base;
-        const uint32_t kth = radix_kth(sh, nc, TOPK, [&](int i) { return sh.keys[i]; }, &krem);
-        ordered_winners(sh, nc, kth, krem, [&](int i) { return sh.keys[i]; },
-                        [&](int i) { return sh.cj[i]; }, out);
-    } else {
-        // many exact ties at theta: radix passes over the whole list
-        const uint32_t kth = radix_kth(sh, n, TOPK, [&](int i) { return score_key(sc(i)); }, &krem);
-        ordered_winners(sh, n, kth, krem, [&](int i) { return score_key(sc(i)); },
-                        [&](int i) { return jj(i); }, out);
-    }
-    return TOPK;
-}
 
-// One block per query row of length n(t) <= TOPK_SEG, or per (row, segment)
-// when the cache is longer (then writes the segment's winners as candidates).
-__global__ void __launch_bounds__(TK_THREADS) k_topk(int B, int Tq,
-                                                     const int32_t* __restrict__ q_pos0,
-                                                     const int32_t* __restrict__ n_entries,
-                                                     const float* __restrict__ S,
-                                                     int64_t entry_stride, int nseg,
-                                                     int32_t* __restrict__ idx,
-                                                     int32_t* __restrict__ cnt,
-                                                     int32_t* __restrict__ seg_j,
-                                                     float* __restrict__ seg_s,
-                                                     int32_t* __restrict__ seg_n) {
-    __shared__ TopkShared sh;
-    const int row = blockIdx.x;
-    const int seg = blockIdx.y;
-    const int b = row / Tq, t = row - b * Tq;
-    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
-    const float* srow = S + (int64_t)row * entry_stride;
-    if (nseg == 1) {
-        const int c = select_list(sh, (int)n, [&](int i) { return srow[i]; },
-                                  [&](int i) { return i; }, idx + (int64_t)row * TOPK);
-        if (threadIdx.x == 0) cnt[row] = c;
-        return;
-    }
-    const int64_t j0 = (int64_t)seg * TOPK_SEG;
-    int len = (int)(n - j0 < TOPK_SEG ? n - j0 : TOPK_SEG);
-    len = len < 0 ? 0 : len;
-    int32_t* oj = seg_j + ((int64_t)row * nseg + seg) * TOPK;
-    const int c = select_list(sh, len, [&](int i) { return srow[j0 + i]; },
-                              [&](int i) { return (int)(j0 + i); }, oj);
-    __syncthreads();
-    // scores of this segment's winners for the merge
-    float* os = seg_s + ((int64_t)row * nseg + seg) * TOPK;
-    for (int i = threadIdx.x; i < c; i += TK_THREADS) os[i] = srow[oj[i]];
-    if (threadIdx.x == 0) seg_n[(int64_t)row * nseg + seg] = c;
-}
-
-// Merge of the segments' candidates of one row (in segment order, i.e. entry order).
-__global__ void __launch_bounds__(TK_THREADS) k_topk_merge(int B, int Tq, int nseg,
-                                                           const int32_t* __restrict__ seg_j,
-                                                           const float* __restrict__ seg_s,
-                                                           const int32_t* __restrict__ seg_n,
-                                                           int32_t* __restrict__ idx,
-                                                           int32_t* __restrict__ cnt) {
-    __shared__ TopkShared sh;
-    __shared__ int32_t off[65];
-    const int row = blockIdx.x;
-    const int tid = threadIdx.x;
-    // prefix of the segments' counts (nseg <= 64)
-    if (tid == 0) {
-        int acc = 0;
-        for (int s = 0; s < nseg; ++s) {
-            off[s] = acc;
-            acc += seg_n[(int64_t)row * nseg + s];
+    // the top 512 in list order to out_j (padded with -1) and, if given, their keys;
+    // *kth_out = the 512th largest key (0 when fewer than 512 elements)
+    __device__ int finish(int32_t* out_j, uint32_t* out_key, uint32_t* kth_out) {
+        const int lane = threadIdx.x & 63;
+        if (nc > TOPK) {
+            uint32_t kr[16], krem;
+            load_keys(ws, nc, kr);
+            const uint32_t kth = wave_threshold(ws, kr, TOPK, 0, true, &krem);
+            nc = wave_keep(ws, nc, kr, kth, krem);
         }
-        off[nseg] = acc;
+        uint32_t mn = 0xFFFFFFFFu;
+        for (int i = lane; i < TOPK; i += 64) {
+            out_j[i] = i < nc ? ws.j[i] : -1;
+            if (i < nc) {
+                mn = min(mn, ws.key[i]);
+                if (out_key) out_key[i] = ws.key[i];
+            }
+        }
+        if (kth_out) *kth_out = nc == TOPK ? wave_min(mn) : 0u;
+        return nc;
     }
-    __syncthreads();
-    const int total = off[nseg];
-    const int32_t* sj = seg_j + (int64_t)row * nseg * TOPK;
-    const float* ss = seg_s + (int64_t)row * nseg * TOPK;
-    auto where = [&](int i) {
-        int s = 0;
-        while (s + 1 < nseg && off[s + 1] <= i) ++s;   // nseg is small
-        return s * TOPK + (i - off[s]);
+};
+
+// One wave per (query row, segment).  Row scores are spad floats apart (spad a
+// multiple of 64); segment s covers entries [s*seg_len, (s+1)*seg_len).  With one
+// segment the result goes to idx/cnt, otherwise to the segment buffers.
+__global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const float* __restrict__ S, int64_t spad, int64_t entry_stride, int nseg, int seg_len,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cnt, uint32_t* __restrict__ seg_key,
+    int32_t* __restrict__ seg_j, int32_t* __restrict__ seg_n, uint32_t* __restrict__ seg_kth) {
+    __shared__ WaveSel sel[WS_WAVES];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * WS_WAVES + wave;
+    if (item >= (int64_t)B * Tq * nseg) return;
+    const int64_t row = item / nseg;
+    const int seg = (int)(item - row * nseg);
+    const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int64_t j0 = (int64_t)seg * seg_len;
+    int len = (int)(n - j0 < seg_len ? n - j0 : seg_len);
+    len = len < 0 ? 0 : len;
+    const float* src = S + row * spad + j0;       // 16-byte aligned
+    WaveTopk st{sel[wave], 0, 0u};
+    // 1024 elements per step: four 256-element groups, the next step's loads in flight
+    auto fetch = [&](int base, float4 (&v)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i0 = base + 256 * u + 4 * lane;
+            if (i0 + 3 < len) {
+                v[u] = *(const float4*)(src + i0);
+            } else {
+                v[u].x = i0 < len ? src[i0] : 0.f;
+                v[u].y = i0 + 1 < len ? src[i0 + 1] : 0.f;
+                v[u].z = i0 + 2 < len ? src[i0 + 2] : 0.f;
+                v[u].w = i0 + 3 < len ? src[i0 + 3] : 0.f;
+            }
+        }
     };
-    const int c = select_list(sh, total, [&](int i) { return ss[where(i)]; },
-                              [&](int i) { return sj[where(i)]; }, idx + (int64_t)row * TOPK);
-    if (tid == 0) cnt[row] = c;
+    float4 nxt[4];
+    if (len > 0) fetch(0, nxt);
+    for (int base = 0; base < len; base += 1024) {
+        float4 cur[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+        if (base + 1024 < len) fetch(base + 1024, nxt);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i0 = base + 256 * u + 4 * lane;
+            if (base + 256 * u >= len) break;
+            const uint32_t k[4] = {i0 < len ? score_key(cur[u].x) : 0u, i0 + 1 < len ? score_key(cur[u].y) : 0u,
+                                   i0 + 2 < len ? score_key(cur[u].z) : 0u, i0 + 3 < len ? score_key(cur[u].w) : 0u};
+            const int32_t jj[4] = {(int32_t)(j0 + i0), (int32_t)(j0 + i0 + 1), (int32_t)(j0 + i0 + 2),
+                                   (int32_t)(j0 + i0 + 3)};
+            st.push(k, jj);
+        }
+    }
+    if (nseg == 1) {
+        const int c = st.finish(idx + row * TOPK, nullptr, nullptr);
+        if (lane == 0) cnt[row] = c;
+    } else {
+        uint32_t kth;
+        const int c = st.finish(seg_j + item * TOPK, seg_key + item * TOPK, &kth);
+        if (lane == 0) {
+            seg_n[item] = c;
+            seg_kth[item] = kth;
+        }
+    }
+}
+
+// Merge of a row's segment winners (segments in entry order): one wave per row.
+// The largest of the segments' 512th keys bounds the row's 512th key from below
+// (that segment alone holds 512 keys at or above it), so only keys at or above
+// it are streamed.
+__global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
+    int rows, int nseg, const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ seg_j,
+    const int32_t* __restrict__ seg_n, const uint32_t* __restrict__ seg_kth,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+    __shared__ WaveSel sel[WS_WAVES];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * WS_WAVES + wave;
+    if (row >= rows) return;
+    const uint32_t bound = wave_max(lane < nseg ? seg_kth[row * nseg + lane] : 0u);
+    WaveTopk st{sel[wave], 0, bound > 0u ? bound - 1u : 0u};
+    // each segment's 512 slots in one step: two 256-element groups, vector loads
+    auto fetch = [&](int s, uint4 (&kv)[2], int4 (&jv)[2]) {
+        const int64_t it = row * nseg + s;
+        int m = seg_n[it];
+        m = m < 0 ? 0 : (m > TOPK ? TOPK : m);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i0 = 256 * u + 4 * lane;
+            kv[u] = *(const uint4*)(seg_key + it * TOPK + i0);
+            jv[u] = *(const int4*)(seg_j + it * TOPK + i0);
+            if (i0 >= m) kv[u].x = 0u;
+            if (i0 + 1 >= m) kv[u].y = 0u;
+            if (i0 + 2 >= m) kv[u].z = 0u;
+            if (i0 + 3 >= m) kv[u].w = 0u;
+        }
+    };
+    uint4 nk[2];
+    int4 nj[2];
+    fetch(0, nk, nj);
+    for (int s = 0; s < nseg; ++s) {
+        const uint4 ck[2] = {nk[0], nk[1]};
+        const int4 cj[2] = {nj[0], nj[1]};
+        if (s + 1 < nseg) fetch(s + 1, nk, nj);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t k[4] = {ck[u].x, ck[u].y, ck[u].z, ck[u].w};
+            const int32_t jj[4] = {cj[u].x, cj[u].y, cj[u].z, cj[u].w};
+            st.push(k, jj);
+        }
+    }
+    const int c = st.finish(idx + row * TOPK, nullptr, nullptr);
+    if (lane == 0) cnt[row] = c;
 }
 
 template __global__ void k_index_scores<1>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int, int);
+                                           float*, int64_t, int, int);
 template __global__ void k_index_scores<4>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int, int);
+                                           float*, int64_t, int, int);
 template __global__ void k_index_scores<8>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int, int);
+                                           float*, int64_t, int, int);
 
 }  // namespace csa2

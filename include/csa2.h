@@ -123,7 +123,6 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
  *            padded with -1.  Ties: larger score, then smaller entry.
  *  cnt       [B][Tq] int32 out: min(512, min(floor((p+1)/2), n_entries)).
  *  ws        workspace of at least csa2_workspace_size(CSA2_OP_INDEX_TOPK, ...).
- *  entry_stride is at most 2097152 (longer caches: CSA2_ERR_UNSUPPORTED).
  */
 csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
