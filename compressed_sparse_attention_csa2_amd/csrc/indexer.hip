@@ -79,8 +79,9 @@ __device__ __forceinline__ float rowsum_scatter4(float a, float b, float c, floa
 
 // Scores S[(b*Tq + t)][j] for j < n(t).  One wave per (request, TOK tokens,
 // chunk of IDX_CHUNK entries); work items are ordered heaviest tokens first.
-// The next 16 entries' codes and scales are loaded while the current ones are
-// multiplied.
+// The codes and scales of the next tiles of 16 entries are in flight while the
+// current tile is multiplied; all products of a tile are issued before the
+// first is read.
 template <int TOK>
 __global__ void __launch_bounds__(256) k_index_scores(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
     int64_t entry_stride, float* __restrict__ S, int64_t s_stride, int n_tg, int n_ch) {
     static_assert(TOK == 1 || TOK % 4 == 0, "token slots per wave");
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
     if (item >= (int64_t)B * n_tg * n_ch) return;
     const int ch = (int)(item % n_ch);
@@ -130,6 +131,11 @@ __global__ void __launch_bounds__(256) k_index_scores(
     const uint8_t* kbase = ki_codes + ((int64_t)b * entry_stride + j_begin) * 64 + 16 * grp;
     const uint8_t* sbase = ki_scales + ((int64_t)b * entry_stride + j_begin) * 4;
     float* Sbase = S + ((int64_t)b * Tq + t0) * s_stride + j_begin;
+    // Stores go through a buffer resource: lanes past their token's candidates
+    // get an out-of-range offset and are dropped by the hardware, so the loop has
+    // no branch around memory operations and every wait is exact.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        Sbase, (short)0, (int)((int64_t)TOK * s_stride * 4), 0x00020000);
 
     auto load = [&](int jt, uint4& kc, uint32_t& sw) {
         int j = jt + col;
@@ -137,34 +143,50 @@ __global__ void __launch_bounds__(256) k_index_scores(
         kc = *(const uint4*)(kbase + (int64_t)j * 64);
         sw = *(const uint32_t*)(sbase + (int64_t)j * 4);
     };
-    uint4 kc_n;
-    uint32_t sw_n;
-    load(0, kc_n, sw_n);
-#pragma unroll 2
-    for (int jt = 0; jt < j_len; jt += 16) {
-        const uint4 kc = kc_n;
-        const uint32_t sw = sw_n;
-        if (jt + 16 < j_len) load(jt + 16, kc_n, sw_n);
+    // PF tiles of 16 entries in flight (deeper for the single-token scan, whose
+    // registers allow it); loads are clamped to the chunk, so always issued
+    constexpr int PF = TOK == 1 ? 4 : 1;
+    uint4 kr[PF];
+    uint32_t sr[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load(16 * p, kr[p], sr[p]);
+    for (int jt0 = 0; jt0 < j_len; jt0 += 16 * PF)
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int jt = jt0 + 16 * p;
+        if (PF > 1 && jt >= j_len) break;
+        const uint4 kc = kr[p];
+        const uint32_t sw = sr[p];
+        load(jt + 16 * PF, kr[p], sr[p]);
         const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
         const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
         float s[TOK];
+        constexpr int KG = TOK < 4 ? TOK : 4;     // tokens whose products are issued together
 #pragma unroll
-        for (int k = 0; k < TOK; ++k) {
-            const f4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                A[k][0], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
-            const f4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                A[k][1], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
-            float acc = 0.0f;
+        for (int k0 = 0; k0 < TOK; k0 += KG) {
+            f4 d[KG][2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k][0][i], relu(d0[i]), acc);
+            for (int k = 0; k < KG; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k][1][i], relu(d1[i]), acc);
-            s[k] = acc;
+                for (int tile = 0; tile < 2; ++tile)
+                    d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+            __builtin_amdgcn_sched_barrier(0);   // all products issued before the first is read
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][0][i], relu(d[k][0][i]), acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][1][i], relu(d[k][1][i]), acc);
+                s[k0 + k] = acc;
+            }
         }
         const int j = jt + col;
         if (TOK == 1) {
             const float tot = rowsum_scatter4(s[0], s[0], s[0], s[0]);
-            if (grp == 0 && j < ncand[0]) Sbase[j] = tot;
+            const int off = (grp == 0 && j < ncand[0]) ? 4 * j : 0x7FFFFFFF;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), srs, off, 0, 0);
         } else {
 #pragma unroll
             for (int k4 = 0; k4 < TOK; k4 += 4) {
@@ -176,7 +198,8 @@ __global__ void __launch_bounds__(256) k_index_scores(
 #pragma unroll
                 for (int g = 1; g < 4; ++g)
                     if (grp == g) nc = ncand[k4 + g < TOK ? k4 + g : k4];
-                if (j < nc) Sbase[(int64_t)(k4 + grp) * s_stride + j] = tot;
+                const int off = j < nc ? 4 * ((k4 + grp) * (int)s_stride + j) : 0x7FFFFFFF;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), srs, off, 0, 0);
             }
         }
     }
