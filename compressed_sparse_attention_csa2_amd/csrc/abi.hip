@@ -196,6 +196,10 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
                         const float* rc, const float* rs, int64_t rope_rows, uint16_t* O,
                         float* lse, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
+    // the kernel addresses one request's caches with 32-bit byte offsets
+    if ((int64_t)cap * D > (int64_t)0xFFFFFFFF || stride * 256 > (int64_t)0xFFFFFFFF)
+        return fail(CSA2_ERR_RANGE, "sparse_attn: cap=%d (at most 8388607) or entry stride=%lld "
+                    "(at most 16777215) too large", cap, (long long)stride);
     const AttnWs L = attn_ws(B, Tq, H);
     float* pO = (float*)((uint8_t*)ws + L.pO);
     float* pml = (float*)((uint8_t*)ws + L.pml);

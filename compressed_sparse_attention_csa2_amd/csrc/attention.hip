@@ -10,10 +10,10 @@
 //
 // One block of 8 waves per (query token, split of its rows).  The rows are
 // taken 32 at a time ("chunks"; window rows and compressed rows never share a
-// chunk).  Per chunk:
+// chunk, and each kind has its own compiled chunk body).  Per chunk:
 //   staging  the chunk's raw codes (FP8 window rows or FP4 entries with their
-//            E8M0 block scales) are loaded one chunk ahead into registers and
-//            stored to LDS (double-buffered), swizzled by 16-byte unit;
+//            E8M0 block scales) are copied straight into LDS three chunks
+//            ahead (four raw buffers), swizzled by 16-byte unit;
 //   QK       wave (g4 = w/2, half = w%2) computes S for 16 heads x 16 rows
 //            with the block-scaled MFMA 16x16x128: A = the raw row codes (FP4
 //            with their own block scales, or FP8), B = the query split into
@@ -21,40 +21,47 @@
 //            which together reproduce the bf16 query exactly up to the
 //            smallest elements of a block.  The same wave dequantises one
 //            quarter of its rows' channels to bf16 for the PV product;
-//   softmax  online, in log2 units, with a lazy maximum: the running maximum
-//            of a head only moves when the chunk exceeds it by more than
-//            2^8, so rescales are rare.  P (bf16) goes to LDS as [head][row];
+//   softmax  online, in log2 units, against a running maximum per head that
+//            only moves when a chunk exceeds it by more than 2^32: each wave
+//            writes P for its 16 rows with the current maximum, and a chunk
+//            that passes the headroom (always the first) raises a flag after
+//            which the whole block exchanges row-half maxima, rescales and
+//            redoes P.  P (bf16) goes to LDS as [head][row], double-buffered;
 //   PV       wave w owns channels 64w..64w+63 for every head: O^T += G^T P^T
 //            with bf16 MFMA 16x16x32; G^T is read with the transposing LDS
 //            load (ds_read_b64_tr_b16), so each bf16 row is stored once.
+// One block barrier per chunk (after P), plus one on flagged chunks.
 // Window rows enter as E4M3 codes; their fp32 row scale multiplies the logit
 // and is folded into P.  Splits of the chunk range write (m, l, unnormalised
 // O) partials that k_attn_combine merges.
+#include <type_traits>
+
 #include "csa2_device.h"
 
 namespace csa2 {
 
 constexpr int CH = 32;                 // rows per chunk
 constexpr int ATT_THREADS = 512;       // 8 waves
-constexpr float LAZY_TAU = 8.0f;       // log2 headroom before the running max is moved
+constexpr float LAZY_TAU = 32.0f;      // log2 headroom before the running max is moved
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(4))) short s4;
 typedef __attribute__((address_space(3))) s4 lds_s4;
 typedef __attribute__((ext_vector_type(2))) short s2v;
 
-constexpr int NRAW = 3;                // raw staging buffers (chunks in flight)
+constexpr int NRAW = 4;                // raw staging buffers (chunks in flight)
 
-// Direct-to-LDS copies: every active lane copies 16 (4) bytes from its own
-// global address to lds + 16 (4) * lane; lds is wave-uniform and goes to M0.
-// The kernel uses M0 for nothing else.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory");
+// Direct-to-LDS copies: every active lane copies 16 (4) bytes from a
+// wave-uniform base plus its own 32-bit byte offset to lds + 16 (4) * lane;
+// lds is wave-uniform and goes to M0.  The kernel uses M0 for nothing else.
+// Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds) : "memory");
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 // Workgroup barrier after this wave's LDS operations and all but its N most
 // recent direct-to-LDS copies have completed.
@@ -91,47 +98,6 @@ __device__ __forceinline__ int gb_swz(int r) {
 // P [head][32 rows] bf16, 64 bytes per head: unit u at u ^ ((h >> 2) & 3)
 __device__ __forceinline__ int pb_off(int h, int u) { return h * 64 + ((u ^ ((h >> 2) & 3)) << 4); }
 
-// Chunk k of a token: window chunks first (rows [32k, ..) of the window), then
-// compressed chunks.  Returns the valid row count; *win and *base describe it.
-__device__ __forceinline__ int chunk_rows(int k, int nwch, int nwin, int ncmp, bool* win,
-                                          int* base) {
-    if (k < nwch) {
-        *win = true;
-        *base = k * CH;
-        const int n = nwin - k * CH;
-        return n < CH ? n : CH;
-    }
-    *win = false;
-    *base = (k - nwch) * CH;
-    const int n = ncmp - (k - nwch) * CH;
-    return n < CH ? n : CH;
-}
-
-// One MFMA step of S for channel block M (128 channels): A = raw row codes, B =
-// query hi (into ah) and lo (into al).  Scale registers carry the block
-// exponent in their low byte (byte M of the packed words).
-template <int M, bool WIN>
-__device__ __forceinline__ void qk_step(const uint8_t* rrow, int r15, int g, uint32_t zsc,
-                                        const i8 (&qh)[4], const i8 (&ql)[4], uint32_t qsh,
-                                        uint32_t qsl, f4& ah, f4& al, i8* keep) {
-    const int sh = (int)((qsh >> (8 * M)) & 0xFFu), sl = (int)((qsl >> (8 * M)) & 0xFFu);
-    i8 a;
-    if constexpr (WIN) {
-        const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * M + g) ^ r15));
-        const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * M + 4 + g) ^ r15));
-        a = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], ah, 0, 0, 0, 127, 0, sh);
-        al = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], al, 0, 0, 0, 127, 0, sl);
-    } else {
-        const int sa = (int)((zsc >> (8 * M)) & 0xFFu);
-        const uint4 x = *(const uint4*)(rrow + 16 * ((4 * M + g) ^ r15));
-        a = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        ah = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[M], ah, 4, 0, 0, sa, 0, sh);
-        al = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[M], al, 4, 0, 0, sa, 0, sl);
-    }
-    if (keep) *keep = a;
-}
-
 template <int HT>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     int B, int Tq, int H, const int32_t* __restrict__ q_pos0, const uint16_t* __restrict__ Q,
@@ -146,9 +112,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     __shared__ __attribute__((aligned(16))) uint32_t zsc[NRAW][CH][4];
     __shared__ __attribute__((aligned(16))) float rscl[NRAW][CH];
     __shared__ __attribute__((aligned(16))) uint16_t Gb[2][CH * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Pb[64 * CH];
-    __shared__ float mxb[2][64];
+    __shared__ __attribute__((aligned(16))) uint16_t Pb[2][64 * CH];
+    __shared__ float mxb[2][2][64];
     __shared__ float cor[64];
+    __shared__ int flag[2];
     __shared__ float mfin[64], lfin[2][64];
     __shared__ int32_t sidx[TOPK];
 
@@ -199,7 +166,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     i8 qh[4], ql[4];
     uint32_t qsh = 0x7F7F7F7Fu, qsl = 0x7F7F7F7Fu;
     uint4* qx = (uint4*)&Gb[0][0];                 // [g4][m][4 quads][64 lanes]
-    uint32_t* qxs = (uint32_t*)&Pb[0];               // [g4][m][64 lanes] exponents (4 KB)
+    uint32_t* qxs = (uint32_t*)&Pb[0][0];               // [g4][m][64 lanes] exponents (4 KB)
     if (qk) {
         const uint16_t* qrow = Q + (((int64_t)b * H + 16 * g4 + n16) * Tq + t) * D;
 #pragma unroll
@@ -247,6 +214,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             qxs[(g4 * 4 + m) * 64 + lane] = (uint32_t)sh;
         }
     }
+    if (tid < 2) flag[tid] = -1;
     __syncthreads();   // sidx ready, both halves of the query converted
     if (qk) {
 #pragma unroll
@@ -264,36 +232,43 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
 
     // ---- staging: direct-to-LDS copies of chunk k into raw buffer k % NRAW ----
     // Rows past the chunk's end copy the chunk's first row (finite values; their
-    // logits are masked).  Compressed rows are 256 bytes apart, window rows 512.
-    auto dma_chunk = [&](int k) {
+    // logits are masked).  Compressed rows are 256 bytes apart, window rows 512;
+    // lane q of a row copies 16-byte unit q ^ (row & 15) of it to unit q, so the
+    // row's unit u sits at u ^ (row & 15).  Source offsets are 32-bit, relative
+    // to the request's cache base (the caller's sizes are checked for that).
+    auto chunk_entries = [&](int k, int& e, int& e2) {
+        if (k >= k_end || k < nwch) return;
+        const int base = (k - nwch) * CH;
+        const int nv = min(ncmp - base, CH);
+        const int rr = 4 * wave + (lane >> 4);
+        e = sidx[base + (rr < nv ? rr : 0)];
+        e2 = sidx[base + ((lane & 31) < nv ? (lane & 31) : 0)];
+    };
+    auto dma_chunk = [&](int k, bool have_entries, int pe, int pe2) {
         if (k >= k_end) return;
-        bool win;
-        int base;
-        const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
         const int buf = k % NRAW;
-        if (win) {
+        if (k < nwch) {
+            const int base = k * CH;
+            const int nv = min(nwin - base, CH);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int rr = 4 * wave + 2 * h2 + (lane >> 5), q = lane & 31;
                 int slot = slot0 + base + (rr < nv ? rr : 0);
-                if (slot >= cap) slot -= cap;
-                dma16(wrow0 + (int64_t)slot * D + 16 * (q ^ (rr & 15)),
-                      lds_addr(&rawc[buf][(4 * wave + 2 * h2) * 512]));
+                slot = slot >= cap ? slot - cap : slot;
+                dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(q ^ (rr & 15)),
+                       lds_addr(&rawc[buf][(4 * wave + 2 * h2) * 512]));
             }
             if (wave == 0 && lane < CH) {
                 int slot = slot0 + base + (lane < nv ? lane : 0);
-                if (slot >= cap) slot -= cap;
-                dma4(wsc + slot, lds_addr(&rscl[buf][0]));
+                slot = slot >= cap ? slot - cap : slot;
+                dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
             }
         } else {
+            if (!have_entries) chunk_entries(k, pe, pe2);
             const int rr = 4 * wave + (lane >> 4), q = lane & 15;
-            const int e = sidx[base + (rr < nv ? rr : 0)];
-            dma16(zc0 + (int64_t)e * 256 + 16 * (q ^ (rr & 15)),
-                  lds_addr(&rawc[buf][4 * wave * 256]));
-            if (wave == 0 && lane < CH) {
-                const int e2 = sidx[base + (lane < nv ? lane : 0)];
-                dma16(zs0 + (int64_t)e2 * 16, lds_addr(&zsc[buf][0][0]));
-            }
+            dma16s(zc0, (uint32_t)pe * 256u + 16u * (uint32_t)(q ^ (rr & 15)),
+                   lds_addr(&rawc[buf][4 * wave * 256]));
+            if (wave == 0 && lane < CH) dma16s(zs0, (uint32_t)pe2 * 16u, lds_addr(&zsc[buf][0][0]));
         }
     };
 
@@ -302,76 +277,99 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] = f4{0.f, 0.f, 0.f, 0.f};
-    float m_used = -INFINITY, l_part = 0.0f;      // QK waves: head 16*g4 + n16
+    // QK waves, head 16*g4 + n16: running maximum (log2 units) and this lane's
+    // share of the denominator (its four rows of every chunk)
+    float m_used = -INFINITY, l_lane = 0.0f;
     const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
 
-    dma_chunk(k_begin);
-    dma_chunk(k_begin + 1);
-    dma_chunk(k_begin + 2);
+    dma_chunk(k_begin, false, 0, 0);
+    dma_chunk(k_begin + 1, false, 0, 0);
+    dma_chunk(k_begin + 2, false, 0, 0);
     // chunk k_begin staged: every staged chunk is at least one copy per wave, so
-    // two later chunks in flight allow two outstanding copies
+    // n later chunks in flight allow n outstanding copies
     if (k_begin + 2 < k_end) barrier_vm<2>();
+    else if (k_begin + 1 < k_end) barrier_vm<1>();
     else barrier_vm<0>();
 
-    auto chunk = [&](int k) {
-        bool win;
-        int base;
-        const int nv = chunk_rows(k, nwch, nwin, ncmp, &win, &base);
+    // Per-lane constants: the QK operand lane (row 16*half + n16, group g)
+    // reads unit (4m + g) ^ r15 of a compressed row and units (8m + g) ^ r15,
+    // (8m + 4 + g) ^ r15 of a window row; bf16 row r's unit u is at u ^ gb_swz(r).
+    const int r = 16 * half + n16, r15 = r & 15;
+    const int gsw = gb_swz(r);
+    const int h = 16 * g4 + n16;
+    const int rr0 = 16 * half + 4 * g;             // first of this lane's four logit rows
+    const uint32_t sel_g = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
+
+    // One chunk; WIN selects window rows (E4M3 codes, fp32 row scales) or
+    // compressed rows (E2M1 codes, E8M0 block scales) at compile time.
+    auto chunk = [&](int k, auto win_c) {
+        constexpr bool WIN = decltype(win_c)::value;
         const int buf = k & 1, rbuf = k % NRAW;
-        // ---- QK + dequantisation of channel block g4 of rows 16*half.. --------
-        const int r = 16 * half + n16;
-        const int r15 = r & 15;
-        const uint8_t* rrow = &rawc[rbuf][r * (win ? 512 : 256)];
+        const int base = WIN ? k * CH : (k - nwch) * CH;
+        const int nv = min((WIN ? nwin : ncmp) - base, CH);
+        const uint8_t* rrow = &rawc[rbuf][r * (WIN ? 512 : 256)];
         uint16_t* grow = &Gb[buf][r * D];
-        const int gsw = gb_swz(r);
-        f4 ah = f4{0.f, 0.f, 0.f, 0.f}, al = f4{0.f, 0.f, 0.f, 0.f};
-        i8 mine;
-        if (win) {
+
+        // ---- QK: S (16 heads x 16 rows) = rows . (q_hi + q_lo), one chain ----
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+        uint32_t zs = 0;
+        float rs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (WIN) {
             if (qk) {
-                qk_step<0, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 0 ? &mine : nullptr);
-                qk_step<1, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 1 ? &mine : nullptr);
-                qk_step<2, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 2 ? &mine : nullptr);
-                qk_step<3, true>(rrow, r15, g, 0, qh, ql, qsh, qsl, ah, al, g4 == 3 ? &mine : nullptr);
-            } else {
-                const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * g4 + g) ^ r15));
-                const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * g4 + 4 + g) ^ r15));
-                mine = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 x0 = *(const uint4*)(rrow + 16 * ((8 * m + g) ^ r15));
+                    const uint4 x1 = *(const uint4*)(rrow + 16 * ((8 * m + 4 + g) ^ r15));
+                    const i8 a = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                    const int sh = (int)((qsh >> (8 * m)) & 0xFFu), sl = (int)((qsl >> (8 * m)) & 0xFFu);
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[m], acc, 0, 0, 0, 127, 0, sh);
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[m], acc, 0, 0, 0, 127, 0, sl);
+                }
             }
-            // bf16 of channels 128*g4 + 16g..+15 (units 16g4 + 2g, +1) and +64 (units +8)
+            const float4 q4 = *(const float4*)&rscl[rbuf][rr0];
+            rs[0] = q4.x; rs[1] = q4.y; rs[2] = q4.z; rs[3] = q4.w;
+        } else {
+            // the row's scale bytes regrouped for lane group g: byte m = block 4m + g
+            const uint4 z4 = *(const uint4*)&zsc[rbuf][r][0];
+            zs = __builtin_amdgcn_perm(__builtin_amdgcn_perm(z4.w, z4.z, sel_g),
+                                       __builtin_amdgcn_perm(z4.y, z4.x, sel_g), 0x05040100u);
+            if (qk) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 x = *(const uint4*)(rrow + 16 * ((4 * m + g) ^ r15));
+                    const i8 a = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+                    const int sh = (int)((qsh >> (8 * m)) & 0xFFu), sl = (int)((qsl >> (8 * m)) & 0xFFu);
+                    const int sa = (int)((zs >> (8 * m)) & 0xFFu);
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh[m], acc, 4, 0, 0, sa, 0, sh);
+                    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql[m], acc, 4, 0, 0, sa, 0, sl);
+                }
+            }
+        }
+        // ---- bf16 copy of channel block g4 of rows 16*half.. (for PV) ----------
+        int pe = 0, pe2 = 0;
+        chunk_entries(k + NRAW - 1, pe, pe2);
+        if constexpr (WIN) {
+            // channels 128*g4 + 16g..+15 (units 16g4 + 2g, +1) and +64 (units +8)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const uint32_t w0 = (uint32_t)mine[4 * s2], w1 = (uint32_t)mine[4 * s2 + 1];
-                const uint32_t w2 = (uint32_t)mine[4 * s2 + 2], w3 = (uint32_t)mine[4 * s2 + 3];
-                const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                                            fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
-                const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(w2), fp8x2_to_bf16x2<true>(w2),
-                                            fp8x2_to_bf16x2<false>(w3), fp8x2_to_bf16x2<true>(w3));
+                const uint4 x = *(const uint4*)(rrow + 16 * ((8 * g4 + 4 * s2 + g) ^ r15));
+                const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
+                                            fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y));
+                const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(x.z), fp8x2_to_bf16x2<true>(x.z),
+                                            fp8x2_to_bf16x2<false>(x.w), fp8x2_to_bf16x2<true>(x.w));
                 const int u = 16 * g4 + 8 * s2 + 2 * g;
                 *(uint4*)(grow + 8 * (u ^ gsw)) = lo;
                 *(uint4*)(grow + 8 * ((u + 1) ^ gsw)) = hi;
             }
         } else {
-            // the row's scale bytes regrouped for lane group g: byte m = block 4m + g
-            const uint4 z4 = *(const uint4*)&zsc[rbuf][r][0];
-            const uint32_t sel = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
-            const uint32_t zs = __builtin_amdgcn_perm(__builtin_amdgcn_perm(z4.w, z4.z, sel),
-                                                      __builtin_amdgcn_perm(z4.y, z4.x, sel),
-                                                      0x05040100u);
-            if (qk) {
-                qk_step<0, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 0 ? &mine : nullptr);
-                qk_step<1, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 1 ? &mine : nullptr);
-                qk_step<2, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 2 ? &mine : nullptr);
-                qk_step<3, false>(rrow, r15, g, zs, qh, ql, qsh, qsl, ah, al, g4 == 3 ? &mine : nullptr);
-            } else {
-                const uint4 x = *(const uint4*)(rrow + 16 * ((4 * g4 + g) ^ r15));
-                mine = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-            }
-            // bf16 of channels 128*g4 + 32g..+31 (units 16g4 + 4g .. +3)
+            // channels 128*g4 + 32g..+31 (units 16g4 + 4g .. +3)
+            const uint4 x = *(const uint4*)(rrow + 16 * ((4 * g4 + g) ^ r15));
             const float sc = e8m0_to_f32((zs >> (8 * g4)) & 0xFFu);
+            const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) {
-                const uint32_t w = (uint32_t)mine[k2];
+                const uint32_t w = w4[k2];
                 const uint4 v = make_uint4(
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
@@ -380,73 +378,90 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 *(uint4*)(grow + 8 * ((16 * g4 + 4 * g + k2) ^ gsw)) = v;
             }
         }
-        // ---- logits of rows 16*half + 4g + i, head 16*g4 + n16 ---------------
-        const f4 acc = ah + al;
-        float s[4], rs[4], lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * half + 4 * g + i;
-            rs[i] = win ? rscl[rbuf][rr] : 1.0f;
-            float v = acc[i] * (lscale * rs[i]);
-            v = rr < nv ? v : -INFINITY;
-            s[i] = v;
-            lm = fmaxf(lm, v);
-        }
-        lm = rows_max(lm);
-        if (qk && g == 0) mxb[half][16 * g4 + n16] = lm;
-        barrier_lds();     // A: maxima and bf16 rows of chunk k written; raw buffer k free
-        dma_chunk(k + NRAW);
+        // raw buffer (k + NRAW - 1) % NRAW held chunk k - 1, read by every wave before B(k-1)
+        dma_chunk(k + NRAW - 1, true, pe, pe2);
 
+        // ---- logits of rows rr0 + i (log2 units) and P against the running max -
+        float s[4], lm;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = acc[i] * (WIN ? lscale * rs[i] : lscale);
+        if (nv < CH) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = rr0 + i < nv ? s[i] : -INFINITY;
+        }
+        lm = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        uint8_t* pbk = (uint8_t*)&Pb[buf][0] + pb_off(h, rr0 >> 3) + 2 * (rr0 & 7);
+        float ps = 0.0f;
         if (qk) {
-            const float cm = fmaxf(lm, mxb[half ^ 1][16 * g4 + n16]);
-            float corr = 1.0f;
-            if (cm > m_used + LAZY_TAU) {
-                corr = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - cm);
-                m_used = cm;
-            }
-            float ps = 0.0f, pv[4];
+            if (g == 0) mxb[buf][half][h] = lm;
+            // past the headroom (and always on the first chunk, m_used = -inf):
+            // the block redoes P below with both halves' maxima
+            if (lm > m_used + LAZY_TAU) flag[buf] = k;
+            float pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * half + 4 * g + i;
-                const float e = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_used);
+                const float e = __builtin_amdgcn_exp2f(s[i] - m_used);
                 ps += e;
-                pv[i] = e * rs[i];
+                pv[i] = WIN ? e * rs[i] : e;
             }
-            l_part = l_part * corr + rows_sum(ps);
-            const int h = 16 * g4 + n16;
             const uint32_t p01 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[0], (__bf16)pv[1]});
             const uint32_t p23 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[2], (__bf16)pv[3]});
-            const int rr0 = 16 * half + 4 * g;
-            *(uint2*)((uint8_t*)Pb + pb_off(h, rr0 >> 3) + 2 * (rr0 & 7)) = make_uint2(p01, p23);
-            if (half == 0 && g == 0) cor[h] = corr;
+            *(uint2*)pbk = make_uint2(p01, p23);
         }
-        // B: P and corrections visible; chunk k+1 staged (chunks k+2, k+3 may be in flight)
-        if (k + NRAW < k_end) barrier_vm<2>();
+        // B: P, maxima, flag and bf16 rows visible; chunk k+1 staged (k+2, k+3 may be in flight)
+        if (k + 3 < k_end) barrier_vm<2>();
+        else if (k + 2 < k_end) barrier_vm<1>();
         else barrier_vm<0>();
 
         // ---- PV: O^T[64w + 16ct + .., heads] += G^T P^T over the 32 rows -------
-        float cr[HT];
-        bool resc = false;
+        // P and the flag are read together; a flagged chunk redoes P first
+        const bool slow = flag[buf] == k;
+        bf8 pb[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            cr[ht] = cor[16 * ht + n16];
-            resc |= cr[ht] != 1.0f;
-        }
-        if (__any(resc)) {
+        for (int ht = 0; ht < HT; ++ht)
+            pb[ht] = *(const bf8*)((const uint8_t*)&Pb[buf][0] + pb_off(16 * ht + n16, g));
+        if (slow) {
+            // block-uniform: move the maximum of every head whose chunk maximum
+            // (both row halves) is past the headroom, rescale, redo P
+            if (qk) {
+                const float cm = fmaxf(lm, mxb[buf][half ^ 1][h]);
+                float corr = 1.0f;
+                if (cm > m_used + LAZY_TAU) {
+                    corr = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - cm);
+                    m_used = cm;
+                }
+                float ps2 = 0.0f, pv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_used);
+                    ps2 += e;
+                    pv[i] = WIN ? e * rs[i] : e;
+                }
+                l_lane = l_lane * corr + ps2;
+                const uint32_t p01 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[0], (__bf16)pv[1]});
+                const uint32_t p23 = __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[2], (__bf16)pv[3]});
+                *(uint2*)pbk = make_uint2(p01, p23);
+                if (half == 0 && g == 0) cor[h] = corr;
+            }
+            barrier_lds();
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+                pb[ht] = *(const bf8*)((const uint8_t*)&Pb[buf][0] + pb_off(16 * ht + n16, g));
+            float cr[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) cr[ht] = cor[16 * ht + n16];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] *= cr[ht];
+        } else if (qk) {
+            l_lane += ps;
         }
-        bf8 pb[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-            pb[ht] = *(const bf8*)((const uint8_t*)Pb + pb_off(16 * ht + n16, g));
         const int sr = n16 >> 2, sq = n16 & 3;        // transposing-read source: row, 4-channel group
-        const int ra = 8 * g + sr, rb2 = ra + 4;
-        const uint16_t* gba = &Gb[buf][ra * D];
+        const int ra_ = 8 * g + sr, rb2 = ra_ + 4;
+        const uint16_t* gba = &Gb[buf][ra_ * D];
         const uint16_t* gbb = &Gb[buf][rb2 * D];
-        const int swa = gb_swz(ra), swb = gb_swz(rb2);
+        const int swa = gb_swz(ra_), swb = gb_swz(rb2);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const int c0 = 64 * wave + 16 * ct;
@@ -461,13 +476,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         }
     };
 
-    for (int k = k_begin; k < k_end; ++k) chunk(k);
+    {
+        const int kw = nwch < k_end ? nwch : k_end;
+        for (int k = k_begin; k < kw; ++k) chunk(k, std::true_type{});
+        for (int k = (k_begin > nwch ? k_begin : nwch); k < k_end; ++k) chunk(k, std::false_type{});
+    }
 
     // ---- final per-head state ----------------------------------------------
-    if (qk && g == 0) {
-        const int h = 16 * g4 + n16;
-        if (half == 0) mfin[h] = m_used;
-        lfin[half][h] = l_part;
+    {
+        const float l_half = rows_sum(l_lane);
+        if (qk && g == 0) {
+            if (half == 0) mfin[h] = m_used;
+            lfin[half][h] = l_half;
+        }
     }
     __syncthreads();
 #pragma unroll

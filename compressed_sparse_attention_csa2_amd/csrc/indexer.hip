@@ -143,21 +143,10 @@ __global__ void __launch_bounds__(256) k_index_scores(
         kc = *(const uint4*)(kbase + (int64_t)j * 64);
         sw = *(const uint32_t*)(sbase + (int64_t)j * 4);
     };
-    // PF tiles of 16 entries in flight (deeper for the single-token scan, whose
-    // registers allow it); loads are clamped to the chunk, so always issued
-    constexpr int PF = TOK == 1 ? 4 : 1;
-    uint4 kr[PF];
-    uint32_t sr[PF];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load(16 * p, kr[p], sr[p]);
-    for (int jt0 = 0; jt0 < j_len; jt0 += 16 * PF)
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        const int jt = jt0 + 16 * p;
-        if (PF > 1 && jt >= j_len) break;
-        const uint4 kc = kr[p];
-        const uint32_t sw = sr[p];
-        load(jt + 16 * PF, kr[p], sr[p]);
+    // Four tile buffers rotate: the codes and scales of a tile are loaded three
+    // tiles before their products (loads are clamped to the chunk, so always
+    // issued), and no buffer is copied, so no wait lands on a load just issued.
+    auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
         const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
         const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
         float s[TOK];
@@ -202,7 +191,29 @@ __global__ void __launch_bounds__(256) k_index_scores(
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), srs, off, 0, 0);
             }
         }
+    };
+    uint4 kb0, kb1, kb2, kb3;
+    uint32_t sb0, sb1, sb2, sb3;
+    load(0, kb0, sb0);
+    load(16, kb1, sb1);
+    load(32, kb2, sb2);
+    int jt = 0;
+    for (; jt + 64 <= j_len; jt += 64) {
+        load(jt + 48, kb3, sb3);
+        step(jt, kb0, sb0);
+        load(jt + 64, kb0, sb0);
+        step(jt + 16, kb1, sb1);
+        load(jt + 80, kb1, sb1);
+        step(jt + 32, kb2, sb2);
+        load(jt + 96, kb2, sb2);
+        step(jt + 48, kb3, sb3);
     }
+    // up to four tiles left: three already in kb0, kb1, kb2
+    if (jt + 48 < j_len) load(jt + 48, kb3, sb3);
+    if (jt < j_len) step(jt, kb0, sb0);
+    if (jt + 16 < j_len) step(jt + 16, kb1, sb1);
+    if (jt + 32 < j_len) step(jt + 32, kb2, sb2);
+    if (jt + 48 < j_len) step(jt + 48, kb3, sb3);
 }
 
 // ---------------------------------------------------------------------------

@@ -148,7 +148,8 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
  * blog: one key-value vector per place shared by all heads, per-head sink].
  *  H         query heads, a multiple of 16 in 16..64.
  *  Q         [B][H][Tq][512] bf16, already rotated.
- *  cap       window ring capacity, >= Tq + 127.
+ *  cap       window ring capacity, >= Tq + 127 and at most 8388607;
+ *            entry_stride at most 16777215 (CSA2_ERR_RANGE otherwise).
  *  idx, cnt  as produced by csa2_index_topk.
  *  sink      [H] fp32.
  *  O         [B][H][Tq][512] bf16 out.   lse [B][H][Tq] fp32 out or NULL
