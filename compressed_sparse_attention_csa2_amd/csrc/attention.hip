@@ -118,6 +118,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     __shared__ int flag[2];
     __shared__ float mfin[64], lfin[2][64];
     __shared__ int32_t sidx[TOPK];
+    __shared__ float sinkl[64];               // sink of head h
+    __shared__ float ropel[2][PAIRS];         // cos, sin of the token's position
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,15 +145,60 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const float* wsc = w_scale + (int64_t)b * cap;
     const uint8_t* zc0 = z_codes + (int64_t)b * entry_stride * 256;
     const uint8_t* zs0 = z_scales + (int64_t)b * entry_stride * 16;
+    const int emax = (int)entry_stride - 1;        // entries are clamped into the cache on use
+    const int64_t prow = p < rope_rows ? p : rope_rows - 1;
 
-    {   // the row's selected entries, clamped into the cache
-        const int32_t* irow = idx + (int64_t)row * TOPK;
-        const int emax = entry_stride < 0x7FFFFFFF ? (int)entry_stride - 1 : 0x7FFFFFFE;
-        for (int i = tid; i < ncmp; i += ATT_THREADS) {
-            const int e = irow[i];
-            sidx[i] = e < 0 ? 0 : (e > emax ? emax : e);
+    // ---- direct copies that nothing waits for until later --------------------
+    // the row's 512 selected entries (64 per wave), the sinks, the rotary row
+    dma4s(idx + (int64_t)row * TOPK, 4u * (uint32_t)(64 * wave + lane), lds_addr(&sidx[64 * wave]));
+    if (wave == 0 && lane < H) dma4s(sink, 4u * (uint32_t)lane, lds_addr(&sinkl[0]));
+    if (wave == 1 && lane < PAIRS) dma4s(rcos + prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[0][0]));
+    if (wave == 2 && lane < PAIRS) dma4s(rsin + prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[1][0]));
+
+    // ---- staging: direct-to-LDS copies of chunk k into raw buffer k % NRAW ----
+    // Rows past the chunk's end copy the chunk's first row (finite values; their
+    // logits are masked).  Compressed rows are 256 bytes apart, window rows 512;
+    // lane q of a row copies 16-byte unit q ^ (row & 15) of it to unit q, so the
+    // row's unit u sits at u ^ (row & 15).  Source offsets are 32-bit, relative
+    // to the request's cache base (the caller's sizes are checked for that).
+    auto chunk_entries = [&](int k, int& e, int& e2) {
+        if (k >= k_end || k < nwch) return;
+        const int base = (k - nwch) * CH;
+        const int nv = min(ncmp - base, CH);
+        const int rr = 4 * wave + (lane >> 4);
+        e = min(max(sidx[base + (rr < nv ? rr : 0)], 0), emax);
+        e2 = min(max(sidx[base + ((lane & 31) < nv ? (lane & 31) : 0)], 0), emax);
+    };
+    auto dma_chunk = [&](int k, bool have_entries, int pe, int pe2) {
+        if (k >= k_end) return;
+        const int buf = k % NRAW;
+        if (k < nwch) {
+            const int base = k * CH;
+            const int nv = min(nwin - base, CH);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rr = 4 * wave + 2 * h2 + (lane >> 5), q = lane & 31;
+                int slot = slot0 + base + (rr < nv ? rr : 0);
+                slot = slot >= cap ? slot - cap : slot;
+                dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(q ^ (rr & 15)),
+                       lds_addr(&rawc[buf][(4 * wave + 2 * h2) * 512]));
+            }
+            if (wave == 0 && lane < CH) {
+                int slot = slot0 + base + (lane < nv ? lane : 0);
+                slot = slot >= cap ? slot - cap : slot;
+                dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
+            }
+        } else {
+            if (!have_entries) chunk_entries(k, pe, pe2);
+            const int rr = 4 * wave + (lane >> 4), q = lane & 15;
+            dma16s(zc0, (uint32_t)pe * 256u + 16u * (uint32_t)(q ^ (rr & 15)),
+                   lds_addr(&rawc[buf][4 * wave * 256]));
+            if (wave == 0 && lane < CH) dma16s(zs0, (uint32_t)pe2 * 16u, lds_addr(&zsc[buf][0][0]));
         }
-    }
+    };
+
+    // window chunks among the first three need nothing else: start them now
+    for (int k = k_begin; k < k_begin + 3 && k < nwch; ++k) dma_chunk(k, false, 0, 0);
 
     // ---- query of this wave's 16 heads as two E4M3 terms (QK waves) ---------
     // Lane (head 16*g4 + n16, group g) holds, for channel block M, channels
@@ -215,6 +262,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         }
     }
     if (tid < 2) flag[tid] = -1;
+    // every copy issued so far (entries, sinks, rotary row, window chunks) is
+    // older than the query loads just consumed; make the entries visible
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // sidx ready, both halves of the query converted
     if (qk) {
 #pragma unroll
@@ -230,48 +280,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         }
     }
 
-    // ---- staging: direct-to-LDS copies of chunk k into raw buffer k % NRAW ----
-    // Rows past the chunk's end copy the chunk's first row (finite values; their
-    // logits are masked).  Compressed rows are 256 bytes apart, window rows 512;
-    // lane q of a row copies 16-byte unit q ^ (row & 15) of it to unit q, so the
-    // row's unit u sits at u ^ (row & 15).  Source offsets are 32-bit, relative
-    // to the request's cache base (the caller's sizes are checked for that).
-    auto chunk_entries = [&](int k, int& e, int& e2) {
-        if (k >= k_end || k < nwch) return;
-        const int base = (k - nwch) * CH;
-        const int nv = min(ncmp - base, CH);
-        const int rr = 4 * wave + (lane >> 4);
-        e = sidx[base + (rr < nv ? rr : 0)];
-        e2 = sidx[base + ((lane & 31) < nv ? (lane & 31) : 0)];
-    };
-    auto dma_chunk = [&](int k, bool have_entries, int pe, int pe2) {
-        if (k >= k_end) return;
-        const int buf = k % NRAW;
-        if (k < nwch) {
-            const int base = k * CH;
-            const int nv = min(nwin - base, CH);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int rr = 4 * wave + 2 * h2 + (lane >> 5), q = lane & 31;
-                int slot = slot0 + base + (rr < nv ? rr : 0);
-                slot = slot >= cap ? slot - cap : slot;
-                dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(q ^ (rr & 15)),
-                       lds_addr(&rawc[buf][(4 * wave + 2 * h2) * 512]));
-            }
-            if (wave == 0 && lane < CH) {
-                int slot = slot0 + base + (lane < nv ? lane : 0);
-                slot = slot >= cap ? slot - cap : slot;
-                dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
-            }
-        } else {
-            if (!have_entries) chunk_entries(k, pe, pe2);
-            const int rr = 4 * wave + (lane >> 4), q = lane & 15;
-            dma16s(zc0, (uint32_t)pe * 256u + 16u * (uint32_t)(q ^ (rr & 15)),
-                   lds_addr(&rawc[buf][4 * wave * 256]));
-            if (wave == 0 && lane < CH) dma16s(zs0, (uint32_t)pe2 * 16u, lds_addr(&zsc[buf][0][0]));
-        }
-    };
-
     f4 oacc[4][HT];                       // O^T tiles: [channel tile][head tile]
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
@@ -282,9 +290,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     float m_used = -INFINITY, l_lane = 0.0f;
     const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
 
-    dma_chunk(k_begin, false, 0, 0);
-    dma_chunk(k_begin + 1, false, 0, 0);
-    dma_chunk(k_begin + 2, false, 0, 0);
+    // compressed chunks among the first three (issued after the window ones, so
+    // copies stay in chunk order)
+    for (int k = (k_begin > nwch ? k_begin : nwch); k < k_begin + 3; ++k) dma_chunk(k, false, 0, 0);
     // chunk k_begin staged: every staged chunk is at least one copy per wave, so
     // n later chunks in flight allow n outstanding copies
     if (k_begin + 2 < k_end) barrier_vm<2>();
@@ -496,12 +504,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         const int h = 16 * ht + n16;
         const float m = mfin[h], l = lfin[0][h] + lfin[1][h];
         if (nsplit == 1) {
-            const float shv = sink[h] * LOG2E;
+            const float shv = sinkl[h] * LOG2E;
             const float M = fmaxf(m, shv);
             const float em = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
             const float den = l * em + __builtin_amdgcn_exp2f(shv - M);
             const float f = em / den;
-            const int64_t prow = p < rope_rows ? p : rope_rows - 1;
             uint16_t* orow = O + (((int64_t)b * H + h) * Tq + t) * D;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
@@ -512,7 +519,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
 #pragma unroll
                     for (int q2 = 0; q2 < 2; ++q2) {
                         const int pi = (d0 - ROPE_LO) / 2 + q2;
-                        const float co = rcos[prow * PAIRS + pi], si = rsin[prow * PAIRS + pi];
+                        const float co = ropel[0][pi], si = ropel[1][pi];
                         const float x0 = o[2 * q2], x1 = o[2 * q2 + 1];
                         o[2 * q2] = x0 * co + x1 * si;
                         o[2 * q2 + 1] = x1 * co - x0 * si;
