@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     const int g4 = wave >> 1, half = wave & 1;     // QK role: head group, row half
-    const bool qk = g4 < HT;
+    const bool qk = HT == 4 || g4 < HT;
     const int row = blockIdx.x;                    // b * Tq + t
     const int split = blockIdx.y;
     const int b = row / Tq, t = row - b * Tq;
@@ -308,6 +308,32 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const int rr0 = 16 * half + 4 * g;             // first of this lane's four logit rows
     const uint32_t sel_g = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
 
+    // PV of chunk kp: O^T[64w + 16ct + .., heads] += G^T P^T over its 32 rows
+    auto pv = [&](int kp) {
+        const int bp = kp & 1;
+        bf8 pb[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+            pb[ht] = *(const bf8*)((const uint8_t*)&Pb[bp][0] + pb_off(16 * ht + n16, g));
+        const int sr = n16 >> 2, sq = n16 & 3;        // transposing-read source: row, 4-channel group
+        const int ra_ = 8 * g + sr, rb2 = ra_ + 4;
+        const uint16_t* gba = &Gb[bp][ra_ * D];
+        const uint16_t* gbb = &Gb[bp][rb2 * D];
+        const int swa = gb_swz(ra_), swb = gb_swz(rb2);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int c0 = 64 * wave + 16 * ct;
+            const int u = (c0 >> 3) + (sq >> 1);
+            const int off = 4 * (sq & 1);
+            const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gba + 8 * (u ^ swa) + off));
+            const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gbb + 8 * (u ^ swb) + off));
+            const bf8 a = __builtin_bit_cast(bf8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+                oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht], oacc[ct][ht], 0, 0, 0);
+        }
+    };
+
     // One chunk; WIN selects window rows (E4M3 codes, fp32 row scales) or
     // compressed rows (E2M1 codes, E8M0 block scales) at compile time.
     auto chunk = [&](int k, auto win_c) {
@@ -354,6 +380,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 }
             }
         }
+        // PV of the previous chunk shares this phase with the QK products
+        if (k > k_begin) pv(k - 1);
         // ---- bf16 copy of channel block g4 of rows 16*half.. (for PV) ----------
         int pe = 0, pe2 = 0;
         chunk_entries(k + NRAW - 1, pe, pe2);
@@ -421,14 +449,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         else if (k + 2 < k_end) barrier_vm<1>();
         else barrier_vm<0>();
 
-        // ---- PV: O^T[64w + 16ct + .., heads] += G^T P^T over the 32 rows -------
-        // P and the flag are read together; a flagged chunk redoes P first
-        const bool slow = flag[buf] == k;
-        bf8 pb[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-            pb[ht] = *(const bf8*)((const uint8_t*)&Pb[buf][0] + pb_off(16 * ht + n16, g));
-        if (slow) {
+        // a flagged chunk redoes P with both halves' maxima before its PV
+        if (flag[buf] == k) {
             // block-uniform: move the maximum of every head whose chunk maximum
             // (both row halves) is past the headroom, rescale, redo P
             if (qk) {
@@ -452,9 +474,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 if (half == 0 && g == 0) cor[h] = corr;
             }
             barrier_lds();
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-                pb[ht] = *(const bf8*)((const uint8_t*)&Pb[buf][0] + pb_off(16 * ht + n16, g));
+            // PV(k-1) is already in oacc; PV(k) comes with the next chunk
             float cr[HT];
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) cr[ht] = cor[16 * ht + n16];
@@ -465,29 +485,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         } else if (qk) {
             l_lane += ps;
         }
-        const int sr = n16 >> 2, sq = n16 & 3;        // transposing-read source: row, 4-channel group
-        const int ra_ = 8 * g + sr, rb2 = ra_ + 4;
-        const uint16_t* gba = &Gb[buf][ra_ * D];
-        const uint16_t* gbb = &Gb[buf][rb2 * D];
-        const int swa = gb_swz(ra_), swb = gb_swz(rb2);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const int c0 = 64 * wave + 16 * ct;
-            const int u = (c0 >> 3) + (sq >> 1);
-            const int off = 4 * (sq & 1);
-            const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gba + 8 * (u ^ swa) + off));
-            const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gbb + 8 * (u ^ swb) + off));
-            const bf8 a = __builtin_bit_cast(bf8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-                oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht], oacc[ct][ht], 0, 0, 0);
-        }
     };
 
     {
         const int kw = nwch < k_end ? nwch : k_end;
         for (int k = k_begin; k < kw; ++k) chunk(k, std::true_type{});
         for (int k = (k_begin > nwch ? k_begin : nwch); k < k_end; ++k) chunk(k, std::false_type{});
+        if (k_end > k_begin) pv(k_end - 1);
     }
 
     // ---- final per-head state ----------------------------------------------
