@@ -78,6 +78,20 @@ int index_tok(int Tq) { return Tq == 1 ? 1 : (Tq <= 8 ? 8 : 4); }
 
 // split of a token's attention rows (20 chunks of 32 at full size) across
 // blocks when there are too few tokens to fill the chip
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
 int attn_split(int64_t tokens) {
     if (tokens >= 256) return 1;
     const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
@@ -203,7 +217,11 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     const AttnWs L = attn_ws(B, Tq, H);
     float* pO = (float*)((uint8_t*)ws + L.pO);
     float* pml = (float*)((uint8_t*)ws + L.pml);
-    const dim3 grid((unsigned)((int64_t)B * Tq), (unsigned)L.nsplit);
+    // persistent blocks (one per compute unit) walk the (row, split) units
+    const int64_t units = (int64_t)B * Tq * L.nsplit;
+    if (units > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
+    const int64_t nblk = units < device_cus() ? units : device_cus();
+    const dim3 grid((unsigned)nblk);
     const int ht = H / 16;   // head tiles of 16
 #define CSA2_ATTN(HTV)                                                                         \
     hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(512), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
