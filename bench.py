@@ -33,14 +33,14 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.352e10, {
-        "attention.hip": "89d1af482a00c98ad02d3dd4af06b5601f4d8c5e5025c092bb9fe27455d685c1",
+    ("k_attn", "prefill", 65536): (1.382e10, {
+        "attention.hip": "98a39d9fd469c04a93bb806bfddaac087d6f16e69b5b6570912271ba0148db20",
         "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
-    ("k_index_scores", "prefill", 65536): (5.321e9, {
-        "indexer.hip": "f7dc91f1199930d3221211c44fcb891ffd4c4bed9ad1117010a4c1a6043030d3",
+    ("k_index_scores", "prefill", 65536): (5.196e9, {
+        "indexer.hip": "9751a81ed93f08d0f72006e5c021fe19d57a9876203d411ace53239a52eaf6f9",
         "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
-    ("k_index_scores", "decode", 131072): (6.085e8, {
-        "indexer.hip": "f7dc91f1199930d3221211c44fcb891ffd4c4bed9ad1117010a4c1a6043030d3",
+    ("k_index_scores", "decode", 131072): (6.087e8, {
+        "indexer.hip": "9751a81ed93f08d0f72006e5c021fe19d57a9876203d411ace53239a52eaf6f9",
         "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
 }
 
