@@ -125,7 +125,7 @@ IndexWs index_ws(int B, int Tq, int64_t stride) {
     w.seg_j = w.seg_key + align256(segc * sizeof(uint32_t));
     w.seg_n = w.seg_j + align256(segc * sizeof(int32_t));
     w.seg_kth = w.seg_n + align256((nseg > 1 ? rows * nseg : 0) * sizeof(int32_t));
-    w.total = w.seg_kth + align256((nseg > 1 ? rows * nseg : 0) * sizeof(uint32_t));
+    w.total = w.seg_kth + align256((nseg > 1 ? rows * nseg * 2 : 0) * sizeof(uint32_t));
     return w;
 }
 

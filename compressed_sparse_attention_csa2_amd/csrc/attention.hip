@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
 
     if (wave == 0 && lane < H) dma4s(sink, 4u * (uint32_t)lane, lds_addr(&sinkl[0]));
 
-    // The block walks units (query row, split) blockIdx.x, + gridDim.x, ...
+    // The block walks its units (query row, split) in the order unit_at gives.
     // Per unit both roles pass the same barriers: start, one per chunk, final.
     // Between final(u) and start(u + 1) the PV waves write unit u's output while
     // the QK waves load, stage and convert unit u + 1.
@@ -162,12 +162,21 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         return U;
     };
     const int emax = (int)entry_stride - 1;        // entries are clamped into the cache on use
+    // Unit order: block b runs on XCD b % 8 (round-robin dispatch), so the
+    // G/8 blocks of one XCD take G/8 consecutive units at a time and tokens
+    // that share window and selected rows meet in that XCD's L2.
+    const int G = gridDim.x;
+    const bool xcd_order = (G & 7) == 0;
+    const int G8 = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    auto unit_at = [&](int i) -> int {
+        return xcd_order ? ((i * 8 + xcd) * G8 + slot) : (int)blockIdx.x + i * G;
+    };
 
     if (qk_wave) {
         // ======================= QK waves ==================================
         const int h = 16 * q4 + n16;
         const uint32_t sel_g = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
-        for (int u = blockIdx.x, up = 0; u < nunits; u += gridDim.x, up ^= 1) {
+        for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
             const Unit U = unit_of(u);
             const int k_begin = U.k_begin, k_end = U.k_end, nwch = U.nwch, nwin = U.nwin;
             const int ncmp = U.ncmp, slot0 = U.slot0;
@@ -429,7 +438,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     } else {
         // ======================= PV waves ==================================
         const int p4 = q4;
-        for (int u = blockIdx.x, up = 0; u < nunits; u += gridDim.x, up ^= 1) {
+        for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
             const Unit U = unit_of(u);
             const int k_begin = U.k_begin, k_end = U.k_end, nwch = U.nwch;
             barrier_lds();      // start(u)

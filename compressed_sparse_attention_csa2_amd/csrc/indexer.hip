@@ -431,8 +431,10 @@ struct WaveTopk {
     }
 
     // the top 512 in list order to out_j (padded with -1) and, if given, their keys;
-    // *kth_out = the 512th largest key (0 when fewer than 512 elements)
-    __device__ int finish(int32_t* out_j, uint32_t* out_key, uint32_t* kth_out) {
+    // *kth_out = the 512th largest key (0 when fewer than 512 elements); if kq_out
+    // is given, *kq_out = the kq-th largest key (0 when fewer than kq elements)
+    __device__ int finish(int32_t* out_j, uint32_t* out_key, uint32_t* kth_out,
+                          uint32_t kq = 0, uint32_t* kq_out = nullptr) {
         const int lane = threadIdx.x & 63;
         if (nc > TOPK) {
             uint32_t kr[16], krem;
@@ -449,6 +451,15 @@ struct WaveTopk {
             }
         }
         if (kth_out) *kth_out = nc == TOPK ? wave_min(mn) : 0u;
+        if (kq_out) {
+            uint32_t v = 0u;
+            if (kq > 0 && nc >= (int)kq) {
+                uint32_t kr[16], krem;
+                load_keys(ws, nc, kr);
+                v = wave_threshold(ws, kr, kq, 0, true, &krem);
+            }
+            *kq_out = v;
+        }
         return nc;
     }
 };
@@ -511,11 +522,14 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
         const int c = st.finish(idx + row * TOPK, nullptr, nullptr);
         if (lane == 0) cnt[row] = c;
     } else {
-        uint32_t kth;
-        const int c = st.finish(seg_j + item * TOPK, seg_key + item * TOPK, &kth);
+        // the segment's 512th and ceil(512 / nseg)-th largest keys bound the merge
+        uint32_t kth, kqv;
+        const int c = st.finish(seg_j + item * TOPK, seg_key + item * TOPK, &kth,
+                                (uint32_t)((TOPK + nseg - 1) / nseg), &kqv);
         if (lane == 0) {
             seg_n[item] = c;
-            seg_kth[item] = kth;
+            seg_kth[2 * item] = kth;
+            seg_kth[2 * item + 1] = kqv;
         }
     }
 }
@@ -532,7 +546,15 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * WS_WAVES + wave;
     if (row >= rows) return;
-    const uint32_t bound = wave_max(lane < nseg ? seg_kth[row * nseg + lane] : 0u);
+    // Lower bounds of the row's 512th largest key: the largest of the segments'
+    // 512th keys (that segment alone holds 512 keys at or above it), and, when
+    // every segment holds at least q = ceil(512 / nseg) keys, the smallest of
+    // their q-th keys (together the segments hold nseg * q >= 512 keys at or
+    // above it).  Keys below the larger bound cannot be selected.
+    const uint32_t kth_s = lane < nseg ? seg_kth[2 * (row * nseg + lane)] : 0u;
+    const uint32_t kq_s = lane < nseg ? seg_kth[2 * (row * nseg + lane) + 1] : 0xFFFFFFFFu;
+    const uint32_t kq_min = wave_min(kq_s);
+    const uint32_t bound = max(wave_max(kth_s), kq_min);
     WaveTopk st{sel[wave], 0, bound > 0u ? bound - 1u : 0u};
     // each segment's 512 slots in one step: two 256-element groups, vector loads
     auto fetch = [&](int s, uint4 (&kv)[2], int4 (&jv)[2]) {
