@@ -224,7 +224,7 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     const dim3 grid((unsigned)nblk);
     const int ht = H / 16;   // head tiles of 16
 #define CSA2_ATTN(HTV)                                                                         \
-    hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(512), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
+    hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(ATT_THREADS), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
                        w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
                        rope_rows, O, lse, L.nsplit, pO, pml)
     switch (ht) {

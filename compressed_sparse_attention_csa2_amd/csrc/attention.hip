@@ -39,7 +39,6 @@
 namespace csa2 {
 
 constexpr int CH = 32;                 // rows per chunk
-constexpr int ATT_THREADS = 512;       // 8 waves
 constexpr float LAZY_TAU = 32.0f;      // log2 headroom before the running max is moved
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -117,12 +116,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     __shared__ float sinkl[64];               // sink of head h
     __shared__ float ropel[2][2][PAIRS];      // [unit parity][cos, sin] of the token's position
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
+    int lane = tid & 63;            // re-derived opaquely per QK chunk (see there)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     // roles: waves 0..3 stage the rows and take QK and the softmax for heads
-    // 16q..16q+15 (q = wave); waves 4..7 take the bf16 copy and PV for channels
-    // 128p..128p+127 (p = wave - 4).  Wave w and w + 4 share a SIMD.
+    // 16q..16q+15 (q = wave); waves 4..11 take the bf16 copy and PV for channels
+    // 64p..64p+63 (p = wave - 4).  Each SIMD holds one QK wave and two PV waves.
     const bool qk_wave = wave < 4;
     const int q4 = wave & 3;
     const bool qk_on = HT == 4 || q4 < HT;
@@ -317,6 +317,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             auto chunk = [&](int k, auto win_c) {
                 constexpr bool WIN = decltype(win_c)::value;
                 constexpr int RB = WIN ? 512 : 256;      // row bytes
+                // lane coordinates re-derived per chunk: keeps the per-lane
+                // offsets below (and in the copies) from being held across the loop
+                asm volatile("" : "+v"(lane));
+                const int n16 = lane & 15, g = lane >> 4;
                 const int buf = k & 1, rbuf = k % NRAW;
                 const int base = WIN ? k * CH : (k - nwch) * CH;
                 const int nv = min((WIN ? nwin : ncmp) - base, CH);
@@ -325,24 +329,34 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const uint8_t* rrow1 = &rawc[rbuf][(16 + n16) * RB];
                 f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = f4{0.f, 0.f, 0.f, 0.f};
                 float rs0[4] = {1.f, 1.f, 1.f, 1.f}, rs1[4] = {1.f, 1.f, 1.f, 1.f};
+                // entries of chunk k+3 read now: their latency overlaps the products
+                int e0 = 0, e1 = 0, e2 = 0;
+                chunk_entries(k + NRAW - 1, e0, e1, e2);
                 // the products go first on the SIMD: the softmax waits on them
                 __builtin_amdgcn_s_setprio(2);
                 if (qk_on) {
                     if constexpr (WIN) {
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
+                        // operands of block m + 1 are read while block m multiplies
+                        auto ld = [&](int m, i8& a0, i8& a1) {
                             const int u0 = 16 * ((8 * m + g) ^ n16), u1 = 16 * ((8 * m + 4 + g) ^ n16);
                             const uint4 x0 = *(const uint4*)(rrow0 + u0), x1 = *(const uint4*)(rrow0 + u1);
                             const uint4 y0 = *(const uint4*)(rrow1 + u0), y1 = *(const uint4*)(rrow1 + u1);
-                            const i8 a0 = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                             (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                            const i8 a1 = i8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
-                                             (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+                            a0 = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                            a1 = i8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+                        };
+                        i8 a0, a1;
+                        ld(0, a0, a1);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            i8 b0, b1;
+                            if (m < 3) ld(m + 1, b0, b1);
                             const int sh = (int)((qsh >> (8 * m)) & 0xFFu), sl = (int)((qsl >> (8 * m)) & 0xFFu);
                             acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qh[m], acc0, 0, 0, 0, 127, 0, sh);
                             acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qh[m], acc1, 0, 0, 0, 127, 0, sh);
                             acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, ql[m], acc0, 0, 0, 0, 127, 0, sl);
                             acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, ql[m], acc1, 0, 0, 0, 127, 0, sl);
+                            __builtin_amdgcn_sched_barrier(0);
+                            if (m < 3) { a0 = b0; a1 = b1; }
                         }
                         const float4 r0 = *(const float4*)&rscl[rbuf][4 * g];
                         const float4 r1 = *(const float4*)&rscl[rbuf][16 + 4 * g];
@@ -362,6 +376,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                             const uint4 x = *(const uint4*)(rrow0 + uu), y = *(const uint4*)(rrow1 + uu);
                             const i8 a0 = i8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
                             const i8 a1 = i8{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+                            if (m == 1) __builtin_amdgcn_sched_barrier(0);
                             const int sh = (int)((qsh >> (8 * m)) & 0xFFu), sl = (int)((qsl >> (8 * m)) & 0xFFu);
                             const int sa0 = (int)((zs0v >> (8 * m)) & 0xFFu), sa1 = (int)((zs1v >> (8 * m)) & 0xFFu);
                             acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qh[m], acc0, 4, 0, 0, sa0, 0, sh);
@@ -374,11 +389,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 __builtin_amdgcn_s_setprio(0);
                 // this wave's copies of chunk k+3 while the products run; raw
                 // buffer (k + NRAW - 1) % NRAW held chunk k - 1, read before B(k-1)
-                {
-                    int e0 = 0, e1 = 0, e2 = 0;
-                    chunk_entries(k + NRAW - 1, e0, e1, e2);
-                    dma_chunk(k + NRAW - 1, true, e0, e1, e2);
-                }
+                dma_chunk(k + NRAW - 1, true, e0, e1, e2);
                 // ---- softmax: wave-local running maximum with headroom --------
                 if (qk_on) {
                     float s[8];
@@ -437,19 +448,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         }
     } else {
         // ======================= PV waves ==================================
-        const int p4 = q4;
+        const int p8 = wave - 4;
         for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
             const Unit U = unit_of(u);
             const int k_begin = U.k_begin, k_end = U.k_end, nwch = U.nwch;
             barrier_lds();      // start(u)
 
-            f4 oacc[8][HT];                 // O^T tiles: [channel tile][head tile]
+            f4 oacc[4][HT];                 // O^T tiles: [channel tile][head tile]
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+            for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] = f4{0.f, 0.f, 0.f, 0.f};
 
-            // PV of chunk kp: O^T[128p + 16ct + .., heads] += G^T P^T over its
+            // PV of chunk kp: O^T[64p + 16ct + .., heads] += G^T P^T over its
             // 32 rows, after scaling by the chunk's row corrections
             auto pv = [&](int kp) {
                 const int bp = kp & 1;
@@ -460,7 +471,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 for (int ht = 0; ht < HT; ++ht) resc |= cr[ht] != 1.0f;
                 if (__any(resc)) {
 #pragma unroll
-                    for (int ct = 0; ct < 8; ++ct)
+                    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                         for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] *= cr[ht];
                 }
@@ -474,8 +485,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const uint16_t* gbb = &Gb[bp][rb2 * D];
                 const int swa = gb_swz(ra_), swb = gb_swz(rb2);
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    const int c0 = 128 * p4 + 16 * ct;
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int c0 = 64 * p8 + 16 * ct;
                     const int uu = (c0 >> 3) + (sq >> 1);
                     const int off = 4 * (sq & 1);
                     const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gba + 8 * (uu ^ swa) + off));
@@ -486,7 +497,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht], oacc[ct][ht], 0, 0, 0);
                 }
             };
-            // bf16 copy of channels 128p..128p+127 of chunk k's 32 rows: written
+            // bf16 copy of channels 64p..64p+63 of chunk k's 32 rows: written
             // and read by this wave only.  Lane (row r = l & 31, half l >> 5).
             auto dequant = [&](int k) {
                 const int buf = k & 1, rbuf = k % NRAW;
@@ -494,11 +505,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 uint16_t* grow = &Gb[buf][r * D];
                 const int gsw = gb_swz(r);
                 if (k < nwch) {
-                    // window row: 16 channels per 16 bytes of E4M3; units 8p + 4 half + j
+                    // window row: 16 channels per 16 bytes of E4M3; units 4p + 2 half + j
                     const uint8_t* rrow = &rawc[rbuf][r * 512];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int uq = 8 * p4 + 4 * (lane >> 5) + j;
+                    for (int j = 0; j < 2; ++j) {
+                        const int uq = 4 * p8 + 2 * (lane >> 5) + j;
                         const uint4 x = *(const uint4*)(rrow + 16 * (uq ^ r15));
                         const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
                                                     fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y));
@@ -508,26 +519,21 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         *(uint4*)(grow + 8 * ((2 * uq + 1) ^ gsw)) = hi;
                     }
                 } else {
-                    // compressed row: 32 channels per 16 bytes of E2M1, one E8M0 byte each
+                    // compressed row: 32 channels per 16 bytes of E2M1, one E8M0 byte
                     const uint8_t* rrow = &rawc[rbuf][r * 256];
-                    const uint32_t zw = *(const uint32_t*)((const uint8_t*)&zsc[rbuf][r][0] + 4 * p4);
+                    const int uq = 2 * p8 + (lane >> 5);
+                    const float sc = e8m0_to_f32(((const uint8_t*)&zsc[rbuf][r][0])[uq]);
+                    const uint4 x = *(const uint4*)(rrow + 16 * (uq ^ r15));
+                    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int bq = 2 * (lane >> 5) + j;       // block within the quarter
-                        const int uq = 4 * p4 + bq;
-                        const float sc = e8m0_to_f32((zw >> (8 * bq)) & 0xFFu);
-                        const uint4 x = *(const uint4*)(rrow + 16 * (uq ^ r15));
-                        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                        for (int k2 = 0; k2 < 4; ++k2) {
-                            const uint32_t w = w4[k2];
-                            const uint4 v = make_uint4(
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
-                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
-                            *(uint4*)(grow + 8 * ((4 * uq + k2) ^ gsw)) = v;
-                        }
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        const uint32_t w = w4[k2];
+                        const uint4 v = make_uint4(
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+                        *(uint4*)(grow + 8 * ((4 * uq + k2) ^ gsw)) = v;
                     }
                 }
             };
@@ -541,11 +547,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             barrier_lds();      // final(u): the QK waves' m, l
 
             // ---- output ------------------------------------------------------
-            // normalised O of head h, channels 128p..+127, goes through this
-            // wave's own bf16 row buffers (256 bytes per head) to be written as
-            // contiguous 256-byte segments
-            // head hh's 256 bytes sit at row hh & 31 of buffer hh >> 5, bytes 256p..
-            uint8_t* const stage = (uint8_t*)&Gb[0][0] + 256 * p4;
+            // normalised O of head h, channels 64p..+63, goes through this
+            // wave's own bf16 row buffers (128 bytes per head) to be written as
+            // contiguous 128-byte segments
+            // head hh's 128 bytes sit at row hh & 31 of buffer hh >> 5, bytes 128p..
+            uint8_t* const stage = (uint8_t*)&Gb[0][0] + 128 * p8;
             uint8_t* const st_w = stage + n16 * (D * 2) + 8 * g;   // lane's writes: head 16ht + n16
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
@@ -558,8 +564,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     const float den = l * em + __builtin_amdgcn_exp2f(shv - M);
                     const float f = em / den;
 #pragma unroll
-                    for (int ct = 0; ct < 8; ++ct) {
-                        const int d0 = 128 * p4 + 16 * ct + 4 * g;
+                    for (int ct = 0; ct < 4; ++ct) {
+                        const int d0 = 64 * p8 + 16 * ct + 4 * g;
                         float o[4] = {oacc[ct][ht][0] * f, oacc[ct][ht][1] * f, oacc[ct][ht][2] * f,
                                       oacc[ct][ht][3] * f};
                         if (d0 >= ROPE_LO) {
@@ -577,27 +583,28 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         *(uint2*)(st_w + (ht >> 1) * (CH * D * 2) + (ht & 1) * 16 * (D * 2) + 32 * ct) =
                             make_uint2(w0v, w1v);
                     }
-                    if (lse && p4 == 0 && g == 0)
+                    if (lse && p8 == 0 && g == 0)
                         lse[((int64_t)U.b * H + hh) * Tq + U.t] = (M + log2f(den)) * 0.6931471805599453f;
                 } else {
                     const int64_t pbase = ((int64_t)U.row * nsplit + U.split) * H + hh;
                     float* po = part_O + pbase * D;
 #pragma unroll
-                    for (int ct = 0; ct < 8; ++ct) *(f4*)(po + 128 * p4 + 16 * ct + 4 * g) = oacc[ct][ht];
-                    if (p4 == 0 && g == 0) {
+                    for (int ct = 0; ct < 4; ++ct) *(f4*)(po + 64 * p8 + 16 * ct + 4 * g) = oacc[ct][ht];
+                    if (p8 == 0 && g == 0) {
                         part_ml[pbase * 2] = m;          // log2 units
                         part_ml[pbase * 2 + 1] = l;
                     }
                 }
             }
             if (nsplit == 1) {
-                // 16 lanes per head, 16 bytes each: four heads (4i + l/16) per store
-                const uint8_t* st_r = stage + g * (D * 2) + 16 * n16;
-                uint16_t* orow = O + (((int64_t)U.b * H + g) * Tq + U.t) * D + 128 * p4 + 8 * n16;
-                const int64_t ostep = (int64_t)4 * Tq * D;
+                // 8 lanes per head, 16 bytes each: eight heads (8i + l/8) per store
+                const int hl = lane >> 3, c8 = lane & 7;
+                const uint8_t* st_r = stage + hl * (D * 2) + 16 * c8;
+                uint16_t* orow = O + (((int64_t)U.b * H + hl) * Tq + U.t) * D + 64 * p8 + 8 * c8;
+                const int64_t ostep = (int64_t)8 * Tq * D;
 #pragma unroll
-                for (int i = 0; i < 16 * HT / 4; ++i) {
-                    const uint4 v = *(const uint4*)(st_r + (i >> 3) * (CH * D * 2) + (i & 7) * 4 * (D * 2));
+                for (int i = 0; i < 16 * HT / 8; ++i) {
+                    const uint4 v = *(const uint4*)(st_r + (i >> 2) * (CH * D * 2) + (i & 3) * 8 * (D * 2));
                     *(uint4*)(orow + i * ostep) = v;
                 }
             }

@@ -22,6 +22,7 @@ constexpr int DI = 128;         // indexer width
 constexpr int KI_ROPE_LO = 64;  // rotated channels of an index key: 64..127
 constexpr int TOPK = 512;
 constexpr int IDX_CHUNK = 2048;  // index entries scanned by one wave of the score kernel
+constexpr int ATT_THREADS = 768; // attention block: 4 QK waves + 8 PV waves
 
 typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(4))) float f4;

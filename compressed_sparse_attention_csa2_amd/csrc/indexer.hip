@@ -143,9 +143,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
         kc = *(const uint4*)(kbase + (int64_t)j * 64);
         sw = *(const uint32_t*)(sbase + (int64_t)j * 4);
     };
-    // Four tile buffers rotate: the codes and scales of a tile are loaded three
-    // tiles before their products (loads are clamped to the chunk, so always
-    // issued), and no buffer is copied, so no wait lands on a load just issued.
+    // loads are clamped to the chunk, so always issued
     auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
         const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
         const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
@@ -192,28 +190,27 @@ __global__ void __launch_bounds__(256) k_index_scores(
             }
         }
     };
-    uint4 kb0, kb1, kb2, kb3;
-    uint32_t sb0, sb1, sb2, sb3;
-    load(0, kb0, sb0);
-    load(16, kb1, sb1);
-    load(32, kb2, sb2);
+    // NB tile buffers rotate (eight for the single-token scan, whose registers
+    // allow it): tile jt + 16p lives in buffer p % NB and is loaded NB - 1 tiles
+    // ahead; no buffer is copied, so no wait lands on a load just issued.
+    constexpr int NB = TOK == 1 ? 8 : 4;
+    uint4 kb[NB];
+    uint32_t sb[NB];
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load(16 * p, kb[p], sb[p]);
     int jt = 0;
-    for (; jt + 64 <= j_len; jt += 64) {
-        load(jt + 48, kb3, sb3);
-        step(jt, kb0, sb0);
-        load(jt + 64, kb0, sb0);
-        step(jt + 16, kb1, sb1);
-        load(jt + 80, kb1, sb1);
-        step(jt + 32, kb2, sb2);
-        load(jt + 96, kb2, sb2);
-        step(jt + 48, kb3, sb3);
+    for (; jt + 16 * NB <= j_len; jt += 16 * NB) {
+#pragma unroll
+        for (int p = 0; p < NB; ++p) {
+            load(jt + 16 * (p + NB - 1), kb[(p + NB - 1) % NB], sb[(p + NB - 1) % NB]);
+            step(jt + 16 * p, kb[p], sb[p]);
+        }
     }
-    // up to four tiles left: three already in kb0, kb1, kb2
-    if (jt + 48 < j_len) load(jt + 48, kb3, sb3);
-    if (jt < j_len) step(jt, kb0, sb0);
-    if (jt + 16 < j_len) step(jt + 16, kb1, sb1);
-    if (jt + 32 < j_len) step(jt + 32, kb2, sb2);
-    if (jt + 48 < j_len) step(jt + 48, kb3, sb3);
+    // up to NB tiles left: the first NB - 1 already in kb[0..NB-2]
+    if (jt + 16 * (NB - 1) < j_len) load(jt + 16 * (NB - 1), kb[NB - 1], sb[NB - 1]);
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+        if (jt + 16 * p < j_len) step(jt + 16 * p, kb[p], sb[p]);
 }
 
 // ---------------------------------------------------------------------------
