@@ -329,9 +329,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const uint8_t* rrow1 = &rawc[rbuf][(16 + n16) * RB];
                 f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = f4{0.f, 0.f, 0.f, 0.f};
                 float rs0[4] = {1.f, 1.f, 1.f, 1.f}, rs1[4] = {1.f, 1.f, 1.f, 1.f};
-                // entries of chunk k+3 read now: their latency overlaps the products
-                int e0 = 0, e1 = 0, e2 = 0;
-                chunk_entries(k + NRAW - 1, e0, e1, e2);
                 // the products go first on the SIMD: the softmax waits on them
                 __builtin_amdgcn_s_setprio(2);
                 if (qk_on) {
@@ -387,9 +384,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     }
                 }
                 __builtin_amdgcn_s_setprio(0);
-                // this wave's copies of chunk k+3 while the products run; raw
-                // buffer (k + NRAW - 1) % NRAW held chunk k - 1, read before B(k-1)
-                dma_chunk(k + NRAW - 1, true, e0, e1, e2);
                 // ---- softmax: wave-local running maximum with headroom --------
                 if (qk_on) {
                     float s[8];
@@ -428,11 +422,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                                               __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[6], (__bf16)pv[7]}));
                     if (g == 0) corb[buf][n16][q4] = corr;
                 }
-                // B(k): P and corrections of chunk k visible, chunk k+1 staged
-                // (k+2, k+3 may be in flight: at least one copy each)
-                if (k + 3 < k_end) barrier_vm<2>();
-                else if (k + 2 < k_end) barrier_vm<1>();
-                else barrier_vm<0>();
+                // B(k): P and corrections of chunk k visible; this wave's copies
+                // (the unit's first three chunks) complete
+                barrier_vm<0>();
             };
             const int kw = nwch < k_end ? nwch : k_end;
             for (int k = k_begin; k < kw; ++k) chunk(k, std::true_type{});
@@ -537,11 +529,56 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     }
                 }
             };
-            // phase k: PV(k-1), the bf16 copy of chunk k, then B(k)
+            // copies of chunk k (k >= k_begin + 3) into raw buffer k % NRAW: PV wave
+            // p copies rows 4p..4p+3 (the QK waves stage the first three chunks)
+            const int nwin = U.nwin, ncmp = U.ncmp, slot0 = U.slot0;
+            const uint8_t* wrow0 = w_codes + (int64_t)U.b * cap * D;
+            const float* wsc = w_scale + (int64_t)U.b * cap;
+            const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * 256;
+            const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * 16;
+            auto copy_chunk = [&](int k) {
+                if (k >= k_end) return;
+                const int buf = k % NRAW;
+                if (k < nwch) {
+                    const int base = k * CH;
+                    const int nv = min(nwin - base, CH);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int rr = 4 * p8 + 2 * h2 + (lane >> 5), j = lane & 31;
+                        int slot = slot0 + base + (rr < nv ? rr : 0);
+                        slot = slot >= cap ? slot - cap : slot;
+                        dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(j ^ (rr & 15)),
+                               lds_addr(&rawc[buf][(4 * p8 + 2 * h2) * 512]));
+                    }
+                    if (p8 == 0 && lane < CH) {
+                        int slot = slot0 + base + (lane < nv ? lane : 0);
+                        slot = slot >= cap ? slot - cap : slot;
+                        dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
+                    }
+                } else {
+                    const int base = (k - nwch) * CH;
+                    const int nv = min(ncmp - base, CH);
+                    const int rr = 4 * p8 + (lane >> 4), j = lane & 15;
+                    const int e = min(max(sidx[base + (rr < nv ? rr : 0)], 0), emax);
+                    dma16s(zc0, (uint32_t)e * 256u + 16u * (uint32_t)(j ^ (rr & 15)),
+                           lds_addr(&rawc[buf][4 * p8 * 256]));
+                    if (p8 == 0 && lane < CH) {
+                        const int e2 = min(max(sidx[base + (lane < nv ? lane : 0)], 0), emax);
+                        dma16s(zs0, (uint32_t)e2 * 16u, lds_addr(&zsc[buf][0][0]));
+                    }
+                }
+            };
+            // phase k: copies of chunk k+3 (raw buffer (k+3) % NRAW held chunk
+            // k-1, read before B(k-1)), PV(k-1), the bf16 copy of chunk k, B(k)
             for (int k = k_begin; k < k_end; ++k) {
+                copy_chunk(k + NRAW - 1);
                 if (k > k_begin) pv(k - 1);
                 dequant(k);
-                barrier_lds();
+                // B(k): chunk k+1 staged (this wave's copies of k+2, k+3 may be
+                // in flight: at least one copy each)
+                if (k + 3 < k_end) barrier_vm<2>();
+                else if (k + 2 < k_end) barrier_vm<1>();
+                else barrier_vm<0>();
             }
             if (k_end > k_begin) pv(k_end - 1);
             barrier_lds();      // final(u): the QK waves' m, l
