@@ -33,15 +33,15 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.382e10, {
-        "attention.hip": "98a39d9fd469c04a93bb806bfddaac087d6f16e69b5b6570912271ba0148db20",
-        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
-    ("k_index_scores", "prefill", 65536): (5.196e9, {
-        "indexer.hip": "9751a81ed93f08d0f72006e5c021fe19d57a9876203d411ace53239a52eaf6f9",
-        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
-    ("k_index_scores", "decode", 131072): (6.087e8, {
-        "indexer.hip": "9751a81ed93f08d0f72006e5c021fe19d57a9876203d411ace53239a52eaf6f9",
-        "csa2_device.h": "b50c96c2df70ae1482652b605a815d14fb71308bb27fd72aecce17c8314d8445"}),
+    ("k_attn", "prefill", 65536): (1.437e10, {
+        "attention.hip": "4d5770896367ad73223a9ca52c0d938ee05463088d8aeb17429ec2137bafb739",
+        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
+    ("k_index_scores", "prefill", 65536): (5.205e9, {
+        "indexer.hip": "0b13ff2d46624fe641083fc964b14873a66f5c04bad3c9a147c0476c7f5ffd25",
+        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
+    ("k_index_scores", "decode", 131072): (6.088e8, {
+        "indexer.hip": "0b13ff2d46624fe641083fc964b14873a66f5c04bad3c9a147c0476c7f5ffd25",
+        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
 }
 
 
