@@ -166,7 +166,9 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
     const int n_tg = (int)cdiv(Tq, tok);
     const int n_ch = (int)cdiv(stride, IDX_CHUNK);
     const int64_t items = (int64_t)B * n_tg * n_ch;
-    const dim3 grid((unsigned)cdiv(items, 4));
+    // four items per block; with four tokens per wave a block holds four token
+    // groups of one chunk, so the groups are padded to a multiple of four
+    const dim3 grid((unsigned)(tok == 4 ? (int64_t)B * cdiv(n_tg, 4) * n_ch : cdiv(items, 4)));
     if (tok == 1)
         hipLaunchKernelGGL(k_index_scores<1>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
                            wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);

@@ -90,11 +90,31 @@ __global__ void __launch_bounds__(256) k_index_scores(
     int64_t entry_stride, float* __restrict__ S, int64_t s_stride, int n_tg, int n_ch) {
     static_assert(TOK == 1 || TOK % 4 == 0, "token slots per wave");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= (int64_t)B * n_tg * n_ch) return;
-    const int ch = (int)(item % n_ch);
-    const int tg = n_tg - 1 - (int)((item / n_ch) % n_tg);
-    const int b = (int)(item / ((int64_t)n_ch * n_tg));
+    int b, tg, ch;
+    if (TOK == 4) {
+        // A block takes four consecutive token groups (one per wave) at one chunk,
+        // so its waves share the chunk's keys in L1.  Blocks walk the groups of four
+        // heaviest first; within them the chunk index is rotated by the group, so
+        // the blocks that land on one XCD (every eighth) see all chunk indices alike
+        // instead of always the same ones (which would give the XCDs holding the
+        // first chunks several times the work of the others).
+        const int nq = (n_tg + 3) >> 2;
+        const int64_t per_b = (int64_t)nq * n_ch;
+        const int64_t bb = blockIdx.x;
+        if (bb >= (int64_t)B * per_b) return;
+        b = (int)(bb / per_b);
+        const int64_t r = bb % per_b;
+        const int q = nq - 1 - (int)(r / n_ch);
+        ch = (int)((r % n_ch + q) % n_ch);
+        tg = 4 * q + wave;
+        if (tg >= n_tg) return;
+    } else {
+        const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+        if (item >= (int64_t)B * n_tg * n_ch) return;
+        ch = (int)(item % n_ch);
+        tg = n_tg - 1 - (int)((item / n_ch) % n_tg);
+        b = (int)(item / ((int64_t)n_ch * n_tg));
+    }
     const int t0 = tg * TOK;
     const int32_t qp = q_pos0[b], ne = n_entries[b];
     const int tlast = (t0 + TOK - 1 < Tq) ? t0 + TOK - 1 : Tq - 1;
@@ -137,6 +157,107 @@ __global__ void __launch_bounds__(256) k_index_scores(
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         Sbase, (short)0, (int)((int64_t)TOK * s_stride * 4), 0x00020000);
 
+    if constexpr (TOK == 4) {
+        // Software-pipelined form: the products of one token pair run on the matrix
+        // unit while the vector unit reduces the other pair, so one wave keeps both
+        // busy.  Per tile p:  [products of tokens 0,1 on p | head sums of tokens 2,3
+        // of p - 1, then the scatter-sum and store of p - 1]  [products of tokens
+        // 2,3 on p | head sums of tokens 0,1 of p].  Codes and scales come through
+        // buffer resources bounded to the chunk, so the tiles past its end read
+        // zeros (their stores are masked) and the tile count rounds up to groups of
+        // four, the depth of the load rotation.
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(ki_codes + ((int64_t)b * entry_stride + j_begin) * 64), (short)0, j_len * 64,
+            0x00020000);
+        const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(ki_scales + ((int64_t)b * entry_stride + j_begin) * 4), (short)0, j_len * 4,
+            0x00020000);
+        int nc = ncand[0];
+#pragma unroll
+        for (int g = 1; g < 4; ++g)
+            if (grp == g) nc = ncand[g];
+        const int lim = nc - col > 0 ? nc - col : 0;    // tile jt is stored iff jt < lim
+        int kld = col * 64 + 16 * grp;                  // code bytes of the next tile to load
+        int sld = col * 4;                              // and its entry's four block scales
+        int stv = 4 * (grp * (int)s_stride + col) - 64; // store offset of the tile before jt
+        uint4 kb[4];
+        int sb[4];
+        auto ld = [&](int p, uint4& kc, int& sc) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, kld + 1024 * p, 0, 0);
+            kc = uint4{v[0], v[1], v[2], v[3]};
+            sc = (int)__builtin_amdgcn_raw_buffer_load_b32(ksr, sld + 16 * 4 * p, 0, 0);
+        };
+        auto mm2 = [&](int k0, const uint4 kc, const int sw, f4 (&d)[2][2]) {
+            const int sc = (int)(((uint32_t)sw >> (8 * grp)) & 0xFFu);   // block grp's scale
+            const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int tile = 0; tile < 2; ++tile)
+                    d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        };
+        auto epi2 = [&](int k0, const f4 (&d)[2][2], float& sa, float& sb2) {
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a0 = __builtin_fmaf(W[k0][tile][i], relu(d[0][tile][i]), a0);
+                    a1 = __builtin_fmaf(W[k0 + 1][tile][i], relu(d[1][tile][i]), a1);
+                }
+            sa = a0;
+            sb2 = a1;
+        };
+        // lane row g holds token g's sum for entry jt + col
+        auto put = [&](int jt, int p, float s0, float s1, float s2, float s3) {
+            const float tot = rowsum_scatter4(s0, s1, s2, s3);
+            const int off = (unsigned)jt < (unsigned)lim ? stv + 64 * p : 0x7FFFFFFF;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), srs, off, 0, 0);
+        };
+        f4 dA[2][2], dB[2][2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) dB[k][tile] = f4{0.f, 0.f, 0.f, 0.f};
+        float s0 = 0.0f, s1 = 0.0f, s2, s3;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) ld(p, kb[p], sb[p]);
+        kld += 3 * 1024;
+        sld += 3 * 64;
+        auto group = [&](int g) {      // tiles 4g .. 4g + 3
+            const int jt = g * 64;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                ld(p, kb[(p + 3) & 3], sb[(p + 3) & 3]);
+                mm2(0, kb[p], sb[p], dA);
+                epi2(2, dB, s2, s3);
+                put(jt + 16 * p - 16, p, s0, s1, s2, s3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mm2(2, kb[p], sb[p], dB);
+                epi2(0, dA, s0, s1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            kld += 4096;
+            sld += 256;
+            stv += 256;
+        };
+        const int ngroups = (j_len + 63) >> 6;
+        for (int g = 0; g < ngroups; ++g) group(g);
+        epi2(2, dB, s2, s3);
+        put(ngroups * 64 - 16, 0, s0, s1, s2, s3);
+        return;
+    }
     auto load = [&](int jt, uint4& kc, uint32_t& sw) {
         int j = jt + col;
         j = j < j_len ? j : j_len - 1;
