@@ -160,7 +160,7 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
     uint8_t* q8 = base + L.q8;
     float* wq = (float*)(base + L.wq);
     const int64_t qrows = (int64_t)B * Tq * HI;
-    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 4)), dim3(256), 0, st, qI,
+    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 16)), dim3(256), 0, st, qI,
                        wI, qrows, q8, wq);
     const int tok = index_tok(Tq);
     const int n_tg = (int)cdiv(Tq, tok);
