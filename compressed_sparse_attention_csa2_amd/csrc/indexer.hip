@@ -629,6 +629,24 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
             }
         }
     };
+    // Long lists start from a threshold taken on a sample (16 runs of 64 elements
+    // spread over the list): the key th with about 1.5 * 512 * len / 1024 sample
+    // keys at or above it, so that roughly 768 list elements pass.  Elements below
+    // th are skipped.  If fewer than 512 pass, some of the top 512 were skipped and
+    // the list is streamed again from threshold 0; otherwise every skipped key is
+    // below the 512th largest, and all copies of that key were kept.
+    bool sampled = false;
+    if (len >= 4096) {
+        const int gap = (len / 16) & ~63;
+        uint32_t kr[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) kr[g] = score_key(src[g * gap + lane]);
+        const uint32_t r = (uint32_t)((768 * 1024 + len - 1) / len);
+        uint32_t krem;
+        const uint32_t th = wave_threshold(st.ws, kr, r, r + r / 2, false, &krem);
+        st.thr = th - 1u;        // keys of finite scores are >= 1
+        sampled = true;
+    }
     float4 nxt[4];
     if (len > 0) fetch(0, nxt);
     for (int base = 0; base < len; base += 1024) {
@@ -642,6 +660,19 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
             if (base + 256 * u >= len) break;
             const uint32_t k[4] = {i0 < len ? score_key(cur[u].x) : 0u, i0 + 1 < len ? score_key(cur[u].y) : 0u,
                                    i0 + 2 < len ? score_key(cur[u].z) : 0u, i0 + 3 < len ? score_key(cur[u].w) : 0u};
+            const int32_t jj[4] = {(int32_t)(j0 + i0), (int32_t)(j0 + i0 + 1), (int32_t)(j0 + i0 + 2),
+                                   (int32_t)(j0 + i0 + 3)};
+            st.push(k, jj);
+        }
+    }
+    if (sampled && st.nc < TOPK) {
+        // rare: the sample threshold was too high; a plain pass from threshold 0
+        st.nc = 0;
+        st.thr = 0u;
+        for (int base = 0; base < len; base += 256) {
+            const int i0 = base + 4 * lane;
+            const uint32_t k[4] = {i0 < len ? score_key(src[i0]) : 0u, i0 + 1 < len ? score_key(src[i0 + 1]) : 0u,
+                                   i0 + 2 < len ? score_key(src[i0 + 2]) : 0u, i0 + 3 < len ? score_key(src[i0 + 3]) : 0u};
             const int32_t jj[4] = {(int32_t)(j0 + i0), (int32_t)(j0 + i0 + 1), (int32_t)(j0 + i0 + 2),
                                    (int32_t)(j0 + i0 + 3)};
             st.push(k, jj);

@@ -280,3 +280,45 @@ def test_index_scores_match_oracle(dev, orc):
         mass = (Kabs[:n] @ (np.abs(e4[q8]).T * (np.abs(wI[0, i]) * sq)[None, :])).sum(1)
         bound = 2 * (128 + 32 + 2) * u * mass + u * np.abs(ref)
         assert np.all(err <= bound), (i, err.max(), (err / bound).max())
+
+
+@pytest.mark.parametrize("N", [4096, 8192])
+def test_topk_sampled_threshold_fallback(dev, orc, N):
+    """Lists of 4096 or more scores start from a threshold taken on a sample of
+    16 runs of 64 elements (one run every len/16 entries).  Here those runs hold
+    every large score, so fewer than 512 scores pass it and the list must be
+    streamed again from threshold 0; the selection must still be the exact top
+    512 (N=4096: one list; N=8192: two 4096-entry segments and their merge)."""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import tests.test_oracle_compress as tc
+    rng = np.random.default_rng(23)
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    pos = np.arange(N) % 4096
+    hot = (pos % 256) < 64
+    kpre = 0.3 * rng.standard_normal((N, 128)) + np.where(hot, 3.0, -3.0)[:, None] * u[None, :]
+    kc_, ks_ = orc.fp4_encode_rows_bf16(tc.bf16(kpre.astype(np.float32)))
+    qI = tc.bf16((4.0 * u[None, None, None, :]
+                  + 0.3 * rng.standard_normal((1, 1, 32, 128))).astype(np.float32))
+    wI = (np.abs(rng.standard_normal((1, 1, 32))) / 64).astype(np.float32)
+    q0 = 2 * N - 1
+    q8, sq = orc.quant_index_query(qI[0, 0])
+    S = orc.index_scores(q8, sq, wI[0, 0], kc_, ks_, N)
+    # the construction does what it is for: in each 4096-entry list the sample's
+    # 192nd largest score (the rank the kernel aims at) has fewer than 512 above it
+    for s0 in range(0, N, 4096):
+        seg = S[s0:s0 + 4096]
+        smp = np.sort(seg[(np.arange(16)[:, None] * 256 + np.arange(64)[None, :]).ravel()])
+        assert np.count_nonzero(seg >= smp[-192]) < 512
+    log(f"csa2_index_topk sampled-threshold fallback: N={N}")
+    idx = torch.full((1, 1, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((1, 1), -7, dtype=torch.int32, device=dev)
+    ws = csa2.workspace(csa2.OP_INDEX_TOPK, 1, 1, 64, N)
+    csa2.csa2_index_topk(_up(np.array([q0], np.int32)), _up(np.array([N], np.int32)), _up(qI),
+                         _up(wI), _up(kc_[None]), _up(ks_[None]), idx, cnt, ws)
+    torch.cuda.synchronize()
+    r_idx, r_cnt = orc.topk(S, N)
+    swaps = check_selection(_down(idx)[0, 0], _down(cnt)[0, 0], r_idx, r_cnt, S)
+    assert np.all(hot[r_idx[:r_cnt]])
+    log(f"  swaps={swaps}")
