@@ -383,6 +383,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         }
                     }
                 }
+                // the products are consumed here, so they cannot sink below the
+                // priority drop (the compiler may move arithmetic across it)
+                asm volatile("" : "+v"(acc0), "+v"(acc1));
                 __builtin_amdgcn_s_setprio(0);
                 // ---- softmax: wave-local running maximum with headroom --------
                 if (qk_on) {
