@@ -576,7 +576,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             for (int k = k_begin; k < k_end; ++k) {
                 copy_chunk(k + NRAW - 1);
                 if (k > k_begin) pv(k - 1);
+                // the bf16 copy ends this wave's phase, after the MFMA work of
+                // the SIMD's other waves: it goes first on the SIMD
+                __builtin_amdgcn_s_setprio(1);
                 dequant(k);
+                __builtin_amdgcn_s_setprio(0);
                 // B(k): chunk k+1 staged (this wave's copies of k+2, k+3 may be
                 // in flight: at least one copy each)
                 if (k + 3 < k_end) barrier_vm<2>();
