@@ -33,14 +33,14 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.437e10, {
-        "attention.hip": "4d5770896367ad73223a9ca52c0d938ee05463088d8aeb17429ec2137bafb739",
+    ("k_attn", "prefill", 65536): (1.378e10, {
+        "attention.hip": "b54d9a72e389bf5e547df631f6fed7ce0e957000c407e646b28f219699239cc0",
         "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
-    ("k_index_scores", "prefill", 65536): (5.205e9, {
-        "indexer.hip": "0b13ff2d46624fe641083fc964b14873a66f5c04bad3c9a147c0476c7f5ffd25",
+    ("k_index_scores", "prefill", 65536): (7.070e9, {
+        "indexer.hip": "ac89264b8e797f5177620911e6dca238fb43deb22fe51ed84e3d4e8b72ad13f6",
         "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
     ("k_index_scores", "decode", 131072): (6.088e8, {
-        "indexer.hip": "0b13ff2d46624fe641083fc964b14873a66f5c04bad3c9a147c0476c7f5ffd25",
+        "indexer.hip": "ac89264b8e797f5177620911e6dca238fb43deb22fe51ed84e3d4e8b72ad13f6",
         "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
 }
 
