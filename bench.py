@@ -275,6 +275,30 @@ def run_decode(args, result, stream):
                          "traffic": measured_traffic("k_index_scores", "decode",
                                                      dwl.q_pos0 + 1)},
         }
+        # decode append (one new token per request, half of them closing a pair):
+        # window row, pair buffer, entry of a completed pair, into the same caches
+        import compressed_sparse_attention_csa2_amd as csa2
+        B = dwl.B
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=gen).to(torch.bfloat16)
+        a_kc, a_gc, a_wn, a_ki = rnd(B, 512), rnd(B, 512), rnd(B, 512), rnd(B, 128)
+        a_pkc, a_pgc = rnd(B, 512), rnd(B, 512)
+        a_pos = torch.tensor([dwl.q_pos0 - (b & 1) for b in range(B)], dtype=torch.int32,
+                             device="cuda")
+        a_gamma = torch.ones(512, dtype=torch.float32, device="cuda")
+        append = lambda: csa2.csa2_append(a_pos, a_kc, a_gc, a_wn, a_pkc, a_pgc, a_gamma, None,
+                                          None, a_ki, drun.rope_cos, drun.rope_sin, drun.z_codes,
+                                          drun.z_scales, drun.ki_codes, drun.ki_scales,
+                                          drun.w_codes, drun.w_scale)
+        append()
+        ams = time_events(append, args.steps, stream)
+        log(f"decode append: {ams * 1e3:.2f} us per call (B={B})")
+        result["decode"]["append"] = {
+            "workload": f"csa2_append B={B}: one token per request at position 131071 or "
+                        "131070 (half close a pair), given index keys",
+            "us_per_call": ams * 1e3,
+            "bytes_per_call": B * (3 * 1024 + 2 * 1024 + 256 + 516 + 340 / 2),
+            "bound": "launch latency (one block of two waves per request)"}
         del drun
         torch.cuda.empty_cache()
 

@@ -43,6 +43,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.csa2_compress.argtypes = [i32, i32] + [vp] * 9 + [i64] + [vp] * 4 + [i64, vp]
         L.csa2_encode_window.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, vp, i32, vp]
+        L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, vp, vp, i32, vp]
         L.csa2_index_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, vp, sz, vp]
         L.csa2_index_scores.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, sz, vp]
         L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64] +
@@ -127,6 +128,22 @@ def csa2_encode_window(pos0, wn, rope_cos, rope_sin, w_codes, w_scale, stream=No
                                     _p(w_scale, "f32", "w_scale"), w_codes.shape[1],
                                     _stream(stream)), "csa2_encode_window")
 
+
+
+def csa2_append(pos, kc, gc, wn, pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
+                rope_sin, z_codes, z_scales, ki_codes, ki_scales, w_codes, w_scale, stream=None):
+    B = kc.shape[0]
+    _check(lib().csa2_append(B, _p(pos, "i32", "pos"), _p(kc, "bf16", "kc"), _p(gc, "bf16", "gc"),
+                             _p(wn, "bf16", "wn"), _p(pair_kc, "bf16", "pair_kc"),
+                             _p(pair_gc, "bf16", "pair_gc"), _p(gamma_c, "f32", "gamma_c"),
+                             _p(w_ik, "bf16", "w_ik"), _p(gamma_ik, "f32", "gamma_ik"),
+                             _p(ki_given, "bf16", "ki_given"), _p(rope_cos, "f32", "rope_cos"),
+                             _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
+                             _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
+                             _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
+                             z_codes.shape[1], _p(w_codes, "u8", "w_codes"),
+                             _p(w_scale, "f32", "w_scale"), w_codes.shape[1], _stream(stream)),
+           "csa2_append")
 
 def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws, stream=None):
     B, Tq = qI.shape[0], qI.shape[1]

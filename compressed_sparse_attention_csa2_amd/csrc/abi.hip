@@ -17,6 +17,10 @@ __global__ void k_compress(int, int, const int32_t*, const uint16_t*, const uint
                            uint8_t*, int64_t);
 __global__ void k_window_encode(int, int, const int32_t*, const uint16_t*, const float*,
                                 const float*, int64_t, uint8_t*, float*, int);
+__global__ void k_append(int, const int32_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                         uint16_t*, uint16_t*, const float*, const uint16_t*, const float*,
+                         const uint16_t*, const float*, const float*, int64_t, uint8_t*, uint8_t*,
+                         uint8_t*, uint8_t*, int64_t, uint8_t*, float*, int);
 __global__ void k_encode_fp4_rows(const uint16_t*, int64_t, int, uint8_t*, uint8_t*);
 __global__ void k_encode_fp8_rows(const uint16_t*, int64_t, int, uint8_t*, float*);
 __global__ void k_decode_fp4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
@@ -312,6 +316,30 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
     hipLaunchKernelGGL(k_window_encode, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, S(stream),
                        B, T, pos0, wn, rope_cos, rope_sin, rope_rows, w_codes, w_scale, cap);
     csa2_status s = check_launch("csa2_encode_window");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uint16_t* gc,
+                        const uint16_t* wn, uint16_t* pair_kc, uint16_t* pair_gc,
+                        const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
+                        const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
+                        int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
+                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride,
+                        uint8_t* w_codes, float* w_scale, int cap, void* stream) {
+    if (B < 0 || entry_stride < 1 || cap < 1)
+        return fail(CSA2_ERR_SHAPE, "append: B=%d stride=%lld cap=%d", B, (long long)entry_stride, cap);
+    if (!pos || !kc || !gc || !wn || !pair_kc || !pair_gc || !gamma_c || !rope_cos || !rope_sin ||
+        !z_codes || !z_scales || !ki_codes || !ki_scales || !w_codes || !w_scale)
+        return fail(CSA2_ERR_NULL, "append: a required pointer is NULL");
+    if (w_ik ? !gamma_ik : !ki_given)
+        return fail(CSA2_ERR_NULL, "append: need w_ik+gamma_ik (derive) or ki_given (given)");
+    if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "append: empty rotary table");
+    if (B == 0) return ok();
+    hipLaunchKernelGGL(k_append, dim3((unsigned)B), dim3(128), 0, S(stream), B, pos, kc, gc, wn,
+                       pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
+                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, w_codes,
+                       w_scale, cap);
+    csa2_status s = check_launch("csa2_append");
     return s == CSA2_OK ? ok() : s;
 }
 

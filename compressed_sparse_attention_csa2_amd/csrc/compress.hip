@@ -24,34 +24,23 @@
 
 namespace csa2 {
 
-// One wave (64 lanes) per compressed entry.  Lane l owns channels 8l..8l+7 of
-// the 512-wide row; for the 128-wide index key it owns channels 2l, 2l+1.
-__global__ void __launch_bounds__(256) k_compress(
-    int B, int T, const int32_t* __restrict__ pos0, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ gc, const float* __restrict__ gamma_c,
-    const uint16_t* __restrict__ w_ik, const float* __restrict__ gamma_ik,
-    const uint16_t* __restrict__ ki_given, const float* __restrict__ rcos,
-    const float* __restrict__ rsin, int64_t rope_rows, uint8_t* __restrict__ z_codes,
+// Entry j of request b from its two tokens' rows (pooled keys ka, kb and gate
+// logits ga, gb; 512 bf16 each), on one wave: lane l owns channels 8l..8l+7 of
+// the 512-wide row and channels 2l, 2l+1 of the 128-wide index key.  ki_row is
+// the given index key (128 bf16) when w_ik is NULL.  c_lds and ki_lds are this
+// wave's scratch rows in LDS (512 and 128 floats).
+__device__ __forceinline__ void compress_entry(
+    int b, int64_t j, int lane, const uint16_t* __restrict__ ka_row,
+    const uint16_t* __restrict__ kb_row, const uint16_t* __restrict__ ga_row,
+    const uint16_t* __restrict__ gb_row, const uint16_t* __restrict__ ki_row,
+    const float* __restrict__ gamma_c, const uint16_t* __restrict__ w_ik,
+    const float* __restrict__ gamma_ik, const float* __restrict__ cs,
+    const float* __restrict__ sn, float* c_lds, float* ki_lds, uint8_t* __restrict__ z_codes,
     uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
     uint8_t* __restrict__ ki_scales, int64_t entry_stride) {
-    __shared__ float c_lds[4][D];
-    __shared__ float ki_lds[4][DI];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nloc = T / 2;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= (int64_t)B * nloc) return;
-    const int b = (int)(item / nloc), jl = (int)(item % nloc);
-    const int64_t j = (int64_t)(pos0[b] >> 1) + jl;
-    if (j < 0 || j >= entry_stride) return;
-    int64_t prow = 2 * j;
-    if (prow >= rope_rows) prow = rope_rows - 1;
-    const float* cs = rcos + prow * PAIRS;
-    const float* sn = rsin + prow * PAIRS;
-
     // ---- pair gate --------------------------------------------------------
-    const int64_t r0 = ((int64_t)b * T + 2 * jl) * D + 8 * lane;
-    const uint4 ka = *(const uint4*)(kc + r0), kb = *(const uint4*)(kc + r0 + D);
-    const uint4 ga = *(const uint4*)(gc + r0), gb = *(const uint4*)(gc + r0 + D);
+    const uint4 ka = *(const uint4*)(ka_row + 8 * lane), kb = *(const uint4*)(kb_row + 8 * lane);
+    const uint4 ga = *(const uint4*)(ga_row + 8 * lane), gb = *(const uint4*)(gb_row + 8 * lane);
     const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w}, kbw[4] = {kb.x, kb.y, kb.z, kb.w};
     const uint32_t gaw[4] = {ga.x, ga.y, ga.z, ga.w}, gbw[4] = {gb.x, gb.y, gb.z, gb.w};
     float kp[8];
@@ -118,19 +107,19 @@ __global__ void __launch_bounds__(256) k_compress(
     float kn0, kn1;
     if (w_ik) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c_lds[wave][8 * lane + i] = c[i];
+        for (int i = 0; i < 8; ++i) c_lds[8 * lane + i] = c[i];
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         float acc0 = 0.0f, acc1 = 0.0f;
         const uint32_t* W = (const uint32_t*)w_ik;   // [512][64] pairs of bf16
         for (int k = 0; k < D; ++k) {
             const uint32_t wv = W[k * (DI / 2) + lane];
-            const float ck = c_lds[wave][k];
+            const float ck = c_lds[k];
             acc0 = __builtin_fmaf(ck, bf2f((uint16_t)wv), acc0);
             acc1 = __builtin_fmaf(ck, bf2f((uint16_t)(wv >> 16)), acc1);
         }
-        ki_lds[wave][2 * lane] = acc0;
-        ki_lds[wave][2 * lane + 1] = acc1;
+        ki_lds[2 * lane] = acc0;
+        ki_lds[2 * lane + 1] = acc1;
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         // RMSNorm over 128: group g = lane < 16 holds channels 8g..8g+7
@@ -138,7 +127,7 @@ __global__ void __launch_bounds__(256) k_compress(
         if (lane < 16) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float x = ki_lds[wave][8 * lane + i];
+                const float x = ki_lds[8 * lane + i];
                 p2 = __builtin_fmaf(x, x, p2);
             }
         }
@@ -159,8 +148,7 @@ __global__ void __launch_bounds__(256) k_compress(
             kn1 = e + f;
         }
     } else {
-        const uint32_t v =
-            *(const uint32_t*)(ki_given + ((int64_t)b * nloc + jl) * DI + 2 * lane);
+        const uint32_t v = *(const uint32_t*)(ki_row + 2 * lane);
         kn0 = bf2f((uint16_t)v);
         kn1 = bf2f((uint16_t)(v >> 16));
     }
@@ -177,19 +165,43 @@ __global__ void __launch_bounds__(256) k_compress(
     }
 }
 
-// One wave per window row: rotate at its position, FP8 row encode into the ring.
-__global__ void __launch_bounds__(256) k_window_encode(
-    int B, int T, const int32_t* __restrict__ pos0, const uint16_t* __restrict__ wn,
-    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t rope_rows,
-    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap) {
+// One wave (64 lanes) per compressed entry of the call's token pairs.
+__global__ void __launch_bounds__(256) k_compress(
+    int B, int T, const int32_t* __restrict__ pos0, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ gc, const float* __restrict__ gamma_c,
+    const uint16_t* __restrict__ w_ik, const float* __restrict__ gamma_ik,
+    const uint16_t* __restrict__ ki_given, const float* __restrict__ rcos,
+    const float* __restrict__ rsin, int64_t rope_rows, uint8_t* __restrict__ z_codes,
+    uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
+    uint8_t* __restrict__ ki_scales, int64_t entry_stride) {
+    __shared__ float c_lds[4][D];
+    __shared__ float ki_lds[4][DI];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nloc = T / 2;
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= (int64_t)B * T) return;
-    const int b = (int)(item / T), i = (int)(item % T);
-    const int64_t p = (int64_t)pos0[b] + i;
-    if (p < 0) return;
-    int64_t prow = p < rope_rows ? p : rope_rows - 1;
-    const uint4 v = *(const uint4*)(wn + item * D + 8 * lane);
+    if (item >= (int64_t)B * nloc) return;
+    const int b = (int)(item / nloc), jl = (int)(item % nloc);
+    const int64_t j = (int64_t)(pos0[b] >> 1) + jl;
+    if (j < 0 || j >= entry_stride) return;
+    int64_t prow = 2 * j;
+    if (prow >= rope_rows) prow = rope_rows - 1;
+    const int64_t r0 = ((int64_t)b * T + 2 * jl) * D;
+    compress_entry(b, j, lane, kc + r0, kc + r0 + D, gc + r0, gc + r0 + D,
+                   w_ik ? nullptr : ki_given + ((int64_t)b * nloc + jl) * DI, gamma_c, w_ik,
+                   gamma_ik, rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds[wave], ki_lds[wave],
+                   z_codes, z_scales, ki_codes, ki_scales, entry_stride);
+}
+
+// One window row on one wave: the 512 bf16 of wrow rotated at position p
+// (rotary row prow) and written as E4M3FN codes plus one fp32 scale to ring
+// slot `slot` (an index over [B][cap]).  Lane l owns channels 8l..8l+7.
+__device__ __forceinline__ void window_row(int64_t slot, int64_t prow, int lane,
+                                           const uint16_t* __restrict__ wrow,
+                                           const float* __restrict__ rcos,
+                                           const float* __restrict__ rsin,
+                                           uint8_t* __restrict__ w_codes,
+                                           float* __restrict__ w_scale) {
+    const uint4 v = *(const uint4*)(wrow + 8 * lane);
     const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
     float x[8];
 #pragma unroll
@@ -218,9 +230,67 @@ __global__ void __launch_bounds__(256) k_window_encode(
 #pragma unroll
         for (int k = 0; k < 4; ++k) hi |= e4m3_code(div_rn(x[k + 4], scale)) << (8 * k);
     }
-    const int64_t slot = (int64_t)b * cap + (p % cap);
     *(uint2*)(w_codes + slot * D + 8 * lane) = make_uint2(lo, hi);
     if (lane == 0) w_scale[slot] = scale;
+}
+
+// One wave per window row: rotate at its position, FP8 row encode into the ring.
+__global__ void __launch_bounds__(256) k_window_encode(
+    int B, int T, const int32_t* __restrict__ pos0, const uint16_t* __restrict__ wn,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t rope_rows,
+    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)B * T) return;
+    const int b = (int)(item / T), i = (int)(item % T);
+    const int64_t p = (int64_t)pos0[b] + i;
+    if (p < 0) return;
+    const int64_t prow = p < rope_rows ? p : rope_rows - 1;
+    window_row((int64_t)b * cap + (p % cap), prow, lane, wn + item * D, rcos, rsin, w_codes,
+               w_scale);
+}
+
+// Decode append: one new token per request at absolute position pos[b].  Its
+// window row goes to ring slot pos mod cap.  A token at an even position opens
+// a pair: its pooled key and gate logits wait in the pair buffer.  A token at
+// an odd position closes the pair 2j, 2j+1 (j = pos / 2): entry j is computed
+// from the buffered token and this one, exactly as the prefill path computes it.
+// One block of two waves per request: wave 0 the window row, wave 1 the pair.
+__global__ void __launch_bounds__(128) k_append(
+    int B, const int32_t* __restrict__ pos, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ gc, const uint16_t* __restrict__ wn,
+    uint16_t* __restrict__ pair_kc, uint16_t* __restrict__ pair_gc,
+    const float* __restrict__ gamma_c, const uint16_t* __restrict__ w_ik,
+    const float* __restrict__ gamma_ik, const uint16_t* __restrict__ ki_given,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t rope_rows,
+    uint8_t* __restrict__ z_codes, uint8_t* __restrict__ z_scales,
+    uint8_t* __restrict__ ki_codes, uint8_t* __restrict__ ki_scales, int64_t entry_stride,
+    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap) {
+    __shared__ float c_lds[D];
+    __shared__ float ki_lds[DI];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int b = blockIdx.x;
+    if (b >= B) return;
+    const int64_t p = pos[b];
+    if (p < 0) return;
+    const int64_t row = (int64_t)b * D;
+    if (wave == 0) {
+        const int64_t prow = p < rope_rows ? p : rope_rows - 1;
+        window_row((int64_t)b * cap + (p % cap), prow, lane, wn + row, rcos, rsin, w_codes,
+                   w_scale);
+    } else if ((p & 1) == 0) {
+        *(uint4*)(pair_kc + row + 8 * lane) = *(const uint4*)(kc + row + 8 * lane);
+        *(uint4*)(pair_gc + row + 8 * lane) = *(const uint4*)(gc + row + 8 * lane);
+    } else {
+        const int64_t j = p >> 1;
+        if (j >= entry_stride) return;
+        int64_t prow = 2 * j;
+        if (prow >= rope_rows) prow = rope_rows - 1;
+        compress_entry(b, j, lane, pair_kc + row, kc + row, pair_gc + row, gc + row,
+                       w_ik ? nullptr : ki_given + (int64_t)b * DI, gamma_c, w_ik, gamma_ik,
+                       rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds, ki_lds, z_codes,
+                       z_scales, ki_codes, ki_scales, entry_stride);
+    }
 }
 
 // FP4 rows: one thread per 32-element block.

@@ -111,6 +111,40 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
                                uint8_t* w_codes, float* w_scale, int cap, void* stream);
 
 /*
+ * Decode append: one new token per request [atlas, cache note "between
+ * forward calls": the window ring of 128 slots, the compressed and index-key
+ * rows of the pairs seen so far, and the pooling source's pair buffer of two
+ * tensors (pooled keys, gate logits) of 512].  For request b the token at
+ * absolute position p = pos[b]:
+ *   - its window vector is rotated at p and written to ring slot p mod cap,
+ *     as csa2_encode_window does;
+ *   - p even: the token opens pair p/2; its pooled key and gate logits are
+ *     copied to the pair buffer (pair_kc[b], pair_gc[b]) and no entry is written;
+ *   - p odd: the token closes pair j = p/2 with the token held in the pair
+ *     buffer; entry j is computed from (buffer, new token) exactly as
+ *     csa2_compress computes it from two tokens of one call, so appending
+ *     tokens one at a time writes the same bytes as compressing them together.
+ *     Rows j >= entry_stride are skipped.
+ *  pos        [B] int32 device, >= 0 (a negative position skips the request).
+ *  kc, gc, wn [B][512] bf16: the new token's pooled key, gate logits, window vector.
+ *  pair_kc, pair_gc [B][512] bf16 device, caller-owned state carried between
+ *             calls.  After a prefill of odd length the caller seeds them
+ *             with the last token's kc and gc (or appends that token here).
+ *  ki_given   [B][128] bf16 given index key of the entry an odd token closes
+ *             (read only for odd positions, only when w_ik == NULL).
+ *  Other arguments as for csa2_compress and csa2_encode_window.  Requests
+ *  are independent; two calls on one stream are ordered, so the pair buffer
+ *  written by one call is read by the next.
+ */
+csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uint16_t* gc,
+                        const uint16_t* wn, uint16_t* pair_kc, uint16_t* pair_gc,
+                        const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
+                        const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
+                        int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
+                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride,
+                        uint8_t* w_codes, float* w_scale, int cap, void* stream);
+
+/*
  * Lightning indexer and causal top-512 [atlas: S^I_{t,j} = sum_h w^I_{t,h}
  * ReLU(Q^I_{h,t} . K^I_j); I_t = top_512(S^I_{t,j} : j < floor((t+1)/2));
  * blog: 32 heads of 128, one key per entry].
