@@ -253,6 +253,50 @@ def topk(S, n, k=TOPK):
     return idx, cnt
 
 
+
+# Hierarchical candidate pool ("Inside DeepSeek V4.1", the Hierarchical Sparse
+# Indexer paragraph; "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV
+# Cache", section "Hierarchical indexing bounds the later searches"): blocks of
+# 8 entries, 2,048 blocks (16,384 candidates) kept, the newest block always.
+POOL_BLOCK, POOL_BLOCKS = 8, 2048
+
+
+def pool_blocks(S, n, block=POOL_BLOCK, keep=POOL_BLOCKS):
+    """Blocks of the candidate pool, ascending.  Entries 0..n-1 are cut into
+    blocks of `block` (the last one may be short); a block's key is the largest
+    index score in it.  The pool holds the block with the newest entry (n-1)
+    and, of the other blocks, the keep-1 with the largest keys (ties: the
+    smaller block) -- every block when there are at most `keep`."""
+    S = np.asarray(S, np.float32)
+    nb = (n + block - 1) // block
+    if nb <= keep:
+        return np.arange(nb, dtype=np.int32)
+    keys = [float(S[b * block:min(n, (b + 1) * block)].max()) for b in range(nb - 1)]
+    ranked = sorted(range(nb - 1), key=lambda b: (-keys[b], b))
+    return np.array(sorted(ranked[:keep - 1]) + [nb - 1], np.int32)
+
+
+def pool_entries(pool, n, block=POOL_BLOCK):
+    """Entries of the pool's blocks below n, ascending."""
+    if len(pool) == 0:
+        return np.zeros(0, np.int64)
+    return np.concatenate([np.arange(b * block, min(n, (b + 1) * block), dtype=np.int64)
+                           for b in pool])
+
+
+def reindex_topk(q8, sq, w, ki_codes, ki_scales, n, pool, block=POOL_BLOCK, k=TOPK):
+    """Reindex selection: the layer's own index query scores only the pool's
+    candidates against the shared index keys and keeps the top k of them with
+    the rule of topk (score desc, entry asc), in ascending order, -1 padded.
+    Returns (idx, cnt, candidates, their scores)."""
+    cand = pool_entries(pool, n, block)
+    Sc = index_scores(q8, sq, w, np.ascontiguousarray(ki_codes[cand]),
+                      np.ascontiguousarray(ki_scales[cand]), len(cand))
+    pos, cnt = topk(Sc, len(cand), k)
+    idx = np.full(k, -1, np.int32)
+    idx[:cnt] = cand[pos[:cnt]]
+    return idx, cnt, cand, Sc
+
 def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t):
     """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512]"""
     A = _Args()
