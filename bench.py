@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "pool", "copy"], default=None,
                     help="time a single workload (for profiling runs); 'copy' runs a plain "
                          "1 GiB device copy, the calibration kernel for the HBM byte counters")
     ap.add_argument("--no-cpu", action="store_true")
@@ -178,9 +178,9 @@ def main():
                           "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
-    if args.only == "decode":
+    if args.only in ("decode", "pool"):
         args.no_cpu = True
-        run_decode(args, result, stream)
+        (run_decode if args.only == "decode" else run_pool)(args, result, stream)
         print(json.dumps(result), flush=True)
         return
     # ---------------------------------------------------------------- prefill
@@ -235,6 +235,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode and args.only is None:
         run_decode(args, result, stream)
+        run_pool(args, result, stream)
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu:
@@ -290,8 +291,9 @@ def run_decode(args, result, stream):
                                           None, a_ki, drun.rope_cos, drun.rope_sin, drun.z_codes,
                                           drun.z_scales, drun.ki_codes, drun.ki_scales,
                                           drun.w_codes, drun.w_scale)
-        append()
-        ams = time_events(append, args.steps, stream)
+        for _ in range(max(args.warmup, 3)):
+            append()
+        ams = time_events(append, max(args.steps, 20), stream)
         log(f"decode append: {ams * 1e3:.2f} us per call (B={B})")
         result["decode"]["append"] = {
             "workload": f"csa2_append B={B}: one token per request at position 131071 or "
@@ -301,6 +303,71 @@ def run_decode(args, result, stream):
             "bound": "launch latency (one block of two waves per request)"}
         del drun
         torch.cuda.empty_cache()
+
+
+
+def run_pool(args, result, stream):
+    """Hierarchical pool and Reindex at the verify-decode shape (B=16 x 6 queries
+    at 1,048,570.., 524,288 entries): the Full layer's scan with and without the
+    pool, and a Reindex layer's selection over the pool only."""
+    import torch
+    import csa2_harness
+    import csa2_synth as synth
+    import compressed_sparse_attention_csa2_amd as csa2
+    wl = synth.workload(4)
+    B, Tq, N = wl.B, wl.Tq, wl.n_entries
+    log(f"generating index keys: {wl.name}")
+    t0 = time.time()
+    u8 = torch.uint8
+    kc = torch.zeros(B, N, 64, dtype=u8, device="cuda")
+    ks = torch.zeros(B, N, 4, dtype=u8, device="cuda")
+    for b in range(B):
+        for j0 in range(0, N, 1 << 16):
+            n = min(1 << 16, N - j0)
+            k = csa2_harness.up(wl.ki_rows(b, j0, n))
+            csa2.csa2_encode_fp4_rows(k, kc[b, j0:j0 + n].view(n, 64), ks[b, j0:j0 + n].view(n, 4))
+            del k
+    qI, wI = csa2_harness.up(wl.qI()), csa2_harness.up(wl.wI())
+    qI2 = csa2_harness.up(synth.normal(wl.seed, 901, (B, Tq, 32, 128)))     # a Reindex layer's query
+    wI2 = csa2_harness.up(synth.normal(wl.seed, 902, (B, Tq, 32), mul=1.0 / 64.0, dtype="f32"))
+    q0 = torch.full((B,), wl.q_pos0, dtype=torch.int32, device="cuda")
+    ne = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    i32 = torch.int32
+    idx = torch.empty(B, Tq, 512, dtype=i32, device="cuda")
+    cnt = torch.empty(B, Tq, dtype=i32, device="cuda")
+    pool = torch.empty(B, Tq, csa2.POOL_BLOCKS, dtype=i32, device="cuda")
+    pcnt = torch.empty(B, Tq, dtype=i32, device="cuda")
+    idx2, cnt2 = torch.empty_like(idx), torch.empty_like(cnt)
+    ws_t = csa2.workspace(csa2.OP_INDEX_TOPK, B, Tq, 64, N)
+    ws_p = csa2.workspace(csa2.OP_INDEX_POOL, B, Tq, 64, N)
+    ws_r = csa2.workspace(csa2.OP_REINDEX, B, Tq, 64, N)
+    torch.cuda.synchronize()
+    log(f"index keys resident ({time.time() - t0:.1f} s)")
+    full = lambda: csa2.csa2_index_topk(q0, ne, qI, wI, kc, ks, idx, cnt, ws_t)
+    fpool = lambda: csa2.csa2_index_pool(q0, ne, qI, wI, kc, ks, idx, cnt, pool, pcnt, ws_p)
+    reidx = lambda: csa2.csa2_reindex_topk(q0, ne, qI2, wI2, kc, ks, pool, pcnt, idx2, cnt2, ws_r)
+    for f in (full, fpool, reidx):
+        f()
+    torch.cuda.synchronize()
+    t_full = time_events(full, args.steps, stream)
+    t_pool = time_events(fpool, args.steps, stream)
+    t_re = time_events(reidx, args.steps, stream)
+    rows = B * Tq
+    cand = float(pcnt.sum().item()) * 8
+    log(f"pool: full select {t_full:.4f} ms, with pool {t_pool:.4f} ms, reindex {t_re:.4f} ms")
+    gather = cand * 68.0                   # the pool's index keys, gathered per query row
+    result["hierarchical"] = {
+        "workload": f"verify-decode shape: B={B} x {Tq} queries at {wl.q_pos0}.., {N} entries "
+                    "(lognormal keys, 1% exact duplicates); Full layer with the pool, then a "
+                    "Reindex layer's own query over the pool",
+        "full_select_ms": t_full, "full_select_with_pool_ms": t_pool, "reindex_select_ms": t_re,
+        "candidates_per_row": {"full": N, "reindex": cand / rows},
+        "reindex_roofline": {"bound": "hbm", "bytes_per_launch": gather,
+                             "achieved": gather / (t_re * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                             "unit": "GB/s", "frac": gather / (t_re * 1e-3) / PEAK_HBM},
+    }
+    del kc, ks, ws_t, ws_p, ws_r
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

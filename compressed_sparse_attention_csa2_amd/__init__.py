@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 D, WINDOW, HI, DI, TOPK = 512, 128, 32, 128, 512
-OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_SCORES = 1, 2, 3, 4
+OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_SCORES, OP_INDEX_POOL, OP_REINDEX = 1, 2, 3, 4, 5, 6
+POOL_BLOCKS = 2048
 
 _lib = None
 
@@ -46,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, vp, vp, i32, vp]
         L.csa2_index_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, vp, sz, vp]
         L.csa2_index_scores.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, sz, vp]
+        L.csa2_index_pool.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
+        L.csa2_reindex_topk.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
         L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64] +
                                        [vp] * 5 + [i64, vp, vp, vp, sz, vp])
         L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, vp, vp,
@@ -155,6 +158,34 @@ def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "csa2_index_topk")
 
+
+
+def csa2_index_pool(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, pool, pool_cnt, ws,
+                    stream=None):
+    B, Tq = qI.shape[0], qI.shape[1]
+    _check(lib().csa2_index_pool(B, Tq, _p(q_pos0, "i32", "q_pos0"),
+                                 _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
+                                 _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
+                                 _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                 _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
+                                 _p(pool, "i32", "pool"), _p(pool_cnt, "i32", "pool_cnt"),
+                                 _p(ws, None, "ws"), ws.numel() * ws.element_size(),
+                                 _stream(stream)),
+           "csa2_index_pool")
+
+
+def csa2_reindex_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, pool, pool_cnt, idx, cnt,
+                      ws, stream=None):
+    B, Tq = qI.shape[0], qI.shape[1]
+    _check(lib().csa2_reindex_topk(B, Tq, _p(q_pos0, "i32", "q_pos0"),
+                                   _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
+                                   _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
+                                   _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                   _p(pool, "i32", "pool"), _p(pool_cnt, "i32", "pool_cnt"),
+                                   _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
+                                   _p(ws, None, "ws"), ws.numel() * ws.element_size(),
+                                   _stream(stream)),
+           "csa2_reindex_topk")
 
 def csa2_index_scores(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, scores, ws, stream=None):
     B, Tq = qI.shape[0], qI.shape[1]

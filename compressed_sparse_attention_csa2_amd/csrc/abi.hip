@@ -32,7 +32,16 @@ __global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const u
                                const float*, const uint8_t*, const uint8_t*, int64_t, float*,
                                int64_t, int, int);
 __global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int64_t,
-                       int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*, uint32_t*);
+                       int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*, uint32_t*,
+                       const int32_t*);
+__global__ void k_block_keys(int, int, const int32_t*, const int32_t*, int64_t, const float*,
+                             int64_t, uint32_t*, int64_t);
+__global__ void k_pool_select(int, int, const int32_t*, const int32_t*, int64_t, const uint32_t*,
+                              int64_t, int32_t*, int32_t*);
+__global__ void k_pool_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                              const float*, const uint8_t*, const uint8_t*, int64_t,
+                              const int32_t*, const int32_t*, float*, int64_t, int32_t*);
+__global__ void k_pool_map(int64_t, const int32_t*, int32_t*);
 __global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const int32_t*,
                              const uint32_t*, int32_t*, int32_t*);
 template <int HG>
@@ -133,6 +142,36 @@ IndexWs index_ws(int B, int Tq, int64_t stride) {
     return w;
 }
 
+// Full-layer selection with the hierarchical pool: the index workspace, then
+// the block keys [rows][ceil(stride / 8)].
+struct PoolWs {
+    IndexWs ix;
+    size_t keys, total;
+    int64_t kpad;
+};
+PoolWs pool_ws(int B, int Tq, int64_t stride) {
+    PoolWs w;
+    w.ix = index_ws(B, Tq, stride);
+    w.kpad = cdiv(cdiv(stride, 8), 4) * 4;   // rows of keys 16-byte aligned
+    w.keys = w.ix.total;
+    w.total = w.keys + align256((size_t)B * Tq * (size_t)w.kpad * sizeof(uint32_t));
+    return w;
+}
+// Reindex: an index workspace for lists of the pool's 16,384 candidates, then
+// the lists' lengths [rows].
+constexpr int64_t POOL_CAND = (int64_t)POOL_BLOCKS * 8;
+struct ReindexWs {
+    IndexWs ix;
+    size_t len, total;
+};
+ReindexWs reindex_ws(int B, int Tq) {
+    ReindexWs w;
+    w.ix = index_ws(B, Tq, POOL_CAND);
+    w.len = w.ix.total;
+    w.total = w.len + align256((size_t)B * Tq * sizeof(int32_t));
+    return w;
+}
+
 struct AttnWs {
     int nsplit;
     size_t pO, pml, total;
@@ -202,7 +241,7 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     uint32_t* seg_kth = (uint32_t*)((uint8_t*)ws + L.seg_kth);
     hipLaunchKernelGGL(k_topk, dim3((unsigned)cdiv(rows * nseg, 4)), dim3(256), 0, st, B, Tq,
                        q_pos0, n_entries, Sc, pitch, stride, nseg, seg_len, idx, cnt, seg_key,
-                       seg_j, seg_n, seg_kth);
+                       seg_j, seg_n, seg_kth, (const int32_t*)nullptr);
     if (nseg > 1)
         hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
                            (int)rows, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
@@ -273,6 +312,8 @@ size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride) {
     if (bad_sizes(B, Tq, entry_stride)) return 0;
     if (op == CSA2_OP_INDEX_TOPK) return index_ws(B, Tq, entry_stride).total;
     if (op == CSA2_OP_INDEX_SCORES) return index_ws(B, Tq, entry_stride).S;
+    if (op == CSA2_OP_INDEX_POOL) return pool_ws(B, Tq, entry_stride).total;
+    if (op == CSA2_OP_REINDEX) return reindex_ws(B, Tq).total;
     if (H < 16 || H > 64 || H % 16) return 0;
     if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H).total;
     if (op == CSA2_OP_FORWARD) {
@@ -355,6 +396,80 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
                                  entry_stride, idx, cnt, ws, S(stream));
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                            const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
+                            int32_t* cnt, int32_t* pool, int32_t* pool_cnt, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_pool: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt || !pool ||
+        !pool_cnt)
+        return fail(CSA2_ERR_NULL, "index_pool: a required pointer is NULL");
+    const PoolWs L = pool_ws(B, Tq, entry_stride);
+    if (Tq > 0 && (!ws || ws_bytes < L.total))
+        return fail(CSA2_ERR_WORKSPACE, "index_pool: workspace %zu < %zu bytes", ws_bytes, L.total);
+    if (Tq == 0) return ok();
+    hipStream_t st = S(stream);
+    csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
+                                 entry_stride, idx, cnt, ws, st);
+    if (s != CSA2_OK) return s;
+    const float* Sc = (const float*)((uint8_t*)ws + L.ix.S);
+    uint32_t* keys = (uint32_t*)((uint8_t*)ws + L.keys);
+    const int64_t rows = (int64_t)B * Tq;
+    hipLaunchKernelGGL(k_block_keys, dim3((unsigned)cdiv(rows * L.kpad, 256)), dim3(256), 0, st, B,
+                       Tq, q_pos0, n_entries, entry_stride, Sc, score_pitch(entry_stride), keys,
+                       L.kpad);
+    hipLaunchKernelGGL(k_pool_select, dim3((unsigned)rows), dim3(256), 0, st, B, Tq, q_pos0,
+                       n_entries, entry_stride, keys, L.kpad, pool, pool_cnt);
+    s = check_launch("csa2_index_pool");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                              const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                              const uint8_t* ki_scales, int64_t entry_stride, const int32_t* pool,
+                              const int32_t* pool_cnt, int32_t* idx, int32_t* cnt, void* ws,
+                              size_t ws_bytes, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "reindex_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !pool || !pool_cnt ||
+        !idx || !cnt)
+        return fail(CSA2_ERR_NULL, "reindex_topk: a required pointer is NULL");
+    const ReindexWs L = reindex_ws(B, Tq);
+    if (Tq > 0 && (!ws || ws_bytes < L.total))
+        return fail(CSA2_ERR_WORKSPACE, "reindex_topk: workspace %zu < %zu bytes", ws_bytes, L.total);
+    if (Tq == 0) return ok();
+    hipStream_t st = S(stream);
+    uint8_t* base = (uint8_t*)ws;
+    uint8_t* q8 = base + L.ix.q8;
+    float* wq = (float*)(base + L.ix.wq);
+    float* Sc = (float*)(base + L.ix.S);
+    int32_t* len = (int32_t*)(base + L.len);
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t qrows = rows * HI;
+    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 16)), dim3(256), 0, st, qI,
+                       wI, qrows, q8, wq);
+    const int64_t pitch = score_pitch(POOL_CAND);
+    hipLaunchKernelGGL(k_pool_scores, dim3((unsigned)cdiv(rows * (POOL_BLOCKS / 128), 4)),
+                       dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8, wq, ki_codes, ki_scales,
+                       entry_stride, pool, pool_cnt, Sc, pitch, len);
+    const int nseg = topk_segments(rows, POOL_CAND);
+    const int seg_len = topk_seg_len(POOL_CAND, nseg);
+    uint32_t* seg_key = (uint32_t*)(base + L.ix.seg_key);
+    int32_t* seg_j = (int32_t*)(base + L.ix.seg_j);
+    int32_t* seg_n = (int32_t*)(base + L.ix.seg_n);
+    uint32_t* seg_kth = (uint32_t*)(base + L.ix.seg_kth);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)cdiv(rows * nseg, 4)), dim3(256), 0, st, B, Tq,
+                       q_pos0, n_entries, Sc, pitch, POOL_CAND, nseg, seg_len, idx, cnt, seg_key,
+                       seg_j, seg_n, seg_kth, (const int32_t*)len);
+    if (nseg > 1)
+        hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
+                           (int)rows, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
+    hipLaunchKernelGGL(k_pool_map, dim3((unsigned)cdiv(rows * TOPK, 256)), dim3(256), 0, st, rows,
+                       pool, idx);
+    csa2_status s = check_launch("csa2_reindex_topk");
     return s == CSA2_OK ? ok() : s;
 }
 

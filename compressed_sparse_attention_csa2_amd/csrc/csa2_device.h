@@ -21,6 +21,7 @@ constexpr int HI = 32;          // indexer heads
 constexpr int DI = 128;         // indexer width
 constexpr int KI_ROPE_LO = 64;  // rotated channels of an index key: 64..127
 constexpr int TOPK = 512;
+constexpr int POOL_BLOCKS = 2048;  // blocks of 8 entries kept by the hierarchical pool
 constexpr int IDX_CHUNK = 2048;  // index entries scanned by one wave of the score kernel
 constexpr int ATT_THREADS = 768; // attention block: 4 QK waves + 8 PV waves
 

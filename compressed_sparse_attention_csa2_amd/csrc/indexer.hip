@@ -600,7 +600,8 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const float* __restrict__ S, int64_t spad, int64_t entry_stride, int nseg, int seg_len,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, uint32_t* __restrict__ seg_key,
-    int32_t* __restrict__ seg_j, int32_t* __restrict__ seg_n, uint32_t* __restrict__ seg_kth) {
+    int32_t* __restrict__ seg_j, int32_t* __restrict__ seg_n, uint32_t* __restrict__ seg_kth,
+    const int32_t* __restrict__ row_len) {
     __shared__ WaveSel sel[WS_WAVES];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * WS_WAVES + wave;
@@ -608,7 +609,10 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
     const int64_t row = item / nseg;
     const int seg = (int)(item - row * nseg);
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
-    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    // the list is the row's causal candidates, or (row_len given) its first
+    // row_len[row] scores, e.g. the candidates of a hierarchical pool
+    int64_t n = row_len ? (int64_t)row_len[row] : cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    if (n > (int64_t)nseg * seg_len) n = (int64_t)nseg * seg_len;
     const int64_t j0 = (int64_t)seg * seg_len;
     int len = (int)(n - j0 < seg_len ? n - j0 : seg_len);
     len = len < 0 ? 0 : len;
@@ -748,6 +752,274 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
     }
     const int c = st.finish(idx + row * TOPK, nullptr, nullptr);
     if (lane == 0) cnt[row] = c;
+}
+
+// ---------------------------------------------------------------------------
+// Hierarchical candidate pool and Reindex selection.  "Inside DeepSeek V4.1"
+// (the Hierarchical Sparse Indexer paragraph) and "Inside DeepSeek V4.1 Flash:
+// Deriving the 890-Byte KV Cache" (section "Hierarchical indexing bounds the
+// later searches"): the Full layer's scores are grouped into blocks of 8
+// entries ranked by their best score; 2,048 blocks (16,384 candidates) are
+// kept, the block holding the newest entry always; Reindex layers score only
+// the pool with their own index query and take their own top 512.
+// ---------------------------------------------------------------------------
+
+// key[row][k] = largest order-preserving key of the scores of entries
+// 8k..8k+7 below n(row); one thread per (row, block).
+__global__ void __launch_bounds__(256) k_block_keys(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    int64_t entry_stride, const float* __restrict__ S, int64_t spad,
+    uint32_t* __restrict__ keys, int64_t kpad) {
+    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (item >= (int64_t)B * Tq * kpad) return;
+    const int64_t row = item / kpad;
+    const int64_t k = item - row * kpad;
+    const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    if (8 * k >= n) return;
+    const float* src = S + row * spad + 8 * k;        // 32-byte aligned (spad % 64 == 0)
+    const float4 a = *(const float4*)src, c = *(const float4*)(src + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    const int m = n - 8 * k < 8 ? (int)(n - 8 * k) : 8;
+    uint32_t best = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < m) best = max(best, score_key(v[i]));
+    keys[row * kpad + k] = best;
+}
+
+// Block-wide (256 threads) exclusive prefix sum: DPP scans within the waves,
+// the four wave totals through LDS.  Returns the block total in *tot.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wsum, uint32_t* tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_scan_add(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t x = wsum[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    __syncthreads();
+    *tot = all;
+    return before + inc - v;
+}
+
+// The pool of each query row, one block of 256 threads per row: every block
+// when there are at most POOL_BLOCKS, else the newest block plus the
+// POOL_BLOCKS - 1 others with the largest keys (ties: the smaller block).  A
+// radix select (8 bits per pass, the bits common to all keys skipped) finds
+// the threshold key K and how many copies of it are kept; a pass over the keys
+// in tiles of 1024 (4 consecutive keys per thread, block scans for the output
+// offsets) writes the kept blocks in ascending order.  Key rows are padded to
+// a multiple of 4 for the 16-byte loads.
+__global__ void __launch_bounds__(256) k_pool_select(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    int64_t entry_stride, const uint32_t* __restrict__ keys, int64_t kpad,
+    int32_t* __restrict__ pool, int32_t* __restrict__ pool_cnt) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t bc[4];
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    if (row >= (int64_t)B * Tq) return;
+    const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int nb = (int)((n + 7) / 8);
+    int32_t* out = pool + row * POOL_BLOCKS;
+    if (nb <= POOL_BLOCKS) {
+        for (int i = tid; i < POOL_BLOCKS; i += 256) out[i] = i < nb ? i : -1;
+        if (tid == 0) pool_cnt[row] = nb;
+        return;
+    }
+    const int m = nb - 1;                          // blocks other than the newest
+    const uint4* kr4 = (const uint4*)(keys + row * kpad);
+    const int ntile = (m + 1023) / 1024;
+    const uint32_t r = POOL_BLOCKS - 1;            // how many of them are kept
+    auto load4 = [&](int c, uint32_t (&k)[4]) {   // keys 1024c + 4 tid .. +3; 0 past m
+        const int i = 1024 * c + 4 * tid;
+        const uint4 v = i < m ? kr4[(i >> 2)] : make_uint4(0u, 0u, 0u, 0u);
+        k[0] = v.x; k[1] = i + 1 < m ? v.y : 0u; k[2] = i + 2 < m ? v.z : 0u; k[3] = i + 3 < m ? v.w : 0u;
+    };
+    // keys are >= 1 for every real block, so 0 marks "none"
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll 8
+    for (int c = 0; c < ntile; ++c) {
+        uint32_t k[4];
+        load4(c, k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (k[q] != 0u) lo = min(lo, k[q]);
+            hi = max(hi, k[q]);
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((tid & 63) == 0) { hist[tid >> 6] = lo; hist[4 + (tid >> 6)] = hi; }
+    __syncthreads();
+    lo = min(min(hist[0], hist[1]), min(hist[2], hist[3]));
+    hi = max(max(hist[4], hist[5]), max(hist[6], hist[7]));
+    __syncthreads();
+    uint32_t K = hi, krem = r, eq_total = (uint32_t)m;   // all keys equal
+    if (lo < hi) {
+        int hib = 31 - __clz((int)(lo ^ hi));
+        uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
+        uint32_t prefix = lo & pmask;
+        while (hib >= 0) {
+            const int lob = hib - 7 > 0 ? hib - 7 : 0;
+            const uint32_t dmask = (2u << (hib - lob)) - 1u;
+            hist[tid] = 0u;
+            __syncthreads();
+#pragma unroll 8
+            for (int c = 0; c < ntile; ++c) {
+                uint32_t k[4];
+                load4(c, k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k[q] != 0u && (k[q] & pmask) == prefix) atomicAdd(&hist[(k[q] >> lob) & dmask], 1u);
+            }
+            __syncthreads();
+            // digit holding the krem-th largest: bins in descending order, one per thread
+            const int nbins = (int)dmask + 1;
+            const uint32_t h = tid < nbins ? hist[nbins - 1 - tid] : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_excl_sum(h, wsum, &tot);
+            if (tid < nbins && ex < krem && krem <= ex + h) {
+                bc[0] = (uint32_t)(nbins - 1 - tid);
+                bc[1] = ex;
+                bc[2] = h;
+            }
+            __syncthreads();
+            prefix |= bc[0] << lob;
+            pmask |= dmask << lob;
+            krem -= bc[1];
+            eq_total = bc[2];
+            hib = lob - 1;
+            __syncthreads();
+        }
+        K = prefix;
+    }
+    // kept: every key > K and the first krem keys == K in block order
+    const bool all_eq = krem >= eq_total;
+    uint32_t written = 0u, eq_seen = 0u;
+    uint32_t kn[4];
+    load4(0, kn);
+    for (int c = 0; c < ntile; ++c) {
+        uint32_t k[4] = {kn[0], kn[1], kn[2], kn[3]};
+        if (c + 1 < ntile) load4(c + 1, kn);       // next tile in flight during the scans
+        uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gt += k[q] > K;
+            eq += k[q] == K;
+        }
+        uint32_t take = eq;
+        if (!all_eq) {
+            uint32_t eq_tot;
+            const uint32_t eq_ex = block_excl_sum(eq, wsum, &eq_tot);
+            const uint32_t rank0 = eq_seen + eq_ex;
+            take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+            eq_seen += eq_tot;
+        }
+        uint32_t sel_tot;
+        uint32_t off = written + block_excl_sum(gt + take, wsum, &sel_tot);
+        uint32_t taken = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool keep = k[q] > K || (k[q] == K && taken < take);
+            if (keep) {
+                out[off++] = 1024 * c + 4 * tid + q;
+                taken += k[q] == K;
+            }
+        }
+        written += sel_tot;
+    }
+    if (tid == 0) {
+        out[POOL_BLOCKS - 1] = m;                  // the newest block, largest index
+        pool_cnt[row] = POOL_BLOCKS;
+    }
+}
+
+// Reindex scores: the row's own index query against the pool's candidates,
+// written as a list in pool order (entry 8 pool[s] + e at position 8 s + e).
+// One wave per (row, 128 pool slots); a 16-entry tile is two pool blocks.
+// row_len[row] = the list's length: every pool block is full except the
+// newest, the last one.
+__global__ void __launch_bounds__(256) k_pool_scores(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_cnt,
+    float* __restrict__ Sc, int64_t scpad, int32_t* __restrict__ row_len) {
+    constexpr int SLOTS = 128;
+    constexpr int NPC = POOL_BLOCKS / SLOTS;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)B * Tq * NPC) return;
+    const int64_t row = item / NPC;
+    const int pc = (int)(item - row * NPC);
+    const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int cntp = pool_cnt[row];
+    const int64_t nb = (n + 7) / 8;
+    if (pc == 0 && lane == 0) row_len[row] = cntp > 0 ? (int32_t)(n - 8 * (nb - cntp)) : 0;
+    const int s_begin = pc * SLOTS;
+    if (s_begin >= cntp) return;
+    const int s_end = min(s_begin + SLOTS, cntp);
+    const int col = lane & 15, grp = lane >> 4;
+    i8 A[2];
+    f4 W[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        const int64_t qrow = ((int64_t)b * Tq + t) * HI + tile * 16;
+        const uint8_t* src = q8 + (qrow + col) * DI + 16 * grp;
+        const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 64);
+        A[tile] = i8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        const float4 w4 = *(const float4*)(wq + qrow + 4 * grp);
+        W[tile] = f4{w4.x, w4.y, w4.z, w4.w};
+    }
+    const int32_t* prow = pool + row * POOL_BLOCKS;
+    const int64_t ebase = (int64_t)b * entry_stride;
+    auto load = [&](int s0, uint4& kc, uint32_t& sw) {
+        const int s = s0 + (col >> 3);
+        const int blk = s < s_end ? prow[s] : 0;
+        int64_t e = 8 * (int64_t)blk + (col & 7);
+        e = e < n ? e : n - 1;                     // past the list: any valid entry, not stored
+        kc = *(const uint4*)(ki_codes + (ebase + e) * 64 + 16 * grp);
+        sw = *(const uint32_t*)(ki_scales + (ebase + e) * 4);
+    };
+    uint4 kc_n;
+    uint32_t sw_n;
+    load(s_begin, kc_n, sw_n);
+    for (int s0 = s_begin; s0 < s_end; s0 += 2) {
+        const uint4 kc = kc_n;
+        const uint32_t sw = sw_n;
+        if (s0 + 2 < s_end) load(s0 + 2, kc_n, sw_n);
+        const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
+        const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+        const f4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        const f4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[0][i], relu(d0[i]), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[1][i], relu(d1[i]), acc);
+        const float tot = rowsum_scatter4(acc, acc, acc, acc);
+        const int pos = 8 * s0 + col;
+        if (grp == 0 && s0 + (col >> 3) < s_end) Sc[row * scpad + pos] = tot;
+    }
+}
+
+// list positions -> entries: position 8 s + e is entry 8 pool[s] + e.
+__global__ void __launch_bounds__(256) k_pool_map(int64_t rows, const int32_t* __restrict__ pool,
+                                                  int32_t* __restrict__ idx) {
+    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (item >= rows * TOPK) return;
+    const int64_t row = item / TOPK;
+    const int32_t v = idx[item];
+    if (v >= 0) idx[item] = 8 * pool[row * POOL_BLOCKS + (v >> 3)] + (v & 7);
 }
 
 template __global__ void k_index_scores<1>(int, int, const int32_t*, const int32_t*, const uint8_t*,

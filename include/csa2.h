@@ -70,6 +70,8 @@ typedef enum {
 #define CSA2_OP_SPARSE_ATTN 2
 #define CSA2_OP_FORWARD 3
 #define CSA2_OP_INDEX_SCORES 4
+#define CSA2_OP_INDEX_POOL 5
+#define CSA2_OP_REINDEX 6
 
 /*
  * Compression of new positions into the compressed cache and the index-key
@@ -162,6 +164,42 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
                             const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
                             int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Full-layer selection plus the hierarchical candidate pool [blog: the
+ * Hierarchical Sparse Indexer paragraph; zharf: section "Hierarchical indexing
+ * bounds the later searches"].  idx and cnt exactly as csa2_index_topk.  From
+ * the same scores, each query's candidates j < n are cut into blocks of 8
+ * (block k = entries 8k..8k+7, the last may be short) keyed by their largest
+ * score; the pool holds the block with the newest entry (n-1) and the 2,047
+ * other blocks with the largest keys (ties: the smaller block), i.e. every
+ * block when there are at most 2,048: at most 16,384 candidates.
+ *  pool      [B][Tq][2048] int32 out: pool blocks in ascending order, -1 padded.
+ *  pool_cnt  [B][Tq] int32 out: number of pool blocks, min(2048, ceil(n/8)).
+ *  ws        at least csa2_workspace_size(CSA2_OP_INDEX_POOL, ...) bytes.
+ */
+csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                            const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
+                            int32_t* cnt, int32_t* pool, int32_t* pool_cnt, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * Reindex selection [same passages: a Reindex layer borrows the keys and the
+ * pool, runs its own index query over the pool's candidates only, and takes
+ * its own top 512].  Scores the entries of each query's pool blocks below n
+ * with this layer's qI / wI against the shared ki cache (same arithmetic as
+ * csa2_index_topk) and keeps the 512 largest (ties: smaller entry), in
+ * ascending order, -1 padded; cnt = min(512, candidates).  The work per query
+ * is bounded by the pool (16,384 candidates), not by the context.
+ *  pool, pool_cnt  as written by csa2_index_pool for the same q_pos0 / n_entries.
+ *  ws        at least csa2_workspace_size(CSA2_OP_REINDEX, ...) bytes.
+ */
+csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                              const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                              const uint8_t* ki_scales, int64_t entry_stride, const int32_t* pool,
+                              const int32_t* pool_cnt, int32_t* idx, int32_t* cnt, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * The indexer's raw scores without selection [atlas: S^I_{t,j} = sum_h
