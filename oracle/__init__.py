@@ -68,7 +68,7 @@ def lib():
         L.orc_topk.argtypes = [vp, i64, i32, vp]
         L.orc_topk.restype = i32
         L.orc_quant_index_query.argtypes = [vp, vp, vp]
-        L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64]
         L.orc_query_rows.argtypes = [i32, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32,
                                      vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -297,8 +297,12 @@ def reindex_topk(q8, sq, w, ki_codes, ki_scales, n, pool, block=POOL_BLOCK, k=TO
     idx[:cnt] = cand[pos[:cnt]]
     return idx, cnt, cand, Sc
 
-def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t):
-    """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512]"""
+def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t,
+           w_floor=0):
+    """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512].  w_floor: the
+    start s of a bounded replay ("Inside DeepSeek V4.1 Flash: Deriving the 890-Byte
+    KV Cache", section "Bounded replay trades exact state for cheaper
+    resumption"): the window is max(s, p-127) .. p."""
     A = _Args()
     Q = c(Q, np.uint16)
     H = Q.shape[0]
@@ -308,7 +312,7 @@ def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t
     lib().orc_attend(A(Q), H, p, A(w_codes, np.uint8), A(w_scale, np.float32), cap,
                      A(z_codes, np.uint8), A(z_scales, np.uint8), A(idx, np.int32), cnt,
                      A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
-                     A(O), A(lse), A(Ob))
+                     A(O), A(lse), A(Ob), int(w_floor))
     return O, lse, Ob
 
 

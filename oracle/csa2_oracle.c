@@ -467,7 +467,8 @@ void orc_quant_index_query(const uint16_t* q, uint8_t* q8, float* sq) {
 
 /*
  * One query token at absolute position p, H heads [P2 attention equations]:
- *   J^w = {max(0, p-127) .. p} (window rows, ring slot = position mod cap),
+ *   J^w = {max(0, s, p-127) .. p} (window rows, ring slot = position mod cap;
+ *         s = w_floor, the start of a bounded replay, 0 when none),
  *   G   = [W[J^w]; Z[I]]                     (no de-duplication),
  *   S_i = Q_h . G_i / sqrt(512),
  *   A_i = exp S_i / (exp s_h + sum_j exp S_j),
@@ -479,9 +480,12 @@ void orc_quant_index_query(const uint16_t* q, uint8_t* q8, float* sq) {
 void orc_attend(const uint16_t* Q, int H, int64_t p, const uint8_t* w_codes, const float* w_scale,
                 int cap, const uint8_t* z_codes, const uint8_t* z_scales, const int32_t* idx,
                 int cnt, const float* sink, const float* cos_t, const float* sin_t, double* O,
-                double* lse, uint16_t* O_bf16) {
+                double* lse, uint16_t* O_bf16, int64_t w_floor) {
     int64_t w0 = p - (ORC_WINDOW - 1);
     if (w0 < 0) w0 = 0;
+    /* bounded replay from s = w_floor: the window is max(s, p-127) .. p (s > p read as p) */
+    if (w_floor > p) w_floor = p;
+    if (w0 < w_floor) w0 = w_floor;
     int nw = (int)(p - w0 + 1);
     int nr = nw + cnt;
     double* G = (double*)malloc(sizeof(double) * (size_t)nr * ORC_D);
@@ -563,7 +567,7 @@ void orc_query_rows(int nq, const int64_t* pos, int64_t n_entries, const uint16_
             orc_attend(Q + (size_t)i * H * ORC_D, H, p, w_codes, w_scale, cap, z_codes, z_scales,
                        idx + (size_t)i * k, cnt[i], sink, cos_t, sin_t,
                        O ? O + (size_t)i * H * ORC_D : NULL, lse ? lse + (size_t)i * H : NULL,
-                       O_bf16 ? O_bf16 + (size_t)i * H * ORC_D : NULL);
+                       O_bf16 ? O_bf16 + (size_t)i * H * ORC_D : NULL, 0);
     }
     free(S);
 }

@@ -127,10 +127,11 @@ def caches(orc, cap, N, p_last):
     return w_codes[0], w_scale[0], zc, zs, cos_t, sin_t
 
 
-def rows_of(orc, p, cap, w_codes, w_scale, zc, zs, idx, cnt):
-    """G = [W[max(0,p-127)..p]; Z[idx]] from the pinned decoders (window rule of the pages)"""
+def rows_of(orc, p, cap, w_codes, w_scale, zc, zs, idx, cnt, floor=0):
+    """G = [W[max(0,floor,p-127)..p]; Z[idx]] from the pinned decoders (window rule of the
+    pages; floor = the start of a bounded replay)"""
     e4 = e4m3_table(orc)
-    pos = np.arange(max(0, p - 127), p + 1)
+    pos = np.arange(max(0, floor, p - 127), p + 1)
     Wr = e4[w_codes[pos % cap]] * w_scale[pos % cap][:, None].astype(np.float64)
     Zr = orc.fp4_decode(zc[idx[:cnt]], zs[idx[:cnt]])
     return np.concatenate([Wr, Zr])
@@ -161,6 +162,37 @@ def test_sink_identity_against_sdpa(orc):
     A_sink = np.exp(sink.astype(np.float64) - lse)
     A_rows = np.exp(((q @ G.T) / math.sqrt(D)).numpy() - lse[:, None]).sum(1)
     assert np.allclose(A_sink + A_rows, 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("floor", [0, 800, 850, 899, 900])
+def test_bounded_replay_window_against_sdpa(orc, floor):
+    """Bounded replay from s ("Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV
+    Cache", section "Bounded replay trades exact state for cheaper resumption"): the
+    query at p sees window positions max(s, p-127)..p; checked against torch's float64
+    SDPA over exactly those rows plus the selected ones, with the sink identity."""
+    cap, N, p, H = 200, 700, 900, 4
+    w_codes, w_scale, zc, zs, cos_t, sin_t = caches(orc, cap, N, p)
+    idx = np.sort(rng.choice(N, 300, replace=False)).astype(np.int32)
+    Q = bf16((rng.standard_normal((H, D)) * 0.3).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    O, lse, _ = orc.attend(Q, p, w_codes, w_scale, cap, zc, zs, idx, 300, sink, cos_t, sin_t,
+                           w_floor=floor)
+    G = torch.from_numpy(rows_of(orc, p, cap, w_codes, w_scale, zc, zs, idx, 300, floor))
+    assert G.shape[0] == 300 + (p + 1 - max(floor, p - 127))
+    q = torch.from_numpy(f32(Q).astype(np.float64))
+    Op = torch.nn.functional.scaled_dot_product_attention(q[None], G[None], G[None],
+                                                          scale=1 / math.sqrt(D))[0]
+    lse_p = torch.logsumexp((q @ G.T) / math.sqrt(D), dim=1)
+    sk = torch.from_numpy(sink.astype(np.float64))
+    # the inverse rotation of channels 448.. at p is linear: undo it on both sides by
+    # comparing before it (p's rotation applied to the SDPA output instead)
+    expect = (torch.sigmoid(lse_p - sk)[:, None] * Op).numpy()
+    c, s_ = cos_t[p].astype(np.float64), sin_t[p].astype(np.float64)
+    e0, e1 = expect[:, 448::2].copy(), expect[:, 449::2].copy()
+    expect[:, 448::2] = e0 * c + e1 * s_
+    expect[:, 449::2] = -e0 * s_ + e1 * c
+    assert np.max(np.abs(O - expect)) < 1e-12
+    assert np.allclose(lse, torch.logaddexp(lse_p, sk).numpy(), rtol=0, atol=1e-12)
 
 
 def test_first_token_closed_form(orc):
