@@ -50,7 +50,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_index_pool.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
         L.csa2_reindex_topk.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
         L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64] +
-                                       [vp] * 5 + [i64, vp, vp, vp, sz, vp])
+                                       [vp] * 5 + [i64, vp, vp, vp, vp, sz, vp])
         L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, vp, vp,
                                    vp, i32, vp, vp, vp, vp, vp, sz, vp])
         L.csa2_encode_fp4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
@@ -199,7 +199,7 @@ def csa2_index_scores(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, scores, ws
 
 
 def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, sink, rope_cos,
-                     rope_sin, O, lse, ws, stream=None):
+                     rope_sin, O, lse, ws, stream=None, win_floor=None):
     B, H, Tq = Q.shape[0], Q.shape[1], Q.shape[2]
     _check(lib().csa2_sparse_attn(B, Tq, H, _p(q_pos0, "i32", "q_pos0"), _p(Q, "bf16", "Q"),
                                   _p(w_codes, "u8", "w_codes"), _p(w_scale, "f32", "w_scale"),
@@ -208,7 +208,8 @@ def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, s
                                   _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                                   _p(sink, "f32", "sink"), _p(rope_cos, "f32", "rope_cos"),
                                   _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
-                                  _p(O, "bf16", "O"), _p(lse, "f32", "lse"), _p(ws, None, "ws"),
+                                  _p(O, "bf16", "O"), _p(lse, "f32", "lse"),
+                                  _p(win_floor, "i32", "win_floor"), _p(ws, None, "ws"),
                                   ws.numel() * ws.element_size(), _stream(stream)),
            "csa2_sparse_attn")
 

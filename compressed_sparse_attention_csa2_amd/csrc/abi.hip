@@ -48,7 +48,7 @@ template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
                        const int32_t*, const float*, const float*, const float*, int64_t,
-                       uint16_t*, float*, int, float*, float*);
+                       uint16_t*, float*, int, float*, float*, const int32_t*);
 __global__ void k_attn_combine(int, int, int, const int32_t*, const float*, const float*,
                                const float*, int64_t, int, const float*, const float*, uint16_t*,
                                float*);
@@ -253,7 +253,7 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
                         const uint8_t* z_codes, const uint8_t* z_scales, int64_t stride,
                         const int32_t* idx, const int32_t* cnt, const float* sink,
                         const float* rc, const float* rs, int64_t rope_rows, uint16_t* O,
-                        float* lse, void* ws, hipStream_t st) {
+                        float* lse, const int32_t* win_floor, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
     // the kernel addresses one request's caches with 32-bit byte offsets
     if ((int64_t)cap * D > (int64_t)0xFFFFFFFF || stride * 256 > (int64_t)0xFFFFFFFF)
@@ -271,7 +271,7 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
 #define CSA2_ATTN(HTV)                                                                         \
     hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(ATT_THREADS), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
                        w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
-                       rope_rows, O, lse, L.nsplit, pO, pml)
+                       rope_rows, O, lse, L.nsplit, pO, pml, win_floor)
     switch (ht) {
         case 1: CSA2_ATTN(1); break;
         case 2: CSA2_ATTN(2); break;
@@ -496,7 +496,8 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
                              const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
                              const int32_t* idx, const int32_t* cnt, const float* sink,
                              const float* rope_cos, const float* rope_sin, int64_t rope_rows,
-                             uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                             uint16_t* O, float* lse, const int32_t* win_floor, void* ws,
+                             size_t ws_bytes, void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "sparse_attn: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: H=%d (need 16, 32, 48 or 64)", H);
     if (!q_pos0 || !Q || !w_codes || !w_scale || !z_codes || !z_scales || !idx || !cnt || !sink ||
@@ -510,7 +511,7 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
         return fail(CSA2_ERR_WORKSPACE, "sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_attn(B, Tq, H, q_pos0, Q, w_codes, w_scale, cap, z_codes, z_scales,
                                 entry_stride, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O,
-                                lse, ws, S(stream));
+                                lse, win_floor, ws, S(stream));
     return s == CSA2_OK ? ok() : s;
 }
 
@@ -566,7 +567,7 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                      ws, st);
     if (s != CSA2_OK) return s;
     s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride, idx,
-                    cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, ws, st);
+                    cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, nullptr, ws, st);
     return s == CSA2_OK ? ok() : s;
 }
 

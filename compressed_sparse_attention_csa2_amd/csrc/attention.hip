@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const float* __restrict__ sink, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint16_t* __restrict__ O,
     float* __restrict__ lse, int nsplit, float* __restrict__ part_O,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, const int32_t* __restrict__ win_floor) {
     __shared__ __attribute__((aligned(16))) uint8_t rawc[NRAW][CH * 512];
     __shared__ __attribute__((aligned(16))) uint32_t zsc[NRAW][CH][4];
     __shared__ __attribute__((aligned(16))) float rscl[NRAW][CH];
@@ -149,7 +149,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         if (p < 0) p = 0;
         U.p = p;
         U.prow = p < rope_rows ? p : rope_rows - 1;
-        const int64_t w0 = p - (WINDOW - 1) > 0 ? p - (WINDOW - 1) : 0;
+        int64_t w0 = p - (WINDOW - 1) > 0 ? p - (WINDOW - 1) : 0;
+        if (win_floor) {     // bounded replay: the window starts no earlier than s (s <= p)
+            int64_t fl = win_floor[U.b];
+            fl = fl > p ? p : fl;
+            w0 = w0 > fl ? w0 : fl;
+        }
         U.nwin = (int)(p - w0 + 1);
         U.slot0 = (int)(w0 % cap);
         int nc = cnt[U.row];
@@ -716,7 +721,7 @@ __global__ void __launch_bounds__(256) k_attn_combine(
                                          const uint8_t*, int64_t, const int32_t*,              \
                                          const int32_t*, const float*, const float*,           \
                                          const float*, int64_t, uint16_t*, float*, int, float*, \
-                                         float*);
+                                         float*, const int32_t*);
 CSA2_ATTN_INST(1)
 CSA2_ATTN_INST(2)
 CSA2_ATTN_INST(3)

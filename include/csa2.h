@@ -226,13 +226,18 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
  *  sink      [H] fp32.
  *  O         [B][H][Tq][512] bf16 out.   lse [B][H][Tq] fp32 out or NULL
  *            (natural log of the full softmax denominator, sink included).
+ *  win_floor [B] int32 device or NULL: bounded replay [zharf, section
+ *            "Bounded replay trades exact state for cheaper resumption": for
+ *            replay starting at s, a query at p sees window positions
+ *            max(s, p-127) .. p].  s > p is read as s = p.
  */
 csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
                              const uint8_t* w_codes, const float* w_scale, int cap,
                              const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
                              const int32_t* idx, const int32_t* cnt, const float* sink,
                              const float* rope_cos, const float* rope_sin, int64_t rope_rows,
-                             uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+                             uint16_t* O, float* lse, const int32_t* win_floor, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * The whole layer for one call.

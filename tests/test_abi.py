@@ -69,9 +69,9 @@ def test_rejects_before_launch(L):
     s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 16, n)
     assert s == 5 and b"workspace" in L.csa2_last_error()
     # attention: unsupported heads, small ring, missing workspace
-    args = [FAKE] * 4 + [200, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, FAKE]
+    args = [FAKE] * 4 + [200, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
     assert L.csa2_sparse_attn(1, 8, 24, *args, 1 << 30, n) == 3
-    args_ring = [FAKE] * 4 + [100, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, FAKE]
+    args_ring = [FAKE] * 4 + [100, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
     assert L.csa2_sparse_attn(1, 8, 64, *args_ring, 1 << 30, n) == 4
     assert L.csa2_sparse_attn(4, 1, 64, *args, 0, n) == 5
     # forward: decode without n_entries

@@ -216,6 +216,53 @@ def test_sparse_attn_given_oracle_selection(dev, synth):
     log(f"  max|dO|={mx:.2e} rel={rel:.2e}")
 
 
+def test_sparse_attn_bounded_replay_floor(dev, synth):
+    """attention with a per-request replay start s: request 0 none, request 1 a start
+    inside the 128-row window, request 2 a start past every query (one window row)"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import oracle
+    from oracle.reference import DecodeReference
+    B, Tq, N, H = 3, 5, 2600, 64
+    wl = synth.decode_workload(B=B, Tq=Tq, n_entries=N, H=H)
+    p0 = wl.q_pos0
+    floors = np.array([0, p0 - 40, p0 + 100], np.int32)
+    log(f"csa2_sparse_attn with replay starts {floors.tolist()}: {wl.name}")
+    g = np.random.default_rng(17)
+    cnts = np.array([[512, 300, 1, 0, 512]] * B, np.int32)
+    idx = np.full((B, Tq, 512), -1, np.int32)
+    refs = [DecodeReference(wl, b) for b in range(B)]
+    for b in range(B):
+        for i in range(Tq):
+            c = cnts[b, i]
+            idx[b, i, :c] = np.sort(g.choice(N, c, replace=False))
+        refs[b]._ensure_z(idx[b].reshape(-1))
+    O = torch.zeros(B, H, Tq, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(B, H, Tq, dtype=torch.float32, device=dev)
+    cos_t, sin_t = synth.rope_table(wl.rope_rows)
+    ws = csa2.workspace(csa2.OP_SPARSE_ATTN, B, Tq, H, N)
+    stack = lambda name: _up(np.stack([getattr(r, name) for r in refs]))
+    csa2.csa2_sparse_attn(_up(np.full(B, p0, np.int32)), _up(wl.Q()), stack("w_codes"),
+                          stack("w_scale"), stack("z_codes"), stack("z_scales"), _up(idx),
+                          _up(cnts), _up(refs[0].sink), _up(cos_t), _up(sin_t), O, lse, ws,
+                          win_floor=_up(floors))
+    torch.cuda.synchronize()
+    got_O, got_lse = _down(O), _down(lse)
+    Q = wl.Q()
+    for b in range(B):
+        r = refs[b]
+        exp = np.zeros((Tq, H, 512))
+        exp_lse = np.zeros((Tq, H))
+        for i in range(Tq):
+            exp[i], exp_lse[i], _ = oracle.attend(Q[b][:, i, :], p0 + i, r.w_codes, r.w_scale,
+                                                  wl.cap, r.z_codes, r.z_scales, idx[b, i],
+                                                  int(cnts[b, i]), r.sink, r.cos, r.sin,
+                                                  w_floor=int(floors[b]))
+        mx, rel = check_attention(got_O[b].transpose(1, 0, 2), exp, f"floor {floors[b]}")
+        assert np.max(np.abs(got_lse[b].T - exp_lse)) < 1e-3
+        log(f"  request {b} (s={floors[b]}): max|dO|={mx:.2e} rel={rel:.2e}")
+
+
 # ---------------------------------------------------------------- decode
 @pytest.mark.parametrize("Tq,N,keys", [(1, 3000, "flat"), (6, 2600, "lognormal_dup")])
 def test_decode_small(dev, synth, Tq, N, keys):
