@@ -130,6 +130,7 @@ class Workload:
     seed: int = 0
     name: str = ""
     extra: dict = field(default_factory=dict)
+    ratio: int = 2       # positions per compressed entry (2: pairs; 1: one entry per token)
 
     # ---- geometry -------------------------------------------------------
     @property
@@ -228,7 +229,7 @@ class Workload:
         return out
 
     def ki_given(self):
-        n = self.Tq // 2 if self.kind == "prefill" else self.n_entries
+        n = self.Tq // self.ratio if self.kind == "prefill" else self.n_entries
         return np.stack([self.ki_rows(b, 0, n) for b in range(self.B)])
 
     def z_rows(self, b: int, j0: int, n: int) -> np.ndarray:
@@ -236,17 +237,19 @@ class Workload:
         return normal(self.seed, ID_ZROW, (n, D), start=(b * self.n_entries + j0) * D)
 
 
-def workload(cid: int, T: int | None = None, H: int | None = None) -> Workload:
-    """The five measured workloads; T/H overrides give same-recipe smaller prefills."""
+def workload(cid: int, T: int | None = None, H: int | None = None, ratio: int = 2) -> Workload:
+    """The five measured workloads; T/H overrides give same-recipe smaller prefills, ratio 1
+    the one-entry-per-token form of a prefill."""
     seed = 0xC5A20000 + cid
+    tag = "" if ratio == 2 else f" ratio {ratio}"
     if cid == 0:
         T = T or 256
-        return Workload(cid, "prefill", 1, T, H or 16, T // 2, T + WINDOW - 1, 0, "derive", seed,
-                        f"prefill T={T} H={H or 16} derived index keys")
+        return Workload(cid, "prefill", 1, T, H or 16, T // ratio, T + WINDOW - 1, 0, "derive",
+                        seed, f"prefill T={T} H={H or 16} derived index keys{tag}", ratio=ratio)
     if cid in (1, 2):
         T = T or (8192 if cid == 1 else 65536)
-        return Workload(cid, "prefill", 1, T, H or 64, T // 2, T + WINDOW - 1, 0, "clustered", seed,
-                        f"prefill T={T} H={H or 64} clustered index keys")
+        return Workload(cid, "prefill", 1, T, H or 64, T // ratio, T + WINDOW - 1, 0, "clustered",
+                        seed, f"prefill T={T} H={H or 64} clustered index keys{tag}", ratio=ratio)
     if cid == 3:
         return Workload(3, "decode", 128, 1, H or 64, 65536, 128, 131071, "flat", seed,
                         "decode B=128 x 1 @ 131072 context")
@@ -257,8 +260,11 @@ def workload(cid: int, T: int | None = None, H: int | None = None) -> Workload:
 
 
 def decode_workload(B: int, Tq: int, n_entries: int, H: int = 64, keys: str = "flat",
-                    seed: int = 0xC5A20010, q_pos0: int | None = None) -> Workload:
-    """A smaller decode workload with the recipe of workloads 3/4 (for tests)."""
-    q0 = (2 * n_entries - Tq) if q_pos0 is None else q_pos0
+                    seed: int = 0xC5A20010, q_pos0: int | None = None,
+                    ratio: int = 2) -> Workload:
+    """A decode workload with the recipe of workloads 3/4 (ratio 2), or its one-entry-per-token
+    form (ratio 1): the queries follow the last entry's positions."""
+    q0 = (ratio * n_entries - Tq) if q_pos0 is None else q_pos0
+    tag = "" if ratio == 2 else f" ratio {ratio}"
     return Workload(99, "decode", B, Tq, H, n_entries, Tq + WINDOW - 1, q0, keys, seed,
-                    f"decode B={B} x {Tq} @ {2 * n_entries}")
+                    f"decode B={B} x {Tq} @ {ratio * n_entries}{tag}", ratio=ratio)

@@ -60,7 +60,7 @@ def lib():
         L.orc_fp8_encode_row.argtypes = [vp, i32, vp, vp]
         L.orc_rmsnorm.argtypes = [vp, vp, i32, vp]
         L.orc_compress_entry.argtypes = [vp] * 16
-        L.orc_compress.argtypes = [i32, i32, i32] + [vp] * 12 + [i64]
+        L.orc_compress.argtypes = [i32, i32, i32] + [vp] * 12 + [i64, i32]
         L.orc_window_encode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp]
         L.orc_fp4_encode_rows.argtypes = [vp, i64, i32, vp, vp]
         L.orc_fp8_encode_rows.argtypes = [vp, i64, i32, vp, vp]
@@ -70,7 +70,7 @@ def lib():
         L.orc_quant_index_query.argtypes = [vp, vp, vp]
         L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64]
         L.orc_query_rows.argtypes = [i32, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32,
-                                     vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+                                     vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -182,7 +182,8 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- steps
 def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn):
-    """one entry; returns (z_codes, z_scales, ki_codes, ki_scales, z_pre, ki_pre)"""
+    """one entry; returns (z_codes, z_scales, ki_codes, ki_scales, z_pre, ki_pre).
+    kc1 = None: compression ratio one, the entry is the one position kc0 (gates unused)."""
     A = _Args()
     zc = np.zeros(256, np.uint8)
     zs = np.zeros(16, np.uint8)
@@ -198,8 +199,13 @@ def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn
     return zc, zs, kc_, ks, zp, kp
 
 
-def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stride, pos0=0):
-    """kc, gc [B,T,512] bf16 -> caches [B, entry_stride, ...] (entries pos0/2 .. (pos0+T)/2-1)"""
+def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stride, pos0=0,
+             ratio=2):
+    """kc, gc [B,T,512] bf16 -> caches [B, entry_stride, ...]: entries pos0/2 .. (pos0+T)/2-1
+    pooled from pairs (ratio 2), or entries pos0 .. pos0+T-1, one per position, rotated at
+    their own position (ratio 1, "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV
+    Cache", CSA2 section; gc may be None)."""
+    assert ratio in (1, 2)
     A = _Args()
     kc = c(kc, np.uint16)
     gc = c(gc, np.uint16)
@@ -212,7 +218,7 @@ def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stri
                        A(None if w_ik is None else c(w_ik, np.uint16)), A(gamma_ik, np.float32),
                        A(None if ki_given is None else c(ki_given, np.uint16)),
                        A(cos_t, np.float32), A(sin_t, np.float32),
-                       A(z_codes), A(z_scales), A(ki_codes), A(ki_scales), entry_stride)
+                       A(z_codes), A(z_scales), A(ki_codes), A(ki_scales), entry_stride, ratio)
     return z_codes, z_scales, ki_codes, ki_scales
 
 
@@ -317,8 +323,10 @@ def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t
 
 
 def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales, w_codes,
-               w_scale, cap, sink, cos_t, sin_t, k=TOPK, want_scores=False, want_O=True):
-    """Selection and attention for query tokens of ONE request (caches of that request)."""
+               w_scale, cap, sink, cos_t, sin_t, k=TOPK, want_scores=False, want_O=True,
+               ratio=2):
+    """Selection and attention for query tokens of ONE request (caches of that request).
+    A query at p sees entries j < min(floor((p+1)/ratio), n_entries)."""
     A = _Args()
     pos = c(pos, np.int64)
     nq = pos.shape[0]
@@ -335,5 +343,5 @@ def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales
                          A(z_codes, np.uint8), A(z_scales, np.uint8),
                          A(w_codes, np.uint8), A(w_scale, np.float32), cap,
                          A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
-                         k, A(idx), A(cnt), A(O), A(Ob), A(lse), A(S))
+                         k, A(idx), A(cnt), A(O), A(Ob), A(lse), A(S), ratio)
     return dict(idx=idx, cnt=cnt, O=O, O_bf16=Ob, lse=lse, S=S)

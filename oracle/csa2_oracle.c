@@ -24,9 +24,11 @@
  *       indexer, 64 heads sharing one latent, per-head sink) and "890 bytes"
  *       (FP4 entries with 8-bit block scales, the 22.6 value bound).
  *  [P4] "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache",
- *       sections "Deriving the 890 bytes per token" (entry byte layouts) and
+ *       sections "Deriving the 890 bytes per token" (entry byte layouts),
  *       "FP4 is a storage choice" (quantisation after RoPE, keep block size,
- *       scale type and rounding).
+ *       scale type and rounding), the CSA2 section (compression ratio one is
+ *       a supported case; the decoder layers use it) and "Bounded replay
+ *       trades exact state for cheaper resumption".
  *
  * Precision.  Steps whose result is an integer code (the FP4/FP8 encodings
  * and everything feeding them: pair gate, RMSNorm, rotation, index-key
@@ -267,6 +269,10 @@ static void rope_fwd(float* x, int lo, const float* cs, const float* sn) {
 /*
  * One compressed entry j from positions 2j, 2j+1 [P2 pooling equations]:
  *   k^p = sum_i softmax_i(g^c_i) (.) k^c_i          (per channel, i in {2j, 2j+1})
+ * or, at compression ratio one [zharf, CSA2 section: ratio one is a supported
+ * case; blog: decoder layers keep one entry per token], from the one position
+ * j alone (kc1 == NULL): the softmax over a single logit is 1, so k^p = k^c_j
+ * and the gate logits are not read.
  *   c   = RMSNorm_{gamma_C}(k^p)
  *   Z_j = FP4(c with channels 448.. rotated by R_{2j})
  *   K^I_j = FP4(RMSNorm_{gamma_IK}(c W_IK) with channels 64.. rotated by R_{2j})
@@ -280,7 +286,8 @@ void orc_compress_entry(const uint16_t* kc0, const uint16_t* kc1, const uint16_t
                         const float* sn, uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
                         uint8_t* ki_scales, float* z_pre, float* ki_pre) {
     float kp[ORC_D], c[ORC_D], z[ORC_D], ki[ORC_DI], kn[ORC_DI];
-    for (int ch = 0; ch < ORC_D; ++ch) {
+    for (int ch = 0; ch < ORC_D && !kc1; ++ch) kp[ch] = bf16f(kc0[ch]);
+    for (int ch = 0; ch < ORC_D && kc1; ++ch) {
         float a = bf16f(gc0[ch]), b = bf16f(gc1[ch]);
         float m = fmaxf(a, b);
         float ea = orc_exp(a - m), eb = orc_exp(b - m);
@@ -313,8 +320,9 @@ void orc_compress_entry(const uint16_t* kc0, const uint16_t* kc1, const uint16_t
 
 /*
  * Compression of B requests x T new positions starting at absolute position
- * pos0 (even).  Entry j (absolute) pools positions 2j, 2j+1 and is rotated at
- * 2j; T odd leaves the last position pending (floor(T/2) entries).
+ * pos0.  ratio 2: pos0 even; entry j (absolute) pools positions 2j, 2j+1 and
+ * is rotated at 2j; T odd leaves the last position pending (floor(T/2)
+ * entries).  ratio 1: entry j is position j alone, rotated at j (T entries).
  * Layouts: kc, gc [B][T][512] bf16; ki_given [B][T/2][128] bf16 or NULL;
  * caches [B][entry_stride][...]; cos/sin [rows][32] indexed by absolute position.
  */
@@ -322,17 +330,18 @@ void orc_compress(int B, int T, int pos0, const uint16_t* kc, const uint16_t* gc
                   const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
                   const uint16_t* ki_given, const float* cos_t, const float* sin_t,
                   uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                  int64_t entry_stride) {
-    int nloc = T / 2;
+                  int64_t entry_stride, int ratio) {
+    int nloc = T / ratio;
     for (int b = 0; b < B; ++b) {
         for (int jl = 0; jl < nloc; ++jl) {
-            int64_t j = pos0 / 2 + jl;
-            const uint16_t* k0 = kc + ((int64_t)b * T + 2 * jl) * ORC_D;
-            const uint16_t* g0 = gc + ((int64_t)b * T + 2 * jl) * ORC_D;
+            int64_t j = pos0 / ratio + jl;
+            const uint16_t* k0 = kc + ((int64_t)b * T + ratio * jl) * ORC_D;
+            const uint16_t* g0 = gc ? gc + ((int64_t)b * T + ratio * jl) * ORC_D : NULL;
             const uint16_t* kg = ki_given ? ki_given + ((int64_t)b * nloc + jl) * ORC_DI : NULL;
             int64_t e = (int64_t)b * entry_stride + j;
-            orc_compress_entry(k0, k0 + ORC_D, g0, g0 + ORC_D, gamma_c, w_ik, gamma_ik, kg,
-                               cos_t + 2 * j * ORC_PAIRS, sin_t + 2 * j * ORC_PAIRS,
+            orc_compress_entry(k0, ratio == 2 ? k0 + ORC_D : NULL, g0,
+                               ratio == 2 ? g0 + ORC_D : NULL, gamma_c, w_ik, gamma_ik, kg,
+                               cos_t + ratio * j * ORC_PAIRS, sin_t + ratio * j * ORC_PAIRS,
                                z_codes + e * 256, z_scales + e * 16, ki_codes + e * 64,
                                ki_scales + e * 4, NULL, NULL);
         }
@@ -539,7 +548,7 @@ void orc_attend(const uint16_t* Q, int H, int64_t p, const uint8_t* w_codes, con
 
 /*
  * Selection + attention for a list of query tokens of one request.
- * For query i at absolute position pos[i]: n = min(floor((pos+1)/2), n_entries)
+ * For query i at absolute position pos[i]: n = min(floor((pos+1)/ratio), n_entries)
  * candidates; q^I row quantised to FP8; scores; top-k; attention.
  * qI: [nq][32][128] bf16, wI: [nq][32], Q: [nq][H][512] bf16.
  * Outputs: idx [nq][k], cnt [nq], O [nq][H][512] double (optional),
@@ -551,13 +560,13 @@ void orc_query_rows(int nq, const int64_t* pos, int64_t n_entries, const uint16_
                     const uint8_t* ki_scales, const uint8_t* z_codes, const uint8_t* z_scales,
                     const uint8_t* w_codes, const float* w_scale, int cap, const float* sink,
                     const float* cos_t, const float* sin_t, int k, int32_t* idx, int32_t* cnt,
-                    double* O, uint16_t* O_bf16, double* lse, float* S_out) {
+                    double* O, uint16_t* O_bf16, double* lse, float* S_out, int ratio) {
     uint8_t q8[ORC_HI * ORC_DI];
     float sq[ORC_HI];
     float* S = (float*)malloc(sizeof(float) * (size_t)(n_entries > 0 ? n_entries : 1));
     for (int i = 0; i < nq; ++i) {
         int64_t p = pos[i];
-        int64_t n = (p + 1) / 2;
+        int64_t n = (p + 1) / ratio;
         if (n > n_entries) n = n_entries;
         orc_quant_index_query(qI + (size_t)i * ORC_HI * ORC_DI, q8, sq);
         orc_index_scores(q8, sq, wI + (size_t)i * ORC_HI, ki_codes, ki_scales, n, S);

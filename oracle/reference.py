@@ -23,13 +23,13 @@ class PrefillReference:
         T = wl.Tq
         self.cos, self.sin = synth.rope_table(wl.rope_rows)
         kc = wl.kc()[b:b + 1]
-        gc = wl.gc()[b:b + 1]
+        gc = wl.gc()[b:b + 1] if wl.ratio == 2 else None     # ratio 1 reads no gates
         derive = wl.keys == "derive"
         ki_given = None if derive else wl.ki_given()[b:b + 1]
         self.z_codes, self.z_scales, self.ki_codes, self.ki_scales = compress(
             kc, gc, wl.gamma_c(), wl.w_ik() if derive else None, wl.gamma_ik(), ki_given,
-            self.cos, self.sin, entry_stride=T // 2)
-        self.n_entries = T // 2
+            self.cos, self.sin, entry_stride=T // wl.ratio, ratio=wl.ratio)
+        self.n_entries = T // wl.ratio
         self.cap = wl.cap
         self.w_codes = np.zeros((1, wl.cap, 512), np.uint8)
         self.w_scale = np.zeros((1, wl.cap), np.float32)
@@ -62,7 +62,7 @@ class PrefillReference:
         return query_rows(t, self.n_entries, self.wl.qI_rows(self.b, t), self.wI[t], Q,
                           self.ki_codes[0], self.ki_scales[0], self.z_codes[0], self.z_scales[0],
                           self.w_codes[0], self.w_scale[0], self.cap, self.sink, self.cos,
-                          self.sin, TOPK, want_scores=want_scores)
+                          self.sin, TOPK, want_scores=want_scores, ratio=self.wl.ratio)
 
 
 class DecodeReference:
@@ -112,7 +112,7 @@ class DecodeReference:
         qI = wl.qI()[self.b, qi]
         sel = query_rows(pos, wl.n_entries, qI, self.wI[qi], None, self.ki_codes, self.ki_scales,
                          None, None, None, None, wl.cap, self.sink, self.cos, self.sin, TOPK,
-                         want_scores=want_scores)
+                         want_scores=want_scores, ratio=wl.ratio)
         if not want_attn:
             return sel
         self._ensure_z(sel["idx"].reshape(-1))

@@ -183,6 +183,74 @@ def test_compress_batch_matches_entries_and_positions(orc, synth):
         assert np.array_equal(kic[0, j], e[2]) and np.array_equal(kis[0, j], e[3])
 
 
+# ---------------------------------------------------------------- compression ratio one
+# "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache", CSA2 section: ratio one
+# is a supported case (the decoder layers use it); entry j is then position j alone.
+def test_ratio_one_entry_is_the_equal_gate_pair_of_one_token(orc, synth):
+    """the one-position entry equals the pair formula with the token doubled under equal
+    gates (weights 1/2 each, exact: k^p = k^c), byte for byte, index key included"""
+    cos_t, sin_t = synth.rope_table(64)
+    gamma = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    W = bf16((rng.standard_normal((D, 128)) / math.sqrt(D)).astype(np.float32))
+    g_ik = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    for _ in range(4):
+        ka, g = rand_bf16(D, 3.0), rand_bf16(D)
+        one = orc.compress_entry(ka, None, None, None, gamma, W, g_ik, None, cos_t[37], sin_t[37])
+        two = orc.compress_entry(ka, ka, g, g, gamma, W, g_ik, None, cos_t[37], sin_t[37])
+        for a, b in zip(one, two):
+            assert np.array_equal(a, b)
+
+
+def test_ratio_one_entry_values_in_float64(orc, synth):
+    """z = R_p(gamma_C k^c / rms(k^c)) and k^n = R_p(gamma_IK k^i / rms(k^i)), k^i = c W_IK,
+    evaluated in float64 from the equations: agree to fp32 rounding"""
+    cos_t, sin_t = synth.rope_table(64)
+    gamma = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    W = bf16((rng.standard_normal((D, 128)) / math.sqrt(D)).astype(np.float32))
+    g_ik = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    ka = rand_bf16(D, 2.0)
+    p = 45
+    out = orc.compress_entry(ka, None, None, None, gamma, W, g_ik, None, cos_t[p], sin_t[p])
+    x = f32(ka).astype(np.float64)
+    c = gamma * x / np.sqrt(np.mean(x * x) + 1e-20)
+    def rot(v, lo):
+        v = v.copy()
+        cs, sn = cos_t[p].astype(np.float64), sin_t[p].astype(np.float64)
+        a, b = v[lo::2].copy(), v[lo + 1::2].copy()
+        v[lo::2], v[lo + 1::2] = a * cs - b * sn, a * sn + b * cs
+        return v
+    z = rot(c, 448)
+    assert np.max(np.abs(out[4] - z)) < 2e-6 * np.max(np.abs(z))
+    ki = c @ f32(W).astype(np.float64)
+    kn = rot(g_ik * ki / np.sqrt(np.mean(ki * ki) + 1e-20), 64)
+    assert np.max(np.abs(out[5] - kn)) < 2e-5 * np.max(np.abs(kn))
+
+
+@pytest.mark.parametrize("derive", [True, False])
+def test_ratio_one_batch_one_entry_per_position(orc, synth, derive):
+    """ratio 1 over T positions from an odd start p0: entry p0+i is position i alone,
+    rotated at its own position p0+i (not 2j), given keys one per position"""
+    wl = synth.workload(0, T=12, ratio=1)
+    T, p0 = 12, 21
+    cos_t, sin_t = synth.rope_table(2 * (p0 + T) + 1)
+    kc = wl.kc()
+    ki = None if derive else rand_bf16(T * 128).reshape(1, T, 128)
+    w_ik = wl.w_ik() if derive else None
+    zc, zs, kic, kis = orc.compress(kc, None, wl.gamma_c(), w_ik, wl.gamma_ik(), ki, cos_t,
+                                    sin_t, entry_stride=p0 + T + 3, pos0=p0, ratio=1)
+    for i in range(T):
+        j = p0 + i
+        e = orc.compress_entry(kc[0, i], None, None, None, wl.gamma_c(), w_ik, wl.gamma_ik(),
+                               None if derive else ki[0, i], cos_t[j], sin_t[j])
+        assert np.array_equal(zc[0, j], e[0]) and np.array_equal(zs[0, j], e[1])
+        assert np.array_equal(kic[0, j], e[2]) and np.array_equal(kis[0, j], e[3])
+    assert not zc[0, :p0].any() and not zc[0, p0 + T:].any()      # nothing else written
+    # the rotation row matters: at 2j the rotated channels would differ
+    e2 = orc.compress_entry(kc[0, 0], None, None, None, wl.gamma_c(), w_ik, wl.gamma_ik(),
+                            None if derive else ki[0, 0], cos_t[2 * p0], sin_t[2 * p0])
+    assert not np.array_equal(zc[0, p0], e2[0])
+
+
 # ---------------------------------------------------------------- window
 def test_window_rows_rotated_at_position_into_ring_slot(orc, synth):
     cap, T = 8, 13

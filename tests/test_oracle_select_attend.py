@@ -113,6 +113,28 @@ def test_causal_count_and_640_rows(orc, synth):
         assert np.all(np.diff(r["idx"][i, :c]) > 0)
 
 
+def test_causal_count_ratio_one(orc, synth):
+    """compression ratio one ("Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache",
+    CSA2 section): a query at p sees entries j < floor((p+1)/1), i.e. j <= p, its own
+    position's entry included; the selection is the brute-force top-512 of those"""
+    import oracle
+    N = 1500
+    kc, ks = rand_keys(orc, N)
+    qI = bf16(rng.standard_normal((8, 32, 128)).astype(np.float32))
+    wI = (rng.standard_normal((8, 32)) / 64).astype(np.float32)
+    pos = np.array([0, 1, 5, 510, 511, 512, 900, 1499])
+    r = oracle.query_rows(pos, N, qI, wI, None, kc, ks, None, None, None, None, 128, None,
+                          None, None, want_scores=True, ratio=1)
+    assert list(r["cnt"]) == [min(512, p + 1) for p in pos]
+    for i, p in enumerate(pos):
+        ref, rc = brute_topk(r["S"][i], p + 1)
+        assert r["cnt"][i] == rc and np.array_equal(r["idx"][i], ref)
+    # the same rows at ratio 2 see half as many
+    r2 = oracle.query_rows(pos, N, qI, wI, None, kc, ks, None, None, None, None, 128, None,
+                           None, None, ratio=2)
+    assert list(r2["cnt"]) == [min(512, (p + 1) // 2) for p in pos]
+
+
 # ---------------------------------------------------------------- attention
 def zero_angle_table(rows):
     return np.ones((rows, 32), np.float32), np.zeros((rows, 32), np.float32)
