@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 D, WINDOW, HI, DI, TOPK = 512, 128, 32, 128, 512
 OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_SCORES, OP_INDEX_POOL, OP_REINDEX = 1, 2, 3, 4, 5, 6
 POOL_BLOCKS = 2048
+ABI_VERSION = 2
 
 _lib = None
 
@@ -42,27 +43,28 @@ def lib() -> ctypes.CDLL:
         L.csa2_status_string.argtypes = [i32]
         L.csa2_workspace_size.restype = sz
         L.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i64]
-        L.csa2_compress.argtypes = [i32, i32] + [vp] * 9 + [i64] + [vp] * 4 + [i64, vp]
+        L.csa2_compress.argtypes = [i32, i32] + [vp] * 9 + [i64] + [vp] * 4 + [i64, i32, vp]
         L.csa2_encode_window.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, vp, i32, vp]
-        L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, vp, vp, i32, vp]
-        L.csa2_index_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, vp, sz, vp]
-        L.csa2_index_scores.argtypes = [i32, i32] + [vp] * 6 + [i64, vp, vp, sz, vp]
-        L.csa2_index_pool.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
-        L.csa2_reindex_topk.argtypes = [i32, i32] + [vp] * 6 + [i64] + [vp] * 5 + [sz, vp]
+        L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, i32, vp, vp, i32,
+                                                                          vp]
+        L.csa2_index_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, i32, vp, vp, vp, sz, vp]
+        L.csa2_index_scores.argtypes = [i32, i32] + [vp] * 6 + [i64, i32, vp, vp, sz, vp]
+        L.csa2_index_pool.argtypes = [i32, i32] + [vp] * 6 + [i64, i32] + [vp] * 5 + [sz, vp]
+        L.csa2_reindex_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, i32] + [vp] * 5 + [sz, vp]
         L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64] +
                                        [vp] * 5 + [i64, vp, vp, vp, vp, sz, vp])
-        L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, vp, vp,
-                                   vp, i32, vp, vp, vp, vp, vp, sz, vp])
+        L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, i32, vp,
+                                   vp, vp, i32, vp, vp, vp, vp, vp, sz, vp])
         L.csa2_encode_fp4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_encode_fp8_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_decode_fp4_rows.argtypes = [vp, vp, i64, i32, vp, vp]
         L.csa2_decode_fp8_rows.argtypes = [vp, i64, i32, vp, vp]
-        for name in ("csa2_compress", "csa2_encode_window", "csa2_index_topk", "csa2_index_scores",
-                     "csa2_sparse_attn",
+        for name in ("csa2_compress", "csa2_encode_window", "csa2_append", "csa2_index_topk",
+                     "csa2_index_scores", "csa2_index_pool", "csa2_reindex_topk", "csa2_sparse_attn",
                      "csa2_forward", "csa2_encode_fp4_rows", "csa2_encode_fp8_rows",
                      "csa2_decode_fp4_rows", "csa2_decode_fp8_rows"):
             getattr(L, name).restype = i32
-        if L.csa2_abi_version() != 1:
+        if L.csa2_abi_version() != ABI_VERSION:
             raise CSA2Error("libcsa2.so ABI version mismatch")
         _lib = L
     return _lib
@@ -111,7 +113,7 @@ def workspace(op: int, B: int, Tq: int, H: int, entry_stride: int, device="cuda"
 
 
 def csa2_compress(pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin, z_codes,
-                  z_scales, ki_codes, ki_scales, stream=None):
+                  z_scales, ki_codes, ki_scales, stream=None, ratio=2):
     B, T = kc.shape[0], kc.shape[1]
     _check(lib().csa2_compress(B, T, _p(pos0, "i32", "pos0"), _p(kc, "bf16", "kc"),
                                _p(gc, "bf16", "gc"), _p(gamma_c, "f32", "gamma_c"),
@@ -120,7 +122,7 @@ def csa2_compress(pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rop
                                _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                                _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                                _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                               z_codes.shape[1], _stream(stream)), "csa2_compress")
+                               z_codes.shape[1], ratio, _stream(stream)), "csa2_compress")
 
 
 def csa2_encode_window(pos0, wn, rope_cos, rope_sin, w_codes, w_scale, stream=None):
@@ -134,7 +136,8 @@ def csa2_encode_window(pos0, wn, rope_cos, rope_sin, w_codes, w_scale, stream=No
 
 
 def csa2_append(pos, kc, gc, wn, pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
-                rope_sin, z_codes, z_scales, ki_codes, ki_scales, w_codes, w_scale, stream=None):
+                rope_sin, z_codes, z_scales, ki_codes, ki_scales, w_codes, w_scale, stream=None,
+                ratio=2):
     B = kc.shape[0]
     _check(lib().csa2_append(B, _p(pos, "i32", "pos"), _p(kc, "bf16", "kc"), _p(gc, "bf16", "gc"),
                              _p(wn, "bf16", "wn"), _p(pair_kc, "bf16", "pair_kc"),
@@ -144,16 +147,17 @@ def csa2_append(pos, kc, gc, wn, pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_g
                              _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                              _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                              _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                             z_codes.shape[1], _p(w_codes, "u8", "w_codes"),
+                             z_codes.shape[1], ratio, _p(w_codes, "u8", "w_codes"),
                              _p(w_scale, "f32", "w_scale"), w_codes.shape[1], _stream(stream)),
            "csa2_append")
 
-def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws, stream=None):
+def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws, stream=None,
+                    ratio=2):
     B, Tq = qI.shape[0], qI.shape[1]
     _check(lib().csa2_index_topk(B, Tq, _p(q_pos0, "i32", "q_pos0"),
                                  _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
                                  _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
-                                 _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                 _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1], ratio,
                                  _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"), _p(ws, None, "ws"),
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "csa2_index_topk")
@@ -161,12 +165,12 @@ def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws
 
 
 def csa2_index_pool(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, pool, pool_cnt, ws,
-                    stream=None):
+                    stream=None, ratio=2):
     B, Tq = qI.shape[0], qI.shape[1]
     _check(lib().csa2_index_pool(B, Tq, _p(q_pos0, "i32", "q_pos0"),
                                  _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
                                  _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
-                                 _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                 _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1], ratio,
                                  _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                                  _p(pool, "i32", "pool"), _p(pool_cnt, "i32", "pool_cnt"),
                                  _p(ws, None, "ws"), ws.numel() * ws.element_size(),
@@ -175,24 +179,25 @@ def csa2_index_pool(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, po
 
 
 def csa2_reindex_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, pool, pool_cnt, idx, cnt,
-                      ws, stream=None):
+                      ws, stream=None, ratio=2):
     B, Tq = qI.shape[0], qI.shape[1]
     _check(lib().csa2_reindex_topk(B, Tq, _p(q_pos0, "i32", "q_pos0"),
                                    _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
                                    _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
-                                   _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                   _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1], ratio,
                                    _p(pool, "i32", "pool"), _p(pool_cnt, "i32", "pool_cnt"),
                                    _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                                    _p(ws, None, "ws"), ws.numel() * ws.element_size(),
                                    _stream(stream)),
            "csa2_reindex_topk")
 
-def csa2_index_scores(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, scores, ws, stream=None):
+def csa2_index_scores(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, scores, ws, stream=None,
+                      ratio=2):
     B, Tq = qI.shape[0], qI.shape[1]
     _check(lib().csa2_index_scores(B, Tq, _p(q_pos0, "i32", "q_pos0"),
                                    _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
                                    _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
-                                   _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                   _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1], ratio,
                                    _p(scores, "f32", "scores"), _p(ws, None, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream)),
            "csa2_index_scores")
@@ -217,7 +222,7 @@ def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, s
 def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, ki_codes,
                  ki_scales, w_codes, w_scale, idx, cnt, O, ws, kc=None, gc=None, wn=None,
                  gamma_c=None, w_ik=None, gamma_ik=None, ki_given=None, n_entries=None, lse=None,
-                 stream=None):
+                 stream=None, ratio=2):
     B, H, T = Q.shape[0], Q.shape[1], Q.shape[2]
     _check(lib().csa2_forward(B, T, H, _p(pos0, "i32", "pos0"), _p(kc, "bf16", "kc"),
                               _p(gc, "bf16", "gc"), _p(wn, "bf16", "wn"),
@@ -228,7 +233,7 @@ def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, k
                               _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                               _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                               _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                              z_codes.shape[1], _p(n_entries, "i32", "n_entries"),
+                              z_codes.shape[1], ratio, _p(n_entries, "i32", "n_entries"),
                               _p(w_codes, "u8", "w_codes"), _p(w_scale, "f32", "w_scale"),
                               w_codes.shape[1], _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                               _p(O, "bf16", "O"), _p(lse, "f32", "lse"), _p(ws, None, "ws"),

@@ -14,33 +14,33 @@ namespace csa2 {
 __global__ void k_compress(int, int, const int32_t*, const uint16_t*, const uint16_t*,
                            const float*, const uint16_t*, const float*, const uint16_t*,
                            const float*, const float*, int64_t, uint8_t*, uint8_t*, uint8_t*,
-                           uint8_t*, int64_t);
+                           uint8_t*, int64_t, int);
 __global__ void k_window_encode(int, int, const int32_t*, const uint16_t*, const float*,
                                 const float*, int64_t, uint8_t*, float*, int);
 __global__ void k_append(int, const int32_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                          uint16_t*, uint16_t*, const float*, const uint16_t*, const float*,
                          const uint16_t*, const float*, const float*, int64_t, uint8_t*, uint8_t*,
-                         uint8_t*, uint8_t*, int64_t, uint8_t*, float*, int);
+                         uint8_t*, uint8_t*, int64_t, uint8_t*, float*, int, int);
 __global__ void k_encode_fp4_rows(const uint16_t*, int64_t, int, uint8_t*, uint8_t*);
 __global__ void k_encode_fp8_rows(const uint16_t*, int64_t, int, uint8_t*, float*);
 __global__ void k_decode_fp4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
 __global__ void k_decode_fp8_rows(const uint8_t*, int64_t, int, uint16_t*);
-__global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*);
+__global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*, int);
 __global__ void k_quant_index_query(const uint16_t*, const float*, int64_t, uint8_t*, float*);
 template <int TOK>
 __global__ void k_index_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                const float*, const uint8_t*, const uint8_t*, int64_t, float*,
-                               int64_t, int, int);
+                               int64_t, int, int, int);
 __global__ void k_topk(int, int, const int32_t*, const int32_t*, const float*, int64_t, int64_t,
                        int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*, uint32_t*,
-                       const int32_t*);
+                       const int32_t*, int);
 __global__ void k_block_keys(int, int, const int32_t*, const int32_t*, int64_t, const float*,
-                             int64_t, uint32_t*, int64_t);
+                             int64_t, uint32_t*, int64_t, int);
 __global__ void k_pool_select(int, int, const int32_t*, const int32_t*, int64_t, const uint32_t*,
-                              int64_t, int32_t*, int32_t*);
+                              int64_t, int32_t*, int32_t*, int);
 __global__ void k_pool_scores(int, int, const int32_t*, const int32_t*, const uint8_t*,
                               const float*, const uint8_t*, const uint8_t*, int64_t,
-                              const int32_t*, const int32_t*, float*, int64_t, int32_t*);
+                              const int32_t*, const int32_t*, float*, int64_t, int32_t*, int);
 __global__ void k_pool_map(int64_t, const int32_t*, int32_t*);
 __global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const int32_t*,
                              const uint32_t*, int32_t*, int32_t*);
@@ -190,14 +190,18 @@ AttnWs attn_ws(int B, int Tq, int H) {
     return w;
 }
 
+// positions per compressed entry: 2 (pooled pairs) or 1 (one entry per
+// position); the kernels take its log2
+bool bad_ratio(int ratio) { return ratio != 1 && ratio != 2; }
+
 bool bad_sizes(int B, int Tq, int64_t stride) {
     return B < 1 || Tq < 0 || stride < 1 || (int64_t)B * Tq > (int64_t)0x7FFFFFFF;
 }
 
 void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                    const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                   const uint8_t* ki_scales, int64_t stride, float* Sc, int64_t s_stride, void* ws,
-                   hipStream_t st) {
+                   const uint8_t* ki_scales, int64_t stride, float* Sc, int64_t s_stride, int rsh,
+                   void* ws, hipStream_t st) {
     const IndexWs L = index_ws(B, Tq, stride);
     uint8_t* base = (uint8_t*)ws;
     uint8_t* q8 = base + L.q8;
@@ -214,24 +218,25 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
     const dim3 grid((unsigned)(tok == 4 ? (int64_t)B * cdiv(n_tg, 4) * n_ch : cdiv(items, 4)));
     if (tok == 1)
         hipLaunchKernelGGL(k_index_scores<1>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
     else if (tok == 8)
         hipLaunchKernelGGL(k_index_scores<8>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
     else
         hipLaunchKernelGGL(k_index_scores<4>, grid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8,
-                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch);
+                           wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
 }
 
 csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                          const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                         const uint8_t* ki_scales, int64_t stride, int32_t* idx, int32_t* cnt,
-                         void* ws, hipStream_t st) {
+                         const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
+                         int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
     const IndexWs L = index_ws(B, Tq, stride);
     float* Sc = (float*)((uint8_t*)ws + L.S);
     const int64_t pitch = score_pitch(stride);
-    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, pitch, ws, st);
+    launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, pitch, rsh, ws,
+                  st);
     const int64_t rows = (int64_t)B * Tq;
     const int nseg = topk_segments(rows, stride);
     const int seg_len = topk_seg_len(stride, nseg);
@@ -241,7 +246,7 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     uint32_t* seg_kth = (uint32_t*)((uint8_t*)ws + L.seg_kth);
     hipLaunchKernelGGL(k_topk, dim3((unsigned)cdiv(rows * nseg, 4)), dim3(256), 0, st, B, Tq,
                        q_pos0, n_entries, Sc, pitch, stride, nseg, seg_len, idx, cnt, seg_key,
-                       seg_j, seg_n, seg_kth, (const int32_t*)nullptr);
+                       seg_j, seg_n, seg_kth, (const int32_t*)nullptr, rsh);
     if (nseg > 1)
         hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
                            (int)rows, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
@@ -328,19 +333,21 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
                           const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
                           const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
                           uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                          int64_t entry_stride, void* stream) {
+                          int64_t entry_stride, int ratio, void* stream) {
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "compress: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
-    if (!pos0 || !kc || !gc || !gamma_c || !rope_cos || !rope_sin || !z_codes || !z_scales ||
-        !ki_codes || !ki_scales)
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "compress: ratio=%d (need 1 or 2)", ratio);
+    if (!pos0 || !kc || (ratio == 2 && !gc) || !gamma_c || !rope_cos || !rope_sin || !z_codes ||
+        !z_scales || !ki_codes || !ki_scales)
         return fail(CSA2_ERR_NULL, "compress: a required pointer is NULL");
     if (w_ik ? !gamma_ik : !ki_given)
         return fail(CSA2_ERR_NULL, "compress: need w_ik+gamma_ik (derive) or ki_given (given)");
     if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "compress: empty rotary table");
-    const int64_t items = (int64_t)B * (T / 2);
+    const int rsh = ratio == 2 ? 1 : 0;
+    const int64_t items = (int64_t)B * (T >> rsh);
     if (items == 0) return ok();
     hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, S(stream), B, T,
                        pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
-                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride);
+                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, rsh);
     csa2_status s = check_launch("csa2_compress");
     return s == CSA2_OK ? ok() : s;
 }
@@ -365,12 +372,14 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
                         const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
                         const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
                         int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
-                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride,
+                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride, int ratio,
                         uint8_t* w_codes, float* w_scale, int cap, void* stream) {
     if (B < 0 || entry_stride < 1 || cap < 1)
         return fail(CSA2_ERR_SHAPE, "append: B=%d stride=%lld cap=%d", B, (long long)entry_stride, cap);
-    if (!pos || !kc || !gc || !wn || !pair_kc || !pair_gc || !gamma_c || !rope_cos || !rope_sin ||
-        !z_codes || !z_scales || !ki_codes || !ki_scales || !w_codes || !w_scale)
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "append: ratio=%d (need 1 or 2)", ratio);
+    if (!pos || !kc || !wn || (ratio == 2 && (!gc || !pair_kc || !pair_gc)) || !gamma_c ||
+        !rope_cos || !rope_sin || !z_codes || !z_scales || !ki_codes || !ki_scales || !w_codes ||
+        !w_scale)
         return fail(CSA2_ERR_NULL, "append: a required pointer is NULL");
     if (w_ik ? !gamma_ik : !ki_given)
         return fail(CSA2_ERR_NULL, "append: need w_ik+gamma_ik (derive) or ki_given (given)");
@@ -379,32 +388,36 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
     hipLaunchKernelGGL(k_append, dim3((unsigned)B), dim3(128), 0, S(stream), B, pos, kc, gc, wn,
                        pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
                        rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, w_codes,
-                       w_scale, cap);
+                       w_scale, cap, ratio == 2 ? 1 : 0);
     csa2_status s = check_launch("csa2_append");
     return s == CSA2_OK ? ok() : s;
 }
 
 csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
-                            int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+                            const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                            int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes,
+                            void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_topk: ratio=%d (need 1 or 2)", ratio);
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
     const size_t need = index_ws(B, Tq, entry_stride).total;
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
-                                 entry_stride, idx, cnt, ws, S(stream));
+                                 entry_stride, ratio == 2 ? 1 : 0, idx, cnt, ws, S(stream));
     return s == CSA2_OK ? ok() : s;
 }
 
 csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
-                            int32_t* cnt, int32_t* pool, int32_t* pool_cnt, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                            int32_t* idx, int32_t* cnt, int32_t* pool, int32_t* pool_cnt,
+                            void* ws, size_t ws_bytes, void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_pool: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_pool: ratio=%d (need 1 or 2)", ratio);
+    const int rsh = ratio == 2 ? 1 : 0;
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt || !pool ||
         !pool_cnt)
         return fail(CSA2_ERR_NULL, "index_pool: a required pointer is NULL");
@@ -414,26 +427,28 @@ csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (Tq == 0) return ok();
     hipStream_t st = S(stream);
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
-                                 entry_stride, idx, cnt, ws, st);
+                                 entry_stride, rsh, idx, cnt, ws, st);
     if (s != CSA2_OK) return s;
     const float* Sc = (const float*)((uint8_t*)ws + L.ix.S);
     uint32_t* keys = (uint32_t*)((uint8_t*)ws + L.keys);
     const int64_t rows = (int64_t)B * Tq;
     hipLaunchKernelGGL(k_block_keys, dim3((unsigned)cdiv(rows * L.kpad, 256)), dim3(256), 0, st, B,
                        Tq, q_pos0, n_entries, entry_stride, Sc, score_pitch(entry_stride), keys,
-                       L.kpad);
+                       L.kpad, rsh);
     hipLaunchKernelGGL(k_pool_select, dim3((unsigned)rows), dim3(256), 0, st, B, Tq, q_pos0,
-                       n_entries, entry_stride, keys, L.kpad, pool, pool_cnt);
+                       n_entries, entry_stride, keys, L.kpad, pool, pool_cnt, rsh);
     s = check_launch("csa2_index_pool");
     return s == CSA2_OK ? ok() : s;
 }
 
 csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                              const uint8_t* ki_scales, int64_t entry_stride, const int32_t* pool,
-                              const int32_t* pool_cnt, int32_t* idx, int32_t* cnt, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                              const int32_t* pool, const int32_t* pool_cnt, int32_t* idx,
+                              int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "reindex_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "reindex_topk: ratio=%d (need 1 or 2)", ratio);
+    const int rsh = ratio == 2 ? 1 : 0;
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !pool || !pool_cnt ||
         !idx || !cnt)
         return fail(CSA2_ERR_NULL, "reindex_topk: a required pointer is NULL");
@@ -454,7 +469,7 @@ csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_
     const int64_t pitch = score_pitch(POOL_CAND);
     hipLaunchKernelGGL(k_pool_scores, dim3((unsigned)cdiv(rows * (POOL_BLOCKS / 128), 4)),
                        dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8, wq, ki_codes, ki_scales,
-                       entry_stride, pool, pool_cnt, Sc, pitch, len);
+                       entry_stride, pool, pool_cnt, Sc, pitch, len, rsh);
     const int nseg = topk_segments(rows, POOL_CAND);
     const int seg_len = topk_seg_len(POOL_CAND, nseg);
     uint32_t* seg_key = (uint32_t*)(base + L.ix.seg_key);
@@ -463,7 +478,7 @@ csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_
     uint32_t* seg_kth = (uint32_t*)(base + L.ix.seg_kth);
     hipLaunchKernelGGL(k_topk, dim3((unsigned)cdiv(rows * nseg, 4)), dim3(256), 0, st, B, Tq,
                        q_pos0, n_entries, Sc, pitch, POOL_CAND, nseg, seg_len, idx, cnt, seg_key,
-                       seg_j, seg_n, seg_kth, (const int32_t*)len);
+                       seg_j, seg_n, seg_kth, (const int32_t*)len, rsh);
     if (nseg > 1)
         hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, st,
                            (int)rows, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
@@ -475,9 +490,10 @@ csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_
 
 csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                              const uint8_t* ki_scales, int64_t entry_stride, float* scores,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                              float* scores, void* ws, size_t ws_bytes, void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_scores: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_scores: ratio=%d (need 1 or 2)", ratio);
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !scores)
         return fail(CSA2_ERR_NULL, "index_scores: a required pointer is NULL");
     const size_t need = index_ws(B, Tq, entry_stride).S;
@@ -485,8 +501,7 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
         return fail(CSA2_ERR_WORKSPACE, "index_scores: workspace %zu < %zu bytes", ws_bytes, need);
     if (Tq == 0) return ok();
     launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, scores,
-                  entry_stride, ws,
-                  S(stream));
+                  entry_stride, ratio == 2 ? 1 : 0, ws, S(stream));
     csa2_status s = check_launch("csa2_index_scores");
     return s == CSA2_OK ? ok() : s;
 }
@@ -521,17 +536,20 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
                          const float* rope_cos, const float* rope_sin, int64_t rope_rows,
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
-                         uint8_t* ki_scales, int64_t entry_stride, const int32_t* n_entries,
-                         uint8_t* w_codes, float* w_scale, int cap, int32_t* idx, int32_t* cnt,
-                         uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                         const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
+                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "forward: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "forward: ratio=%d (need 1 or 2)", ratio);
+    const int rsh = ratio == 2 ? 1 : 0;
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "forward: H=%d (need 16, 32, 48 or 64)", H);
     const bool prefill = kc != nullptr;
     if (!pos0 || !Q || !qI || !wI || !sink || !rope_cos || !rope_sin || !z_codes || !z_scales ||
         !ki_codes || !ki_scales || !w_codes || !w_scale || !idx || !cnt || !O)
         return fail(CSA2_ERR_NULL, "forward: a required pointer is NULL");
-    if (prefill && (!gc || !wn || !gamma_c || (w_ik ? !gamma_ik : !ki_given)))
-        return fail(CSA2_ERR_NULL, "forward: prefill needs gc, wn, gamma_c and w_ik+gamma_ik or ki_given");
+    if (prefill && ((ratio == 2 && !gc) || !wn || !gamma_c || (w_ik ? !gamma_ik : !ki_given)))
+        return fail(CSA2_ERR_NULL, "forward: prefill needs gc (ratio 2), wn, gamma_c and w_ik+gamma_ik or ki_given");
     if (!prefill && !n_entries) return fail(CSA2_ERR_NULL, "forward: decode needs n_entries");
     if ((int64_t)cap < (int64_t)T + WINDOW - 1)
         return fail(CSA2_ERR_RANGE, "forward: window ring cap=%d < T+127=%lld", cap, (long long)T + WINDOW - 1);
@@ -549,22 +567,22 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                            cap);
     }
     if (prefill) {
-        const int64_t items = (int64_t)B * (T / 2);
+        const int64_t items = (int64_t)B * (T >> rsh);
         if (items > 0)
             hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st, B, T,
                                pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
                                rope_sin, rope_rows, z_codes, z_scales, ki_codes, ki_scales,
-                               entry_stride);
+                               entry_stride, rsh);
         if (!n_entries) {
             hipLaunchKernelGGL(k_prefill_entries, dim3((unsigned)cdiv(B, 256)), dim3(256), 0, st,
-                               B, T, pos0, entry_stride, ne);
+                               B, T, pos0, entry_stride, ne, rsh);
             n_entries = ne;
         }
     }
     csa2_status s = check_launch("csa2_forward (encode)");
     if (s != CSA2_OK) return s;
-    s = launch_index(B, T, pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, idx, cnt,
-                     ws, st);
+    s = launch_index(B, T, pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, rsh, idx,
+                     cnt, ws, st);
     if (s != CSA2_OK) return s;
     s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride, idx,
                     cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, nullptr, ws, st);

@@ -7,7 +7,10 @@
 // Attention RMSNorm"); rotation of channels 448..511 at position 2j; FP4
 // storage; the index-key projection 512->128, its RMSNorm, rotation of
 // channels 64..127 at 2j and FP4 storage; the window rows rotated at their own
-// position and stored FP8.
+// position and stored FP8.  At compression ratio one ("Inside DeepSeek V4.1
+// Flash: Deriving the 890-Byte KV Cache", CSA2 section) entry j is position j
+// alone: the softmax over its single gate logit is 1, so the pooled key is its
+// k^c, and both rotations are at j.
 //
 // Every value that decides a storage code is computed in fp32 with a fixed
 // operation order (no contraction, explicit fma where one is meant,
@@ -25,7 +28,8 @@
 namespace csa2 {
 
 // Entry j of request b from its two tokens' rows (pooled keys ka, kb and gate
-// logits ga, gb; 512 bf16 each), on one wave: lane l owns channels 8l..8l+7 of
+// logits ga, gb; 512 bf16 each), or from the one row ka when kb_row is NULL
+// (ratio one; no gate is read), on one wave: lane l owns channels 8l..8l+7 of
 // the 512-wide row and channels 2l, 2l+1 of the 128-wide index key.  ki_row is
 // the given index key (128 bf16) when w_ik is NULL.  c_lds and ki_lds are this
 // wave's scratch rows in LDS (512 and 128 floats).
@@ -39,22 +43,29 @@ __device__ __forceinline__ void compress_entry(
     uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
     uint8_t* __restrict__ ki_scales, int64_t entry_stride) {
     // ---- pair gate --------------------------------------------------------
-    const uint4 ka = *(const uint4*)(ka_row + 8 * lane), kb = *(const uint4*)(kb_row + 8 * lane);
-    const uint4 ga = *(const uint4*)(ga_row + 8 * lane), gb = *(const uint4*)(gb_row + 8 * lane);
-    const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w}, kbw[4] = {kb.x, kb.y, kb.z, kb.w};
-    const uint32_t gaw[4] = {ga.x, ga.y, ga.z, ga.w}, gbw[4] = {gb.x, gb.y, gb.z, gb.w};
+    const uint4 ka = *(const uint4*)(ka_row + 8 * lane);
+    const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
     float kp[8];
+    if (!kb_row) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int w = i >> 1, sh = (i & 1) * 16;
-        const float a = bf2f((uint16_t)(gaw[w] >> sh)), bb = bf2f((uint16_t)(gbw[w] >> sh));
-        const float m = fmaxf(a, bb);
-        const float ea = exp_neg(a - m), eb = exp_neg(bb - m);
-        const float s = ea + eb;
-        const float wa = div_rn(ea, s), wb = div_rn(eb, s);
-        const float pa = wa * bf2f((uint16_t)(kaw[w] >> sh));
-        const float pb = wb * bf2f((uint16_t)(kbw[w] >> sh));
-        kp[i] = pa + pb;
+        for (int i = 0; i < 8; ++i) kp[i] = bf2f((uint16_t)(kaw[i >> 1] >> ((i & 1) * 16)));
+    } else {
+        const uint4 kb = *(const uint4*)(kb_row + 8 * lane);
+        const uint4 ga = *(const uint4*)(ga_row + 8 * lane), gb = *(const uint4*)(gb_row + 8 * lane);
+        const uint32_t kbw[4] = {kb.x, kb.y, kb.z, kb.w};
+        const uint32_t gaw[4] = {ga.x, ga.y, ga.z, ga.w}, gbw[4] = {gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int w = i >> 1, sh = (i & 1) * 16;
+            const float a = bf2f((uint16_t)(gaw[w] >> sh)), bb = bf2f((uint16_t)(gbw[w] >> sh));
+            const float m = fmaxf(a, bb);
+            const float ea = exp_neg(a - m), eb = exp_neg(bb - m);
+            const float s = ea + eb;
+            const float wa = div_rn(ea, s), wb = div_rn(eb, s);
+            const float pa = wa * bf2f((uint16_t)(kaw[w] >> sh));
+            const float pb = wb * bf2f((uint16_t)(kbw[w] >> sh));
+            kp[i] = pa + pb;
+        }
     }
 
     // ---- RMSNorm over 512: lane = group of 8 channels ----------------------
@@ -72,7 +83,7 @@ __device__ __forceinline__ void compress_entry(
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = gamma_c[8 * lane + i] * (kp[i] * rr);
 
-    // ---- Z: rotate channels 448.. at 2j, FP4 ------------------------------
+    // ---- Z: rotate channels 448.. at the entry's position, FP4 -------------
     float z[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = c[i];
@@ -165,7 +176,8 @@ __device__ __forceinline__ void compress_entry(
     }
 }
 
-// One wave (64 lanes) per compressed entry of the call's token pairs.
+// One wave (64 lanes) per compressed entry of the call: a token pair (ratio
+// 2, rsh = 1) or one token (ratio 1, rsh = 0).
 __global__ void __launch_bounds__(256) k_compress(
     int B, int T, const int32_t* __restrict__ pos0, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ gc, const float* __restrict__ gamma_c,
@@ -173,20 +185,21 @@ __global__ void __launch_bounds__(256) k_compress(
     const uint16_t* __restrict__ ki_given, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint8_t* __restrict__ z_codes,
     uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
-    uint8_t* __restrict__ ki_scales, int64_t entry_stride) {
+    uint8_t* __restrict__ ki_scales, int64_t entry_stride, int rsh) {
     __shared__ float c_lds[4][D];
     __shared__ float ki_lds[4][DI];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nloc = T / 2;
+    const int nloc = T >> rsh;
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
     if (item >= (int64_t)B * nloc) return;
     const int b = (int)(item / nloc), jl = (int)(item % nloc);
-    const int64_t j = (int64_t)(pos0[b] >> 1) + jl;
+    const int64_t j = (int64_t)(pos0[b] >> rsh) + jl;
     if (j < 0 || j >= entry_stride) return;
-    int64_t prow = 2 * j;
+    int64_t prow = j << rsh;
     if (prow >= rope_rows) prow = rope_rows - 1;
-    const int64_t r0 = ((int64_t)b * T + 2 * jl) * D;
-    compress_entry(b, j, lane, kc + r0, kc + r0 + D, gc + r0, gc + r0 + D,
+    const int64_t r0 = ((int64_t)b * T + ((int64_t)jl << rsh)) * D;
+    compress_entry(b, j, lane, kc + r0, rsh ? kc + r0 + D : nullptr, rsh ? gc + r0 : nullptr,
+                   rsh ? gc + r0 + D : nullptr,
                    w_ik ? nullptr : ki_given + ((int64_t)b * nloc + jl) * DI, gamma_c, w_ik,
                    gamma_ik, rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds[wave], ki_lds[wave],
                    z_codes, z_scales, ki_codes, ki_scales, entry_stride);
@@ -255,7 +268,9 @@ __global__ void __launch_bounds__(256) k_window_encode(
 // a pair: its pooled key and gate logits wait in the pair buffer.  A token at
 // an odd position closes the pair 2j, 2j+1 (j = pos / 2): entry j is computed
 // from the buffered token and this one, exactly as the prefill path computes it.
-// One block of two waves per request: wave 0 the window row, wave 1 the pair.
+// At ratio one (rsh = 0) every token writes its own entry j = pos and the pair
+// buffer is not used.
+// One block of two waves per request: wave 0 the window row, wave 1 the entry.
 __global__ void __launch_bounds__(128) k_append(
     int B, const int32_t* __restrict__ pos, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ gc, const uint16_t* __restrict__ wn,
@@ -265,7 +280,7 @@ __global__ void __launch_bounds__(128) k_append(
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t rope_rows,
     uint8_t* __restrict__ z_codes, uint8_t* __restrict__ z_scales,
     uint8_t* __restrict__ ki_codes, uint8_t* __restrict__ ki_scales, int64_t entry_stride,
-    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap) {
+    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap, int rsh) {
     __shared__ float c_lds[D];
     __shared__ float ki_lds[DI];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -278,6 +293,13 @@ __global__ void __launch_bounds__(128) k_append(
         const int64_t prow = p < rope_rows ? p : rope_rows - 1;
         window_row((int64_t)b * cap + (p % cap), prow, lane, wn + row, rcos, rsin, w_codes,
                    w_scale);
+    } else if (rsh == 0) {
+        if (p >= entry_stride) return;
+        const int64_t prow = p < rope_rows ? p : rope_rows - 1;
+        compress_entry(b, p, lane, kc + row, nullptr, nullptr, nullptr,
+                       w_ik ? nullptr : ki_given + (int64_t)b * DI, gamma_c, w_ik, gamma_ik,
+                       rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds, ki_lds, z_codes,
+                       z_scales, ki_codes, ki_scales, entry_stride);
     } else if ((p & 1) == 0) {
         *(uint4*)(pair_kc + row + 8 * lane) = *(const uint4*)(kc + row + 8 * lane);
         *(uint4*)(pair_gc + row + 8 * lane) = *(const uint4*)(gc + row + 8 * lane);
@@ -388,12 +410,12 @@ __global__ void k_decode_fp8_rows(const uint8_t* __restrict__ codes, int64_t row
     *(uint4*)(out + r * cols + 8 * c8) = o;
 }
 
-// n_entries[b] = floor((pos0[b] + T) / 2), clamped to the cache.
+// n_entries[b] = floor((pos0[b] + T) / ratio), clamped to the cache.
 __global__ void k_prefill_entries(int B, int T, const int32_t* __restrict__ pos0,
-                                  int64_t entry_stride, int32_t* __restrict__ n_entries) {
+                                  int64_t entry_stride, int32_t* __restrict__ n_entries, int rsh) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
-    int64_t n = ((int64_t)pos0[b] + T) / 2;
+    int64_t n = ((int64_t)pos0[b] + T) >> rsh;
     if (n > entry_stride) n = entry_stride;
     if (n < 0) n = 0;
     n_entries[b] = (int32_t)n;

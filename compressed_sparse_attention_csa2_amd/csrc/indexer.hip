@@ -60,9 +60,12 @@ __global__ void __launch_bounds__(256) k_quant_index_query(const uint16_t* __res
 }
 
 
+// Causal candidates of the query at p = qpos0 + t: entries j < floor((p+1)/ratio)
+// (ratio = 1 << rsh: 2 for pooled pairs, 1 for one entry per position), at
+// most the request's n_ent valid rows and the cache's stride.
 __device__ __forceinline__ int64_t cand_count(int32_t qpos0, int t, int32_t n_ent,
-                                              int64_t stride) {
-    int64_t n = ((int64_t)qpos0 + t + 1) / 2;
+                                              int64_t stride, int rsh) {
+    int64_t n = ((int64_t)qpos0 + t + 1) >> rsh;
     int64_t cap = n_ent < 0 ? 0 : (int64_t)n_ent;
     if (cap > stride) cap = stride;
     return n < cap ? (n < 0 ? 0 : n) : cap;
@@ -98,7 +101,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const uint8_t* __restrict__ q8, const float* __restrict__ wq,
     const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
-    int64_t entry_stride, float* __restrict__ S, int64_t s_stride, int n_tg, int n_ch) {
+    int64_t entry_stride, float* __restrict__ S, int64_t s_stride, int n_tg, int n_ch, int rsh) {
     static_assert(TOK == 1 || TOK % 4 == 0, "token slots per wave");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     int b, tg, ch;
@@ -129,7 +132,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     const int t0 = tg * TOK;
     const int32_t qp = q_pos0[b], ne = n_entries[b];
     const int tlast = (t0 + TOK - 1 < Tq) ? t0 + TOK - 1 : Tq - 1;
-    const int64_t n_max = cand_count(qp, tlast, ne, entry_stride);
+    const int64_t n_max = cand_count(qp, tlast, ne, entry_stride, rsh);
     const int64_t j_begin = (int64_t)ch * IDX_CHUNK;
     if (j_begin >= n_max) return;
     const int j_len = (int)((j_begin + IDX_CHUNK < n_max) ? IDX_CHUNK : n_max - j_begin);
@@ -142,7 +145,7 @@ __global__ void __launch_bounds__(256) k_index_scores(
     for (int k = 0; k < TOK; ++k) {
         const int t = t0 + k;
         const bool ok = t < Tq;
-        const int64_t nk = ok ? cand_count(qp, t, ne, entry_stride) - j_begin : 0;
+        const int64_t nk = ok ? cand_count(qp, t, ne, entry_stride, rsh) - j_begin : 0;
         ncand[k] = nk < 0 ? 0 : (int)nk;
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -601,7 +604,7 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
     const float* __restrict__ S, int64_t spad, int64_t entry_stride, int nseg, int seg_len,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, uint32_t* __restrict__ seg_key,
     int32_t* __restrict__ seg_j, int32_t* __restrict__ seg_n, uint32_t* __restrict__ seg_kth,
-    const int32_t* __restrict__ row_len) {
+    const int32_t* __restrict__ row_len, int rsh) {
     __shared__ WaveSel sel[WS_WAVES];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * WS_WAVES + wave;
@@ -611,7 +614,7 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
     // the list is the row's causal candidates, or (row_len given) its first
     // row_len[row] scores, e.g. the candidates of a hierarchical pool
-    int64_t n = row_len ? (int64_t)row_len[row] : cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    int64_t n = row_len ? (int64_t)row_len[row] : cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
     if (n > (int64_t)nseg * seg_len) n = (int64_t)nseg * seg_len;
     const int64_t j0 = (int64_t)seg * seg_len;
     int len = (int)(n - j0 < seg_len ? n - j0 : seg_len);
@@ -769,13 +772,13 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
 __global__ void __launch_bounds__(256) k_block_keys(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     int64_t entry_stride, const float* __restrict__ S, int64_t spad,
-    uint32_t* __restrict__ keys, int64_t kpad) {
+    uint32_t* __restrict__ keys, int64_t kpad, int rsh) {
     const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (item >= (int64_t)B * Tq * kpad) return;
     const int64_t row = item / kpad;
     const int64_t k = item - row * kpad;
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
-    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
     if (8 * k >= n) return;
     const float* src = S + row * spad + 8 * k;        // 32-byte aligned (spad % 64 == 0)
     const float4 a = *(const float4*)src, c = *(const float4*)(src + 4);
@@ -818,7 +821,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wsum, u
 __global__ void __launch_bounds__(256) k_pool_select(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     int64_t entry_stride, const uint32_t* __restrict__ keys, int64_t kpad,
-    int32_t* __restrict__ pool, int32_t* __restrict__ pool_cnt) {
+    int32_t* __restrict__ pool, int32_t* __restrict__ pool_cnt, int rsh) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t bc[4];
@@ -826,7 +829,7 @@ __global__ void __launch_bounds__(256) k_pool_select(
     const int64_t row = blockIdx.x;
     if (row >= (int64_t)B * Tq) return;
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
-    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
     const int nb = (int)((n + 7) / 8);
     int32_t* out = pool + row * POOL_BLOCKS;
     if (nb <= POOL_BLOCKS) {
@@ -952,7 +955,7 @@ __global__ void __launch_bounds__(256) k_pool_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ wq,
     const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
     int64_t entry_stride, const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_cnt,
-    float* __restrict__ Sc, int64_t scpad, int32_t* __restrict__ row_len) {
+    float* __restrict__ Sc, int64_t scpad, int32_t* __restrict__ row_len, int rsh) {
     constexpr int SLOTS = 128;
     constexpr int NPC = POOL_BLOCKS / SLOTS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -961,7 +964,7 @@ __global__ void __launch_bounds__(256) k_pool_scores(
     const int64_t row = item / NPC;
     const int pc = (int)(item - row * NPC);
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
-    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride);
+    const int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
     const int cntp = pool_cnt[row];
     const int64_t nb = (n + 7) / 8;
     if (pc == 0 && lane == 0) row_len[row] = cntp > 0 ? (int32_t)(n - 8 * (nb - cntp)) : 0;
@@ -1024,12 +1027,12 @@ __global__ void __launch_bounds__(256) k_pool_map(int64_t rows, const int32_t* _
 
 template __global__ void k_index_scores<1>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int64_t, int, int);
+                                           float*, int64_t, int, int, int);
 template __global__ void k_index_scores<4>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int64_t, int, int);
+                                           float*, int64_t, int, int, int);
 template __global__ void k_index_scores<8>(int, int, const int32_t*, const int32_t*, const uint8_t*,
                                            const float*, const uint8_t*, const uint8_t*, int64_t,
-                                           float*, int64_t, int, int);
+                                           float*, int64_t, int, int, int);
 
 }  // namespace csa2

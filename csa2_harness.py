@@ -40,10 +40,11 @@ class PrefillRun:
         assert wl.kind == "prefill"
         self.wl = wl
         B, T, H = wl.B, wl.Tq, wl.H
-        self.stride = max(T // 2, 1)
+        self.stride = max(T // wl.ratio, 1)
         cos_t, sin_t = synth.rope_table(wl.rope_rows)
         self.rope_cos, self.rope_sin = up(cos_t, dev), up(sin_t, dev)
-        self.kc, self.gc, self.wn = up(wl.kc(), dev), up(wl.gc(), dev), up(wl.wn(), dev)
+        self.kc, self.wn = up(wl.kc(), dev), up(wl.wn(), dev)
+        self.gc = up(wl.gc(), dev) if wl.ratio == 2 else None     # ratio 1 reads no gates
         self.Q = up(wl.Q(), dev)
         self.qI, self.wI = up(wl.qI(), dev), up(wl.wI(), dev)
         self.gamma_c, self.gamma_ik = up(wl.gamma_c(), dev), up(wl.gamma_ik(), dev)
@@ -71,7 +72,7 @@ class PrefillRun:
                           self.ki_scales, self.w_codes, self.w_scale, self.idx, self.cnt, self.O,
                           self.ws, kc=self.kc, gc=self.gc, wn=self.wn, gamma_c=self.gamma_c,
                           w_ik=self.w_ik, gamma_ik=self.gamma_ik, ki_given=self.ki_given,
-                          lse=self.lse, stream=stream)
+                          lse=self.lse, stream=stream, ratio=self.wl.ratio)
 
     def fetch(self, big=True) -> dict:
         out = dict(z_codes=down(self.z_codes), z_scales=down(self.z_scales),
@@ -129,7 +130,8 @@ class DecodeRun:
         csa2.csa2_forward(self.q_pos0, self.Q, self.qI, self.wI, self.sink, self.rope_cos,
                           self.rope_sin, self.z_codes, self.z_scales, self.ki_codes,
                           self.ki_scales, self.w_codes, self.w_scale, self.idx, self.cnt, self.O,
-                          self.ws, n_entries=self.n_entries, lse=self.lse, stream=stream)
+                          self.ws, n_entries=self.n_entries, lse=self.lse, stream=stream,
+                          ratio=self.wl.ratio)
 
     def fetch(self) -> dict:
         return dict(idx=down(self.idx), cnt=down(self.cnt), O=down(self.O), lse=down(self.lse))

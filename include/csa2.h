@@ -14,8 +14,15 @@
  *    in the bracketed order.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously; no call synchronises.
- *  - Positions are absolute token positions.  Compressed entry j pools the
- *    tokens at positions 2j and 2j+1 and is rotated at position 2j.
+ *  - Positions are absolute token positions.  `ratio` is the number of
+ *    positions per compressed entry [zharf, CSA2 section: compression ratio
+ *    one is a supported case; the decoder layers use it]:
+ *      ratio 2: entry j pools the tokens at positions 2j and 2j+1 and is
+ *               rotated at position 2j; a query at p sees j < floor((p+1)/2);
+ *      ratio 1: entry j is the token at position j alone (the pooling softmax
+ *               over one logit is 1, so no gate logits are read), rotated at
+ *               j; a query at p sees j <= p.
+ *    Any other ratio returns CSA2_ERR_UNSUPPORTED.
  *  - Caches (per request b, `entry_stride` entries apart):
  *      z_codes  [B][entry_stride][256]  E2M1 pairs, element 2i in the low nibble of byte i
  *      z_scales [B][entry_stride][16]   E8M0 bytes, one per 32 channels (2^(byte-127))
@@ -40,8 +47,9 @@
  *  [blog]   "Inside DeepSeek V4.1", sections "Attention that looks at 640
  *           places" and "890 bytes".
  *  [zharf]  "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache",
- *           sections "Deriving the 890 bytes per token" and "FP4 is a storage
- *           choice".
+ *           sections "Deriving the 890 bytes per token", "FP4 is a storage
+ *           choice", the CSA2 section and "Bounded replay trades exact state
+ *           for cheaper resumption".
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -53,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
     CSA2_OK = 0,
@@ -80,17 +88,19 @@ typedef enum {
  * Z_{j,448:} <- R_{2j} c_{j,448:}; Z <- FP4(Z); k^i = c W_IK; k^n = RMSNorm;
  * K^I_{j,64:} <- R_{2j} k^n_{j,64:}; K^I <- FP4(K^I)].
  *
- *  B, T      requests, new positions per request (T >= 0; floor(T/2) entries
- *            are written; an odd last position is left for the caller).
+ *  B, T      requests, new positions per request (T >= 0; floor(T/ratio)
+ *            entries are written; at ratio 2 an odd last position is left
+ *            for the caller).
  *  pos0      [B] int32 device: absolute position of each request's first new
- *            token; must be even.  Entry j = pos0/2 + i is written at cache
- *            row j (rows >= entry_stride are skipped).
- *  kc, gc    [B][T][512] bf16: pooled keys and gate logits of the new tokens.
+ *            token; even at ratio 2.  Entry j = pos0/ratio + i is written at
+ *            cache row j (rows >= entry_stride are skipped).
+ *  kc, gc    [B][T][512] bf16: pooled keys and gate logits of the new tokens
+ *            (gc is not read, and may be NULL, at ratio 1).
  *  gamma_c   [512] fp32 RMSNorm gain of the compressed rows.
  *  w_ik      [512][128] bf16 index-key projection, or NULL for given mode.
  *  gamma_ik  [128] fp32 gain of the index-key norm (derive mode only).
- *  ki_given  [B][T/2][128] bf16 given index keys (already normalised and
- *            rotated; only encoded), used when w_ik == NULL.
+ *  ki_given  [B][T/ratio][128] bf16 given index keys (already normalised
+ *            and rotated; only encoded), used when w_ik == NULL.
  *  rope_*    rotary table, rope_rows >= 1.
  *  outputs   z_codes, z_scales, ki_codes, ki_scales as described above.
  */
@@ -99,7 +109,7 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
                           const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
                           const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
                           uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                          int64_t entry_stride, void* stream);
+                          int64_t entry_stride, int ratio, void* stream);
 
 /*
  * Window rows [atlas: W_{t,448:} <- R_t w^n_{t,448:}; W <- FP8(W); blog: the
@@ -127,6 +137,8 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
  *     csa2_compress computes it from two tokens of one call, so appending
  *     tokens one at a time writes the same bytes as compressing them together.
  *     Rows j >= entry_stride are skipped.
+ *   - ratio 1: every token writes its own entry j = p (and its window row);
+ *     the pair buffer and gc are not used and may be NULL.
  *  pos        [B] int32 device, >= 0 (a negative position skips the request).
  *  kc, gc, wn [B][512] bf16: the new token's pooled key, gate logits, window vector.
  *  pair_kc, pair_gc [B][512] bf16 device, caller-owned state carried between
@@ -143,12 +155,13 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
                         const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
                         const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
                         int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
-                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride,
+                        uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride, int ratio,
                         uint8_t* w_codes, float* w_scale, int cap, void* stream);
 
 /*
  * Lightning indexer and causal top-512 [atlas: S^I_{t,j} = sum_h w^I_{t,h}
- * ReLU(Q^I_{h,t} . K^I_j); I_t = top_512(S^I_{t,j} : j < floor((t+1)/2));
+ * ReLU(Q^I_{h,t} . K^I_j); I_t = top_512(S^I_{t,j} : j < floor((t+1)/2)), with
+ * the entries' ratio in place of 2;
  * blog: 32 heads of 128, one key per entry].
  *  Tq        query tokens per request, at positions q_pos0[b] + i.
  *  q_pos0    [B] int32 device.   n_entries [B] int32 device: valid cache rows.
@@ -157,13 +170,14 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
  *  wI        [B][Tq][32] fp32 head weights (the 1/sqrt(128*32) already applied).
  *  idx       [B][Tq][512] int32 out: chosen entries in ascending order,
  *            padded with -1.  Ties: larger score, then smaller entry.
- *  cnt       [B][Tq] int32 out: min(512, min(floor((p+1)/2), n_entries)).
+ *  cnt       [B][Tq] int32 out: min(512, min(floor((p+1)/ratio), n_entries)).
  *  ws        workspace of at least csa2_workspace_size(CSA2_OP_INDEX_TOPK, ...).
  */
 csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
-                            int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+                            const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                            int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /*
  * Full-layer selection plus the hierarchical candidate pool [blog: the
@@ -180,9 +194,9 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
  */
 csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                             const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                            const uint8_t* ki_scales, int64_t entry_stride, int32_t* idx,
-                            int32_t* cnt, int32_t* pool, int32_t* pool_cnt, void* ws,
-                            size_t ws_bytes, void* stream);
+                            const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                            int32_t* idx, int32_t* cnt, int32_t* pool, int32_t* pool_cnt,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Reindex selection [same passages: a Reindex layer borrows the keys and the
@@ -197,21 +211,21 @@ csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t*
  */
 csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                              const uint8_t* ki_scales, int64_t entry_stride, const int32_t* pool,
-                              const int32_t* pool_cnt, int32_t* idx, int32_t* cnt, void* ws,
-                              size_t ws_bytes, void* stream);
+                              const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                              const int32_t* pool, const int32_t* pool_cnt, int32_t* idx,
+                              int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The indexer's raw scores without selection [atlas: S^I_{t,j} = sum_h
  * w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j)], same queries and keys as
  * csa2_index_topk.  scores [B][Tq][entry_stride] fp32: for query i of request
- * b only entries j < min(floor((p+1)/2), n_entries[b]) are written.
+ * b only entries j < min(floor((p+1)/ratio), n_entries[b]) are written.
  *  ws  at least csa2_workspace_size(CSA2_OP_INDEX_SCORES, ...) bytes.
  */
 csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
-                              const uint8_t* ki_scales, int64_t entry_stride, float* scores,
-                              void* ws, size_t ws_bytes, void* stream);
+                              const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                              float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Sparse shared-latent attention with a sink [atlas: J^w_t = {max(0,t-127)..t};
@@ -243,7 +257,7 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
  * The whole layer for one call.
  *  Prefill (kc != NULL): compress the T new positions, write their window
  *  rows, then select and attend for every new position; n_entries may be NULL
- *  (then floor((pos0+T)/2) per request).
+ *  (then floor((pos0+T)/ratio) per request).
  *  Decode (kc == NULL): caches are given.  If wn != NULL the new tokens'
  *  window rows are written first.  n_entries is required.
  *  Arguments as in the calls above; T is the number of query tokens.
@@ -254,9 +268,10 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
                          const float* rope_cos, const float* rope_sin, int64_t rope_rows,
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
-                         uint8_t* ki_scales, int64_t entry_stride, const int32_t* n_entries,
-                         uint8_t* w_codes, float* w_scale, int cap, int32_t* idx, int32_t* cnt,
-                         uint16_t* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+                         uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                         const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
+                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Bytes of workspace an op needs for these sizes (0 on invalid sizes). */
 size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride);

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 1
+    assert L.csa2_abi_version() == 2
     for s in range(7):
         assert L.csa2_status_string(s)
 
@@ -53,21 +53,30 @@ def test_rejects_before_launch(L):
     n = None
     # compress: NULL kc
     s = L.csa2_compress(1, 4, FAKE, n, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, n)
+                        FAKE, 8, 2, n)
     assert s == 1 and b"NULL" in L.csa2_last_error()
+    # compress: ratio 2 needs gate logits, ratio 1 does not; only ratios 1 and 2
+    s = L.csa2_compress(1, 4, FAKE, FAKE, n, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                        FAKE, 8, 2, n)
+    assert s == 1
+    s = L.csa2_compress(1, 4, FAKE, FAKE, n, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                        FAKE, 8, 3, n)
+    assert s == 3 and b"ratio" in L.csa2_last_error()
     # compress: negative T
     s = L.csa2_compress(1, -2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE,
-                        FAKE, FAKE, 8, n)
+                        FAKE, FAKE, 8, 2, n)
     assert s == 2
     # compress: neither projection nor given keys
     s = L.csa2_compress(1, 4, FAKE, FAKE, FAKE, FAKE, n, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, n)
+                        FAKE, 8, 2, n)
     assert s == 1
     # window: cap 0
     assert L.csa2_encode_window(1, 4, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, n) == 2
     # index: workspace too small
-    s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 16, n)
+    s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2, FAKE, FAKE, FAKE, 16, n)
     assert s == 5 and b"workspace" in L.csa2_last_error()
+    s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0, FAKE, FAKE, FAKE, 16, n)
+    assert s == 3 and b"ratio" in L.csa2_last_error()
     # attention: unsupported heads, small ring, missing workspace
     args = [FAKE] * 4 + [200, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
     assert L.csa2_sparse_attn(1, 8, 24, *args, 1 << 30, n) == 3
@@ -76,12 +85,12 @@ def test_rejects_before_launch(L):
     assert L.csa2_sparse_attn(4, 1, 64, *args, 0, n) == 5
     # forward: decode without n_entries
     s = L.csa2_forward(1, 1, 64, FAKE, n, n, n, n, n, n, n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
-                       FAKE, FAKE, FAKE, FAKE, 64, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n, FAKE,
+                       FAKE, FAKE, FAKE, FAKE, 64, 2, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n, FAKE,
                        1 << 30, n)
     assert s == 1 and b"n_entries" in L.csa2_last_error()
     # forward: ring smaller than T + 127
     s = L.csa2_forward(1, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, FAKE,
-                       FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, n, FAKE, FAKE, 100, FAKE, FAKE,
+                       FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, 2, n, FAKE, FAKE, 100, FAKE, FAKE,
                        FAKE, n, FAKE, 1 << 30, n)
     assert s == 4
     # encoders: bad widths

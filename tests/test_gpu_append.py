@@ -19,8 +19,10 @@ def log(*a):
     print("[gpu]", *a, flush=True)
 
 
+@pytest.mark.parametrize("ratio", [2, 1])
 @pytest.mark.parametrize("mode", ["derive", "given"])
-def test_append_matches_prefill_and_oracle(mode):
+def test_append_matches_prefill_and_oracle(mode, ratio):
+    """ratio 1: every appended token writes its own entry; no pair buffer, no gates"""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -29,7 +31,8 @@ def test_append_matches_prefill_and_oracle(mode):
     import oracle
     from csa2_harness import up, down
 
-    B, T, cap, stride = 3, 40, 48, 24
+    B, T, cap = 3, 40, 48
+    stride = T // ratio + 4
     prefill = [10, 12, 11]
     seed = 0xC5A2A000
     kc = synth.normal(seed, 201, (B, T, 512))
@@ -42,11 +45,14 @@ def test_append_matches_prefill_and_oracle(mode):
         ki = None
     else:
         w_ik = None
-        ki = synth.normal(seed, 207, (B, T // 2, 128))
+        ki = synth.normal(seed, 207, (B, T // ratio, 128))
     cos_t, sin_t = synth.rope_table(T)
-    log(f"csa2_append: mode={mode} B={B} T={T} prefill={prefill}")
+    if ratio == 1:
+        gc = None                           # never read at ratio 1
+    log(f"csa2_append: mode={mode} ratio={ratio} B={B} T={T} prefill={prefill}")
 
-    oz, ozs, ok_, oks = oracle.compress(kc, gc, gamma_c, w_ik, gamma_ik, ki, cos_t, sin_t, stride)
+    oz, ozs, ok_, oks = oracle.compress(kc, gc, gamma_c, w_ik, gamma_ik, ki, cos_t, sin_t, stride,
+                                        ratio=ratio)
     ow, ows = oracle.window_encode(wn, cos_t, sin_t, cap)
 
     def caches():
@@ -59,27 +65,31 @@ def test_append_matches_prefill_and_oracle(mode):
 
     g_gc, g_gik, g_cos, g_sin = up(gamma_c), up(gamma_ik), up(cos_t), up(sin_t)
     g_wik = None if w_ik is None else up(w_ik)
-    g_kc, g_gcl, g_wn = up(kc), up(gc), up(wn)
+    g_kc, g_wn = up(kc), up(wn)
+    g_gcl = None if gc is None else up(gc)
 
     # one call over all tokens
     A = caches()
     zero = torch.zeros(B, dtype=torch.int32, device="cuda")
     csa2.csa2_compress(zero, g_kc, g_gcl, g_gc, g_wik, g_gik, None if ki is None else up(ki),
-                       g_cos, g_sin, A["z_codes"], A["z_scales"], A["ki_codes"], A["ki_scales"])
+                       g_cos, g_sin, A["z_codes"], A["z_scales"], A["ki_codes"], A["ki_scales"],
+                       ratio=ratio)
     csa2.csa2_encode_window(zero, g_wn, g_cos, g_sin, A["w_codes"], A["w_scale"])
 
     # per-request prefills, then one token per call
     Bc = caches()
-    pair_kc = torch.zeros(B, 512, dtype=torch.bfloat16, device="cuda")
-    pair_gc = torch.zeros(B, 512, dtype=torch.bfloat16, device="cuda")
+    pair_kc = torch.zeros(B, 512, dtype=torch.bfloat16, device="cuda") if ratio == 2 else None
+    pair_gc = torch.zeros(B, 512, dtype=torch.bfloat16, device="cuda") if ratio == 2 else None
     z1 = torch.zeros(1, dtype=torch.int32, device="cuda")
     for b, P in enumerate(prefill):
         sl = {k: v[b:b + 1] for k, v in Bc.items()}
-        csa2.csa2_compress(z1, up(kc[b:b + 1, :P]), up(gc[b:b + 1, :P]), g_gc, g_wik, g_gik,
-                           None if ki is None else up(ki[b:b + 1, :P // 2]), g_cos, g_sin,
-                           sl["z_codes"], sl["z_scales"], sl["ki_codes"], sl["ki_scales"])
+        csa2.csa2_compress(z1, up(kc[b:b + 1, :P]), None if gc is None else up(gc[b:b + 1, :P]),
+                           g_gc, g_wik, g_gik,
+                           None if ki is None else up(ki[b:b + 1, :P // ratio]), g_cos, g_sin,
+                           sl["z_codes"], sl["z_scales"], sl["ki_codes"], sl["ki_scales"],
+                           ratio=ratio)
         csa2.csa2_encode_window(z1, up(wn[b:b + 1, :P]), g_cos, g_sin, sl["w_codes"], sl["w_scale"])
-        if P % 2:
+        if ratio == 2 and P % 2:
             pair_kc[b] = up(kc[b, P - 1])
             pair_gc[b] = up(gc[b, P - 1])
     for i in range(T - min(prefill)):
@@ -87,15 +97,16 @@ def test_append_matches_prefill_and_oracle(mode):
         take = np.maximum(pos, 0)
         ki_new = None
         if ki is not None:
-            ki_new = up(np.ascontiguousarray(ki[np.arange(B), take // 2]))
+            ki_new = up(np.ascontiguousarray(ki[np.arange(B), take // ratio]))
         csa2.csa2_append(up(pos), up(np.ascontiguousarray(kc[np.arange(B), take])),
-                         up(np.ascontiguousarray(gc[np.arange(B), take])),
+                         None if gc is None else up(np.ascontiguousarray(gc[np.arange(B), take])),
                          up(np.ascontiguousarray(wn[np.arange(B), take])), pair_kc, pair_gc,
                          g_gc, g_wik, g_gik, ki_new, g_cos, g_sin, Bc["z_codes"], Bc["z_scales"],
-                         Bc["ki_codes"], Bc["ki_scales"], Bc["w_codes"], Bc["w_scale"])
+                         Bc["ki_codes"], Bc["ki_scales"], Bc["w_codes"], Bc["w_scale"],
+                         ratio=ratio)
     torch.cuda.synchronize()
 
-    n = T // 2
+    n = T // ratio
     ref = dict(z_codes=oz, z_scales=ozs, ki_codes=ok_, ki_scales=oks, w_codes=ow, w_scale=ows)
     for k in ref:
         a, bb = down(A[k]), down(Bc[k])

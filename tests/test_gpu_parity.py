@@ -170,6 +170,23 @@ def test_prefill_clustered_keys_ragged(dev, synth):
     _check_prefill_rows(wl, out, ref, rows)
 
 
+@pytest.mark.parametrize("cid,T,H", [(0, 257, 16), (1, 1400, 16)])
+def test_prefill_ratio_one(dev, synth, cid, T, H):
+    """compression ratio one: T entries, entry t rotated at t, a query at t sees entries
+    0..t (top-512 active from t = 512 on); caches bit-exact, rows against the oracle"""
+    from oracle.reference import PrefillReference
+    wl = synth.workload(cid, T=T, H=H, ratio=1)
+    out = _prefill(wl).fetch()
+    ref = PrefillReference(wl)
+    for k in ("z_codes", "z_scales", "ki_codes", "ki_scales"):
+        assert np.array_equal(out[k][0, :T], getattr(ref, k)[0, :T]), k
+    rows = np.arange(T) if T < 300 else np.unique(np.concatenate(
+        [np.arange(0, 6), [510, 511, 512, 513, 1023], np.arange(T - 5, T),
+         np.random.default_rng(5).integers(0, T, 30)]))
+    assert np.all(out["cnt"][0, rows] == np.minimum(rows + 1, 512))
+    _check_prefill_rows(wl, out, ref, rows)
+
+
 def test_prefill_deterministic(dev, synth):
     import torch
     import csa2_harness
@@ -264,12 +281,15 @@ def test_sparse_attn_bounded_replay_floor(dev, synth):
 
 
 # ---------------------------------------------------------------- decode
-@pytest.mark.parametrize("Tq,N,keys", [(1, 3000, "flat"), (6, 2600, "lognormal_dup")])
-def test_decode_small(dev, synth, Tq, N, keys):
+@pytest.mark.parametrize("Tq,N,keys,ratio", [(1, 3000, "flat", 2), (6, 2600, "lognormal_dup", 2),
+                                             (6, 2600, "lognormal_dup", 1), (1, 700, "flat", 1)])
+def test_decode_small(dev, synth, Tq, N, keys, ratio):
+    """ratio 1: one entry per position, a query at p sees entries 0..p (700 entries: every
+    one selectable only up to 512, the window and the entries overlap)"""
     import torch
     import csa2_harness
     from oracle.reference import DecodeReference
-    wl = synth.decode_workload(B=3, Tq=Tq, n_entries=N, H=64, keys=keys)
+    wl = synth.decode_workload(B=3, Tq=Tq, n_entries=N, H=64, keys=keys, ratio=ratio)
     log(f"csa2_forward decode: {wl.name} keys={keys}")
     run = csa2_harness.DecodeRun(wl)
     run.forward()

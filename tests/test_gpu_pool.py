@@ -49,7 +49,10 @@ def _bf16(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def test_pool_and_reindex_match_oracle():
+@pytest.mark.parametrize("ratio", [2, 1])
+def test_pool_and_reindex_match_oracle(ratio):
+    """ratio 1 (one entry per position, as in the decoder layers that use the pool):
+    the same rows at positions that see the same entry counts"""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -71,9 +74,9 @@ def test_pool_and_reindex_match_oracle():
     wI = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
     qI2 = _bf16(rng.standard_normal((B, Tq, 32, 128)))
     wI2 = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
-    q_pos0 = np.array([2 * N, 2 * 18_001 - 1, 2 * 9_000], np.int32)
+    q_pos0 = np.array([ratio * N, ratio * 18_001 - 1, ratio * 9_000], np.int32)
     n_entries = np.full(B, N, np.int32)
-    log(f"csa2_index_pool / csa2_reindex_topk: B={B} Tq={Tq} N={N}")
+    log(f"csa2_index_pool / csa2_reindex_topk: B={B} Tq={Tq} N={N} ratio={ratio}")
 
     g = dict(q0=up(q_pos0), ne=up(n_entries), kc=up(kc), ks=up(ks))
     idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device="cuda")
@@ -82,19 +85,19 @@ def test_pool_and_reindex_match_oracle():
     pcnt = torch.full((B, Tq), -7, dtype=torch.int32, device="cuda")
     ws = csa2.workspace(csa2.OP_INDEX_POOL, B, Tq, 64, N)
     csa2.csa2_index_pool(g["q0"], g["ne"], up(qI), up(wI), g["kc"], g["ks"], idx, cnt, pool, pcnt,
-                         ws)
+                         ws, ratio=ratio)
     # reindex with the Full query over the GPU pool; with another query over the oracle pool
     idx_same = torch.full_like(idx, -7)
     cnt_same = torch.full_like(cnt, -7)
     wsr = csa2.workspace(csa2.OP_REINDEX, B, Tq, 64, N)
     csa2.csa2_reindex_topk(g["q0"], g["ne"], up(qI), up(wI), g["kc"], g["ks"], pool, pcnt,
-                           idx_same, cnt_same, wsr)
+                           idx_same, cnt_same, wsr, ratio=ratio)
     o_pools = np.full((B, Tq, 2048), -1, np.int32)
     o_pcnt = np.zeros((B, Tq), np.int32)
     ref = {}
     for b in range(B):
         for i in range(Tq):
-            n = min((int(q_pos0[b]) + i + 1) // 2, N)
+            n = min((int(q_pos0[b]) + i + 1) // ratio, N)
             q8, sq = oracle.quant_index_query(qI[b, i])
             S = oracle.index_scores(q8, sq, wI[b, i], kc[b], ks[b], n)
             p = oracle.pool_blocks(S, n)
@@ -104,7 +107,7 @@ def test_pool_and_reindex_match_oracle():
     idx2 = torch.full_like(idx, -7)
     cnt2 = torch.full_like(cnt, -7)
     csa2.csa2_reindex_topk(g["q0"], g["ne"], up(qI2), up(wI2), g["kc"], g["ks"], up(o_pools),
-                           up(o_pcnt), idx2, cnt2, wsr)
+                           up(o_pcnt), idx2, cnt2, wsr, ratio=ratio)
     torch.cuda.synchronize()
     gi, gc_, gp, gpc = down(idx), down(cnt), down(pool), down(pcnt)
     gis, gcs, gi2, gc2 = down(idx_same), down(cnt_same), down(idx2), down(cnt2)
