@@ -95,12 +95,13 @@ def stage_times(run, steps: int, stream):
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     ws_i = run.ws
+    r = run.wl.ratio
     out = {}
     if hasattr(run, "kc"):
         out["compress"] = time_events(lambda: csa2.csa2_compress(
             run.pos0, run.kc, run.gc, run.gamma_c, run.w_ik, run.gamma_ik, run.ki_given,
-            run.rope_cos, run.rope_sin, run.z_codes, run.z_scales, run.ki_codes, run.ki_scales),
-            steps, stream)
+            run.rope_cos, run.rope_sin, run.z_codes, run.z_scales, run.ki_codes, run.ki_scales,
+            ratio=r), steps, stream)
         out["window"] = time_events(lambda: csa2.csa2_encode_window(
             run.pos0, run.wn, run.rope_cos, run.rope_sin, run.w_codes, run.w_scale), steps, stream)
         q_pos0 = run.pos0
@@ -110,11 +111,12 @@ def stage_times(run, steps: int, stream):
     scores = torch.empty(run.idx.shape[0], run.idx.shape[1], run.stride, dtype=torch.float32,
                          device="cuda")
     out["index_scores"] = time_events(lambda: csa2.csa2_index_scores(
-        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, scores, ws_i), steps, stream)
+        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, scores, ws_i, ratio=r), steps,
+        stream)
     del scores
     out["index_topk"] = time_events(lambda: csa2.csa2_index_topk(
-        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, run.idx, run.cnt, ws_i),
-        steps, stream)
+        q_pos0, n_ent, run.qI, run.wI, run.ki_codes, run.ki_scales, run.idx, run.cnt, ws_i,
+        ratio=r), steps, stream)
     out["sparse_attn"] = time_events(lambda: csa2.csa2_sparse_attn(
         q_pos0, run.Q, run.w_codes, run.w_scale, run.z_codes, run.z_scales, run.idx, run.cnt,
         run.sink, run.rope_cos, run.rope_sin, run.O, run.lse, run.ws), steps, stream)
@@ -147,9 +149,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "pool", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "pool", "decode1", "pool1", "copy"],
+                    default=None,
                     help="time a single workload (for profiling runs); 'copy' runs a plain "
-                         "1 GiB device copy, the calibration kernel for the HBM byte counters")
+                         "1 GiB device copy, the calibration kernel for the HBM byte counters; "
+                         "decode1 / pool1 are the ratio-1 forms")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
     args = ap.parse_args()
@@ -178,9 +182,10 @@ def main():
                           "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
-    if args.only in ("decode", "pool"):
+    if args.only in ("decode", "pool", "decode1", "pool1"):
         args.no_cpu = True
-        (run_decode if args.only == "decode" else run_pool)(args, result, stream)
+        fn = run_decode if args.only.startswith("decode") else run_pool
+        fn(args, result, stream, ratio=1 if args.only.endswith("1") else 2)
         print(json.dumps(result), flush=True)
         return
     # ---------------------------------------------------------------- prefill
@@ -236,6 +241,8 @@ def main():
     if not args.no_decode and args.only is None:
         run_decode(args, result, stream)
         run_pool(args, result, stream)
+        run_decode(args, result, stream, ratio=1)
+        run_pool(args, result, stream, ratio=1)
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu:
@@ -244,12 +251,20 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_decode(args, result, stream):
+def run_decode(args, result, stream, ratio=2):
+    """Batched decode B=128 x 1 query at position 131071.  ratio 2: the measured
+    workload (65,536 pooled entries per request); ratio 1: its decoder-layer form
+    (131,072 entries, one per position)."""
+    import dataclasses
     import torch
     import csa2_harness
     import csa2_synth as synth
     if True:
         dwl = synth.workload(3)
+        if ratio == 1:
+            dwl = dataclasses.replace(dwl, n_entries=dwl.q_pos0 + 1, ratio=1,
+                                      name=dwl.name + " ratio 1")
+        key = "decode" if ratio == 2 else "decode_ratio1"
         log(f"generating caches: {dwl.name}")
         t0 = time.time()
         drun = csa2_harness.DecodeRun(dwl)
@@ -259,12 +274,13 @@ def run_decode(args, result, stream):
         torch.cuda.synchronize()
         dms = time_events(drun.forward, args.steps, stream)
         dstages = stage_times(drun, args.steps, stream)
-        log(f"decode: {dms:.4f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in dstages.items()})}")
+        log(f"{key}: {dms:.4f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in dstages.items()})}")
         nbytes = decode_bytes(dwl.B, dwl.Tq, dwl.n_entries, dwl.H)
         scan_bytes = 68.0 * dwl.n_entries * dwl.B
-        result["decode"] = {
-            "workload": "CSA2 batched decode B=128 x 1 query, 131072 context (65536 FP4 entries "
-                        "+ 128 FP8 window rows), H=64, top-512",
+        result[key] = {
+            "workload": f"CSA2 batched decode B=128 x 1 query, 131072 context ({dwl.n_entries} "
+                        f"FP4 entries at compression ratio {ratio} + 128 FP8 window rows), H=64, "
+                        "top-512",
             "value": dwl.B * dwl.Tq / (dms * 1e-3), "unit": "query-tokens/s", "ms_per_step": dms,
             "stages_ms": dstages,
             "hbm_frac_step": nbytes / (dms * 1e-3) / PEAK_HBM,
@@ -274,7 +290,7 @@ def run_decode(args, result, stream):
                          "frac": scan_bytes / (dstages["index_scores"] * 1e-3) / PEAK_HBM,
                          "bytes_per_launch": scan_bytes,
                          "traffic": measured_traffic("k_index_scores", "decode",
-                                                     dwl.q_pos0 + 1)},
+                                                     dwl.q_pos0 + 1) if ratio == 2 else None},
         }
         # decode append (one new token per request, half of them closing a pair):
         # window row, pair buffer, entry of a completed pair, into the same caches
@@ -284,37 +300,47 @@ def run_decode(args, result, stream):
         rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=gen).to(torch.bfloat16)
         a_kc, a_gc, a_wn, a_ki = rnd(B, 512), rnd(B, 512), rnd(B, 512), rnd(B, 128)
         a_pkc, a_pgc = rnd(B, 512), rnd(B, 512)
+        if ratio == 1:
+            a_gc = a_pkc = a_pgc = None
         a_pos = torch.tensor([dwl.q_pos0 - (b & 1) for b in range(B)], dtype=torch.int32,
                              device="cuda")
         a_gamma = torch.ones(512, dtype=torch.float32, device="cuda")
         append = lambda: csa2.csa2_append(a_pos, a_kc, a_gc, a_wn, a_pkc, a_pgc, a_gamma, None,
                                           None, a_ki, drun.rope_cos, drun.rope_sin, drun.z_codes,
                                           drun.z_scales, drun.ki_codes, drun.ki_scales,
-                                          drun.w_codes, drun.w_scale)
+                                          drun.w_codes, drun.w_scale, ratio=ratio)
         for _ in range(max(args.warmup, 3)):
             append()
         ams = time_events(append, max(args.steps, 20), stream)
-        log(f"decode append: {ams * 1e3:.2f} us per call (B={B})")
-        result["decode"]["append"] = {
+        log(f"{key} append: {ams * 1e3:.2f} us per call (B={B})")
+        result[key]["append"] = {
             "workload": f"csa2_append B={B}: one token per request at position 131071 or "
-                        "131070 (half close a pair), given index keys",
+                        "131070 " + ("(half close a pair)" if ratio == 2 else "(each writes its "
+                                     "entry)") + ", given index keys",
             "us_per_call": ams * 1e3,
-            "bytes_per_call": B * (3 * 1024 + 2 * 1024 + 256 + 516 + 340 / 2),
+            "bytes_per_call": B * (3 * 1024 + 2 * 1024 + 256 + 516 + 340 / 2) if ratio == 2 else
+                              B * (2 * 1024 + 256 + 516 + 340),
             "bound": "launch latency (one block of two waves per request)"}
         del drun
         torch.cuda.empty_cache()
 
 
 
-def run_pool(args, result, stream):
+def run_pool(args, result, stream, ratio=2):
     """Hierarchical pool and Reindex at the verify-decode shape (B=16 x 6 queries
-    at 1,048,570.., 524,288 entries): the Full layer's scan with and without the
-    pool, and a Reindex layer's selection over the pool only."""
+    at 1,048,570..): the Full layer's scan with and without the pool, and a
+    Reindex layer's selection over the pool only.  ratio 2: 524,288 pooled
+    entries; ratio 1 (the decoder layers that use the pool): 1,048,576."""
+    import dataclasses
     import torch
     import csa2_harness
     import csa2_synth as synth
     import compressed_sparse_attention_csa2_amd as csa2
     wl = synth.workload(4)
+    if ratio == 1:
+        wl = dataclasses.replace(wl, n_entries=wl.q_pos0 + wl.Tq, ratio=1,
+                                 name=wl.name + " ratio 1")
+    key = "hierarchical" if ratio == 2 else "hierarchical_ratio1"
     B, Tq, N = wl.B, wl.Tq, wl.n_entries
     log(f"generating index keys: {wl.name}")
     t0 = time.time()
@@ -343,9 +369,11 @@ def run_pool(args, result, stream):
     ws_r = csa2.workspace(csa2.OP_REINDEX, B, Tq, 64, N)
     torch.cuda.synchronize()
     log(f"index keys resident ({time.time() - t0:.1f} s)")
-    full = lambda: csa2.csa2_index_topk(q0, ne, qI, wI, kc, ks, idx, cnt, ws_t)
-    fpool = lambda: csa2.csa2_index_pool(q0, ne, qI, wI, kc, ks, idx, cnt, pool, pcnt, ws_p)
-    reidx = lambda: csa2.csa2_reindex_topk(q0, ne, qI2, wI2, kc, ks, pool, pcnt, idx2, cnt2, ws_r)
+    full = lambda: csa2.csa2_index_topk(q0, ne, qI, wI, kc, ks, idx, cnt, ws_t, ratio=ratio)
+    fpool = lambda: csa2.csa2_index_pool(q0, ne, qI, wI, kc, ks, idx, cnt, pool, pcnt, ws_p,
+                                         ratio=ratio)
+    reidx = lambda: csa2.csa2_reindex_topk(q0, ne, qI2, wI2, kc, ks, pool, pcnt, idx2, cnt2, ws_r,
+                                           ratio=ratio)
     for f in (full, fpool, reidx):
         f()
     torch.cuda.synchronize()
@@ -354,12 +382,12 @@ def run_pool(args, result, stream):
     t_re = time_events(reidx, args.steps, stream)
     rows = B * Tq
     cand = float(pcnt.sum().item()) * 8
-    log(f"pool: full select {t_full:.4f} ms, with pool {t_pool:.4f} ms, reindex {t_re:.4f} ms")
+    log(f"{key}: full select {t_full:.4f} ms, with pool {t_pool:.4f} ms, reindex {t_re:.4f} ms")
     gather = cand * 68.0                   # the pool's index keys, gathered per query row
-    result["hierarchical"] = {
+    result[key] = {
         "workload": f"verify-decode shape: B={B} x {Tq} queries at {wl.q_pos0}.., {N} entries "
-                    "(lognormal keys, 1% exact duplicates); Full layer with the pool, then a "
-                    "Reindex layer's own query over the pool",
+                    f"at compression ratio {ratio} (lognormal keys, 1% exact duplicates); Full "
+                    "layer with the pool, then a Reindex layer's own query over the pool",
         "full_select_ms": t_full, "full_select_with_pool_ms": t_pool, "reindex_select_ms": t_re,
         "candidates_per_row": {"full": N, "reindex": cand / rows},
         "reindex_roofline": {"bound": "hbm", "bytes_per_launch": gather,
