@@ -131,6 +131,7 @@ class Workload:
     name: str = ""
     extra: dict = field(default_factory=dict)
     ratio: int = 2       # positions per compressed entry (2: pairs; 1: one entry per token)
+    z_format: int = 0    # compressed-row storage: 0 one E8M0 scale per 32, 1 one E4M3 per 16
 
     # ---- geometry -------------------------------------------------------
     @property
@@ -237,19 +238,22 @@ class Workload:
         return normal(self.seed, ID_ZROW, (n, D), start=(b * self.n_entries + j0) * D)
 
 
-def workload(cid: int, T: int | None = None, H: int | None = None, ratio: int = 2) -> Workload:
+def workload(cid: int, T: int | None = None, H: int | None = None, ratio: int = 2,
+             z_format: int = 0) -> Workload:
     """The five measured workloads; T/H overrides give same-recipe smaller prefills, ratio 1
     the one-entry-per-token form of a prefill."""
     seed = 0xC5A20000 + cid
-    tag = "" if ratio == 2 else f" ratio {ratio}"
+    tag = ("" if ratio == 2 else f" ratio {ratio}") + ("" if z_format == 0 else " Z per-16 E4M3")
     if cid == 0:
         T = T or 256
         return Workload(cid, "prefill", 1, T, H or 16, T // ratio, T + WINDOW - 1, 0, "derive",
-                        seed, f"prefill T={T} H={H or 16} derived index keys{tag}", ratio=ratio)
+                        seed, f"prefill T={T} H={H or 16} derived index keys{tag}", ratio=ratio,
+                        z_format=z_format)
     if cid in (1, 2):
         T = T or (8192 if cid == 1 else 65536)
         return Workload(cid, "prefill", 1, T, H or 64, T // ratio, T + WINDOW - 1, 0, "clustered",
-                        seed, f"prefill T={T} H={H or 64} clustered index keys{tag}", ratio=ratio)
+                        seed, f"prefill T={T} H={H or 64} clustered index keys{tag}", ratio=ratio,
+                        z_format=z_format)
     if cid == 3:
         return Workload(3, "decode", 128, 1, H or 64, 65536, 128, 131071, "flat", seed,
                         "decode B=128 x 1 @ 131072 context")
@@ -261,10 +265,11 @@ def workload(cid: int, T: int | None = None, H: int | None = None, ratio: int = 
 
 def decode_workload(B: int, Tq: int, n_entries: int, H: int = 64, keys: str = "flat",
                     seed: int = 0xC5A20010, q_pos0: int | None = None,
-                    ratio: int = 2) -> Workload:
+                    ratio: int = 2, z_format: int = 0) -> Workload:
     """A decode workload with the recipe of workloads 3/4 (ratio 2), or its one-entry-per-token
     form (ratio 1): the queries follow the last entry's positions."""
     q0 = (ratio * n_entries - Tq) if q_pos0 is None else q_pos0
-    tag = "" if ratio == 2 else f" ratio {ratio}"
+    tag = ("" if ratio == 2 else f" ratio {ratio}") + ("" if z_format == 0 else " Z per-16 E4M3")
     return Workload(99, "decode", B, Tq, H, n_entries, Tq + WINDOW - 1, q0, keys, seed,
-                    f"decode B={B} x {Tq} @ {ratio * n_entries}{tag}", ratio=ratio)
+                    f"decode B={B} x {Tq} @ {ratio * n_entries}{tag}", ratio=ratio,
+                    z_format=z_format)

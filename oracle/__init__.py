@@ -59,8 +59,12 @@ def lib():
         L.orc_fp4_value.restype = ctypes.c_double
         L.orc_fp8_encode_row.argtypes = [vp, i32, vp, vp]
         L.orc_rmsnorm.argtypes = [vp, vp, i32, vp]
-        L.orc_compress_entry.argtypes = [vp] * 16
-        L.orc_compress.argtypes = [i32, i32, i32] + [vp] * 12 + [i64, i32]
+        L.orc_compress_entry.argtypes = [vp] * 16 + [i32]
+        L.orc_compress.argtypes = [i32, i32, i32] + [vp] * 12 + [i64, i32, i32]
+        L.orc_fp4e4_encode.argtypes = [vp, i32, vp, vp]
+        L.orc_fp4e4_value.argtypes = [vp, vp, i32]
+        L.orc_fp4e4_value.restype = ctypes.c_double
+        L.orc_fp4e4_encode_rows.argtypes = [vp, i64, i32, vp, vp]
         L.orc_window_encode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp]
         L.orc_fp4_encode_rows.argtypes = [vp, i64, i32, vp, vp]
         L.orc_fp8_encode_rows.argtypes = [vp, i64, i32, vp, vp]
@@ -68,9 +72,10 @@ def lib():
         L.orc_topk.argtypes = [vp, i64, i32, vp]
         L.orc_topk.restype = i32
         L.orc_quant_index_query.argtypes = [vp, vp, vp]
-        L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64]
+        L.orc_attend.argtypes = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64,
+                                 i32]
         L.orc_query_rows.argtypes = [i32, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32,
-                                     vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32]
+                                     vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32]
         _lib = L
     return _lib
 
@@ -138,6 +143,48 @@ def fp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
+def fp4e4_encode(x: np.ndarray):
+    """the pages' format: x [rows, n] fp32 -> codes [rows, n/2] u8, E4M3 scales [rows, n/16] u8"""
+    A = _Args()
+    x = c(x, np.float32)
+    rows, n = x.shape
+    codes = np.zeros((rows, n // 2), np.uint8)
+    scales = np.zeros((rows, n // 16), np.uint8)
+    for r in range(rows):
+        lib().orc_fp4e4_encode(A(x[r]), n, A(codes[r]), A(scales[r]))
+    return codes, scales
+
+
+def fp4e4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """exact values (double) of rows in the pages' format"""
+    A = _Args()
+    codes = c(codes, np.uint8)
+    scales = c(scales, np.uint8)
+    rows = codes.shape[0]
+    n = codes.shape[1] * 2
+    out = np.empty((rows, n), np.float64)
+    for r in range(rows):
+        pc, ps = A(codes[r]), A(scales[r])
+        for k in range(n):
+            out[r, k] = lib().orc_fp4e4_value(pc, ps, k)
+    return out
+
+
+def fp4e4_encode_rows_bf16(x: np.ndarray):
+    A = _Args()
+    x = c(x, np.uint16)
+    rows, n = x.shape
+    codes = np.zeros((rows, n // 2), np.uint8)
+    scales = np.zeros((rows, n // 16), np.uint8)
+    lib().orc_fp4e4_encode_rows(A(x), rows, n, A(codes), A(scales))
+    return codes, scales
+
+
+def z_encode_rows_bf16(x: np.ndarray, z_format: int = 0):
+    """Z rows in storage format z_format (0: one E8M0 scale per 32; 1: one E4M3 per 16)"""
+    return fp4e4_encode_rows_bf16(x) if z_format == 1 else fp4_encode_rows_bf16(x)
+
+
 def fp8_encode_row(x: np.ndarray):
     A = _Args()
     x = c(x, np.float32)
@@ -181,12 +228,13 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- steps
-def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn):
+def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn, z_format=0):
     """one entry; returns (z_codes, z_scales, ki_codes, ki_scales, z_pre, ki_pre).
-    kc1 = None: compression ratio one, the entry is the one position kc0 (gates unused)."""
+    kc1 = None: compression ratio one, the entry is the one position kc0 (gates unused).
+    z_format 1: Z in the pages' format (32 E4M3 scale bytes)."""
     A = _Args()
     zc = np.zeros(256, np.uint8)
-    zs = np.zeros(16, np.uint8)
+    zs = np.zeros(32 if z_format == 1 else 16, np.uint8)
     kc_ = np.zeros(64, np.uint8)
     ks = np.zeros(4, np.uint8)
     zp = np.zeros(512, np.float32)
@@ -195,12 +243,13 @@ def compress_entry(kc0, kc1, gc0, gc1, gamma_c, w_ik, gamma_ik, ki_given, cs, sn
             c(gamma_c, np.float32), None if w_ik is None else c(w_ik, np.uint16),
             c(gamma_ik, np.float32), None if ki_given is None else c(ki_given, np.uint16),
             c(cs, np.float32), c(sn, np.float32)]
-    lib().orc_compress_entry(*[A(a) for a in args], A(zc), A(zs), A(kc_), A(ks), A(zp), A(kp))
+    lib().orc_compress_entry(*[A(a) for a in args], A(zc), A(zs), A(kc_), A(ks), A(zp), A(kp),
+                             z_format)
     return zc, zs, kc_, ks, zp, kp
 
 
 def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stride, pos0=0,
-             ratio=2):
+             ratio=2, z_format=0):
     """kc, gc [B,T,512] bf16 -> caches [B, entry_stride, ...]: entries pos0/2 .. (pos0+T)/2-1
     pooled from pairs (ratio 2), or entries pos0 .. pos0+T-1, one per position, rotated at
     their own position (ratio 1, "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV
@@ -211,14 +260,15 @@ def compress(kc, gc, gamma_c, w_ik, gamma_ik, ki_given, cos_t, sin_t, entry_stri
     gc = c(gc, np.uint16)
     B, T, _ = kc.shape
     z_codes = np.zeros((B, entry_stride, 256), np.uint8)
-    z_scales = np.zeros((B, entry_stride, 16), np.uint8)
+    z_scales = np.zeros((B, entry_stride, 32 if z_format == 1 else 16), np.uint8)
     ki_codes = np.zeros((B, entry_stride, 64), np.uint8)
     ki_scales = np.zeros((B, entry_stride, 4), np.uint8)
     lib().orc_compress(B, T, pos0, A(kc), A(gc), A(gamma_c, np.float32),
                        A(None if w_ik is None else c(w_ik, np.uint16)), A(gamma_ik, np.float32),
                        A(None if ki_given is None else c(ki_given, np.uint16)),
                        A(cos_t, np.float32), A(sin_t, np.float32),
-                       A(z_codes), A(z_scales), A(ki_codes), A(ki_scales), entry_stride, ratio)
+                       A(z_codes), A(z_scales), A(ki_codes), A(ki_scales), entry_stride, ratio,
+                       z_format)
     return z_codes, z_scales, ki_codes, ki_scales
 
 
@@ -304,7 +354,7 @@ def reindex_topk(q8, sq, w, ki_codes, ki_scales, n, pool, block=POOL_BLOCK, k=TO
     return idx, cnt, cand, Sc
 
 def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t, sin_t,
-           w_floor=0):
+           w_floor=0, z_format=0):
     """Q [H,512] bf16 -> O [H,512] double, lse [H], O_bf16 [H,512].  w_floor: the
     start s of a bounded replay ("Inside DeepSeek V4.1 Flash: Deriving the 890-Byte
     KV Cache", section "Bounded replay trades exact state for cheaper
@@ -318,13 +368,13 @@ def attend(Q, p, w_codes, w_scale, cap, z_codes, z_scales, idx, cnt, sink, cos_t
     lib().orc_attend(A(Q), H, p, A(w_codes, np.uint8), A(w_scale, np.float32), cap,
                      A(z_codes, np.uint8), A(z_scales, np.uint8), A(idx, np.int32), cnt,
                      A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
-                     A(O), A(lse), A(Ob), int(w_floor))
+                     A(O), A(lse), A(Ob), int(w_floor), int(z_format))
     return O, lse, Ob
 
 
 def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales, w_codes,
                w_scale, cap, sink, cos_t, sin_t, k=TOPK, want_scores=False, want_O=True,
-               ratio=2):
+               ratio=2, z_format=0):
     """Selection and attention for query tokens of ONE request (caches of that request).
     A query at p sees entries j < min(floor((p+1)/ratio), n_entries)."""
     A = _Args()
@@ -343,5 +393,5 @@ def query_rows(pos, n_entries, qI, wI, Q, ki_codes, ki_scales, z_codes, z_scales
                          A(z_codes, np.uint8), A(z_scales, np.uint8),
                          A(w_codes, np.uint8), A(w_scale, np.float32), cap,
                          A(sink, np.float32), A(cos_t, np.float32), A(sin_t, np.float32),
-                         k, A(idx), A(cnt), A(O), A(Ob), A(lse), A(S), ratio)
+                         k, A(idx), A(cnt), A(O), A(Ob), A(lse), A(S), ratio, z_format)
     return dict(idx=idx, cnt=cnt, O=O, O_bf16=Ob, lse=lse, S=S)

@@ -188,6 +188,42 @@ double orc_fp4_value(const uint8_t* codes, const uint8_t* scales, int k) {
 }
 
 /*
+ * The pages' main-entry format [P4 "Deriving the 890 bytes per token": E2M1
+ * values, one one-byte E4M3 scale per 16 channels, 288 bytes per entry; P4
+ * "FP4 is a storage choice": E4M3 block scales in the manner of NVFP4's local
+ * scaling, without its second, global scale].  Per block of 16 the scale is
+ * E4M3FN(max|x| / 6) (6 = the largest E2M1 magnitude; division in fp32,
+ * correctly rounded; nearest code, ties to even), and every element is
+ * E2M1(x / s) with s the scale code's value (fp32 division; nearest, ties to
+ * even, saturating at 6).  A scale that rounds to 0 gives an all-zero block.
+ * Codes packed as in orc_fp4_encode; scales one byte per 16 elements.
+ */
+void orc_fp4e4_encode(const float* x, int n, uint8_t* codes, uint8_t* scales) {
+    for (int b = 0; b < n / 16; ++b) {
+        const float* xb = x + 16 * b;
+        float amax = 0.0f;
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xb[i]));
+        int sc = orc_e4m3_encode(amax / 6.0f);
+        float s = orc_e4m3_value(sc);
+        scales[b] = (uint8_t)sc;
+        for (int i = 0; i < 16; i += 2) {
+            int c0 = 0, c1 = 0;
+            if (s > 0.0f) {
+                c0 = orc_e2m1_encode(xb[i] / s);
+                c1 = orc_e2m1_encode(xb[i + 1] / s);
+            }
+            codes[8 * b + i / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
+/* exact value of element k of a row in the pages' format */
+double orc_fp4e4_value(const uint8_t* codes, const uint8_t* scales, int k) {
+    int c = (codes[k / 2] >> ((k & 1) * 4)) & 15;
+    return (double)orc_e2m1_value(c) * (double)orc_e4m3_value(scales[k / 16]);
+}
+
+/*
  * FP8 row encoding: scale = max|x| / 448 (fp32, correctly rounded), element
  * code = E4M3FN(x / scale).  An all-zero row gets scale 1.  [P2 "W <- FP8(W)";
  * P1 "the window cache stays FP8".]
@@ -279,12 +315,15 @@ static void rope_fwd(float* x, int lo, const float* cs, const float* sn) {
  * In given mode (w_ik == NULL) the index key's pre-quantisation values are
  * ki_given (already normalised and rotated) and are only encoded.
  * z_pre / ki_pre (optional) receive the fp32 values before quantisation.
+ * z_fmt selects Z's storage: 0 = one E8M0 scale per 32 (16 scale bytes),
+ * 1 = the pages' one E4M3 scale per 16 (32 scale bytes); K^I is always the
+ * former.
  */
 void orc_compress_entry(const uint16_t* kc0, const uint16_t* kc1, const uint16_t* gc0,
                         const uint16_t* gc1, const float* gamma_c, const uint16_t* w_ik,
                         const float* gamma_ik, const uint16_t* ki_given, const float* cs,
                         const float* sn, uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
-                        uint8_t* ki_scales, float* z_pre, float* ki_pre) {
+                        uint8_t* ki_scales, float* z_pre, float* ki_pre, int z_fmt) {
     float kp[ORC_D], c[ORC_D], z[ORC_D], ki[ORC_DI], kn[ORC_DI];
     for (int ch = 0; ch < ORC_D && !kc1; ++ch) kp[ch] = bf16f(kc0[ch]);
     for (int ch = 0; ch < ORC_D && kc1; ++ch) {
@@ -301,7 +340,10 @@ void orc_compress_entry(const uint16_t* kc0, const uint16_t* kc1, const uint16_t
     memcpy(z, c, sizeof z);
     rope_fwd(z, ORC_ROPE_LO, cs, sn);
     if (z_pre) memcpy(z_pre, z, sizeof z);
-    orc_fp4_encode(z, ORC_D, z_codes, z_scales);
+    if (z_fmt == 1)
+        orc_fp4e4_encode(z, ORC_D, z_codes, z_scales);
+    else
+        orc_fp4_encode(z, ORC_D, z_codes, z_scales);
 
     if (w_ik) {
         for (int n = 0; n < ORC_DI; ++n) {
@@ -330,7 +372,8 @@ void orc_compress(int B, int T, int pos0, const uint16_t* kc, const uint16_t* gc
                   const float* gamma_c, const uint16_t* w_ik, const float* gamma_ik,
                   const uint16_t* ki_given, const float* cos_t, const float* sin_t,
                   uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                  int64_t entry_stride, int ratio) {
+                  int64_t entry_stride, int ratio, int z_fmt) {
+    const int zsb = z_fmt == 1 ? 32 : 16;   /* scale bytes per Z entry */
     int nloc = T / ratio;
     for (int b = 0; b < B; ++b) {
         for (int jl = 0; jl < nloc; ++jl) {
@@ -342,8 +385,8 @@ void orc_compress(int B, int T, int pos0, const uint16_t* kc, const uint16_t* gc
             orc_compress_entry(k0, ratio == 2 ? k0 + ORC_D : NULL, g0,
                                ratio == 2 ? g0 + ORC_D : NULL, gamma_c, w_ik, gamma_ik, kg,
                                cos_t + ratio * j * ORC_PAIRS, sin_t + ratio * j * ORC_PAIRS,
-                               z_codes + e * 256, z_scales + e * 16, ki_codes + e * 64,
-                               ki_scales + e * 4, NULL, NULL);
+                               z_codes + e * 256, z_scales + e * zsb, ki_codes + e * 64,
+                               ki_scales + e * 4, NULL, NULL, z_fmt);
         }
     }
 }
@@ -374,6 +417,16 @@ void orc_fp4_encode_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* cod
     for (int64_t r = 0; r < rows; ++r) {
         for (int k = 0; k < cols; ++k) tmp[k] = bf16f(x[r * cols + k]);
         orc_fp4_encode(tmp, cols, codes + r * (cols / 2), scales + r * (cols / 32));
+    }
+    free(tmp);
+}
+
+void orc_fp4e4_encode_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                           uint8_t* scales) {
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)cols);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int k = 0; k < cols; ++k) tmp[k] = bf16f(x[r * cols + k]);
+        orc_fp4e4_encode(tmp, cols, codes + r * (cols / 2), scales + r * (cols / 16));
     }
     free(tmp);
 }
@@ -482,14 +535,15 @@ void orc_quant_index_query(const uint16_t* q, uint8_t* q8, float* sq) {
  *   S_i = Q_h . G_i / sqrt(512),
  *   A_i = exp S_i / (exp s_h + sum_j exp S_j),
  *   O_h = sum_i A_i G_i,  then channels 448.. turned back by R_p^{-1}.
- * G rows are the exact dequantised values; everything is in double.
+ * G rows are the exact dequantised values (Z in format z_fmt, as for
+ * orc_compress_entry); everything is in double.
  * Q: [H][512] bf16.  Out: O [H][512] double, lse [H] (log of the full
  * denominator, sink included), O_bf16 [H][512] (nearest bf16).
  */
 void orc_attend(const uint16_t* Q, int H, int64_t p, const uint8_t* w_codes, const float* w_scale,
                 int cap, const uint8_t* z_codes, const uint8_t* z_scales, const int32_t* idx,
                 int cnt, const float* sink, const float* cos_t, const float* sin_t, double* O,
-                double* lse, uint16_t* O_bf16, int64_t w_floor) {
+                double* lse, uint16_t* O_bf16, int64_t w_floor, int z_fmt) {
     int64_t w0 = p - (ORC_WINDOW - 1);
     if (w0 < 0) w0 = 0;
     /* bounded replay from s = w_floor: the window is max(s, p-127) .. p (s > p read as p) */
@@ -507,7 +561,9 @@ void orc_attend(const uint16_t* Q, int H, int64_t p, const uint8_t* w_codes, con
     for (int r = 0; r < cnt; ++r) {
         int64_t j = idx[r];
         for (int k = 0; k < ORC_D; ++k)
-            G[(size_t)(nw + r) * ORC_D + k] = orc_fp4_value(z_codes + j * 256, z_scales + j * 16, k);
+            G[(size_t)(nw + r) * ORC_D + k] =
+                z_fmt == 1 ? orc_fp4e4_value(z_codes + j * 256, z_scales + j * 32, k)
+                           : orc_fp4_value(z_codes + j * 256, z_scales + j * 16, k);
     }
     double* s = (double*)malloc(sizeof(double) * (size_t)nr);
     double qd[ORC_D], o[ORC_D];
@@ -560,7 +616,8 @@ void orc_query_rows(int nq, const int64_t* pos, int64_t n_entries, const uint16_
                     const uint8_t* ki_scales, const uint8_t* z_codes, const uint8_t* z_scales,
                     const uint8_t* w_codes, const float* w_scale, int cap, const float* sink,
                     const float* cos_t, const float* sin_t, int k, int32_t* idx, int32_t* cnt,
-                    double* O, uint16_t* O_bf16, double* lse, float* S_out, int ratio) {
+                    double* O, uint16_t* O_bf16, double* lse, float* S_out, int ratio,
+                    int z_fmt) {
     uint8_t q8[ORC_HI * ORC_DI];
     float sq[ORC_HI];
     float* S = (float*)malloc(sizeof(float) * (size_t)(n_entries > 0 ? n_entries : 1));
@@ -576,7 +633,7 @@ void orc_query_rows(int nq, const int64_t* pos, int64_t n_entries, const uint16_
             orc_attend(Q + (size_t)i * H * ORC_D, H, p, w_codes, w_scale, cap, z_codes, z_scales,
                        idx + (size_t)i * k, cnt[i], sink, cos_t, sin_t,
                        O ? O + (size_t)i * H * ORC_D : NULL, lse ? lse + (size_t)i * H : NULL,
-                       O_bf16 ? O_bf16 + (size_t)i * H * ORC_D : NULL, 0);
+                       O_bf16 ? O_bf16 + (size_t)i * H * ORC_D : NULL, 0, z_fmt);
     }
     free(S);
 }

@@ -11,7 +11,8 @@ import time
 import numpy as np
 
 import csa2_synth as synth
-from . import (compress, fp4_encode_rows_bf16, query_rows, window_encode, attend, TOPK, WINDOW)
+from . import (compress, fp4_encode_rows_bf16, z_encode_rows_bf16, query_rows, window_encode,
+               attend, TOPK, WINDOW)
 
 
 class PrefillReference:
@@ -28,7 +29,7 @@ class PrefillReference:
         ki_given = None if derive else wl.ki_given()[b:b + 1]
         self.z_codes, self.z_scales, self.ki_codes, self.ki_scales = compress(
             kc, gc, wl.gamma_c(), wl.w_ik() if derive else None, wl.gamma_ik(), ki_given,
-            self.cos, self.sin, entry_stride=T // wl.ratio, ratio=wl.ratio)
+            self.cos, self.sin, entry_stride=T // wl.ratio, ratio=wl.ratio, z_format=wl.z_format)
         self.n_entries = T // wl.ratio
         self.cap = wl.cap
         self.w_codes = np.zeros((1, wl.cap, 512), np.uint8)
@@ -62,7 +63,8 @@ class PrefillReference:
         return query_rows(t, self.n_entries, self.wl.qI_rows(self.b, t), self.wI[t], Q,
                           self.ki_codes[0], self.ki_scales[0], self.z_codes[0], self.z_scales[0],
                           self.w_codes[0], self.w_scale[0], self.cap, self.sink, self.cos,
-                          self.sin, TOPK, want_scores=want_scores, ratio=self.wl.ratio)
+                          self.sin, TOPK, want_scores=want_scores, ratio=self.wl.ratio,
+                          z_format=self.wl.z_format)
 
 
 class DecodeReference:
@@ -87,7 +89,7 @@ class DecodeReference:
         self.sink = wl.sink()
         self.wI = wl.wI()[b]
         self.z_codes = np.zeros((N, 256), np.uint8)
-        self.z_scales = np.zeros((N, 16), np.uint8)
+        self.z_scales = np.zeros((N, 32 if wl.z_format == 1 else 16), np.uint8)
         self._z_done = np.zeros(N, bool)
 
     def _ensure_z(self, js):
@@ -99,7 +101,7 @@ class DecodeReference:
         raw = np.empty((len(js), 512), np.uint16)
         synth.lib().synth_normal_rows(self.wl.seed, synth.ID_ZROW, synth._ptr(rows), len(js),
                                       512, 1.0, 0.0, 1, synth._ptr(raw))
-        cc, ss = fp4_encode_rows_bf16(raw)
+        cc, ss = z_encode_rows_bf16(raw, self.wl.z_format)
         self.z_codes[js] = cc
         self.z_scales[js] = ss
         self._z_done[js] = True
@@ -124,7 +126,8 @@ class DecodeReference:
         for i in range(len(qi)):
             O[i], lse[i], Ob[i] = attend(Q[i], int(pos[i]), self.w_codes, self.w_scale, wl.cap,
                                          self.z_codes, self.z_scales, sel["idx"][i],
-                                         int(sel["cnt"][i]), self.sink, self.cos, self.sin)
+                                         int(sel["cnt"][i]), self.sink, self.cos, self.sin,
+                                         z_format=wl.z_format)
         sel.update(O=O, O_bf16=Ob, lse=lse)
         return sel
 

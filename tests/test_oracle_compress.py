@@ -276,3 +276,18 @@ def test_entry_byte_sizes():
     assert 512 * 4 // 8 + 512 // 32 == 272
     assert 512 * 4 // 8 + 512 // 16 == 288
     assert (3 / 2 + 1) * (288 + 68) == 890
+
+
+def test_pages_z_format_encodes_the_same_values(orc, synth):
+    """z_format 1 stores the same pre-code values in the pages' per-16 E4M3 format;
+    the index key keeps its per-32 format"""
+    cos_t, sin_t = synth.rope_table(64)
+    W = bf16((rng.standard_normal((D, 128)) / math.sqrt(D)).astype(np.float32))
+    ka, kb, ga, gb = rand_bf16(D), rand_bf16(D), rand_bf16(D), rand_bf16(D)
+    gamma, g_ik = np.ones(D, np.float32), np.ones(128, np.float32)
+    a = orc.compress_entry(ka, kb, ga, gb, gamma, W, g_ik, None, cos_t[9], sin_t[9])
+    b = orc.compress_entry(ka, kb, ga, gb, gamma, W, g_ik, None, cos_t[9], sin_t[9], z_format=1)
+    assert np.array_equal(a[4], b[4]) and np.array_equal(a[5], b[5])
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+    zc, zs = orc.fp4e4_encode(b[4][None])
+    assert np.array_equal(b[0], zc[0]) and np.array_equal(b[1], zs[0]) and len(b[1]) == 32

@@ -164,3 +164,74 @@ def test_exp_within_two_ulp_of_libm(orc):
     assert worst <= 2.0, worst
     assert orc.exp32(0.0) == 1.0
     assert orc.exp32(-87.5) == 0.0 and orc.exp32(-1000.0) == 0.0
+
+
+# ---------------------------------------------------------------- the pages' Z format
+# "Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV Cache", section "Deriving the
+# 890 bytes per token" (E2M1 values, one one-byte E4M3 scale per 16 channels: 288 bytes
+# per 512-wide entry) and "FP4 is a storage choice" (E4M3 block scales as in NVFP4's
+# local scaling, no global scale).  Reading: scale = E4M3(max|x| / 6), elements
+# E2M1(x / scale), both nearest-even, the elements saturating at 6.
+def _e4m3_torch(v):
+    return int(torch.tensor([v], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+
+
+def test_fp4e4_scale_and_codes_against_torch_and_brute_force(orc):
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((40, 512)) * np.exp(rng.standard_normal((40, 1)) * 2)).astype(np.float32)
+    x[3, :16] = 0.0                         # a zero block
+    x[4, 16:32] = 1e-4                      # max/6 below half the smallest E4M3 step: scale 0
+    codes, scales = orc.fp4e4_encode(x)
+    assert codes.shape == (40, 256) and scales.shape == (40, 32)
+    for r in range(40):
+        for g in range(32):
+            blk = x[r, 16 * g:16 * g + 16]
+            amax = np.float32(np.max(np.abs(blk)))
+            sc = _e4m3_torch(np.float32(amax / np.float32(6.0)))
+            assert scales[r, g] == sc, (r, g)
+            s = np.float32(e4m3_from_bits(sc))
+            for i in range(16):
+                k = 16 * g + i
+                c = (codes[r, k // 2] >> (4 * (k & 1))) & 15
+                want = 0 if s == 0 else brute_e2m1(float(np.float32(blk[i]) / s))
+                assert c == want, (r, k)
+    assert not codes[3, :8].any() and scales[3, 0] == 0
+    assert scales[4, 1] == 0 and not codes[4, 8:16].any()
+
+
+def test_fp4e4_decode_and_round_trip(orc):
+    rng = np.random.default_rng(32)
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    svals = np.array([e4m3_from_bits(c) for c in range(1, 127)], np.float64)
+    x = np.zeros((8, 512), np.float32)
+    for r in range(8):
+        for g in range(32):
+            s = rng.choice(svals[20:110])
+            v = rng.choice(mags, 16) * rng.choice([-1, 1], 16)
+            v[rng.integers(16)] = 6.0 * rng.choice([-1, 1])      # amax = 6 s exactly
+            x[r, 16 * g:16 * g + 16] = (v * s).astype(np.float32)
+    codes, scales = orc.fp4e4_encode(x)
+    dec = orc.fp4e4_decode(codes, scales)
+    assert np.array_equal(dec, x.astype(np.float64))
+    # decode is code value times scale value, from the bit fields
+    k = np.arange(512)
+    for r in range(2):
+        c = (codes[r, k // 2] >> (4 * (k & 1))) & 15
+        ref = np.array([e2m1_from_bits(int(a)) * e4m3_from_bits(int(scales[r, i // 16]))
+                        for i, a in enumerate(c)])
+        assert np.array_equal(dec[r], ref)
+
+
+def test_fp4e4_error_bound_random(orc):
+    """|x - dec| <= s: half the widest E2M1 gap (2) below saturation, and at most
+    6 s (1/(1 - 2^-4) - 1) < s above it (s = amax/6 rounded to 4 significant bits)"""
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal((64, 512)) * np.exp(rng.standard_normal((64, 1)))).astype(np.float32)
+    codes, scales = orc.fp4e4_encode(x)
+    dec = orc.fp4e4_decode(codes, scales)
+    s = np.array([[e4m3_from_bits(int(b)) for b in row] for row in scales]).repeat(16, axis=1)
+    assert np.all(np.abs(dec - x) <= s + 0.0)
+    # finer than the per-32 power-of-two format on the same data, on average
+    c0, s0 = orc.fp4_encode(x)
+    d0 = orc.fp4_decode(c0, s0)
+    assert np.mean((dec - x) ** 2) < np.mean((d0 - x) ** 2)

@@ -186,6 +186,32 @@ def test_sink_identity_against_sdpa(orc):
     assert np.allclose(A_sink + A_rows, 1.0, atol=1e-12)
 
 
+def test_pages_z_format_attention_against_sdpa(orc):
+    """compressed rows stored in the pages' per-16 E4M3 format are attended as their
+    exact decoded values (float64 SDPA over those rows, with the sink)"""
+    cap, N, p, H = 200, 600, 900, 4
+    w_codes, w_scale, _, _, cos_t, sin_t = caches(orc, cap, 8, p)
+    zc, zs = orc.fp4e4_encode((rng.standard_normal((N, D)) * 2).astype(np.float32))
+    idx = np.sort(rng.choice(N, 400, replace=False)).astype(np.int32)
+    Q = bf16((rng.standard_normal((H, D)) * 0.3).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    O, lse, _ = orc.attend(Q, p, w_codes, w_scale, cap, zc, zs, idx, 400, sink, cos_t, sin_t,
+                           z_format=1)
+    e4 = e4m3_table(orc)
+    pos = np.arange(p - 127, p + 1)
+    G = np.concatenate([e4[w_codes[pos % cap]] * w_scale[pos % cap][:, None].astype(np.float64),
+                        orc.fp4e4_decode(zc[idx], zs[idx])])
+    G = torch.from_numpy(G)
+    q = torch.from_numpy(f32(Q).astype(np.float64))
+    Op = torch.nn.functional.scaled_dot_product_attention(q[None], G[None], G[None],
+                                                          scale=1 / math.sqrt(D))[0]
+    lse_p = torch.logsumexp((q @ G.T) / math.sqrt(D), dim=1)
+    s = torch.from_numpy(sink.astype(np.float64))
+    expect = (torch.sigmoid(lse_p - s)[:, None] * Op).numpy()   # zero angles: R_p = I
+    assert np.max(np.abs(O - expect)) < 1e-12
+    assert np.allclose(lse, torch.logaddexp(lse_p, s).numpy(), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("floor", [0, 800, 850, 899, 900])
 def test_bounded_replay_window_against_sdpa(orc, floor):
     """Bounded replay from s ("Inside DeepSeek V4.1 Flash: Deriving the 890-Byte KV
