@@ -101,7 +101,7 @@ def stage_times(run, steps: int, stream):
         out["compress"] = time_events(lambda: csa2.csa2_compress(
             run.pos0, run.kc, run.gc, run.gamma_c, run.w_ik, run.gamma_ik, run.ki_given,
             run.rope_cos, run.rope_sin, run.z_codes, run.z_scales, run.ki_codes, run.ki_scales,
-            ratio=r), steps, stream)
+            ratio=r, z_format=run.wl.z_format), steps, stream)
         out["window"] = time_events(lambda: csa2.csa2_encode_window(
             run.pos0, run.wn, run.rope_cos, run.rope_sin, run.w_codes, run.w_scale), steps, stream)
         q_pos0 = run.pos0
@@ -119,7 +119,8 @@ def stage_times(run, steps: int, stream):
         ratio=r), steps, stream)
     out["sparse_attn"] = time_events(lambda: csa2.csa2_sparse_attn(
         q_pos0, run.Q, run.w_codes, run.w_scale, run.z_codes, run.z_scales, run.idx, run.cnt,
-        run.sink, run.rope_cos, run.rope_sin, run.O, run.lse, run.ws), steps, stream)
+        run.sink, run.rope_cos, run.rope_sin, run.O, run.lse, run.ws, z_format=run.wl.z_format),
+        steps, stream)
     return out
 
 

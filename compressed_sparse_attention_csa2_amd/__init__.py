@@ -43,26 +43,29 @@ def lib() -> ctypes.CDLL:
         L.csa2_status_string.argtypes = [i32]
         L.csa2_workspace_size.restype = sz
         L.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i64]
-        L.csa2_compress.argtypes = [i32, i32] + [vp] * 9 + [i64] + [vp] * 4 + [i64, i32, vp]
+        L.csa2_compress.argtypes = [i32, i32] + [vp] * 9 + [i64] + [vp] * 4 + [i64, i32, i32, vp]
         L.csa2_encode_window.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, vp, i32, vp]
-        L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, i32, vp, vp, i32,
-                                                                          vp]
+        L.csa2_append.argtypes = [i32] + [vp] * 12 + [i64] + [vp] * 4 + [i64, i32, i32, vp, vp,
+                                                                          i32, vp]
         L.csa2_index_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, i32, vp, vp, vp, sz, vp]
         L.csa2_index_scores.argtypes = [i32, i32] + [vp] * 6 + [i64, i32, vp, vp, sz, vp]
         L.csa2_index_pool.argtypes = [i32, i32] + [vp] * 6 + [i64, i32] + [vp] * 5 + [sz, vp]
         L.csa2_reindex_topk.argtypes = [i32, i32] + [vp] * 6 + [i64, i32] + [vp] * 5 + [sz, vp]
-        L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64] +
+        L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64, i32] +
                                        [vp] * 5 + [i64, vp, vp, vp, vp, sz, vp])
-        L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, i32, vp,
-                                   vp, vp, i32, vp, vp, vp, vp, vp, sz, vp])
+        L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, i32, i32,
+                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp])
         L.csa2_encode_fp4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_encode_fp8_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_decode_fp4_rows.argtypes = [vp, vp, i64, i32, vp, vp]
+        L.csa2_encode_fp4e4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
+        L.csa2_decode_fp4e4_rows.argtypes = [vp, vp, i64, i32, vp, vp]
         L.csa2_decode_fp8_rows.argtypes = [vp, i64, i32, vp, vp]
         for name in ("csa2_compress", "csa2_encode_window", "csa2_append", "csa2_index_topk",
                      "csa2_index_scores", "csa2_index_pool", "csa2_reindex_topk", "csa2_sparse_attn",
                      "csa2_forward", "csa2_encode_fp4_rows", "csa2_encode_fp8_rows",
-                     "csa2_decode_fp4_rows", "csa2_decode_fp8_rows"):
+                     "csa2_decode_fp4_rows", "csa2_decode_fp8_rows", "csa2_encode_fp4e4_rows",
+                     "csa2_decode_fp4e4_rows"):
             getattr(L, name).restype = i32
         if L.csa2_abi_version() != ABI_VERSION:
             raise CSA2Error("libcsa2.so ABI version mismatch")
@@ -113,7 +116,7 @@ def workspace(op: int, B: int, Tq: int, H: int, entry_stride: int, device="cuda"
 
 
 def csa2_compress(pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin, z_codes,
-                  z_scales, ki_codes, ki_scales, stream=None, ratio=2):
+                  z_scales, ki_codes, ki_scales, stream=None, ratio=2, z_format=0):
     B, T = kc.shape[0], kc.shape[1]
     _check(lib().csa2_compress(B, T, _p(pos0, "i32", "pos0"), _p(kc, "bf16", "kc"),
                                _p(gc, "bf16", "gc"), _p(gamma_c, "f32", "gamma_c"),
@@ -122,7 +125,8 @@ def csa2_compress(pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rop
                                _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                                _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                                _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                               z_codes.shape[1], ratio, _stream(stream)), "csa2_compress")
+                               z_codes.shape[1], ratio, z_format, _stream(stream)),
+           "csa2_compress")
 
 
 def csa2_encode_window(pos0, wn, rope_cos, rope_sin, w_codes, w_scale, stream=None):
@@ -137,7 +141,7 @@ def csa2_encode_window(pos0, wn, rope_cos, rope_sin, w_codes, w_scale, stream=No
 
 def csa2_append(pos, kc, gc, wn, pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
                 rope_sin, z_codes, z_scales, ki_codes, ki_scales, w_codes, w_scale, stream=None,
-                ratio=2):
+                ratio=2, z_format=0):
     B = kc.shape[0]
     _check(lib().csa2_append(B, _p(pos, "i32", "pos"), _p(kc, "bf16", "kc"), _p(gc, "bf16", "gc"),
                              _p(wn, "bf16", "wn"), _p(pair_kc, "bf16", "pair_kc"),
@@ -147,7 +151,7 @@ def csa2_append(pos, kc, gc, wn, pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_g
                              _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                              _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                              _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                             z_codes.shape[1], ratio, _p(w_codes, "u8", "w_codes"),
+                             z_codes.shape[1], ratio, z_format, _p(w_codes, "u8", "w_codes"),
                              _p(w_scale, "f32", "w_scale"), w_codes.shape[1], _stream(stream)),
            "csa2_append")
 
@@ -204,12 +208,12 @@ def csa2_index_scores(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, scores, ws
 
 
 def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, sink, rope_cos,
-                     rope_sin, O, lse, ws, stream=None, win_floor=None):
+                     rope_sin, O, lse, ws, stream=None, win_floor=None, z_format=0):
     B, H, Tq = Q.shape[0], Q.shape[1], Q.shape[2]
     _check(lib().csa2_sparse_attn(B, Tq, H, _p(q_pos0, "i32", "q_pos0"), _p(Q, "bf16", "Q"),
                                   _p(w_codes, "u8", "w_codes"), _p(w_scale, "f32", "w_scale"),
                                   w_codes.shape[1], _p(z_codes, "u8", "z_codes"),
-                                  _p(z_scales, "u8", "z_scales"), z_codes.shape[1],
+                                  _p(z_scales, "u8", "z_scales"), z_codes.shape[1], z_format,
                                   _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                                   _p(sink, "f32", "sink"), _p(rope_cos, "f32", "rope_cos"),
                                   _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
@@ -222,7 +226,7 @@ def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, s
 def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, ki_codes,
                  ki_scales, w_codes, w_scale, idx, cnt, O, ws, kc=None, gc=None, wn=None,
                  gamma_c=None, w_ik=None, gamma_ik=None, ki_given=None, n_entries=None, lse=None,
-                 stream=None, ratio=2):
+                 stream=None, ratio=2, z_format=0):
     B, H, T = Q.shape[0], Q.shape[1], Q.shape[2]
     _check(lib().csa2_forward(B, T, H, _p(pos0, "i32", "pos0"), _p(kc, "bf16", "kc"),
                               _p(gc, "bf16", "gc"), _p(wn, "bf16", "wn"),
@@ -233,7 +237,7 @@ def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, k
                               _p(rope_sin, "f32", "rope_sin"), rope_cos.shape[0],
                               _p(z_codes, "u8", "z_codes"), _p(z_scales, "u8", "z_scales"),
                               _p(ki_codes, "u8", "ki_codes"), _p(ki_scales, "u8", "ki_scales"),
-                              z_codes.shape[1], ratio, _p(n_entries, "i32", "n_entries"),
+                              z_codes.shape[1], ratio, z_format, _p(n_entries, "i32", "n_entries"),
                               _p(w_codes, "u8", "w_codes"), _p(w_scale, "f32", "w_scale"),
                               w_codes.shape[1], _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
                               _p(O, "bf16", "O"), _p(lse, "f32", "lse"), _p(ws, None, "ws"),
@@ -259,6 +263,20 @@ def csa2_decode_fp4_rows(codes, scales, out, stream=None):
     _check(lib().csa2_decode_fp4_rows(_p(codes, "u8", "codes"), _p(scales, "u8", "scales"), rows,
                                       cols, _p(out, "bf16", "out"), _stream(stream)),
            "csa2_decode_fp4_rows")
+
+
+def csa2_encode_fp4e4_rows(x, codes, scales, stream=None):
+    rows, cols = x.shape
+    _check(lib().csa2_encode_fp4e4_rows(_p(x, "bf16", "x"), rows, cols, _p(codes, "u8", "codes"),
+                                        _p(scales, "u8", "scales"), _stream(stream)),
+           "csa2_encode_fp4e4_rows")
+
+
+def csa2_decode_fp4e4_rows(codes, scales, out, stream=None):
+    rows, cols = out.shape
+    _check(lib().csa2_decode_fp4e4_rows(_p(codes, "u8", "codes"), _p(scales, "u8", "scales"),
+                                        rows, cols, _p(out, "bf16", "out"), _stream(stream)),
+           "csa2_decode_fp4e4_rows")
 
 
 def csa2_decode_fp8_rows(codes, out, stream=None):

@@ -14,15 +14,21 @@ namespace csa2 {
 __global__ void k_compress(int, int, const int32_t*, const uint16_t*, const uint16_t*,
                            const float*, const uint16_t*, const float*, const uint16_t*,
                            const float*, const float*, int64_t, uint8_t*, uint8_t*, uint8_t*,
-                           uint8_t*, int64_t, int);
+                           uint8_t*, int64_t, int, int);
 __global__ void k_window_encode(int, int, const int32_t*, const uint16_t*, const float*,
                                 const float*, int64_t, uint8_t*, float*, int);
 __global__ void k_append(int, const int32_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                          uint16_t*, uint16_t*, const float*, const uint16_t*, const float*,
                          const uint16_t*, const float*, const float*, int64_t, uint8_t*, uint8_t*,
-                         uint8_t*, uint8_t*, int64_t, uint8_t*, float*, int, int);
+                         uint8_t*, uint8_t*, int64_t, uint8_t*, float*, int, int, int);
 __global__ void k_encode_fp4_rows(const uint16_t*, int64_t, int, uint8_t*, uint8_t*);
 __global__ void k_encode_fp8_rows(const uint16_t*, int64_t, int, uint8_t*, float*);
+__global__ void k_encode_fp4e4_rows(const uint16_t*, int64_t, int, uint8_t*, uint8_t*);
+__global__ void k_decode_fp4e4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
+__global__ void k_attn_dq(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
+                          const float*, int, const uint8_t*, const uint8_t*, int64_t,
+                          const int32_t*, const int32_t*, const float*, const float*,
+                          const float*, int64_t, uint16_t*, float*, const int32_t*);
 __global__ void k_decode_fp4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
 __global__ void k_decode_fp8_rows(const uint8_t*, int64_t, int, uint16_t*);
 __global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*, int);
@@ -194,6 +200,10 @@ AttnWs attn_ws(int B, int Tq, int H) {
 // position); the kernels take its log2
 bool bad_ratio(int ratio) { return ratio != 1 && ratio != 2; }
 
+// compressed-row storage: 0 = one E8M0 scale per 32 channels (16 scale bytes per
+// entry), 1 = the pages' one E4M3 scale per 16 channels (32 scale bytes)
+bool bad_zfmt(int z_format) { return z_format != 0 && z_format != 1; }
+
 bool bad_sizes(int B, int Tq, int64_t stride) {
     return B < 1 || Tq < 0 || stride < 1 || (int64_t)B * Tq > (int64_t)0x7FFFFFFF;
 }
@@ -256,10 +266,19 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
 csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
                         const uint8_t* w_codes, const float* w_scale, int cap,
                         const uint8_t* z_codes, const uint8_t* z_scales, int64_t stride,
-                        const int32_t* idx, const int32_t* cnt, const float* sink,
+                        int z_format, const int32_t* idx, const int32_t* cnt, const float* sink,
                         const float* rc, const float* rs, int64_t rope_rows, uint16_t* O,
                         float* lse, const int32_t* win_floor, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
+    if (z_format == 1) {
+        // rows in the pages' format: the dequantising kernel, one block per query
+        const int64_t rows = (int64_t)B * Tq;
+        if (rows > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
+        hipLaunchKernelGGL(k_attn_dq, dim3((unsigned)rows), dim3(256), 0, st, B, Tq, H, q_pos0,
+                           Q, w_codes, w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink,
+                           rc, rs, rope_rows, O, lse, win_floor);
+        return check_launch("csa2_sparse_attn");
+    }
     // the kernel addresses one request's caches with 32-bit byte offsets
     if ((int64_t)cap * D > (int64_t)0xFFFFFFFF || stride * 256 > (int64_t)0xFFFFFFFF)
         return fail(CSA2_ERR_RANGE, "sparse_attn: cap=%d (at most 8388607) or entry stride=%lld "
@@ -333,9 +352,10 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
                           const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
                           const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
                           uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                          int64_t entry_stride, int ratio, void* stream) {
+                          int64_t entry_stride, int ratio, int z_format, void* stream) {
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "compress: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "compress: ratio=%d (need 1 or 2)", ratio);
+    if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "compress: z_format=%d (need 0 or 1)", z_format);
     if (!pos0 || !kc || (ratio == 2 && !gc) || !gamma_c || !rope_cos || !rope_sin || !z_codes ||
         !z_scales || !ki_codes || !ki_scales)
         return fail(CSA2_ERR_NULL, "compress: a required pointer is NULL");
@@ -347,7 +367,8 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
     if (items == 0) return ok();
     hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, S(stream), B, T,
                        pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
-                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, rsh);
+                       rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, rsh,
+                       z_format);
     csa2_status s = check_launch("csa2_compress");
     return s == CSA2_OK ? ok() : s;
 }
@@ -373,10 +394,11 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
                         const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
                         int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
                         uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride, int ratio,
-                        uint8_t* w_codes, float* w_scale, int cap, void* stream) {
+                        int z_format, uint8_t* w_codes, float* w_scale, int cap, void* stream) {
     if (B < 0 || entry_stride < 1 || cap < 1)
         return fail(CSA2_ERR_SHAPE, "append: B=%d stride=%lld cap=%d", B, (long long)entry_stride, cap);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "append: ratio=%d (need 1 or 2)", ratio);
+    if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "append: z_format=%d (need 0 or 1)", z_format);
     if (!pos || !kc || !wn || (ratio == 2 && (!gc || !pair_kc || !pair_gc)) || !gamma_c ||
         !rope_cos || !rope_sin || !z_codes || !z_scales || !ki_codes || !ki_scales || !w_codes ||
         !w_scale)
@@ -388,7 +410,7 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
     hipLaunchKernelGGL(k_append, dim3((unsigned)B), dim3(128), 0, S(stream), B, pos, kc, gc, wn,
                        pair_kc, pair_gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos, rope_sin,
                        rope_rows, z_codes, z_scales, ki_codes, ki_scales, entry_stride, w_codes,
-                       w_scale, cap, ratio == 2 ? 1 : 0);
+                       w_scale, cap, ratio == 2 ? 1 : 0, z_format);
     csa2_status s = check_launch("csa2_append");
     return s == CSA2_OK ? ok() : s;
 }
@@ -509,10 +531,11 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
 csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
                              const uint8_t* w_codes, const float* w_scale, int cap,
                              const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
-                             const int32_t* idx, const int32_t* cnt, const float* sink,
-                             const float* rope_cos, const float* rope_sin, int64_t rope_rows,
-                             uint16_t* O, float* lse, const int32_t* win_floor, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             int z_format, const int32_t* idx, const int32_t* cnt,
+                             const float* sink, const float* rope_cos, const float* rope_sin,
+                             int64_t rope_rows, uint16_t* O, float* lse, const int32_t* win_floor,
+                             void* ws, size_t ws_bytes, void* stream) {
+    if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: z_format=%d (need 0 or 1)", z_format);
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "sparse_attn: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: H=%d (need 16, 32, 48 or 64)", H);
     if (!q_pos0 || !Q || !w_codes || !w_scale || !z_codes || !z_scales || !idx || !cnt || !sink ||
@@ -525,8 +548,8 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
     if (Tq > 0 && need > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_attn(B, Tq, H, q_pos0, Q, w_codes, w_scale, cap, z_codes, z_scales,
-                                entry_stride, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O,
-                                lse, win_floor, ws, S(stream));
+                                entry_stride, z_format, idx, cnt, sink, rope_cos, rope_sin,
+                                rope_rows, O, lse, win_floor, ws, S(stream));
     return s == CSA2_OK ? ok() : s;
 }
 
@@ -536,12 +559,13 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
                          const float* rope_cos, const float* rope_sin, int64_t rope_rows,
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
-                         uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                         uint8_t* ki_scales, int64_t entry_stride, int ratio, int z_format,
                          const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
                          int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
                          size_t ws_bytes, void* stream) {
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "forward: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "forward: ratio=%d (need 1 or 2)", ratio);
+    if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "forward: z_format=%d (need 0 or 1)", z_format);
     const int rsh = ratio == 2 ? 1 : 0;
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "forward: H=%d (need 16, 32, 48 or 64)", H);
     const bool prefill = kc != nullptr;
@@ -572,7 +596,7 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
             hipLaunchKernelGGL(k_compress, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st, B, T,
                                pos0, kc, gc, gamma_c, w_ik, gamma_ik, ki_given, rope_cos,
                                rope_sin, rope_rows, z_codes, z_scales, ki_codes, ki_scales,
-                               entry_stride, rsh);
+                               entry_stride, rsh, z_format);
         if (!n_entries) {
             hipLaunchKernelGGL(k_prefill_entries, dim3((unsigned)cdiv(B, 256)), dim3(256), 0, st,
                                B, T, pos0, entry_stride, ne, rsh);
@@ -584,8 +608,9 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
     s = launch_index(B, T, pos0, n_entries, qI, wI, ki_codes, ki_scales, entry_stride, rsh, idx,
                      cnt, ws, st);
     if (s != CSA2_OK) return s;
-    s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride, idx,
-                    cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, nullptr, ws, st);
+    s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride,
+                    z_format, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, nullptr, ws,
+                    st);
     return s == CSA2_OK ? ok() : s;
 }
 
@@ -598,6 +623,30 @@ csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint
     hipLaunchKernelGGL(k_encode_fp4_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
                        S(stream), x, rows, cols, codes, scales);
     csa2_status s = check_launch("csa2_encode_fp4_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_encode_fp4e4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                   uint8_t* scales, void* stream) {
+    if (rows < 0 || cols < 16 || cols % 16) return fail(CSA2_ERR_SHAPE, "encode_fp4e4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!x || !codes || !scales) return fail(CSA2_ERR_NULL, "encode_fp4e4_rows: NULL pointer");
+    const int64_t items = rows * (cols / 16);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_encode_fp4e4_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
+                       S(stream), x, rows, cols, codes, scales);
+    csa2_status s = check_launch("csa2_encode_fp4e4_rows");
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_decode_fp4e4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                   int cols, uint16_t* out, void* stream) {
+    if (rows < 0 || cols < 16 || cols % 16) return fail(CSA2_ERR_SHAPE, "decode_fp4e4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (!codes || !scales || !out) return fail(CSA2_ERR_NULL, "decode_fp4e4_rows: NULL pointer");
+    const int64_t items = rows * (cols / 8);
+    if (items == 0) return ok();
+    hipLaunchKernelGGL(k_decode_fp4e4_rows, dim3((unsigned)cdiv(items, 256)), dim3(256), 0,
+                       S(stream), codes, scales, rows, cols, out);
+    csa2_status s = check_launch("csa2_decode_fp4e4_rows");
     return s == CSA2_OK ? ok() : s;
 }
 

@@ -41,7 +41,7 @@ __device__ __forceinline__ void compress_entry(
     const float* __restrict__ gamma_ik, const float* __restrict__ cs,
     const float* __restrict__ sn, float* c_lds, float* ki_lds, uint8_t* __restrict__ z_codes,
     uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
-    uint8_t* __restrict__ ki_scales, int64_t entry_stride) {
+    uint8_t* __restrict__ ki_scales, int64_t entry_stride, int zfmt) {
     // ---- pair gate --------------------------------------------------------
     const uint4 ka = *(const uint4*)(ka_row + 8 * lane);
     const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
@@ -98,7 +98,23 @@ __device__ __forceinline__ void compress_entry(
             z[2 * q + 1] = e + f;
         }
     }
-    {
+    if (zfmt == 1) {
+        // the pages' format: lanes 2k, 2k+1 share block k of 16 channels and its
+        // E4M3 scale E4M3(max/6); elements E2M1(z / scale)
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(z[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const uint32_t sc = e4m3_code(div_rn(amax, 6.0f));
+        const float sv = e4m3_to_f32(sc);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(div_rn(z[i], sv)) << (4 * i);
+        if (!(sv > 0.0f)) word = 0;
+        const int64_t ent = (int64_t)b * entry_stride + j;
+        *(uint32_t*)(z_codes + ent * 256 + 4 * lane) = word;
+        if ((lane & 1) == 0) z_scales[ent * 32 + (lane >> 1)] = (uint8_t)sc;
+    } else {
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(z[i]));
@@ -185,7 +201,7 @@ __global__ void __launch_bounds__(256) k_compress(
     const uint16_t* __restrict__ ki_given, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint8_t* __restrict__ z_codes,
     uint8_t* __restrict__ z_scales, uint8_t* __restrict__ ki_codes,
-    uint8_t* __restrict__ ki_scales, int64_t entry_stride, int rsh) {
+    uint8_t* __restrict__ ki_scales, int64_t entry_stride, int rsh, int zfmt) {
     __shared__ float c_lds[4][D];
     __shared__ float ki_lds[4][DI];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -202,7 +218,7 @@ __global__ void __launch_bounds__(256) k_compress(
                    rsh ? gc + r0 + D : nullptr,
                    w_ik ? nullptr : ki_given + ((int64_t)b * nloc + jl) * DI, gamma_c, w_ik,
                    gamma_ik, rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds[wave], ki_lds[wave],
-                   z_codes, z_scales, ki_codes, ki_scales, entry_stride);
+                   z_codes, z_scales, ki_codes, ki_scales, entry_stride, zfmt);
 }
 
 // One window row on one wave: the 512 bf16 of wrow rotated at position p
@@ -280,7 +296,7 @@ __global__ void __launch_bounds__(128) k_append(
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t rope_rows,
     uint8_t* __restrict__ z_codes, uint8_t* __restrict__ z_scales,
     uint8_t* __restrict__ ki_codes, uint8_t* __restrict__ ki_scales, int64_t entry_stride,
-    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap, int rsh) {
+    uint8_t* __restrict__ w_codes, float* __restrict__ w_scale, int cap, int rsh, int zfmt) {
     __shared__ float c_lds[D];
     __shared__ float ki_lds[DI];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -299,7 +315,7 @@ __global__ void __launch_bounds__(128) k_append(
         compress_entry(b, p, lane, kc + row, nullptr, nullptr, nullptr,
                        w_ik ? nullptr : ki_given + (int64_t)b * DI, gamma_c, w_ik, gamma_ik,
                        rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds, ki_lds, z_codes,
-                       z_scales, ki_codes, ki_scales, entry_stride);
+                       z_scales, ki_codes, ki_scales, entry_stride, zfmt);
     } else if ((p & 1) == 0) {
         *(uint4*)(pair_kc + row + 8 * lane) = *(const uint4*)(kc + row + 8 * lane);
         *(uint4*)(pair_gc + row + 8 * lane) = *(const uint4*)(gc + row + 8 * lane);
@@ -311,7 +327,7 @@ __global__ void __launch_bounds__(128) k_append(
         compress_entry(b, j, lane, pair_kc + row, kc + row, pair_gc + row, gc + row,
                        w_ik ? nullptr : ki_given + (int64_t)b * DI, gamma_c, w_ik, gamma_ik,
                        rcos + prow * PAIRS, rsin + prow * PAIRS, c_lds, ki_lds, z_codes,
-                       z_scales, ki_codes, ki_scales, entry_stride);
+                       z_scales, ki_codes, ki_scales, entry_stride, zfmt);
     }
 }
 
@@ -346,6 +362,55 @@ __global__ void k_encode_fp4_rows(const uint16_t* __restrict__ x, int64_t rows, 
     }
     *(uint4*)(codes + r * (cols / 2) + 16 * blk) = make_uint4(out[0], out[1], out[2], out[3]);
     scales[r * nb + blk] = (uint8_t)(amax > 0.0f ? e + 127 : 0);
+}
+
+// Rows in the pages' format (E2M1, one E4M3 scale per 16): one thread per block.
+__global__ void k_encode_fp4e4_rows(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int nb = cols / 16;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= rows * nb) return;
+    const int64_t r = g / nb;
+    const int blk = (int)(g % nb);
+    const uint16_t* src = x + r * cols + 16 * blk;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint4 u = *(const uint4*)(src + 8 * q);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[8 * q + k] = bf2f((uint16_t)(w[k >> 1] >> ((k & 1) * 16)));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    const uint32_t sc = e4m3_code(div_rn(amax, 6.0f));
+    const float sv = e4m3_to_f32(sc);
+    uint32_t out[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) wv |= e2m1_code(div_rn(v[8 * q + k], sv)) << (4 * k);
+        out[q] = sv > 0.0f ? wv : 0u;
+    }
+    *(uint2*)(codes + r * (cols / 2) + 8 * blk) = make_uint2(out[0], out[1]);
+    scales[r * nb + blk] = (uint8_t)sc;
+}
+
+__global__ void k_decode_fp4e4_rows(const uint8_t* __restrict__ codes,
+                                    const uint8_t* __restrict__ scales, int64_t rows, int cols,
+                                    uint16_t* __restrict__ out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per = cols / 8;
+    if (g >= rows * per) return;
+    const int64_t r = g / per;
+    const int c8 = (int)(g % per);
+    const uint32_t w = *(const uint32_t*)(codes + r * (cols / 2) + 4 * c8);
+    const float sv = e4m3_to_f32(scales[r * (cols / 16) + (8 * c8) / 16]);
+    const uint4 o = make_uint4(fp4x2_e4_to_bf16x2(w, 0, sv), fp4x2_e4_to_bf16x2(w, 1, sv),
+                               fp4x2_e4_to_bf16x2(w, 2, sv), fp4x2_e4_to_bf16x2(w, 3, sv));
+    *(uint4*)(out + r * cols + 8 * c8) = o;
 }
 
 // FP8 rows: one wave per row (cols <= 1024).

@@ -114,7 +114,23 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return c | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
+// E4M3FN code of a non-negative finite value -> fp32 (exact)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    return e ? ldexpf((float)(8u + m), (int)e - 10) : (float)m * 0.001953125f;
+}
+
 // ---- dequantisation to bf16 (exact) ----------------------------------------
+
+// two E2M1 values (byte k of w) times an E4M3 scale value s, as packed bf16 (low =
+// element 2i): the product has at most 6 significant bits, so the bf16 is exact
+__device__ __forceinline__ uint32_t fp4x2_e4_to_bf16x2(uint32_t w, int k, float s) {
+    const bf2 v = k == 0 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)
+                : k == 1 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)
+                : k == 2 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)
+                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    return (uint32_t)f2bf((float)v[0] * s) | ((uint32_t)f2bf((float)v[1] * s) << 16);
+}
 
 // two E2M1 values of one byte, times 2^(sbyte-127), as packed bf16 (low = element 2i)
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t byte, float scale) {

@@ -55,7 +55,8 @@ class PrefillRun:
         self.pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
         u8 = torch.uint8
         self.z_codes = torch.zeros(B, self.stride, 256, dtype=u8, device=dev)
-        self.z_scales = torch.zeros(B, self.stride, 16, dtype=u8, device=dev)
+        zsb = 32 if wl.z_format == 1 else 16          # scale bytes per compressed row
+        self.z_scales = torch.zeros(B, self.stride, zsb, dtype=u8, device=dev)
         self.ki_codes = torch.zeros(B, self.stride, 64, dtype=u8, device=dev)
         self.ki_scales = torch.zeros(B, self.stride, 4, dtype=u8, device=dev)
         self.w_codes = torch.zeros(B, wl.cap, D, dtype=u8, device=dev)
@@ -72,7 +73,8 @@ class PrefillRun:
                           self.ki_scales, self.w_codes, self.w_scale, self.idx, self.cnt, self.O,
                           self.ws, kc=self.kc, gc=self.gc, wn=self.wn, gamma_c=self.gamma_c,
                           w_ik=self.w_ik, gamma_ik=self.gamma_ik, ki_given=self.ki_given,
-                          lse=self.lse, stream=stream, ratio=self.wl.ratio)
+                          lse=self.lse, stream=stream, ratio=self.wl.ratio,
+                          z_format=self.wl.z_format)
 
     def fetch(self, big=True) -> dict:
         out = dict(z_codes=down(self.z_codes), z_scales=down(self.z_scales),
@@ -96,15 +98,17 @@ class DecodeRun:
         self.rope_cos, self.rope_sin = up(cos_t, dev), up(sin_t, dev)
         u8 = torch.uint8
         self.z_codes = torch.zeros(B, N, 256, dtype=u8, device=dev)
-        self.z_scales = torch.zeros(B, N, 16, dtype=u8, device=dev)
+        zsb = 32 if wl.z_format == 1 else 16          # scale bytes per compressed row
+        self.z_scales = torch.zeros(B, N, zsb, dtype=u8, device=dev)
+        enc_z = csa2.csa2_encode_fp4e4_rows if wl.z_format == 1 else csa2.csa2_encode_fp4_rows
         self.ki_codes = torch.zeros(B, N, 64, dtype=u8, device=dev)
         self.ki_scales = torch.zeros(B, N, 4, dtype=u8, device=dev)
         for b in range(B):
             for j0 in range(0, N, chunk_rows):
                 n = min(chunk_rows, N - j0)
                 z = up(wl.z_rows(b, j0, n), dev)
-                csa2.csa2_encode_fp4_rows(z, self.z_codes[b, j0:j0 + n].view(n, 256),
-                                          self.z_scales[b, j0:j0 + n].view(n, 16))
+                enc_z(z, self.z_codes[b, j0:j0 + n].view(n, 256),
+                      self.z_scales[b, j0:j0 + n].view(n, zsb))
                 k = up(wl.ki_rows(b, j0, n), dev)
                 csa2.csa2_encode_fp4_rows(k, self.ki_codes[b, j0:j0 + n].view(n, 64),
                                           self.ki_scales[b, j0:j0 + n].view(n, 4))
@@ -131,7 +135,7 @@ class DecodeRun:
                           self.rope_sin, self.z_codes, self.z_scales, self.ki_codes,
                           self.ki_scales, self.w_codes, self.w_scale, self.idx, self.cnt, self.O,
                           self.ws, n_entries=self.n_entries, lse=self.lse, stream=stream,
-                          ratio=self.wl.ratio)
+                          ratio=self.wl.ratio, z_format=self.wl.z_format)
 
     def fetch(self) -> dict:
         return dict(idx=down(self.idx), cnt=down(self.cnt), O=down(self.O), lse=down(self.lse))

@@ -25,7 +25,14 @@
  *    Any other ratio returns CSA2_ERR_UNSUPPORTED.
  *  - Caches (per request b, `entry_stride` entries apart):
  *      z_codes  [B][entry_stride][256]  E2M1 pairs, element 2i in the low nibble of byte i
- *      z_scales [B][entry_stride][16]   E8M0 bytes, one per 32 channels (2^(byte-127))
+ *      z_scales [B][entry_stride][16]   z_format 0: E8M0 bytes, one per 32 channels
+ *                                       (2^(byte-127)); 272 bytes per entry
+ *               [B][entry_stride][32]   z_format 1, the pages' format [zharf, "Deriving
+ *                                       the 890 bytes per token"; "FP4 is a storage
+ *                                       choice"]: E4M3FN bytes, one per 16 channels,
+ *                                       scale = E4M3(max|x|/6), element = E2M1(x/scale);
+ *                                       288 bytes per entry.  Other values of z_format
+ *                                       return CSA2_ERR_UNSUPPORTED.
  *      ki_codes [B][entry_stride][64], ki_scales [B][entry_stride][4]   same format, 128 wide
  *      w_codes  [B][cap][512] E4M3FN, w_scale [B][cap] fp32: window ring, the
  *               row of position p lives in slot p mod cap.
@@ -109,7 +116,7 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
                           const float* gamma_ik, const uint16_t* ki_given, const float* rope_cos,
                           const float* rope_sin, int64_t rope_rows, uint8_t* z_codes,
                           uint8_t* z_scales, uint8_t* ki_codes, uint8_t* ki_scales,
-                          int64_t entry_stride, int ratio, void* stream);
+                          int64_t entry_stride, int ratio, int z_format, void* stream);
 
 /*
  * Window rows [atlas: W_{t,448:} <- R_t w^n_{t,448:}; W <- FP8(W); blog: the
@@ -156,7 +163,7 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
                         const uint16_t* ki_given, const float* rope_cos, const float* rope_sin,
                         int64_t rope_rows, uint8_t* z_codes, uint8_t* z_scales,
                         uint8_t* ki_codes, uint8_t* ki_scales, int64_t entry_stride, int ratio,
-                        uint8_t* w_codes, float* w_scale, int cap, void* stream);
+                        int z_format, uint8_t* w_codes, float* w_scale, int cap, void* stream);
 
 /*
  * Lightning indexer and causal top-512 [atlas: S^I_{t,j} = sum_h w^I_{t,h}
@@ -240,6 +247,9 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
  *  sink      [H] fp32.
  *  O         [B][H][Tq][512] bf16 out.   lse [B][H][Tq] fp32 out or NULL
  *            (natural log of the full softmax denominator, sink included).
+ *  z_format  storage of z_codes / z_scales (see the cache layout above).  With
+ *            z_format 1 the rows are dequantised to bf16 before both products
+ *            (the MFMA's scale operand is one power of two per 32 elements).
  *  win_floor [B] int32 device or NULL: bounded replay [zharf, section
  *            "Bounded replay trades exact state for cheaper resumption": for
  *            replay starting at s, a query at p sees window positions
@@ -248,10 +258,10 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
 csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint16_t* Q,
                              const uint8_t* w_codes, const float* w_scale, int cap,
                              const uint8_t* z_codes, const uint8_t* z_scales, int64_t entry_stride,
-                             const int32_t* idx, const int32_t* cnt, const float* sink,
-                             const float* rope_cos, const float* rope_sin, int64_t rope_rows,
-                             uint16_t* O, float* lse, const int32_t* win_floor, void* ws,
-                             size_t ws_bytes, void* stream);
+                             int z_format, const int32_t* idx, const int32_t* cnt,
+                             const float* sink, const float* rope_cos, const float* rope_sin,
+                             int64_t rope_rows, uint16_t* O, float* lse, const int32_t* win_floor,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The whole layer for one call.
@@ -268,7 +278,7 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          const uint16_t* Q, const uint16_t* qI, const float* wI, const float* sink,
                          const float* rope_cos, const float* rope_sin, int64_t rope_rows,
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
-                         uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                         uint8_t* ki_scales, int64_t entry_stride, int ratio, int z_format,
                          const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
                          int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
                          size_t ws_bytes, void* stream);
@@ -280,16 +290,22 @@ size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride);
  * Storage encoders used to fill caches from given values [zharf: E2M1 with
  * block scales; blog: FP8 window].  x [rows][cols] bf16.
  *  fp4: cols a multiple of 32; codes [rows][cols/2], scales [rows][cols/32].
+ *  fp4e4 (the pages' format, z_format 1): cols a multiple of 16; codes
+ *       [rows][cols/2], E4M3 scales [rows][cols/16].
  *  fp8: cols in 1..1024; codes [rows][cols], scale [rows] (max|x|/448, 1 if 0).
  */
 csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                  uint8_t* scales, void* stream);
+csa2_status csa2_encode_fp4e4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
+                                   uint8_t* scales, void* stream);
 csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                  float* scale, void* stream);
 
 /* Dequantisation as the attention kernel performs it, to bf16 (exact for these formats). */
 csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                  int cols, uint16_t* out, void* stream);
+csa2_status csa2_decode_fp4e4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                   int cols, uint16_t* out, void* stream);
 csa2_status csa2_decode_fp8_rows(const uint8_t* codes, int64_t rows, int cols, uint16_t* out,
                                  void* stream);
 

@@ -53,22 +53,22 @@ def test_rejects_before_launch(L):
     n = None
     # compress: NULL kc
     s = L.csa2_compress(1, 4, FAKE, n, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, 2, n)
+                        FAKE, 8, 2, 0, n)
     assert s == 1 and b"NULL" in L.csa2_last_error()
     # compress: ratio 2 needs gate logits, ratio 1 does not; only ratios 1 and 2
     s = L.csa2_compress(1, 4, FAKE, FAKE, n, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, 2, n)
+                        FAKE, 8, 2, 0, n)
     assert s == 1
     s = L.csa2_compress(1, 4, FAKE, FAKE, n, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, 3, n)
+                        FAKE, 8, 3, 0, n)
     assert s == 3 and b"ratio" in L.csa2_last_error()
     # compress: negative T
     s = L.csa2_compress(1, -2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE,
-                        FAKE, FAKE, 8, 2, n)
+                        FAKE, FAKE, 8, 2, 0, n)
     assert s == 2
     # compress: neither projection nor given keys
     s = L.csa2_compress(1, 4, FAKE, FAKE, FAKE, FAKE, n, FAKE, n, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
-                        FAKE, 8, 2, n)
+                        FAKE, 8, 2, 0, n)
     assert s == 1
     # window: cap 0
     assert L.csa2_encode_window(1, 4, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, n) == 2
@@ -78,23 +78,27 @@ def test_rejects_before_launch(L):
     s = L.csa2_index_topk(1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0, FAKE, FAKE, FAKE, 16, n)
     assert s == 3 and b"ratio" in L.csa2_last_error()
     # attention: unsupported heads, small ring, missing workspace
-    args = [FAKE] * 4 + [200, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
+    args = [FAKE] * 4 + [200, FAKE, FAKE, 64, 0] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
     assert L.csa2_sparse_attn(1, 8, 24, *args, 1 << 30, n) == 3
-    args_ring = [FAKE] * 4 + [100, FAKE, FAKE, 64] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
+    args_ring = [FAKE] * 4 + [100, FAKE, FAKE, 64, 0] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
     assert L.csa2_sparse_attn(1, 8, 64, *args_ring, 1 << 30, n) == 4
     assert L.csa2_sparse_attn(4, 1, 64, *args, 0, n) == 5
+    args_fmt = [FAKE] * 4 + [200, FAKE, FAKE, 64, 2] + [FAKE] * 5 + [16, FAKE, n, n, FAKE]
+    assert L.csa2_sparse_attn(1, 8, 64, *args_fmt, 1 << 30, n) == 3
     # forward: decode without n_entries
     s = L.csa2_forward(1, 1, 64, FAKE, n, n, n, n, n, n, n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
-                       FAKE, FAKE, FAKE, FAKE, 64, 2, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n, FAKE,
-                       1 << 30, n)
+                       FAKE, FAKE, FAKE, FAKE, 64, 2, 0, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n,
+                       FAKE, 1 << 30, n)
     assert s == 1 and b"n_entries" in L.csa2_last_error()
     # forward: ring smaller than T + 127
     s = L.csa2_forward(1, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, FAKE,
-                       FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, 2, n, FAKE, FAKE, 100, FAKE, FAKE,
-                       FAKE, n, FAKE, 1 << 30, n)
+                       FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, 2, 0, n, FAKE, FAKE, 100, FAKE,
+                       FAKE, FAKE, n, FAKE, 1 << 30, n)
     assert s == 4
     # encoders: bad widths
     assert L.csa2_encode_fp4_rows(FAKE, 4, 48, FAKE, FAKE, n) == 2
+    assert L.csa2_encode_fp4e4_rows(FAKE, 4, 40, FAKE, FAKE, n) == 2
+    assert L.csa2_decode_fp4e4_rows(FAKE, FAKE, 4, 24, FAKE, n) == 2
     assert L.csa2_encode_fp8_rows(FAKE, 4, 2048, FAKE, FAKE, n) == 2
     assert L.csa2_decode_fp8_rows(FAKE, 4, 12, FAKE, n) == 2
 

@@ -19,10 +19,12 @@ def log(*a):
     print("[gpu]", *a, flush=True)
 
 
+@pytest.mark.parametrize("zf", [0, 1])
 @pytest.mark.parametrize("ratio", [2, 1])
 @pytest.mark.parametrize("mode", ["derive", "given"])
-def test_append_matches_prefill_and_oracle(mode, ratio):
-    """ratio 1: every appended token writes its own entry; no pair buffer, no gates"""
+def test_append_matches_prefill_and_oracle(mode, ratio, zf):
+    """ratio 1: every appended token writes its own entry; no pair buffer, no gates.
+    zf = 1: entries in the pages' per-16 E4M3 format"""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -52,12 +54,13 @@ def test_append_matches_prefill_and_oracle(mode, ratio):
     log(f"csa2_append: mode={mode} ratio={ratio} B={B} T={T} prefill={prefill}")
 
     oz, ozs, ok_, oks = oracle.compress(kc, gc, gamma_c, w_ik, gamma_ik, ki, cos_t, sin_t, stride,
-                                        ratio=ratio)
+                                        ratio=ratio, z_format=zf)
     ow, ows = oracle.window_encode(wn, cos_t, sin_t, cap)
 
     def caches():
         return dict(z_codes=torch.zeros(B, stride, 256, dtype=torch.uint8, device="cuda"),
-                    z_scales=torch.zeros(B, stride, 16, dtype=torch.uint8, device="cuda"),
+                    z_scales=torch.zeros(B, stride, 32 if zf else 16, dtype=torch.uint8,
+                                         device="cuda"),
                     ki_codes=torch.zeros(B, stride, 64, dtype=torch.uint8, device="cuda"),
                     ki_scales=torch.zeros(B, stride, 4, dtype=torch.uint8, device="cuda"),
                     w_codes=torch.zeros(B, cap, 512, dtype=torch.uint8, device="cuda"),
@@ -73,7 +76,7 @@ def test_append_matches_prefill_and_oracle(mode, ratio):
     zero = torch.zeros(B, dtype=torch.int32, device="cuda")
     csa2.csa2_compress(zero, g_kc, g_gcl, g_gc, g_wik, g_gik, None if ki is None else up(ki),
                        g_cos, g_sin, A["z_codes"], A["z_scales"], A["ki_codes"], A["ki_scales"],
-                       ratio=ratio)
+                       ratio=ratio, z_format=zf)
     csa2.csa2_encode_window(zero, g_wn, g_cos, g_sin, A["w_codes"], A["w_scale"])
 
     # per-request prefills, then one token per call
@@ -87,7 +90,7 @@ def test_append_matches_prefill_and_oracle(mode, ratio):
                            g_gc, g_wik, g_gik,
                            None if ki is None else up(ki[b:b + 1, :P // ratio]), g_cos, g_sin,
                            sl["z_codes"], sl["z_scales"], sl["ki_codes"], sl["ki_scales"],
-                           ratio=ratio)
+                           ratio=ratio, z_format=zf)
         csa2.csa2_encode_window(z1, up(wn[b:b + 1, :P]), g_cos, g_sin, sl["w_codes"], sl["w_scale"])
         if ratio == 2 and P % 2:
             pair_kc[b] = up(kc[b, P - 1])
@@ -103,7 +106,7 @@ def test_append_matches_prefill_and_oracle(mode, ratio):
                          up(np.ascontiguousarray(wn[np.arange(B), take])), pair_kc, pair_gc,
                          g_gc, g_wik, g_gik, ki_new, g_cos, g_sin, Bc["z_codes"], Bc["z_scales"],
                          Bc["ki_codes"], Bc["ki_scales"], Bc["w_codes"], Bc["w_scale"],
-                         ratio=ratio)
+                         ratio=ratio, z_format=zf)
     torch.cuda.synchronize()
 
     n = T // ratio

@@ -99,6 +99,16 @@ def test_encoders_bit_exact(dev, orc):
         oc8, os8 = orc.fp8_encode_rows_bf16(x)
         assert np.array_equal(_down(c4), oc4) and np.array_equal(_down(s4), os4)
         assert np.array_equal(_down(c8), oc8) and np.array_equal(_down(s8), os8)
+        # the pages' per-16 E4M3 format, and its dequantisation
+        ce = torch.zeros(len(x), cols // 2, dtype=torch.uint8, device=dev)
+        se = torch.zeros(len(x), cols // 16, dtype=torch.uint8, device=dev)
+        csa2.csa2_encode_fp4e4_rows(xd, ce, se)
+        de = torch.zeros(len(x), cols, dtype=torch.bfloat16, device=dev)
+        csa2.csa2_decode_fp4e4_rows(ce, se, de)
+        torch.cuda.synchronize()
+        oce, ose = orc.fp4e4_encode_rows_bf16(x)
+        assert np.array_equal(_down(ce), oce) and np.array_equal(_down(se), ose)
+        assert np.array_equal(bf16_to_f64(_down(de)), orc.fp4e4_decode(oce, ose))
 
 
 # ---------------------------------------------------------------- prefill
@@ -128,7 +138,7 @@ def _check_prefill_rows(wl, out, ref, rows, attn=True):
                 O, _, _ = oracle.attend(wl.Q_rows(0, [t])[0], int(t), ref.w_codes[0],
                                         ref.w_scale[0], ref.cap, ref.z_codes[0], ref.z_scales[0],
                                         out["idx"][0, t], int(out["cnt"][0, t]), ref.sink,
-                                        ref.cos, ref.sin)
+                                        ref.cos, ref.sin, z_format=wl.z_format)
                 exp = exp.copy()
                 exp[i] = O
         mx, rel = check_attention(got, exp, wl.name)
@@ -170,12 +180,14 @@ def test_prefill_clustered_keys_ragged(dev, synth):
     _check_prefill_rows(wl, out, ref, rows)
 
 
-@pytest.mark.parametrize("cid,T,H", [(0, 257, 16), (1, 1400, 16)])
-def test_prefill_ratio_one(dev, synth, cid, T, H):
+@pytest.mark.parametrize("cid,T,H,zf", [(0, 257, 16, 0), (1, 1400, 16, 0), (0, 257, 16, 1),
+                                         (1, 1400, 32, 1)])
+def test_prefill_ratio_one(dev, synth, cid, T, H, zf):
     """compression ratio one: T entries, entry t rotated at t, a query at t sees entries
-    0..t (top-512 active from t = 512 on); caches bit-exact, rows against the oracle"""
+    0..t (top-512 active from t = 512 on); caches bit-exact, rows against the oracle.
+    zf = 1: compressed rows in the pages' per-16 E4M3 format (dequantising attention)"""
     from oracle.reference import PrefillReference
-    wl = synth.workload(cid, T=T, H=H, ratio=1)
+    wl = synth.workload(cid, T=T, H=H, ratio=1, z_format=zf)
     out = _prefill(wl).fetch()
     ref = PrefillReference(wl)
     for k in ("z_codes", "z_scales", "ki_codes", "ki_scales"):
@@ -185,6 +197,21 @@ def test_prefill_ratio_one(dev, synth, cid, T, H):
          np.random.default_rng(5).integers(0, T, 30)]))
     assert np.all(out["cnt"][0, rows] == np.minimum(rows + 1, 512))
     _check_prefill_rows(wl, out, ref, rows)
+
+
+@pytest.mark.parametrize("T,H", [(256, 16), (131, 48)])
+def test_prefill_pages_z_format(dev, synth, T, H):
+    """ratio 2 with compressed rows in the pages' per-16 E4M3 format: caches bit-exact
+    (288-byte entries), every row's selection and attention against the oracle"""
+    from oracle.reference import PrefillReference
+    wl = synth.workload(0, T=T, H=H, z_format=1)
+    out = _prefill(wl).fetch()
+    ref = PrefillReference(wl)
+    n = T // 2
+    assert out["z_scales"].shape[2] == 32
+    for k in ("z_codes", "z_scales", "ki_codes", "ki_scales"):
+        assert np.array_equal(out[k][0, :n], getattr(ref, k)[0, :n]), k
+    _check_prefill_rows(wl, out, ref, np.arange(T))
 
 
 def test_prefill_deterministic(dev, synth):
@@ -233,15 +260,17 @@ def test_sparse_attn_given_oracle_selection(dev, synth):
     log(f"  max|dO|={mx:.2e} rel={rel:.2e}")
 
 
-def test_sparse_attn_bounded_replay_floor(dev, synth):
+@pytest.mark.parametrize("zf", [0, 1])
+def test_sparse_attn_bounded_replay_floor(dev, synth, zf):
     """attention with a per-request replay start s: request 0 none, request 1 a start
-    inside the 128-row window, request 2 a start past every query (one window row)"""
+    inside the 128-row window, request 2 a start past every query (one window row);
+    zf = 1: compressed rows in the pages' per-16 E4M3 format"""
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     import oracle
     from oracle.reference import DecodeReference
     B, Tq, N, H = 3, 5, 2600, 64
-    wl = synth.decode_workload(B=B, Tq=Tq, n_entries=N, H=H)
+    wl = synth.decode_workload(B=B, Tq=Tq, n_entries=N, H=H, z_format=zf)
     p0 = wl.q_pos0
     floors = np.array([0, p0 - 40, p0 + 100], np.int32)
     log(f"csa2_sparse_attn with replay starts {floors.tolist()}: {wl.name}")
@@ -262,7 +291,7 @@ def test_sparse_attn_bounded_replay_floor(dev, synth):
     csa2.csa2_sparse_attn(_up(np.full(B, p0, np.int32)), _up(wl.Q()), stack("w_codes"),
                           stack("w_scale"), stack("z_codes"), stack("z_scales"), _up(idx),
                           _up(cnts), _up(refs[0].sink), _up(cos_t), _up(sin_t), O, lse, ws,
-                          win_floor=_up(floors))
+                          win_floor=_up(floors), z_format=zf)
     torch.cuda.synchronize()
     got_O, got_lse = _down(O), _down(lse)
     Q = wl.Q()
@@ -274,22 +303,28 @@ def test_sparse_attn_bounded_replay_floor(dev, synth):
             exp[i], exp_lse[i], _ = oracle.attend(Q[b][:, i, :], p0 + i, r.w_codes, r.w_scale,
                                                   wl.cap, r.z_codes, r.z_scales, idx[b, i],
                                                   int(cnts[b, i]), r.sink, r.cos, r.sin,
-                                                  w_floor=int(floors[b]))
+                                                  w_floor=int(floors[b]), z_format=zf)
         mx, rel = check_attention(got_O[b].transpose(1, 0, 2), exp, f"floor {floors[b]}")
         assert np.max(np.abs(got_lse[b].T - exp_lse)) < 1e-3
         log(f"  request {b} (s={floors[b]}): max|dO|={mx:.2e} rel={rel:.2e}")
 
 
 # ---------------------------------------------------------------- decode
-@pytest.mark.parametrize("Tq,N,keys,ratio", [(1, 3000, "flat", 2), (6, 2600, "lognormal_dup", 2),
-                                             (6, 2600, "lognormal_dup", 1), (1, 700, "flat", 1)])
-def test_decode_small(dev, synth, Tq, N, keys, ratio):
+@pytest.mark.parametrize("Tq,N,keys,ratio,zf", [(1, 3000, "flat", 2, 0),
+                                                (6, 2600, "lognormal_dup", 2, 0),
+                                                (6, 2600, "lognormal_dup", 1, 0),
+                                                (1, 700, "flat", 1, 0),
+                                                (6, 2600, "lognormal_dup", 1, 1),
+                                                (1, 3000, "flat", 2, 1)])
+def test_decode_small(dev, synth, Tq, N, keys, ratio, zf):
     """ratio 1: one entry per position, a query at p sees entries 0..p (700 entries: every
-    one selectable only up to 512, the window and the entries overlap)"""
+    one selectable only up to 512, the window and the entries overlap); zf = 1: the
+    pages' per-16 E4M3 compressed rows"""
     import torch
     import csa2_harness
     from oracle.reference import DecodeReference
-    wl = synth.decode_workload(B=3, Tq=Tq, n_entries=N, H=64, keys=keys, ratio=ratio)
+    wl = synth.decode_workload(B=3, Tq=Tq, n_entries=N, H=64, keys=keys, ratio=ratio,
+                               z_format=zf)
     log(f"csa2_forward decode: {wl.name} keys={keys}")
     run = csa2_harness.DecodeRun(wl)
     run.forward()
@@ -309,7 +344,8 @@ def test_decode_small(dev, synth, Tq, N, keys, ratio):
                 ref._ensure_z(out["idx"][b, i])
                 exp[i] = oracle.attend(wl.Q()[b][:, i, :], wl.q_pos0 + i, ref.w_codes, ref.w_scale,
                                        wl.cap, ref.z_codes, ref.z_scales, out["idx"][b, i],
-                                       int(out["cnt"][b, i]), ref.sink, ref.cos, ref.sin)[0]
+                                       int(out["cnt"][b, i]), ref.sink, ref.cos, ref.sin,
+                                       z_format=zf)[0]
         mx, rel = check_attention(out["O"][b].transpose(1, 0, 2), exp, wl.name)
         log(f"  request {b}: swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
 
