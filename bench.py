@@ -150,11 +150,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "pool", "decode1", "pool1", "copy"],
-                    default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "pool", "decode1", "decode1z", "pool1",
+                                       "copy"], default=None,
                     help="time a single workload (for profiling runs); 'copy' runs a plain "
                          "1 GiB device copy, the calibration kernel for the HBM byte counters; "
-                         "decode1 / pool1 are the ratio-1 forms")
+                         "decode1 / pool1 are the ratio-1 forms, decode1z the ratio-1 form with "
+                         "the pages' 288-byte rows")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
     args = ap.parse_args()
@@ -183,10 +184,13 @@ def main():
                           "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
-    if args.only in ("decode", "pool", "decode1", "pool1"):
+    if args.only in ("decode", "pool", "decode1", "pool1", "decode1z"):
         args.no_cpu = True
-        fn = run_decode if args.only.startswith("decode") else run_pool
-        fn(args, result, stream, ratio=1 if args.only.endswith("1") else 2)
+        if args.only.startswith("decode"):
+            run_decode(args, result, stream, ratio=1 if "1" in args.only else 2,
+                       z_format=1 if args.only.endswith("z") else 0)
+        else:
+            run_pool(args, result, stream, ratio=1 if args.only.endswith("1") else 2)
         print(json.dumps(result), flush=True)
         return
     # ---------------------------------------------------------------- prefill
@@ -243,6 +247,7 @@ def main():
         run_decode(args, result, stream)
         run_pool(args, result, stream)
         run_decode(args, result, stream, ratio=1)
+        run_decode(args, result, stream, ratio=1, z_format=1)
         run_pool(args, result, stream, ratio=1)
 
     # ---------------------------------------------------------------- CPU oracle
@@ -252,10 +257,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_decode(args, result, stream, ratio=2):
+def run_decode(args, result, stream, ratio=2, z_format=0):
     """Batched decode B=128 x 1 query at position 131071.  ratio 2: the measured
     workload (65,536 pooled entries per request); ratio 1: its decoder-layer form
-    (131,072 entries, one per position)."""
+    (131,072 entries, one per position); z_format 1: compressed rows in the pages'
+    288-byte format (one E4M3 scale per 16), attended by the dequantising kernel."""
     import dataclasses
     import torch
     import csa2_harness
@@ -265,7 +271,9 @@ def run_decode(args, result, stream, ratio=2):
         if ratio == 1:
             dwl = dataclasses.replace(dwl, n_entries=dwl.q_pos0 + 1, ratio=1,
                                       name=dwl.name + " ratio 1")
-        key = "decode" if ratio == 2 else "decode_ratio1"
+        if z_format == 1:
+            dwl = dataclasses.replace(dwl, z_format=1, name=dwl.name + " Z per-16 E4M3")
+        key = ("decode" if ratio == 2 else "decode_ratio1") + ("_z16" if z_format == 1 else "")
         log(f"generating caches: {dwl.name}")
         t0 = time.time()
         drun = csa2_harness.DecodeRun(dwl)
@@ -280,8 +288,9 @@ def run_decode(args, result, stream, ratio=2):
         scan_bytes = 68.0 * dwl.n_entries * dwl.B
         result[key] = {
             "workload": f"CSA2 batched decode B=128 x 1 query, 131072 context ({dwl.n_entries} "
-                        f"FP4 entries at compression ratio {ratio} + 128 FP8 window rows), H=64, "
-                        "top-512",
+                        f"FP4 entries at compression ratio {ratio}, "
+                        f"{'288-byte (E4M3 per 16)' if z_format else '272-byte (E8M0 per 32)'} "
+                        "rows, + 128 FP8 window rows), H=64, top-512",
             "value": dwl.B * dwl.Tq / (dms * 1e-3), "unit": "query-tokens/s", "ms_per_step": dms,
             "stages_ms": dstages,
             "hbm_frac_step": nbytes / (dms * 1e-3) / PEAK_HBM,
@@ -293,6 +302,15 @@ def run_decode(args, result, stream, ratio=2):
                          "traffic": measured_traffic("k_index_scores", "decode",
                                                      dwl.q_pos0 + 1) if ratio == 2 else None},
         }
+        # attention's own traffic: the selected rows, the window rows, Q and O
+        zrow = 288.0 if z_format else 272.0
+        att_bytes = dwl.B * dwl.Tq * (512 * zrow + 128 * 516 + 2 * dwl.H * 512 * 2)
+        result[key]["attention"] = {
+            "kernel": "k_attn_dq (dequantise to bf16 in LDS, bf16 MFMA)" if z_format else
+                      "k_attn (FP8/FP4 scaled MFMA QK, bf16 MFMA PV)",
+            "ms": dstages["sparse_attn"], "bytes": att_bytes,
+            "GB/s": att_bytes / (dstages["sparse_attn"] * 1e-3) / 1e9,
+            "frac_hbm": att_bytes / (dstages["sparse_attn"] * 1e-3) / PEAK_HBM}
         # decode append (one new token per request, half of them closing a pair):
         # window row, pair buffer, entry of a completed pair, into the same caches
         import compressed_sparse_attention_csa2_amd as csa2
@@ -309,7 +327,8 @@ def run_decode(args, result, stream, ratio=2):
         append = lambda: csa2.csa2_append(a_pos, a_kc, a_gc, a_wn, a_pkc, a_pgc, a_gamma, None,
                                           None, a_ki, drun.rope_cos, drun.rope_sin, drun.z_codes,
                                           drun.z_scales, drun.ki_codes, drun.ki_scales,
-                                          drun.w_codes, drun.w_scale, ratio=ratio)
+                                          drun.w_codes, drun.w_scale, ratio=ratio,
+                                          z_format=z_format)
         for _ in range(max(args.warmup, 3)):
             append()
         ams = time_events(append, max(args.steps, 20), stream)

@@ -28,7 +28,8 @@ __global__ void k_decode_fp4e4_rows(const uint8_t*, const uint8_t*, int64_t, int
 __global__ void k_attn_dq(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                           const float*, int, const uint8_t*, const uint8_t*, int64_t,
                           const int32_t*, const int32_t*, const float*, const float*,
-                          const float*, int64_t, uint16_t*, float*, const int32_t*);
+                          const float*, int64_t, uint16_t*, float*, const int32_t*, int, float*,
+                          float*);
 __global__ void k_decode_fp4_rows(const uint8_t*, const uint8_t*, int64_t, int, uint16_t*);
 __global__ void k_decode_fp8_rows(const uint8_t*, int64_t, int, uint16_t*);
 __global__ void k_prefill_entries(int, int, const int32_t*, int64_t, int32_t*, int);
@@ -271,12 +272,22 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
                         float* lse, const int32_t* win_floor, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
     if (z_format == 1) {
-        // rows in the pages' format: the dequantising kernel, one block per query
-        const int64_t rows = (int64_t)B * Tq;
-        if (rows > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
-        hipLaunchKernelGGL(k_attn_dq, dim3((unsigned)rows), dim3(256), 0, st, B, Tq, H, q_pos0,
+        // rows in the pages' format: the dequantising kernel, one block per (query,
+        // split); the splits' partials are merged as on the per-32 path
+        const AttnWs L = attn_ws(B, Tq, H);
+        float* pO = (float*)((uint8_t*)ws + L.pO);
+        float* pml = (float*)((uint8_t*)ws + L.pml);
+        const int64_t units = (int64_t)B * Tq * L.nsplit;
+        if (units > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
+        hipLaunchKernelGGL(k_attn_dq, dim3((unsigned)units), dim3(256), 0, st, B, Tq, H, q_pos0,
                            Q, w_codes, w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink,
-                           rc, rs, rope_rows, O, lse, win_floor);
+                           rc, rs, rope_rows, O, lse, win_floor, L.nsplit, pO, pml);
+        if (L.nsplit > 1) {
+            const int64_t items = (int64_t)B * Tq * H;
+            hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st,
+                               B, Tq, H, q_pos0, sink, rc, rs, rope_rows, L.nsplit, pO, pml, O,
+                               lse);
+        }
         return check_launch("csa2_sparse_attn");
     }
     // the kernel addresses one request's caches with 32-bit byte offsets

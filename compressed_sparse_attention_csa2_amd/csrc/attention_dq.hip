@@ -13,7 +13,10 @@
 // the selected rows; S = Q G / sqrt(512); a per-head sink in the softmax
 // denominator; O = A G; channels 448.. turned back by R_p^{-1}.
 //
-// One block of four waves per query token.  Per chunk of 32 rows: all waves
+// One block of four waves per (query token, split of its rows); with several
+// splits the blocks leave unnormalised partials (O, running max in log2 units,
+// denominator) for the merge kernel shared with the per-32 path.  Per chunk of
+// 32 rows: all waves
 // copy the rows into LDS twice, row-major (the operand of Q G^T) and
 // channel-major (the operand of G^T P^T); wave w then owns heads 16w..16w+15
 // (its Q in registers as the MFMA A operand) and keeps its O^T in 32 tiles of
@@ -26,7 +29,8 @@ namespace csa2 {
 namespace {
 constexpr int DQ_ROWS = 32;              // rows per chunk
 constexpr int GS_PITCH = D + 8;          // row-major copy: 1040 bytes per row
-constexpr int GT_PITCH = DQ_ROWS + 8;    // channel-major copy: 80 bytes per channel
+constexpr int GT_PITCH = DQ_ROWS + 8;    // channel-major copy: 80 bytes per channel, and
+constexpr int GT_SKEW = 32;              // 64 more bytes per block of 32 channels (banks)
 constexpr int PT_PITCH = DQ_ROWS + 8;    // P^T staging: 80 bytes per head
 constexpr float DQ_LOG2E = 1.4426950408889634f;
 }  // namespace
@@ -38,17 +42,20 @@ __global__ void __launch_bounds__(256) k_attn_dq(
     int64_t entry_stride, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     const float* __restrict__ sink, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint16_t* __restrict__ O,
-    float* __restrict__ lse, const int32_t* __restrict__ win_floor) {
+    float* __restrict__ lse, const int32_t* __restrict__ win_floor, int nsplit,
+    float* __restrict__ part_O, float* __restrict__ part_ml) {
     __shared__ __attribute__((aligned(16))) uint16_t Gs[DQ_ROWS * GS_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Gt[D * GT_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t Gt[D * GT_PITCH + (D / 32) * GT_SKEW];
     __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * PT_PITCH];
     __shared__ float rsc[DQ_ROWS];
+    __shared__ int32_t sidx[TOPK];
     __shared__ float corr_s[4][16];
     __shared__ float ml_s[4][2][16];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
-    const int64_t qrow = blockIdx.x;
+    const int64_t qrow = blockIdx.x / nsplit;
+    const int split = (int)(blockIdx.x - qrow * nsplit);
     if (qrow >= (int64_t)B * Tq) return;
     const int b = (int)(qrow / Tq), t = (int)(qrow - (int64_t)b * Tq);
     int64_t p = (int64_t)q_pos0[b] + t;
@@ -88,33 +95,64 @@ __global__ void __launch_bounds__(256) k_attn_dq(
     float l_run[4] = {0.f, 0.f, 0.f, 0.f};
     const float lscale = DQ_LOG2E / sqrtf((float)D);
 
-    // copy role: rows 2rp, 2rp+1 of the chunk, channels 32cq..32cq+31
-    const int rp = tid >> 4, cq = tid & 15;
+    // copy role: rows 2rp, 2rp+1 of the chunk, channels 32cq..32cq+31 (a wave's
+    // lanes take 16 row pairs of 4 channel blocks: its channel-major writes fall
+    // in distinct banks)
+    const int rp = tid & 15, cq = tid >> 4;
+    uint16_t* const gtw = &Gt[32 * cq * GT_PITCH + cq * GT_SKEW + 2 * rp];
     const int nchunks = (nrows + DQ_ROWS - 1) / DQ_ROWS;
-    for (int ck = 0; ck < nchunks; ++ck) {
+    const int cps = (nchunks + nsplit - 1) / nsplit;
+    const int ck0 = split * cps, ck1 = ck0 + cps < nchunks ? ck0 + cps : nchunks;
+    // the selected entries, clamped into the cache
+    for (int k = tid; k < nc; k += 256) {
+        const int32_t e = sel[k];
+        sidx[k] = e < 0 ? 0 : (e > emax ? (int32_t)emax : e);
+    }
+    __syncthreads();
+    // raw bytes of this thread's two rows of chunk ck: loaded one chunk ahead
+    uint4 ra[2], rb[2];
+    uint32_t rw[2];                          // window: fp32 scale bits; compressed: scale bytes
+    int kind[2];                             // 0 no row, 1 window row, 2 compressed row
+    auto load = [&](int ck) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int i = ck * DQ_ROWS + 2 * rp + h2;
+            if (i < nwin) {
+                const int64_t slot = (w0 + i) % cap;
+                const uint8_t* src = wrow0 + slot * D + 32 * cq;
+                ra[h2] = *(const uint4*)src;
+                rb[h2] = *(const uint4*)(src + 16);
+                rw[h2] = __float_as_uint(wsc0[slot]);
+                kind[h2] = 1;
+            } else if (i < nrows) {
+                const int64_t e = sidx[i - nwin];
+                ra[h2] = *(const uint4*)(zc0 + e * 256 + 16 * cq);
+                rw[h2] = *(const uint16_t*)(zs0 + e * 32 + 2 * cq);
+                kind[h2] = 2;
+            } else {
+                kind[h2] = 0;
+            }
+        }
+    };
+    if (ck0 < ck1) load(ck0);
+    for (int ck = ck0; ck < ck1; ++ck) {
         // ---- copy: two rows, 32 channels each, into both LDS layouts -------
         uint32_t v[2][16];                   // packed bf16 pairs: channels 32cq + 2k, +1
         float scale[2] = {0.0f, 0.0f};       // row scale: window rows' fp32 scale, else 1 (0: no row)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const int i = ck * DQ_ROWS + 2 * rp + h2;
-            if (i < nwin) {
-                int64_t slot = (w0 + i) % cap;
-                const uint8_t* src = wrow0 + slot * D + 32 * cq;
-                const uint4 a = *(const uint4*)src, c = *(const uint4*)(src + 16);
+            if (kind[h2] == 1) {
+                const uint4 a = ra[h2], c = rb[h2];
                 const uint32_t wv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     v[h2][2 * k] = fp8x2_to_bf16x2<false>(wv[k]);
                     v[h2][2 * k + 1] = fp8x2_to_bf16x2<true>(wv[k]);
                 }
-                scale[h2] = wsc0[slot];
-            } else if (i < nrows) {
-                int64_t e = sel[i - nwin];
-                e = e < 0 ? 0 : (e > emax ? emax : e);
-                const uint4 a = *(const uint4*)(zc0 + e * 256 + 16 * cq);
-                const uint32_t sw = *(const uint16_t*)(zs0 + e * 32 + 2 * cq);
-                const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32(sw >> 8);
+                scale[h2] = __uint_as_float(rw[h2]);
+            } else if (kind[h2] == 2) {
+                const uint4 a = ra[h2];
+                const float s0 = e4m3_to_f32(rw[h2] & 0xFFu), s1 = e4m3_to_f32(rw[h2] >> 8);
                 const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -146,10 +184,11 @@ __global__ void __launch_bounds__(256) k_attn_dq(
         for (int k = 0; k < 16; ++k) {
             // channels 32cq + 2k and +1: rows 2rp, 2rp+1 side by side
             const uint32_t a = v[0][k], c = v[1][k];
-            *(uint32_t*)&Gt[(32 * cq + 2 * k) * GT_PITCH + 2 * rp] = (a & 0xFFFFu) | (c << 16);
-            *(uint32_t*)&Gt[(32 * cq + 2 * k + 1) * GT_PITCH + 2 * rp] = (a >> 16) | (c & 0xFFFF0000u);
+            *(uint32_t*)(gtw + (2 * k) * GT_PITCH) = (a & 0xFFFFu) | (c << 16);
+            *(uint32_t*)(gtw + (2 * k + 1) * GT_PITCH) = (a >> 16) | (c & 0xFFFF0000u);
         }
         __syncthreads();
+        if (ck + 1 < ck1) load(ck + 1);      // in flight during this chunk's products
         if (!heads) continue;
 
         // ---- S = Q G^T over the chunk's two tiles of 16 rows -------------------
@@ -215,8 +254,8 @@ __global__ void __launch_bounds__(256) k_attn_dq(
         const uint16_t* gt = &Gt[n16 * GT_PITCH + 8 * g];
 #pragma unroll
         for (int ct = 0; ct < 32; ++ct)
-            oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf8*)(gt + 16 * ct * GT_PITCH),
-                                                               pb, oacc[ct], 0, 0, 0);
+            oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *(const bf8*)(gt + 16 * ct * GT_PITCH + (ct >> 1) * GT_SKEW), pb, oacc[ct], 0, 0, 0);
         // Pt and corr_s are rewritten next chunk only after the block barrier
     }
     if (!heads) return;
@@ -232,6 +271,18 @@ __global__ void __launch_bounds__(256) k_attn_dq(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     const float m = ml_s[wave][0][n16], l = ml_s[wave][1][n16];
+    if (nsplit > 1) {
+        // partials of this split: O^T tiles as they are, (m, l) per head
+        const int64_t pbase = (qrow * nsplit + split) * H + hq;
+        float* po = part_O + pbase * D;
+#pragma unroll
+        for (int ct = 0; ct < 32; ++ct) *(f4*)(po + 16 * ct + 4 * g) = oacc[ct];
+        if (g == 0) {
+            part_ml[pbase * 2] = m;
+            part_ml[pbase * 2 + 1] = l;
+        }
+        return;
+    }
     const float shv = sink[hq] * DQ_LOG2E;
     const float M = fmaxf(m, shv);
     const float em = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
