@@ -367,6 +367,7 @@ csa2_status csa2_compress(int B, int T, const int32_t* pos0, const uint16_t* kc,
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "compress: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "compress: ratio=%d (need 1 or 2)", ratio);
     if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "compress: z_format=%d (need 0 or 1)", z_format);
+    if (T == 0) return ok();     // no work: no pointer is read
     if (!pos0 || !kc || (ratio == 2 && !gc) || !gamma_c || !rope_cos || !rope_sin || !z_codes ||
         !z_scales || !ki_codes || !ki_scales)
         return fail(CSA2_ERR_NULL, "compress: a required pointer is NULL");
@@ -388,6 +389,7 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
                                const float* rope_cos, const float* rope_sin, int64_t rope_rows,
                                uint8_t* w_codes, float* w_scale, int cap, void* stream) {
     if (bad_sizes(B, T, 1) || cap < 1) return fail(CSA2_ERR_SHAPE, "encode_window: B=%d T=%d cap=%d", B, T, cap);
+    if (T == 0) return ok();     // no work: no pointer is read
     if (!pos0 || !wn || !rope_cos || !rope_sin || !w_codes || !w_scale)
         return fail(CSA2_ERR_NULL, "encode_window: a required pointer is NULL");
     if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "encode_window: empty rotary table");
@@ -410,6 +412,7 @@ csa2_status csa2_append(int B, const int32_t* pos, const uint16_t* kc, const uin
         return fail(CSA2_ERR_SHAPE, "append: B=%d stride=%lld cap=%d", B, (long long)entry_stride, cap);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "append: ratio=%d (need 1 or 2)", ratio);
     if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "append: z_format=%d (need 0 or 1)", z_format);
+    if (B == 0) return ok();     // no work: no pointer is read
     if (!pos || !kc || !wn || (ratio == 2 && (!gc || !pair_kc || !pair_gc)) || !gamma_c ||
         !rope_cos || !rope_sin || !z_codes || !z_scales || !ki_codes || !ki_scales || !w_codes ||
         !w_scale)
@@ -433,6 +436,7 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
                             void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_topk: ratio=%d (need 1 or 2)", ratio);
+    if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
     const size_t need = index_ws(B, Tq, entry_stride).total;
@@ -451,6 +455,7 @@ csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_pool: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_pool: ratio=%d (need 1 or 2)", ratio);
     const int rsh = ratio == 2 ? 1 : 0;
+    if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt || !pool ||
         !pool_cnt)
         return fail(CSA2_ERR_NULL, "index_pool: a required pointer is NULL");
@@ -482,6 +487,7 @@ csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "reindex_topk: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "reindex_topk: ratio=%d (need 1 or 2)", ratio);
     const int rsh = ratio == 2 ? 1 : 0;
+    if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !pool || !pool_cnt ||
         !idx || !cnt)
         return fail(CSA2_ERR_NULL, "reindex_topk: a required pointer is NULL");
@@ -527,6 +533,7 @@ csa2_status csa2_index_scores(int B, int Tq, const int32_t* q_pos0, const int32_
                               float* scores, void* ws, size_t ws_bytes, void* stream) {
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_scores: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_scores: ratio=%d (need 1 or 2)", ratio);
+    if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !scores)
         return fail(CSA2_ERR_NULL, "index_scores: a required pointer is NULL");
     const size_t need = index_ws(B, Tq, entry_stride).S;
@@ -549,6 +556,7 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
     if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: z_format=%d (need 0 or 1)", z_format);
     if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "sparse_attn: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "sparse_attn: H=%d (need 16, 32, 48 or 64)", H);
+    if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !Q || !w_codes || !w_scale || !z_codes || !z_scales || !idx || !cnt || !sink ||
         !rope_cos || !rope_sin || !O)
         return fail(CSA2_ERR_NULL, "sparse_attn: a required pointer is NULL");
@@ -580,6 +588,7 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
     const int rsh = ratio == 2 ? 1 : 0;
     if (H < 16 || H > 64 || H % 16) return fail(CSA2_ERR_UNSUPPORTED, "forward: H=%d (need 16, 32, 48 or 64)", H);
     const bool prefill = kc != nullptr;
+    if (T == 0) return ok();     // no work: no pointer is read
     if (!pos0 || !Q || !qI || !wI || !sink || !rope_cos || !rope_sin || !z_codes || !z_scales ||
         !ki_codes || !ki_scales || !w_codes || !w_scale || !idx || !cnt || !O)
         return fail(CSA2_ERR_NULL, "forward: a required pointer is NULL");
@@ -628,6 +637,7 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
 csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                  uint8_t* scales, void* stream) {
     if (rows < 0 || cols < 32 || cols % 32) return fail(CSA2_ERR_SHAPE, "encode_fp4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!x || !codes || !scales) return fail(CSA2_ERR_NULL, "encode_fp4_rows: NULL pointer");
     const int64_t items = rows * (cols / 32);
     if (items == 0) return ok();
@@ -640,6 +650,7 @@ csa2_status csa2_encode_fp4_rows(const uint16_t* x, int64_t rows, int cols, uint
 csa2_status csa2_encode_fp4e4_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                    uint8_t* scales, void* stream) {
     if (rows < 0 || cols < 16 || cols % 16) return fail(CSA2_ERR_SHAPE, "encode_fp4e4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!x || !codes || !scales) return fail(CSA2_ERR_NULL, "encode_fp4e4_rows: NULL pointer");
     const int64_t items = rows * (cols / 16);
     if (items == 0) return ok();
@@ -652,6 +663,7 @@ csa2_status csa2_encode_fp4e4_rows(const uint16_t* x, int64_t rows, int cols, ui
 csa2_status csa2_decode_fp4e4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                    int cols, uint16_t* out, void* stream) {
     if (rows < 0 || cols < 16 || cols % 16) return fail(CSA2_ERR_SHAPE, "decode_fp4e4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!codes || !scales || !out) return fail(CSA2_ERR_NULL, "decode_fp4e4_rows: NULL pointer");
     const int64_t items = rows * (cols / 8);
     if (items == 0) return ok();
@@ -664,6 +676,7 @@ csa2_status csa2_decode_fp4e4_rows(const uint8_t* codes, const uint8_t* scales, 
 csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                  float* scale, void* stream) {
     if (rows < 0 || cols < 1 || cols > 1024) return fail(CSA2_ERR_SHAPE, "encode_fp8_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!x || !codes || !scale) return fail(CSA2_ERR_NULL, "encode_fp8_rows: NULL pointer");
     if (rows == 0) return ok();
     hipLaunchKernelGGL(k_encode_fp8_rows, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, S(stream),
@@ -675,6 +688,7 @@ csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint
 csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                  int cols, uint16_t* out, void* stream) {
     if (rows < 0 || cols < 32 || cols % 32) return fail(CSA2_ERR_SHAPE, "decode_fp4_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!codes || !scales || !out) return fail(CSA2_ERR_NULL, "decode_fp4_rows: NULL pointer");
     const int64_t items = rows * (cols / 8);
     if (items == 0) return ok();
@@ -687,6 +701,7 @@ csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, in
 csa2_status csa2_decode_fp8_rows(const uint8_t* codes, int64_t rows, int cols, uint16_t* out,
                                  void* stream) {
     if (rows < 0 || cols < 8 || cols % 8) return fail(CSA2_ERR_SHAPE, "decode_fp8_rows: rows=%lld cols=%d", (long long)rows, cols);
+    if (rows == 0) return ok();     // no work: no pointer is read
     if (!codes || !out) return fail(CSA2_ERR_NULL, "decode_fp8_rows: NULL pointer");
     const int64_t items = rows * (cols / 8);
     if (items == 0) return ok();

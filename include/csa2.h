@@ -44,6 +44,8 @@
  *    of bounds.  Host-visible sizes are validated before anything is launched:
  *    on failure the call returns a status, launches nothing, writes nothing
  *    and records a message for csa2_last_error().
+ *  - A call with no work (T, Tq or rows = 0; B = 0 for csa2_append) returns
+ *    CSA2_OK after the size checks, reads no pointer and launches nothing.
  *  - No C++ exception crosses this boundary.  Calls are thread-safe.
  *
  * Citations name the page and the passage that defines each operation:

@@ -103,6 +103,18 @@ def test_rejects_before_launch(L):
     assert L.csa2_decode_fp8_rows(FAKE, 4, 12, FAKE, n) == 2
 
 
+def test_empty_calls_read_no_pointer(L):
+    """T / Tq / rows = 0: CSA2_OK with every pointer NULL (nothing is launched)"""
+    n = None
+    assert L.csa2_compress(1, 0, n, n, n, n, n, n, n, n, n, 16, n, n, n, n, 8, 2, 0, n) == 0
+    assert L.csa2_index_topk(1, 0, n, n, n, n, n, n, 64, 2, n, n, n, 0, n) == 0
+    assert L.csa2_index_scores(1, 0, n, n, n, n, n, n, 64, 1, n, n, 0, n) == 0
+    assert L.csa2_sparse_attn(1, 0, 64, n, n, n, n, 200, n, n, 64, 1, n, n, n, n, n, 16, n, n, n,
+                              n, 0, n) == 0
+    assert L.csa2_encode_fp4e4_rows(n, 0, 512, n, n, n) == 0
+    assert L.csa2_append(0, *([n] * 12), 16, n, n, n, n, 8, 2, 0, n, n, 128, n) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     import compressed_sparse_attention_csa2_amd as csa2

@@ -425,3 +425,77 @@ def test_topk_sampled_threshold_fallback(dev, orc, N):
     swaps = check_selection(_down(idx)[0, 0], _down(cnt)[0, 0], r_idx, r_cnt, S)
     assert np.all(hot[r_idx[:r_cnt]])
     log(f"  swaps={swaps}")
+
+
+# ---------------------------------------------------------------- degenerate calls
+def test_degenerate_calls(dev, synth):
+    """empty calls write nothing; requests with no compressed entries attend over the window
+    alone (cnt 0); a single new token at ratio 2 writes no entry, at ratio 1 one entry"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import oracle
+    from oracle.reference import DecodeReference
+    B, N, H = 2, 64, 16
+    wl = synth.decode_workload(B=B, Tq=3, n_entries=N, H=H)
+    log(f"degenerate calls: {wl.name}")
+    refs = [DecodeReference(wl, b) for b in range(B)]
+    cos_t, sin_t = synth.rope_table(wl.rope_rows)
+    g = {k: _up(np.stack([getattr(r, k) for r in refs])) for k in
+         ("ki_codes", "ki_scales", "w_codes", "w_scale")}
+    for r in refs:
+        r._ensure_z(np.arange(N))
+    zc, zs = _up(np.stack([r.z_codes for r in refs])), _up(np.stack([r.z_scales for r in refs]))
+    q0 = _up(np.full(B, wl.q_pos0, np.int32))
+    # Tq = 0: nothing is launched, outputs untouched
+    idx0 = torch.full((B, 0, 512), -7, dtype=torch.int32, device=dev)
+    ws = csa2.workspace(csa2.OP_INDEX_TOPK, B, 1, H, N)
+    csa2.csa2_index_topk(q0, _up(np.full(B, N, np.int32)), _up(wl.qI()[:, :0]),
+                         _up(wl.wI()[:, :0]), g["ki_codes"], g["ki_scales"], idx0,
+                         torch.zeros(B, 0, dtype=torch.int32, device=dev), ws)
+    # n_entries = 0 for request 0, 5 for request 1: counts 0 and 5
+    ne = np.array([0, 5], np.int32)
+    idx = torch.full((B, 3, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, 3), -7, dtype=torch.int32, device=dev)
+    csa2.csa2_index_topk(q0, _up(ne), _up(wl.qI()), _up(wl.wI()), g["ki_codes"], g["ki_scales"],
+                         idx, cnt, csa2.workspace(csa2.OP_INDEX_TOPK, B, 3, H, N))
+    torch.cuda.synchronize()
+    c, ix = _down(cnt), _down(idx)
+    assert np.all(c[0] == 0) and np.all(ix[0] == -1)
+    assert np.all(c[1] == 5) and np.all(ix[1][:, :5] == np.arange(5)) and np.all(ix[1][:, 5:] == -1)
+    for zf in (0, 1):
+        if zf == 1:
+            zs1 = [oracle.fp4e4_encode_rows_bf16(synth.normal(wl.seed, 14, (N, 512)))
+                   for _ in range(B)]
+            zc_, zs_ = _up(np.stack([a for a, _ in zs1])), _up(np.stack([b_ for _, b_ in zs1]))
+            zc_h, zs_h = [a for a, _ in zs1], [b_ for _, b_ in zs1]
+        else:
+            zc_, zs_ = zc, zs
+            zc_h, zs_h = [r.z_codes for r in refs], [r.z_scales for r in refs]
+        O = torch.zeros(B, H, 3, 512, dtype=torch.bfloat16, device=dev)
+        lse = torch.zeros(B, H, 3, dtype=torch.float32, device=dev)
+        csa2.csa2_sparse_attn(q0, _up(wl.Q()), g["w_codes"], g["w_scale"], zc_, zs_, idx, cnt,
+                              _up(refs[0].sink), _up(cos_t), _up(sin_t), O, lse,
+                              csa2.workspace(csa2.OP_SPARSE_ATTN, B, 3, H, N), z_format=zf)
+        torch.cuda.synchronize()
+        got = _down(O)
+        for b in range(B):
+            r = refs[b]
+            exp = np.stack([oracle.attend(wl.Q()[b][:, i, :], wl.q_pos0 + i, r.w_codes, r.w_scale,
+                                          wl.cap, zc_h[b], zs_h[b], ix[b, i], int(c[b, i]), r.sink,
+                                          r.cos, r.sin, z_format=zf)[0] for i in range(3)])
+            check_attention(got[b].transpose(1, 0, 2), exp, f"degenerate b={b} zf={zf}")
+    # one new token: ratio 2 writes no entry (the pair is open), ratio 1 writes entry pos0
+    for ratio in (2, 1):
+        one = synth.workload(0, T=1, H=16, ratio=ratio)
+        zc1 = torch.zeros(1, 4, 256, dtype=torch.uint8, device=dev)
+        zs1 = torch.zeros(1, 4, 16, dtype=torch.uint8, device=dev)
+        kc1 = torch.zeros(1, 4, 64, dtype=torch.uint8, device=dev)
+        ks1 = torch.zeros(1, 4, 4, dtype=torch.uint8, device=dev)
+        ct, st = synth.rope_table(4)
+        csa2.csa2_compress(_up(np.array([2], np.int32)), _up(one.kc()),
+                           _up(one.gc()) if ratio == 2 else None, _up(one.gamma_c()),
+                           _up(one.w_ik()), _up(one.gamma_ik()), None, _up(ct), _up(st), zc1, zs1,
+                           kc1, ks1, ratio=ratio)
+        torch.cuda.synchronize()
+        written = np.flatnonzero(_down(zs1)[0].any(axis=1))
+        assert list(written) == ([] if ratio == 2 else [2]), (ratio, written)
