@@ -33,15 +33,15 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.378e10, {
-        "attention.hip": "b54d9a72e389bf5e547df631f6fed7ce0e957000c407e646b28f219699239cc0",
-        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
-    ("k_index_scores", "prefill", 65536): (7.070e9, {
-        "indexer.hip": "ac89264b8e797f5177620911e6dca238fb43deb22fe51ed84e3d4e8b72ad13f6",
-        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
+    ("k_attn", "prefill", 65536): (1.383e10, {
+        "attention.hip": "9ac6af5fc9a1a9dd9793887800afa9925622b9ba6c095b718491b7a70d31ba2e",
+        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
+    ("k_index_scores", "prefill", 65536): (7.063e9, {
+        "indexer.hip": "678d3f572b8fc6d6fef487817d9564ba372ca08f42ecdd13fe13770966f82495",
+        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
     ("k_index_scores", "decode", 131072): (6.088e8, {
-        "indexer.hip": "ac89264b8e797f5177620911e6dca238fb43deb22fe51ed84e3d4e8b72ad13f6",
-        "csa2_device.h": "3c73d1f55143cd1e4f77f3a7645bf7bd12679c2ffcf92039d5b55f07c859c2fa"}),
+        "indexer.hip": "678d3f572b8fc6d6fef487817d9564ba372ca08f42ecdd13fe13770966f82495",
+        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
 }
 
 
