@@ -157,7 +157,7 @@ def main():
                          "decode1 / pool1 are the ratio-1 forms, decode1z the ratio-1 form with "
                          "the pages' 288-byte rows")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=256)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs the layer on one GPU; multi-GPU sharding is "

@@ -126,3 +126,55 @@ def test_pool_and_reindex_match_oracle(ratio):
             full[cand] = Sc
             rswaps += check_selection(gi2[b, i], gc2[b, i], o_idx, o_cnt, full)
     log(f"  rows={B * Tq} topk swaps={swaps} pool swaps={pswaps} reindex swaps={rswaps}")
+
+
+def test_pool_many_blocks_skewed_keys():
+    """12,500 blocks per row (six times the pool): request 0 with log-normal key norms;
+    request 1 with 1,024 blocks on a regular lattice holding keys far above all others
+    (a pool of those plus the best of the rest).  Both against the oracle."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_csa2_amd as csa2
+    import oracle
+    from csa2_harness import up, down
+
+    rng = np.random.default_rng(43)
+    B, Tq, N = 2, 1, 100_000
+    nb = (N + 7) // 8
+    m = nb - 1
+    sampled = np.unique(((np.arange(1024, dtype=np.int64)) * m) >> 10)
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.zeros((B, N, 4), np.uint8)
+    x0 = rng.standard_normal((N, 128)) * np.exp(rng.standard_normal((N, 1)))
+    kc[0], ks[0] = oracle.fp4_encode(x0.astype(np.float32))
+    x1 = rng.standard_normal((N, 128))
+    big = np.zeros(N, bool)
+    for k in sampled:
+        big[8 * k:8 * k + 8] = True
+    x1[big] *= 16.0
+    kc[1], ks[1] = oracle.fp4_encode(x1.astype(np.float32))
+    qI = _bf16(rng.standard_normal((B, Tq, 32, 128)))
+    wI = (np.abs(rng.standard_normal((B, Tq, 32))) / 64).astype(np.float32)   # S grows with |k|
+    q_pos0 = np.full(B, N - 1, np.int32)                # ratio 1: every entry visible
+    log(f"pool over many blocks: B={B} N={N} blocks={nb}")
+    idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Tq), -7, dtype=torch.int32, device="cuda")
+    pool = torch.full((B, Tq, 2048), -7, dtype=torch.int32, device="cuda")
+    pcnt = torch.full((B, Tq), -7, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(csa2.OP_INDEX_POOL, B, Tq, 64, N)
+    csa2.csa2_index_pool(up(q_pos0), up(np.full(B, N, np.int32)), up(qI), up(wI), up(kc), up(ks),
+                         idx, cnt, pool, pcnt, ws, ratio=1)
+    torch.cuda.synchronize()
+    gp, gpc, gi, gc_ = down(pool), down(pcnt), down(idx), down(cnt)
+    for b in range(B):
+        q8, sq = oracle.quant_index_query(qI[b, 0])
+        S = oracle.index_scores(q8, sq, wI[b, 0], kc[b], ks[b], N)
+        p = oracle.pool_blocks(S, N)
+        if b == 1:     # the construction: the lattice blocks hold the largest keys
+            keys = np.array([S[8 * k:8 * k + 8].max() for k in range(m)])
+            assert np.all(np.sort(keys)[::-1][:len(sampled)] >= keys[~np.isin(np.arange(m), sampled)].max())
+        swaps = check_pool(gp[b, 0], gpc[b, 0], p, S, N)
+        r_idx, r_cnt = oracle.topk(S, N)
+        swaps += check_selection(gi[b, 0], gc_[b, 0], r_idx, r_cnt, S)
+        log(f"  request {b}: pool {len(p)} blocks, swaps {swaps}")
