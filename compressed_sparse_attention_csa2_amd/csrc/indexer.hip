@@ -841,14 +841,19 @@ __global__ void __launch_bounds__(256) k_pool_select(
     const uint4* kr4 = (const uint4*)(keys + row * kpad);
     const int ntile = (m + 1023) / 1024;
     const uint32_t r = POOL_BLOCKS - 1;            // how many of them are kept
+    // the row's keys through a buffer resource bounded to the m keys: loads past
+    // them return zeros, so the passes have no branch around their loads and
+    // keep many in flight
+    const __amdgpu_buffer_rsrc_t krb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(keys + row * kpad), (short)0, 4 * m, 0x00020000);
     auto load4 = [&](int c, uint32_t (&k)[4]) {   // keys 1024c + 4 tid .. +3; 0 past m
         const int i = 1024 * c + 4 * tid;
-        const uint4 v = i < m ? kr4[(i >> 2)] : make_uint4(0u, 0u, 0u, 0u);
-        k[0] = v.x; k[1] = i + 1 < m ? v.y : 0u; k[2] = i + 2 < m ? v.z : 0u; k[3] = i + 3 < m ? v.w : 0u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(krb, 4 * i, 0, 0);
+        k[0] = v[0]; k[1] = i + 1 < m ? v[1] : 0u; k[2] = i + 2 < m ? v[2] : 0u; k[3] = i + 3 < m ? v[3] : 0u;
     };
     // keys are >= 1 for every real block, so 0 marks "none"
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll 8
+#pragma unroll 16
     for (int c = 0; c < ntile; ++c) {
         uint32_t k[4];
         load4(c, k);
@@ -875,13 +880,18 @@ __global__ void __launch_bounds__(256) k_pool_select(
             const uint32_t dmask = (2u << (hib - lob)) - 1u;
             hist[tid] = 0u;
             __syncthreads();
-#pragma unroll 8
-            for (int c = 0; c < ntile; ++c) {
-                uint32_t k[4];
-                load4(c, k);
+            // sixteen tiles' loads issued together, then their atomics (tiles
+            // past the keys read zeros, which are never counted)
+            for (int c0 = 0; c0 < ntile; c0 += 16) {
+                uint32_t kk[16][4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (k[q] != 0u && (k[q] & pmask) == prefix) atomicAdd(&hist[(k[q] >> lob) & dmask], 1u);
+                for (int u = 0; u < 16; ++u) load4(c0 + u, kk[u]);
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (kk[u][q] != 0u && (kk[u][q] & pmask) == prefix)
+                            atomicAdd(&hist[(kk[u][q] >> lob) & dmask], 1u);
             }
             __syncthreads();
             // digit holding the krem-th largest: bins in descending order, one per thread
@@ -904,40 +914,76 @@ __global__ void __launch_bounds__(256) k_pool_select(
         }
         K = prefix;
     }
-    // kept: every key > K and the first krem keys == K in block order
+    // kept: every key > K and the first krem keys == K in block order.  Each
+    // wave owns a contiguous run of the keys: a first pass counts its keys
+    // above and equal to K, the four counts give each wave its output offset and
+    // the equal keys before it, and a second pass writes its kept blocks in
+    // order with in-wave ballot ranks (no block barrier per tile).
     const bool all_eq = krem >= eq_total;
-    uint32_t written = 0u, eq_seen = 0u;
-    uint32_t kn[4];
-    load4(0, kn);
-    for (int c = 0; c < ntile; ++c) {
-        uint32_t k[4] = {kn[0], kn[1], kn[2], kn[3]};
-        if (c + 1 < ntile) load4(c + 1, kn);       // next tile in flight during the scans
-        uint32_t gt = 0u, eq = 0u;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int per = (m + 1023) / 1024 * 256;      // keys per wave, a multiple of 256
+    const int wbeg = wave * per, wend = min(m, wbeg + per);
+    auto ldw = [&](int i, uint32_t (&k)[4]) {      // keys i..i+3 of this wave's run, 0 past it
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(krb, 4 * i, 0, 0);
+        k[0] = i < wend ? v[0] : 0u; k[1] = i + 1 < wend ? v[1] : 0u;
+        k[2] = i + 2 < wend ? v[2] : 0u; k[3] = i + 3 < wend ? v[3] : 0u;
+    };
+    uint32_t cg = 0u, ce = 0u;
+#pragma unroll 16
+    for (int i = wbeg + 4 * lane; i < wend; i += 256) {
+        uint32_t k[4];
+        ldw(i, k);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            gt += k[q] > K;
-            eq += k[q] == K;
+            cg += k[q] > K;
+            ce += k[q] == K;
         }
-        uint32_t take = eq;
-        if (!all_eq) {
-            uint32_t eq_tot;
-            const uint32_t eq_ex = block_excl_sum(eq, wsum, &eq_tot);
-            const uint32_t rank0 = eq_seen + eq_ex;
-            take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+    }
+    cg = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(cg), 63);
+    ce = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(ce), 63);
+    if (lane == 0) { hist[2 * wave] = cg; hist[2 * wave + 1] = ce; }
+    __syncthreads();
+    uint32_t off = 0u, eq_seen = 0u;               // output offset, equal keys before this wave
+    for (int w = 0; w < wave; ++w) {
+        const uint32_t e = hist[2 * w + 1];
+        off += hist[2 * w] + (all_eq ? e : (krem > eq_seen ? min(krem - eq_seen, e) : 0u));
+        eq_seen += e;
+    }
+    uint32_t kq[4][4];                             // four groups' loads in flight
+#pragma unroll
+    for (int d = 0; d < 4; ++d) ldw(wbeg + 256 * d + 4 * lane, kq[d]);
+    for (int base0 = wbeg; base0 < wend; base0 += 1024) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int base = base0 + 256 * d;
+            if (base >= wend) break;
+            uint32_t k[4] = {kq[d][0], kq[d][1], kq[d][2], kq[d][3]};
+            ldw(base + 1024 + 4 * lane, kq[d]);
+            uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gt += k[q] > K;
+                eq += k[q] == K;
+            }
+            // this lane's equal keys rank after those of the lanes before it
+            const uint32_t eq_inc = wave_scan_add(eq);
+            const uint32_t eq_tot = (uint32_t)__builtin_amdgcn_readlane((int)eq_inc, 63);
+            const uint32_t rank0 = eq_seen + eq_inc - eq;
+            const uint32_t take = all_eq ? eq : (krem > rank0 ? min(krem - rank0, eq) : 0u);
+            const uint32_t sel_inc = wave_scan_add(gt + take);
+            const uint32_t sel_tot = (uint32_t)__builtin_amdgcn_readlane((int)sel_inc, 63);
+            uint32_t o = off + sel_inc - (gt + take), taken = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool keep = k[q] > K || (k[q] == K && taken < take);
+                if (keep) {
+                    out[o++] = base + 4 * lane + q;
+                    taken += k[q] == K;
+                }
+            }
+            off += sel_tot;
             eq_seen += eq_tot;
         }
-        uint32_t sel_tot;
-        uint32_t off = written + block_excl_sum(gt + take, wsum, &sel_tot);
-        uint32_t taken = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool keep = k[q] > K || (k[q] == K && taken < take);
-            if (keep) {
-                out[off++] = 1024 * c + 4 * tid + q;
-                taken += k[q] == K;
-            }
-        }
-        written += sel_tot;
     }
     if (tid == 0) {
         out[POOL_BLOCKS - 1] = m;                  // the newest block, largest index
