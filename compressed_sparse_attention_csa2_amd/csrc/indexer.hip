@@ -621,19 +621,20 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
     len = len < 0 ? 0 : len;
     const float* src = S + row * spad + j0;       // 16-byte aligned
     WaveTopk st{sel[wave], 0, 0u};
-    // 1024 elements per step: four 256-element groups, the next step's loads in flight
+    // 1024 elements per step: four 256-element groups, the next step's loads in
+    // flight.  The list comes through a buffer resource bounded to its len scores
+    // rounded up to a whole 16-byte group (inside the row's padded storage), so a
+    // group is either wholly in range or reads zeros, and no load sits behind a
+    // branch; the keys past len are masked below.
+    const __amdgpu_buffer_rsrc_t srb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)src, (short)0, 4 * ((len + 3) & ~3), 0x00020000);
     auto fetch = [&](int base, float4 (&v)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i0 = base + 256 * u + 4 * lane;
-            if (i0 + 3 < len) {
-                v[u] = *(const float4*)(src + i0);
-            } else {
-                v[u].x = i0 < len ? src[i0] : 0.f;
-                v[u].y = i0 + 1 < len ? src[i0 + 1] : 0.f;
-                v[u].z = i0 + 2 < len ? src[i0 + 2] : 0.f;
-                v[u].w = i0 + 3 < len ? src[i0 + 3] : 0.f;
-            }
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * i0, 0, 0);
+            v[u] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                               __uint_as_float(w[3]));
         }
     };
     // Long lists start from a threshold taken on a sample (16 runs of 64 elements
@@ -841,11 +842,12 @@ __global__ void __launch_bounds__(256) k_pool_select(
     const uint4* kr4 = (const uint4*)(keys + row * kpad);
     const int ntile = (m + 1023) / 1024;
     const uint32_t r = POOL_BLOCKS - 1;            // how many of them are kept
-    // the row's keys through a buffer resource bounded to the m keys: loads past
-    // them return zeros, so the passes have no branch around their loads and
-    // keep many in flight
+    // the row's keys through a buffer resource bounded to the m keys rounded up
+    // to a whole 16-byte group (rows are padded to that): a group is either in
+    // range or reads zeros, so the passes have no branch around their loads and
+    // keep many in flight (keys past m are masked)
     const __amdgpu_buffer_rsrc_t krb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(keys + row * kpad), (short)0, 4 * m, 0x00020000);
+        (void*)(keys + row * kpad), (short)0, 4 * ((m + 3) & ~3), 0x00020000);
     auto load4 = [&](int c, uint32_t (&k)[4]) {   // keys 1024c + 4 tid .. +3; 0 past m
         const int i = 1024 * c + 4 * tid;
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(krb, 4 * i, 0, 0);
