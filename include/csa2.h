@@ -153,8 +153,9 @@ csa2_status csa2_encode_window(int B, int T, const int32_t* pos0, const uint16_t
  *  pair_kc, pair_gc [B][512] bf16 device, caller-owned state carried between
  *             calls.  After a prefill of odd length the caller seeds them
  *             with the last token's kc and gc (or appends that token here).
- *  ki_given   [B][128] bf16 given index key of the entry an odd token closes
- *             (read only for odd positions, only when w_ik == NULL).
+ *  ki_given   [B][128] bf16 given index key of the entry the token writes: at
+ *             ratio 2 the entry an odd token closes (read only for odd
+ *             positions), at ratio 1 the token's own; only when w_ik == NULL.
  *  Other arguments as for csa2_compress and csa2_encode_window.  Requests
  *  are independent; two calls on one stream are ordered, so the pair buffer
  *  written by one call is read by the next.
