@@ -160,8 +160,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=256)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs the layer on one GPU; multi-GPU sharding is "
-                                   "described in DESIGN.md but not implemented", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the layer runs on one GPU; sharding it across GPUs is not "
+                                   "implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
