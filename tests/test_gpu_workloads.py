@@ -31,7 +31,8 @@ def _attn_expected(wl, ref, b, rows_local, positions, g_idx, g_cnt, r, Qrows):
                                     ref.w_scale if ref.w_scale.ndim == 1 else ref.w_scale[0], wl.cap,
                                     ref.z_codes if ref.z_codes.ndim == 2 else ref.z_codes[0],
                                     ref.z_scales if ref.z_scales.ndim == 2 else ref.z_scales[0],
-                                    g_idx[i], int(g_cnt[i]), ref.sink, ref.cos, ref.sin)
+                                    g_idx[i], int(g_cnt[i]), ref.sink, ref.cos, ref.sin,
+                                    z_format=wl.z_format)
             exp[i] = O
     return exp
 
@@ -69,12 +70,21 @@ def test_prefill_workload(dev, synth, cid, nrows):
     log(f"  rows={len(rows)} swaps={swaps} max|dO|={mx:.2e} rel={rel:.2e}")
 
 
-@pytest.mark.parametrize("cid,reqs,qrows", [(3, (0, 77, 127), (0,)), (4, (5,), (0, 5))])
-def test_decode_workload(dev, synth, cid, reqs, qrows):
+@pytest.mark.parametrize("cid,reqs,qrows,form", [(3, (0, 77, 127), (0,), None),
+                                                (4, (5,), (0, 5), None),
+                                                (3, (0, 77, 127), (0,), "ratio1_z16")])
+def test_decode_workload(dev, synth, cid, reqs, qrows, form):
+    """the measured decode shapes at full size; ratio1_z16: the B=128 decode in the
+    decoder layers' form as the benchmark runs it (131,072 entries per request at
+    compression ratio 1, rows in the pages' 288-byte format)"""
+    import dataclasses
     import torch
     import csa2_harness
     from oracle.reference import DecodeReference
     wl = synth.workload(cid)
+    if form == "ratio1_z16":
+        wl = dataclasses.replace(wl, n_entries=wl.q_pos0 + wl.Tq, ratio=1, z_format=1,
+                                 name=wl.name + " ratio 1 Z per-16 E4M3")
     log(f"workload {cid}: {wl.name}")
     run = csa2_harness.DecodeRun(wl)
     run.forward()
