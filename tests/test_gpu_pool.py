@@ -178,3 +178,67 @@ def test_pool_many_blocks_skewed_keys():
         r_idx, r_cnt = oracle.topk(S, N)
         swaps += check_selection(gi[b, 0], gc_[b, 0], r_idx, r_cnt, S)
         log(f"  request {b}: pool {len(p)} blocks, swaps {swaps}")
+
+
+@pytest.mark.parametrize("ratio", [2, 1])
+def test_pool_verify_decode_full_size(ratio):
+    """the verify-decode shape as the benchmark runs it (B=16 x 6 queries at 1,048,570..,
+    log-normal keys with 1% exact duplicates; 524,288 entries at ratio 2, 1,048,576 at
+    ratio 1): request 5, query rows 0 and 5 -- Full selection, pool and a Reindex
+    layer's selection against the oracle"""
+    import dataclasses
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_csa2_amd as csa2
+    import csa2_synth as synth
+    import oracle
+    from csa2_harness import up, down
+    from oracle.reference import DecodeReference
+    wl = synth.workload(4)
+    if ratio == 1:
+        wl = dataclasses.replace(wl, n_entries=wl.q_pos0 + wl.Tq, ratio=1)
+    B, Tq, N = wl.B, wl.Tq, wl.n_entries
+    log(f"pool at the verify-decode shape: ratio {ratio}, {N} entries")
+    kc = torch.zeros(B, N, 64, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(B, N, 4, dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        for j0 in range(0, N, 1 << 16):
+            n = min(1 << 16, N - j0)
+            csa2.csa2_encode_fp4_rows(up(wl.ki_rows(b, j0, n)), kc[b, j0:j0 + n].view(n, 64),
+                                      ks[b, j0:j0 + n].view(n, 4))
+    qI2 = synth.normal(wl.seed, 901, (B, Tq, 32, 128))
+    wI2 = synth.normal(wl.seed, 902, (B, Tq, 32), mul=1.0 / 64.0, dtype="f32")
+    q0 = torch.full((B,), wl.q_pos0, dtype=torch.int32, device="cuda")
+    ne = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Tq), -7, dtype=torch.int32, device="cuda")
+    pool = torch.full((B, Tq, 2048), -7, dtype=torch.int32, device="cuda")
+    pcnt = torch.full((B, Tq), -7, dtype=torch.int32, device="cuda")
+    idx2, cnt2 = torch.full_like(idx, -7), torch.full_like(cnt, -7)
+    csa2.csa2_index_pool(q0, ne, up(wl.qI()), up(wl.wI()), kc, ks, idx, cnt, pool, pcnt,
+                         csa2.workspace(csa2.OP_INDEX_POOL, B, Tq, 64, N), ratio=ratio)
+    csa2.csa2_reindex_topk(q0, ne, up(qI2), up(wI2), kc, ks, pool, pcnt, idx2, cnt2,
+                           csa2.workspace(csa2.OP_REINDEX, B, Tq, 64, N), ratio=ratio)
+    torch.cuda.synchronize()
+    gi, gc_, gp, gpc, gi2, gc2 = (down(x) for x in (idx, cnt, pool, pcnt, idx2, cnt2))
+    del kc, ks
+    torch.cuda.empty_cache()
+    b = 5
+    ref = DecodeReference(wl, b)
+    for i in (0, 5):
+        n = min((wl.q_pos0 + i + 1) // ratio, N)
+        q8, sq = oracle.quant_index_query(wl.qI()[b, i])
+        S = oracle.index_scores(q8, sq, wl.wI()[b, i], ref.ki_codes, ref.ki_scales, n)
+        r_idx, r_cnt = oracle.topk(S, n)
+        swaps = check_selection(gi[b, i], gc_[b, i], r_idx, r_cnt, S)
+        p = oracle.pool_blocks(S, n)
+        pswaps = check_pool(gp[b, i], gpc[b, i], p, S, n)
+        q8b, sqb = oracle.quant_index_query(qI2[b, i])
+        o_idx, o_cnt, cand, Sc = oracle.reindex_topk(q8b, sqb, wI2[b, i], ref.ki_codes,
+                                                     ref.ki_scales, n, gp[b, i][:int(gpc[b, i])])
+        full = np.full(n, np.nan)
+        full[cand] = Sc
+        rswaps = check_selection(gi2[b, i], gc2[b, i], o_idx, o_cnt, full)
+        log(f"  request {b} row {i}: n={n} topk swaps={swaps} pool swaps={pswaps} "
+            f"reindex swaps={rswaps}")
