@@ -51,6 +51,8 @@ __global__ void k_pool_scores(int, int, const int32_t*, const int32_t*, const ui
 __global__ void k_pool_map(int64_t, const int32_t*, int32_t*);
 __global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const int32_t*,
                              const uint32_t*, int32_t*, int32_t*);
+__global__ void k_topk_row(int, int, const int32_t*, const int32_t*, const float*, int64_t,
+                           int64_t, int32_t*, int32_t*, int);
 template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
@@ -251,6 +253,12 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     launch_scores(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride, Sc, pitch, rsh, ws,
                   st);
     const int64_t rows = (int64_t)B * Tq;
+    if (rows <= 1024 && stride >= 16384 && stride <= 131072) {
+        // few rows of moderate length: one block per row, no segments to merge
+        hipLaunchKernelGGL(k_topk_row, dim3((unsigned)rows), dim3(512), 0, st, B, Tq, q_pos0,
+                           n_entries, Sc, pitch, stride, idx, cnt, rsh);
+        return check_launch("csa2_index_topk");
+    }
     const int nseg = topk_segments(rows, stride);
     const int seg_len = topk_seg_len(stride, nseg);
     uint32_t* seg_key = (uint32_t*)((uint8_t*)ws + L.seg_key);

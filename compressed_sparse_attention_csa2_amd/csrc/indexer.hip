@@ -758,6 +758,229 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
     if (lane == 0) cnt[row] = c;
 }
 
+// Exclusive prefix sum over a block of NW waves (DPP scans in the waves, the
+// wave totals through LDS); *tot = the block total.
+template <int NW>
+__device__ __forceinline__ uint32_t block_scan_nw(uint32_t v, uint32_t* wsum, uint32_t* tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_scan_add(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t x = wsum[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    __syncthreads();
+    *tot = all;
+    return before + inc - v;
+}
+
+// The selection for few query rows of moderate length (one block of eight waves
+// per row instead of segments and a merge): a threshold from 1,024 sampled
+// scores (about 2,048 of the row's scores above it) filters the row, each wave
+// compacting its contiguous eighth in order into LDS; an exact radix select
+// over those candidates finds the 512th largest key K and how many copies of it
+// are kept (the first, as in every selection here), and a block scan writes the
+// kept entries in ascending order.  When the sample misjudges (fewer than 512
+// candidates, or more than the buffer holds) wave 0 selects the row exactly
+// with the one-segment streaming selection.
+constexpr int TR_WAVES = 8, TR_WCAP = 512;
+__global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const float* __restrict__ S, int64_t spad, int64_t entry_stride, int32_t* __restrict__ idx,
+    int32_t* __restrict__ cnt, int rsh) {
+    constexpr int NSLOT = TR_WAVES * TR_WCAP;
+    __shared__ uint32_t ck[NSLOT];
+    __shared__ int32_t cj[NSLOT];
+    __shared__ WaveSel wsel;
+    __shared__ uint32_t wcnt[TR_WAVES];
+    __shared__ uint32_t wsum[TR_WAVES];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t bc[4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t row = blockIdx.x;
+    if (row >= (int64_t)B * Tq) return;
+    const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
+    const int n = (int)cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
+    int32_t* out = idx + row * TOPK;
+    if (n <= TOPK) {
+        for (int i = tid; i < TOPK; i += 64 * TR_WAVES) out[i] = i < n ? i : -1;
+        if (tid == 0) cnt[row] = n;
+        return;
+    }
+    const float* src = S + row * spad;              // spad: a multiple of 64 floats
+    const __amdgpu_buffer_rsrc_t srb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)src, (short)0, 4 * ((n + 3) & ~3), 0x00020000);
+    if (n <= NSLOT) {                               // every score fits: no sample
+        if (tid == 0) bc[0] = 1u;
+    } else if (wave == 0) {
+        uint32_t kr[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) kr[g] = score_key(src[((int64_t)(64 * g + lane) * n) >> 10]);
+        const uint32_t ks = (uint32_t)((2048ll * 1024 + n - 1) / n);   // < 512
+        uint32_t krem;
+        const uint32_t th = wave_threshold(wsel, kr, ks, ks + ks / 2, false, &krem);
+        if (lane == 0) bc[0] = th;
+    }
+    __syncthreads();
+    const uint32_t th = bc[0];
+    // filter: wave w compacts the keys >= th of its run, in order
+    const int per = (n + TR_WAVES * 256 - 1) / (TR_WAVES * 256) * 256;
+    const int r0 = wave * per, r1 = min(n, r0 + per);
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t nc = 0u;
+    bool over = false;
+    for (int base = r0; base < r1; base += 1024) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * (base + 256 * u + 4 * lane), 0, 0);
+            v[u] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                               __uint_as_float(w[3]));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i0 = base + 256 * u + 4 * lane;
+            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t k[4];
+            uint64_t m[4];
+            uint32_t c = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                k[q] = i0 + q < r1 ? score_key(f[q]) : 0u;
+                m[q] = __ballot(k[q] >= th && k[q] != 0u);
+                c += (uint32_t)__popcll(m[q]);
+            }
+            if (nc + c > (uint32_t)TR_WCAP) {
+                over = true;
+            } else {
+                uint32_t pos = (uint32_t)(wave * TR_WCAP) + nc;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pos += (uint32_t)__popcll(m[q] & below);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (k[q] >= th && k[q] != 0u) {
+                        ck[pos] = k[q];
+                        cj[pos] = i0 + q;
+                        ++pos;
+                    }
+                }
+                nc += c;
+            }
+        }
+        if (over) break;
+    }
+    if (lane == 0) wcnt[wave] = over ? 0xFFFFFFFFu : nc;
+    __syncthreads();
+    uint32_t total = 0u;
+    bool fallback = false;
+#pragma unroll
+    for (int w = 0; w < TR_WAVES; ++w) {
+        fallback |= wcnt[w] == 0xFFFFFFFFu;
+        total += wcnt[w] == 0xFFFFFFFFu ? 0u : wcnt[w];
+    }
+    if (fallback || total < (uint32_t)TOPK) {
+        if (wave == 0) {
+            WaveTopk st{wsel, 0, 0u};
+            for (int base = 0; base < n; base += 256) {
+                const int i0 = base + 4 * lane;
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * i0, 0, 0);
+                const uint32_t k[4] = {i0 < n ? score_key(__uint_as_float(w[0])) : 0u,
+                                       i0 + 1 < n ? score_key(__uint_as_float(w[1])) : 0u,
+                                       i0 + 2 < n ? score_key(__uint_as_float(w[2])) : 0u,
+                                       i0 + 3 < n ? score_key(__uint_as_float(w[3])) : 0u};
+                const int32_t jj[4] = {i0, i0 + 1, i0 + 2, i0 + 3};
+                st.push(k, jj);
+            }
+            const int c = st.finish(out, nullptr, nullptr);
+            if (lane == 0) cnt[row] = c;
+        }
+        return;
+    }
+    // slots in order: wave region w, positions below wcnt[w] (ascending entries)
+    auto slot_key = [&](int s) -> uint32_t {
+        return (uint32_t)(s % TR_WCAP) < wcnt[s / TR_WCAP] ? ck[s] : 0u;
+    };
+    constexpr int SPT = NSLOT / (64 * TR_WAVES);    // slots per thread: 8, consecutive
+    uint32_t kv[SPT];
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) kv[e] = slot_key(SPT * tid + e);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        if (kv[e] != 0u) lo = min(lo, kv[e]);
+        hi = max(hi, kv[e]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) { hist[wave] = lo; hist[TR_WAVES + wave] = hi; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TR_WAVES; ++w) { lo = min(lo, hist[w]); hi = max(hi, hist[TR_WAVES + w]); }
+    __syncthreads();
+    uint32_t K = hi, krem = TOPK, eq_total = total;  // all candidates equal
+    if (lo < hi) {
+        int hib = 31 - __clz((int)(lo ^ hi));
+        uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
+        uint32_t prefix = lo & pmask;
+        while (hib >= 0) {
+            const int lob = hib - 7 > 0 ? hib - 7 : 0;
+            const uint32_t dmask = (2u << (hib - lob)) - 1u;
+            if (tid < 256) hist[tid] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < SPT; ++e)
+                if (kv[e] != 0u && (kv[e] & pmask) == prefix) atomicAdd(&hist[(kv[e] >> lob) & dmask], 1u);
+            __syncthreads();
+            const int nbins = (int)dmask + 1;
+            const uint32_t h = tid < nbins ? hist[nbins - 1 - tid] : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_scan_nw<TR_WAVES>(h, wsum, &tot);
+            if (tid < nbins && ex < krem && krem <= ex + h) {
+                bc[1] = (uint32_t)(nbins - 1 - tid);
+                bc[2] = ex;
+                bc[3] = h;
+            }
+            __syncthreads();
+            prefix |= bc[1] << lob;
+            pmask |= dmask << lob;
+            krem -= bc[2];
+            eq_total = bc[3];
+            hib = lob - 1;
+            __syncthreads();
+        }
+        K = prefix;
+    }
+    // ordered write: keys > K and the first krem keys == K
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        gt += kv[e] > K;
+        eq += kv[e] == K;
+    }
+    uint32_t take = eq;
+    if (krem < eq_total) {
+        uint32_t eq_tot;
+        const uint32_t rank0 = block_scan_nw<TR_WAVES>(eq, wsum, &eq_tot);
+        take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+    }
+    uint32_t sel_tot;
+    uint32_t off = block_scan_nw<TR_WAVES>(gt + take, wsum, &sel_tot);
+    uint32_t taken = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        const bool keep = kv[e] > K || (kv[e] == K && taken < take);
+        if (keep) {
+            out[off++] = cj[SPT * tid + e];
+            taken += kv[e] == K;
+        }
+    }
+    if (tid == 0) cnt[row] = TOPK;
+}
+
 // ---------------------------------------------------------------------------
 // Hierarchical candidate pool and Reindex selection.  "Inside DeepSeek V4.1"
 // (the Hierarchical Sparse Indexer paragraph) and "Inside DeepSeek V4.1 Flash:

@@ -499,3 +499,41 @@ def test_degenerate_calls(dev, synth):
         torch.cuda.synchronize()
         written = np.flatnonzero(_down(zs1)[0].any(axis=1))
         assert list(written) == ([] if ratio == 2 else [2]), (ratio, written)
+
+
+def test_topk_row_paths(dev, orc):
+    """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
+    three paths: a sampled threshold (20,000 candidates), every score kept without a
+    sample (3,000), and the exact fallback when the sample cannot separate the scores
+    (all 20,000 keys identical: the first 512 entries)"""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    rng = np.random.default_rng(71)
+    B, Tq, N = 3, 2, 20_000
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.zeros((B, N, 4), np.uint8)
+    for b in range(2):
+        kc[b], ks[b] = orc.fp4_encode(rng.standard_normal((N, 128)).astype(np.float32))
+    one_c, one_s = orc.fp4_encode(rng.standard_normal((1, 128)).astype(np.float32))
+    kc[2], ks[2] = one_c[0], one_s[0]
+    import tests.test_oracle_compress as tc
+    qI = tc.bf16(rng.standard_normal((B, Tq, 32, 128)).astype(np.float32))
+    wI = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
+    ne = np.array([N, 3000, N], np.int32)
+    q0 = np.full(B, 2 * N, np.int32)
+    log(f"k_topk_row paths: B={B} Tq={Tq} stride={N}")
+    idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, Tq), -7, dtype=torch.int32, device=dev)
+    csa2.csa2_index_topk(_up(q0), _up(ne), _up(qI), _up(wI), _up(kc), _up(ks), idx, cnt,
+                         csa2.workspace(csa2.OP_INDEX_TOPK, B, Tq, 64, N))
+    torch.cuda.synchronize()
+    gi, gc_ = _down(idx), _down(cnt)
+    for b in range(B):
+        for i in range(Tq):
+            n = int(ne[b])
+            q8, sq = orc.quant_index_query(qI[b, i])
+            S = orc.index_scores(q8, sq, wI[b, i], kc[b], ks[b], n)
+            r_idx, r_cnt = orc.topk(S, n)
+            check_selection(gi[b, i], gc_[b, i], r_idx, r_cnt, S)
+            if b == 2:
+                assert np.array_equal(gi[b, i], np.arange(512)), "ties: the first 512 entries"
