@@ -52,7 +52,7 @@ __global__ void k_pool_map(int64_t, const int32_t*, int32_t*);
 __global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const int32_t*,
                              const uint32_t*, int32_t*, int32_t*);
 __global__ void k_topk_row(int, int, const int32_t*, const int32_t*, const float*, int64_t,
-                           int64_t, int32_t*, int32_t*, int);
+                           int64_t, int32_t*, int32_t*, int, const int32_t*);
 template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
@@ -256,7 +256,7 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
     if (rows <= 1024 && stride >= 16384 && stride <= 131072) {
         // few rows of moderate length: one block per row, no segments to merge
         hipLaunchKernelGGL(k_topk_row, dim3((unsigned)rows), dim3(512), 0, st, B, Tq, q_pos0,
-                           n_entries, Sc, pitch, stride, idx, cnt, rsh);
+                           n_entries, Sc, pitch, stride, idx, cnt, rsh, (const int32_t*)nullptr);
         return check_launch("csa2_index_topk");
     }
     const int nseg = topk_segments(rows, stride);
@@ -519,6 +519,16 @@ csa2_status csa2_reindex_topk(int B, int Tq, const int32_t* q_pos0, const int32_
     hipLaunchKernelGGL(k_pool_scores, dim3((unsigned)cdiv(rows * (POOL_BLOCKS / 128), 4)),
                        dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8, wq, ki_codes, ki_scales,
                        entry_stride, pool, pool_cnt, Sc, pitch, len, rsh);
+    if (rows <= 1024) {
+        // the pool lists (at most 16,384 scores each): one block per row
+        hipLaunchKernelGGL(k_topk_row, dim3((unsigned)rows), dim3(512), 0, st, B, Tq, q_pos0,
+                           n_entries, Sc, pitch, (int64_t)POOL_CAND, idx, cnt, rsh,
+                           (const int32_t*)len);
+        hipLaunchKernelGGL(k_pool_map, dim3((unsigned)cdiv(rows * TOPK, 256)), dim3(256), 0, st,
+                           rows, pool, idx);
+        csa2_status s = check_launch("csa2_reindex_topk");
+        return s == CSA2_OK ? ok() : s;
+    }
     const int nseg = topk_segments(rows, POOL_CAND);
     const int seg_len = topk_seg_len(POOL_CAND, nseg);
     uint32_t* seg_key = (uint32_t*)(base + L.ix.seg_key);

@@ -791,7 +791,7 @@ constexpr int TR_WAVES = 8, TR_WCAP = 512;
 __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const float* __restrict__ S, int64_t spad, int64_t entry_stride, int32_t* __restrict__ idx,
-    int32_t* __restrict__ cnt, int rsh) {
+    int32_t* __restrict__ cnt, int rsh, const int32_t* __restrict__ row_len) {
     constexpr int NSLOT = TR_WAVES * TR_WCAP;
     __shared__ uint32_t ck[NSLOT];
     __shared__ int32_t cj[NSLOT];
@@ -804,7 +804,10 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     const int64_t row = blockIdx.x;
     if (row >= (int64_t)B * Tq) return;
     const int b = (int)(row / Tq), t = (int)(row - (int64_t)b * Tq);
-    const int n = (int)cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
+    // the row's causal candidates, or (row_len given) its first row_len[row]
+    // scores, the list of a hierarchical pool
+    int n = row_len ? row_len[row] : (int)cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
+    n = n < 0 ? 0 : (n > (int)entry_stride ? (int)entry_stride : n);
     int32_t* out = idx + row * TOPK;
     if (n <= TOPK) {
         for (int i = tid; i < TOPK; i += 64 * TR_WAVES) out[i] = i < n ? i : -1;
