@@ -33,14 +33,14 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.383e10, {
+    ("k_attn", "prefill", 65536): (1.383e+10, {
         "attention.hip": "9ac6af5fc9a1a9dd9793887800afa9925622b9ba6c095b718491b7a70d31ba2e",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_scores", "prefill", 65536): (7.073e9, {
-        "indexer.hip": "48813a6b74e53896785f25a19a2397172dcd6cd974e159f84f9523c25a7c2960",
+    ("k_index_scores", "prefill", 65536): (7.074e+09, {
+        "indexer.hip": "46bcbfd90e528267e58ffdae475159a0397bd7a517c64877e32f4ad1b822fc6c",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_scores", "decode", 131072): (6.088e8, {
-        "indexer.hip": "48813a6b74e53896785f25a19a2397172dcd6cd974e159f84f9523c25a7c2960",
+    ("k_index_scores", "decode", 131072): (6.088e+08, {
+        "indexer.hip": "46bcbfd90e528267e58ffdae475159a0397bd7a517c64877e32f4ad1b822fc6c",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
 }
 
