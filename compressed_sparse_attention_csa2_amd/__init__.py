@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 D, WINDOW, HI, DI, TOPK = 512, 128, 32, 128, 512
 OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_SCORES, OP_INDEX_POOL, OP_REINDEX = 1, 2, 3, 4, 5, 6
 POOL_BLOCKS = 2048
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -54,7 +54,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn.argtypes = ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, i64, i32] +
                                        [vp] * 5 + [i64, vp, vp, vp, vp, sz, vp])
         L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, i32, i32,
-                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp])
+                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp])
+        L.csa2_quant_index_query.argtypes = [vp, vp, i64, vp, vp, vp]
         L.csa2_encode_fp4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_encode_fp8_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_decode_fp4_rows.argtypes = [vp, vp, i64, i32, vp, vp]
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
                      "csa2_index_scores", "csa2_index_pool", "csa2_reindex_topk", "csa2_sparse_attn",
                      "csa2_forward", "csa2_encode_fp4_rows", "csa2_encode_fp8_rows",
                      "csa2_decode_fp4_rows", "csa2_decode_fp8_rows", "csa2_encode_fp4e4_rows",
-                     "csa2_decode_fp4e4_rows"):
+                     "csa2_decode_fp4e4_rows", "csa2_quant_index_query"):
             getattr(L, name).restype = i32
         if L.csa2_abi_version() != ABI_VERSION:
             raise CSA2Error("libcsa2.so ABI version mismatch")
@@ -226,7 +227,7 @@ def csa2_sparse_attn(q_pos0, Q, w_codes, w_scale, z_codes, z_scales, idx, cnt, s
 def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, ki_codes,
                  ki_scales, w_codes, w_scale, idx, cnt, O, ws, kc=None, gc=None, wn=None,
                  gamma_c=None, w_ik=None, gamma_ik=None, ki_given=None, n_entries=None, lse=None,
-                 stream=None, ratio=2, z_format=0):
+                 stream=None, ratio=2, z_format=0, win_floor=None):
     B, H, T = Q.shape[0], Q.shape[1], Q.shape[2]
     _check(lib().csa2_forward(B, T, H, _p(pos0, "i32", "pos0"), _p(kc, "bf16", "kc"),
                               _p(gc, "bf16", "gc"), _p(wn, "bf16", "wn"),
@@ -240,8 +241,19 @@ def csa2_forward(pos0, Q, qI, wI, sink, rope_cos, rope_sin, z_codes, z_scales, k
                               z_codes.shape[1], ratio, z_format, _p(n_entries, "i32", "n_entries"),
                               _p(w_codes, "u8", "w_codes"), _p(w_scale, "f32", "w_scale"),
                               w_codes.shape[1], _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
-                              _p(O, "bf16", "O"), _p(lse, "f32", "lse"), _p(ws, None, "ws"),
+                              _p(O, "bf16", "O"), _p(lse, "f32", "lse"),
+                              _p(win_floor, "i32", "win_floor"), _p(ws, None, "ws"),
                               ws.numel() * ws.element_size(), _stream(stream)), "csa2_forward")
+
+
+def csa2_quant_index_query(qI, wI, q8, wq, stream=None):
+    """qI [..., 128] bf16 and wI [...] fp32 with the same leading shape -> q8 codes, wq"""
+    rows = wI.numel()
+    if qI.numel() != rows * DI or q8.numel() != rows * DI or wq.numel() != rows:
+        raise CSA2Error("csa2_quant_index_query: qI/q8 need 128 values per wI element")
+    _check(lib().csa2_quant_index_query(_p(qI, "bf16", "qI"), _p(wI, "f32", "wI"), rows,
+                                        _p(q8, "u8", "q8"), _p(wq, "f32", "wq"), _stream(stream)),
+           "csa2_quant_index_query")
 
 
 def csa2_encode_fp4_rows(x, codes, scales, stream=None):

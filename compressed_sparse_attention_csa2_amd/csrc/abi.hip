@@ -3,6 +3,7 @@
 // entry point are in include/csa2.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -98,22 +99,23 @@ constexpr int MAX_ROWS = WINDOW + TOPK;
 
 int index_tok(int Tq) { return Tq == 1 ? 1 : (Tq <= 8 ? 8 : 4); }
 
-// split of a token's attention rows (20 chunks of 32 at full size) across
-// blocks when there are too few tokens to fill the chip
-// Compute units of the current device (queried once per device).
+// Compute units of the current device, queried once per device.  The cache is
+// atomic: concurrent first calls may both query, and both store the same value.
 int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
             v = 256;
-        cus[dev] = v;
+        cus[dev].store(v, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return v;
 }
 
+// split of a token's attention rows (20 chunks of 32 at full size) across
+// blocks when there are too few tokens to fill the chip
 int attn_split(int64_t tokens) {
     if (tokens >= 256) return 1;
     const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
@@ -600,8 +602,8 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
                          uint8_t* ki_scales, int64_t entry_stride, int ratio, int z_format,
                          const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
-                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse,
+                         const int32_t* win_floor, void* ws, size_t ws_bytes, void* stream) {
     if (bad_sizes(B, T, entry_stride)) return fail(CSA2_ERR_SHAPE, "forward: B=%d T=%d stride=%lld", B, T, (long long)entry_stride);
     if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "forward: ratio=%d (need 1 or 2)", ratio);
     if (bad_zfmt(z_format)) return fail(CSA2_ERR_UNSUPPORTED, "forward: z_format=%d (need 0 or 1)", z_format);
@@ -649,8 +651,19 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                      cnt, ws, st);
     if (s != CSA2_OK) return s;
     s = launch_attn(B, T, H, pos0, Q, w_codes, w_scale, cap, z_codes, z_scales, entry_stride,
-                    z_format, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, nullptr, ws,
-                    st);
+                    z_format, idx, cnt, sink, rope_cos, rope_sin, rope_rows, O, lse, win_floor,
+                    ws, st);
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_quant_index_query(const uint16_t* qI, const float* wI, int64_t rows, uint8_t* q8,
+                                   float* wq, void* stream) {
+    if (rows < 0) return fail(CSA2_ERR_SHAPE, "quant_index_query: rows=%lld", (long long)rows);
+    if (rows == 0) return ok();     // no work: no pointer is read
+    if (!qI || !wI || !q8 || !wq) return fail(CSA2_ERR_NULL, "quant_index_query: NULL pointer");
+    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(rows, 16)), dim3(256), 0,
+                       S(stream), qI, wI, rows, q8, wq);
+    csa2_status s = check_launch("csa2_quant_index_query");
     return s == CSA2_OK ? ok() : s;
 }
 

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
     CSA2_OK = 0,
@@ -267,12 +267,18 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The whole layer for one call.
- *  Prefill (kc != NULL): compress the T new positions, write their window
- *  rows, then select and attend for every new position; n_entries may be NULL
- *  (then floor((pos0+T)/ratio) per request).
+ * The whole layer for one call [atlas, the compressed-sparse-attention
+ * equations in order: pooling of pairs, compressed RMSNorm, rotation at 2j and
+ * FP4 storage of Z and K^I; the FP8 window; the indexer score and the causal
+ * top-512; the gather of window and selected rows; the sink softmax; the
+ * inverse rotation of the output; blog, "Attention that looks at 640 places"].
+ *  Prefill (kc != NULL): compress the T new positions (at pos0[b] .. pos0[b]+T-1,
+ *  pos0 even at ratio 2; entries below pos0/ratio are the caches' earlier
+ *  contents), write their window rows, then select and attend for every new
+ *  position; n_entries may be NULL (then floor((pos0+T)/ratio) per request).
  *  Decode (kc == NULL): caches are given.  If wn != NULL the new tokens'
  *  window rows are written first.  n_entries is required.
+ *  win_floor [B] int32 device or NULL: bounded replay, as for csa2_sparse_attn.
  *  Arguments as in the calls above; T is the number of query tokens.
  */
 csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_t* kc,
@@ -283,8 +289,8 @@ csa2_status csa2_forward(int B, int T, int H, const int32_t* pos0, const uint16_
                          uint8_t* z_codes, uint8_t* z_scales, uint8_t* ki_codes,
                          uint8_t* ki_scales, int64_t entry_stride, int ratio, int z_format,
                          const int32_t* n_entries, uint8_t* w_codes, float* w_scale, int cap,
-                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse, void* ws,
-                         size_t ws_bytes, void* stream);
+                         int32_t* idx, int32_t* cnt, uint16_t* O, float* lse,
+                         const int32_t* win_floor, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace an op needs for these sizes (0 on invalid sizes). */
 size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride);
@@ -303,6 +309,19 @@ csa2_status csa2_encode_fp4e4_rows(const uint16_t* x, int64_t rows, int cols, ui
                                    uint8_t* scales, void* stream);
 csa2_status csa2_encode_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes,
                                  float* scale, void* stream);
+
+/*
+ * The index queries as the indexer's matrix products take them [atlas:
+ * indexer equation; the query rows quantised to FP8 for the FP8 x FP4
+ * product].  Each (token, head) row of 128 bf16 values x gets the scale
+ * s = max|x| / 448 (1 for an all-zero row) and the codes E4M3FN(x / s)
+ * (fp32 division, nearest even, saturating); the row's head weight is folded
+ * with its scale, wq = wI * s (one fp32 product).  The indexer's scoring
+ * kernels quantise with the same device routine.
+ *  qI [rows][128] bf16, wI [rows] fp32 -> q8 [rows][128] E4M3FN codes, wq [rows] fp32.
+ */
+csa2_status csa2_quant_index_query(const uint16_t* qI, const float* wI, int64_t rows, uint8_t* q8,
+                                   float* wq, void* stream);
 
 /* Dequantisation as the attention kernel performs it, to bf16 (exact for these formats). */
 csa2_status csa2_decode_fp4_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,

@@ -54,3 +54,32 @@ def check_attention(gpu_bf16, oracle_f64, what=""):
     mx, rel = attention_error(gpu_bf16, oracle_f64)
     assert mx <= MAX_ABS and rel <= REL_RMS, f"{what}: max|dO|={mx:.3e} rel_rms={rel:.3e}"
     return mx, rel
+
+
+def oracle_threads() -> int:
+    """worker threads for oracle evaluations: the C oracle releases the GIL inside
+    each call and keeps no shared state, so disjoint rows run in parallel"""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def parallel_map(fn, items, threads=None):
+    """[fn(x) for x in items], evaluated on a thread pool (order kept)"""
+    from concurrent.futures import ThreadPoolExecutor
+    items = list(items)
+    with ThreadPoolExecutor(max_workers=threads or oracle_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+def prefill_rows_parallel(ref, rows, chunk=8, **kw):
+    """PrefillReference.rows over many rows in parallel chunks; the window must
+    already be encoded (ref.window_full()), so no call mutates the reference"""
+    import numpy as np
+    rows = np.asarray(rows, np.int64)
+    parts = [rows[i:i + chunk] for i in range(0, len(rows), chunk)]
+    res = parallel_map(lambda r: ref.rows(r, **kw), parts)
+    out = {}
+    for k in res[0]:
+        vals = [r[k] for r in res]
+        out[k] = None if vals[0] is None else np.concatenate(vals)
+    return out

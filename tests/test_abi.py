@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.csa2_abi_version() == 2
+    assert L.csa2_abi_version() == 3
     for s in range(7):
         assert L.csa2_status_string(s)
 
@@ -88,12 +88,12 @@ def test_rejects_before_launch(L):
     # forward: decode without n_entries
     s = L.csa2_forward(1, 1, 64, FAKE, n, n, n, n, n, n, n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
                        FAKE, FAKE, FAKE, FAKE, 64, 2, 0, n, FAKE, FAKE, 128, FAKE, FAKE, FAKE, n,
-                       FAKE, 1 << 30, n)
+                       n, FAKE, 1 << 30, n)
     assert s == 1 and b"n_entries" in L.csa2_last_error()
     # forward: ring smaller than T + 127
     s = L.csa2_forward(1, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, FAKE,
                        FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 32, 2, 0, n, FAKE, FAKE, 100, FAKE,
-                       FAKE, FAKE, n, FAKE, 1 << 30, n)
+                       FAKE, FAKE, n, n, FAKE, 1 << 30, n)
     assert s == 4
     # encoders: bad widths
     assert L.csa2_encode_fp4_rows(FAKE, 4, 48, FAKE, FAKE, n) == 2
@@ -101,6 +101,9 @@ def test_rejects_before_launch(L):
     assert L.csa2_decode_fp4e4_rows(FAKE, FAKE, 4, 24, FAKE, n) == 2
     assert L.csa2_encode_fp8_rows(FAKE, 4, 2048, FAKE, FAKE, n) == 2
     assert L.csa2_decode_fp8_rows(FAKE, 4, 12, FAKE, n) == 2
+    # index-query quantiser: negative rows, NULL output
+    assert L.csa2_quant_index_query(FAKE, FAKE, -1, FAKE, FAKE, n) == 2
+    assert L.csa2_quant_index_query(FAKE, FAKE, 4, n, FAKE, n) == 1
 
 
 def test_empty_calls_read_no_pointer(L):
@@ -112,6 +115,7 @@ def test_empty_calls_read_no_pointer(L):
     assert L.csa2_sparse_attn(1, 0, 64, n, n, n, n, 200, n, n, 64, 1, n, n, n, n, n, 16, n, n, n,
                               n, 0, n) == 0
     assert L.csa2_encode_fp4e4_rows(n, 0, 512, n, n, n) == 0
+    assert L.csa2_quant_index_query(n, n, 0, n, n, n) == 0
     assert L.csa2_append(0, *([n] * 12), 16, n, n, n, n, 8, 2, 0, n, n, 128, n) == 0
 
 

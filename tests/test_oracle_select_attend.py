@@ -62,6 +62,36 @@ def test_relu_difference_is_linear_form(orc):
     assert np.any(~full)
 
 
+def test_index_scores_direct_definition_signed_weights(orc):
+    """The indexer equation of "DeepSeek V4.1 -- Pooled group -> Source layer, pairs
+    pooled" evaluated directly in float64 numpy: S[j] = sum_h w_h * max(q_h . k_j, 0)
+    with weights of both signs and dot products of both signs, on the exact decoded
+    values of the FP8 queries and FP4 keys.  The placements of the ReLU and of the
+    weight that a kernel could plausibly get wrong -- max(w_h d_h, 0), |w_h| max(d_h, 0),
+    or no ReLU -- each differ from it by far more than the fp32 rounding allowed here."""
+    n = 600
+    kc, ks = rand_keys(orc, n)
+    K = orc.fp4_decode(kc, ks)                                   # [n, 128] exact values
+    q = bf16(rng.standard_normal((32, 128)).astype(np.float32))
+    w = (rng.standard_normal(32) / 64).astype(np.float32)
+    w[:16] = np.abs(w[:16])                                      # both signs present
+    w[16:] = -np.abs(w[16:])
+    q8, sq = orc.quant_index_query(q)
+    Qd = e4m3_table(orc)[q8] * sq[:, None].astype(np.float64)   # [32, 128] decoded queries
+    d = K @ Qd.T                                                 # [n, 32] dot products
+    assert (d > 0).mean() > 0.3 and (d < 0).mean() > 0.3
+    wd = w.astype(np.float64)[None, :]
+    direct = (wd * np.maximum(d, 0.0)).sum(1)
+    S = orc.index_scores(q8, sq, w, kc, ks, n).astype(np.float64)
+    mass = (np.abs(wd) * np.abs(d)).sum(1)
+    # the oracle rounds the exact value once to fp32
+    assert np.all(np.abs(S - direct) <= 2.0 ** -24 * np.abs(direct) + 1e-12 * mass)
+    # each plausible misplacement is caught with a wide margin
+    for wrong in (np.maximum(wd * d, 0.0).sum(1), (np.abs(wd) * np.maximum(d, 0.0)).sum(1),
+                  (wd * d).sum(1)):
+        assert np.max(np.abs(S - wrong) / mass) > 1e-2
+
+
 def test_zero_weights_zero_scores_and_tie_rule(orc):
     n = 1000
     kc, ks = rand_keys(orc, n)
