@@ -43,7 +43,7 @@ def stratified_rows(T, nrows, seed):
     drawn evenly from 48 equal strata of [0, T)"""
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 2, 1021, 1022, 1023, 1024] + list(range(T - 32, T))
-    per = max(1, (nrows - len(fixed)) // 48)
+    per = max(1, -(-(nrows - len(fixed)) // 48))
     edges = np.linspace(0, T, 49).astype(np.int64)
     strata = [rng.integers(edges[i], edges[i + 1], per) for i in range(48)]
     return np.unique(np.concatenate([fixed] + strata))
