@@ -54,6 +54,12 @@ __global__ void k_topk_merge(int, int, const uint32_t*, const int32_t*, const in
                              const uint32_t*, int32_t*, int32_t*);
 __global__ void k_topk_row(int, int, const int32_t*, const int32_t*, const float*, int64_t,
                            int64_t, int32_t*, int32_t*, int, const int32_t*);
+template <int TOK>
+__global__ void k_index_select(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                               const float*, const uint8_t*, const uint8_t*, int64_t, int, int,
+                               int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*,
+                               uint32_t*, uint32_t*);
+__global__ void k_zero_u32(uint32_t*, int64_t);
 template <int HG>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
@@ -185,6 +191,39 @@ ReindexWs reindex_ws(int B, int Tq) {
     return w;
 }
 
+// Fused scores + selection: the quantised queries, and when rows are cut into
+// segments, the segments' winners and one arrival counter per row.  Rows are
+// cut so that about 2,048 waves scan (segments of at least 4,096 entries, at
+// most 64 per row) and no segment exceeds 65,536 entries.
+struct SelWs {
+    int tok, n_tg, nseg, seg_len;
+    size_t q8, wq, seg_key, seg_j, seg_n, seg_kth, done, total;
+};
+SelWs select_ws(int B, int Tq, int64_t stride) {
+    SelWs w;
+    const size_t rows = (size_t)B * Tq;
+    w.tok = index_tok(Tq);
+    w.n_tg = (int)cdiv(Tq, w.tok);
+    const int64_t groups = (int64_t)B * w.n_tg;
+    int64_t ns = groups < 2048 ? cdiv(2048, groups) : 1;
+    if (ns > 64) ns = 64;
+    if (ns > stride / 4096) ns = stride / 4096;
+    if (ns < cdiv(stride, 65536)) ns = cdiv(stride, 65536);   // entry offsets are 16-bit
+    if (ns < 1) ns = 1;
+    w.seg_len = (int)(cdiv(cdiv(stride, ns), 64) * 64);
+    w.nseg = (int)cdiv(stride, w.seg_len);
+    w.q8 = 0;
+    w.wq = align256(rows * HI * DI);
+    w.seg_key = w.wq + align256(rows * HI * sizeof(float));
+    const size_t segc = w.nseg > 1 ? rows * w.nseg * TOPK : 0;
+    w.seg_j = w.seg_key + align256(segc * sizeof(uint32_t));
+    w.seg_n = w.seg_j + align256(segc * sizeof(int32_t));
+    w.seg_kth = w.seg_n + align256((w.nseg > 1 ? rows * w.nseg : 0) * sizeof(int32_t));
+    w.done = w.seg_kth + align256((w.nseg > 1 ? rows * w.nseg * 2 : 0) * sizeof(uint32_t));
+    w.total = w.done + align256((w.nseg > 1 ? rows : 0) * sizeof(uint32_t));
+    return w;
+}
+
 struct AttnWs {
     int nsplit;
     size_t pO, pml, total;
@@ -244,10 +283,47 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
                            wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
 }
 
+// Scores and selection in one kernel: no score row is written (csa2_index_topk,
+// csa2_forward).
 csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                          const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
                          const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
                          int32_t* cnt, void* ws, hipStream_t st) {
+    if (Tq == 0) return CSA2_OK;
+    const SelWs L = select_ws(B, Tq, stride);
+    uint8_t* base = (uint8_t*)ws;
+    uint8_t* q8 = base + L.q8;
+    float* wq = (float*)(base + L.wq);
+    uint32_t* seg_key = (uint32_t*)(base + L.seg_key);
+    int32_t* seg_j = (int32_t*)(base + L.seg_j);
+    int32_t* seg_n = (int32_t*)(base + L.seg_n);
+    uint32_t* seg_kth = (uint32_t*)(base + L.seg_kth);
+    uint32_t* done = (uint32_t*)(base + L.done);
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t qrows = rows * HI;
+    hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 16)), dim3(256), 0, st, qI,
+                       wI, qrows, q8, wq);
+    if (L.nseg > 1)
+        hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, st, done, rows);
+    const int64_t items = (int64_t)B * L.n_tg * L.nseg;
+    if (items > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "index_topk: too many rows");
+#define CSA2_SEL(T)                                                                            \
+    hipLaunchKernelGGL(k_index_select<T>, dim3((unsigned)items), dim3(64), 0, st, B, Tq, q_pos0, \
+                       n_entries, q8, wq, ki_codes, ki_scales, stride, L.n_tg, L.nseg,          \
+                       L.seg_len, rsh, idx, cnt, seg_key, seg_j, seg_n, seg_kth, done)
+    if (L.tok == 1) CSA2_SEL(1);
+    else if (L.tok == 8) CSA2_SEL(8);
+    else CSA2_SEL(4);
+#undef CSA2_SEL
+    return check_launch("csa2_index_topk");
+}
+
+// Scores written to the workspace, then a selection pass over them (the pool
+// needs every score for its block keys).
+csa2_status launch_index_2pass(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                               const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
+                               int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
     const IndexWs L = index_ws(B, Tq, stride);
     float* Sc = (float*)((uint8_t*)ws + L.S);
@@ -357,14 +433,14 @@ const char* csa2_status_string(csa2_status s) {
 
 size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride) {
     if (bad_sizes(B, Tq, entry_stride)) return 0;
-    if (op == CSA2_OP_INDEX_TOPK) return index_ws(B, Tq, entry_stride).total;
+    if (op == CSA2_OP_INDEX_TOPK) return select_ws(B, Tq, entry_stride).total;
     if (op == CSA2_OP_INDEX_SCORES) return index_ws(B, Tq, entry_stride).S;
     if (op == CSA2_OP_INDEX_POOL) return pool_ws(B, Tq, entry_stride).total;
     if (op == CSA2_OP_REINDEX) return reindex_ws(B, Tq).total;
     if (H < 16 || H > 64 || H % 16) return 0;
     if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H).total;
     if (op == CSA2_OP_FORWARD) {
-        size_t a = index_ws(B, Tq, entry_stride).total, c = attn_ws(B, Tq, H).total;
+        size_t a = select_ws(B, Tq, entry_stride).total, c = attn_ws(B, Tq, H).total;
         return (a > c ? a : c) + align256((size_t)B * sizeof(int32_t));
     }
     return 0;
@@ -451,7 +527,7 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
-    const size_t need = index_ws(B, Tq, entry_stride).total;
+    const size_t need = select_ws(B, Tq, entry_stride).total;
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
@@ -476,8 +552,8 @@ csa2_status csa2_index_pool(int B, int Tq, const int32_t* q_pos0, const int32_t*
         return fail(CSA2_ERR_WORKSPACE, "index_pool: workspace %zu < %zu bytes", ws_bytes, L.total);
     if (Tq == 0) return ok();
     hipStream_t st = S(stream);
-    csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
-                                 entry_stride, rsh, idx, cnt, ws, st);
+    csa2_status s = launch_index_2pass(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
+                                       entry_stride, rsh, idx, cnt, ws, st);
     if (s != CSA2_OK) return s;
     const float* Sc = (const float*)((uint8_t*)ws + L.ix.S);
     uint32_t* keys = (uint32_t*)((uint8_t*)ws + L.keys);

@@ -1,0 +1,425 @@
+// Lightning indexer with the causal top-512 fused in: no score row ever
+// reaches memory.
+//
+// "DeepSeek V4.1 -- Pooled group -> Source layer, pairs pooled", indexer and
+// top-k equations: S^I_{t,j} = sum_h w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j) and
+// I_t = top_512(S^I_{t,j} : j < floor((t+1)/2)) (the entries' ratio in place
+// of 2).  "Inside DeepSeek V4.1", section "Attention that looks at 640
+// places": every compressed entry is scored, 512 go on to attention.
+//
+// One wave per (group of TOK query tokens of one request, segment of entries).
+// The wave loads its tokens' E4M3 query rows once and walks the segment's
+// entries in order, 16 per tile, with the same block-scaled FP8 x FP4 MFMA and
+// the same epilogue (integer-max ReLU, head weights folded with the query
+// scales, lane-swap head sums) as the score-only kernel, so every score is the
+// same fp32 value.  After a tile, lane row g holds token g's 16 scores; each
+// is compared with that token's running threshold and the passing ones are
+// appended, in entry order, to the token's candidate buffer in LDS (ballot
+// ranks, no branch: lanes that do not pass write a spare slot).  When a buffer
+// is nearly full, a wave-wide radix select over it finds a key theta with at
+// least 512 candidates at or above it and at most a few hundred more, keeps
+// those in order and makes theta the token's new (strict) threshold: a later
+// entry equal to theta ranks below every kept one, which has a smaller j.
+// At the end an exact select keeps the 512 largest (ties: smaller j).
+//
+// Segments: prefill rows are many and each wave takes all of its tokens'
+// entries (one segment).  Decode rows are few and long, so a row is cut into
+// segments; each segment's wave writes its winners (at most 512 keys and
+// entries, its 512th and ceil(512/nseg)-th keys), and the last segment wave of
+// a row to finish -- counted with a device-scope atomic per row -- merges them
+// while other rows are still being scanned.
+#include "index_device.h"
+
+namespace csa2 {
+
+// Per-token candidate buffers: the scores' bit patterns and the entries as
+// 16-bit offsets from the segment's first entry (segments are at most 65,536
+// entries).  cap slots per token (plus one spare slot per lane column), sized
+// so that the four-token form fits two waves per SIMD in LDS.  tiles: tiles
+// between two checks of the fill; a buffer past `cap - 16 * (tiles + 1)` is
+// refilled, so the admissions before the next check always fit.  keep: a refill
+// keeps at most about this many.  waves: the occupancy the registers are
+// budgeted for.
+template <int TOK> struct SelCfg {
+    static constexpr int cap = TOK == 1 ? 1024 : 768;
+    static constexpr int pad = cap + 16;
+    static constexpr int tiles = TOK == 1 ? 8 : 4;
+    static constexpr int keep = cap - 192;
+    static constexpr int waves = TOK == 1 ? 3 : (TOK == 4 ? 2 : 1);
+};
+
+template <int TOK>
+struct SelBuf {
+    uint32_t key[TOK][SelCfg<TOK>::pad];     // bit patterns of the candidates' scores
+    uint16_t j[TOK][SelCfg<TOK>::pad];       // their entries (offsets), ascending
+    uint32_t hist[256];
+};
+// the wave's LDS: the candidate buffers while scanning, a merge buffer after
+template <int TOK>
+union SelLds {
+    SelBuf<TOK> b;
+    WaveSel ws;
+};
+
+template <int TOK>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<TOK>::waves))) k_index_select(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int n_tg, int nseg, int seg_len, int rsh, int32_t* __restrict__ idx,
+    int32_t* __restrict__ cnt, uint32_t* __restrict__ seg_key, int32_t* __restrict__ seg_j,
+    int32_t* __restrict__ seg_n, uint32_t* __restrict__ seg_kth, uint32_t* __restrict__ row_done) {
+    static_assert(TOK == 1 || TOK == 4 || TOK == 8, "token slots per wave");
+    constexpr int NR = TOK == 8 ? 2 : 1;          // lane-row sets: tokens 4r .. 4r+3
+    constexpr int CAP = SelCfg<TOK>::cap;
+    constexpr int CHK = SelCfg<TOK>::tiles;
+    constexpr int TRIGGER = CAP - 16 * (CHK + 1);
+    __shared__ SelLds<TOK> L;
+    const int lane = threadIdx.x;
+    const int col = lane & 15, grp = lane >> 4;
+
+    // ---- work item: heaviest token groups first, a row's segments together
+    const int64_t item = blockIdx.x;
+    const int seg = (int)(item % nseg);
+    const int64_t rest = item / nseg;
+    const int b = (int)(rest % B);
+    const int tg = n_tg - 1 - (int)(rest / B);
+    if (tg < 0) return;
+    const int t0 = tg * TOK;
+    const int32_t qp = q_pos0[b], ne = n_entries[b];
+    const int64_t j0 = (int64_t)seg * seg_len;
+
+    // this lane row's tokens: candidates inside the segment, threshold, fill
+    int lim[NR];                 // tile jt of this lane is a candidate iff jt < lim (unsigned)
+    int ncnd[NR];                // the row's token's candidates in the segment
+    float thr[NR];
+    int fill[NR];
+    int jlen = 0;                // entries the segment scans: the largest ncnd
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int k = TOK == 1 ? 0 : 4 * r + grp;
+        const int t = t0 + k;
+        int64_t n = (t < Tq && (TOK > 1 || grp == 0)) ? cand_count(qp, t, ne, entry_stride, rsh) - j0 : 0;
+        n = n < 0 ? 0 : (n > seg_len ? seg_len : n);
+        ncnd[r] = (int)n;
+        lim[r] = (int)n - col > 0 ? (int)n - col : 0;
+        thr[r] = -INFINITY;
+        fill[r] = 0;
+        jlen = max(jlen, (int)n);
+    }
+    jlen = (int)wave_max((uint32_t)jlen);
+
+    // ---- query operands (as the score-only kernel loads them)
+    i8 A[TOK][2];
+    f4 W[TOK][2];
+#pragma unroll
+    for (int k = 0; k < TOK; ++k) {
+        const int t = t0 + k;
+        const bool ok = t < Tq;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const int64_t row = ((int64_t)b * Tq + (ok ? t : 0)) * HI + tile * 16;
+            const uint8_t* src = q8 + (row + col) * DI + 16 * grp;
+            const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 64);
+            A[k][tile] = ok ? i8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w}
+                            : i8{0, 0, 0, 0, 0, 0, 0, 0};
+            const float4 w4 = *(const float4*)(wq + row + 4 * grp);
+            W[k][tile] = ok ? f4{w4.x, w4.y, w4.z, w4.w} : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // ---- admission of one tile's scores: lane row g holds token 4r + g's score
+    // of entry jt + col (TOK = 1: row 0 holds token 0's, the other rows copies).
+    // The passing lanes of a row take consecutive slots in lane (entry) order:
+    // an inclusive prefix count over the row's 16 lanes (DPP row shifts) and the
+    // row's total from its last lane (DPP row broadcast).
+    auto admit = [&](int r, int jt, float tot) {
+        const bool pass = (TOK > 1 || grp == 0) && (unsigned)jt < (unsigned)lim[r] && tot > thr[r];
+        const int b = pass ? 1 : 0;
+        int sc = b;
+        sc += __builtin_amdgcn_update_dpp(0, sc, 0x111, 0xf, 0xf, true);   // row_shr:1
+        sc += __builtin_amdgcn_update_dpp(0, sc, 0x112, 0xf, 0xf, true);   // row_shr:2
+        sc += __builtin_amdgcn_update_dpp(0, sc, 0x114, 0xf, 0xf, true);   // row_shr:4
+        sc += __builtin_amdgcn_update_dpp(0, sc, 0x118, 0xf, 0xf, true);   // row_shr:8
+        const int total = __builtin_amdgcn_update_dpp(0, sc, 0x15F, 0xf, 0xf, false);  // row_newbcast:15
+        const int slot = pass ? fill[r] + sc - 1 : CAP + col;
+        const int tk = TOK == 1 ? 0 : 4 * r + grp;
+        L.b.key[tk][slot] = __float_as_uint(tot);
+        L.b.j[tk][slot] = (uint16_t)(jt + col);
+        fill[r] += total;
+    };
+
+    // ---- refill of token tk's buffer (whole wave): keep the candidates at or
+    // above a key theta that at least 512 of them reach, theta becomes strict
+    auto refill = [&](int r, int g) {      // r: a compile-time row set, g: the lane row
+        const int tk = TOK == 1 ? 0 : 4 * r + g;
+        const int nc = __builtin_amdgcn_readlane(fill[r], 16 * g);
+        uint32_t kr[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = 64 * q + lane;
+            kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+        }
+        uint32_t krem;
+        uint32_t theta = wave_threshold_h(L.b.hist, kr, TOPK, SelCfg<TOK>::keep, false, &krem);
+        int kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, krem);
+        if (kept > SelCfg<TOK>::keep) {
+            // only when every key is equal (a non-exact threshold otherwise keeps at
+            // most `keep`): the buffer came back unchanged; keep the first 512
+            theta = wave_threshold_h(L.b.hist, kr, TOPK, 0, true, &krem);
+            kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, krem);
+        }
+        if (grp == g) {
+            fill[r] = kept;
+            thr[r] = key_score(theta);
+        }
+    };
+    auto check = [&]() {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint64_t over = __ballot(fill[r] > TRIGGER) & (TOK == 1 ? 0xFFFFull : ~0ull);
+            while (over) {
+                const int g = (__ffsll((long long)over) - 1) >> 4;
+                refill(r, g);
+                over = __ballot(fill[r] > TRIGGER) & (TOK == 1 ? 0xFFFFull : ~0ull);
+            }
+        }
+    };
+
+    const uint8_t* kbase = ki_codes + ((int64_t)b * entry_stride + j0) * 64;
+    const uint8_t* sbase = ki_scales + ((int64_t)b * entry_stride + j0) * 4;
+    // codes and scales through buffer resources bounded to the scanned entries:
+    // tiles past them read zeros (their scores are never admitted), so no load
+    // sits behind a branch and every wait is exact
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kbase, (short)0, jlen * 64, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sbase, (short)0, jlen * 4, 0x00020000);
+
+    if constexpr (TOK == 4) {
+        // Software-pipelined by token pairs, as in the score-only kernel: the
+        // products of one pair run on the matrix unit while the vector unit
+        // reduces the other pair.  Per tile p: [products of tokens 0,1 on p |
+        // head sums of tokens 2,3 of p - 1, then the admission of p - 1]
+        // [products of tokens 2,3 on p | head sums of tokens 0,1 of p].
+        int kld = col * 64 + 16 * grp;
+        int sld = col * 4;
+        uint4 kb[4];
+        int sb[4];
+        auto ld = [&](int p, uint4& kc, int& sc) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, kld + 1024 * p, 0, 0);
+            kc = uint4{v[0], v[1], v[2], v[3]};
+            sc = (int)__builtin_amdgcn_raw_buffer_load_b32(ksr, sld + 16 * 4 * p, 0, 0);
+        };
+        auto mm2 = [&](int k0, const uint4 kc, const int sw, f4 (&d)[2][2]) {
+            const int sc = (int)(((uint32_t)sw >> (8 * grp)) & 0xFFu);
+            const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int tile = 0; tile < 2; ++tile)
+                    d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        };
+        auto epi2 = [&](int k0, const f4 (&d)[2][2], float& sa, float& sb2) {
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a0 = __builtin_fmaf(W[k0][tile][i], relu(d[0][tile][i]), a0);
+                    a1 = __builtin_fmaf(W[k0 + 1][tile][i], relu(d[1][tile][i]), a1);
+                }
+            sa = a0;
+            sb2 = a1;
+        };
+        f4 dA[2][2], dB[2][2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) dB[k][tile] = f4{0.f, 0.f, 0.f, 0.f};
+        float s0 = 0.0f, s1 = 0.0f, s2, s3;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) ld(p, kb[p], sb[p]);
+        kld += 3 * 1024;
+        sld += 3 * 64;
+        const int ngroups = (jlen + 63) >> 6;
+        for (int gi = 0; gi < ngroups; ++gi) {      // tiles 4 gi .. 4 gi + 3
+            const int jt = gi * 64;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                ld(p, kb[(p + 3) & 3], sb[(p + 3) & 3]);
+                mm2(0, kb[p], sb[p], dA);
+                epi2(2, dB, s2, s3);
+                admit(0, jt + 16 * p - 16, rowsum_scatter4(s0, s1, s2, s3));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mm2(2, kb[p], sb[p], dB);
+                epi2(0, dA, s0, s1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            kld += 4096;
+            sld += 256;
+            check();
+        }
+        epi2(2, dB, s2, s3);
+        admit(0, ngroups * 64 - 16, rowsum_scatter4(s0, s1, s2, s3));
+    } else {
+        auto load = [&](int jt, uint4& kc, uint32_t& sw) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (jt + col) * 64 + 16 * grp, 0, 0);
+            kc = uint4{v[0], v[1], v[2], v[3]};
+            sw = __builtin_amdgcn_raw_buffer_load_b32(ksr, (jt + col) * 4, 0, 0);
+        };
+        auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
+            const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
+            const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+            float s[TOK];
+            constexpr int KG = TOK < 4 ? TOK : 4;
+#pragma unroll
+            for (int k0 = 0; k0 < TOK; k0 += KG) {
+                f4 d[KG][2];
+#pragma unroll
+                for (int k = 0; k < KG; ++k)
+#pragma unroll
+                    for (int tile = 0; tile < 2; ++tile)
+                        d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < KG; ++k) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][0][i], relu(d[k][0][i]), acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][1][i], relu(d[k][1][i]), acc);
+                    s[k0 + k] = acc;
+                }
+            }
+            if (TOK == 1) {
+                admit(0, jt, rowsum_scatter4(s[0], s[0], s[0], s[0]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    admit(r, jt, rowsum_scatter4(s[4 * r], s[4 * r + 1], s[4 * r + 2], s[4 * r + 3]));
+            }
+        };
+        // NB tile buffers rotate; tile jt + 16p lives in buffer p % NB and is
+        // loaded NB - 1 tiles ahead (buffer loads past the entries read zeros)
+        constexpr int NB = CHK;
+        uint4 kb[NB];
+        uint32_t sb[NB];
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p) load(16 * p, kb[p], sb[p]);
+        for (int jt = 0; jt < jlen; jt += 16 * NB) {
+#pragma unroll
+            for (int p = 0; p < NB; ++p) {
+                load(jt + 16 * (p + NB - 1), kb[(p + NB - 1) % NB], sb[(p + NB - 1) % NB]);
+                step(jt + 16 * p, kb[p], sb[p]);
+            }
+            check();
+        }
+    }
+
+    // ---- results per token: the exact top 512 of its candidates, in entry order
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const int r = TOK == 1 ? 0 : tk >> 2, g = TOK == 1 ? 0 : tk & 3;
+        const int t = t0 + tk;
+        if (t >= Tq) break;
+        const int64_t row = (int64_t)b * Tq + t;
+        int nc = __builtin_amdgcn_readlane(fill[r], 16 * g);
+        uint32_t kr[16];
+        if (nc > TOPK || nseg > 1) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int i = 64 * q + lane;
+                kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+            }
+        }
+        if (nc > TOPK) {
+            uint32_t krem;
+            const uint32_t kth = wave_threshold_h(L.b.hist, kr, TOPK, 0, true, &krem);
+            nc = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, kth, krem);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int i = 64 * q + lane;
+                kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+            }
+        }
+        if (nseg == 1) {
+            int32_t* out = idx + row * TOPK;
+            for (int i = lane; i < TOPK; i += 64) out[i] = i < nc ? (int)j0 + L.b.j[tk][i] : -1;
+            if (lane == 0) cnt[row] = nc;
+        } else {
+            // the segment's winners, its 512th key (0 when it has fewer) and its
+            // ceil(512 / nseg)-th key (0 when it has fewer), for the merge's bound
+            const int64_t it = row * nseg + seg;
+            uint32_t mn = 0xFFFFFFFFu;
+            for (int i = lane; i < TOPK; i += 64) {
+                const bool v = i < nc;
+                const uint32_t kv = v ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+                seg_key[it * TOPK + i] = kv;
+                seg_j[it * TOPK + i] = v ? (int)j0 + L.b.j[tk][i] : -1;
+                if (v) mn = min(mn, kv);
+            }
+            const uint32_t kq = (uint32_t)((TOPK + nseg - 1) / nseg);
+            uint32_t kqv = 0u;
+            if (nc >= (int)kq) {
+                uint32_t krem;
+                kqv = wave_threshold_h(L.b.hist, kr, kq, 0, true, &krem);
+            }
+            const uint32_t kth = nc == TOPK ? wave_min(mn) : 0u;
+            if (lane == 0) {
+                seg_n[it] = nc;
+                seg_kth[2 * it] = kth;
+                seg_kth[2 * it + 1] = kqv;
+            }
+        }
+    }
+    if (nseg == 1) return;
+
+    // ---- the last segment wave of a row merges the row's winners
+    WaveSel& ws = L.ws;
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const int t = t0 + tk;
+        if (t >= Tq) break;
+        const int64_t row = (int64_t)b * Tq + t;
+        __threadfence();                   // this wave's winners are visible device-wide
+        uint32_t prev = 0u;
+        if (lane == 0) prev = atomicAdd(&row_done[row], 1u);
+        prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+        if (prev == (uint32_t)(nseg - 1)) {
+            __threadfence();               // and the other segments' winners are visible here
+            merge_segments(ws, row, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
+        }
+    }
+}
+
+// rows of a u32 array set to zero (the per-row arrival counters of the merge)
+__global__ void __launch_bounds__(256) k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+#define CSA2_SEL_INST(T)                                                                       \
+    template __global__ void k_index_select<T>(                                                \
+        int, int, const int32_t*, const int32_t*, const uint8_t*, const float*, const uint8_t*, \
+        const uint8_t*, int64_t, int, int, int, int, int32_t*, int32_t*, uint32_t*, int32_t*,  \
+        int32_t*, uint32_t*, uint32_t*);
+CSA2_SEL_INST(1)
+CSA2_SEL_INST(4)
+CSA2_SEL_INST(8)
+#undef CSA2_SEL_INST
+
+}  // namespace csa2

@@ -22,7 +22,7 @@
 // channels.  A wave holds TOK tokens (2 MFMA rows each) and walks a chunk of
 // entries 16 at a time; lane l of the result holds entry l%16 and heads
 // 4(l/16)..4(l/16)+3, so the head sum is 8 in-lane fmas and two cross-lane adds.
-#include "csa2_device.h"
+#include "index_device.h"
 
 namespace csa2 {
 
@@ -59,37 +59,6 @@ __global__ void __launch_bounds__(256) k_quant_index_query(const uint16_t* __res
     if (l16 == 0) wq[r] = wI[r] * sc;
 }
 
-
-// Causal candidates of the query at p = qpos0 + t: entries j < floor((p+1)/ratio)
-// (ratio = 1 << rsh: 2 for pooled pairs, 1 for one entry per position), at
-// most the request's n_ent valid rows and the cache's stride.
-__device__ __forceinline__ int64_t cand_count(int32_t qpos0, int t, int32_t n_ent,
-                                              int64_t stride, int rsh) {
-    int64_t n = ((int64_t)qpos0 + t + 1) >> rsh;
-    int64_t cap = n_ent < 0 ? 0 : (int64_t)n_ent;
-    if (cap > stride) cap = stride;
-    return n < cap ? (n < 0 ? 0 : n) : cap;
-}
-
-// max(x, 0) as one integer max on the bit pattern: every negative float
-// (including -0) is a negative integer.
-__device__ __forceinline__ float relu(float x) {
-    return __int_as_float(max(__float_as_int(x), 0));
-}
-
-// Sum over the four 16-lane rows, scattered: after the call lane row g holds
-// the total of token slot g (slots: a, b, c, d).  Built from the gfx950 lane
-// swaps: permlane32 exchanges the upper half of its first operand with the
-// lower half of its second, permlane16 the odd rows of the first with the even
-// rows of the second.
-__device__ __forceinline__ float rowsum_scatter4(float a, float b, float c, float d) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(d), false, false);
-    const float u0 = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows: a(0+2), a(1+3) | c ...
-    const float u1 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u0), __float_as_uint(u1), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Scores S[(b*Tq + t)][j] for j < n(t).  One wave per (request, TOK tokens,
 // chunk of IDX_CHUNK entries); work items are ordered heaviest tokens first.
@@ -348,254 +317,6 @@ __global__ void __launch_bounds__(256) k_index_scores(
         if (jt + 16 * p < j_len) step(jt + 16 * p, kb[p], sb[p]);
 }
 
-// ---------------------------------------------------------------------------
-// Top-512 selection.  Keys are the scores mapped to order-preserving u32 (-0
-// first turned into +0 so equal scores compare equal; 0 never occurs for a
-// finite score and marks "no element").  Ties: larger score, then smaller
-// entry index; output in ascending entry order, padded with -1.
-//
-// One wave per list (a query row, a segment of a long row, or the merged
-// candidates of a row's segments), no block barriers.  The list is streamed
-// once, in order, 256 elements per step (lane l holds elements 4l..4l+3), and
-// every element whose key exceeds the wave's threshold is appended to a
-// per-wave LDS buffer (ballot compaction keeps list order).  When the buffer
-// would overflow, a wave-local radix select finds its 512th largest key K
-// (and how many copies of K belong to the top 512); the buffer is compacted
-// to exactly those 512 and the threshold becomes K, now strict: a later
-// element equal to K ranks below the 512 kept ones (all earlier in the list).
-// At the end the same select trims the buffer to 512.
-// ---------------------------------------------------------------------------
-constexpr int WS_CAP = 1024;          // per-wave candidate buffer
-constexpr int WS_WAVES = 4;           // lists per block
-
-__device__ __forceinline__ uint32_t score_key(float f) {
-    f = f + 0.0f;   // -0 -> +0 so equal scores compare equal
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-struct WaveSel {
-    uint32_t key[WS_CAP];
-    int32_t j[WS_CAP];
-    uint32_t hist[256];
-};
-
-// Wave-wide inclusive prefix sum with DPP row shifts and row broadcasts (no LDS).
-__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return v;
-}
-// Wave-wide min / max of u32 values (DPP; lanes outside a row keep the identity),
-// returned in every lane.
-template <int CTRL, int RMASK>
-__device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
-    return min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)v, CTRL, RMASK, 0xf, false));
-}
-template <int CTRL, int RMASK>
-__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
-    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RMASK, 0xf, false));
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-    v = dpp_min<0x111, 0xf>(v);
-    v = dpp_min<0x112, 0xf>(v);
-    v = dpp_min<0x114, 0xf>(v);
-    v = dpp_min<0x118, 0xf>(v);
-    v = dpp_min<0x142, 0xa>(v);
-    v = dpp_min<0x143, 0xc>(v);
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-    v = dpp_max<0x111, 0xf>(v);
-    v = dpp_max<0x112, 0xf>(v);
-    v = dpp_max<0x114, 0xf>(v);
-    v = dpp_max<0x118, 0xf>(v);
-    v = dpp_max<0x142, 0xa>(v);
-    v = dpp_max<0x143, 0xc>(v);
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Radix threshold over the buffer's keys, held in registers (lane l: elements
-// l + 64r, r < 16; 0 past nc).  Returns theta with at least k keys >= theta.
-// exact: theta is the k-th largest key and *krem the number of its copies in
-// the top k.  Otherwise refinement stops as soon as at most `limit` keys are
-// >= theta (*krem is then "all copies"); if equal keys keep the count above the
-// limit to the last bit, the exact answer is returned.  The bits common to all
-// keys are skipped; 8 bits per pass.
-__device__ uint32_t wave_threshold(WaveSel& ws, const uint32_t (&kr)[16], uint32_t k,
-                                   uint32_t limit, bool exact, uint32_t* krem_out) {
-    const int lane = threadIdx.x & 63;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (kr[r] != 0u) lo = min(lo, kr[r]);
-        hi = max(hi, kr[r]);
-    }
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lo >= hi) {                 // all keys equal
-        *krem_out = exact ? k : 0xFFFFFFFFu;
-        return hi;
-    }
-    int hib = 31 - __clz((int)(lo ^ hi));
-    uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
-    uint32_t prefix = lo & pmask, krem = k, above_all = 0;
-    while (hib >= 0) {
-        const int lob = hib - 7 > 0 ? hib - 7 : 0;
-        const uint32_t dmask = (2u << (hib - lob)) - 1u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ws.hist[4 * lane + q] = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (kr[r] != 0u && (kr[r] & pmask) == prefix) atomicAdd(&ws.hist[(kr[r] >> lob) & dmask], 1u);
-        // digit holding the krem-th largest: bins in descending order, 4 per lane
-        uint32_t h[4], loc = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { h[q] = ws.hist[255 - 4 * lane - q]; loc += h[q]; }
-        const uint32_t inc = wave_scan_add(loc);
-        uint32_t above = inc - loc, dsel = 0, asel = 0, hsel = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (above < krem && krem <= above + h[q]) {
-                dsel = 255u - 4u * lane - q;
-                asel = above;
-                hsel = h[q];
-                found = true;
-            }
-            above += h[q];
-        }
-        const int src = __ffsll((long long)__ballot(found)) - 1;
-        dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
-        asel = (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
-        hsel = (uint32_t)__builtin_amdgcn_readlane((int)hsel, src);
-        prefix |= dsel << lob;
-        pmask |= dmask << lob;
-        krem -= asel;
-        above_all += asel;
-        hib = lob - 1;
-        if (!exact && above_all + hsel <= limit) {   // keys >= prefix (low bits 0) fit
-            *krem_out = 0xFFFFFFFFu;
-            return prefix;
-        }
-    }
-    // every bit resolved: the k-th largest itself, and its copies in the top k
-    // (also when a non-exact search could not get under the limit: many equal keys)
-    *krem_out = krem;
-    return prefix;
-}
-
-// Keep, in order, the buffered elements above theta and the first krem equal to it.
-__device__ int wave_keep(WaveSel& ws, int nc, const uint32_t (&kr)[16], uint32_t theta,
-                         uint32_t krem) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int32_t jr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) jr[r] = 64 * r + lane < nc ? ws.j[64 * r + lane] : 0;
-    uint32_t kept = 0, eq = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (64 * r >= nc) break;
-        const bool valid = 64 * r + lane < nc;
-        const uint64_t meq = __ballot(valid && kr[r] == theta);
-        const bool keep = valid && (kr[r] > theta ||
-                                    (kr[r] == theta && eq + (uint32_t)__popcll(meq & below) < krem));
-        const uint64_t mk = __ballot(keep);
-        if (keep) {
-            const uint32_t pos = kept + (uint32_t)__popcll(mk & below);
-            ws.key[pos] = kr[r];
-            ws.j[pos] = jr[r];
-        }
-        kept += (uint32_t)__popcll(mk);
-        eq += (uint32_t)__popcll(meq);
-    }
-    return (int)kept;
-}
-
-__device__ __forceinline__ void load_keys(const WaveSel& ws, int nc, uint32_t (&kr)[16]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) kr[r] = 64 * r + lane < nc ? ws.key[64 * r + lane] : 0u;
-}
-
-struct WaveTopk {
-    WaveSel& ws;
-    int nc;
-    uint32_t thr;     // elements with key > thr are appended (0: every element)
-
-    // four elements per lane, in list order (lane, then q); key 0 = no element
-    __device__ void push(const uint32_t (&k)[4], const int32_t (&jj)[4]) {
-        const int lane = threadIdx.x & 63;
-        const uint64_t below = (1ull << lane) - 1ull;
-        uint64_t m[4];
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { m[q] = __ballot(k[q] > thr); cnt += (uint32_t)__popcll(m[q]); }
-        if (nc + (int)cnt > WS_CAP) {
-            // keep every key >= theta, where at least 512 are >= theta: a later key
-            // equal to theta ranks below all of them
-            uint32_t kr[16], krem;
-            load_keys(ws, nc, kr);
-            const uint32_t theta = wave_threshold(ws, kr, TOPK, WS_CAP - 256, false, &krem);
-            nc = wave_keep(ws, nc, kr, theta, krem);
-            thr = theta;
-            cnt = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) { m[q] = __ballot(k[q] > thr); cnt += (uint32_t)__popcll(m[q]); }
-        }
-        uint32_t pos = (uint32_t)nc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pos += (uint32_t)__popcll(m[q] & below);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (k[q] > thr) {
-                ws.key[pos] = k[q];
-                ws.j[pos] = jj[q];
-                ++pos;
-            }
-        }
-        nc += (int)cnt;
-    }
-
-    // the top 512 in list order to out_j (padded with -1) and, if given, their keys;
-    // *kth_out = the 512th largest key (0 when fewer than 512 elements); if kq_out
-    // is given, *kq_out = the kq-th largest key (0 when fewer than kq elements)
-    __device__ int finish(int32_t* out_j, uint32_t* out_key, uint32_t* kth_out,
-                          uint32_t kq = 0, uint32_t* kq_out = nullptr) {
-        const int lane = threadIdx.x & 63;
-        if (nc > TOPK) {
-            uint32_t kr[16], krem;
-            load_keys(ws, nc, kr);
-            const uint32_t kth = wave_threshold(ws, kr, TOPK, 0, true, &krem);
-            nc = wave_keep(ws, nc, kr, kth, krem);
-        }
-        uint32_t mn = 0xFFFFFFFFu;
-        for (int i = lane; i < TOPK; i += 64) {
-            out_j[i] = i < nc ? ws.j[i] : -1;
-            if (i < nc) {
-                mn = min(mn, ws.key[i]);
-                if (out_key) out_key[i] = ws.key[i];
-            }
-        }
-        if (kth_out) *kth_out = nc == TOPK ? wave_min(mn) : 0u;
-        if (kq_out) {
-            uint32_t v = 0u;
-            if (kq > 0 && nc >= (int)kq) {
-                uint32_t kr[16], krem;
-                load_keys(ws, nc, kr);
-                v = wave_threshold(ws, kr, kq, 0, true, &krem);
-            }
-            *kq_out = v;
-        }
-        return nc;
-    }
-};
-
 // One wave per (query row, segment).  Row scores are spad floats apart (spad a
 // multiple of 64); segment s covers entries [s*seg_len, (s+1)*seg_len).  With one
 // segment the result goes to idx/cnt, otherwise to the segment buffers.
@@ -703,59 +424,15 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
 }
 
 // Merge of a row's segment winners (segments in entry order): one wave per row.
-// The largest of the segments' 512th keys bounds the row's 512th key from below
-// (that segment alone holds 512 keys at or above it), so only keys at or above
-// it are streamed.
 __global__ void __launch_bounds__(64 * WS_WAVES) k_topk_merge(
     int rows, int nseg, const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ seg_j,
     const int32_t* __restrict__ seg_n, const uint32_t* __restrict__ seg_kth,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
     __shared__ WaveSel sel[WS_WAVES];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * WS_WAVES + wave;
     if (row >= rows) return;
-    // Lower bounds of the row's 512th largest key: the largest of the segments'
-    // 512th keys (that segment alone holds 512 keys at or above it), and, when
-    // every segment holds at least q = ceil(512 / nseg) keys, the smallest of
-    // their q-th keys (together the segments hold nseg * q >= 512 keys at or
-    // above it).  Keys below the larger bound cannot be selected.
-    const uint32_t kth_s = lane < nseg ? seg_kth[2 * (row * nseg + lane)] : 0u;
-    const uint32_t kq_s = lane < nseg ? seg_kth[2 * (row * nseg + lane) + 1] : 0xFFFFFFFFu;
-    const uint32_t kq_min = wave_min(kq_s);
-    const uint32_t bound = max(wave_max(kth_s), kq_min);
-    WaveTopk st{sel[wave], 0, bound > 0u ? bound - 1u : 0u};
-    // each segment's 512 slots in one step: two 256-element groups, vector loads
-    auto fetch = [&](int s, uint4 (&kv)[2], int4 (&jv)[2]) {
-        const int64_t it = row * nseg + s;
-        int m = seg_n[it];
-        m = m < 0 ? 0 : (m > TOPK ? TOPK : m);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i0 = 256 * u + 4 * lane;
-            kv[u] = *(const uint4*)(seg_key + it * TOPK + i0);
-            jv[u] = *(const int4*)(seg_j + it * TOPK + i0);
-            if (i0 >= m) kv[u].x = 0u;
-            if (i0 + 1 >= m) kv[u].y = 0u;
-            if (i0 + 2 >= m) kv[u].z = 0u;
-            if (i0 + 3 >= m) kv[u].w = 0u;
-        }
-    };
-    uint4 nk[2];
-    int4 nj[2];
-    fetch(0, nk, nj);
-    for (int s = 0; s < nseg; ++s) {
-        const uint4 ck[2] = {nk[0], nk[1]};
-        const int4 cj[2] = {nj[0], nj[1]};
-        if (s + 1 < nseg) fetch(s + 1, nk, nj);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint32_t k[4] = {ck[u].x, ck[u].y, ck[u].z, ck[u].w};
-            const int32_t jj[4] = {cj[u].x, cj[u].y, cj[u].z, cj[u].w};
-            st.push(k, jj);
-        }
-    }
-    const int c = st.finish(idx + row * TOPK, nullptr, nullptr);
-    if (lane == 0) cnt[row] = c;
+    merge_segments(sel[wave], row, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
 }
 
 // Exclusive prefix sum over a block of NW waves (DPP scans in the waves, the
