@@ -224,6 +224,12 @@ SelWs select_ws(int B, int Tq, int64_t stride) {
     return w;
 }
 
+bool two_pass_rows(int64_t rows, int64_t stride);
+size_t index_topk_ws(int B, int Tq, int64_t stride) {
+    return two_pass_rows((int64_t)B * Tq, stride) ? index_ws(B, Tq, stride).total
+                                                  : select_ws(B, Tq, stride).total;
+}
+
 struct AttnWs {
     int nsplit;
     size_t pO, pml, total;
@@ -283,13 +289,26 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
                            wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
 }
 
+// Few long rows (the decode shapes): scores to the workspace and a selection
+// pass win there -- the fused kernel would cut each row into many segments,
+// each selecting its own 512.
+bool two_pass_rows(int64_t rows, int64_t stride) { return rows <= 1024 && stride >= 16384; }
+
+csa2_status launch_index_2pass(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
+                               const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
+                               const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
+                               int32_t* cnt, void* ws, hipStream_t st);
+
 // Scores and selection in one kernel: no score row is written (csa2_index_topk,
-// csa2_forward).
+// csa2_forward), except for few long rows (two_pass_rows).
 csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                          const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
                          const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
                          int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
+    if (two_pass_rows((int64_t)B * Tq, stride))
+        return launch_index_2pass(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride,
+                                  rsh, idx, cnt, ws, st);
     const SelWs L = select_ws(B, Tq, stride);
     uint8_t* base = (uint8_t*)ws;
     uint8_t* q8 = base + L.q8;
@@ -433,14 +452,14 @@ const char* csa2_status_string(csa2_status s) {
 
 size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride) {
     if (bad_sizes(B, Tq, entry_stride)) return 0;
-    if (op == CSA2_OP_INDEX_TOPK) return select_ws(B, Tq, entry_stride).total;
+    if (op == CSA2_OP_INDEX_TOPK) return index_topk_ws(B, Tq, entry_stride);
     if (op == CSA2_OP_INDEX_SCORES) return index_ws(B, Tq, entry_stride).S;
     if (op == CSA2_OP_INDEX_POOL) return pool_ws(B, Tq, entry_stride).total;
     if (op == CSA2_OP_REINDEX) return reindex_ws(B, Tq).total;
     if (H < 16 || H > 64 || H % 16) return 0;
     if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H).total;
     if (op == CSA2_OP_FORWARD) {
-        size_t a = select_ws(B, Tq, entry_stride).total, c = attn_ws(B, Tq, H).total;
+        size_t a = index_topk_ws(B, Tq, entry_stride), c = attn_ws(B, Tq, H).total;
         return (a > c ? a : c) + align256((size_t)B * sizeof(int32_t));
     }
     return 0;
@@ -527,7 +546,7 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
     if (Tq == 0) return ok();     // no work: no pointer is read
     if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
         return fail(CSA2_ERR_NULL, "index_topk: a required pointer is NULL");
-    const size_t need = select_ws(B, Tq, entry_stride).total;
+    const size_t need = index_topk_ws(B, Tq, entry_stride);
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
