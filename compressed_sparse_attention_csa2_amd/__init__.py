@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_forward.argtypes = ([i32, i32, i32] + [vp] * 14 + [i64] + [vp] * 4 + [i64, i32, i32,
                                    vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp])
         L.csa2_quant_index_query.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.csa2_index_topk_noalloc.argtypes = [i32, i32] + [vp] * 6 + [i64, i32, vp, vp, vp]
         L.csa2_encode_fp4_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_encode_fp8_rows.argtypes = [vp, i64, i32, vp, vp, vp]
         L.csa2_decode_fp4_rows.argtypes = [vp, vp, i64, i32, vp, vp]
@@ -66,7 +67,8 @@ def lib() -> ctypes.CDLL:
                      "csa2_index_scores", "csa2_index_pool", "csa2_reindex_topk", "csa2_sparse_attn",
                      "csa2_forward", "csa2_encode_fp4_rows", "csa2_encode_fp8_rows",
                      "csa2_decode_fp4_rows", "csa2_decode_fp8_rows", "csa2_encode_fp4e4_rows",
-                     "csa2_decode_fp4e4_rows", "csa2_quant_index_query"):
+                     "csa2_decode_fp4e4_rows", "csa2_quant_index_query",
+                     "csa2_index_topk_noalloc"):
             getattr(L, name).restype = i32
         if L.csa2_abi_version() != ABI_VERSION:
             raise CSA2Error("libcsa2.so ABI version mismatch")
@@ -167,6 +169,22 @@ def csa2_index_topk(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, ws
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "csa2_index_topk")
 
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def csa2_index_topk_noalloc(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt,
+                            stream=None, ratio=2):
+    """csa2_index_topk with the library's own scratch array (no workspace argument)"""
+    B, Tq = qI.shape[0], qI.shape[1]
+    _check(lib().csa2_index_topk_noalloc(B, Tq, _p(q_pos0, "i32", "q_pos0"),
+                                         _p(n_entries, "i32", "n_entries"), _p(qI, "bf16", "qI"),
+                                         _p(wI, "f32", "wI"), _p(ki_codes, "u8", "ki_codes"),
+                                         _p(ki_scales, "u8", "ki_scales"), ki_codes.shape[1],
+                                         ratio, _p(idx, "i32", "idx"), _p(cnt, "i32", "cnt"),
+                                         _stream(stream)),
+           "csa2_index_topk_noalloc")
 
 
 def csa2_index_pool(q_pos0, n_entries, qI, wI, ki_codes, ki_scales, idx, cnt, pool, pool_cnt, ws,

@@ -72,6 +72,11 @@ __global__ void k_attn_combine(int, int, int, const int32_t*, const float*, cons
 
 using namespace csa2;
 
+// Scratch of csa2_index_topk_noalloc: one array per GPU, part of the library's
+// code object.  In host code `scratch` only names the symbol; its device address
+// comes from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -118,6 +123,29 @@ int device_cus() {
         cus[dev].store(v, std::memory_order_relaxed);
     }
     return v;
+}
+
+// Device address of the current device's scratch array, looked up on the first
+// call per device (with that device current) and kept; concurrent first calls
+// store the same address.  NULL (and an error message) if the lookup fails.
+void* scratch_ptr() {
+    static std::atomic<void*> ptrs[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        fail(CSA2_ERR_HIP, "scratch: no current device (%s)", hipGetErrorString(e));
+        return nullptr;
+    }
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            fail(CSA2_ERR_HIP, "scratch: hipGetSymbolAddress failed (%s)", hipGetErrorString(e));
+            return nullptr;
+        }
+        ptrs[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 // split of a token's attention rows (20 chunks of 32 at full size) across
@@ -549,6 +577,27 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
     const size_t need = index_topk_ws(B, Tq, entry_stride);
     if (Tq > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "index_topk: workspace %zu < %zu bytes", ws_bytes, need);
+    csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
+                                 entry_stride, ratio == 2 ? 1 : 0, idx, cnt, ws, S(stream));
+    return s == CSA2_OK ? ok() : s;
+}
+
+csa2_status csa2_index_topk_noalloc(int B, int Tq, const int32_t* q_pos0,
+                                    const int32_t* n_entries, const uint16_t* qI,
+                                    const float* wI, const uint8_t* ki_codes,
+                                    const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                                    int32_t* idx, int32_t* cnt, void* stream) {
+    if (bad_sizes(B, Tq, entry_stride)) return fail(CSA2_ERR_SHAPE, "index_topk_noalloc: B=%d Tq=%d stride=%lld", B, Tq, (long long)entry_stride);
+    if (bad_ratio(ratio)) return fail(CSA2_ERR_UNSUPPORTED, "index_topk_noalloc: ratio=%d (need 1 or 2)", ratio);
+    if (Tq == 0) return ok();     // no work: no pointer is read
+    if (!q_pos0 || !n_entries || !qI || !wI || !ki_codes || !ki_scales || !idx || !cnt)
+        return fail(CSA2_ERR_NULL, "index_topk_noalloc: a required pointer is NULL");
+    const size_t need = index_topk_ws(B, Tq, entry_stride);
+    if (need > CSA2_NOALLOC_SCRATCH_BYTES)
+        return fail(CSA2_ERR_WORKSPACE, "index_topk_noalloc: these sizes need %zu bytes of scratch, "
+                    "more than the library's %zu", need, (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+    void* ws = scratch_ptr();
+    if (ws == nullptr) return CSA2_ERR_HIP;
     csa2_status s = launch_index(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales,
                                  entry_stride, ratio == 2 ? 1 : 0, idx, cnt, ws, S(stream));
     return s == CSA2_OK ? ok() : s;

@@ -190,6 +190,26 @@ csa2_status csa2_index_topk(int B, int Tq, const int32_t* q_pos0, const int32_t*
                             void* stream);
 
 /*
+ * csa2_index_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * csa2_index_topk; its scratch is one array of CSA2_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends (its address is
+ * looked up once per device, with that device current, on the first call).
+ * Sizes whose workspace (csa2_workspace_size(CSA2_OP_INDEX_TOPK, ...)) exceeds
+ * it return CSA2_ERR_WORKSPACE.  Every call on a GPU uses that GPU's one array
+ * and leaves its contents behind: two calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results; calls ordered on one
+ * stream are safe.  The current device must be the one `stream` belongs to.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+csa2_status csa2_index_topk_noalloc(int B, int Tq, const int32_t* q_pos0,
+                                    const int32_t* n_entries, const uint16_t* qI,
+                                    const float* wI, const uint8_t* ki_codes,
+                                    const uint8_t* ki_scales, int64_t entry_stride, int ratio,
+                                    int32_t* idx, int32_t* cnt, void* stream);
+
+/*
  * Full-layer selection plus the hierarchical candidate pool [blog: the
  * Hierarchical Sparse Indexer paragraph; zharf: section "Hierarchical indexing
  * bounds the later searches"].  idx and cnt exactly as csa2_index_topk.  From
