@@ -124,23 +124,79 @@ def stage_times(run, steps: int, stream):
     return out
 
 
+def host_cpu():
+    """host CPU model and the cores this process may use"""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
 def cpu_baseline_prefill(wl, n_rows: int):
-    """the oracle on a bounded sample: all compression + n_rows query rows spread over T"""
+    """the oracle on a bounded sample: all compression + n_rows query rows spread
+    over T, once on one thread (Oracle-1) and once on all usable cores (Oracle-N:
+    the same single-threaded routine on disjoint rows; the C oracle releases the
+    interpreter lock inside each call and keeps no shared state)"""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle.reference import PrefillReference
+    model, nproc, usable = host_cpu()
     t0 = time.perf_counter()
     ref = PrefillReference(wl)
     t_compress = time.perf_counter() - t0
+    ref.window_full()
     rows = np.linspace(0, wl.Tq - 1, n_rows).astype(np.int64)
     t1 = time.perf_counter()
     for t in rows:
         ref.rows([t])
     t_rows = time.perf_counter() - t1
-    per_token = t_compress / wl.Tq + t_rows / n_rows
-    return {"value": 1.0 / per_token, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"full compression of {wl.Tq} positions ({t_compress:.1f} s) + {n_rows} "
-                      f"query rows evenly spaced over t=0..{wl.Tq - 1} ({t_rows:.1f} s), "
-                      f"single-threaded C oracle, rate = 1 / (compress s/token + row s/row)"}
+    per_token_1 = t_compress / wl.Tq + t_rows / n_rows
+    nthr = max(1, min(16, usable))
+    # Oracle-N: compression in nthr chunks of positions, then the rows, each on
+    # nthr threads (every call its own outputs)
+    import oracle
+    import csa2_synth as synth
+    derive = wl.keys == "derive"
+    kc, gc = wl.kc(), (wl.gc() if wl.ratio == 2 else None)
+    kig = None if derive else wl.ki_given()
+    cos_t, sin_t = synth.rope_table(wl.rope_rows)
+    step = -(-wl.Tq // nthr // 2) * 2
+    spans = [(p, min(wl.Tq, p + step)) for p in range(0, wl.Tq, step)]
+    r = wl.ratio
+
+    def comp(span):
+        p0, p1 = span
+        oracle.compress(kc[:, p0:p1], None if gc is None else gc[:, p0:p1], wl.gamma_c(),
+                        wl.w_ik() if derive else None, wl.gamma_ik(),
+                        None if kig is None else kig[:, p0 // r:p1 // r], cos_t, sin_t,
+                        entry_stride=wl.Tq // r, pos0=p0, ratio=r, z_format=wl.z_format)
+    t2 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(comp, spans))
+    t_compress_n = time.perf_counter() - t2
+    t3 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(lambda t: ref.rows([t]), rows))
+    t_rows_n = time.perf_counter() - t3
+    per_token_n = t_compress_n / wl.Tq + t_rows_n / n_rows
+    return {"value": 1.0 / per_token_n, "unit": "query-tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"full compression of {wl.Tq} positions + {n_rows} query rows evenly spaced "
+                      f"over t=0..{wl.Tq - 1}; the single-threaded C oracle on {nthr} threads "
+                      f"over disjoint position chunks ({t_compress_n:.2f} s) and rows "
+                      f"({t_rows_n:.2f} s); rate = 1 / (compress s/token + row s/row), the rows' "
+                      "mean time standing for all 65,536 rows",
+            "host_cpu": model, "nproc": nproc, "usable_cores": usable,
+            "oracle_1": {"value": 1.0 / per_token_1, "unit": "query-tokens/s", "cores": 1,
+                         "seconds": {"compress": t_compress, "rows": t_rows}}}
 
 
 def main():
@@ -151,11 +207,13 @@ def main():
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: 65536)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "pool", "decode1", "decode1z", "pool1",
-                                       "copy"], default=None,
+                                       "copy", "read", "verify", "prefill8k"], default=None,
                     help="time a single workload (for profiling runs); 'copy' runs a plain "
                          "1 GiB device copy, the calibration kernel for the HBM byte counters; "
                          "decode1 / pool1 are the ratio-1 forms, decode1z the ratio-1 form with "
-                         "the pages' 288-byte rows")
+                         "the pages' 288-byte rows; 'read' a read-only streaming kernel over 2 GiB "
+                         "(the ceiling a scan can reach); verify / prefill8k the verify-decode and "
+                         "8,192-token prefill workloads alone")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
     args = ap.parse_args()
@@ -182,6 +240,14 @@ def main():
         ms = time_events(lambda: dst.copy_(src), args.steps, stream)
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
                           "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+        return
+    if args.only == "read":
+        result["read"] = read_ceiling(args, stream)
+        print(json.dumps(result), flush=True)
+        return
+    if args.only in ("verify", "prefill8k"):
+        (run_verify if args.only == "verify" else run_prefill_small)(args, result, stream)
+        print(json.dumps(result), flush=True)
         return
     wl = synth.workload(2, T=args.T) if args.T != 8192 else synth.workload(1)
     if args.only in ("decode", "pool", "decode1", "pool1", "decode1z"):
@@ -212,39 +278,48 @@ def main():
     log(f"stages (ms): {json.dumps({k: round(v, 4) for k, v in stages.items()})}")
     flop_idx, flop_att = prefill_work(wl.Tq, wl.H)
     t_att = stages["sparse_attn"] * 1e-3
-    t_idx = stages["index_scores"] * 1e-3
-    if t_att >= t_idx:
-        dom = {"kernel": "k_attn (csa2_sparse_attn: gather, dequant, bf16 MFMA QK^T/PV, sink "
-                         "softmax, inverse rotation)", "bound": "mfma", "achieved":
-               flop_att / t_att / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-               "flop_per_launch": flop_att}
-    else:
-        dom = {"kernel": "k_index_scores (csa2_index_scores: q^I FP8 pre-pass + FP8xFP4 MFMA "
-                         "scores)", "bound": "mfma", "achieved": flop_idx / t_idx / 1e12,
-               "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s", "flop_per_launch": flop_idx}
-    dom["frac"] = dom["achieved"] / dom["peak"]
-    dom["traffic"] = measured_traffic("k_attn" if t_att >= t_idx else "k_index_scores", "prefill",
-                                      wl.Tq)
+    t_sel = stages["index_topk"] * 1e-3
+    att = {"kernel": "k_attn (csa2_sparse_attn launches it alone at this size: gather, QK on "
+                     "the stored FP4/FP8 rows, sink softmax, bf16 PV, inverse rotation)",
+           "bound": "mfma", "achieved": flop_att / t_att / 1e12, "peak": PEAK_BF16 / 1e12,
+           "unit": "TFLOP/s", "flop_per_launch": flop_att,
+           "traffic": measured_traffic("k_attn", "prefill", wl.Tq)}
+    sel = {"kernel": "k_index_select (csa2_index_topk: the q^I E4M3 pass, then scores and the "
+                     "streaming top-512 in one kernel; no score row in memory)",
+           "bound": "mfma", "achieved": flop_idx / t_sel / 1e12, "peak": PEAK_FP8 / 1e12,
+           "unit": "TFLOP/s", "flop_per_launch": flop_idx,
+           "traffic": measured_traffic("k_index_select", "prefill", wl.Tq)}
+    for d in (att, sel):
+        d["frac"] = d["achieved"] / d["peak"]
+    dom, other = (att, sel) if t_att >= t_sel else (sel, att)
     value = wl.Tq / (ms * 1e-3)
     mixed_time = flop_idx / PEAK_FP8 + flop_att / PEAK_BF16
     result.update({
         "metric": "CSA2 query-tokens/s (prefill T=64K; decode B=128@128K) + % of MFMA/HBM roofline",
         "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8xfp4 indexer + bf16 attention",
+        "vs_baseline": None,
+        "dtype": "indexer: fp8 (E4M3 query) x fp4 (E2M1 key) MFMA; attention: QK as a two-term "
+                 "E4M3 query on the scaled fp8/fp4 MFMA against the stored rows, PV bf16 MFMA; "
+                 "fp32 accumulation and softmax",
         "data": "synthetic (seeded; shapes and distributions of the workload description)",
         "config": {"workload": f"CSA2 prefill B=1 T={wl.Tq} H={wl.H} d=512 window 128 "
                                f"top-512, {wl.Tq // 2} compressed entries, clustered index keys",
                    "global_batch": 1, "seq_len": wl.Tq, "parallelism": "none (1 GPU)"},
         "roofline": dom,
+        "roofline_other": other,
         "stages_ms": stages,
         "mixed_roofline_frac": mixed_time / (ms * 1e-3),
         "fp8_peak_frac_literal": (flop_idx + flop_att) / (ms * 1e-3) / PEAK_FP8,
     })
     del run
     torch.cuda.empty_cache()
+    if args.only is None and args.T == 65536:
+        run_prefill_small(args, result, stream)
     if not args.no_decode and args.only is None:
+        result["read_ceiling"] = read_ceiling(args, stream)
         run_decode(args, result, stream)
+        run_verify(args, result, stream)
         run_pool(args, result, stream)
         run_decode(args, result, stream, ratio=1)
         run_decode(args, result, stream, ratio=1, z_format=1)
@@ -255,6 +330,98 @@ def main():
         log(f"timing the CPU oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def read_ceiling(args, stream):
+    """HBM read bandwidth of a plain streaming read over 2 GiB (libcsa2calib.so)"""
+    import ctypes
+    import torch
+    from compressed_sparse_attention_csa2_amd import _build
+    if not os.path.exists(_build.CALIB):
+        raise RuntimeError(f"{_build.CALIB} is missing: run __graft_entry__.build() first")
+    L = ctypes.CDLL(_build.CALIB)
+    L.csa2_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    n = 2 << 30
+    buf = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    best = None
+    for blocks in (2048, 4096, 8192):
+        f = lambda: L.csa2_calib_read(buf.data_ptr(), n, sink.data_ptr(), blocks, sp)
+        assert f() == 0
+        ms = time_events(f, max(args.steps, 10), stream)
+        gbs = n / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["GB/s"]:
+            best = {"GB/s": gbs, "bytes": n, "ms": ms, "blocks": blocks}
+    del buf
+    torch.cuda.empty_cache()
+    best["frac_of_8TBps"] = best["GB/s"] * 1e9 / PEAK_HBM
+    log(f"read ceiling: {best['GB/s']:.0f} GB/s ({best['blocks']} blocks)")
+    return best
+
+
+def run_prefill_small(args, result, stream):
+    """The 8,192-token prefill (workload 1) as one csa2_forward per step."""
+    import torch
+    import csa2_harness
+    import csa2_synth as synth
+    wl = synth.workload(1)
+    log(f"generating inputs: {wl.name}")
+    run = csa2_harness.PrefillRun(wl)
+    for _ in range(args.warmup):
+        run.forward()
+    torch.cuda.synchronize()
+    ms = time_events(run.forward, args.steps, stream)
+    st = stage_times(run, args.steps, stream)
+    flop_idx, flop_att = prefill_work(wl.Tq, wl.H)
+    mixed = flop_idx / PEAK_FP8 + flop_att / PEAK_BF16
+    log(f"prefill T={wl.Tq}: {ms:.3f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in st.items()})}")
+    result["prefill_T8192"] = {
+        "workload": f"CSA2 prefill B=1 T={wl.Tq} H={wl.H}, {wl.Tq // 2} compressed entries, "
+                    "clustered index keys",
+        "value": wl.Tq / (ms * 1e-3), "unit": "query-tokens/s", "ms_per_step": ms,
+        "stages_ms": st, "mixed_roofline_frac": mixed / (ms * 1e-3),
+        "attention_bf16_frac": flop_att / (st["sparse_attn"] * 1e-3) / PEAK_BF16}
+    del run
+    torch.cuda.empty_cache()
+
+
+def run_verify(args, result, stream):
+    """The speculative-verify decode (workload 4: B=16 x 6 queries over 524,288 entries)
+    as one csa2_forward per step; near the ridge, so both fractions are given: the
+    step's time at the MFMA peaks (FP8 indexer + BF16 attention) and at the HBM peak
+    (index-key scan + gathered rows + Q/O + window), each over the measured time."""
+    import torch
+    import csa2_harness
+    import csa2_synth as synth
+    wl = synth.workload(4)
+    log(f"generating caches: {wl.name}")
+    t0 = time.time()
+    run = csa2_harness.DecodeRun(wl)
+    log(f"caches resident ({time.time() - t0:.1f} s)")
+    for _ in range(args.warmup):
+        run.forward()
+    torch.cuda.synchronize()
+    ms = time_events(run.forward, args.steps, stream)
+    st = stage_times(run, args.steps, stream)
+    rows = wl.B * wl.Tq
+    pairs = wl.B * sum(min((wl.q_pos0 + t + 1) // 2, wl.n_entries) for t in range(wl.Tq))
+    flop_idx = 8192.0 * pairs
+    flop_att = 4.0 * 512 * wl.H * rows * 640
+    t_mfma = flop_idx / PEAK_FP8 + flop_att / PEAK_BF16
+    nbytes = decode_bytes(wl.B, wl.Tq, wl.n_entries, wl.H)
+    log(f"verify decode: {ms:.4f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in st.items()})}")
+    result["verify_decode"] = {
+        "workload": "CSA2 speculative-verify decode B=16 x 6 queries at 1048570..1048575, "
+                    "524,288 FP4 entries per request (log-normal key norms, 1% exact duplicates), "
+                    "window 133, H=64, top-512",
+        "value": rows / (ms * 1e-3), "unit": "query-tokens/s", "ms_per_step": ms,
+        "stages_ms": st, "flop": {"indexer_fp8": flop_idx, "attention": flop_att},
+        "mfma_roofline_frac": t_mfma / (ms * 1e-3), "hbm_bytes": nbytes,
+        "hbm_roofline_frac": nbytes / (ms * 1e-3) / PEAK_HBM}
+    del run
+    torch.cuda.empty_cache()
 
 
 def run_decode(args, result, stream, ratio=2, z_format=0):
@@ -302,6 +469,11 @@ def run_decode(args, result, stream, ratio=2, z_format=0):
                          "traffic": measured_traffic("k_index_scores", "decode",
                                                      dwl.q_pos0 + 1) if ratio == 2 else None},
         }
+        if "read_ceiling" in result:
+            rc = result["read_ceiling"]["GB/s"] * 1e9
+            result[key]["roofline"]["frac_of_read_ceiling"] = (
+                scan_bytes / (dstages["index_scores"] * 1e-3) / rc)
+            result[key]["hbm_frac_step_of_read_ceiling"] = nbytes / (dms * 1e-3) / rc
         # attention's own traffic: the selected rows, the window rows, Q and O
         zrow = 288.0 if z_format else 272.0
         att_bytes = dwl.B * dwl.Tq * (512 * zrow + 128 * 516 + 2 * dwl.H * 512 * 2)

@@ -33,6 +33,23 @@ def hipcc() -> str:
     return "hipcc"
 
 
+CALIB = os.path.join(HERE, "libcsa2calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """the read-only streaming kernel the benchmark calibrates the decode scan with"""
+    tmp = CALIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, "calib.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libcsa2calib.so")
+    os.replace(tmp, CALIB)
+    return CALIB
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
@@ -55,3 +72,4 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_calib(verbose=True))
