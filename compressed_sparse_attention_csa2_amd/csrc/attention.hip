@@ -8,30 +8,41 @@
 // that looks at 640 places": 64 query heads share one key-value vector per
 // place, and each head has a sink.
 //
-// Persistent blocks of 8 waves, one per compute unit, walk the (query token,
+// Persistent blocks of 12 waves, one per compute unit, walk the (query token,
 // split of its rows) units.  The rows of a unit are taken 32 at a time
 // ("chunks"; window rows and compressed rows never share a chunk, and each
 // kind has its own compiled QK body).  Waves 0..3 ("QK waves", head group q)
-// and waves 4..7 ("PV waves", channel quarter p) share the SIMDs pairwise and
-// work one chunk apart; one block barrier B(k) per chunk:
-//   QK wave  stages rows: direct-to-LDS copies three chunks ahead (four raw
-//            buffers, swizzled by 16-byte unit); computes S for its 16 heads x
-//            32 rows with the block-scaled MFMA 16x16x128 (A = the raw row
-//            codes, FP4 with their own block scales or FP8; B = the query as
-//            two E4M3 terms hi + lo with an E8M0 scale per 128 channels, which
-//            together reproduce the bf16 query up to the smallest elements of
-//            a block); then the online softmax in log2 units with a wave-local
-//            running maximum that only moves when a chunk exceeds it by more
-//            than 2^32; P (bf16, [head][row]) and the row correction go to LDS.
-//   PV wave  PV(k-1): O^T[128p.., heads] += G^T P^T with bf16 MFMA 16x16x32,
-//            G^T read with the transposing LDS load (ds_read_b64_tr_b16) from
-//            its own bf16 copy of the rows; then that copy of chunk k
-//            (dequantised from the raw codes, channels 128p..128p+127).
-// Between units the PV waves normalise and write the finished unit (staged in
-// LDS, written as contiguous 256-byte head segments) while the QK waves load,
-// stage and convert the next one.  Window rows enter as E4M3 codes; their fp32
-// row scale multiplies the logit and is folded into P.  Splits of a token's
-// chunk range write (m, l, unnormalised O) partials that k_attn_combine merges.
+// and waves 4..11 ("PV waves", channel eighth p) share the SIMDs (one QK wave
+// and two PV waves each) and work one chunk apart; one block barrier B(k) per
+// chunk:
+//   QK wave  computes S for its 16 heads x 32 rows of chunk k with the
+//            block-scaled MFMA 16x16x128 (A = the raw row codes, FP4 with their
+//            own block scales or FP8; B = the query as two E4M3 terms hi + lo
+//            with an E8M0 scale per 128 channels, which together reproduce the
+//            bf16 query up to the smallest elements of a block); then the
+//            online softmax in log2 units with a wave-local running maximum
+//            that only moves when a chunk exceeds it by more than 2^32; P (bf16,
+//            [head][row]), the row corrections and a "some maximum moved" flag
+//            go to LDS.
+//   PV wave  copies rows four chunks ahead (direct-to-LDS into five raw
+//            buffers, swizzled by 16-byte unit); PV(k-1): O^T[64p.., heads] +=
+//            G^T P^T with bf16 MFMA 16x16x32 on the operand converted in phase
+//            k-1 (rescaled first only when a flag is set); then converts chunk
+//            k: a 4-bit (FP4 rows) or 8-bit (FP8 rows) transposing LDS load hands
+//            each lane one channel's values of 8 rows (the MFMA's A operand
+//            layout) straight from the staged bytes, and the lane converts them
+//            to bf16 -- FP4 with each row's own E8M0 block scale (exact, from a
+//            per-wave fp32 scale table), FP8 unscaled (the row's fp32 scale is
+//            already in P).  No bf16 copy of the rows is made.
+// A unit's entries, rotary row, first window chunks and query are fetched
+// while the previous unit is finished; its scalars come from LDS, copied 64
+// units at a time.  At the end of a unit the QK waves normalise (sink
+// included) and write the row's log-sum-exp; the PV waves write the unit's
+// output during the next unit's first chunk (staged in LDS one head tile at a
+// time, written as contiguous 128-byte head segments).  Window rows enter as
+// E4M3 codes; their fp32 row scale multiplies the logit and is folded into P.
+// Splits of a token's chunk range write (m, l, unnormalised O) partials that
+// k_attn_combine merges.
 #include <type_traits>
 
 #include "csa2_device.h"
@@ -46,7 +57,9 @@ typedef __attribute__((ext_vector_type(4))) short s4;
 typedef __attribute__((address_space(3))) s4 lds_s4;
 typedef __attribute__((ext_vector_type(2))) short s2v;
 
-constexpr int NRAW = 4;                // raw staging buffers (chunks in flight)
+// raw staging buffers: chunk k is copied four chunks ahead and read in phase
+// k by the QK waves (products) and the PV waves (conversion), so five are in use
+constexpr int NRAW = 5;
 
 // Direct-to-LDS copies: every active lane copies 16 (4) bytes from a
 // wave-uniform base plus its own 32-bit byte offset to lds + 16 (4) * lane;
@@ -86,12 +99,13 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// bf16 copy of a chunk, [row][512]: 16-byte unit u of row r sits at u ^ gb_swz(r).
-// Conflict-free for the transposing reads (16 rows x 32 bytes per read, two
-// half-waves of 8 rows) and for the dequantising writes (16 rows, one unit).
-__device__ __forceinline__ int gb_swz(int r) {
-    return (((r & 3) | ((r >> 1) & 4)) << 1) | ((r >> 2) & 1);
+// the two E2M1 codes of byte SEL of w, times sc, as packed bf16 (low nibble first)
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float sc) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, SEL));
 }
+typedef __attribute__((ext_vector_type(2))) int v2i;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 // P [head][32 rows] bf16, 64 bytes per head: unit u at u ^ ((h >> 2) & 3)
 __device__ __forceinline__ int pb_off(int h, int u) { return h * 64 + ((u ^ ((h >> 2) & 3)) << 4); }
 
@@ -108,20 +122,23 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     __shared__ __attribute__((aligned(16))) uint8_t rawc[NRAW][CH * 512];
     __shared__ __attribute__((aligned(16))) uint32_t zsc[NRAW][CH][4];
     __shared__ __attribute__((aligned(16))) float rscl[NRAW][CH];
-    __shared__ __attribute__((aligned(16))) uint16_t Gb[2][CH * D];
     __shared__ __attribute__((aligned(16))) uint16_t Pb[2][64 * CH];
     __shared__ __attribute__((aligned(16))) float corb[2][16][4];   // [n16][head tile]
-    __shared__ float mfin[64], lfin[64];
+    __shared__ __attribute__((aligned(16))) uint32_t cflag[2][4];   // QK wave q moved a maximum
+    __shared__ __attribute__((aligned(16))) float sfw[8][2][CH];    // PV wave's block scales [block][row]
+    __shared__ float mfin[2][64], lfin[2][64], finf[2][64];   // [unit parity][head]
+    __shared__ __attribute__((aligned(16))) uint8_t Ost[8][16 * 128];   // PV wave's output staging
     __shared__ int32_t sidx[TOPK];
     __shared__ float sinkl[64];               // sink of head h
     __shared__ float ropel[2][2][PAIRS];      // [unit parity][cos, sin] of the token's position
+    __shared__ int32_t uinfo[2][3][64];       // [batch parity][cnt, q_pos0, win_floor][unit]
 
     const int tid = threadIdx.x;
     int lane = tid & 63;            // re-derived opaquely per QK chunk (see there)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     // roles: waves 0..3 stage the rows and take QK and the softmax for heads
-    // 16q..16q+15 (q = wave); waves 4..11 take the bf16 copy and PV for channels
+    // 16q..16q+15 (q = wave); waves 4..11 take the conversion and PV for channels
     // 64p..64p+63 (p = wave - 4).  Each SIMD holds one QK wave and two PV waves.
     const bool qk_wave = wave < 4;
     const int q4 = wave & 3;
@@ -134,30 +151,36 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     // The block walks its units (query row, split) in the order unit_at gives.
     // Per unit both roles pass the same barriers: start, one per chunk, final.
     // Between final(u) and start(u + 1) the PV waves write unit u's output while
-    // the QK waves load, stage and convert unit u + 1.
+    // the QK waves convert the query of unit u + 1 (its rows, entries and
+    // query were fetched during unit u).  A unit's three scalars from global
+    // memory (its entry count, its request's first position and window floor)
+    // come from LDS, copied 64 units at a time, so that no barrier waits on a
+    // scalar load.
     struct Unit {
         int row, split, b, t, nwin, slot0, ncmp, nwch, k_begin, k_end;
         int64_t p, prow;
     };
-    auto unit_of = [&](int u) {
+    // u = unit_at(i): the block's i-th unit
+    auto unit_of = [&](int u, int i) {
+        const int32_t* inf = &uinfo[(i >> 6) & 1][0][i & 63];
         Unit U;
         U.row = u / nsplit;
         U.split = u - U.row * nsplit;
         U.b = U.row / Tq;
         U.t = U.row - U.b * Tq;
-        int64_t p = (int64_t)q_pos0[U.b] + U.t;
+        int64_t p = (int64_t)inf[64] + U.t;
         if (p < 0) p = 0;
         U.p = p;
         U.prow = p < rope_rows ? p : rope_rows - 1;
         int64_t w0 = p - (WINDOW - 1) > 0 ? p - (WINDOW - 1) : 0;
         if (win_floor) {     // bounded replay: the window starts no earlier than s (s <= p)
-            int64_t fl = win_floor[U.b];
+            int64_t fl = inf[128];
             fl = fl > p ? p : fl;
             w0 = w0 > fl ? w0 : fl;
         }
         U.nwin = (int)(p - w0 + 1);
         U.slot0 = (int)(w0 % cap);
-        int nc = cnt[U.row];
+        int nc = inf[0];
         U.ncmp = nc < 0 ? 0 : (nc > TOPK ? TOPK : nc);
         U.nwch = (U.nwin + CH - 1) / CH;
         const int nch = U.nwch + (U.ncmp + CH - 1) / CH;
@@ -176,78 +199,120 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     auto unit_at = [&](int i) -> int {
         return xcd_order ? ((i * 8 + xcd) * G8 + slot) : (int)blockIdx.x + i * G;
     };
+    // wave 0: the scalars of the block's units i0 .. i0 + 63 (past the end: row 0's)
+    auto info_issue = [&](int i0) {
+        const int par = (i0 >> 6) & 1;
+        const int uu = unit_at(i0 + lane);
+        const int row = uu < nunits ? uu / nsplit : 0;
+        const int b = row / Tq;
+        dma4s(cnt, 4u * (uint32_t)row, lds_addr(&uinfo[par][0][0]));
+        dma4s(q_pos0, 4u * (uint32_t)b, lds_addr(&uinfo[par][1][0]));
+        if (win_floor) dma4s(win_floor, 4u * (uint32_t)b, lds_addr(&uinfo[par][2][0]));
+    };
+    if (wave == 0) {
+        info_issue(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    barrier_lds();
 
     if (qk_wave) {
         // ======================= QK waves ==================================
         const int h = 16 * q4 + n16;
         const uint32_t sel_g = 0x0c0c0400u + 0x00000101u * (uint32_t)g;
+        // bf16 query of head h for a unit: lane group g's 16-channel pieces of
+        // every 64 channels (block m, half s2), all sixteen loads in flight at once
+        // (a wave with no heads reads head H - 1 and discards it).  Issued
+        // unconditionally, so the registers hold nothing across the chunk loop.
+        uint4 qraw[4][4];
+        auto q_issue = [&](int b, int t) {
+            const int hq = h < H ? h : H - 1;
+            const uint16_t* qrow = Q + (((int64_t)b * H + hq) * Tq + t) * D;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const uint16_t* src = qrow + 128 * m + 64 * s2 + 16 * g;
+                    qraw[m][2 * s2] = *(const uint4*)src;
+                    qraw[m][2 * s2 + 1] = *(const uint4*)(src + 8);
+                }
+        };
+        // ---- staging: direct-to-LDS copies of a chunk into a raw buffer.
+        // QK wave q copies rows 8q..8q+7.  Rows past the chunk's end copy the
+        // chunk's first row (finite values; their logits are masked).
+        // Compressed rows are 256 bytes apart, window rows 512; lane j of a
+        // row copies 16-byte unit j ^ (row & 15) of it to unit j, so the
+        // row's unit u sits at u ^ (row & 15).  Source offsets are 32-bit,
+        // relative to the request's cache base (sizes are checked for that).
+        auto stage_win = [&](const Unit& V, int k, int buf) {
+            const uint8_t* wrow0 = w_codes + (int64_t)V.b * cap * D;
+            const float* wsc = w_scale + (int64_t)V.b * cap;
+            const int base = k * CH;
+            const int nv = min(V.nwin - base, CH);
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2) {
+                const int rr = 8 * q4 + 2 * h2 + (lane >> 5), j = lane & 31;
+                int slot = V.slot0 + base + (rr < nv ? rr : 0);
+                slot = slot >= cap ? slot - cap : slot;
+                dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(j ^ (rr & 15)),
+                       lds_addr(&rawc[buf][(8 * q4 + 2 * h2) * 512]));
+            }
+            if (wave == 0 && lane < CH) {
+                int slot = V.slot0 + base + (lane < nv ? lane : 0);
+                slot = slot >= cap ? slot - cap : slot;
+                dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
+            }
+        };
+        // Everything unit V needs before its first chunk, issued while the
+        // previous unit is still being finished: its 512 selected entries (every
+        // QK wave copies all of them: the same values, and each wave waits only
+        // for its own copy), its rotary row, the window chunks among its first
+        // four (raw buffers rb, rb + 1, ..); then its query, whose loads are
+        // the youngest, so waiting for them (the compiler does, before
+        // converting) also completes the copies.
+        auto prefetch = [&](const Unit& V, int rb, int vp) {
+            const int32_t* irow = idx + (int64_t)V.row * TOPK;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                dma4s(irow, 4u * (uint32_t)(64 * j + lane), lds_addr(&sidx[64 * j]));
+            if (wave == 1 && lane < PAIRS) dma4s(rcos + V.prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[vp][0][0]));
+            if (wave == 2 && lane < PAIRS) dma4s(rsin + V.prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[vp][1][0]));
+            const int kw4 = min(min(V.k_begin + 4, V.nwch), V.k_end);
+            for (int k = V.k_begin; k < kw4; ++k) stage_win(V, k, (rb + k - V.k_begin) % NRAW);
+        };
+        int rb0 = 0;                    // raw buffer of the unit's first chunk
+        if (unit_at(0) < nunits) {
+            const Unit U0 = unit_of(unit_at(0), 0);
+            prefetch(U0, 0, 0);
+            q_issue(U0.b, U0.t);
+        }
         for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
-            const Unit U = unit_of(u);
+            const Unit U = unit_of(u, i);
             const int k_begin = U.k_begin, k_end = U.k_end, nwch = U.nwch, nwin = U.nwin;
-            const int ncmp = U.ncmp, slot0 = U.slot0;
-            const uint8_t* wrow0 = w_codes + (int64_t)U.b * cap * D;
-            const float* wsc = w_scale + (int64_t)U.b * cap;
+            const int ncmp = U.ncmp;
+            // the next 64 units' scalars (the other half of uinfo, last read for
+            // units i - 64 .. i - 1), complete before start(u)
+            const bool info = wave == 0 && (i & 63) == 0 && unit_at(i + 64) < nunits;
+            if (info) info_issue(i + 64);
+            const int nch = k_end > k_begin ? k_end - k_begin : 0;
             const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * 256;
             const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * 16;
-
-            // ---- the row's 512 selected entries (every QK wave copies all of
-            // them: the same values, and each wave waits only for its own copy)
-            // and the rotary row
-            {
-                const int32_t* irow = idx + (int64_t)U.row * TOPK;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    dma4s(irow, 4u * (uint32_t)(64 * j + lane), lds_addr(&sidx[64 * j]));
-                if (wave == 1 && lane < PAIRS) dma4s(rcos + U.prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[up][0][0]));
-                if (wave == 2 && lane < PAIRS) dma4s(rsin + U.prow * PAIRS, 4u * (uint32_t)lane, lds_addr(&ropel[up][1][0]));
-            }
-            // ---- staging: direct-to-LDS copies of chunk k into raw buffer k % NRAW
-            // QK wave q copies rows 8q..8q+7.  Rows past the chunk's end copy the
-            // chunk's first row (finite values; their logits are masked).
-            // Compressed rows are 256 bytes apart, window rows 512; lane j of a
-            // row copies 16-byte unit j ^ (row & 15) of it to unit j, so the
-            // row's unit u sits at u ^ (row & 15).  Source offsets are 32-bit,
-            // relative to the request's cache base (sizes are checked for that).
-            auto chunk_entries = [&](int k, int& e0, int& e1, int& e2) {
-                if (k >= k_end || k < nwch) return;
+            auto bufi = [&](int k) { return (rb0 + k - k_begin) % NRAW; };
+            // compressed chunk k (k < k_end) of this unit
+            auto stage_cmp = [&](int k) {
+                const int buf = bufi(k);
                 const int base = (k - nwch) * CH;
                 const int nv = min(ncmp - base, CH);
                 const int ra = 8 * q4 + (lane >> 4), rb = ra + 4;
-                e0 = min(max(sidx[base + (ra < nv ? ra : 0)], 0), emax);
-                e1 = min(max(sidx[base + (rb < nv ? rb : 0)], 0), emax);
-                e2 = min(max(sidx[base + ((lane & 31) < nv ? (lane & 31) : 0)], 0), emax);
+                const int e0 = min(max(sidx[base + (ra < nv ? ra : 0)], 0), emax);
+                const int e1 = min(max(sidx[base + (rb < nv ? rb : 0)], 0), emax);
+                const int e2 = min(max(sidx[base + ((lane & 31) < nv ? (lane & 31) : 0)], 0), emax);
+                const int j = lane & 15;
+                dma16s(zc0, (uint32_t)e0 * 256u + 16u * (uint32_t)(j ^ (ra & 15)),
+                       lds_addr(&rawc[buf][8 * q4 * 256]));
+                dma16s(zc0, (uint32_t)e1 * 256u + 16u * (uint32_t)(j ^ (rb & 15)),
+                       lds_addr(&rawc[buf][(8 * q4 + 4) * 256]));
+                if (wave == 0 && lane < CH) dma16s(zs0, (uint32_t)e2 * 16u, lds_addr(&zsc[buf][0][0]));
             };
-            auto dma_chunk = [&](int k, bool have, int e0, int e1, int e2) {
-                if (k >= k_end) return;
-                const int buf = k % NRAW;
-                if (k < nwch) {
-                    const int base = k * CH;
-                    const int nv = min(nwin - base, CH);
-#pragma unroll
-                    for (int h2 = 0; h2 < 4; ++h2) {
-                        const int rr = 8 * q4 + 2 * h2 + (lane >> 5), j = lane & 31;
-                        int slot = slot0 + base + (rr < nv ? rr : 0);
-                        slot = slot >= cap ? slot - cap : slot;
-                        dma16s(wrow0, (uint32_t)slot * D + 16u * (uint32_t)(j ^ (rr & 15)),
-                               lds_addr(&rawc[buf][(8 * q4 + 2 * h2) * 512]));
-                    }
-                    if (wave == 0 && lane < CH) {
-                        int slot = slot0 + base + (lane < nv ? lane : 0);
-                        slot = slot >= cap ? slot - cap : slot;
-                        dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
-                    }
-                } else {
-                    if (!have) chunk_entries(k, e0, e1, e2);
-                    const int ra = 8 * q4 + (lane >> 4), j = lane & 15;
-                    dma16s(zc0, (uint32_t)e0 * 256u + 16u * (uint32_t)(j ^ (ra & 15)),
-                           lds_addr(&rawc[buf][8 * q4 * 256]));
-                    dma16s(zc0, (uint32_t)e1 * 256u + 16u * (uint32_t)(j ^ ((ra + 4) & 15)),
-                           lds_addr(&rawc[buf][(8 * q4 + 4) * 256]));
-                    if (wave == 0 && lane < CH) dma16s(zs0, (uint32_t)e2 * 16u, lds_addr(&zsc[buf][0][0]));
-                }
-            };
-            // window chunks among the first three need nothing else: start them now
-            for (int k = k_begin; k < k_begin + 3 && k < nwch; ++k) dma_chunk(k, false, 0, 0, 0);
 
             // ---- query of heads 16q..16q+15 as two E4M3 terms ----------------
             // Lane (head 16q + n16, group g) holds, for channel block M,
@@ -261,14 +326,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             i8 qh[4], ql[4];
             uint32_t qsh = 0x7F7F7F7Fu, qsl = 0x7F7F7F7Fu;
             if (qk_on) {
-                const uint16_t* qrow = Q + (((int64_t)U.b * H + h) * Tq + U.t) * D;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     uint32_t w[16];
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
-                        const uint16_t* src = qrow + 128 * m + 64 * s2 + 16 * g;
-                        const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 8);
+                        const uint4 u0 = qraw[m][2 * s2], u1 = qraw[m][2 * s2 + 1];
                         w[8 * s2 + 0] = u0.x; w[8 * s2 + 1] = u0.y; w[8 * s2 + 2] = u0.z; w[8 * s2 + 3] = u0.w;
                         w[8 * s2 + 4] = u1.x; w[8 * s2 + 5] = u1.y; w[8 * s2 + 6] = u1.z; w[8 * s2 + 7] = u1.w;
                     }
@@ -305,14 +368,18 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     qsl = (qsl & ~(0xFFu << (8 * m))) | (bl << (8 * m));
                 }
             }
-            // this wave's copies so far (entries, rotary row, window chunks) are
-            // older than the query loads: the entries are in LDS
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            // compressed chunks among the first three (after the window ones, so
-            // copies stay in chunk order)
-            for (int k = (k_begin > nwch ? k_begin : nwch); k < k_begin + 3; ++k) dma_chunk(k, false, 0, 0, 0);
+            // compressed chunks among the first four (after the window ones, so
+            // copies stay in chunk order), once this wave's copy of the entries
+            // is in LDS
+            const int kc0 = k_begin > nwch ? k_begin : nwch, kc1 = min(k_begin + 4, k_end);
+            if (kc0 < kc1) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                for (int k = kc0; k < kc1; ++k) stage_cmp(k);
+            }
+            if (info) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             // start(u): chunk k_begin staged (n later chunks in flight: n copies)
-            if (k_begin + 2 < k_end) barrier_vm<2>();
+            if (k_begin + 3 < k_end) barrier_vm<3>();
+            else if (k_begin + 2 < k_end) barrier_vm<2>();
             else if (k_begin + 1 < k_end) barrier_vm<1>();
             else barrier_vm<0>();
 
@@ -326,7 +393,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 // offsets below (and in the copies) from being held across the loop
                 asm volatile("" : "+v"(lane));
                 const int n16 = lane & 15, g = lane >> 4;
-                const int buf = k & 1, rbuf = k % NRAW;
+                const int buf = k & 1, rbuf = bufi(k);
                 const int base = WIN ? k * CH : (k - nwch) * CH;
                 const int nv = min((WIN ? nwin : ncmp) - base, CH);
                 // lane (tile t2, row 16 t2 + n16, group g); row & 15 = n16
@@ -393,6 +460,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 asm volatile("" : "+v"(acc0), "+v"(acc1));
                 __builtin_amdgcn_s_setprio(0);
                 // ---- softmax: wave-local running maximum with headroom --------
+                uint32_t moved = 0;
                 if (qk_on) {
                     float s[8];
 #pragma unroll
@@ -429,116 +497,218 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     *(uint2*)pb1 = make_uint2(__builtin_bit_cast(uint32_t, bf2{(__bf16)pv[4], (__bf16)pv[5]}),
                                               __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[6], (__bf16)pv[7]}));
                     if (g == 0) corb[buf][n16][q4] = corr;
+                    moved = __builtin_amdgcn_ballot_w64(corr != 1.0f) != 0;
                 }
-                // B(k): P and corrections of chunk k visible; this wave's copies
-                // (the unit's first three chunks) complete
+                if (lane == 0) cflag[buf][q4] = moved;
+                // B(k): P, corrections and flags of chunk k visible; this wave's
+                // copies (the unit's first four chunks) complete
                 barrier_vm<0>();
             };
             const int kw = nwch < k_end ? nwch : k_end;
             for (int k = k_begin; k < kw; ++k) chunk(k, std::true_type{});
             for (int k = (k_begin > nwch ? k_begin : nwch); k < k_end; ++k) chunk(k, std::false_type{});
 
-            // final(u): this unit's per-head state for the PV waves
+            // the next unit's entries, rotary row, first window chunks and query
+            // are fetched while the PV waves finish this one: its chunks take the
+            // raw buffers after this unit's (the PV waves still read the last)
+            {
+                const int un = unit_at(i + 1);
+                const bool more = un < nunits;
+                const Unit N = more ? unit_of(un, i + 1) : U;
+                if (more) prefetch(N, (rb0 + nch) % NRAW, up ^ 1);
+                q_issue(N.b, N.t);      // the last unit re-reads its own query
+            }
+            // final(u): this unit's per-head state for the PV waves: running
+            // maximum and denominator (log2 units), and, for a whole row, the
+            // normalisation with the sink and the row's log-sum-exp
             const float l_tot = rows_sum(l_lane);
             if (qk_on && g == 0) {
-                mfin[h] = m_used;
-                lfin[h] = l_tot;
+                mfin[up][h] = m_used;
+                lfin[up][h] = l_tot;
+                if (nsplit == 1) {
+                    const float shv = sinkl[h] * LOG2E;
+                    const float M = fmaxf(m_used, shv);
+                    const float em = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - M);
+                    const float den = l_tot * em + __builtin_amdgcn_exp2f(shv - M);
+                    finf[up][h] = em / den;
+                    if (lse) lse[((int64_t)U.b * H + h) * Tq + U.t] = (M + log2f(den)) * 0.6931471805599453f;
+                }
             }
             barrier_lds();
+            rb0 = (rb0 + nch) % NRAW;
         }
     } else {
         // ======================= PV waves ==================================
         const int p8 = wave - 4;
+        f4 oacc[4][HT];                 // O^T tiles: [channel tile][head tile]
+        // ---- output of unit P (parity pp) -----------------------------------
+        // A unit's output is written after start of the next unit, while the QK
+        // waves take its first chunk.  Lane (head 16ht + n16, group g) holds
+        // channels 64p + 16ct + 4g..+3.  A whole row is normalised (sink
+        // included), rotated back where rotary, converted to bf16 and staged in
+        // this wave's LDS, one head tile at a time, to leave as contiguous
+        // 128-byte head segments (8 lanes per head; the 16-byte unit u of head
+        // h's segment sits at u ^ (h & 7)).  A split writes its unnormalised
+        // partial and (m, l).
+        struct Done { int b, t, row, split; };      // a unit whose output is pending
+        auto output = [&](const Done& P, int pp) {
+            uint8_t* const stage = &Ost[p8][0];
+            float rco[4][2], rsi[4][2];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const int d0 = 64 * p8 + 16 * ct + 4 * g;
+                    const int pi = d0 >= ROPE_LO ? (d0 - ROPE_LO) / 2 + q2 : 0;
+                    rco[ct][q2] = ropel[pp][0][pi];
+                    rsi[ct][q2] = ropel[pp][1][pi];
+                }
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const int hh = 16 * ht + n16;
+                if (nsplit == 1) {
+                    const float f = finf[pp][hh];
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        const int d0 = 64 * p8 + 16 * ct + 4 * g;
+                        float o[4] = {oacc[ct][ht][0] * f, oacc[ct][ht][1] * f, oacc[ct][ht][2] * f,
+                                      oacc[ct][ht][3] * f};
+                        if (d0 >= ROPE_LO) {
+#pragma unroll
+                            for (int q2 = 0; q2 < 2; ++q2) {
+                                const float co = rco[ct][q2], si = rsi[ct][q2];
+                                const float x0 = o[2 * q2], x1 = o[2 * q2 + 1];
+                                o[2 * q2] = x0 * co + x1 * si;
+                                o[2 * q2 + 1] = x1 * co - x0 * si;
+                            }
+                        }
+                        const uint32_t w0v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[0], (__bf16)o[1]});
+                        const uint32_t w1v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[2], (__bf16)o[3]});
+                        *(uint2*)(stage + n16 * 128 + (((2 * ct + (g >> 1)) ^ (n16 & 7)) << 4) + 8 * (g & 1)) =
+                            make_uint2(w0v, w1v);
+                    }
+                    // heads 16ht + hl + 8i, channels 64p + 8c8 .. + 7
+                    const int hl = lane >> 3, c8 = lane & 7;
+#pragma unroll
+                    for (int i2 = 0; i2 < 2; ++i2) {
+                        const int hr = hl + 8 * i2;
+                        const uint4 v = *(const uint4*)(stage + hr * 128 + ((c8 ^ (hr & 7)) << 4));
+                        *(uint4*)(O + (((int64_t)P.b * H + 16 * ht + hr) * Tq + P.t) * D + 64 * p8 + 8 * c8) = v;
+                    }
+                } else {
+                    const int64_t pbase = ((int64_t)P.row * nsplit + P.split) * H + hh;
+                    float* po = part_O + pbase * D;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) *(f4*)(po + 64 * p8 + 16 * ct + 4 * g) = oacc[ct][ht];
+                    if (p8 == 0 && g == 0) {
+                        part_ml[pbase * 2] = mfin[pp][hh];          // log2 units
+                        part_ml[pbase * 2 + 1] = lfin[pp][hh];
+                    }
+                }
+            }
+        };
+        int rb0 = 0;                    // raw buffer of the unit's first chunk
+        Done Uprev{0, 0, 0, 0};
+        int nmine = 0;                  // units taken so far
         for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
-            const Unit U = unit_of(u);
+            nmine = i + 1;
+            const Unit U = unit_of(u, i);
             const int k_begin = U.k_begin, k_end = U.k_end, nwch = U.nwch;
+            const int nch = k_end > k_begin ? k_end - k_begin : 0;
+            auto bufi = [&](int k) { return (rb0 + k - k_begin) % NRAW; };
             barrier_lds();      // start(u)
-
-            f4 oacc[4][HT];                 // O^T tiles: [channel tile][head tile]
+            // the previous unit's output goes out first (its stores are older
+            // than this unit's copies)
+            if (i > 0) output(Uprev, up ^ 1);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] = f4{0.f, 0.f, 0.f, 0.f};
 
-            // PV of chunk kp: O^T[64p + 16ct + .., heads] += G^T P^T over its
-            // 32 rows, after scaling by the chunk's row corrections
-            auto pv = [&](int kp) {
-                const int bp = kp & 1;
-                const float4 c4 = *(const float4*)&corb[bp][n16][0];
-                const float cr[4] = {c4.x, c4.y, c4.z, c4.w};
-                bool resc = false;
+            // A operand of chunk k for channel tile ct (channel 64p + 16ct + n16,
+            // rows 8g..8g+7), converted to bf16 from the raw chunk through the
+            // transposing loads: in each 16-lane group, destination lane j
+            // receives element j of every source lane's 8 bytes.  FP4 rows (256
+            // bytes): source lanes 2m and 2m+1 read row 8g+m, channels 32b +
+            // 0..15 and 32b + 16..31 of block b, so byte m of the result holds two
+            // channels of row m -- one block scale, applied exactly in the
+            // conversion.  FP8 rows (512 bytes): source lanes 2m, 2m+1 read row
+            // 8g+m, channels c0..c0+7 and c0+8..c0+15, so byte m is channel c0 + j
+            // of row m (its fp32 row scale is in P).  Units of a staged row are
+            // swizzled: unit u of row r at u ^ (r & 15).
+            const int sr = 8 * g + (n16 >> 1), sh = n16 & 1;   // source row and half of this lane
+            auto convert = [&](int k, bf8 (&a)[4]) {
+                const int rb = bufi(k);
+                if (k < nwch) {
+                    const uint8_t* rrow = &rawc[rb][sr * 512];
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) resc |= cr[ht] != 1.0f;
-                if (__any(resc)) {
+                    for (int ct = 0; ct < 4; ++ct) {
+                        const int u = 4 * p8 + ct;                  // channels 16u .. 16u + 15
+                        const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (lds_v2i*)(rrow + 16 * (u ^ (sr & 15)) + 8 * sh));
+                        const uint32_t w0 = (uint32_t)v[0], w1 = (uint32_t)v[1];
+                        a[ct] = __builtin_bit_cast(bf8, make_uint4(
+                            fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                            fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)));
+                    }
+                } else {
+                    // this wave's 64 block scales (rows 0..31 of blocks 2p, 2p+1),
+                    // one per lane, as fp32 in its own table [block][row]
+                    {
+                        const int zr = lane & 31, zb = lane >> 5;
+                        const uint8_t e = ((const uint8_t*)&zsc[rb][zr][0])[2 * p8 + zb];
+                        sfw[p8][zb][zr] = e8m0_to_f32(e);
+                    }
+                    const uint8_t* rrow = &rawc[rb][sr * 256];
+#pragma unroll
+                    for (int bl = 0; bl < 2; ++bl) {
+                        const int u = 2 * p8 + bl;                  // block: channels 32u .. 32u + 31
+                        const v2i v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                            (lds_v2i*)(rrow + 16 * (u ^ (sr & 15)) + 8 * sh));
+                        const float4 s0 = *(const float4*)&sfw[p8][bl][8 * g];
+                        const float4 s1 = *(const float4*)&sfw[p8][bl][8 * g + 4];
+                        const uint32_t v0 = (uint32_t)v[0], v1 = (uint32_t)v[1];
+                        const uint32_t res[8] = {fp4x2_bf16<0>(v0, s0.x), fp4x2_bf16<1>(v0, s0.y),
+                                                 fp4x2_bf16<2>(v0, s0.z), fp4x2_bf16<3>(v0, s0.w),
+                                                 fp4x2_bf16<0>(v1, s1.x), fp4x2_bf16<1>(v1, s1.y),
+                                                 fp4x2_bf16<2>(v1, s1.z), fp4x2_bf16<3>(v1, s1.w)};
+                        uint32_t lo[4], hi[4];
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            lo[d] = __builtin_amdgcn_perm(res[2 * d + 1], res[2 * d], 0x05040100u);
+                            hi[d] = __builtin_amdgcn_perm(res[2 * d + 1], res[2 * d], 0x07060302u);
+                        }
+                        a[2 * bl] = __builtin_bit_cast(bf8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                        a[2 * bl + 1] = __builtin_bit_cast(bf8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                    }
+                }
+            };
+            // PV of chunk kp: O^T[64p + 16ct + .., heads] += G^T P^T over its 32
+            // rows (A converted in the previous phase), after scaling by the
+            // chunk's row corrections where a QK wave moved its maximum
+            auto pv = [&](int kp, const bf8 (&a)[4]) {
+                const int bp = kp & 1;
+                const uint4 fl = *(const uint4*)&cflag[bp][0];
+                bf8 pb[HT];
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    pb[ht] = *(const bf8*)((const uint8_t*)&Pb[bp][0] + pb_off(16 * ht + n16, g));
+                if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+                    const float4 c4 = *(const float4*)&corb[bp][n16][0];
+                    const float cr[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                         for (int ht = 0; ht < HT; ++ht) oacc[ct][ht] *= cr[ht];
                 }
-                bf8 pb[HT];
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-                    pb[ht] = *(const bf8*)((const uint8_t*)&Pb[bp][0] + pb_off(16 * ht + n16, g));
-                const int sr = n16 >> 2, sq = n16 & 3;    // transposing-read source: row, 4-channel group
-                const int ra_ = 8 * g + sr, rb2 = ra_ + 4;
-                const uint16_t* gba = &Gb[bp][ra_ * D];
-                const uint16_t* gbb = &Gb[bp][rb2 * D];
-                const int swa = gb_swz(ra_), swb = gb_swz(rb2);
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const int c0 = 64 * p8 + 16 * ct;
-                    const int uu = (c0 >> 3) + (sq >> 1);
-                    const int off = 4 * (sq & 1);
-                    const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gba + 8 * (uu ^ swa) + off));
-                    const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(gbb + 8 * (uu ^ swb) + off));
-                    const bf8 a = __builtin_bit_cast(bf8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                     for (int ht = 0; ht < HT; ++ht)
-                        oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht], oacc[ct][ht], 0, 0, 0);
-                }
+                        oacc[ct][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ct], pb[ht], oacc[ct][ht], 0, 0, 0);
             };
-            // bf16 copy of channels 64p..64p+63 of chunk k's 32 rows: written
-            // and read by this wave only.  Lane (row r = l & 31, half l >> 5).
-            auto dequant = [&](int k) {
-                const int buf = k & 1, rbuf = k % NRAW;
-                const int r = lane & 31, r15 = r & 15;
-                uint16_t* grow = &Gb[buf][r * D];
-                const int gsw = gb_swz(r);
-                if (k < nwch) {
-                    // window row: 16 channels per 16 bytes of E4M3; units 4p + 2 half + j
-                    const uint8_t* rrow = &rawc[rbuf][r * 512];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int uq = 4 * p8 + 2 * (lane >> 5) + j;
-                        const uint4 x = *(const uint4*)(rrow + 16 * (uq ^ r15));
-                        const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
-                                                    fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y));
-                        const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(x.z), fp8x2_to_bf16x2<true>(x.z),
-                                                    fp8x2_to_bf16x2<false>(x.w), fp8x2_to_bf16x2<true>(x.w));
-                        *(uint4*)(grow + 8 * ((2 * uq) ^ gsw)) = lo;
-                        *(uint4*)(grow + 8 * ((2 * uq + 1) ^ gsw)) = hi;
-                    }
-                } else {
-                    // compressed row: 32 channels per 16 bytes of E2M1, one E8M0 byte
-                    const uint8_t* rrow = &rawc[rbuf][r * 256];
-                    const int uq = 2 * p8 + (lane >> 5);
-                    const float sc = e8m0_to_f32(((const uint8_t*)&zsc[rbuf][r][0])[uq]);
-                    const uint4 x = *(const uint4*)(rrow + 16 * (uq ^ r15));
-                    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2) {
-                        const uint32_t w = w4[k2];
-                        const uint4 v = make_uint4(
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
-                        *(uint4*)(grow + 8 * ((4 * uq + k2) ^ gsw)) = v;
-                    }
-                }
-            };
-            // copies of chunk k (k >= k_begin + 3) into raw buffer k % NRAW: PV wave
-            // p copies rows 4p..4p+3 (the QK waves stage the first three chunks)
+            // copies of chunk k (k >= k_begin + 4) into its raw buffer: PV wave
+            // p copies rows 4p..4p+3 (the QK waves stage the first four chunks)
             const int nwin = U.nwin, ncmp = U.ncmp, slot0 = U.slot0;
             const uint8_t* wrow0 = w_codes + (int64_t)U.b * cap * D;
             const float* wsc = w_scale + (int64_t)U.b * cap;
@@ -546,7 +716,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * 16;
             auto copy_chunk = [&](int k) {
                 if (k >= k_end) return;
-                const int buf = k % NRAW;
+                const int buf = bufi(k);
                 if (k < nwch) {
                     const int base = k * CH;
                     const int nv = min(nwin - base, CH);
@@ -576,88 +746,39 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     }
                 }
             };
-            // phase k: copies of chunk k+3 (raw buffer (k+3) % NRAW held chunk
-            // k-1, read before B(k-1)), PV(k-1), the bf16 copy of chunk k, B(k)
-            for (int k = k_begin; k < k_end; ++k) {
-                copy_chunk(k + NRAW - 1);
-                if (k > k_begin) pv(k - 1);
-                // the bf16 copy ends this wave's phase, after the MFMA work of
-                // the SIMD's other waves: it goes first on the SIMD
-                __builtin_amdgcn_s_setprio(1);
-                dequant(k);
-                __builtin_amdgcn_s_setprio(0);
-                // B(k): chunk k+1 staged (this wave's copies of k+2, k+3 may be
-                // in flight: at least one copy each)
-                if (k + 3 < k_end) barrier_vm<2>();
+            // phase k: copies of chunk k+4 (raw buffer (k+4) % NRAW held chunk
+            // k-1, converted before B(k-1)), PV(k-1) on the operand converted in
+            // phase k-1, conversion of chunk k, B(k).  B(k) needs chunk k+1
+            // staged: the QK waves staged the first four; of this wave's copies
+            // those of k+2, k+3, k+4 may be in flight (at least one copy each),
+            // and the previous unit's output stores may be in flight until
+            // B(k_begin + 3)
+            auto phase = [&](int k, const bf8 (&ap)[4], bf8 (&an)[4]) {
+                copy_chunk(k + 4);
+                if (k > k_begin) pv(k - 1, ap);
+                // the products go out first; the conversion runs while they (and
+                // the other waves of the SIMD) use the matrix core
+                __builtin_amdgcn_sched_barrier(0);
+                convert(k, an);
+                if (k + 1 < k_begin + 4) barrier_vm<63>();   // the QK waves staged chunk k+1
+                else if (k + 4 < k_end) barrier_vm<3>();
+                else if (k + 3 < k_end) barrier_vm<2>();
                 else if (k + 2 < k_end) barrier_vm<1>();
                 else barrier_vm<0>();
+            };
+            bf8 a0[4], a1[4];
+            for (int k = k_begin; k < k_end; ++k) {
+                phase(k, a1, a0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) a1[ct] = a0[ct];
             }
-            if (k_end > k_begin) pv(k_end - 1);
-            barrier_lds();      // final(u): the QK waves' m, l
-
-            // ---- output ------------------------------------------------------
-            // normalised O of head h, channels 64p..+63, goes through this
-            // wave's own bf16 row buffers (128 bytes per head) to be written as
-            // contiguous 128-byte segments
-            // head hh's 128 bytes sit at row hh & 31 of buffer hh >> 5, bytes 128p..
-            uint8_t* const stage = (uint8_t*)&Gb[0][0] + 128 * p8;
-            uint8_t* const st_w = stage + n16 * (D * 2) + 8 * g;   // lane's writes: head 16ht + n16
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const int hh = 16 * ht + n16;
-                const float m = mfin[hh], l = lfin[hh];
-                if (nsplit == 1) {
-                    const float shv = sinkl[hh] * LOG2E;
-                    const float M = fmaxf(m, shv);
-                    const float em = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-                    const float den = l * em + __builtin_amdgcn_exp2f(shv - M);
-                    const float f = em / den;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        const int d0 = 64 * p8 + 16 * ct + 4 * g;
-                        float o[4] = {oacc[ct][ht][0] * f, oacc[ct][ht][1] * f, oacc[ct][ht][2] * f,
-                                      oacc[ct][ht][3] * f};
-                        if (d0 >= ROPE_LO) {
-#pragma unroll
-                            for (int q2 = 0; q2 < 2; ++q2) {
-                                const int pi = (d0 - ROPE_LO) / 2 + q2;
-                                const float co = ropel[up][0][pi], si = ropel[up][1][pi];
-                                const float x0 = o[2 * q2], x1 = o[2 * q2 + 1];
-                                o[2 * q2] = x0 * co + x1 * si;
-                                o[2 * q2 + 1] = x1 * co - x0 * si;
-                            }
-                        }
-                        const uint32_t w0v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[0], (__bf16)o[1]});
-                        const uint32_t w1v = __builtin_bit_cast(uint32_t, bf2{(__bf16)o[2], (__bf16)o[3]});
-                        *(uint2*)(st_w + (ht >> 1) * (CH * D * 2) + (ht & 1) * 16 * (D * 2) + 32 * ct) =
-                            make_uint2(w0v, w1v);
-                    }
-                    if (lse && p8 == 0 && g == 0)
-                        lse[((int64_t)U.b * H + hh) * Tq + U.t] = (M + log2f(den)) * 0.6931471805599453f;
-                } else {
-                    const int64_t pbase = ((int64_t)U.row * nsplit + U.split) * H + hh;
-                    float* po = part_O + pbase * D;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) *(f4*)(po + 64 * p8 + 16 * ct + 4 * g) = oacc[ct][ht];
-                    if (p8 == 0 && g == 0) {
-                        part_ml[pbase * 2] = m;          // log2 units
-                        part_ml[pbase * 2 + 1] = l;
-                    }
-                }
-            }
-            if (nsplit == 1) {
-                // 8 lanes per head, 16 bytes each: eight heads (8i + l/8) per store
-                const int hl = lane >> 3, c8 = lane & 7;
-                const uint8_t* st_r = stage + hl * (D * 2) + 16 * c8;
-                uint16_t* orow = O + (((int64_t)U.b * H + hl) * Tq + U.t) * D + 64 * p8 + 8 * c8;
-                const int64_t ostep = (int64_t)8 * Tq * D;
-#pragma unroll
-                for (int i = 0; i < 16 * HT / 8; ++i) {
-                    const uint4 v = *(const uint4*)(st_r + (i >> 2) * (CH * D * 2) + (i & 3) * 8 * (D * 2));
-                    *(uint4*)(orow + i * ostep) = v;
-                }
-            }
+            if (k_end > k_begin) pv(k_end - 1, a1);
+            barrier_lds();      // final(u): the QK waves' m, l and normalisation
+            Uprev = Done{U.b, U.t, U.row, U.split};
+            rb0 = (rb0 + nch) % NRAW;
         }
+        // the last unit's output
+        if (nmine > 0) output(Uprev, (nmine - 1) & 1);
     }
 }
 
