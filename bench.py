@@ -33,14 +33,16 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.383e+10, {
-        "attention.hip": "9ac6af5fc9a1a9dd9793887800afa9925622b9ba6c095b718491b7a70d31ba2e",
+    ("k_attn", "prefill", 65536): (1.406e+10, {
+        "attention.hip": "333b67d04f56b5d0765db48c76bc511fbc64d15312ed723ccb6ae03cf68ab3c2",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_scores", "prefill", 65536): (7.074e+09, {
-        "indexer.hip": "46bcbfd90e528267e58ffdae475159a0397bd7a517c64877e32f4ad1b822fc6c",
+    ("k_index_select", "prefill", 65536): (5.120e+08, {
+        "index_select.hip": "7f0acd03267449fc81a4c2c603918b948c3ee2c2f29858c8246a237f056b124c",
+        "index_device.h": "7919782e2cbb25c2755c5323fe4b724e31987a53b36eb145c9945dd523e0d9f9",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
     ("k_index_scores", "decode", 131072): (6.088e+08, {
-        "indexer.hip": "46bcbfd90e528267e58ffdae475159a0397bd7a517c64877e32f4ad1b822fc6c",
+        "indexer.hip": "38884e262d3bf8243d25b2eec70c0767aac1291aa8a79f09cabcbf7dc6488d2c",
+        "index_device.h": "7919782e2cbb25c2755c5323fe4b724e31987a53b36eb145c9945dd523e0d9f9",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
 }
 
