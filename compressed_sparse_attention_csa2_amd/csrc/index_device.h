@@ -105,6 +105,44 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Wave-wide sum of u32 values, returned in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(v), 63);
+}
+
+// A key theta that at least k and at most `limit` of the buffered keys (held in
+// registers as below, 0 = no element) reach, found by halving the interval
+// [smallest key, largest key]: each step counts the keys >= its middle.
+// Returns 0 when no such theta exists (so many keys equal one value that every
+// threshold leaves either fewer than k or more than `limit`; all keys equal
+// included).  The caller's buffer holds more than `limit` keys.
+__device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[16], uint32_t k, uint32_t limit) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (kr[r] != 0u) lo = min(lo, kr[r]);
+        hi = max(hi, kr[r]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    uint32_t a = lo;                        // at least k keys >= a
+    uint64_t b = (uint64_t)hi + 1u;         // fewer than k keys >= b
+    while (b - a > 1u) {
+        const uint32_t mid = (uint32_t)(a + ((b - a) >> 1));
+        uint32_t c = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c += kr[r] >= mid ? 1u : 0u;
+        c = wave_sum(c);
+        if (c >= k) {
+            a = mid;
+            if (c <= limit) return a;
+        } else {
+            b = mid;
+        }
+    }
+    return 0u;
+}
+
 // Radix threshold over the buffer's keys, held in registers (lane l: elements
 // l + 64r, r < 16; 0 past nc).  Returns theta with at least k keys >= theta.
 // exact: theta is the k-th largest key and *krem the number of its copies in

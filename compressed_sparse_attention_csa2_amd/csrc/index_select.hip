@@ -16,10 +16,11 @@
 // is compared with that token's running threshold and the passing ones are
 // appended, in entry order, to the token's candidate buffer in LDS (ballot
 // ranks, no branch: lanes that do not pass write a spare slot).  When a buffer
-// is nearly full, a wave-wide radix select over it finds a key theta with at
-// least 512 candidates at or above it and at most a few hundred more, keeps
-// those in order and makes theta the token's new (strict) threshold: a later
-// entry equal to theta ranks below every kept one, which has a smaller j.
+// is nearly full, a wave-wide search over it (halving the key range, counting
+// with compares and a DPP sum) finds a key theta with at least 512 candidates
+// at or above it and at most `keep`, keeps those in order and makes theta the
+// token's new (strict) threshold: a later entry equal to theta ranks below
+// every kept one, which has a smaller j.
 // At the end an exact select keeps the 512 largest (ties: smaller j).
 //
 // Segments: prefill rows are many and each wave takes all of its tokens'
@@ -161,12 +162,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             const int i = 64 * q + lane;
             kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
         }
-        uint32_t krem;
-        uint32_t theta = wave_threshold_h(L.b.hist, kr, TOPK, SelCfg<TOK>::keep, false, &krem);
-        int kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, krem);
-        if (kept > SelCfg<TOK>::keep) {
-            // only when every key is equal (a non-exact threshold otherwise keeps at
-            // most `keep`): the buffer came back unchanged; keep the first 512
+        uint32_t theta = wave_threshold_bisect(kr, TOPK, SelCfg<TOK>::keep);
+        int kept;
+        if (theta != 0u) {
+            kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, 0xFFFFFFFFu);
+        } else {
+            // so many equal keys that no threshold keeps between 512 and `keep`:
+            // the exact 512th key and its copies among the first 512
+            uint32_t krem;
             theta = wave_threshold_h(L.b.hist, kr, TOPK, 0, true, &krem);
             kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, krem);
         }

@@ -501,6 +501,47 @@ def test_degenerate_calls(dev, synth):
         assert list(written) == ([] if ratio == 2 else [2]), (ratio, written)
 
 
+@pytest.mark.parametrize("Tq", [1, 8, 12])
+def test_fused_select_clustered_scores(dev, orc, Tq):
+    """the fused scores + selection kernel when scores repeat: every cache row drawn
+    from one key (all scores equal: the first 512 entries), from 3 keys (about 2,700
+    copies of each score) and from 40 keys (about 200 copies).  The buffer trims then
+    cannot always land between 512 and the buffer's keep limit and take the exact
+    tie-broken cut instead.  Tq 1, 8 and 12 run the kernel's 1-, 8- and 4-token forms
+    (12: a ragged last group); 8,192 entries make two 4,096-entry segments and a merge."""
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import tests.test_oracle_compress as tc
+    rng = np.random.default_rng(97 + Tq)
+    B, N = 3, 8192
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.zeros((B, N, 4), np.uint8)
+    for b, nd in enumerate((1, 3, 40)):
+        dc, ds = orc.fp4_encode(rng.standard_normal((nd, 128)).astype(np.float32))
+        pick = rng.integers(0, nd, N)
+        kc[b], ks[b] = dc[pick], ds[pick]
+    qI = tc.bf16(rng.standard_normal((B, Tq, 32, 128)).astype(np.float32))
+    wI = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
+    ne = np.full(B, N, np.int32)
+    q0 = np.full(B, 2 * N, np.int32)
+    log(f"fused selection, repeated scores: B={B} Tq={Tq} N={N}")
+    idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, Tq), -7, dtype=torch.int32, device=dev)
+    csa2.csa2_index_topk(_up(q0), _up(ne), _up(qI), _up(wI), _up(kc), _up(ks), idx, cnt,
+                         csa2.workspace(csa2.OP_INDEX_TOPK, B, Tq, 64, N))
+    torch.cuda.synchronize()
+    gi, gc_ = _down(idx), _down(cnt)
+    for b in range(B):
+        for i in range(Tq):
+            q8, sq = orc.quant_index_query(qI[b, i])
+            S = orc.index_scores(q8, sq, wI[b, i], kc[b], ks[b], N)
+            r_idx, r_cnt = orc.topk(S, N)
+            if b == 0:
+                assert np.array_equal(r_idx, np.arange(512))
+            # equal keys give equal scores on both sides: the cut is the same entries
+            assert gc_[b, i] == r_cnt and np.array_equal(gi[b, i], r_idx), (b, i)
+
+
 def test_topk_row_paths(dev, orc):
     """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
     three paths: a sampled threshold (20,000 candidates), every score kept without a
