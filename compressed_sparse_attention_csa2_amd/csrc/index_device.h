@@ -105,6 +105,64 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Reductions over a 16-lane row (DPP row rotations by 1, 2, 4 and 8): every
+// lane of the row gets the row's result.
+__device__ __forceinline__ uint32_t row_sum(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false);   // row_ror:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false);   // row_ror:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);   // row_ror:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);   // row_ror:8
+    return v;
+}
+__device__ __forceinline__ uint32_t row_min(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));
+    return v;
+}
+__device__ __forceinline__ uint32_t row_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));
+    return v;
+}
+
+// Per 16-lane row: a key theta that at least r and at most rhi of the row's
+// 16 x NS keys reach (halving the row's key range), or, when repeated keys
+// leave none, the largest key that at least r reach.  Needs r <= 16 * NS.
+template <int NS>
+__device__ __forceinline__ uint32_t row_threshold_bisect(const uint32_t (&kv)[NS], uint32_t r, uint32_t rhi) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        lo = min(lo, kv[s]);
+        hi = max(hi, kv[s]);
+    }
+    uint32_t a = row_min(lo);                       // at least r keys >= a
+    uint64_t b = (uint64_t)row_max(hi) + 1u;        // fewer than r keys >= b
+    bool done = false;
+    for (int it = 0; it < 33; ++it) {               // the interval halves every step
+        done = done || b - a <= 1u;
+        if (__ballot(!done) == 0ull) break;
+        const uint32_t mid = (uint32_t)(a + ((b - a) >> 1));
+        uint32_t c = 0u;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) c += kv[s] >= mid ? 1u : 0u;
+        c = row_sum(c);
+        if (!done) {
+            if (c >= r) {
+                a = mid;
+                done = c <= rhi;
+            } else {
+                b = mid;
+            }
+        }
+    }
+    return a;
+}
+
 // Wave-wide sum of u32 values, returned in every lane.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(v), 63);

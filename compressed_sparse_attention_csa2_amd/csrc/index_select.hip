@@ -48,6 +48,8 @@ template <int TOK> struct SelCfg {
     static constexpr int keep = cap - 192;
     static constexpr int waves = TOK == 1 ? 3 : (TOK == 4 ? 2 : 1);
 };
+// lists at least this long start from a sampled threshold (four-token form)
+constexpr int SAMPLE_MIN = 4096;
 
 template <int TOK>
 struct SelBuf {
@@ -201,19 +203,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         (void*)sbase, (short)0, jlen * 4, 0x00020000);
 
     if constexpr (TOK == 4) {
-        // Software-pipelined by token pairs, as in the score-only kernel: the
-        // products of one pair run on the matrix unit while the vector unit
-        // reduces the other pair.  Per tile p: [products of tokens 0,1 on p |
-        // head sums of tokens 2,3 of p - 1, then the admission of p - 1]
-        // [products of tokens 2,3 on p | head sums of tokens 0,1 of p].
-        int kld = col * 64 + 16 * grp;
-        int sld = col * 4;
-        uint4 kb[4];
-        int sb[4];
-        auto ld = [&](int p, uint4& kc, int& sc) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, kld + 1024 * p, 0, 0);
+        const int kld0 = col * 64 + 16 * grp;
+        const int sld0 = col * 4;
+        auto ld = [&](int off, uint4& kc, int& sc) {     // off: the tile's first entry
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, kld0 + 64 * off, 0, 0);
             kc = uint4{v[0], v[1], v[2], v[3]};
-            sc = (int)__builtin_amdgcn_raw_buffer_load_b32(ksr, sld + 16 * 4 * p, 0, 0);
+            sc = (int)__builtin_amdgcn_raw_buffer_load_b32(ksr, sld0 + 4 * off, 0, 0);
         };
         auto mm2 = [&](int k0, const uint4 kc, const int sw, f4 (&d)[2][2]) {
             const int sc = (int)(((uint32_t)sw >> (8 * grp)) & 0xFFu);
@@ -237,46 +232,99 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             sa = a0;
             sb2 = a1;
         };
-        f4 dA[2][2], dB[2][2];
+
+        // Starting thresholds from a sample: 16 tiles spread evenly over the
+        // entries every token of the group may select.  With p = 512 / n the
+        // fraction of a token's n candidates in its top 512, about 256 p of the
+        // sample's scores fall there; a threshold reached by r = 256 p + 3
+        // sqrt(256 p) + 1 of them (up to 1.5 r) leaves fewer than 512 scores
+        // above it only rarely, and then the token is scanned again from
+        // minus infinity.  Without it a token's threshold starts at minus
+        // infinity and rises only as its buffer fills, so a long list is
+        // trimmed many more times.
+        const int nmin = (int)wave_min((uint32_t)ncnd[0]);
+        bool sampled = false;
+        if (nmin >= SAMPLE_MIN) {
+            constexpr int NS = 16;
+            uint4 skc[NS];
+            int ssc[NS];
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+            for (int q = 0; q < NS; ++q) ld((((2 * q + 1) * nmin) / (2 * NS)) & ~15, skc[q], ssc[q]);
+            uint32_t kv[NS];
 #pragma unroll
-            for (int tile = 0; tile < 2; ++tile) dB[k][tile] = f4{0.f, 0.f, 0.f, 0.f};
-        float s0 = 0.0f, s1 = 0.0f, s2, s3;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) ld(p, kb[p], sb[p]);
-        kld += 3 * 1024;
-        sld += 3 * 64;
-        const int ngroups = (jlen + 63) >> 6;
-        for (int gi = 0; gi < ngroups; ++gi) {      // tiles 4 gi .. 4 gi + 3
-            const int jt = gi * 64;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                ld(p, kb[(p + 3) & 3], sb[(p + 3) & 3]);
-                mm2(0, kb[p], sb[p], dA);
-                epi2(2, dB, s2, s3);
-                admit(0, jt + 16 * p - 16, rowsum_scatter4(s0, s1, s2, s3));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                mm2(2, kb[p], sb[p], dB);
-                epi2(0, dA, s0, s1);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < NS; ++q) {
+                f4 d0[2][2], d1[2][2];
+                mm2(0, skc[q], ssc[q], d0);
+                mm2(2, skc[q], ssc[q], d1);
+                float a0, a1, a2, a3;
+                epi2(0, d0, a0, a1);
+                epi2(2, d1, a2, a3);
+                kv[q] = score_key(rowsum_scatter4(a0, a1, a2, a3));
             }
-            kld += 4096;
-            sld += 256;
-            check();
+            const float mean = 256.0f * (float)TOPK / (float)nmin;
+            const uint32_t r = (uint32_t)ceilf(mean + 3.0f * sqrtf(mean) + 1.0f);
+            const uint32_t a = row_threshold_bisect<NS>(kv, r, r + (r >> 1));
+            // admission is strict: the threshold is the score just below key a
+            // (below +0 when a is the key of +0, which -0 shares)
+            const uint32_t kb = a == 0x80000000u ? 0x7FFFFFFEu : a - 1u;
+            thr[0] = key_score(kb);
+            sampled = true;
         }
-        epi2(2, dB, s2, s3);
-        admit(0, ngroups * 64 - 16, rowsum_scatter4(s0, s1, s2, s3));
+
+        for (int pass = 0; pass < 2; ++pass) {
+            // Software-pipelined by token pairs, as in the score-only kernel: the
+            // products of one pair run on the matrix unit while the vector unit
+            // reduces the other pair.  Per tile p: [products of tokens 0,1 on p |
+            // head sums of tokens 2,3 of p - 1, then the admission of p - 1]
+            // [products of tokens 2,3 on p | head sums of tokens 0,1 of p].
+            uint4 kb[4];
+            int sb[4];
+            f4 dA[2][2], dB[2][2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int tile = 0; tile < 2; ++tile) dB[k][tile] = f4{0.f, 0.f, 0.f, 0.f};
+            float s0 = 0.0f, s1 = 0.0f, s2, s3;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) ld(16 * p, kb[p], sb[p]);
+            const int ngroups = (jlen + 63) >> 6;
+            for (int gi = 0; gi < ngroups; ++gi) {      // tiles 4 gi .. 4 gi + 3
+                const int jt = gi * 64;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    ld(jt + 16 * (p + 3), kb[(p + 3) & 3], sb[(p + 3) & 3]);
+                    mm2(0, kb[p], sb[p], dA);
+                    epi2(2, dB, s2, s3);
+                    admit(0, jt + 16 * p - 16, rowsum_scatter4(s0, s1, s2, s3));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    mm2(2, kb[p], sb[p], dB);
+                    epi2(0, dA, s0, s1);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                check();
+            }
+            epi2(2, dB, s2, s3);
+            admit(0, ngroups * 64 - 16, rowsum_scatter4(s0, s1, s2, s3));
+            if (!sampled) break;
+            // a refill keeps at least 512, so a short buffer never had one: its
+            // sampled threshold let too few through; rescan those tokens alone
+            const bool short_ = fill[0] < min(TOPK, ncnd[0]);
+            if (__ballot(short_) == 0ull) break;
+            lim[0] = short_ ? max(ncnd[0] - col, 0) : 0;
+            thr[0] = short_ ? -INFINITY : thr[0];
+            fill[0] = short_ ? 0 : fill[0];
+            sampled = false;
+        }
     } else {
         auto load = [&](int jt, uint4& kc, uint32_t& sw) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (jt + col) * 64 + 16 * grp, 0, 0);

@@ -542,6 +542,64 @@ def test_fused_select_clustered_scores(dev, orc, Tq):
             assert gc_[b, i] == r_cnt and np.array_equal(gi[b, i], r_idx), (b, i)
 
 
+def test_fused_select_sampled_start(dev, orc):
+    """the four-token form of the fused kernel starts long lists (4,096 entries or
+    more) from a threshold taken on 16 tiles of 16 entries spread evenly over the
+    list, and scans a token again from minus infinity when fewer than 512 scores
+    pass it.  Here every large score sits in those tiles for the tokens whose query
+    follows the keys' common direction (tokens 0 and 1 of each group of four), and
+    ReLU zeroes every other score of theirs (a tie of 16,128 zeros at the cut): they
+    take the rescan.  Of the other tokens (random queries) some keep their sampled
+    start, some rescan.  All must give the exact top 512."""
+    import math
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import tests.test_oracle_compress as tc
+    rng = np.random.default_rng(29)
+    N, Tq = 16384, 12
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    starts = (((2 * np.arange(16) + 1) * N) // 32) & ~15
+    hot = np.zeros(N, bool)
+    for s0 in starts:
+        hot[s0:s0 + 16] = True
+    kpre = 0.3 * rng.standard_normal((N, 128)) + np.where(hot, 3.0, -3.0)[:, None] * u[None, :]
+    kc_, ks_ = orc.fp4_encode_rows_bf16(tc.bf16(kpre.astype(np.float32)))
+    aligned = (np.arange(Tq) % 4) < 2
+    qpre = 0.3 * rng.standard_normal((1, Tq, 32, 128))
+    qpre[0, aligned] += 4.0 * u
+    qpre[0, ~aligned] = rng.standard_normal((int((~aligned).sum()), 32, 128))
+    qI = tc.bf16(qpre.astype(np.float32))
+    wI = (np.abs(rng.standard_normal((1, Tq, 32))) / 64).astype(np.float32)
+    q0 = 2 * N
+    mean = 256 * 512 / N
+    r = math.ceil(mean + 3 * math.sqrt(mean) + 1)
+    Ss, above = [], []
+    for i in range(Tq):
+        q8, sq = orc.quant_index_query(qI[0, i])
+        S = orc.index_scores(q8, sq, wI[0, i], kc_, ks_, N)
+        Ss.append(S)
+        smp = np.sort(np.concatenate([S[s0:s0 + 16] for s0 in starts]))
+        above.append(np.count_nonzero(S >= smp[-r]))
+    # the construction does what it is for: the aligned tokens' sample has fewer than
+    # 512 scores above its r-th largest; some random token has more than enough
+    assert all(above[i] < 512 for i in range(Tq) if aligned[i])
+    assert any(above[i] >= 1024 for i in range(Tq) if not aligned[i])
+    log(f"fused selection, sampled start and rescan: Tq={Tq} N={N}")
+    idx = torch.full((1, Tq, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((1, Tq), -7, dtype=torch.int32, device=dev)
+    csa2.csa2_index_topk(_up(np.array([q0], np.int32)), _up(np.array([N], np.int32)), _up(qI),
+                         _up(wI), _up(kc_[None]), _up(ks_[None]), idx, cnt,
+                         csa2.workspace(csa2.OP_INDEX_TOPK, 1, Tq, 64, N))
+    torch.cuda.synchronize()
+    gi, gc_ = _down(idx), _down(cnt)
+    swaps = 0
+    for i in range(Tq):
+        r_idx, r_cnt = orc.topk(Ss[i], N)
+        swaps += check_selection(gi[0, i], gc_[0, i], r_idx, r_cnt, Ss[i])
+    log(f"  swaps={swaps}")
+
+
 def test_topk_row_paths(dev, orc):
     """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
     three paths: a sampled threshold (20,000 candidates), every score kept without a
