@@ -201,6 +201,48 @@ __device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[1
     return 0u;
 }
 
+// The k-th largest of the buffered keys (registers as below, 0 = no element;
+// at least k keys present) and in *krem_out how many of its copies belong to
+// the k largest (0xFFFFFFFF: all of them), by halving [smallest, largest key]:
+// each step counts the keys >= its middle.  Stops early when exactly k keys
+// reach the middle (the k-th largest is then their minimum).
+__device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[16], uint32_t k, uint32_t* krem_out) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (kr[r] != 0u) lo = min(lo, kr[r]);
+        hi = max(hi, kr[r]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    uint32_t a = lo;                        // at least k keys >= a
+    uint64_t b = (uint64_t)hi + 1u;         // fewer than k keys >= b: cb of them
+    uint32_t cb = 0u;
+    while (b - a > 1u) {
+        const uint32_t mid = (uint32_t)(a + ((b - a) >> 1));
+        uint32_t c = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c += kr[r] >= mid ? 1u : 0u;
+        c = wave_sum(c);
+        if (c == k) {
+            uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kr[r] >= mid) m = min(m, kr[r]);
+            *krem_out = 0xFFFFFFFFu;
+            return wave_min(m);
+        }
+        if (c > k) {
+            a = mid;
+        } else {
+            b = mid;
+            cb = c;
+        }
+    }
+    *krem_out = k - cb;
+    return a;
+}
+
 // Radix threshold over the buffer's keys, held in registers (lane l: elements
 // l + 64r, r < 16; 0 past nc).  Returns theta with at least k keys >= theta.
 // exact: theta is the k-th largest key and *krem the number of its copies in

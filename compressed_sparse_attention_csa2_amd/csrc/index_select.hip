@@ -55,7 +55,6 @@ template <int TOK>
 struct SelBuf {
     uint32_t key[TOK][SelCfg<TOK>::pad];     // bit patterns of the candidates' scores
     uint16_t j[TOK][SelCfg<TOK>::pad];       // their entries (offsets), ascending
-    uint32_t hist[256];
 };
 // the wave's LDS: the candidate buffers while scanning, a merge buffer after
 template <int TOK>
@@ -172,7 +171,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             // so many equal keys that no threshold keeps between 512 and `keep`:
             // the exact 512th key and its copies among the first 512
             uint32_t krem;
-            theta = wave_threshold_h(L.b.hist, kr, TOPK, 0, true, &krem);
+            theta = wave_kth_bisect(kr, TOPK, &krem);
             kept = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, theta, krem);
         }
         if (grp == g) {
@@ -399,7 +398,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         }
         if (nc > TOPK) {
             uint32_t krem;
-            const uint32_t kth = wave_threshold_h(L.b.hist, kr, TOPK, 0, true, &krem);
+            const uint32_t kth = wave_kth_bisect(kr, TOPK, &krem);
             nc = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, kth, krem);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
@@ -427,7 +426,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             uint32_t kqv = 0u;
             if (nc >= (int)kq) {
                 uint32_t krem;
-                kqv = wave_threshold_h(L.b.hist, kr, kq, 0, true, &krem);
+                kqv = wave_kth_bisect(kr, kq, &krem);
             }
             const uint32_t kth = nc == TOPK ? wave_min(mn) : 0u;
             if (lane == 0) {
