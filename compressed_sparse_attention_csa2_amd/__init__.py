@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+# CSA2_LIB names another build of the same library to load (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(_HERE, "libcsa2.so")
 
 D, WINDOW, HI, DI, TOPK = 512, 128, 32, 128, 512
 OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_SCORES, OP_INDEX_POOL, OP_REINDEX = 1, 2, 3, 4, 5, 6

@@ -70,6 +70,23 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """the library with its host code (argument checks, workspace layout, launch set-up)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests of the
+    checks that run before any launch; the device code is built as usual"""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    san = ["-Xarch_host", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    cmd = [hipcc(), *HIPCC_FLAGS, *san, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs,
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building the host-sanitized library")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_calib(verbose=True))

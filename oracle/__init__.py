@@ -21,7 +21,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libcsa2oracle.so")
+# CSA2_ORACLE_LIB names another build of the oracle to load (the tests' sanitizer build)
+_SO = os.environ.get("CSA2_ORACLE_LIB") or os.path.join(_HERE, "libcsa2oracle.so")
 
 D, ROPE_LO, WINDOW, HI, DI, TOPK = 512, 448, 128, 32, 128, 512
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
@@ -36,6 +37,15 @@ def build(verbose: bool = False) -> str:
     return _SO
 
 
+def build_sanitized(out: str, cc: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """the oracle built with AddressSanitizer and UndefinedBehaviorSanitizer (clang, so that
+    it shares one sanitizer runtime with the host-sanitized HIP library)"""
+    cmd = [cc, *CFLAGS, "-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", os.path.join(_HERE, "csa2_oracle.c"), "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 _lib = None
 
 
@@ -43,6 +53,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_SO):
+            if os.environ.get("CSA2_ORACLE_LIB"):
+                raise FileNotFoundError(_SO)
             build()
         L = ctypes.CDLL(_SO)
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
