@@ -252,9 +252,9 @@ SelWs select_ws(int B, int Tq, int64_t stride) {
     return w;
 }
 
-bool two_pass_rows(int64_t rows, int64_t stride);
+bool two_pass_rows(int B, int Tq, int64_t stride);
 size_t index_topk_ws(int B, int Tq, int64_t stride) {
-    return two_pass_rows((int64_t)B * Tq, stride) ? index_ws(B, Tq, stride).total
+    return two_pass_rows(B, Tq, stride) ? index_ws(B, Tq, stride).total
                                                   : select_ws(B, Tq, stride).total;
 }
 
@@ -317,10 +317,15 @@ void launch_scores(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entrie
                            wq, ki_codes, ki_scales, stride, Sc, s_stride, n_tg, n_ch, rsh);
 }
 
-// Few long rows (the decode shapes): scores to the workspace and a selection
-// pass win there -- the fused kernel would cut each row into many segments,
-// each selecting its own 512.
-bool two_pass_rows(int64_t rows, int64_t stride) { return rows <= 1024 && stride >= 16384; }
+// Few long rows (the decode and verify shapes): scores to the workspace and a
+// selection pass win there.  Measured at 128 single-token rows of 65,536
+// entries: 161 us for the two passes against 210 us fused (16 segments a row,
+// each from a sampled threshold, then a merge); the fused scan alone, without
+// the merge, took 190 us -- two waves a SIMD streaming the keys with the
+// admission work of every tile keep it below the score pass's bandwidth.
+bool two_pass_rows(int B, int Tq, int64_t stride) {
+    return (int64_t)B * Tq <= 1024 && stride >= 16384;
+}
 
 csa2_status launch_index_2pass(int B, int Tq, const int32_t* q_pos0, const int32_t* n_entries,
                                const uint16_t* qI, const float* wI, const uint8_t* ki_codes,
@@ -334,7 +339,7 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
                          const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
                          int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
-    if (two_pass_rows((int64_t)B * Tq, stride))
+    if (two_pass_rows(B, Tq, stride))
         return launch_index_2pass(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride,
                                   rsh, idx, cnt, ws, st);
     const SelWs L = select_ws(B, Tq, stride);

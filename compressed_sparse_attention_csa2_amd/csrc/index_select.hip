@@ -111,6 +111,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
     }
     jlen = (int)wave_max((uint32_t)jlen);
 
+    // the whole row of a single-token item (its segments' union), for the sampled start
+    const int n_row = TOK == 1 ? (int)min(cand_count(qp, t0, ne, entry_stride, rsh), (int64_t)0x7FFFFFFF) : 0;
+    const bool row_sampled = TOK == 1 && n_row >= SAMPLE_MIN && n_row <= 65536;   // offsets fit 16 bits
+    const __amdgpu_buffer_rsrc_t krow = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ki_codes + (int64_t)b * entry_stride * 64), (short)0, row_sampled ? n_row * 64 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ki_scales + (int64_t)b * entry_stride * 4), (short)0, row_sampled ? n_row * 4 : 0, 0x00020000);
+
     // ---- query operands (as the score-only kernel loads them)
     i8 A[TOK][2];
     f4 W[TOK][2];
@@ -200,6 +208,91 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         (void*)kbase, (short)0, jlen * 64, 0x00020000);
     const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)sbase, (short)0, jlen * 4, 0x00020000);
+
+    auto load = [&](const __amdgpu_buffer_rsrc_t kr_, const __amdgpu_buffer_rsrc_t sr_, int jt,
+                    uint4& kc, uint32_t& sw) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr_, (jt + col) * 64 + 16 * grp, 0, 0);
+        kc = uint4{v[0], v[1], v[2], v[3]};
+        sw = __builtin_amdgcn_raw_buffer_load_b32(sr_, (jt + col) * 4, 0, 0);
+    };
+    // one tile's head sums per token (lane row g: heads 4g..4g+3 of each 16)
+    auto sums = [&](const uint4 kc, const uint32_t sw, float (&s)[TOK]) {
+        const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
+        const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+        constexpr int KG = TOK < 4 ? TOK : 4;
+#pragma unroll
+        for (int k0 = 0; k0 < TOK; k0 += KG) {
+            f4 d[KG][2];
+#pragma unroll
+            for (int k = 0; k < KG; ++k)
+#pragma unroll
+                for (int tile = 0; tile < 2; ++tile)
+                    d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][0][i], relu(d[k][0][i]), acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][1][i], relu(d[k][1][i]), acc);
+                s[k0 + k] = acc;
+            }
+        }
+    };
+    auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
+        float s[TOK];
+        sums(kc, sw, s);
+        if (TOK == 1) {
+            admit(0, jt, rowsum_scatter4(s[0], s[0], s[0], s[0]));
+        } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                admit(r, jt, rowsum_scatter4(s[4 * r], s[4 * r + 1], s[4 * r + 2], s[4 * r + 3]));
+        }
+    };
+    // the entries [0, len) of the resources, NB tile buffers rotating: tile
+    // jt + 16p lives in buffer p % NB and is loaded NB - 1 tiles ahead
+    // (buffer loads past the entries read zeros)
+    constexpr int NB = CHK;
+    auto scan = [&](const __amdgpu_buffer_rsrc_t kr_, const __amdgpu_buffer_rsrc_t sr_, int len) {
+        uint4 kb[NB];
+        uint32_t sb[NB];
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p) load(kr_, sr_, 16 * p, kb[p], sb[p]);
+        for (int jt = 0; jt < len; jt += 16 * NB) {
+#pragma unroll
+            for (int p = 0; p < NB; ++p) {
+                load(kr_, sr_, jt + 16 * (p + NB - 1), kb[(p + NB - 1) % NB], sb[(p + NB - 1) % NB]);
+                step(jt + 16 * p, kb[p], sb[p]);
+            }
+            check();
+        }
+    };
+    // a single-token row scanned whole from minus infinity (the sampled start
+    // was too high), then cut to its exact top 512, written in entry order
+    auto rescan_row = [&](int64_t row) {
+        thr[0] = -INFINITY;
+        fill[0] = 0;
+        lim[0] = grp == 0 ? max(n_row - col, 0) : 0;
+        scan(krow, srow, n_row);
+        int nc = __builtin_amdgcn_readfirstlane(fill[0]);
+        if (nc > TOPK) {
+            uint32_t kr[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int i = 64 * q + lane;
+                kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[0][i])) : 0u;
+            }
+            uint32_t krem;
+            const uint32_t kth = wave_kth_bisect(kr, TOPK, &krem);
+            nc = wave_keep_buf<true>(L.b.key[0], L.b.j[0], nc, kr, kth, krem);
+        }
+        int32_t* out = idx + row * TOPK;
+        for (int i = lane; i < TOPK; i += 64) out[i] = i < nc ? (int)L.b.j[0][i] : -1;
+        if (lane == 0) cnt[row] = nc;
+    };
 
     if constexpr (TOK == 4) {
         const int kld0 = col * 64 + 16 * grp;
@@ -325,58 +418,44 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             sampled = false;
         }
     } else {
-        auto load = [&](int jt, uint4& kc, uint32_t& sw) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (jt + col) * 64 + 16 * grp, 0, 0);
-            kc = uint4{v[0], v[1], v[2], v[3]};
-            sw = __builtin_amdgcn_raw_buffer_load_b32(ksr, (jt + col) * 4, 0, 0);
-        };
-        auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
-            const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
-            const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
-            float s[TOK];
-            constexpr int KG = TOK < 4 ? TOK : 4;
+        if constexpr (TOK == 1) {
+            // A row of 4,096 to 65,536 entries starts every one of its segments
+            // from one threshold taken on 16 tiles spread evenly over the row (all
+            // of them score the same sample, so all agree): with p = 512 / n,
+            // about 256 p sampled scores fall in the row's top 512, and a
+            // threshold reached by r = 256 p + 4 sqrt(256 p) + 2 of them (up to
+            // 1.5 r) leaves fewer than 512 of the row's scores above it only
+            // rarely.  Each segment then admits a small share of its entries
+            // instead of selecting its own 512.  If the row ends up short, it is
+            // scanned again from minus infinity: here when it is one segment, by
+            // the wave that merges it otherwise.
+            if (row_sampled) {
+                uint4 skc[16];
+                uint32_t ssc[16];
 #pragma unroll
-            for (int k0 = 0; k0 < TOK; k0 += KG) {
-                f4 d[KG][2];
+                for (int q = 0; q < 16; ++q)
+                    load(krow, srow, (((2 * q + 1) * n_row) / 32) & ~15, skc[q], ssc[q]);
+                uint32_t kv[16];
 #pragma unroll
-                for (int k = 0; k < KG; ++k)
-#pragma unroll
-                    for (int tile = 0; tile < 2; ++tile)
-                        d[k][tile] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            A[k0 + k][tile], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int k = 0; k < KG; ++k) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][0][i], relu(d[k][0][i]), acc);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[k0 + k][1][i], relu(d[k][1][i]), acc);
-                    s[k0 + k] = acc;
+                for (int q = 0; q < 16; ++q) {
+                    float s1[TOK];
+                    sums(skc[q], ssc[q], s1);
+                    kv[q] = score_key(rowsum_scatter4(s1[0], s1[0], s1[0], s1[0]));
                 }
+                const float mean = 256.0f * (float)TOPK / (float)n_row;
+                const uint32_t r = (uint32_t)ceilf(mean + 4.0f * sqrtf(mean) + 2.0f);
+                const uint32_t a = row_threshold_bisect<16>(kv, r, r + (r >> 1));
+                thr[0] = key_score(a == 0x80000000u ? 0x7FFFFFFEu : a - 1u);
             }
-            if (TOK == 1) {
-                admit(0, jt, rowsum_scatter4(s[0], s[0], s[0], s[0]));
-            } else {
-#pragma unroll
-                for (int r = 0; r < NR; ++r)
-                    admit(r, jt, rowsum_scatter4(s[4 * r], s[4 * r + 1], s[4 * r + 2], s[4 * r + 3]));
+            scan(krs, ksr, jlen);
+            if (row_sampled && nseg == 1 &&
+                __builtin_amdgcn_readfirstlane(fill[0]) < min(TOPK, __builtin_amdgcn_readfirstlane(ncnd[0]))) {
+                thr[0] = -INFINITY;
+                fill[0] = 0;
+                scan(krs, ksr, jlen);
             }
-        };
-        // NB tile buffers rotate; tile jt + 16p lives in buffer p % NB and is
-        // loaded NB - 1 tiles ahead (buffer loads past the entries read zeros)
-        constexpr int NB = CHK;
-        uint4 kb[NB];
-        uint32_t sb[NB];
-#pragma unroll
-        for (int p = 0; p < NB - 1; ++p) load(16 * p, kb[p], sb[p]);
-        for (int jt = 0; jt < jlen; jt += 16 * NB) {
-#pragma unroll
-            for (int p = 0; p < NB; ++p) {
-                load(jt + 16 * (p + NB - 1), kb[(p + NB - 1) % NB], sb[(p + NB - 1) % NB]);
-                step(jt + 16 * p, kb[p], sb[p]);
-            }
-            check();
+        } else {
+            scan(krs, ksr, jlen);
         }
     }
 
@@ -451,6 +530,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
         if (prev == (uint32_t)(nseg - 1)) {
             __threadfence();               // and the other segments' winners are visible here
+            if (TOK == 1 && row_sampled) {
+                // the segments' candidates together: at least min(512, n) of them
+                // means the row's top 512 are among them
+                const int m = lane < nseg ? seg_n[row * nseg + lane] : 0;
+                const int total = (int)wave_sum((uint32_t)max(m, 0));
+                if (total < min(TOPK, n_row)) {
+                    rescan_row(row);
+                    continue;
+                }
+            }
             merge_segments(ws, row, nseg, seg_key, seg_j, seg_n, seg_kth, idx, cnt);
         }
     }

@@ -40,8 +40,12 @@ def test_workspace_sizes(L):
     # the selection is fused into the scoring: no score rows, only the quantised
     # queries (4,224 bytes per query row) -- and segment winners when rows are few
     assert 65536 * 4224 <= ws(csa2.OP_INDEX_TOPK, 1, 65536, 64, 32768) < 65536 * 4224 + 4096
-    # few long rows (decode) keep their score rows: the selection pass after it is faster there
+    # few long rows (decode, verify) keep their score rows: the selection pass after
+    # it is faster there
     assert ws(csa2.OP_INDEX_TOPK, 128, 1, 64, 65536) >= 128 * 65536 * 4
+    assert ws(csa2.OP_INDEX_TOPK, 16, 6, 64, 524288) >= 96 * 524288 * 4
+    # many single-token rows stay fused: segment winners only
+    assert ws(csa2.OP_INDEX_TOPK, 2048, 1, 64, 8192) < 2048 * 8192 * 4 // 4
     assert ws(csa2.OP_INDEX_TOPK, 3, 6, 64, 2600) <= 18 * (4224 + 16) + 4096
     assert ws(csa2.OP_INDEX_SCORES, 1, 65536, 64, 32768) < 65536 * 4224 + 4096
     assert ws(csa2.OP_FORWARD, 1, 256, 16, 128) > 0

@@ -600,6 +600,64 @@ def test_fused_select_sampled_start(dev, orc):
     log(f"  swaps={swaps}")
 
 
+@pytest.mark.parametrize("N", [6000, 12000])
+def test_single_token_rows_sampled_start(dev, orc, N):
+    """single-token rows of 4,096 or more entries on the fused kernel: every segment
+    of a row starts from one threshold taken on 16 tiles spread over the row.  Row 0
+    puts every large score in those tiles, so too few scores pass and the row is
+    scanned again from minus infinity (N=6000: one segment, rescanned in place;
+    N=12000: two segments, rescanned by the wave that merges them).  Row 1 has
+    random keys (the sampled start holds), row 2 identical keys (every score ties:
+    the first 512 entries)."""
+    import math
+    import torch
+    import compressed_sparse_attention_csa2_amd as csa2
+    import tests.test_oracle_compress as tc
+    rng = np.random.default_rng(31 + N)
+    B = 3
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    starts = (((2 * np.arange(16) + 1) * N) // 32) & ~15
+    hot = np.zeros(N, bool)
+    for s0 in starts:
+        hot[s0:s0 + 16] = True
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.zeros((B, N, 4), np.uint8)
+    kpre = 0.3 * rng.standard_normal((N, 128)) + np.where(hot, 3.0, -3.0)[:, None] * u[None, :]
+    kc[0], ks[0] = orc.fp4_encode_rows_bf16(tc.bf16(kpre.astype(np.float32)))
+    kc[1], ks[1] = orc.fp4_encode(rng.standard_normal((N, 128)).astype(np.float32))
+    one_c, one_s = orc.fp4_encode(rng.standard_normal((1, 128)).astype(np.float32))
+    kc[2], ks[2] = one_c[0], one_s[0]
+    qpre = rng.standard_normal((B, 1, 32, 128))
+    qpre[0, 0] = 4.0 * u + 0.3 * rng.standard_normal((32, 128))
+    qI = tc.bf16(qpre.astype(np.float32))
+    wI = (np.abs(rng.standard_normal((B, 1, 32))) / 64).astype(np.float32)
+    S = []
+    for b in range(B):
+        q8, sq = orc.quant_index_query(qI[b, 0])
+        S.append(orc.index_scores(q8, sq, wI[b, 0], kc[b], ks[b], N))
+    # the construction does what it is for: row 0's sample has fewer than 512 scores
+    # at or above its r-th largest
+    mean = 256 * 512 / N
+    r = math.ceil(mean + 4 * math.sqrt(mean) + 2)
+    smp = np.sort(np.concatenate([S[0][s0:s0 + 16] for s0 in starts]))
+    assert np.count_nonzero(S[0] >= smp[-r]) < 512
+    log(f"single-token rows, sampled start: B={B} N={N}")
+    idx = torch.full((B, 1, 512), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, 1), -7, dtype=torch.int32, device=dev)
+    q0 = np.full(B, 2 * N, np.int32)
+    csa2.csa2_index_topk(_up(q0), _up(np.full(B, N, np.int32)), _up(qI), _up(wI), _up(kc), _up(ks),
+                         idx, cnt, csa2.workspace(csa2.OP_INDEX_TOPK, B, 1, 64, N))
+    torch.cuda.synchronize()
+    gi, gc_ = _down(idx), _down(cnt)
+    swaps = 0
+    for b in range(B):
+        r_idx, r_cnt = orc.topk(S[b], N)
+        swaps += check_selection(gi[b, 0], gc_[b, 0], r_idx, r_cnt, S[b])
+    assert np.array_equal(gi[2, 0], np.arange(512)), "ties: the first 512 entries"
+    log(f"  swaps={swaps}")
+
+
 def test_topk_row_paths(dev, orc):
     """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
     three paths: a sampled threshold (20,000 candidates), every score kept without a
