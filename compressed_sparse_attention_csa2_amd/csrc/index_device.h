@@ -63,7 +63,6 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 struct WaveSel {
     uint32_t key[WS_CAP];
     int32_t j[WS_CAP];
-    uint32_t hist[256];
 };
 
 // Wave-wide inclusive prefix sum with DPP row shifts and row broadcasts (no LDS).
@@ -243,83 +242,6 @@ __device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[16], ui
     return a;
 }
 
-// Radix threshold over the buffer's keys, held in registers (lane l: elements
-// l + 64r, r < 16; 0 past nc).  Returns theta with at least k keys >= theta.
-// exact: theta is the k-th largest key and *krem the number of its copies in
-// the top k.  Otherwise refinement stops as soon as at most `limit` keys are
-// >= theta (*krem is then "all copies"); if equal keys keep the count above the
-// limit to the last bit, the exact answer is returned.  The bits common to all
-// keys are skipped; 8 bits per pass.
-// hist: 256 words of LDS owned by the wave.
-__device__ __forceinline__ uint32_t wave_threshold_h(uint32_t* hist, const uint32_t (&kr)[16], uint32_t k,
-                                     uint32_t limit, bool exact, uint32_t* krem_out) {
-    const int lane = threadIdx.x & 63;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (kr[r] != 0u) lo = min(lo, kr[r]);
-        hi = max(hi, kr[r]);
-    }
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lo >= hi) {                 // all keys equal
-        *krem_out = exact ? k : 0xFFFFFFFFu;
-        return hi;
-    }
-    int hib = 31 - __clz((int)(lo ^ hi));
-    uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
-    uint32_t prefix = lo & pmask, krem = k, above_all = 0;
-    while (hib >= 0) {
-        const int lob = hib - 7 > 0 ? hib - 7 : 0;
-        const uint32_t dmask = (2u << (hib - lob)) - 1u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (kr[r] != 0u && (kr[r] & pmask) == prefix) atomicAdd(&hist[(kr[r] >> lob) & dmask], 1u);
-        // digit holding the krem-th largest: bins in descending order, 4 per lane
-        uint32_t h[4], loc = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { h[q] = hist[255 - 4 * lane - q]; loc += h[q]; }
-        const uint32_t inc = wave_scan_add(loc);
-        uint32_t above = inc - loc, dsel = 0, asel = 0, hsel = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (above < krem && krem <= above + h[q]) {
-                dsel = 255u - 4u * lane - q;
-                asel = above;
-                hsel = h[q];
-                found = true;
-            }
-            above += h[q];
-        }
-        const int src = __ffsll((long long)__ballot(found)) - 1;
-        dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
-        asel = (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
-        hsel = (uint32_t)__builtin_amdgcn_readlane((int)hsel, src);
-        prefix |= dsel << lob;
-        pmask |= dmask << lob;
-        krem -= asel;
-        above_all += asel;
-        hib = lob - 1;
-        if (!exact && above_all + hsel <= limit) {   // keys >= prefix (low bits 0) fit
-            *krem_out = 0xFFFFFFFFu;
-            return prefix;
-        }
-    }
-    // every bit resolved: the k-th largest itself, and its copies in the top k
-    // (also when a non-exact search could not get under the limit: many equal keys)
-    *krem_out = krem;
-    return prefix;
-}
-
-__device__ __forceinline__ uint32_t wave_threshold(WaveSel& ws, const uint32_t (&kr)[16],
-                                                   uint32_t k, uint32_t limit, bool exact,
-                                                   uint32_t* krem_out) {
-    return wave_threshold_h(ws.hist, kr, k, limit, exact, krem_out);
-}
-
 // Keep, in order, the buffered elements above theta and the first krem equal to
 // it; the buffer (key, jb) holds keys, or with AS_SCORE the scores' bit patterns.
 template <bool AS_SCORE, typename JT>
@@ -372,11 +294,12 @@ __device__ __forceinline__ void load_keys(const WaveSel& ws, int nc, uint32_t (&
 // once, in order, 256 elements per step (lane l holds elements 4l..4l+3), and
 // every element whose key exceeds the wave's threshold is appended to a
 // per-wave LDS buffer (ballot compaction keeps list order).  When the buffer
-// would overflow, a wave-local radix select finds its 512th largest key K
-// (and how many copies of K belong to the top 512); the buffer is compacted
-// to exactly those 512 and the threshold becomes K, now strict: a later
-// element equal to K ranks below the 512 kept ones (all earlier in the list).
-// At the end the same select trims the buffer to 512.
+// would overflow, a wave-wide search halving the key range finds a key K that
+// between 512 and 768 of the buffered keys reach (or, when repeated keys leave
+// none, the exact 512th key and how many of its copies belong to the top 512);
+// the buffer is compacted to those and the threshold becomes K, now strict: a
+// later element equal to K ranks below every kept one (all earlier in the
+// list).  At the end an exact search of the same kind trims the buffer to 512.
 // ---------------------------------------------------------------------------
 struct WaveTopk {
     WaveSel& ws;
@@ -394,9 +317,12 @@ struct WaveTopk {
         if (nc + (int)cnt > WS_CAP) {
             // keep every key >= theta, where at least 512 are >= theta: a later key
             // equal to theta ranks below all of them
-            uint32_t kr[16], krem;
+            // (more than WS_CAP - 256 >= 512 are buffered: a theta between the
+            // bounds, found by halving the key range, or the exact 512th key)
+            uint32_t kr[16], krem = 0xFFFFFFFFu;
             load_keys(ws, nc, kr);
-            const uint32_t theta = wave_threshold(ws, kr, TOPK, WS_CAP - 256, false, &krem);
+            uint32_t theta = wave_threshold_bisect(kr, TOPK, WS_CAP - 256);
+            if (theta == 0u) theta = wave_kth_bisect(kr, TOPK, &krem);
             nc = wave_keep(ws, nc, kr, theta, krem);
             thr = theta;
             cnt = 0;
@@ -426,7 +352,7 @@ struct WaveTopk {
         if (nc > TOPK) {
             uint32_t kr[16], krem;
             load_keys(ws, nc, kr);
-            const uint32_t kth = wave_threshold(ws, kr, TOPK, 0, true, &krem);
+            const uint32_t kth = wave_kth_bisect(kr, TOPK, &krem);
             nc = wave_keep(ws, nc, kr, kth, krem);
         }
         uint32_t mn = 0xFFFFFFFFu;
@@ -443,7 +369,7 @@ struct WaveTopk {
             if (kq > 0 && nc >= (int)kq) {
                 uint32_t kr[16], krem;
                 load_keys(ws, nc, kr);
-                v = wave_threshold(ws, kr, kq, 0, true, &krem);
+                v = wave_kth_bisect(kr, kq, &krem);
             }
             *kq_out = v;
         }

@@ -371,8 +371,11 @@ __global__ void __launch_bounds__(64 * WS_WAVES) k_topk(
 #pragma unroll
         for (int g = 0; g < 16; ++g) kr[g] = score_key(src[g * gap + lane]);
         const uint32_t r = (uint32_t)((768 * 1024 + len - 1) / len);
-        uint32_t krem;
-        const uint32_t th = wave_threshold(st.ws, kr, r, r + r / 2, false, &krem);
+        uint32_t th = wave_threshold_bisect(kr, r, r + r / 2);
+        if (th == 0u) {          // repeated keys: the sample's r-th largest
+            uint32_t krem;
+            th = wave_kth_bisect(kr, r, &krem);
+        }
         st.thr = th - 1u;        // keys of finite scores are >= 1
         sampled = true;
     }
@@ -457,14 +460,16 @@ __device__ __forceinline__ uint32_t block_scan_nw(uint32_t v, uint32_t* wsum, ui
 
 // The selection for few query rows of moderate length (one block of eight waves
 // per row instead of segments and a merge): a threshold from 1,024 sampled
-// scores (about 2,048 of the row's scores above it) filters the row, each wave
-// compacting its contiguous eighth in order into LDS; an exact radix select
-// over those candidates finds the 512th largest key K and how many copies of it
-// are kept (the first, as in every selection here), and a block scan writes the
-// kept entries in ascending order.  When the sample misjudges (fewer than 512
+// scores (2,048 to 2,560 of the row's scores above it, by the sample; each wave
+// has room for 768, so a wave's eighth may hold half again its share) filters
+// the row, each wave
+// compacting its contiguous eighth in order into LDS; a block-wide search
+// halving the candidates' key range finds the 512th largest key K and how many
+// copies of it are kept (the first, as in every selection here), and a block
+// scan writes the kept entries in ascending order.  When the sample misjudges (fewer than 512
 // candidates, or more than the buffer holds) wave 0 selects the row exactly
 // with the one-segment streaming selection.
-constexpr int TR_WAVES = 8, TR_WCAP = 512;
+constexpr int TR_WAVES = 8, TR_WCAP = 768;
 __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const float* __restrict__ S, int64_t spad, int64_t entry_stride, int32_t* __restrict__ idx,
@@ -501,28 +506,34 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
 #pragma unroll
         for (int g = 0; g < 16; ++g) kr[g] = score_key(src[((int64_t)(64 * g + lane) * n) >> 10]);
         const uint32_t ks = (uint32_t)((2048ll * 1024 + n - 1) / n);   // < 512
-        uint32_t krem;
-        const uint32_t th = wave_threshold(wsel, kr, ks, ks + ks / 2, false, &krem);
+        uint32_t th = wave_threshold_bisect(kr, ks, ks + ks / 4);
+        if (th == 0u) {                 // repeated keys: the sample's ks-th largest
+            uint32_t krem;
+            th = wave_kth_bisect(kr, ks, &krem);
+        }
         if (lane == 0) bc[0] = th;
     }
     __syncthreads();
     const uint32_t th = bc[0];
-    // filter: wave w compacts the keys >= th of its run, in order
+    // filter: wave w compacts the keys >= th of its run, in order; 2,048 scores a
+    // step, the next step's loads issued before this one is compacted
     const int per = (n + TR_WAVES * 256 - 1) / (TR_WAVES * 256) * 256;
     const int r0 = wave * per, r1 = min(n, r0 + per);
     const uint64_t below = (1ull << lane) - 1ull;
     uint32_t nc = 0u;
     bool over = false;
-    for (int base = r0; base < r1; base += 1024) {
-        float4 v[4];
+    constexpr int FU = 8;                          // 16-byte loads a lane a step
+    auto ldc = [&](int base, float4 (&v)[FU]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < FU; ++u) {
             const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * (base + 256 * u + 4 * lane), 0, 0);
             v[u] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
                                __uint_as_float(w[3]));
         }
+    };
+    auto compact = [&](int base, const float4 (&v)[FU]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < FU; ++u) {
             const int i0 = base + 256 * u + 4 * lane;
             const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
             uint32_t k[4];
@@ -551,7 +562,19 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
                 nc += c;
             }
         }
-        if (over) break;
+    };
+    {
+        float4 va[FU], vb[FU];
+        if (r0 < r1) ldc(r0, va);
+        for (int base = r0; base < r1; base += 2 * 256 * FU) {
+            const int b1 = base + 256 * FU;
+            if (b1 < r1) ldc(b1, vb);
+            compact(base, va);
+            if (over || b1 >= r1) break;
+            if (b1 + 256 * FU < r1) ldc(b1 + 256 * FU, va);
+            compact(b1, vb);
+            if (over) break;
+        }
     }
     if (lane == 0) wcnt[wave] = over ? 0xFFFFFFFFu : nc;
     __syncthreads();
@@ -584,7 +607,7 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     auto slot_key = [&](int s) -> uint32_t {
         return (uint32_t)(s % TR_WCAP) < wcnt[s / TR_WCAP] ? ck[s] : 0u;
     };
-    constexpr int SPT = NSLOT / (64 * TR_WAVES);    // slots per thread: 8, consecutive
+    constexpr int SPT = NSLOT / (64 * TR_WAVES);    // slots per thread: 12, consecutive
     uint32_t kv[SPT];
 #pragma unroll
     for (int e = 0; e < SPT; ++e) kv[e] = slot_key(SPT * tid + e);
@@ -601,39 +624,48 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
 #pragma unroll
     for (int w = 0; w < TR_WAVES; ++w) { lo = min(lo, hist[w]); hi = max(hi, hist[TR_WAVES + w]); }
     __syncthreads();
-    uint32_t K = hi, krem = TOPK, eq_total = total;  // all candidates equal
-    if (lo < hi) {
-        int hib = 31 - __clz((int)(lo ^ hi));
-        uint32_t pmask = hib == 31 ? 0u : ~((2u << hib) - 1u);
-        uint32_t prefix = lo & pmask;
-        while (hib >= 0) {
-            const int lob = hib - 7 > 0 ? hib - 7 : 0;
-            const uint32_t dmask = (2u << (hib - lob)) - 1u;
-            if (tid < 256) hist[tid] = 0u;
-            __syncthreads();
+    // the 512th largest key K by halving [lo, hi] (block-wide counts), stopping
+    // early when exactly 512 keys reach the middle (K is then their minimum);
+    // krem = how many copies of K are kept, eq_total = how many there are
+    auto block_count = [&](uint32_t th2) -> uint32_t {     // keys >= th2 (th2 >= 1)
+        uint32_t c = 0u;
 #pragma unroll
-            for (int e = 0; e < SPT; ++e)
-                if (kv[e] != 0u && (kv[e] & pmask) == prefix) atomicAdd(&hist[(kv[e] >> lob) & dmask], 1u);
-            __syncthreads();
-            const int nbins = (int)dmask + 1;
-            const uint32_t h = tid < nbins ? hist[nbins - 1 - tid] : 0u;
-            uint32_t tot;
-            const uint32_t ex = block_scan_nw<TR_WAVES>(h, wsum, &tot);
-            if (tid < nbins && ex < krem && krem <= ex + h) {
-                bc[1] = (uint32_t)(nbins - 1 - tid);
-                bc[2] = ex;
-                bc[3] = h;
-            }
-            __syncthreads();
-            prefix |= bc[1] << lob;
-            pmask |= dmask << lob;
-            krem -= bc[2];
-            eq_total = bc[3];
-            hib = lob - 1;
-            __syncthreads();
+        for (int e = 0; e < SPT; ++e) c += kv[e] >= th2 ? 1u : 0u;
+        c = wave_sum(c);
+        if (lane == 0) wsum[wave] = c;
+        __syncthreads();
+        uint32_t t2 = 0u;
+#pragma unroll
+        for (int w = 0; w < TR_WAVES; ++w) t2 += wsum[w];
+        __syncthreads();
+        return t2;
+    };
+    uint32_t a = lo;
+    uint64_t bnd = (uint64_t)hi + 1u;
+    while (bnd - a > 1u) {
+        const uint32_t mid = (uint32_t)(a + ((bnd - a) >> 1));
+        const uint32_t c = block_count(mid);
+        if (c >= (uint32_t)TOPK) {
+            a = mid;
+            if (c == (uint32_t)TOPK) break;
+        } else {
+            bnd = mid;
         }
-        K = prefix;
     }
+    uint32_t mk = 0xFFFFFFFFu;                 // K: the smallest key >= a
+#pragma unroll
+    for (int e = 0; e < SPT; ++e)
+        if (kv[e] >= a) mk = min(mk, kv[e]);
+    mk = wave_min(mk);
+    if (lane == 0) wsum[wave] = mk;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TR_WAVES; ++w) mk = min(mk, wsum[w]);
+    __syncthreads();
+    const uint32_t K = mk;
+    const uint32_t above = block_count(K + 1u);
+    const uint32_t krem = (uint32_t)TOPK - above;
+    const uint32_t eq_total = block_count(K) - above;
     // ordered write: keys > K and the first krem keys == K
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll

@@ -660,23 +660,33 @@ def test_single_token_rows_sampled_start(dev, orc, N):
 
 def test_topk_row_paths(dev, orc):
     """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
-    three paths: a sampled threshold (20,000 candidates), every score kept without a
+    paths: a sampled threshold (20,000 candidates), every score kept without a
     sample (3,000), and the exact fallback when the sample cannot separate the scores
-    (all 20,000 keys identical: the first 512 entries)"""
+    (all 20,000 keys identical: the first 512 entries) or when the large scores sit
+    in one contiguous run (entries 5,000..7,499: the wave whose eighth holds them
+    has more candidates than room)"""
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     rng = np.random.default_rng(71)
-    B, Tq, N = 3, 2, 20_000
+    B, Tq, N = 4, 2, 20_000
     kc = np.zeros((B, N, 64), np.uint8)
     ks = np.zeros((B, N, 4), np.uint8)
     for b in range(2):
         kc[b], ks[b] = orc.fp4_encode(rng.standard_normal((N, 128)).astype(np.float32))
     one_c, one_s = orc.fp4_encode(rng.standard_normal((1, 128)).astype(np.float32))
     kc[2], ks[2] = one_c[0], one_s[0]
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    run = (np.arange(N) >= 5000) & (np.arange(N) < 7500)
+    kpre = rng.standard_normal((N, 128)) + np.where(run, 3.0, 0.0)[:, None] * u[None, :]
+    kc[3], ks[3] = orc.fp4_encode(kpre.astype(np.float32))
     import tests.test_oracle_compress as tc
-    qI = tc.bf16(rng.standard_normal((B, Tq, 32, 128)).astype(np.float32))
+    qpre = rng.standard_normal((B, Tq, 32, 128))
+    qpre[3] = 4.0 * u + 0.3 * rng.standard_normal((Tq, 32, 128))
+    qI = tc.bf16(qpre.astype(np.float32))
     wI = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
-    ne = np.array([N, 3000, N], np.int32)
+    wI[3] = np.abs(wI[3])
+    ne = np.array([N, 3000, N, N], np.int32)
     q0 = np.full(B, 2 * N, np.int32)
     log(f"k_topk_row paths: B={B} Tq={Tq} stride={N}")
     idx = torch.full((B, Tq, 512), -7, dtype=torch.int32, device=dev)
@@ -694,3 +704,11 @@ def test_topk_row_paths(dev, orc):
             check_selection(gi[b, i], gc_[b, i], r_idx, r_cnt, S)
             if b == 2:
                 assert np.array_equal(gi[b, i], np.arange(512)), "ties: the first 512 entries"
+            if b == 3:
+                # the construction does what it is for: above the sample's threshold
+                # (its 105th largest of 1,024 spread scores) one wave's eighth of the
+                # row holds more than its 768 slots
+                smp = S[(np.arange(1024) * n) >> 10]
+                th = np.sort(smp)[::-1][(2048 * 1024 + n - 1) // n - 1]
+                per = (n + 2047) // 2048 * 256
+                assert max(np.count_nonzero(S[w * per:(w + 1) * per] >= th) for w in range(8)) > 768
