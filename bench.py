@@ -33,16 +33,16 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.406e+10, {
+    ("k_attn", "prefill", 65536): (1.405e+10, {
         "attention.hip": "333b67d04f56b5d0765db48c76bc511fbc64d15312ed723ccb6ae03cf68ab3c2",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_select", "prefill", 65536): (5.120e+08, {
-        "index_select.hip": "7f0acd03267449fc81a4c2c603918b948c3ee2c2f29858c8246a237f056b124c",
-        "index_device.h": "7919782e2cbb25c2755c5323fe4b724e31987a53b36eb145c9945dd523e0d9f9",
+    ("k_index_select", "prefill", 65536): (4.827e+08, {
+        "index_select.hip": "cd09ef39a4afbf84a5508cc4c26ded44489607de93f0efceb4226d95dfde28d1",
+        "index_device.h": "4fc7954ba2e0f34237e857a40b9266a2588f34c652e09c4888bce58229cb8e7b",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
     ("k_index_scores", "decode", 131072): (6.088e+08, {
-        "indexer.hip": "38884e262d3bf8243d25b2eec70c0767aac1291aa8a79f09cabcbf7dc6488d2c",
-        "index_device.h": "7919782e2cbb25c2755c5323fe4b724e31987a53b36eb145c9945dd523e0d9f9",
+        "indexer.hip": "90268b84256a5ecd9b6717ec0692420efe6bc46bcc5cc15155248957dd7c612b",
+        "index_device.h": "4fc7954ba2e0f34237e857a40b9266a2588f34c652e09c4888bce58229cb8e7b",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
 }
 
