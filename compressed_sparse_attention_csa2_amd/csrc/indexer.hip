@@ -480,6 +480,7 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     __shared__ WaveSel wsel;
     __shared__ uint32_t wcnt[TR_WAVES];
     __shared__ uint32_t wsum[TR_WAVES];
+    __shared__ uint32_t wcount[2][TR_WAVES];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t bc[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -499,6 +500,22 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     const float* src = S + row * spad;              // spad: a multiple of 64 floats
     const __amdgpu_buffer_rsrc_t srb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)src, (short)0, 4 * ((n + 3) & ~3), 0x00020000);
+    // wave w filters its run [r0, r1) of the row, 8,192 scores a step held in
+    // registers; the first step's loads are issued before the threshold is
+    // known, so they overlap the sample
+    const int per = (n + TR_WAVES * 256 - 1) / (TR_WAVES * 256) * 256;
+    const int r0 = wave * per, r1 = min(n, r0 + per);
+    constexpr int FU = 32;                         // 16-byte loads a lane a step
+    float4 v[FU];
+    auto ldc = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < FU; ++u) {
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * (base + 256 * u + 4 * lane), 0, 0);
+            v[u] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                               __uint_as_float(w[3]));
+        }
+    };
+    if (r0 < r1) ldc(r0);
     if (n <= NSLOT) {                               // every score fits: no sample
         if (tid == 0) bc[0] = 1u;
     } else if (wave == 0) {
@@ -515,23 +532,11 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     }
     __syncthreads();
     const uint32_t th = bc[0];
-    // filter: wave w compacts the keys >= th of its run, in order; 2,048 scores a
-    // step, the next step's loads issued before this one is compacted
-    const int per = (n + TR_WAVES * 256 - 1) / (TR_WAVES * 256) * 256;
-    const int r0 = wave * per, r1 = min(n, r0 + per);
+    // the keys >= th of the run, compacted in order into the wave's region
     const uint64_t below = (1ull << lane) - 1ull;
     uint32_t nc = 0u;
     bool over = false;
-    constexpr int FU = 8;                          // 16-byte loads a lane a step
-    auto ldc = [&](int base, float4 (&v)[FU]) {
-#pragma unroll
-        for (int u = 0; u < FU; ++u) {
-            const auto w = __builtin_amdgcn_raw_buffer_load_b128(srb, 4 * (base + 256 * u + 4 * lane), 0, 0);
-            v[u] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
-                               __uint_as_float(w[3]));
-        }
-    };
-    auto compact = [&](int base, const float4 (&v)[FU]) {
+    auto compact = [&](int base) {
 #pragma unroll
         for (int u = 0; u < FU; ++u) {
             const int i0 = base + 256 * u + 4 * lane;
@@ -563,18 +568,10 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
             }
         }
     };
-    {
-        float4 va[FU], vb[FU];
-        if (r0 < r1) ldc(r0, va);
-        for (int base = r0; base < r1; base += 2 * 256 * FU) {
-            const int b1 = base + 256 * FU;
-            if (b1 < r1) ldc(b1, vb);
-            compact(base, va);
-            if (over || b1 >= r1) break;
-            if (b1 + 256 * FU < r1) ldc(b1 + 256 * FU, va);
-            compact(b1, vb);
-            if (over) break;
-        }
+    for (int base = r0; base < r1; base += 256 * FU) {
+        if (base != r0) ldc(base);
+        compact(base);
+        if (over) break;
     }
     if (lane == 0) wcnt[wave] = over ? 0xFFFFFFFFu : nc;
     __syncthreads();
@@ -627,17 +624,21 @@ __global__ void __launch_bounds__(64 * TR_WAVES) k_topk_row(
     // the 512th largest key K by halving [lo, hi] (block-wide counts), stopping
     // early when exactly 512 keys reach the middle (K is then their minimum);
     // krem = how many copies of K are kept, eq_total = how many there are
-    auto block_count = [&](uint32_t th2) -> uint32_t {     // keys >= th2 (th2 >= 1)
+    // keys >= th2 (th2 >= 1) over the block; one barrier a call: the wave totals
+    // alternate between two slot sets, and a set is rewritten only after the
+    // next call's barrier, which every reader of it has passed
+    int par = 0;
+    auto block_count = [&](uint32_t th2) -> uint32_t {
         uint32_t c = 0u;
 #pragma unroll
         for (int e = 0; e < SPT; ++e) c += kv[e] >= th2 ? 1u : 0u;
         c = wave_sum(c);
-        if (lane == 0) wsum[wave] = c;
+        if (lane == 0) wcount[par][wave] = c;
         __syncthreads();
         uint32_t t2 = 0u;
 #pragma unroll
-        for (int w = 0; w < TR_WAVES; ++w) t2 += wsum[w];
-        __syncthreads();
+        for (int w = 0; w < TR_WAVES; ++w) t2 += wcount[par][w];
+        par ^= 1;
         return t2;
     };
     uint32_t a = lo;
