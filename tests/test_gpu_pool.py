@@ -1,11 +1,12 @@
 """GPU parity of the hierarchical candidate pool and the Reindex selection
 (csa2_index_pool, csa2_reindex_topk) through the C ABI, against the oracle.
 
-Three requests over a 20,000-entry index-key cache with 2% of the entries
+Four requests over a 20,000-entry index-key cache with 2% of the entries
 copying earlier entries' bytes (exact score ties), queried at positions where
 the rows see 20,000 / about 18,000 entries (more than 2,048 blocks of 8: the
-pool is a real subset, the newest block partial) and about 9,000 entries
-(every block in the pool).  Checks: the Full selection as csa2_index_topk; the
+pool is a real subset, the newest block partial), about 9,000 entries (every
+block in the pool) and about 3,000 entries (fewer than 512 blocks: Reindex
+selects from a list shorter than the one-block-per-row kernel's sample size).  Checks: the Full selection as csa2_index_topk; the
 pool block sets (boundary swaps between blocks whose oracle keys agree to
 1e-5 relative, as for the top-512); the newest block present; Reindex with
 another layer's query over the oracle's pool against the oracle's Reindex
@@ -61,7 +62,7 @@ def test_pool_and_reindex_match_oracle(ratio):
     from csa2_harness import up, down
 
     rng = np.random.default_rng(41)
-    B, Tq, N = 3, 3, 20_000
+    B, Tq, N = 4, 3, 20_000
     kc = np.zeros((B, N, 64), np.uint8)
     ks = np.zeros((B, N, 4), np.uint8)
     for b in range(B):
@@ -74,7 +75,7 @@ def test_pool_and_reindex_match_oracle(ratio):
     wI = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
     qI2 = _bf16(rng.standard_normal((B, Tq, 32, 128)))
     wI2 = (rng.standard_normal((B, Tq, 32)) / 64).astype(np.float32)
-    q_pos0 = np.array([ratio * N, ratio * 18_001 - 1, ratio * 9_000], np.int32)
+    q_pos0 = np.array([ratio * N, ratio * 18_001 - 1, ratio * 9_000, ratio * 3_000], np.int32)
     n_entries = np.full(B, N, np.int32)
     log(f"csa2_index_pool / csa2_reindex_topk: B={B} Tq={Tq} N={N} ratio={ratio}")
 
