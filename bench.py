@@ -37,7 +37,7 @@ TRAFFIC = {
         "attention.hip": "333b67d04f56b5d0765db48c76bc511fbc64d15312ed723ccb6ae03cf68ab3c2",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
     ("k_index_select", "prefill", 65536): (4.827e+08, {
-        "index_select.hip": "cd09ef39a4afbf84a5508cc4c26ded44489607de93f0efceb4226d95dfde28d1",
+        "index_select.hip": "5fdd172ede2fae924619737dcf18698bfcc5853990b4fb175acce9ad3d8a7243",
         "index_device.h": "4fc7954ba2e0f34237e857a40b9266a2588f34c652e09c4888bce58229cb8e7b",
         "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
     ("k_index_scores", "decode", 131072): (6.088e+08, {

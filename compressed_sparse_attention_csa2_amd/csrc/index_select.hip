@@ -14,21 +14,25 @@
 // scales, lane-swap head sums) as the score-only kernel, so every score is the
 // same fp32 value.  After a tile, lane row g holds token g's 16 scores; each
 // is compared with that token's running threshold and the passing ones are
-// appended, in entry order, to the token's candidate buffer in LDS (ballot
-// ranks, no branch: lanes that do not pass write a spare slot).  When a buffer
-// is nearly full, a wave-wide search over it (halving the key range, counting
-// with compares and a DPP sum) finds a key theta with at least 512 candidates
-// at or above it and at most `keep`, keeps those in order and makes theta the
-// token's new (strict) threshold: a later entry equal to theta ranks below
-// every kept one, which has a smaller j.
+// appended, in entry order, to the token's candidate buffer in LDS (a DPP
+// prefix count over the lane row gives the slots; no branch: lanes that do not
+// pass write a spare slot).  Long lists start from a threshold scored on a
+// sample of 16 tiles spread over the entries (a token left with too few
+// candidates is scanned again from minus infinity); without it the threshold
+// starts at minus infinity and the buffers fill many more times.  When a
+// buffer is nearly full, a wave-wide search over it (halving the key range,
+// counting with compares and a DPP sum) finds a key theta with at least 512
+// candidates at or above it and at most `keep`, keeps those in order and makes
+// theta the token's new (strict) threshold: a later entry equal to theta ranks
+// below every kept one, which has a smaller j.
 // At the end an exact select keeps the 512 largest (ties: smaller j).
 //
-// Segments: prefill rows are many and each wave takes all of its tokens'
-// entries (one segment).  Decode rows are few and long, so a row is cut into
-// segments; each segment's wave writes its winners (at most 512 keys and
-// entries, its 512th and ceil(512/nseg)-th keys), and the last segment wave of
-// a row to finish -- counted with a device-scope atomic per row -- merges them
-// while other rows are still being scanned.
+// Segments: when the token groups are many, each wave takes all of its
+// tokens' entries (one segment).  When they are too few to fill the GPU, a row
+// is cut into segments; each segment's wave writes its winners (at most 512
+// keys and entries, its 512th and ceil(512/nseg)-th keys), and the last
+// segment wave of a row to finish -- counted with a device-scope atomic per
+// row -- merges them while other rows are still being scanned.
 #include "index_device.h"
 
 namespace csa2 {
@@ -48,7 +52,8 @@ template <int TOK> struct SelCfg {
     static constexpr int keep = cap - 192;
     static constexpr int waves = TOK == 1 ? 3 : (TOK == 4 ? 2 : 1);
 };
-// lists at least this long start from a sampled threshold (four-token form)
+// lists at least this long start from a sampled threshold (the four-token form,
+// and single-token rows up to 65,536 entries)
 constexpr int SAMPLE_MIN = 4096;
 
 template <int TOK>
