@@ -157,12 +157,12 @@ int attn_split(int64_t tokens) {
 }
 
 // Segments per query row for the selection: enough lists (one wave each) to
-// fill the chip when rows are few, at most 16 segments of at least 8192 entries
-// (B=128 decode over 65,536 entries: 8 segments beat 16 and 4; 96 rows over
-// 524,288 entries want all 16).
+// fill the chip when rows are few, at most 32 segments of at least 8192 entries
+// (96 rows over 524,288 entries: 32 segments 455 us, 16 559 us, 48 or 64
+// 480-488 us; B=128 decode over 65,536 entries: 8 segments beat 16 and 4).
 int topk_segments(int64_t rows, int64_t stride) {
-    int64_t ns = cdiv(4096, rows > 0 ? rows : 1);
-    if (ns > 16) ns = 16;
+    int64_t ns = cdiv(8192, rows > 0 ? rows : 1);
+    if (ns > 32) ns = 32;
     const int64_t by_len = stride / 8192;
     if (ns > by_len) ns = by_len;
     return ns < 1 ? 1 : (int)ns;
