@@ -60,7 +60,8 @@ __global__ void k_index_select(int, int, const int32_t*, const int32_t*, const u
                                int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*,
                                uint32_t*, uint32_t*);
 __global__ void k_zero_u32(uint32_t*, int64_t);
-template <int HG>
+__global__ void k_z_fp8_rows(int64_t, const uint8_t*, const uint8_t*, uint8_t*, float*);
+template <int HG, bool ZF8>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
                        const int32_t*, const float*, const float*, const float*, int64_t,
@@ -258,13 +259,24 @@ size_t index_topk_ws(int B, int Tq, int64_t stride) {
                                                   : select_ws(B, Tq, stride).total;
 }
 
+// Attention reads the compressed rows re-encoded as E4M3 rows with an fp32 row
+// scale (k_z_fp8_rows, once per call) when the call gathers each entry of the
+// caches at least four times on average (Tq * 512 >= 4 * entry_stride: a
+// prefill), and the re-encoded rows stay within the kernel's 32-bit offsets.
+bool attn_zf8(int B, int Tq, int64_t stride) {
+    return (int64_t)Tq * TOPK >= 4 * stride && stride * 512 <= (int64_t)0xFFFFFFFF &&
+           (int64_t)B * stride <= ((int64_t)1 << 26);
+}
+
 struct AttnWs {
     int nsplit;
-    size_t pO, pml, total;
+    bool zf8;
+    size_t pO, pml, zq, zs, total;
 };
-AttnWs attn_ws(int B, int Tq, int H) {
+AttnWs attn_ws(int B, int Tq, int H, int64_t stride) {
     AttnWs w;
     w.nsplit = attn_split((int64_t)B * Tq);
+    w.zf8 = attn_zf8(B, Tq, stride);
     w.pO = 0;
     w.pml = 0;
     w.total = 0;
@@ -272,6 +284,13 @@ AttnWs attn_ws(int B, int Tq, int H) {
         const size_t n = (size_t)B * Tq * w.nsplit * H;
         w.pml = align256(n * D * sizeof(float));
         w.total = w.pml + align256(n * 2 * sizeof(float));
+    }
+    w.zq = w.total;
+    w.zs = w.zq;
+    if (w.zf8) {
+        const size_t ne = (size_t)B * (size_t)stride;
+        w.zs = w.zq + align256(ne * D);
+        w.total = w.zs + align256(ne * sizeof(float));
     }
     return w;
 }
@@ -414,7 +433,7 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     if (z_format == 1) {
         // rows in the pages' format: the dequantising kernel, one block per (query,
         // split); the splits' partials are merged as on the per-32 path
-        const AttnWs L = attn_ws(B, Tq, H);
+        const AttnWs L = attn_ws(B, Tq, H, stride);
         float* pO = (float*)((uint8_t*)ws + L.pO);
         float* pml = (float*)((uint8_t*)ws + L.pml);
         const int64_t units = (int64_t)B * Tq * L.nsplit;
@@ -434,24 +453,43 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
     if ((int64_t)cap * D > (int64_t)0xFFFFFFFF || stride * 256 > (int64_t)0xFFFFFFFF)
         return fail(CSA2_ERR_RANGE, "sparse_attn: cap=%d (at most 8388607) or entry stride=%lld "
                     "(at most 16777215) too large", cap, (long long)stride);
-    const AttnWs L = attn_ws(B, Tq, H);
+    const AttnWs L = attn_ws(B, Tq, H, stride);
     float* pO = (float*)((uint8_t*)ws + L.pO);
     float* pml = (float*)((uint8_t*)ws + L.pml);
+    if (L.zf8) {
+        // the compressed rows in the window's format (E4M3 + fp32 row scale)
+        uint8_t* zq = (uint8_t*)ws + L.zq;
+        float* zsf = (float*)((uint8_t*)ws + L.zs);
+        const int64_t ne = (int64_t)B * stride;
+        hipLaunchKernelGGL(k_z_fp8_rows, dim3((unsigned)cdiv(ne, 8)), dim3(256), 0, st, ne,
+                           z_codes, z_scales, zq, zsf);
+        z_codes = zq;
+        z_scales = (const uint8_t*)zsf;
+    }
     // persistent blocks (one per compute unit) walk the (row, split) units
     const int64_t units = (int64_t)B * Tq * L.nsplit;
     if (units > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
     const int64_t nblk = units < device_cus() ? units : device_cus();
     const dim3 grid((unsigned)nblk);
     const int ht = H / 16;   // head tiles of 16
-#define CSA2_ATTN(HTV)                                                                         \
-    hipLaunchKernelGGL(k_attn<HTV>, grid, dim3(ATT_THREADS), 0, st, B, Tq, H, q_pos0, Q, w_codes,        \
-                       w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,        \
+#define CSA2_ATTN(HTV, ZF)                                                                     \
+    hipLaunchKernelGGL((k_attn<HTV, ZF>), grid, dim3(ATT_THREADS), 0, st, B, Tq, H, q_pos0, Q,     \
+                       w_codes, w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,   \
                        rope_rows, O, lse, L.nsplit, pO, pml, win_floor)
-    switch (ht) {
-        case 1: CSA2_ATTN(1); break;
-        case 2: CSA2_ATTN(2); break;
-        case 3: CSA2_ATTN(3); break;
-        default: CSA2_ATTN(4); break;
+    if (L.zf8) {
+        switch (ht) {
+            case 1: CSA2_ATTN(1, true); break;
+            case 2: CSA2_ATTN(2, true); break;
+            case 3: CSA2_ATTN(3, true); break;
+            default: CSA2_ATTN(4, true); break;
+        }
+    } else {
+        switch (ht) {
+            case 1: CSA2_ATTN(1, false); break;
+            case 2: CSA2_ATTN(2, false); break;
+            case 3: CSA2_ATTN(3, false); break;
+            default: CSA2_ATTN(4, false); break;
+        }
     }
 #undef CSA2_ATTN
     if (L.nsplit > 1) {
@@ -490,9 +528,9 @@ size_t csa2_workspace_size(int op, int B, int Tq, int H, int64_t entry_stride) {
     if (op == CSA2_OP_INDEX_POOL) return pool_ws(B, Tq, entry_stride).total;
     if (op == CSA2_OP_REINDEX) return reindex_ws(B, Tq).total;
     if (H < 16 || H > 64 || H % 16) return 0;
-    if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H).total;
+    if (op == CSA2_OP_SPARSE_ATTN) return attn_ws(B, Tq, H, entry_stride).total;
     if (op == CSA2_OP_FORWARD) {
-        size_t a = index_topk_ws(B, Tq, entry_stride), c = attn_ws(B, Tq, H).total;
+        size_t a = index_topk_ws(B, Tq, entry_stride), c = attn_ws(B, Tq, H, entry_stride).total;
         return (a > c ? a : c) + align256((size_t)B * sizeof(int32_t));
     }
     return 0;
@@ -734,7 +772,7 @@ csa2_status csa2_sparse_attn(int B, int Tq, int H, const int32_t* q_pos0, const 
     if ((int64_t)cap < (int64_t)Tq + WINDOW - 1)
         return fail(CSA2_ERR_RANGE, "sparse_attn: window ring cap=%d < Tq+127=%lld", cap, (long long)Tq + WINDOW - 1);
     if (rope_rows < 1) return fail(CSA2_ERR_RANGE, "sparse_attn: empty rotary table");
-    const size_t need = attn_ws(B, Tq, H).total;
+    const size_t need = attn_ws(B, Tq, H, entry_stride).total;
     if (Tq > 0 && need > 0 && (!ws || ws_bytes < need))
         return fail(CSA2_ERR_WORKSPACE, "sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
     csa2_status s = launch_attn(B, Tq, H, q_pos0, Q, w_codes, w_scale, cap, z_codes, z_scales,

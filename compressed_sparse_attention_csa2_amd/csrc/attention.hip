@@ -109,7 +109,7 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 // P [head][32 rows] bf16, 64 bytes per head: unit u at u ^ ((h >> 2) & 3)
 __device__ __forceinline__ int pb_off(int h, int u) { return h * 64 + ((u ^ ((h >> 2) & 3)) << 4); }
 
-template <int HT>
+template <int HT, bool ZF8>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     int B, int Tq, int H, const int32_t* __restrict__ q_pos0, const uint16_t* __restrict__ Q,
     const uint8_t* __restrict__ w_codes, const float* __restrict__ w_scale, int cap,
@@ -294,14 +294,29 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             const bool info = wave == 0 && (i & 63) == 0 && unit_at(i + 64) < nunits;
             if (info) info_issue(i + 64);
             const int nch = k_end > k_begin ? k_end - k_begin : 0;
-            const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * 256;
-            const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * 16;
+            const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * (ZF8 ? 512 : 256);
+            const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * (ZF8 ? 4 : 16);
             auto bufi = [&](int k) { return (rb0 + k - k_begin) % NRAW; };
             // compressed chunk k (k < k_end) of this unit
             auto stage_cmp = [&](int k) {
                 const int buf = bufi(k);
                 const int base = (k - nwch) * CH;
                 const int nv = min(ncmp - base, CH);
+                if constexpr (ZF8) {
+                    // FP8 rows of 512 bytes, as the window's; QK wave q copies rows 8q..8q+7
+#pragma unroll
+                    for (int h2 = 0; h2 < 4; ++h2) {
+                        const int rr = 8 * q4 + 2 * h2 + (lane >> 5), j = lane & 31;
+                        const int e = min(max(sidx[base + (rr < nv ? rr : 0)], 0), emax);
+                        dma16s(zc0, (uint32_t)e * 512u + 16u * (uint32_t)(j ^ (rr & 15)),
+                               lds_addr(&rawc[buf][(8 * q4 + 2 * h2) * 512]));
+                    }
+                    if (wave == 0 && lane < CH) {
+                        const int e2 = min(max(sidx[base + (lane < nv ? lane : 0)], 0), emax);
+                        dma4s(zs0, 4u * (uint32_t)e2, lds_addr(&rscl[buf][0]));
+                    }
+                    return;
+                }
                 const int ra = 8 * q4 + (lane >> 4), rb = ra + 4;
                 const int e0 = min(max(sidx[base + (ra < nv ? ra : 0)], 0), emax);
                 const int e1 = min(max(sidx[base + (rb < nv ? rb : 0)], 0), emax);
@@ -388,7 +403,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             float m_used = -INFINITY, l_lane = 0.0f;
             auto chunk = [&](int k, auto win_c) {
                 constexpr bool WIN = decltype(win_c)::value;
-                constexpr int RB = WIN ? 512 : 256;      // row bytes
+                constexpr bool F8 = WIN || ZF8;          // rows of E4M3 codes with an fp32 row scale
+                constexpr int RB = F8 ? 512 : 256;       // row bytes
                 // lane coordinates re-derived per chunk: keeps the per-lane
                 // offsets below (and in the copies) from being held across the loop
                 asm volatile("" : "+v"(lane));
@@ -404,7 +420,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 // the products go first on the SIMD: the softmax waits on them
                 __builtin_amdgcn_s_setprio(2);
                 if (qk_on) {
-                    if constexpr (WIN) {
+                    if constexpr (F8) {
                         // operands of block m + 1 are read while block m multiplies
                         auto ld = [&](int m, i8& a0, i8& a1) {
                             const int u0 = 16 * ((8 * m + g) ^ n16), u1 = 16 * ((8 * m + 4 + g) ^ n16);
@@ -465,8 +481,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     float s[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        s[i] = acc0[i] * (WIN ? lscale * rs0[i] : lscale);
-                        s[4 + i] = acc1[i] * (WIN ? lscale * rs1[i] : lscale);
+                        s[i] = acc0[i] * (F8 ? lscale * rs0[i] : lscale);
+                        s[4 + i] = acc1[i] * (F8 ? lscale * rs1[i] : lscale);
                     }
                     if (nv < CH) {
 #pragma unroll
@@ -487,7 +503,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     for (int i = 0; i < 8; ++i) {
                         const float e = __builtin_amdgcn_exp2f(s[i] - m_used);
                         ps += e;
-                        pv[i] = WIN ? e * (i < 4 ? rs0[i] : rs1[i - 4]) : e;
+                        pv[i] = F8 ? e * (i < 4 ? rs0[i] : rs1[i - 4]) : e;
                     }
                     l_lane = l_lane * corr + ps;
                     uint8_t* pb0 = (uint8_t*)&Pb[buf][0] + pb_off(h, (4 * g) >> 3) + 2 * ((4 * g) & 7);
@@ -639,7 +655,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             const int sr = 8 * g + (n16 >> 1), sh = n16 & 1;   // source row and half of this lane
             auto convert = [&](int k, bf8 (&a)[4]) {
                 const int rb = bufi(k);
-                if (k < nwch) {
+                if (ZF8 || k < nwch) {
                     const uint8_t* rrow = &rawc[rb][sr * 512];
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
@@ -712,8 +728,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             const int nwin = U.nwin, ncmp = U.ncmp, slot0 = U.slot0;
             const uint8_t* wrow0 = w_codes + (int64_t)U.b * cap * D;
             const float* wsc = w_scale + (int64_t)U.b * cap;
-            const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * 256;
-            const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * 16;
+            const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * (ZF8 ? 512 : 256);
+            const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * (ZF8 ? 4 : 16);
             auto copy_chunk = [&](int k) {
                 if (k >= k_end) return;
                 const int buf = bufi(k);
@@ -732,6 +748,20 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         int slot = slot0 + base + (lane < nv ? lane : 0);
                         slot = slot >= cap ? slot - cap : slot;
                         dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
+                    }
+                } else if constexpr (ZF8) {
+                    const int base = (k - nwch) * CH;
+                    const int nv = min(ncmp - base, CH);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int rr = 4 * p8 + 2 * h2 + (lane >> 5), j = lane & 31;
+                        const int e = min(max(sidx[base + (rr < nv ? rr : 0)], 0), emax);
+                        dma16s(zc0, (uint32_t)e * 512u + 16u * (uint32_t)(j ^ (rr & 15)),
+                               lds_addr(&rawc[buf][(4 * p8 + 2 * h2) * 512]));
+                    }
+                    if (p8 == 0 && lane < CH) {
+                        const int e2 = min(max(sidx[base + (lane < nv ? lane : 0)], 0), emax);
+                        dma4s(zs0, 4u * (uint32_t)e2, lds_addr(&rscl[buf][0]));
                     }
                 } else {
                     const int base = (k - nwch) * CH;
@@ -780,6 +810,53 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         // the last unit's output
         if (nmine > 0) output(Uprev, (nmine - 1) & 1);
     }
+}
+
+// FP4 rows (E2M1 codes, one E8M0 scale per 32 channels) rewritten as E4M3
+// rows with one fp32 scale per row, for attention calls that gather each
+// entry many times (a prefill): the attention kernel then reads every row in
+// the window's format.  Row scale S = 2^(Emax - 127 - 6) for the row's largest
+// block exponent byte Emax; element x * 2^(E_b - 127) becomes the E4M3 code of
+// x * 2^(E_b - Emax + 6), at most 6 * 2^6 = 384.  That is exact whenever every
+// block exponent is within 14 of the row's largest (E4M3 keeps two significant
+// bits down to 2^-8); a smaller block rounds to nearest even.  32 lanes per
+// entry, 16 elements each.
+__global__ void __launch_bounds__(256) k_z_fp8_rows(int64_t n, const uint8_t* __restrict__ zc,
+                                                    const uint8_t* __restrict__ zs,
+                                                    uint8_t* __restrict__ oc,
+                                                    float* __restrict__ os) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+    const int l = threadIdx.x & 31;
+    if (e >= n) return;
+    const uint4 sv = *(const uint4*)(zs + e * 16);
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint32_t emx = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) emx = max(emx, (sw[w] >> (8 * b)) & 0xFFu);
+    const int eb = (int)((sw[l >> 3] >> (8 * ((l >> 1) & 3))) & 0xFFu);
+    const float f = ldexpf(1.0f, eb - (int)emx + 6);
+    const uint2 c = *(const uint2*)(zc + e * 256 + 8 * l);
+    const uint32_t cw[2] = {c.x, c.y};
+    uint32_t out[4];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t q[8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f2 v = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 0)
+                       : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 1)
+                       : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 2)
+                                : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 3);
+            q[2 * b] = e4m3_code(v[0] * f);
+            q[2 * b + 1] = e4m3_code(v[1] * f);
+        }
+        out[2 * w] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        out[2 * w + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+    }
+    *(uint4*)(oc + e * 512 + 16 * l) = make_uint4(out[0], out[1], out[2], out[3]);
+    if (l == 0) os[e] = ldexpf(1.0f, (int)emx - 133);
 }
 
 // Merge split partials: one wave per (token, head), lane owns channels 8l..8l+7.
@@ -836,17 +913,21 @@ __global__ void __launch_bounds__(256) k_attn_combine(
     if (lse && lane == 0) lse[((int64_t)b * H + h) * Tq + t] = (M + log2f(den)) * 0.6931471805599453f;
 }
 
-#define CSA2_ATTN_INST(HTV)                                                                    \
-    template __global__ void k_attn<HTV>(int, int, int, const int32_t*, const uint16_t*,       \
+#define CSA2_ATTN_INST(HTV, ZF)                                                                \
+    template __global__ void k_attn<HTV, ZF>(int, int, int, const int32_t*, const uint16_t*,   \
                                          const uint8_t*, const float*, int, const uint8_t*,    \
                                          const uint8_t*, int64_t, const int32_t*,              \
                                          const int32_t*, const float*, const float*,           \
                                          const float*, int64_t, uint16_t*, float*, int, float*, \
                                          float*, const int32_t*);
-CSA2_ATTN_INST(1)
-CSA2_ATTN_INST(2)
-CSA2_ATTN_INST(3)
-CSA2_ATTN_INST(4)
+CSA2_ATTN_INST(1, false)
+CSA2_ATTN_INST(2, false)
+CSA2_ATTN_INST(3, false)
+CSA2_ATTN_INST(4, false)
+CSA2_ATTN_INST(1, true)
+CSA2_ATTN_INST(2, true)
+CSA2_ATTN_INST(3, true)
+CSA2_ATTN_INST(4, true)
 #undef CSA2_ATTN_INST
 
 }  // namespace csa2

@@ -51,8 +51,13 @@ def test_workspace_sizes(L):
     assert ws(csa2.OP_FORWARD, 1, 256, 16, 128) > 0
     assert ws(csa2.OP_FORWARD, 1, 256, 17, 128) == 0          # heads not a multiple of 16
     assert ws(csa2.OP_FORWARD, 0, 256, 16, 128) == 0
-    assert ws(csa2.OP_SPARSE_ATTN, 1, 65536, 64, 32768) == 0  # one split: no partials
+    # a prefill: one split (no partials); the compressed rows re-encoded as E4M3
+    # rows with an fp32 scale (512 + 4 bytes per entry), each 256-byte aligned
+    assert ws(csa2.OP_SPARSE_ATTN, 1, 65536, 64, 32768) == 32768 * 512 + 32768 * 4
     assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) > 0     # decode splits the rows
+    # decode gathers each entry less than four times on average: no re-encoding
+    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) < 128 * 65536 * 516
+    assert ws(csa2.OP_SPARSE_ATTN, 16, 6, 64, 524288) < 16 * 524288 * 516
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
