@@ -99,6 +99,13 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// max of three floats in one instruction (the logits are never NaN; no quieting)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // the two E2M1 codes of byte SEL of w, times sc, as packed bf16 (low nibble first)
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float sc) {
@@ -401,9 +408,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             // running maximum (log2 units) of head h and this lane's share of
             // its denominator (rows 4g..4g+3 and 16+4g..16+4g+3 of every chunk)
             float m_used = -INFINITY, l_lane = 0.0f;
+            // the raw logit (Q.G, before the 1/sqrt(512) and log2 e factors) above
+            // which a chunk moves the running maximum: (m_used + TAU) / lscale
+            float m_thr = -INFINITY;
             auto chunk = [&](int k, auto win_c) {
                 constexpr bool WIN = decltype(win_c)::value;
-                constexpr bool F8 = WIN || ZF8;          // rows of E4M3 codes with an fp32 row scale
+                constexpr bool F8 = WIN || ZF8;          // rows of E4M3 codes with a row scale
                 constexpr int RB = F8 ? 512 : 256;       // row bytes
                 // lane coordinates re-derived per chunk: keeps the per-lane
                 // offsets below (and in the copies) from being held across the loop
@@ -412,20 +422,36 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const int buf = k & 1, rbuf = bufi(k);
                 const int base = WIN ? k * CH : (k - nwch) * CH;
                 const int nv = min((WIN ? nwin : ncmp) - base, CH);
-                // lane (tile t2, row 16 t2 + n16, group g); row & 15 = n16
-                const uint8_t* rrow0 = &rawc[rbuf][n16 * RB];
-                const uint8_t* rrow1 = &rawc[rbuf][(16 + n16) * RB];
                 f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = f4{0.f, 0.f, 0.f, 0.f};
-                float rs0[4] = {1.f, 1.f, 1.f, 1.f}, rs1[4] = {1.f, 1.f, 1.f, 1.f};
+                float4 r0 = make_float4(1.f, 1.f, 1.f, 1.f), r1 = r0;
                 // the products go first on the SIMD: the softmax waits on them
                 __builtin_amdgcn_s_setprio(2);
                 if (qk_on) {
                     if constexpr (F8) {
-                        // operands of block m + 1 are read while block m multiplies
+                        // Lane (row n16 of tile 0 and 16 + n16 of tile 1, group g)
+                        // takes 16-byte units (8m + g) ^ n16 and (8m + 4 + g) ^ n16
+                        // of its rows for channel block m.  With X = g ^ n16 (< 16)
+                        // those are X ^ 8(m & 1) + 16(m >> 1) and the same ^ 4, so
+                        // the byte addresses are A, A ^ 64, A ^ 128, A ^ 192 (m = 0,
+                        // 1) and the same + 256 (m = 2, 3); tile 1 is 16 rows on.
+                        const uint32_t A = lds_addr(&rawc[rbuf][0]) + (uint32_t)(n16 * 512 + 16 * (g ^ n16));
+                        const uint32_t Ad[4] = {A, A ^ 64u, A ^ 128u, A ^ 192u};
+                        auto rd = [&](uint32_t a) {
+                            const i4 v = *(const __attribute__((address_space(3))) i4*)(size_t)a;
+                            return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+                        };
+                        // row scales: the window's fp32 scales multiply the products
+                        // below; the re-encoded compressed rows' scales are powers of
+                        // two and enter the product as the rows' E8M0 block scale
+                        int sa0 = 127, sa1 = 127;
+                        if constexpr (!WIN) {
+                            sa0 = (int)((__float_as_uint(rscl[rbuf][n16]) >> 23) & 0xFFu);
+                            sa1 = (int)((__float_as_uint(rscl[rbuf][16 + n16]) >> 23) & 0xFFu);
+                        }
                         auto ld = [&](int m, i8& a0, i8& a1) {
-                            const int u0 = 16 * ((8 * m + g) ^ n16), u1 = 16 * ((8 * m + 4 + g) ^ n16);
-                            const uint4 x0 = *(const uint4*)(rrow0 + u0), x1 = *(const uint4*)(rrow0 + u1);
-                            const uint4 y0 = *(const uint4*)(rrow1 + u0), y1 = *(const uint4*)(rrow1 + u1);
+                            const uint32_t o = 256u * (uint32_t)(m >> 1);
+                            const uint4 x0 = rd(Ad[2 * (m & 1)] + o), x1 = rd(Ad[2 * (m & 1) + 1] + o);
+                            const uint4 y0 = rd(Ad[2 * (m & 1)] + o + 8192u), y1 = rd(Ad[2 * (m & 1) + 1] + o + 8192u);
                             a0 = i8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
                             a1 = i8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
                         };
@@ -436,18 +462,18 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                             i8 b0, b1;
                             if (m < 3) ld(m + 1, b0, b1);
                             const int sh = (int)((qsh >> (8 * m)) & 0xFFu), sl = (int)((qsl >> (8 * m)) & 0xFFu);
-                            acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qh[m], acc0, 0, 0, 0, 127, 0, sh);
-                            acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qh[m], acc1, 0, 0, 0, 127, 0, sh);
-                            acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, ql[m], acc0, 0, 0, 0, 127, 0, sl);
-                            acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, ql[m], acc1, 0, 0, 0, 127, 0, sl);
+                            acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qh[m], acc0, 0, 0, 0, sa0, 0, sh);
+                            acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qh[m], acc1, 0, 0, 0, sa1, 0, sh);
+                            acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, ql[m], acc0, 0, 0, 0, sa0, 0, sl);
+                            acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, ql[m], acc1, 0, 0, 0, sa1, 0, sl);
                             __builtin_amdgcn_sched_barrier(0);
                             if (m < 3) { a0 = b0; a1 = b1; }
                         }
-                        const float4 r0 = *(const float4*)&rscl[rbuf][4 * g];
-                        const float4 r1 = *(const float4*)&rscl[rbuf][16 + 4 * g];
-                        rs0[0] = r0.x; rs0[1] = r0.y; rs0[2] = r0.z; rs0[3] = r0.w;
-                        rs1[0] = r1.x; rs1[1] = r1.y; rs1[2] = r1.z; rs1[3] = r1.w;
+                        r0 = *(const float4*)&rscl[rbuf][4 * g];
+                        r1 = *(const float4*)&rscl[rbuf][16 + 4 * g];
                     } else {
+                        const uint8_t* rrow0 = &rawc[rbuf][n16 * RB];
+                        const uint8_t* rrow1 = &rawc[rbuf][(16 + n16) * RB];
                         // the rows' scale bytes regrouped for lane group g: byte m = block 4m + g
                         const uint4 z0 = *(const uint4*)&zsc[rbuf][n16][0];
                         const uint4 z1 = *(const uint4*)&zsc[rbuf][16 + n16][0];
@@ -476,34 +502,45 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 asm volatile("" : "+v"(acc0), "+v"(acc1));
                 __builtin_amdgcn_s_setprio(0);
                 // ---- softmax: wave-local running maximum with headroom --------
+                // x: this lane's raw logits (rows 4g..4g+3 and 16+4g..16+4g+3 of the
+                // chunk, head h).  The running maximum m_used (log2 units) moves
+                // only when some logit passes it by TAU: the lane compares its own
+                // largest logit with m_thr, and only when a lane of the wave passes
+                // does the wave take the head's maximum over its four lanes.
                 uint32_t moved = 0;
                 if (qk_on) {
-                    float s[8];
+                    const float rs[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                    float x[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        s[i] = acc0[i] * (F8 ? lscale * rs0[i] : lscale);
-                        s[4 + i] = acc1[i] * (F8 ? lscale * rs1[i] : lscale);
+                        x[i] = WIN ? acc0[i] * rs[i] : acc0[i];
+                        x[4 + i] = WIN ? acc1[i] * rs[4 + i] : acc1[i];
                     }
                     if (nv < CH) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            s[i] = 4 * g + i < nv ? s[i] : -INFINITY;
-                            s[4 + i] = 16 + 4 * g + i < nv ? s[4 + i] : -INFINITY;
+                            x[i] = 4 * g + i < nv ? x[i] : -INFINITY;
+                            x[4 + i] = 16 + 4 * g + i < nv ? x[4 + i] : -INFINITY;
                         }
                     }
-                    const float lm = rows_max(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                                                    fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
+                    const float lmax = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], x[7]));
                     float corr = 1.0f;
-                    if (lm > m_used + LAZY_TAU) {
-                        corr = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - lm);
-                        m_used = lm;
+                    if (__builtin_amdgcn_ballot_w64(lmax > m_thr) != 0) {
+                        const float lm = rows_max(lmax) * lscale;
+                        if (lm > m_used + LAZY_TAU) {
+                            corr = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - lm);
+                            m_used = lm;
+                            m_thr = (lm + LAZY_TAU) * (1.0f / lscale);
+                        }
+                        if (g == 0) corb[buf][n16][q4] = corr;
+                        moved = __builtin_amdgcn_ballot_w64(corr != 1.0f) != 0;
                     }
                     float ps = 0.0f, pv[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(s[i] - m_used);
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], lscale, -m_used));
                         ps += e;
-                        pv[i] = F8 ? e * (i < 4 ? rs0[i] : rs1[i - 4]) : e;
+                        pv[i] = e * rs[i];
                     }
                     l_lane = l_lane * corr + ps;
                     uint8_t* pb0 = (uint8_t*)&Pb[buf][0] + pb_off(h, (4 * g) >> 3) + 2 * ((4 * g) & 7);
@@ -512,8 +549,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                                               __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[2], (__bf16)pv[3]}));
                     *(uint2*)pb1 = make_uint2(__builtin_bit_cast(uint32_t, bf2{(__bf16)pv[4], (__bf16)pv[5]}),
                                               __builtin_bit_cast(uint32_t, bf2{(__bf16)pv[6], (__bf16)pv[7]}));
-                    if (g == 0) corb[buf][n16][q4] = corr;
-                    moved = __builtin_amdgcn_ballot_w64(corr != 1.0f) != 0;
                 }
                 if (lane == 0) cflag[buf][q4] = moved;
                 // B(k): P, corrections and flags of chunk k visible; this wave's
@@ -710,8 +745,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 for (int ht = 0; ht < HT; ++ht)
                     pb[ht] = *(const bf8*)((const uint8_t*)&Pb[bp][0] + pb_off(16 * ht + n16, g));
                 if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+                    // a QK wave writes its corrections only in a chunk where it moved
+                    // a maximum: the head tiles of the others keep theirs
                     const float4 c4 = *(const float4*)&corb[bp][n16][0];
-                    const float cr[4] = {c4.x, c4.y, c4.z, c4.w};
+                    const float cr[4] = {fl.x ? c4.x : 1.0f, fl.y ? c4.y : 1.0f, fl.z ? c4.z : 1.0f,
+                                         fl.w ? c4.w : 1.0f};
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -730,6 +768,15 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             const float* wsc = w_scale + (int64_t)U.b * cap;
             const uint8_t* zc0 = z_codes + (int64_t)U.b * entry_stride * (ZF8 ? 512 : 256);
             const uint8_t* zs0 = z_scales + (int64_t)U.b * entry_stride * (ZF8 ? 4 : 16);
+            // the entries of the two rows this wave copies in compressed chunk kk
+            // (re-encoded rows), read one phase ahead of their copies
+            auto cmp_entries = [&](int kk, int& e0, int& e1) {
+                const int base = min(max(kk - nwch, 0), TOPK / CH - 1) * CH;
+                const int r = 4 * p8 + (lane >> 5);
+                e0 = sidx[base + r];
+                e1 = sidx[base + r + 2];
+            };
+            int ce0 = 0, ce1 = 0;
             auto copy_chunk = [&](int k) {
                 if (k >= k_end) return;
                 const int buf = bufi(k);
@@ -750,12 +797,15 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                         dma4s(wsc, 4u * (uint32_t)slot, lds_addr(&rscl[buf][0]));
                     }
                 } else if constexpr (ZF8) {
+                    // rows past the chunk's end copy whatever entry their slot names,
+                    // clamped into the cache: every re-encoded row is finite, and
+                    // their logits are masked
                     const int base = (k - nwch) * CH;
                     const int nv = min(ncmp - base, CH);
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int rr = 4 * p8 + 2 * h2 + (lane >> 5), j = lane & 31;
-                        const int e = min(max(sidx[base + (rr < nv ? rr : 0)], 0), emax);
+                        const int e = min(max(h2 ? ce1 : ce0, 0), emax);
                         dma16s(zc0, (uint32_t)e * 512u + 16u * (uint32_t)(j ^ (rr & 15)),
                                lds_addr(&rawc[buf][(4 * p8 + 2 * h2) * 512]));
                     }
@@ -785,6 +835,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             // B(k_begin + 3)
             auto phase = [&](int k, const bf8 (&ap)[4], bf8 (&an)[4]) {
                 copy_chunk(k + 4);
+                if constexpr (ZF8) cmp_entries(k + 5, ce0, ce1);
                 if (k > k_begin) pv(k - 1, ap);
                 // the products go out first; the conversion runs while they (and
                 // the other waves of the SIMD) use the matrix core
@@ -797,6 +848,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 else barrier_vm<0>();
             };
             bf8 a0[4], a1[4];
+            if constexpr (ZF8) cmp_entries(k_begin + 4, ce0, ce1);
             for (int k = k_begin; k < k_end; ++k) {
                 phase(k, a1, a0);
 #pragma unroll
@@ -815,12 +867,14 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
 // FP4 rows (E2M1 codes, one E8M0 scale per 32 channels) rewritten as E4M3
 // rows with one fp32 scale per row, for attention calls that gather each
 // entry many times (a prefill): the attention kernel then reads every row in
-// the window's format.  Row scale S = 2^(Emax - 127 - 6) for the row's largest
-// block exponent byte Emax; element x * 2^(E_b - 127) becomes the E4M3 code of
+// the window's format.  Row scale S = 2^(Emax - 127 - 6), Emax the larger of
+// the row's largest block exponent byte and 7 (S is a normal number, and a
+// power of two, so the kernel passes it to the matrix unit as the row's E8M0
+// scale); element x * 2^(E_b - 127) becomes the E4M3 code of
 // x * 2^(E_b - Emax + 6), at most 6 * 2^6 = 384.  That is exact whenever every
-// block exponent is within 14 of the row's largest (E4M3 keeps two significant
-// bits down to 2^-8); a smaller block rounds to nearest even.  32 lanes per
-// entry, 16 elements each.
+// block exponent is within 14 of Emax (E4M3 keeps two significant bits down to
+// 2^-8); a smaller block rounds to nearest even.  32 lanes per entry, 16
+// elements each.
 __global__ void __launch_bounds__(256) k_z_fp8_rows(int64_t n, const uint8_t* __restrict__ zc,
                                                     const uint8_t* __restrict__ zs,
                                                     uint8_t* __restrict__ oc,
@@ -830,7 +884,7 @@ __global__ void __launch_bounds__(256) k_z_fp8_rows(int64_t n, const uint8_t* __
     if (e >= n) return;
     const uint4 sv = *(const uint4*)(zs + e * 16);
     const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-    uint32_t emx = 0;
+    uint32_t emx = 7;       // at least 7: the row scale stays a normal fp32 number
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
