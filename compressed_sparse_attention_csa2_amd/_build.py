@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "index_select.hip", "attention.hip",
-           "attention_dq.hip"]
+SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "index_select.hip", "decode_select.hip",
+           "attention.hip", "attention_dq.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

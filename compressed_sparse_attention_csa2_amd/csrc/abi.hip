@@ -60,6 +60,14 @@ __global__ void k_index_select(int, int, const int32_t*, const int32_t*, const u
                                int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*,
                                uint32_t*, uint32_t*);
 __global__ void k_zero_u32(uint32_t*, int64_t);
+__global__ void k_fs_threshold(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
+                               const uint8_t*, const uint8_t*, int64_t, int, uint32_t*);
+__global__ void k_fs_scan(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
+                          const uint8_t*, const uint8_t*, int64_t, int, int, const uint32_t*,
+                          uint32_t*, int32_t*, int32_t*);
+__global__ void k_fs_select(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
+                            const uint8_t*, const uint8_t*, int64_t, int, int, const uint32_t*,
+                            const uint32_t*, const int32_t*, const int32_t*, int32_t*, int32_t*);
 __global__ void k_z_fp8_rows(int64_t, const uint8_t*, const uint8_t*, uint8_t*, float*);
 template <int HG, bool ZF8>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
@@ -254,9 +262,34 @@ SelWs select_ws(int B, int Tq, int64_t stride) {
 }
 
 bool two_pass_rows(int B, int Tq, int64_t stride);
+
+// Single-token rows over long caches (batched decode): a sampled threshold, a
+// scan that keeps only the keys at or above it (FS_WCAP slots per chunk of
+// IDX_CHUNK entries, in entry order) and a cut of those; no score row.
+bool fs_rows(int B, int Tq, int64_t stride) { return Tq == 1 && two_pass_rows(B, Tq, stride); }
+struct FsWs {
+    int n_ch;
+    size_t q8, wq, th, ccnt, ck, cj, total;
+};
+FsWs fs_ws(int B, int64_t stride) {
+    FsWs w;
+    const size_t rows = (size_t)B;
+    w.n_ch = (int)cdiv(stride, IDX_CHUNK);
+    const size_t slots = rows * (size_t)w.n_ch * FS_WCAP;
+    w.q8 = 0;
+    w.wq = align256(rows * HI * DI);
+    w.th = w.wq + align256(rows * HI * sizeof(float));
+    w.ccnt = w.th + align256(rows * sizeof(uint32_t));
+    w.ck = w.ccnt + align256(rows * (size_t)w.n_ch * sizeof(int32_t));
+    w.cj = w.ck + align256(slots * sizeof(uint32_t));
+    w.total = w.cj + align256(slots * sizeof(int32_t));
+    return w;
+}
+
 size_t index_topk_ws(int B, int Tq, int64_t stride) {
+    if (fs_rows(B, Tq, stride)) return fs_ws(B, stride).total;
     return two_pass_rows(B, Tq, stride) ? index_ws(B, Tq, stride).total
-                                                  : select_ws(B, Tq, stride).total;
+                                        : select_ws(B, Tq, stride).total;
 }
 
 // Attention reads the compressed rows re-encoded as E4M3 rows with an fp32 row
@@ -358,6 +391,28 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
                          const uint8_t* ki_scales, int64_t stride, int rsh, int32_t* idx,
                          int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
+    if (fs_rows(B, Tq, stride)) {
+        const FsWs L = fs_ws(B, stride);
+        uint8_t* base = (uint8_t*)ws;
+        uint8_t* q8 = base + L.q8;
+        float* wq = (float*)(base + L.wq);
+        uint32_t* th = (uint32_t*)(base + L.th);
+        int32_t* ccnt = (int32_t*)(base + L.ccnt);
+        uint32_t* ck = (uint32_t*)(base + L.ck);
+        int32_t* cj = (int32_t*)(base + L.cj);
+        const int64_t qrows = (int64_t)B * HI;
+        hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 16)), dim3(256), 0, st,
+                           qI, wI, qrows, q8, wq);
+        hipLaunchKernelGGL(k_fs_threshold, dim3((unsigned)B), dim3(256), 0, st, B, q_pos0,
+                           n_entries, q8, wq, ki_codes, ki_scales, stride, rsh, th);
+        hipLaunchKernelGGL(k_fs_scan, dim3((unsigned)cdiv((int64_t)B * L.n_ch, 4)), dim3(256), 0,
+                           st, B, q_pos0, n_entries, q8, wq, ki_codes, ki_scales, stride, L.n_ch,
+                           rsh, (const uint32_t*)th, ck, cj, ccnt);
+        hipLaunchKernelGGL(k_fs_select, dim3((unsigned)B), dim3(512), 0, st, B, q_pos0, n_entries,
+                           q8, wq, ki_codes, ki_scales, stride, L.n_ch, rsh, (const uint32_t*)th,
+                           (const uint32_t*)ck, (const int32_t*)cj, (const int32_t*)ccnt, idx, cnt);
+        return check_launch("csa2_index_topk");
+    }
     if (two_pass_rows(B, Tq, stride))
         return launch_index_2pass(B, Tq, q_pos0, n_entries, qI, wI, ki_codes, ki_scales, stride,
                                   rsh, idx, cnt, ws, st);

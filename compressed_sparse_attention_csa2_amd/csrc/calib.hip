@@ -6,20 +6,28 @@
 
 namespace {
 
-// Grid-stride reads of 16 bytes per thread, four loads in flight; the values
-// are folded into one word that is stored only if it equals a fixed pattern,
-// so the loads cannot be removed and almost nothing is written.
+// Every block reads one contiguous span, 16 bytes per thread and step, eight
+// steps in flight, with non-temporal loads (data read once; on this device
+// the hint is worth about 15% of read bandwidth).  The values are folded into
+// one word that is stored only if it equals a fixed pattern, so the loads
+// cannot be removed and almost nothing is written.
 __global__ void __launch_bounds__(256) k_read(const uint4* __restrict__ p, int64_t n16,
                                               uint32_t* __restrict__ sink) {
+    typedef __attribute__((ext_vector_type(4))) unsigned int u4v;
+    constexpr int U = 8;
     uint32_t acc = 0u;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-               d.z ^ d.w;
+    const int64_t per = n16 / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = blockIdx.x + 1 == gridDim.x ? n16 : lo + per;
+    int64_t i = lo + threadIdx.x;
+    for (; i + (U - 1) * 256 < hi; i += U * 256) {
+        u4v v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load((const u4v*)(p + i + u * 256));
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
-    for (; i < n16; i += stride) {
+    for (; i < hi; i += 256) {
         const uint4 a = p[i];
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }

@@ -1,0 +1,428 @@
+// Top-512 of single-token query rows over long caches (batched decode) without
+// writing the rows' scores.
+//
+// "DeepSeek V4.1 -- Pooled group -> Source layer, pairs pooled", indexer and
+// top-k equations: S^I_{t,j} = sum_h w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j) and
+// I_t = top_512(S^I_{t,j} : j < floor((t+1)/2)) (the entries' ratio in place
+// of 2).  "Inside DeepSeek V4.1", section "Attention that looks at 640
+// places": every compressed entry is scored, 512 go on to attention.
+//
+// A decode step reads each request's index keys once, so its time is the key
+// stream; writing every fp32 score and reading it back for the selection cost
+// as much as a third of that stream again.  Three passes instead:
+//   k_fs_threshold  one block per row scores 1,024 entries spread evenly over
+//                   the row and takes a key th that ceil(2^21 / n) of the
+//                   sample reach (about 2,048 of the row's n scores by the
+//                   sample);
+//   k_fs_scan       one wave per (row, chunk of IDX_CHUNK entries) scores the
+//                   chunk and keeps the keys >= th with their entries, in entry
+//                   order, in the chunk's own slots (no atomics, so the order
+//                   survives);
+//   k_fs_select     one block per row gathers the chunks' candidates in order
+//                   and cuts the exact top 512 (ties: smaller entry) by halving
+//                   the key range.
+// When at least 512 keys reach th, the 512th largest key is >= th, so every
+// key of the top 512 -- and every copy of the 512th -- is a candidate, and the
+// cut equals the full selection.  When the sample misjudges (fewer than 512
+// candidates, a chunk's slots overflow, or more candidates than the cut holds)
+// and for rows of 513..FS_MIN-1 entries, one wave of k_fs_select scores the
+// whole row again and selects it exactly with the streaming selection.
+// Scores are the same fp32 values the other indexer kernels produce (the same
+// products, head-sum order and lane sums).
+#include "index_device.h"
+
+namespace csa2 {
+
+constexpr int FS_MIN = 16384;                      // shorter rows: the fallback
+constexpr int FS_WAVES = 8;                        // waves of a select block
+constexpr int FS_NSLOT = FS_WAVES * 768;           // candidates a select block cuts
+constexpr uint32_t FS_ALL = 0xFFFFFFFFu;           // threshold word: at most 512 entries, take all
+constexpr uint32_t FS_SLOW = 0u;                   // threshold word: select by the fallback
+
+// The row's index query as FP8 MFMA operands and its folded head weights.
+// Lane (col, grp): head col of each 16-head tile, channel bytes 16grp..+15 and
+// 64+16grp..+15 (the A layout against an FP4 B operand), weights of heads
+// 4grp..4grp+3 of each tile.
+struct RowQuery {
+    i8 A[2];
+    f4 W[2];
+    __device__ __forceinline__ void load(const uint8_t* q8, const float* wq, int64_t row, int col,
+                                         int grp) {
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const int64_t hr = row * HI + tile * 16;
+            const uint8_t* src = q8 + (hr + col) * DI + 16 * grp;
+            const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 64);
+            A[tile] = i8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                         (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+            const float4 w4 = *(const float4*)(wq + hr + 4 * grp);
+            W[tile] = f4{w4.x, w4.y, w4.z, w4.w};
+        }
+    }
+    // this lane's part of the head sum for its entry of a 16-entry tile: the
+    // tile's FP4 codes (16 bytes, block grp) and that block's E8M0 scale sc
+    __device__ __forceinline__ float partial(const uint4 kc, int sc) const {
+        const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+        const f4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            A[0], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        const f4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            A[1], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[0][i], relu(d0[i]), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[1][i], relu(d1[i]), acc);
+        return acc;
+    }
+};
+
+// entries of a single-token row (request b at its position q_pos0[b])
+__device__ __forceinline__ int fs_row_len(const int32_t* q_pos0, const int32_t* n_entries, int b,
+                                          int64_t entry_stride, int rsh) {
+    int64_t n = cand_count(q_pos0[b], 0, n_entries[b], entry_stride, rsh);
+    return (int)(n < 0 ? 0 : (n > entry_stride ? entry_stride : n));
+}
+
+// ---- threshold: one block of four waves per row ----------------------------
+__global__ void __launch_bounds__(256) k_fs_threshold(
+    int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int rsh, uint32_t* __restrict__ th_out) {
+    __shared__ uint32_t skey[1024];
+    const int b = blockIdx.x;
+    if (b >= B) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
+    if (n <= TOPK || n < FS_MIN) {
+        if (tid == 0) th_out[b] = n <= TOPK ? FS_ALL : FS_SLOW;
+        return;
+    }
+    RowQuery q;
+    q.load(q8, wq, b, col, grp);
+    const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
+    const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
+    // wave w scores samples 256w .. 256w + 255 (sample i is entry floor(i n / 1024)),
+    // sixteen tiles of sixteen; four tiles' sums leave through one row-sum scatter
+#pragma unroll
+    for (int u0 = 0; u0 < 16; u0 += 4) {
+        uint4 kc[4];
+        int sc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int i = 256 * wave + 16 * (u0 + g) + col;
+            const int64_t e = ((int64_t)i * n) >> 10;
+            kc[g] = *(const uint4*)(kb + e * 64);
+            sc[g] = (int)sb[e * 4];
+        }
+        float p[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) p[g] = q.partial(kc[g], sc[g]);
+        // lane 16g + col now holds sample 256w + 16(u0 + g) + col
+        skey[256 * wave + 16 * u0 + lane] = score_key(rowsum_scatter4(p[0], p[1], p[2], p[3]));
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t kr[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) kr[g] = skey[64 * g + lane];
+        const uint32_t ks = (uint32_t)((2048ll * 1024 + n - 1) / n);     // <= 128
+        uint32_t th = wave_threshold_bisect(kr, ks, ks + ks / 4);
+        if (th == 0u) {                 // repeated keys: the sample's ks-th largest
+            uint32_t krem;
+            th = wave_kth_bisect(kr, ks, &krem);
+        }
+        if (lane == 0) th_out[b] = th;   // a key of a finite score: never 0 or FS_ALL
+    }
+}
+
+// ---- filter: one wave per (row, chunk) --------------------------------------
+// ck/cj [B][n_ch][FS_WCAP]: the chunk's keys >= th and their entries, in entry
+// order; ccnt [B][n_ch]: how many passed (more than FS_WCAP: the slots overflowed).
+__global__ void __launch_bounds__(256) k_fs_scan(
+    int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int n_ch, int rsh, const uint32_t* __restrict__ th_in,
+    uint32_t* __restrict__ ck, int32_t* __restrict__ cj, int32_t* __restrict__ ccnt) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)B * n_ch) return;
+    const int b = (int)(item / n_ch), ch = (int)(item - (int64_t)b * n_ch);
+    const uint32_t th = th_in[b];
+    if (th == FS_ALL || th == FS_SLOW) return;            // the select pass handles the row
+    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
+    const int j_begin = ch * IDX_CHUNK;
+    const int64_t slot0 = item * FS_WCAP;
+    if (j_begin >= n) {
+        if (lane == 0) ccnt[item] = 0;
+        return;
+    }
+    const int j_len = min(IDX_CHUNK, n - j_begin);
+    const int col = lane & 15, grp = lane >> 4;
+    RowQuery q;
+    q.load(q8, wq, b, col, grp);
+    // the query and weights complete before the key stream starts, so the
+    // loop's waits only ever count key loads
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* kbase = ki_codes + ((int64_t)b * entry_stride + j_begin) * 64 + 16 * grp;
+    const uint8_t* sbase = ki_scales + ((int64_t)b * entry_stride + j_begin) * 4 + grp;
+    // each key is read by this wave only: non-temporal loads; each lane loads the
+    // one scale byte its block needs
+    auto load = [&](int jt, uint4& kc, uint32_t& sw) {
+        int j = jt + col;
+        j = j < j_len ? j : j_len - 1;
+        const u4v k4 = __builtin_nontemporal_load((const u4v*)(kbase + (int64_t)j * 64));
+        kc = uint4{k4[0], k4[1], k4[2], k4[3]};
+        sw = __builtin_nontemporal_load(sbase + (int64_t)j * 4);
+    };
+    const uint64_t below = (1ull << lane) - 1ull;
+    int nc = 0;
+    uint4 kb[8];
+    uint32_t sb[8];
+#pragma unroll
+    for (int p = 0; p < 7; ++p) {           // issued in tile order (the waits count on it)
+        load(16 * p, kb[p], sb[p]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int jt = 0; jt < j_len; jt += 128) {
+        float sp[4];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            load(jt + 16 * (p + 7), kb[(p + 7) & 7], sb[(p + 7) & 7]);
+            sp[p & 3] = q.partial(kb[p], (int)sb[p]);
+            if ((p & 3) == 3) {
+                // lane l: entry jt + 16(p - 3) + l of the chunk
+                const int jl = jt + 16 * (p - 3) + lane;
+                const float tot = rowsum_scatter4(sp[0], sp[1], sp[2], sp[3]);
+                const uint32_t key = jl < j_len ? score_key(tot) : 0u;
+                const bool adm = key != 0u && key >= th;
+                const uint64_t m = __ballot(adm);
+                const int pos = nc + (int)__popcll(m & below);
+                if (adm && pos < FS_WCAP) {
+                    ck[slot0 + pos] = key;
+                    cj[slot0 + pos] = j_begin + jl;
+                }
+                nc += (int)__popcll(m);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (lane == 0) ccnt[item] = nc;
+}
+
+// Exclusive prefix sum over the block (FS_WAVES waves); *tot = the block total.
+__device__ __forceinline__ uint32_t fs_block_scan(uint32_t v, uint32_t* wsum, uint32_t* tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_scan_add(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < FS_WAVES; ++w) {
+        const uint32_t x = wsum[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    __syncthreads();
+    *tot = all;
+    return before + inc - v;
+}
+
+// ---- cut: one block of FS_WAVES waves per row --------------------------------
+__global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
+    int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int n_ch, int rsh, const uint32_t* __restrict__ th_in,
+    const uint32_t* __restrict__ ck, const int32_t* __restrict__ cj,
+    const int32_t* __restrict__ ccnt, int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+    __shared__ uint32_t sk[FS_NSLOT];
+    __shared__ int32_t sj[FS_NSLOT];
+    __shared__ WaveSel wsel;
+    __shared__ uint32_t wsum[FS_WAVES];
+    __shared__ uint32_t wcount[2][FS_WAVES];
+    __shared__ uint32_t bc[2 * FS_WAVES + 2];
+    __shared__ uint32_t spre[2 * 64 * FS_WAVES];     // a gather pass's chunk offsets and counts
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x;
+    if (b >= B) return;
+    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
+    int32_t* out = idx + (int64_t)b * TOPK;
+    const uint32_t th = th_in[b];
+    if (th == FS_ALL) {
+        for (int i = tid; i < TOPK; i += 64 * FS_WAVES) out[i] = i < n ? i : -1;
+        if (tid == 0) cnt[b] = n;
+        return;
+    }
+    // the chunks' counts: total, and whether any chunk overflowed its slots
+    uint32_t total = 0u;
+    bool bad = th == FS_SLOW;
+    if (!bad) {
+        uint32_t t = 0u, over = 0u;
+        for (int c = tid; c < n_ch; c += 64 * FS_WAVES) {
+            const int k = ccnt[(int64_t)b * n_ch + c];
+            over |= (uint32_t)(k < 0 || k > FS_WCAP);
+            t += (uint32_t)(k < 0 ? 0 : (k > FS_WCAP ? FS_WCAP : k));
+        }
+        t = wave_sum(t);
+        over = wave_max(over);
+        if (lane == 0) { bc[wave] = t; bc[FS_WAVES + wave] = over; }
+        __syncthreads();
+        uint32_t ov = 0u;
+#pragma unroll
+        for (int w = 0; w < FS_WAVES; ++w) { total += bc[w]; ov |= bc[FS_WAVES + w]; }
+        __syncthreads();
+        bad = ov != 0u || total < (uint32_t)TOPK || total > (uint32_t)FS_NSLOT;
+    }
+    if (bad) {
+        // the exact selection of the whole row: wave 0 scores it again, 64
+        // entries a step (one per lane, in entry order), into the streaming selection
+        if (wave != 0) return;
+        const int col = lane & 15, grp = lane >> 4;
+        RowQuery q;
+        q.load(q8, wq, b, col, grp);
+        const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
+        const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
+        WaveTopk st{wsel, 0, 0u};
+        for (int jt = 0; jt < n; jt += 64) {
+            float p[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                int e = jt + 16 * g + col;
+                e = e < n ? e : n - 1;
+                const uint4 kc = *(const uint4*)(kb + (int64_t)e * 64);
+                p[g] = q.partial(kc, (int)sb[(int64_t)e * 4]);
+            }
+            const float tot = rowsum_scatter4(p[0], p[1], p[2], p[3]);
+            const uint32_t k[4] = {jt + lane < n ? score_key(tot) : 0u, 0u, 0u, 0u};
+            const int32_t jj[4] = {jt + lane, 0, 0, 0};
+            st.push(k, jj);
+        }
+        const int c = st.finish(out, nullptr, nullptr);
+        if (lane == 0) cnt[b] = c;
+        return;
+    }
+    // gather the candidates in entry order: chunk c's to slots pre[c] .., the
+    // chunks' offsets by a block scan, 512 chunks a pass; wave w copies chunks
+    // w, w + 8, .. of the pass, a lane per candidate
+    {
+        uint32_t run = 0u;                 // slots before this pass's chunks
+        for (int c0 = 0; c0 < n_ch; c0 += 64 * FS_WAVES) {
+            const int c = c0 + tid;
+            uint32_t k = 0u;
+            if (c < n_ch) {
+                const int kk = ccnt[(int64_t)b * n_ch + c];
+                k = (uint32_t)(kk < 0 ? 0 : kk);
+            }
+            uint32_t tot;
+            const uint32_t pre = run + fs_block_scan(k, wsum, &tot);
+            spre[tid] = pre;
+            spre[64 * FS_WAVES + tid] = k;
+            __syncthreads();
+            const int nc = min(n_ch - c0, 64 * FS_WAVES);
+            for (int cc = wave; cc < nc; cc += FS_WAVES) {
+                const uint32_t p0 = spre[cc], kc = spre[64 * FS_WAVES + cc];
+                const int64_t s0 = ((int64_t)b * n_ch + c0 + cc) * FS_WCAP;
+                for (uint32_t i = lane; i < kc; i += 64) {
+                    sk[p0 + i] = ck[s0 + i];
+                    sj[p0 + i] = cj[s0 + i];
+                }
+            }
+            __syncthreads();
+            run += tot;
+        }
+    }
+    // the 512th largest key K by halving the key range (block-wide counts),
+    // stopping early when exactly 512 keys reach the middle; then keys > K and
+    // the first (512 - #(> K)) copies of K, written in ascending entry order
+    constexpr int SPT = FS_NSLOT / (64 * FS_WAVES);      // consecutive slots per thread
+    uint32_t kv[SPT];
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        const int s = SPT * tid + e;
+        kv[e] = s < (int)total ? sk[s] : 0u;
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        if (kv[e] != 0u) lo = min(lo, kv[e]);
+        hi = max(hi, kv[e]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) { bc[wave] = lo; bc[FS_WAVES + wave] = hi; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < FS_WAVES; ++w) { lo = min(lo, bc[w]); hi = max(hi, bc[FS_WAVES + w]); }
+    __syncthreads();
+    int par = 0;
+    // keys >= th2 (th2 >= 1) over the block; one barrier a call (the wave totals
+    // alternate between two slot sets)
+    auto block_count = [&](uint32_t th2) -> uint32_t {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < SPT; ++e) c += kv[e] >= th2 ? 1u : 0u;
+        c = wave_sum(c);
+        if (lane == 0) wcount[par][wave] = c;
+        __syncthreads();
+        uint32_t t2 = 0u;
+#pragma unroll
+        for (int w = 0; w < FS_WAVES; ++w) t2 += wcount[par][w];
+        par ^= 1;
+        return t2;
+    };
+    uint32_t a = lo;
+    uint64_t bnd = (uint64_t)hi + 1u;
+    while (bnd - a > 1u) {
+        const uint32_t mid = (uint32_t)(a + ((bnd - a) >> 1));
+        const uint32_t c = block_count(mid);
+        if (c >= (uint32_t)TOPK) {
+            a = mid;
+            if (c == (uint32_t)TOPK) break;
+        } else {
+            bnd = mid;
+        }
+    }
+    uint32_t mk = 0xFFFFFFFFu;                 // K: the smallest key >= a
+#pragma unroll
+    for (int e = 0; e < SPT; ++e)
+        if (kv[e] >= a) mk = min(mk, kv[e]);
+    mk = wave_min(mk);
+    if (lane == 0) wsum[wave] = mk;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < FS_WAVES; ++w) mk = min(mk, wsum[w]);
+    __syncthreads();
+    const uint32_t K = mk;
+    const uint32_t above = block_count(K + 1u);
+    const uint32_t krem = (uint32_t)TOPK - above;
+    const uint32_t eq_total = block_count(K) - above;
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        gt += kv[e] > K;
+        eq += kv[e] == K;
+    }
+    uint32_t take = eq;
+    if (krem < eq_total) {
+        uint32_t eq_tot;
+        const uint32_t rank0 = fs_block_scan(eq, wsum, &eq_tot);
+        take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+    }
+    uint32_t sel_tot;
+    uint32_t off = fs_block_scan(gt + take, wsum, &sel_tot);
+    uint32_t taken = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+        const bool keep = kv[e] > K || (kv[e] == K && taken < take);
+        if (keep) {
+            out[off++] = sj[SPT * tid + e];
+            taken += kv[e] == K;
+        }
+    }
+    if (tid == 0) cnt[b] = TOPK;
+}
+
+}  // namespace csa2

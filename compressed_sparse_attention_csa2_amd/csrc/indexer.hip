@@ -241,15 +241,20 @@ __global__ void __launch_bounds__(256) k_index_scores(
         put(ngroups * 64 - 16, 0, s0, s1, s2, s3);
         return;
     }
+    // Few query rows per request (decode, verify): each key is read by one wave
+    // only, so the loads are non-temporal (they stream past the caches).
+    // Each lane loads the one scale byte its 32-channel block needs (no byte
+    // extraction, which the compiler would hoist ahead of the loop's waits).
     auto load = [&](int jt, uint4& kc, uint32_t& sw) {
         int j = jt + col;
         j = j < j_len ? j : j_len - 1;
-        kc = *(const uint4*)(kbase + (int64_t)j * 64);
-        sw = *(const uint32_t*)(sbase + (int64_t)j * 4);
+        const u4v k4 = __builtin_nontemporal_load((const u4v*)(kbase + (int64_t)j * 64));
+        kc = uint4{k4[0], k4[1], k4[2], k4[3]};
+        sw = __builtin_nontemporal_load(sbase + (int64_t)j * 4 + grp);
     };
     // loads are clamped to the chunk, so always issued
     auto step = [&](int jt, const uint4 kc, const uint32_t sw) {
-        const int sc = (int)((sw >> (8 * grp)) & 0xFFu);
+        const int sc = (int)sw;
         const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
         float s[TOK];
         constexpr int KG = TOK < 4 ? TOK : 4;     // tokens whose products are issued together
@@ -294,10 +299,63 @@ __global__ void __launch_bounds__(256) k_index_scores(
             }
         }
     };
-    // NB tile buffers rotate (eight for the single-token scan, whose registers
-    // allow it): tile jt + 16p lives in buffer p % NB and is loaded NB - 1 tiles
-    // ahead; no buffer is copied, so no wait lands on a load just issued.
-    constexpr int NB = TOK == 1 ? 8 : 4;
+    if constexpr (TOK == 1) {
+        // One query row: the head sums of four tiles go through one row-sum
+        // scatter, which leaves tile g's sums on lane row g, so lane l holds the
+        // score of entry jt + l and the four tiles leave in one coalesced store.
+        // Eight tile buffers rotate: tile jt + 16p lives in buffer p and is loaded
+        // seven tiles ahead.
+        const __amdgpu_buffer_rsrc_t srs1 = __builtin_amdgcn_make_buffer_rsrc(
+            Sbase, (short)0, ncand[0] * 4, 0x00020000);
+        auto partial = [&](const uint4 kc, const uint32_t sw) {
+            const int sc = (int)sw;
+            const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+            const f4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A[0][0], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+            const f4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A[0][1], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[0][0][i], relu(d0[i]), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[0][1][i], relu(d1[i]), acc);
+            return acc;
+        };
+        // the query and weights complete before the key stream starts, so the
+        // loop's waits only ever count key loads (otherwise the loop head waits
+        // for every load in flight on each pass)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint4 kb[8];
+        uint32_t sb[8];
+        // issued in tile order (the loop's waits count on it)
+#pragma unroll
+        for (int p = 0; p < 7; ++p) {
+            load(16 * p, kb[p], sb[p]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int jt = 0; jt < j_len; jt += 128) {
+            float sp[4];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                // tile p + 7 goes into the buffer tile p - 1 used (a fixed rotation,
+                // so every wait is on the oldest loads)
+                load(jt + 16 * (p + 7), kb[(p + 7) & 7], sb[(p + 7) & 7]);
+                sp[p & 3] = partial(kb[p], sb[p]);
+                if ((p & 3) == 3) {
+                    const float tot = rowsum_scatter4(sp[0], sp[1], sp[2], sp[3]);
+                    // entries past the row's candidates fall outside the resource: dropped
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), srs1,
+                                                          4 * (jt + 16 * (p - 3) + lane), 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+    // NB tile buffers rotate: tile jt + 16p lives in buffer p % NB and is loaded
+    // NB - 1 tiles ahead; no buffer is copied, so no wait lands on a load just
+    // issued.
+    constexpr int NB = 4;
     uint4 kb[NB];
     uint32_t sb[NB];
 #pragma unroll

@@ -40,9 +40,10 @@ def test_workspace_sizes(L):
     # the selection is fused into the scoring: no score rows, only the quantised
     # queries (4,224 bytes per query row) -- and segment winners when rows are few
     assert 65536 * 4224 <= ws(csa2.OP_INDEX_TOPK, 1, 65536, 64, 32768) < 65536 * 4224 + 4096
-    # few long rows (decode, verify) keep their score rows: the selection pass after
-    # it is faster there
-    assert ws(csa2.OP_INDEX_TOPK, 128, 1, 64, 65536) >= 128 * 65536 * 4
+    # single-token rows over long caches (decode): no score rows, only the kept
+    # candidates (512 slots of key and entry per 2,048 entries: 2 bytes an entry)
+    assert 128 * 65536 * 2 <= ws(csa2.OP_INDEX_TOPK, 128, 1, 64, 65536) < 128 * 65536 * 2 + 2**20
+    # few long multi-token rows (verify) keep their score rows
     assert ws(csa2.OP_INDEX_TOPK, 16, 6, 64, 524288) >= 96 * 524288 * 4
     # many single-token rows stay fused: segment winners only
     assert ws(csa2.OP_INDEX_TOPK, 2048, 1, 64, 8192) < 2048 * 8192 * 4 // 4
