@@ -60,14 +60,20 @@ __global__ void k_index_select(int, int, const int32_t*, const int32_t*, const u
                                int, int, int32_t*, int32_t*, uint32_t*, int32_t*, int32_t*,
                                uint32_t*, uint32_t*);
 __global__ void k_zero_u32(uint32_t*, int64_t);
-__global__ void k_fs_threshold(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
-                               const uint8_t*, const uint8_t*, int64_t, int, uint32_t*);
+__global__ void k_fs_threshold(int, int, const int32_t*, const int32_t*, const uint16_t*,
+                               const float*, uint8_t*, float*, const uint8_t*, const uint8_t*,
+                               int64_t, int, uint32_t*);
 __global__ void k_fs_scan(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
-                          const uint8_t*, const uint8_t*, int64_t, int, int, const uint32_t*,
+                          const uint8_t*, const uint8_t*, int64_t, int, int, int, const uint32_t*,
                           uint32_t*, int32_t*, int32_t*);
-__global__ void k_fs_select(int, const int32_t*, const int32_t*, const uint8_t*, const float*,
-                            const uint8_t*, const uint8_t*, int64_t, int, int, const uint32_t*,
-                            const uint32_t*, const int32_t*, const int32_t*, int32_t*, int32_t*);
+template <int NT>
+__global__ void k_fs_scan_nt(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                             const float*, const uint8_t*, const uint8_t*, int64_t, int, int, int,
+                             const uint32_t*, uint32_t*, int32_t*, int32_t*);
+__global__ void k_fs_select(int, int, const int32_t*, const int32_t*, const uint8_t*, const float*,
+                            const uint8_t*, const uint8_t*, int64_t, int, int, int,
+                            const uint32_t*, const uint32_t*, const int32_t*, const int32_t*,
+                            int32_t*, int32_t*);
 __global__ void k_z_fp8_rows(int64_t, const uint8_t*, const uint8_t*, uint8_t*, float*);
 template <int HG, bool ZF8>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
@@ -158,9 +164,11 @@ void* scratch_ptr() {
 }
 
 // split of a token's attention rows (20 chunks of 32 at full size) across
-// blocks when there are too few tokens to fill the chip
+// blocks when there are too few tokens to fill the chip; from 128 tokens on one
+// block per token (B=128 decode: 33 us, against 28 us + a 9 us merge of the
+// partials with two splits)
 int attn_split(int64_t tokens) {
-    if (tokens >= 256) return 1;
+    if (tokens >= 128) return 1;
     const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
     return ns > 8 ? 8 : ns;
 }
@@ -263,19 +271,23 @@ SelWs select_ws(int B, int Tq, int64_t stride) {
 
 bool two_pass_rows(int B, int Tq, int64_t stride);
 
-// Single-token rows over long caches (batched decode): a sampled threshold, a
-// scan that keeps only the keys at or above it (FS_WCAP slots per chunk of
-// IDX_CHUNK entries, in entry order) and a cut of those; no score row.
-bool fs_rows(int B, int Tq, int64_t stride) { return Tq == 1 && two_pass_rows(B, Tq, stride); }
+// Decode rows (one to eight tokens a request) over long caches: a sampled
+// threshold, a scan that keeps only the keys at or above it (wcap slots per
+// chunk of IDX_CHUNK entries, in entry order) and a cut of those; no score row.
+// The threshold aims at about 2,048 candidates a row, about 2^22 / stride a
+// chunk: wcap = 2^26 / stride (16 times that) between 64 and 512 slots.
+bool fs_rows(int B, int Tq, int64_t stride) { return Tq <= 8 && two_pass_rows(B, Tq, stride); }
 struct FsWs {
-    int n_ch;
+    int n_ch, wcap;
     size_t q8, wq, th, ccnt, ck, cj, total;
 };
-FsWs fs_ws(int B, int64_t stride) {
+FsWs fs_ws(int B, int Tq, int64_t stride) {
     FsWs w;
-    const size_t rows = (size_t)B;
+    const size_t rows = (size_t)B * Tq;
     w.n_ch = (int)cdiv(stride, IDX_CHUNK);
-    const size_t slots = rows * (size_t)w.n_ch * FS_WCAP;
+    const int64_t wc = ((int64_t)1 << 26) / stride;
+    w.wcap = (int)(wc < 64 ? 64 : (wc > 512 ? 512 : wc));
+    const size_t slots = rows * (size_t)w.n_ch * w.wcap;
     w.q8 = 0;
     w.wq = align256(rows * HI * DI);
     w.th = w.wq + align256(rows * HI * sizeof(float));
@@ -287,7 +299,7 @@ FsWs fs_ws(int B, int64_t stride) {
 }
 
 size_t index_topk_ws(int B, int Tq, int64_t stride) {
-    if (fs_rows(B, Tq, stride)) return fs_ws(B, stride).total;
+    if (fs_rows(B, Tq, stride)) return fs_ws(B, Tq, stride).total;
     return two_pass_rows(B, Tq, stride) ? index_ws(B, Tq, stride).total
                                         : select_ws(B, Tq, stride).total;
 }
@@ -392,7 +404,7 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
                          int32_t* cnt, void* ws, hipStream_t st) {
     if (Tq == 0) return CSA2_OK;
     if (fs_rows(B, Tq, stride)) {
-        const FsWs L = fs_ws(B, stride);
+        const FsWs L = fs_ws(B, Tq, stride);
         uint8_t* base = (uint8_t*)ws;
         uint8_t* q8 = base + L.q8;
         float* wq = (float*)(base + L.wq);
@@ -400,17 +412,34 @@ csa2_status launch_index(int B, int Tq, const int32_t* q_pos0, const int32_t* n_
         int32_t* ccnt = (int32_t*)(base + L.ccnt);
         uint32_t* ck = (uint32_t*)(base + L.ck);
         int32_t* cj = (int32_t*)(base + L.cj);
-        const int64_t qrows = (int64_t)B * HI;
-        hipLaunchKernelGGL(k_quant_index_query, dim3((unsigned)cdiv(qrows, 16)), dim3(256), 0, st,
-                           qI, wI, qrows, q8, wq);
-        hipLaunchKernelGGL(k_fs_threshold, dim3((unsigned)B), dim3(256), 0, st, B, q_pos0,
-                           n_entries, q8, wq, ki_codes, ki_scales, stride, rsh, th);
-        hipLaunchKernelGGL(k_fs_scan, dim3((unsigned)cdiv((int64_t)B * L.n_ch, 4)), dim3(256), 0,
-                           st, B, q_pos0, n_entries, q8, wq, ki_codes, ki_scales, stride, L.n_ch,
-                           rsh, (const uint32_t*)th, ck, cj, ccnt);
-        hipLaunchKernelGGL(k_fs_select, dim3((unsigned)B), dim3(512), 0, st, B, q_pos0, n_entries,
-                           q8, wq, ki_codes, ki_scales, stride, L.n_ch, rsh, (const uint32_t*)th,
-                           (const uint32_t*)ck, (const int32_t*)cj, (const int32_t*)ccnt, idx, cnt);
+        const int rows = B * Tq;
+        hipLaunchKernelGGL(k_fs_threshold, dim3((unsigned)rows), dim3(512), 0, st, B, Tq, q_pos0,
+                           n_entries, qI, wI, q8, wq, ki_codes, ki_scales, stride, rsh, th);
+        const dim3 sgrid((unsigned)cdiv((int64_t)B * L.n_ch, 4));
+        if (Tq == 1)
+            hipLaunchKernelGGL(k_fs_scan, sgrid, dim3(256), 0, st, B, q_pos0, n_entries, q8, wq,
+                               ki_codes, ki_scales, stride, L.n_ch, rsh, L.wcap,
+                               (const uint32_t*)th, ck, cj, ccnt);
+        else {
+#define CSA2_FSN(NT)                                                                           \
+    hipLaunchKernelGGL((k_fs_scan_nt<NT>), sgrid, dim3(256), 0, st, B, Tq, q_pos0, n_entries, q8, \
+                       wq, ki_codes, ki_scales, stride, L.n_ch, rsh, L.wcap, (const uint32_t*)th, \
+                       ck, cj, ccnt)
+            switch (Tq) {
+                case 2: CSA2_FSN(2); break;
+                case 3: CSA2_FSN(3); break;
+                case 4: CSA2_FSN(4); break;
+                case 5: CSA2_FSN(5); break;
+                case 6: CSA2_FSN(6); break;
+                case 7: CSA2_FSN(7); break;
+                default: CSA2_FSN(8); break;
+            }
+#undef CSA2_FSN
+        }
+        hipLaunchKernelGGL(k_fs_select, dim3((unsigned)rows), dim3(512), 0, st, B, Tq, q_pos0,
+                           n_entries, q8, wq, ki_codes, ki_scales, stride, L.n_ch, rsh, L.wcap,
+                           (const uint32_t*)th, (const uint32_t*)ck, (const int32_t*)cj,
+                           (const int32_t*)ccnt, idx, cnt);
         return check_launch("csa2_index_topk");
     }
     if (two_pass_rows(B, Tq, stride))

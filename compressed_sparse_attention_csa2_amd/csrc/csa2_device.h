@@ -23,7 +23,6 @@ constexpr int KI_ROPE_LO = 64;  // rotated channels of an index key: 64..127
 constexpr int TOPK = 512;
 constexpr int POOL_BLOCKS = 2048;  // blocks of 8 entries kept by the hierarchical pool
 constexpr int IDX_CHUNK = 2048;  // index entries scanned by one wave of the score kernel
-constexpr int FS_WCAP = 512;     // selection candidates a chunk of IDX_CHUNK entries keeps (decode)
 constexpr int ATT_THREADS = 768; // attention block: 4 QK waves + 8 PV waves
 
 typedef __attribute__((ext_vector_type(2))) float f2;

@@ -1,5 +1,5 @@
-// Top-512 of single-token query rows over long caches (batched decode) without
-// writing the rows' scores.
+// Top-512 of the query rows of decode steps (one to eight tokens a request)
+// over long caches, without writing the rows' scores.
 //
 // "DeepSeek V4.1 -- Pooled group -> Source layer, pairs pooled", indexer and
 // top-k equations: S^I_{t,j} = sum_h w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j) and
@@ -10,14 +10,15 @@
 // A decode step reads each request's index keys once, so its time is the key
 // stream; writing every fp32 score and reading it back for the selection cost
 // as much as a third of that stream again.  Three passes instead:
-//   k_fs_threshold  one block per row scores 1,024 entries spread evenly over
-//                   the row and takes a key th that ceil(2^21 / n) of the
-//                   sample reach (about 2,048 of the row's n scores by the
-//                   sample);
+//   k_fs_threshold  one block per row quantises the row's index query, scores
+//                   S = 1,024 .. 4,096 entries spread evenly over the row and
+//                   takes a key th that max(24, ceil(2,048 S / n)) of the sample
+//                   reach (about 2,048 of the row's n scores by the sample);
 //   k_fs_scan       one wave per (row, chunk of IDX_CHUNK entries) scores the
 //                   chunk and keeps the keys >= th with their entries, in entry
 //                   order, in the chunk's own slots (no atomics, so the order
-//                   survives);
+//                   survives); k_fs_scan_nt does it for two to eight tokens of a
+//                   request in one stream of the chunk's keys;
 //   k_fs_select     one block per row gathers the chunks' candidates in order
 //                   and cuts the exact top 512 (ties: smaller entry) by halving
 //                   the key range.
@@ -35,7 +36,7 @@ namespace csa2 {
 
 constexpr int FS_MIN = 16384;                      // shorter rows: the fallback
 constexpr int FS_WAVES = 8;                        // waves of a select block
-constexpr int FS_NSLOT = FS_WAVES * 768;           // candidates a select block cuts
+constexpr int FS_NSLOT = FS_WAVES * 1536;          // candidates a select block cuts
 constexpr uint32_t FS_ALL = 0xFFFFFFFFu;           // threshold word: at most 512 entries, take all
 constexpr uint32_t FS_SLOW = 0u;                   // threshold word: select by the fallback
 
@@ -76,75 +77,165 @@ struct RowQuery {
     }
 };
 
-// entries of a single-token row (request b at its position q_pos0[b])
+// entries of query row (request b, token t at position q_pos0[b] + t)
 __device__ __forceinline__ int fs_row_len(const int32_t* q_pos0, const int32_t* n_entries, int b,
-                                          int64_t entry_stride, int rsh) {
-    int64_t n = cand_count(q_pos0[b], 0, n_entries[b], entry_stride, rsh);
+                                          int t, int64_t entry_stride, int rsh) {
+    int64_t n = cand_count(q_pos0[b], t, n_entries[b], entry_stride, rsh);
     return (int)(n < 0 ? 0 : (n > entry_stride ? entry_stride : n));
 }
 
-// ---- threshold: one block of four waves per row ----------------------------
-__global__ void __launch_bounds__(256) k_fs_threshold(
-    int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
-    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
-    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
-    int64_t entry_stride, int rsh, uint32_t* __restrict__ th_out) {
-    __shared__ uint32_t skey[1024];
-    const int b = blockIdx.x;
-    if (b >= B) return;
+// ---- threshold: one block of eight waves per row ---------------------------
+// Also quantises the row's index query (the 32 head rows as k_quant_index_query
+// does) into q8 / wq for the scan and the cut; the sample's key loads are
+// issued first, so they are in flight while the query is quantised.
+__global__ void __launch_bounds__(64 * FS_WAVES) k_fs_threshold(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint16_t* __restrict__ qI, const float* __restrict__ wI, uint8_t* __restrict__ q8,
+    float* __restrict__ wq, const uint8_t* __restrict__ ki_codes,
+    const uint8_t* __restrict__ ki_scales, int64_t entry_stride, int rsh,
+    uint32_t* __restrict__ th_out) {
+    __shared__ uint32_t skey[4096];
+    __shared__ uint32_t cbuf[2][FS_WAVES];
+    __shared__ __attribute__((aligned(16))) uint8_t sq8[HI * DI];
+    __shared__ __attribute__((aligned(16))) float swq[HI];
+    const int row = blockIdx.x;                     // query row: request b, token t
+    if (row >= B * Tq) return;
+    const int b = row / Tq, t = row - b * Tq;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
-    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
-    if (n <= TOPK || n < FS_MIN) {
-        if (tid == 0) th_out[b] = n <= TOPK ? FS_ALL : FS_SLOW;
+    const int n = fs_row_len(q_pos0, n_entries, b, t, entry_stride, rsh);
+    if (n <= TOPK) {                    // every entry is taken: no scan, no query needed
+        if (tid == 0) th_out[row] = FS_ALL;
+        return;
+    }
+    const bool sample = n >= FS_MIN;
+    // S = 1024 m samples (m = 1, 2 or 4 as the row passes 65,536 and 131,072
+    // entries): sample i is entry floor(i n / S); wave w scores samples
+    // 128 m w .. 128 m (w + 1) - 1 in m rounds of eight tiles of sixteen, the
+    // next round's loads in flight during the current one's products
+    const int lm = n <= 65536 ? 0 : (n <= 131072 ? 1 : 2), m = 1 << lm;
+    const int S = 1024 << lm;
+    const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
+    const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
+    uint4 kc[2][8];
+    int sc[2][8];
+    auto issue = [&](int rnd, int buf) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = 128 * (m * wave + rnd) + 16 * u + col;
+            const int64_t e = ((int64_t)i * n) >> (10 + lm);
+            kc[buf][u] = *(const uint4*)(kb + e * 64);
+            sc[buf][u] = (int)sb[e * 4];
+        }
+    };
+    if (sample) issue(0, 0);
+    // the query: head row tid >> 4, sixteen lanes each, into LDS, then to q8 / wq
+    {
+        const int r = tid >> 4, l16 = tid & 15;
+        const int64_t gr = (int64_t)row * HI + r;
+        quant_index_row(qI + gr * DI, wI[gr], &sq8[r * DI], &swq[r], l16);
+        __syncthreads();
+        *(uint2*)(q8 + gr * DI + 8 * l16) = *(const uint2*)&sq8[r * DI + 8 * l16];
+        if (l16 == 0) wq[gr] = swq[r];
+    }
+    if (!sample) {                      // 513 .. FS_MIN - 1 entries: the cut's fallback
+        if (tid == 0) th_out[row] = FS_SLOW;
         return;
     }
     RowQuery q;
-    q.load(q8, wq, b, col, grp);
-    const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
-    const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
-    // wave w scores samples 256w .. 256w + 255 (sample i is entry floor(i n / 1024)),
-    // sixteen tiles of sixteen; four tiles' sums leave through one row-sum scatter
+    q.load(sq8, swq, 0, col, grp);
 #pragma unroll
-    for (int u0 = 0; u0 < 16; u0 += 4) {
-        uint4 kc[4];
-        int sc[4];
+    for (int rnd = 0; rnd < 4; ++rnd) {        // unrolled: the buffers stay in registers
+        if (rnd >= m) break;
+            if (rnd + 1 < m) issue(rnd + 1, (rnd + 1) & 1);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int i = 256 * wave + 16 * (u0 + g) + col;
-            const int64_t e = ((int64_t)i * n) >> 10;
-            kc[g] = *(const uint4*)(kb + e * 64);
-            sc[g] = (int)sb[e * 4];
+        for (int u0 = 0; u0 < 8; u0 += 4) {
+            float p[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) p[g] = q.partial(kc[rnd & 1][u0 + g], sc[rnd & 1][u0 + g]);
+            // lane 16g + col now holds sample 128(m w + rnd) + 16(u0 + g) + col
+            skey[128 * (m * wave + rnd) + 16 * u0 + lane] =
+                score_key(rowsum_scatter4(p[0], p[1], p[2], p[3]));
         }
-        float p[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) p[g] = q.partial(kc[g], sc[g]);
-        // lane 16g + col now holds sample 256w + 16(u0 + g) + col
-        skey[256 * wave + 16 * u0 + lane] = score_key(rowsum_scatter4(p[0], p[1], p[2], p[3]));
     }
     __syncthreads();
-    if (wave == 0) {
-        uint32_t kr[16];
+    const uint32_t ks = (uint32_t)max((int64_t)24, ((int64_t)S * 2048 + n - 1) / n);
+    if (S == 1024) {
+        // one wave holds the 1,024 keys: its own search, no block barrier per step
+        if (wave == 0) {
+            uint32_t kr[16];
 #pragma unroll
-        for (int g = 0; g < 16; ++g) kr[g] = skey[64 * g + lane];
-        const uint32_t ks = (uint32_t)((2048ll * 1024 + n - 1) / n);     // <= 128
-        uint32_t th = wave_threshold_bisect(kr, ks, ks + ks / 4);
-        if (th == 0u) {                 // repeated keys: the sample's ks-th largest
-            uint32_t krem;
-            th = wave_kth_bisect(kr, ks, &krem);
+            for (int g = 0; g < 16; ++g) kr[g] = skey[64 * g + lane];
+            uint32_t th = wave_threshold_bisect(kr, ks, ks + ks / 4);
+            if (th == 0u) {             // repeated keys: the sample's ks-th largest
+                uint32_t krem;
+                th = wave_kth_bisect(kr, ks, &krem);
+            }
+            if (lane == 0) th_out[row] = th;   // a key of a finite score: never 0 or FS_ALL
         }
-        if (lane == 0) th_out[b] = th;   // a key of a finite score: never 0 or FS_ALL
+        return;
     }
+    // A key th that ks .. ks + ks/4 of the S sample keys reach (about 2,048 of the
+    // row's scores by the sample, at least 24 sample keys above th), found by
+    // halving the key range with block-wide counts; with repeated keys and no
+    // such key, the largest key that ks of them reach.
+    uint32_t kv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int i = 8 * tid + e;
+        kv[e] = i < S ? skey[i] : 0u;
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (kv[e] != 0u) lo = min(lo, kv[e]);
+        hi = max(hi, kv[e]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) { cbuf[0][wave] = lo; cbuf[1][wave] = hi; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < FS_WAVES; ++w) { lo = min(lo, cbuf[0][w]); hi = max(hi, cbuf[1][w]); }
+    __syncthreads();
+    const uint32_t lim = ks + ks / 4;
+    int par = 0;
+    auto block_count = [&](uint32_t th2) -> uint32_t {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c += kv[e] >= th2 ? 1u : 0u;
+        c = wave_sum(c);
+        if (lane == 0) cbuf[par][wave] = c;
+        __syncthreads();
+        uint32_t t2 = 0u;
+#pragma unroll
+        for (int w = 0; w < FS_WAVES; ++w) t2 += cbuf[par][w];
+        par ^= 1;
+        return t2;
+    };
+    uint32_t a = lo;                    // count(>= a) >= ks
+    uint64_t bnd = (uint64_t)hi + 1u;   // count(>= bnd) < ks
+    while (bnd - a > 1u) {
+        const uint32_t mid = (uint32_t)(a + ((bnd - a) >> 1));
+        const uint32_t c = block_count(mid);
+        if (c < ks) {
+            bnd = mid;
+        } else {
+            a = mid;
+            if (c <= lim) break;
+        }
+    }
+    if (tid == 0) th_out[row] = a;      // >= the smallest finite key: never 0 or FS_ALL
 }
 
-// ---- filter: one wave per (row, chunk) --------------------------------------
-// ck/cj [B][n_ch][FS_WCAP]: the chunk's keys >= th and their entries, in entry
-// order; ccnt [B][n_ch]: how many passed (more than FS_WCAP: the slots overflowed).
+// ---- filter, single-token rows: one wave per (row, chunk) --------------------
+// ck/cj [rows][n_ch][wcap]: the chunk's keys >= th and their entries, in entry
+// order; ccnt [rows][n_ch]: how many passed (more than wcap: the slots overflowed).
 __global__ void __launch_bounds__(256) k_fs_scan(
     int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
     const uint8_t* __restrict__ q8, const float* __restrict__ wq,
     const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
-    int64_t entry_stride, int n_ch, int rsh, const uint32_t* __restrict__ th_in,
+    int64_t entry_stride, int n_ch, int rsh, int wcap, const uint32_t* __restrict__ th_in,
     uint32_t* __restrict__ ck, int32_t* __restrict__ cj, int32_t* __restrict__ ccnt) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
@@ -152,9 +243,9 @@ __global__ void __launch_bounds__(256) k_fs_scan(
     const int b = (int)(item / n_ch), ch = (int)(item - (int64_t)b * n_ch);
     const uint32_t th = th_in[b];
     if (th == FS_ALL || th == FS_SLOW) return;            // the select pass handles the row
-    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
+    const int n = fs_row_len(q_pos0, n_entries, b, 0, entry_stride, rsh);
     const int j_begin = ch * IDX_CHUNK;
-    const int64_t slot0 = item * FS_WCAP;
+    const int64_t slot0 = item * wcap;
     if (j_begin >= n) {
         if (lane == 0) ccnt[item] = 0;
         return;
@@ -200,7 +291,7 @@ __global__ void __launch_bounds__(256) k_fs_scan(
                 const bool adm = key != 0u && key >= th;
                 const uint64_t m = __ballot(adm);
                 const int pos = nc + (int)__popcll(m & below);
-                if (adm && pos < FS_WCAP) {
+                if (adm && pos < wcap) {
                     ck[slot0 + pos] = key;
                     cj[slot0 + pos] = j_begin + jl;
                 }
@@ -211,6 +302,166 @@ __global__ void __launch_bounds__(256) k_fs_scan(
     }
     if (lane == 0) ccnt[item] = nc;
 }
+
+// ---- filter, NT = 2..8 tokens of a request: one wave per (request, chunk) ----
+// The wave streams the chunk's keys once for all its tokens (as the score pass
+// does for few query rows): per tile, up to four tokens' products and head sums
+// at a time, lane row g then holding token 4r + g's scores of the tile's 16
+// entries; each token keeps its own keys >= its threshold in its own slots.
+// Exactly NT token slots (no padding to eight: the products and head sums of
+// absent tokens would cost as much as real ones).
+template <int NT>
+__global__ void __launch_bounds__(256) k_fs_scan_nt(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int n_ch, int rsh, int wcap, const uint32_t* __restrict__ th_in,
+    uint32_t* __restrict__ ck, int32_t* __restrict__ cj, int32_t* __restrict__ ccnt) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)B * n_ch) return;
+    const int b = (int)(item / n_ch), ch = (int)(item - (int64_t)b * n_ch);
+    const int col = lane & 15, grp = lane >> 4;
+    const int j_begin = ch * IDX_CHUNK;
+    // this lane row's tokens 4r + grp: threshold, candidates in the chunk, slots
+    uint32_t thr[2];
+    int ncand[2];
+    bool act[2];
+    int64_t slot0[2], crow[2];
+    int n_max = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = 4 * r + grp;
+        const bool valid = t < Tq;
+        const int64_t row = (int64_t)b * Tq + (valid ? t : 0);
+        const uint32_t th = valid ? th_in[row] : FS_SLOW;
+        act[r] = valid && th != FS_ALL && th != FS_SLOW;
+        thr[r] = th;
+        const int n = act[r] ? fs_row_len(q_pos0, n_entries, b, t, entry_stride, rsh) : 0;
+        ncand[r] = min(max(n - j_begin, 0), IDX_CHUNK);
+        n_max = max(n_max, n);
+        crow[r] = row * n_ch + ch;
+        slot0[r] = crow[r] * wcap;
+    }
+    if (__ballot(act[0] || act[1]) == 0ull) return;      // every token is the cut's alone
+    n_max = (int)wave_max((uint32_t)n_max);
+    const int j_len = min(IDX_CHUNK, n_max - j_begin);
+    if (j_len <= 0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            if (act[r] && col == 0) ccnt[crow[r]] = 0;
+        return;
+    }
+    // query operands of the NT tokens
+    i8 A[NT][2];
+    f4 W[NT][2];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const bool ok = k < Tq;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const int64_t hr = ((int64_t)b * Tq + (ok ? k : 0)) * HI + tile * 16;
+            const uint8_t* src = q8 + (hr + col) * DI + 16 * grp;
+            const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 64);
+            A[k][tile] = ok ? i8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w}
+                            : i8{0, 0, 0, 0, 0, 0, 0, 0};
+            const float4 w4 = *(const float4*)(wq + hr + 4 * grp);
+            W[k][tile] = ok ? f4{w4.x, w4.y, w4.z, w4.w} : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* kbase = ki_codes + ((int64_t)b * entry_stride + j_begin) * 64 + 16 * grp;
+    const uint8_t* sbase = ki_scales + ((int64_t)b * entry_stride + j_begin) * 4 + grp;
+    auto load = [&](int jt, uint4& kc, uint32_t& sw) {
+        int j = jt + col;
+        j = j < j_len ? j : j_len - 1;
+        const u4v k4 = __builtin_nontemporal_load((const u4v*)(kbase + (int64_t)j * 64));
+        kc = uint4{k4[0], k4[1], k4[2], k4[3]};
+        sw = __builtin_nontemporal_load(sbase + (int64_t)j * 4);
+    };
+    const uint32_t below = (1u << col) - 1u;
+    int nc[2] = {0, 0};
+    auto tile = [&](int jt, const uint4 kc, const int sc) {
+        const i8 Bv = i8{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < (NT + 3) / 4; ++r) {
+            constexpr int NG0 = NT < 4 ? NT : 4;
+            const int ng = r == 0 ? NG0 : NT - 4;          // tokens of this group
+            f4 d[4][2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
+                    if (k < ng)
+                        d[k][t2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            A[4 * r + k][t2], Bv, f4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sc);
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (k >= ng) continue;
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[4 * r + k][0][i], relu(d[k][0][i]), acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(W[4 * r + k][1][i], relu(d[k][1][i]), acc);
+                s4[k] = acc;
+            }
+            const float tot = rowsum_scatter4(s4[0], s4[1], s4[2], s4[3]);
+            const int jl = jt + col;
+            const uint32_t key = act[r] && jl < ncand[r] ? score_key(tot) : 0u;
+            const bool adm = key != 0u && key >= thr[r];
+            const uint32_t mr = (uint32_t)(__ballot(adm) >> (16 * grp)) & 0xFFFFu;
+            const int pos = nc[r] + (int)__popc(mr & below);
+            if (adm && pos < wcap) {
+                ck[slot0[r] + pos] = key;
+                cj[slot0[r] + pos] = j_begin + jl;
+            }
+            nc[r] += (int)__popc(mr);
+        }
+    };
+    uint4 kb[4];
+    uint32_t sb[4];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        load(16 * p, kb[p], sb[p]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int jt = 0; jt < j_len; jt += 64) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            load(jt + 16 * (p + 3), kb[(p + 3) & 3], sb[(p + 3) & 3]);
+            tile(jt + 16 * p, kb[p], (int)sb[p]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        if (act[r] && col == 0) ccnt[crow[r]] = nc[r];
+}
+
+template __global__ void k_fs_scan_nt<2>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<3>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<4>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<5>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<6>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<7>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+template __global__ void k_fs_scan_nt<8>(int, int, const int32_t*, const int32_t*, const uint8_t*,
+                                        const float*, const uint8_t*, const uint8_t*, int64_t, int,
+                                        int, int, const uint32_t*, uint32_t*, int32_t*, int32_t*);
+
 
 // Exclusive prefix sum over the block (FS_WAVES waves); *tot = the block total.
 __device__ __forceinline__ uint32_t fs_block_scan(uint32_t v, uint32_t* wsum, uint32_t* tot) {
@@ -230,114 +481,16 @@ __device__ __forceinline__ uint32_t fs_block_scan(uint32_t v, uint32_t* wsum, ui
     return before + inc - v;
 }
 
-// ---- cut: one block of FS_WAVES waves per row --------------------------------
-__global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
-    int B, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
-    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
-    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
-    int64_t entry_stride, int n_ch, int rsh, const uint32_t* __restrict__ th_in,
-    const uint32_t* __restrict__ ck, const int32_t* __restrict__ cj,
-    const int32_t* __restrict__ ccnt, int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
-    __shared__ uint32_t sk[FS_NSLOT];
-    __shared__ int32_t sj[FS_NSLOT];
-    __shared__ WaveSel wsel;
-    __shared__ uint32_t wsum[FS_WAVES];
-    __shared__ uint32_t wcount[2][FS_WAVES];
-    __shared__ uint32_t bc[2 * FS_WAVES + 2];
-    __shared__ uint32_t spre[2 * 64 * FS_WAVES];     // a gather pass's chunk offsets and counts
+// The cut of a block's candidates sk/sj[0, total) (entry order): the 512th
+// largest key K by halving the key range (block-wide counts), stopping early
+// when exactly 512 keys reach the middle; then the keys > K and the first
+// (512 - #(> K)) copies of K, written to out in ascending entry order.  SPT:
+// consecutive slots per thread (total <= 512 SPT).
+template <int SPT>
+__device__ __forceinline__ void fs_cut(const uint32_t* sk, const int32_t* sj, int total,
+                                       uint32_t* bc, uint32_t (*wcount)[FS_WAVES], uint32_t* wsum,
+                                       int32_t* out, int32_t* cnt_out) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int b = blockIdx.x;
-    if (b >= B) return;
-    const int n = fs_row_len(q_pos0, n_entries, b, entry_stride, rsh);
-    int32_t* out = idx + (int64_t)b * TOPK;
-    const uint32_t th = th_in[b];
-    if (th == FS_ALL) {
-        for (int i = tid; i < TOPK; i += 64 * FS_WAVES) out[i] = i < n ? i : -1;
-        if (tid == 0) cnt[b] = n;
-        return;
-    }
-    // the chunks' counts: total, and whether any chunk overflowed its slots
-    uint32_t total = 0u;
-    bool bad = th == FS_SLOW;
-    if (!bad) {
-        uint32_t t = 0u, over = 0u;
-        for (int c = tid; c < n_ch; c += 64 * FS_WAVES) {
-            const int k = ccnt[(int64_t)b * n_ch + c];
-            over |= (uint32_t)(k < 0 || k > FS_WCAP);
-            t += (uint32_t)(k < 0 ? 0 : (k > FS_WCAP ? FS_WCAP : k));
-        }
-        t = wave_sum(t);
-        over = wave_max(over);
-        if (lane == 0) { bc[wave] = t; bc[FS_WAVES + wave] = over; }
-        __syncthreads();
-        uint32_t ov = 0u;
-#pragma unroll
-        for (int w = 0; w < FS_WAVES; ++w) { total += bc[w]; ov |= bc[FS_WAVES + w]; }
-        __syncthreads();
-        bad = ov != 0u || total < (uint32_t)TOPK || total > (uint32_t)FS_NSLOT;
-    }
-    if (bad) {
-        // the exact selection of the whole row: wave 0 scores it again, 64
-        // entries a step (one per lane, in entry order), into the streaming selection
-        if (wave != 0) return;
-        const int col = lane & 15, grp = lane >> 4;
-        RowQuery q;
-        q.load(q8, wq, b, col, grp);
-        const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
-        const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
-        WaveTopk st{wsel, 0, 0u};
-        for (int jt = 0; jt < n; jt += 64) {
-            float p[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                int e = jt + 16 * g + col;
-                e = e < n ? e : n - 1;
-                const uint4 kc = *(const uint4*)(kb + (int64_t)e * 64);
-                p[g] = q.partial(kc, (int)sb[(int64_t)e * 4]);
-            }
-            const float tot = rowsum_scatter4(p[0], p[1], p[2], p[3]);
-            const uint32_t k[4] = {jt + lane < n ? score_key(tot) : 0u, 0u, 0u, 0u};
-            const int32_t jj[4] = {jt + lane, 0, 0, 0};
-            st.push(k, jj);
-        }
-        const int c = st.finish(out, nullptr, nullptr);
-        if (lane == 0) cnt[b] = c;
-        return;
-    }
-    // gather the candidates in entry order: chunk c's to slots pre[c] .., the
-    // chunks' offsets by a block scan, 512 chunks a pass; wave w copies chunks
-    // w, w + 8, .. of the pass, a lane per candidate
-    {
-        uint32_t run = 0u;                 // slots before this pass's chunks
-        for (int c0 = 0; c0 < n_ch; c0 += 64 * FS_WAVES) {
-            const int c = c0 + tid;
-            uint32_t k = 0u;
-            if (c < n_ch) {
-                const int kk = ccnt[(int64_t)b * n_ch + c];
-                k = (uint32_t)(kk < 0 ? 0 : kk);
-            }
-            uint32_t tot;
-            const uint32_t pre = run + fs_block_scan(k, wsum, &tot);
-            spre[tid] = pre;
-            spre[64 * FS_WAVES + tid] = k;
-            __syncthreads();
-            const int nc = min(n_ch - c0, 64 * FS_WAVES);
-            for (int cc = wave; cc < nc; cc += FS_WAVES) {
-                const uint32_t p0 = spre[cc], kc = spre[64 * FS_WAVES + cc];
-                const int64_t s0 = ((int64_t)b * n_ch + c0 + cc) * FS_WCAP;
-                for (uint32_t i = lane; i < kc; i += 64) {
-                    sk[p0 + i] = ck[s0 + i];
-                    sj[p0 + i] = cj[s0 + i];
-                }
-            }
-            __syncthreads();
-            run += tot;
-        }
-    }
-    // the 512th largest key K by halving the key range (block-wide counts),
-    // stopping early when exactly 512 keys reach the middle; then keys > K and
-    // the first (512 - #(> K)) copies of K, written in ascending entry order
-    constexpr int SPT = FS_NSLOT / (64 * FS_WAVES);      // consecutive slots per thread
     uint32_t kv[SPT];
 #pragma unroll
     for (int e = 0; e < SPT; ++e) {
@@ -422,7 +575,116 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
             taken += kv[e] == K;
         }
     }
-    if (tid == 0) cnt[b] = TOPK;
+    if (tid == 0) *cnt_out = TOPK;
+}
+
+// ---- cut: one block of FS_WAVES waves per row --------------------------------
+__global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
+    int B, int Tq, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ n_entries,
+    const uint8_t* __restrict__ q8, const float* __restrict__ wq,
+    const uint8_t* __restrict__ ki_codes, const uint8_t* __restrict__ ki_scales,
+    int64_t entry_stride, int n_ch, int rsh, int wcap, const uint32_t* __restrict__ th_in,
+    const uint32_t* __restrict__ ck, const int32_t* __restrict__ cj,
+    const int32_t* __restrict__ ccnt, int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+    __shared__ uint32_t sk[FS_NSLOT];
+    __shared__ int32_t sj[FS_NSLOT];
+    __shared__ WaveSel wsel;
+    __shared__ uint32_t wsum[FS_WAVES];
+    __shared__ uint32_t wcount[2][FS_WAVES];
+    __shared__ uint32_t bc[2 * FS_WAVES + 2];
+    __shared__ uint32_t spre[2 * 64 * FS_WAVES];     // a gather pass's chunk offsets and counts
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = blockIdx.x;                     // query row: request b, token t
+    if (row >= B * Tq) return;
+    const int b = row / Tq, t = row - b * Tq;
+    const int n = fs_row_len(q_pos0, n_entries, b, t, entry_stride, rsh);
+    int32_t* out = idx + (int64_t)row * TOPK;
+    const uint32_t th = th_in[row];
+    if (th == FS_ALL) {
+        for (int i = tid; i < TOPK; i += 64 * FS_WAVES) out[i] = i < n ? i : -1;
+        if (tid == 0) cnt[row] = n;
+        return;
+    }
+    // the chunks' counts: total, and whether any chunk overflowed its slots
+    uint32_t total = 0u;
+    bool bad = th == FS_SLOW;
+    if (!bad) {
+        uint32_t tc = 0u, over = 0u;
+        for (int c = tid; c < n_ch; c += 64 * FS_WAVES) {
+            const int k = ccnt[(int64_t)row * n_ch + c];
+            over |= (uint32_t)(k < 0 || k > wcap);
+            tc += (uint32_t)(k < 0 ? 0 : (k > wcap ? wcap : k));
+        }
+        tc = wave_sum(tc);
+        over = wave_max(over);
+        if (lane == 0) { bc[wave] = tc; bc[FS_WAVES + wave] = over; }
+        __syncthreads();
+        uint32_t ov = 0u;
+#pragma unroll
+        for (int w = 0; w < FS_WAVES; ++w) { total += bc[w]; ov |= bc[FS_WAVES + w]; }
+        __syncthreads();
+        bad = ov != 0u || total < (uint32_t)TOPK || total > (uint32_t)FS_NSLOT;
+    }
+    if (bad) {
+        // the exact selection of the whole row: wave 0 scores it again, 64
+        // entries a step (one per lane, in entry order), into the streaming selection
+        if (wave != 0) return;
+        const int col = lane & 15, grp = lane >> 4;
+        RowQuery q;
+        q.load(q8, wq, row, col, grp);
+        const uint8_t* kb = ki_codes + (int64_t)b * entry_stride * 64 + 16 * grp;
+        const uint8_t* sb = ki_scales + (int64_t)b * entry_stride * 4 + grp;
+        WaveTopk st{wsel, 0, 0u};
+        for (int jt = 0; jt < n; jt += 64) {
+            float p[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                int e = jt + 16 * g + col;
+                e = e < n ? e : n - 1;
+                const uint4 kc = *(const uint4*)(kb + (int64_t)e * 64);
+                p[g] = q.partial(kc, (int)sb[(int64_t)e * 4]);
+            }
+            const float tot = rowsum_scatter4(p[0], p[1], p[2], p[3]);
+            const uint32_t k[4] = {jt + lane < n ? score_key(tot) : 0u, 0u, 0u, 0u};
+            const int32_t jj[4] = {jt + lane, 0, 0, 0};
+            st.push(k, jj);
+        }
+        const int c = st.finish(out, nullptr, nullptr);
+        if (lane == 0) cnt[row] = c;
+        return;
+    }
+    // gather the candidates in entry order: chunk c's to slots pre[c] .., the
+    // chunks' offsets by a block scan, 512 chunks a pass; wave w copies chunks
+    // w, w + 8, .. of the pass, a lane per candidate
+    {
+        uint32_t run = 0u;                 // slots before this pass's chunks
+        for (int c0 = 0; c0 < n_ch; c0 += 64 * FS_WAVES) {
+            const int c = c0 + tid;
+            uint32_t k = 0u;
+            if (c < n_ch) {
+                const int kk = ccnt[(int64_t)row * n_ch + c];
+                k = (uint32_t)(kk < 0 ? 0 : kk);
+            }
+            uint32_t tot;
+            const uint32_t pre = run + fs_block_scan(k, wsum, &tot);
+            spre[tid] = pre;
+            spre[64 * FS_WAVES + tid] = k;
+            __syncthreads();
+            const int nc = min(n_ch - c0, 64 * FS_WAVES);
+            for (int cc = wave; cc < nc; cc += FS_WAVES) {
+                const uint32_t p0 = spre[cc], kc = spre[64 * FS_WAVES + cc];
+                const int64_t s0 = ((int64_t)row * n_ch + c0 + cc) * wcap;
+                for (uint32_t i = lane; i < kc; i += 64) {
+                    sk[p0 + i] = ck[s0 + i];
+                    sj[p0 + i] = cj[s0 + i];
+                }
+            }
+            __syncthreads();
+            run += tot;
+        }
+    }
+    if (total <= 12 * 64 * FS_WAVES) fs_cut<12>(sk, sj, (int)total, bc, wcount, wsum, out, cnt + row);
+    else fs_cut<24>(sk, sj, (int)total, bc, wcount, wsum, out, cnt + row);
 }
 
 }  // namespace csa2

@@ -24,6 +24,35 @@ __device__ __forceinline__ int64_t cand_count(int32_t qpos0, int t, int32_t n_en
 
 // max(x, 0) as one integer max on the bit pattern: every negative float
 // (including -0) is a negative integer.
+// One (token, head) row of the index query: 128 bf16 values -> E4M3FN codes
+// with scale s = max|x| / 448 (1 for an all-zero row), and the head weight
+// folded with it, wq = w * s.  Sixteen lanes (one DPP row) per row, eight
+// channels per lane (lane l16 of the row): a 16-byte load, an 8-byte store,
+// the row maximum in four in-row steps.
+__device__ __forceinline__ void quant_index_row(const uint16_t* qrow, float w, uint8_t* q8row,
+                                                float* wq_out, int l16) {
+    const uint4 v = *(const uint4*)(qrow + 8 * l16);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf2f((uint16_t)w4[i]);
+        x[2 * i + 1] = bf2f((uint16_t)(w4[i] >> 16));
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+    }
+#pragma unroll
+    for (int s = 1; s <= 8; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+    const float sc = amax > 0.0f ? div_rn(amax, 448.0f) : 1.0f;
+    uint32_t c[2] = {0u, 0u};
+    if (amax > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i >> 2] |= e4m3_code(div_rn(x[i], sc)) << (8 * (i & 3));
+    }
+    *(uint2*)(q8row + 8 * l16) = uint2{c[0], c[1]};
+    if (l16 == 0) *wq_out = w * sc;
+}
+
 __device__ __forceinline__ float relu(float x) {
     return __int_as_float(max(__float_as_int(x), 0));
 }

@@ -27,38 +27,16 @@
 namespace csa2 {
 
 // q^I [rows][128] bf16 -> E4M3FN codes [rows][128] and wq[row] = w[row] * scale.
-// Sixteen lanes (one DPP row) per (token, head) row, eight channels per lane:
-// 16-byte loads, 8-byte stores, and the row maximum in four in-row steps.
+// Sixteen lanes (one DPP row) per (token, head) row (quant_index_row).
 __global__ void __launch_bounds__(256) k_quant_index_query(const uint16_t* __restrict__ qI,
                                                            const float* __restrict__ wI,
                                                            int64_t rows,
                                                            uint8_t* __restrict__ q8,
                                                            float* __restrict__ wq) {
     const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-    const int l16 = threadIdx.x & 15;
     if (r >= rows) return;          // whole 16-lane rows leave together
-    const uint4 v = *(const uint4*)(qI + r * DI + 8 * l16);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    float x[8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf2f((uint16_t)w4[i]);
-        x[2 * i + 1] = bf2f((uint16_t)(w4[i] >> 16));
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
-    }
-#pragma unroll
-    for (int s = 1; s <= 8; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
-    const float sc = amax > 0.0f ? div_rn(amax, 448.0f) : 1.0f;
-    uint32_t c[2] = {0u, 0u};
-    if (amax > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i >> 2] |= e4m3_code(div_rn(x[i], sc)) << (8 * (i & 3));
-    }
-    *(uint2*)(q8 + r * DI + 8 * l16) = uint2{c[0], c[1]};
-    if (l16 == 0) wq[r] = wI[r] * sc;
+    quant_index_row(qI + r * DI, wI[r], q8 + r * DI, wq + r, threadIdx.x & 15);
 }
-
 
 // Scores S[(b*Tq + t)][j] for j < n(t).  One wave per (request, TOK tokens,
 // chunk of IDX_CHUNK entries); work items are ordered heaviest tokens first.

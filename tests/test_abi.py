@@ -43,8 +43,9 @@ def test_workspace_sizes(L):
     # single-token rows over long caches (decode): no score rows, only the kept
     # candidates (512 slots of key and entry per 2,048 entries: 2 bytes an entry)
     assert 128 * 65536 * 2 <= ws(csa2.OP_INDEX_TOPK, 128, 1, 64, 65536) < 128 * 65536 * 2 + 2**20
-    # few long multi-token rows (verify) keep their score rows
-    assert ws(csa2.OP_INDEX_TOPK, 16, 6, 64, 524288) >= 96 * 524288 * 4
+    # up to eight tokens a request (verify): no score rows either (128 slots per
+    # 2,048 entries at this length)
+    assert ws(csa2.OP_INDEX_TOPK, 16, 6, 64, 524288) < 96 * 524288 * 4 // 4
     # many single-token rows stay fused: segment winners only
     assert ws(csa2.OP_INDEX_TOPK, 2048, 1, 64, 8192) < 2048 * 8192 * 4 // 4
     assert ws(csa2.OP_INDEX_TOPK, 3, 6, 64, 2600) <= 18 * (4224 + 16) + 4096
@@ -55,7 +56,8 @@ def test_workspace_sizes(L):
     # a prefill: one split (no partials); the compressed rows re-encoded as E4M3
     # rows with an fp32 scale (512 + 4 bytes per entry), each 256-byte aligned
     assert ws(csa2.OP_SPARSE_ATTN, 1, 65536, 64, 32768) == 32768 * 512 + 32768 * 4
-    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) > 0     # decode splits the rows
+    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) == 0    # one block per query from 128 on
+    assert ws(csa2.OP_SPARSE_ATTN, 64, 1, 64, 65536) > 0      # fewer queries: split, partials
     # decode gathers each entry less than four times on average: no re-encoding
     assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) < 128 * 65536 * 516
     assert ws(csa2.OP_SPARSE_ATTN, 16, 6, 64, 524288) < 16 * 524288 * 516
