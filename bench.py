@@ -33,17 +33,17 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (1.405e+10, {
-        "attention.hip": "333b67d04f56b5d0765db48c76bc511fbc64d15312ed723ccb6ae03cf68ab3c2",
-        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_select", "prefill", 65536): (4.827e+08, {
+    ("k_attn", "prefill", 65536): (2.0058e+10, {
+        "attention.hip": "25b23f3dcca9eb0e6553a89eaea860045d5ccaae5ef4d92fe31e2ca514720da9",
+        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
+    ("k_index_select", "prefill", 65536): (4.8099e+08, {
         "index_select.hip": "5fdd172ede2fae924619737dcf18698bfcc5853990b4fb175acce9ad3d8a7243",
-        "index_device.h": "4fc7954ba2e0f34237e857a40b9266a2588f34c652e09c4888bce58229cb8e7b",
-        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
-    ("k_index_scores", "decode", 131072): (6.088e+08, {
-        "indexer.hip": "90268b84256a5ecd9b6717ec0692420efe6bc46bcc5cc15155248957dd7c612b",
-        "index_device.h": "4fc7954ba2e0f34237e857a40b9266a2588f34c652e09c4888bce58229cb8e7b",
-        "csa2_device.h": "23c08a45f7aced302a10bbf0471968658a3ce8baff72dd633379897f7cedeec0"}),
+        "index_device.h": "199bc659f1aff50ef65e765600da6c8d7f8d1fabe7c79a5fe6da0f8fc9a7498a",
+        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
+    ("k_fs_scan", "decode", 131072): (5.8596e+08, {
+        "decode_select.hip": "96e381ce5df55e01d0a4b57aad26feb24b3bf3a3003ad4542bd8062b25ea7ec6",
+        "index_device.h": "199bc659f1aff50ef65e765600da6c8d7f8d1fabe7c79a5fe6da0f8fc9a7498a",
+        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
 }
 
 
@@ -463,18 +463,21 @@ def run_decode(args, result, stream, ratio=2, z_format=0):
             "value": dwl.B * dwl.Tq / (dms * 1e-3), "unit": "query-tokens/s", "ms_per_step": dms,
             "stages_ms": dstages,
             "hbm_frac_step": nbytes / (dms * 1e-3) / PEAK_HBM,
-            "roofline": {"kernel": "k_index_scores (index-key scan)", "bound": "hbm",
-                         "achieved": scan_bytes / (dstages["index_scores"] * 1e-3) / 1e9,
+            # the selection stage (csa2_index_topk): threshold from a sample, the
+            # index-key scan keeping only candidates, the cut; its bytes are the scan's
+            "roofline": {"kernel": "k_fs_threshold + k_fs_scan + k_fs_select (index-key scan "
+                                   "with the top-512 cut; no score rows)", "bound": "hbm",
+                         "achieved": scan_bytes / (dstages["index_topk"] * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                         "frac": scan_bytes / (dstages["index_scores"] * 1e-3) / PEAK_HBM,
+                         "frac": scan_bytes / (dstages["index_topk"] * 1e-3) / PEAK_HBM,
                          "bytes_per_launch": scan_bytes,
-                         "traffic": measured_traffic("k_index_scores", "decode",
+                         "traffic": measured_traffic("k_fs_scan", "decode",
                                                      dwl.q_pos0 + 1) if ratio == 2 else None},
         }
         if "read_ceiling" in result:
             rc = result["read_ceiling"]["GB/s"] * 1e9
             result[key]["roofline"]["frac_of_read_ceiling"] = (
-                scan_bytes / (dstages["index_scores"] * 1e-3) / rc)
+                scan_bytes / (dstages["index_topk"] * 1e-3) / rc)
             result[key]["hbm_frac_step_of_read_ceiling"] = nbytes / (dms * 1e-3) / rc
         # attention's own traffic: the selected rows, the window rows, Q and O
         zrow = 288.0 if z_format else 272.0
