@@ -164,11 +164,12 @@ void* scratch_ptr() {
 }
 
 // split of a token's attention rows (20 chunks of 32 at full size) across
-// blocks when there are too few tokens to fill the chip; from 128 tokens on one
-// block per token (B=128 decode: 33 us, against 28 us + a 9 us merge of the
-// partials with two splits)
-int attn_split(int64_t tokens) {
-    if (tokens >= 128) return 1;
+// blocks when there are too few tokens to fill the chip.  The persistent
+// kernel (k_attn) takes one block per token from 128 tokens on (B=128 decode:
+// 33 us, against 28 us + a 9 us merge of the partials with two splits); the
+// dequantising kernel (k_attn_dq, one block of four waves per unit) from 256.
+int attn_split(int64_t tokens, bool dq = false) {
+    if (tokens >= (dq ? 256 : 128)) return 1;
     const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
     return ns > 8 ? 8 : ns;
 }
@@ -314,19 +315,22 @@ bool attn_zf8(int B, int Tq, int64_t stride) {
 }
 
 struct AttnWs {
-    int nsplit;
+    int nsplit, nsplit_dq;
     bool zf8;
     size_t pO, pml, zq, zs, total;
 };
+// (the partials are sized for the larger split count of the two kernels)
 AttnWs attn_ws(int B, int Tq, int H, int64_t stride) {
     AttnWs w;
     w.nsplit = attn_split((int64_t)B * Tq);
+    w.nsplit_dq = attn_split((int64_t)B * Tq, true);
     w.zf8 = attn_zf8(B, Tq, stride);
     w.pO = 0;
     w.pml = 0;
     w.total = 0;
-    if (w.nsplit > 1) {
-        const size_t n = (size_t)B * Tq * w.nsplit * H;
+    const int ns = w.nsplit > w.nsplit_dq ? w.nsplit : w.nsplit_dq;
+    if (ns > 1) {
+        const size_t n = (size_t)B * Tq * ns * H;
         w.pml = align256(n * D * sizeof(float));
         w.total = w.pml + align256(n * 2 * sizeof(float));
     }
@@ -520,15 +524,15 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
         const AttnWs L = attn_ws(B, Tq, H, stride);
         float* pO = (float*)((uint8_t*)ws + L.pO);
         float* pml = (float*)((uint8_t*)ws + L.pml);
-        const int64_t units = (int64_t)B * Tq * L.nsplit;
+        const int64_t units = (int64_t)B * Tq * L.nsplit_dq;
         if (units > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
         hipLaunchKernelGGL(k_attn_dq, dim3((unsigned)units), dim3(256), 0, st, B, Tq, H, q_pos0,
                            Q, w_codes, w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink,
-                           rc, rs, rope_rows, O, lse, win_floor, L.nsplit, pO, pml);
-        if (L.nsplit > 1) {
+                           rc, rs, rope_rows, O, lse, win_floor, L.nsplit_dq, pO, pml);
+        if (L.nsplit_dq > 1) {
             const int64_t items = (int64_t)B * Tq * H;
             hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, st,
-                               B, Tq, H, q_pos0, sink, rc, rs, rope_rows, L.nsplit, pO, pml, O,
+                               B, Tq, H, q_pos0, sink, rc, rs, rope_rows, L.nsplit_dq, pO, pml, O,
                                lse);
         }
         return check_launch("csa2_sparse_attn");

@@ -56,8 +56,10 @@ def test_workspace_sizes(L):
     # a prefill: one split (no partials); the compressed rows re-encoded as E4M3
     # rows with an fp32 scale (512 + 4 bytes per entry), each 256-byte aligned
     assert ws(csa2.OP_SPARSE_ATTN, 1, 65536, 64, 32768) == 32768 * 512 + 32768 * 4
-    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) == 0    # one block per query from 128 on
-    assert ws(csa2.OP_SPARSE_ATTN, 64, 1, 64, 65536) > 0      # fewer queries: split, partials
+    # decode: a query's rows split over blocks below 128 queries (256 for the kernel
+    # over the pages' 288-byte rows): partials, sized for either kernel
+    assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) > 0
+    assert ws(csa2.OP_SPARSE_ATTN, 256, 1, 64, 65536) == 0
     # decode gathers each entry less than four times on average: no re-encoding
     assert ws(csa2.OP_SPARSE_ATTN, 128, 1, 64, 65536) < 128 * 65536 * 516
     assert ws(csa2.OP_SPARSE_ATTN, 16, 6, 64, 524288) < 16 * 524288 * 516
