@@ -281,8 +281,9 @@ def main():
     flop_idx, flop_att = prefill_work(wl.Tq, wl.H)
     t_att = stages["sparse_attn"] * 1e-3
     t_sel = stages["index_topk"] * 1e-3
-    att = {"kernel": "k_attn (csa2_sparse_attn launches it alone at this size: gather, QK on "
-                     "the stored FP4/FP8 rows, sink softmax, bf16 PV, inverse rotation)",
+    att = {"kernel": "k_attn (gather, QK on the stored rows, sink softmax, bf16 PV, inverse "
+                     "rotation; csa2_sparse_attn also runs k_z_fp8_rows first, ~0.02 ms of the "
+                     "timed call, which re-encodes the FP4 compressed rows as E4M3)",
            "bound": "mfma", "achieved": flop_att / t_att / 1e12, "peak": PEAK_BF16 / 1e12,
            "unit": "TFLOP/s", "flop_per_launch": flop_att,
            "traffic": measured_traffic("k_attn", "prefill", wl.Tq)}
