@@ -84,6 +84,71 @@ __device__ __forceinline__ int fs_row_len(const int32_t* q_pos0, const int32_t* 
     return (int)(n < 0 ? 0 : (n > entry_stride ? entry_stride : n));
 }
 
+// Keys >= piv among keys[0, nr) (LDS, 16-byte aligned, nr a multiple of
+// 1,024; unused slots hold 0, which no point (>= 1) counts), counted by one
+// wave with ballots: one vector compare and two scalar operations a key.
+__device__ __forceinline__ uint32_t fs_wave_count(const uint32_t* keys, int nr, uint32_t piv) {
+    const int lane = threadIdx.x & 63;
+    uint32_t c = 0u;
+    for (int i = 4 * lane; i < nr; i += 4 * 256) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const uint4*)(keys + i + 256 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c += (uint32_t)__builtin_popcountll(__ballot(v[u].x >= piv));
+            c += (uint32_t)__builtin_popcountll(__ballot(v[u].y >= piv));
+            c += (uint32_t)__builtin_popcountll(__ballot(v[u].z >= piv));
+            c += (uint32_t)__builtin_popcountll(__ballot(v[u].w >= piv));
+        }
+    }
+    return c;
+}
+
+// Search of the key interval [a, bnd) for a key th with k <= #(keys >= th) <=
+// lim, given ca = #(keys >= a) >= k > cb = #(keys >= bnd): each step the
+// block's eight waves count the keys at eight evenly spaced points of the
+// interval (one point a wave, one barrier a step; the counts alternate
+// between two slot sets), so the interval shrinks ninefold per step.  The
+// counts fall as the points rise, so the points that k keys reach come first
+// and, among them, those that at most lim keys reach come last.  Ends at the
+// first point whose count is in [k, lim] (hit), else when bnd = a + 1: then a
+// is the k-th largest key, ca keys reach it and cb pass it.
+struct FsSearch {
+    uint32_t a, ca, cb;
+    bool hit;
+};
+__device__ __forceinline__ FsSearch fs_pivot_search(const uint32_t* keys, int nr, uint32_t a,
+                                                    uint64_t bnd, uint32_t ca, uint32_t cb,
+                                                    uint32_t k, uint32_t lim,
+                                                    uint32_t (*cbuf)[FS_WAVES]) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr uint32_t NP = FS_WAVES + 1;
+    int par = 0;
+    while (bnd - a > 1u) {
+        // point i = a + floor(w (i + 1) / 9) in 32-bit arithmetic (w < 2^32: a >= 1)
+        const uint32_t w = (uint32_t)(bnd - a), wq = w / NP, wr = w - wq * NP;
+        auto point = [&](int i) { return a + wq * (uint32_t)(i + 1) + wr * (uint32_t)(i + 1) / NP; };
+        const uint32_t c = fs_wave_count(keys, nr, point(wave));
+        if (lane == 0) cbuf[par][wave] = c;
+        __syncthreads();
+        const uint32_t cl = cbuf[par][lane & (FS_WAVES - 1)];
+        par ^= 1;
+        const bool mine = lane < FS_WAVES;
+        const int nk = __builtin_popcountll(__ballot(mine && cl >= k));    // points 0 .. nk-1 reach k
+        const int nl = __builtin_popcountll(__ballot(mine && cl > lim));   // points 0 .. nl-1 pass lim
+        if (nl < nk) return FsSearch{point(nl), (uint32_t)__shfl((int)cl, nl), 0u, true};
+        const uint32_t a2 = nk > 0 ? point(nk - 1) : a;
+        if (nk > 0) ca = (uint32_t)__shfl((int)cl, nk - 1);
+        if (nk < FS_WAVES) {
+            bnd = point(nk);
+            cb = (uint32_t)__shfl((int)cl, nk);
+        }
+        a = a2;
+    }
+    return FsSearch{a, ca, cb, false};
+}
+
 // ---- threshold: one block of eight waves per row ---------------------------
 // Also quantises the row's index query (the 32 head rows as k_quant_index_query
 // does) into q8 / wq for the scan and the cut; the sample's key loads are
@@ -94,8 +159,9 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_threshold(
     float* __restrict__ wq, const uint8_t* __restrict__ ki_codes,
     const uint8_t* __restrict__ ki_scales, int64_t entry_stride, int rsh,
     uint32_t* __restrict__ th_out) {
-    __shared__ uint32_t skey[4096];
+    __shared__ __attribute__((aligned(16))) uint32_t skey[4096];
     __shared__ uint32_t cbuf[2][FS_WAVES];
+    __shared__ uint32_t smm[2][FS_WAVES];
     __shared__ __attribute__((aligned(16))) uint8_t sq8[HI * DI];
     __shared__ __attribute__((aligned(16))) float swq[HI];
     const int row = blockIdx.x;                     // query row: request b, token t
@@ -110,7 +176,10 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_threshold(
     }
     const bool sample = n >= FS_MIN;
     // S = 1024 m samples (m = 1, 2 or 4 as the row passes 65,536 and 131,072
-    // entries): sample i is entry floor(i n / S); wave w scores samples
+    // entries) in S/4 runs of four consecutive entries (two whole 128-byte
+    // lines of codes and one line of scales per run, a quarter of the lines
+    // single entries would touch): sample i is entry 4 floor(r n / (4 R)) +
+    // (i mod 4), r = floor(i / 4), R = S / 4; wave w scores samples
     // 128 m w .. 128 m (w + 1) - 1 in m rounds of eight tiles of sixteen, the
     // next round's loads in flight during the current one's products
     const int lm = n <= 65536 ? 0 : (n <= 131072 ? 1 : 2), m = 1 << lm;
@@ -123,7 +192,7 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_threshold(
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = 128 * (m * wave + rnd) + 16 * u + col;
-            const int64_t e = ((int64_t)i * n) >> (10 + lm);
+            const int64_t e = ((((int64_t)(i >> 2) * n) >> (8 + lm)) & ~(int64_t)3) + (i & 3);
             kc[buf][u] = *(const uint4*)(kb + e * 64);
             sc[buf][u] = (int)sb[e * 4];
         }
@@ -160,71 +229,26 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_threshold(
     }
     __syncthreads();
     const uint32_t ks = (uint32_t)max((int64_t)24, ((int64_t)S * 2048 + n - 1) / n);
-    if (S == 1024) {
-        // one wave holds the 1,024 keys: its own search, no block barrier per step
-        if (wave == 0) {
-            uint32_t kr[16];
-#pragma unroll
-            for (int g = 0; g < 16; ++g) kr[g] = skey[64 * g + lane];
-            uint32_t th = wave_threshold_bisect(kr, ks, ks + ks / 4);
-            if (th == 0u) {             // repeated keys: the sample's ks-th largest
-                uint32_t krem;
-                th = wave_kth_bisect(kr, ks, &krem);
-            }
-            if (lane == 0) th_out[row] = th;   // a key of a finite score: never 0 or FS_ALL
-        }
-        return;
-    }
     // A key th that ks .. ks + ks/4 of the S sample keys reach (about 2,048 of the
-    // row's scores by the sample, at least 24 sample keys above th), found by
-    // halving the key range with block-wide counts; with repeated keys and no
-    // such key, the largest key that ks of them reach.
-    uint32_t kv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int i = 8 * tid + e;
-        kv[e] = i < S ? skey[i] : 0u;
-    }
+    // row's scores by the sample, at least 24 sample keys above th); with
+    // repeated keys and no such key, the ks-th largest sample key.
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        if (kv[e] != 0u) lo = min(lo, kv[e]);
-        hi = max(hi, kv[e]);
+        const int i = tid + 64 * FS_WAVES * e;
+        if (i < S) {
+            lo = min(lo, skey[i]);
+            hi = max(hi, skey[i]);
+        }
     }
     lo = wave_min(lo);
     hi = wave_max(hi);
-    if (lane == 0) { cbuf[0][wave] = lo; cbuf[1][wave] = hi; }
+    if (lane == 0) { smm[0][wave] = lo; smm[1][wave] = hi; }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < FS_WAVES; ++w) { lo = min(lo, cbuf[0][w]); hi = max(hi, cbuf[1][w]); }
-    __syncthreads();
-    const uint32_t lim = ks + ks / 4;
-    int par = 0;
-    auto block_count = [&](uint32_t th2) -> uint32_t {
-        uint32_t c = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c += kv[e] >= th2 ? 1u : 0u;
-        c = wave_sum(c);
-        if (lane == 0) cbuf[par][wave] = c;
-        __syncthreads();
-        uint32_t t2 = 0u;
-#pragma unroll
-        for (int w = 0; w < FS_WAVES; ++w) t2 += cbuf[par][w];
-        par ^= 1;
-        return t2;
-    };
-    uint32_t a = lo;                    // count(>= a) >= ks
-    uint64_t bnd = (uint64_t)hi + 1u;   // count(>= bnd) < ks
-    while (bnd - a > 1u) {
-        const uint32_t mid = (uint32_t)(a + ((bnd - a) >> 1));
-        const uint32_t c = block_count(mid);
-        if (c < ks) {
-            bnd = mid;
-        } else {
-            a = mid;
-            if (c <= lim) break;
-        }
-    }
+    for (int w = 0; w < FS_WAVES; ++w) { lo = min(lo, smm[0][w]); hi = max(hi, smm[1][w]); }
+    const uint32_t a =
+        fs_pivot_search(skey, S, lo, (uint64_t)hi + 1u, (uint32_t)S, 0u, ks, ks + ks / 4, cbuf).a;
     if (tid == 0) th_out[row] = a;      // >= the smallest finite key: never 0 or FS_ALL
 }
 
@@ -482,8 +506,9 @@ __device__ __forceinline__ uint32_t fs_block_scan(uint32_t v, uint32_t* wsum, ui
 }
 
 // The cut of a block's candidates sk/sj[0, total) (entry order): the 512th
-// largest key K by halving the key range (block-wide counts), stopping early
-// when exactly 512 keys reach the middle; then the keys > K and the first
+// largest key K by halving the key range (block-wide counts of the keys the
+// threads hold), ending early at a point p that exactly 512 keys reach (then
+// the keys >= p are the top 512); else the keys > K and the first
 // (512 - #(> K)) copies of K, written to out in ascending entry order.  SPT:
 // consecutive slots per thread (total <= 512 SPT).
 template <int SPT>
@@ -509,7 +534,6 @@ __device__ __forceinline__ void fs_cut(const uint32_t* sk, const int32_t* sj, in
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < FS_WAVES; ++w) { lo = min(lo, bc[w]); hi = max(hi, bc[FS_WAVES + w]); }
-    __syncthreads();
     int par = 0;
     // keys >= th2 (th2 >= 1) over the block; one barrier a call (the wave totals
     // alternate between two slot sets)
@@ -526,43 +550,44 @@ __device__ __forceinline__ void fs_cut(const uint32_t* sk, const int32_t* sj, in
         par ^= 1;
         return t2;
     };
-    uint32_t a = lo;
-    uint64_t bnd = (uint64_t)hi + 1u;
-    while (bnd - a > 1u) {
-        const uint32_t mid = (uint32_t)(a + ((bnd - a) >> 1));
+    // #(keys >= a) = ca >= 512 > cb = #(keys >= bnd)
+    FsSearch r{lo, (uint32_t)total, 0u, false};
+    for (uint64_t bnd = (uint64_t)hi + 1u; bnd - r.a > 1u;) {
+        const uint32_t mid = (uint32_t)(r.a + ((bnd - r.a) >> 1));
         const uint32_t c = block_count(mid);
         if (c >= (uint32_t)TOPK) {
-            a = mid;
-            if (c == (uint32_t)TOPK) break;
+            r.a = mid;
+            r.ca = c;
+            if (c == (uint32_t)TOPK) {
+                r.hit = true;
+                break;
+            }
         } else {
             bnd = mid;
+            r.cb = c;
         }
     }
-    uint32_t mk = 0xFFFFFFFFu;                 // K: the smallest key >= a
-#pragma unroll
-    for (int e = 0; e < SPT; ++e)
-        if (kv[e] >= a) mk = min(mk, kv[e]);
-    mk = wave_min(mk);
-    if (lane == 0) wsum[wave] = mk;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < FS_WAVES; ++w) mk = min(mk, wsum[w]);
-    __syncthreads();
-    const uint32_t K = mk;
-    const uint32_t above = block_count(K + 1u);
-    const uint32_t krem = (uint32_t)TOPK - above;
-    const uint32_t eq_total = block_count(K) - above;
+    // taken: the keys > K and the first `take` copies of K of this thread's slots
+    uint32_t K, take = 0u;
     uint32_t gt = 0u, eq = 0u;
+    if (r.hit) {
+        K = r.a - 1u;                           // the keys >= p: exactly 512
 #pragma unroll
-    for (int e = 0; e < SPT; ++e) {
-        gt += kv[e] > K;
-        eq += kv[e] == K;
-    }
-    uint32_t take = eq;
-    if (krem < eq_total) {
-        uint32_t eq_tot;
-        const uint32_t rank0 = fs_block_scan(eq, wsum, &eq_tot);
-        take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+        for (int e = 0; e < SPT; ++e) gt += kv[e] > K;
+    } else {
+        K = r.a;                                // r.ca keys reach K, r.cb pass it
+        const uint32_t krem = (uint32_t)TOPK - r.cb;
+#pragma unroll
+        for (int e = 0; e < SPT; ++e) {
+            gt += kv[e] > K;
+            eq += kv[e] == K;
+        }
+        take = eq;
+        if (krem < r.ca - r.cb) {
+            uint32_t eq_tot;
+            const uint32_t rank0 = fs_block_scan(eq, wsum, &eq_tot);
+            take = krem > rank0 ? min(krem - rank0, eq) : 0u;
+        }
     }
     uint32_t sel_tot;
     uint32_t off = fs_block_scan(gt + take, wsum, &sel_tot);
@@ -599,6 +624,9 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
     const int b = row / Tq, t = row - b * Tq;
     const int n = fs_row_len(q_pos0, n_entries, b, t, entry_stride, rsh);
     int32_t* out = idx + (int64_t)row * TOPK;
+    // chunk tid's count is loaded beside the threshold word (the slots of a row
+    // that the scan skipped hold stale values, which are then not used)
+    const int k_tid = tid < n_ch ? ccnt[(int64_t)row * n_ch + tid] : 0;
     const uint32_t th = th_in[row];
     if (th == FS_ALL) {
         for (int i = tid; i < TOPK; i += 64 * FS_WAVES) out[i] = i < n ? i : -1;
@@ -607,13 +635,16 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
     }
     // the chunks' counts: total, and whether any chunk overflowed its slots
     uint32_t total = 0u;
+    uint32_t k_first = 0u;                          // chunk tid's count (the first pass's)
     bool bad = th == FS_SLOW;
     if (!bad) {
         uint32_t tc = 0u, over = 0u;
         for (int c = tid; c < n_ch; c += 64 * FS_WAVES) {
-            const int k = ccnt[(int64_t)row * n_ch + c];
+            const int k = c == tid ? k_tid : ccnt[(int64_t)row * n_ch + c];
             over |= (uint32_t)(k < 0 || k > wcap);
-            tc += (uint32_t)(k < 0 ? 0 : (k > wcap ? wcap : k));
+            const uint32_t kc = (uint32_t)(k < 0 ? 0 : (k > wcap ? wcap : k));
+            if (c == tid) k_first = kc;
+            tc += kc;
         }
         tc = wave_sum(tc);
         over = wave_max(over);
@@ -655,28 +686,60 @@ __global__ void __launch_bounds__(64 * FS_WAVES) k_fs_select(
     }
     // gather the candidates in entry order: chunk c's to slots pre[c] .., the
     // chunks' offsets by a block scan, 512 chunks a pass; wave w copies chunks
-    // w, w + 8, .. of the pass, a lane per candidate
+    // w, w + 8, .., four chunks' first 128 candidates in flight at a time (a
+    // chunk holds about 64 at the usual threshold), a lane per candidate
     {
+        constexpr int NT = 64 * FS_WAVES;
         uint32_t run = 0u;                 // slots before this pass's chunks
-        for (int c0 = 0; c0 < n_ch; c0 += 64 * FS_WAVES) {
+        for (int c0 = 0; c0 < n_ch; c0 += NT) {
             const int c = c0 + tid;
             uint32_t k = 0u;
-            if (c < n_ch) {
+            if (n_ch <= NT) {
+                k = k_first;
+            } else if (c < n_ch) {
                 const int kk = ccnt[(int64_t)row * n_ch + c];
                 k = (uint32_t)(kk < 0 ? 0 : kk);
             }
             uint32_t tot;
-            const uint32_t pre = run + fs_block_scan(k, wsum, &tot);
-            spre[tid] = pre;
-            spre[64 * FS_WAVES + tid] = k;
+            spre[tid] = run + fs_block_scan(k, wsum, &tot);
+            spre[NT + tid] = k;
             __syncthreads();
-            const int nc = min(n_ch - c0, 64 * FS_WAVES);
-            for (int cc = wave; cc < nc; cc += FS_WAVES) {
-                const uint32_t p0 = spre[cc], kc = spre[64 * FS_WAVES + cc];
-                const int64_t s0 = ((int64_t)row * n_ch + c0 + cc) * wcap;
-                for (uint32_t i = lane; i < kc; i += 64) {
-                    sk[p0 + i] = ck[s0 + i];
-                    sj[p0 + i] = cj[s0 + i];
+            const int nc = min(n_ch - c0, NT);
+            for (int cc0 = wave; cc0 < nc; cc0 += 4 * FS_WAVES) {
+                uint32_t kq[4][2];
+                int32_t jq[4][2];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cc = cc0 + u * FS_WAVES;
+                    const uint32_t kc = cc < nc ? spre[NT + cc] : 0u;
+                    const int64_t s0 = ((int64_t)row * n_ch + c0 + cc) * wcap;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t i = (uint32_t)(lane + 64 * h);
+                        if (i < kc) {
+                            kq[u][h] = ck[s0 + i];
+                            jq[u][h] = cj[s0 + i];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cc = cc0 + u * FS_WAVES;
+                    if (cc >= nc) break;
+                    const uint32_t p0 = spre[cc], kc = spre[NT + cc];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t i = (uint32_t)(lane + 64 * h);
+                        if (i < kc) {
+                            sk[p0 + i] = kq[u][h];
+                            sj[p0 + i] = jq[u][h];
+                        }
+                    }
+                    const int64_t s0 = ((int64_t)row * n_ch + c0 + cc) * wcap;
+                    for (uint32_t i = (uint32_t)lane + 128u; i < kc; i += 64u) {
+                        sk[p0 + i] = ck[s0 + i];
+                        sj[p0 + i] = cj[s0 + i];
+                    }
                 }
             }
             __syncthreads();

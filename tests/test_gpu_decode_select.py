@@ -42,8 +42,11 @@ CHUNK = 2048               # entries a scan wave covers; 512 candidate slots eac
 
 def _sample_threshold_range(S, n):
     """the keys the sampled threshold can take: between the sample's ks-th and
-    (ks + ks/4)-th largest score of 1,024 entries spread over the row"""
-    smp = np.sort(S[(np.arange(1024) * n) >> 10])[::-1]
+    (ks + ks/4)-th largest score of 1,024 entries spread over the row in 256 runs
+    of four consecutive entries (each run starting at a multiple of four)"""
+    i = np.arange(1024, dtype=np.int64)
+    pos = ((((i >> 2) * n) >> 8) & ~np.int64(3)) + (i & 3)
+    smp = np.sort(S[pos])[::-1]
     ks = (2048 * 1024 + n - 1) // n
     return smp[ks - 1], smp[ks + ks // 4 - 1]
 
@@ -69,7 +72,7 @@ def test_decode_selection_paths(dev, orc):
     kpre[0][dup] = kpre[0][src[dup]]
     kpre[3] = kpre[3][:1]                               # request 3: one key everywhere
     n4 = int(ne[4])
-    hot = (np.arange(100) * 10 * n4) >> 10              # request 4: 100 sampled entries
+    hot = ((((np.arange(100) * 10) >> 2) * n4) >> 8 & ~3) + (np.arange(100) * 10 & 3)   # request 4: 100 sampled entries
     kpre[4][hot] = 6.0 * u
     kpre[5][4096:5596] += 3.0 * u                       # request 5: a run inside chunk 2
     kc = np.zeros((B, N, 64), np.uint8)
