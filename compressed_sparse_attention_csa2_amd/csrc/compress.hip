@@ -253,11 +253,12 @@ __device__ __forceinline__ void window_row(int64_t slot, int64_t prow, int lane,
     for (int s = 1; s <= 32; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
     const float scale = amax > 0.0f ? div_rn(amax, 448.0f) : 1.0f;
     uint32_t lo = 0, hi = 0;
-    if (amax > 0.0f) {
+    if (amax > 0.0f) {          // |x / scale| <= 448 (1 + 2^-23): inside e4m3_pack4's range
+        float y[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lo |= e4m3_code(div_rn(x[k], scale)) << (8 * k);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) hi |= e4m3_code(div_rn(x[k + 4], scale)) << (8 * k);
+        for (int k = 0; k < 8; ++k) y[k] = div_rn(x[k], scale);
+        lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
+        hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
     }
     *(uint2*)(w_codes + slot * D + 8 * lane) = make_uint2(lo, hi);
     if (lane == 0) w_scale[slot] = scale;

@@ -115,6 +115,15 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return c | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
+// E4M3FN codes of four values of magnitude below 464 (byte k = value k), by
+// the hardware fp32 -> fp8 conversion, which rounds to nearest even as
+// e4m3_code does and gives the same code for every such value (448 <= |v| <
+// 464 included: 448).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
 // E4M3FN code of a non-negative finite value -> fp32 (exact)
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;

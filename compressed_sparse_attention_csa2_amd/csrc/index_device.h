@@ -45,9 +45,12 @@ __device__ __forceinline__ void quant_index_row(const uint16_t* qrow, float w, u
     for (int s = 1; s <= 8; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
     const float sc = amax > 0.0f ? div_rn(amax, 448.0f) : 1.0f;
     uint32_t c[2] = {0u, 0u};
-    if (amax > 0.0f) {
+    if (amax > 0.0f) {          // |x / sc| <= 448 (1 + 2^-23): inside e4m3_pack4's range
+        float y[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i >> 2] |= e4m3_code(div_rn(x[i], sc)) << (8 * (i & 3));
+        for (int i = 0; i < 8; ++i) y[i] = div_rn(x[i], sc);
+        c[0] = e4m3_pack4(y[0], y[1], y[2], y[3]);
+        c[1] = e4m3_pack4(y[4], y[5], y[6], y[7]);
     }
     *(uint2*)(q8row + 8 * l16) = uint2{c[0], c[1]};
     if (l16 == 0) *wq_out = w * sc;
