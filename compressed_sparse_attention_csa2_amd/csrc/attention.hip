@@ -896,18 +896,18 @@ __global__ void __launch_bounds__(256) k_z_fp8_rows(int64_t n, const uint8_t* __
     uint32_t out[4];
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-        uint32_t q[8];
+        float q[8];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f2 v = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 0)
                        : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 1)
                        : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 2)
                                 : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[w], 1.0f, 3);
-            q[2 * b] = e4m3_code(v[0] * f);
-            q[2 * b + 1] = e4m3_code(v[1] * f);
+            q[2 * b] = v[0] * f;                // exact: f is a power of two, |v f| <= 384
+            q[2 * b + 1] = v[1] * f;
         }
-        out[2 * w] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        out[2 * w + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        out[2 * w] = e4m3_pack4(q[0], q[1], q[2], q[3]);
+        out[2 * w + 1] = e4m3_pack4(q[4], q[5], q[6], q[7]);
     }
     *(uint4*)(oc + e * 512 + 16 * l) = make_uint4(out[0], out[1], out[2], out[3]);
     if (l == 0) os[e] = ldexpf(1.0f, (int)emx - 133);

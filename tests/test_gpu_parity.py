@@ -659,16 +659,18 @@ def test_single_token_rows_sampled_start(dev, orc, N):
 
 
 def test_topk_row_paths(dev, orc):
-    """the one-block-per-row selection (few rows, 16,384..131,072 cache rows) on its
-    paths: a sampled threshold (20,000 candidates), every score kept without a
-    sample (3,000), and the exact fallback when the sample cannot separate the scores
-    (all 20,000 keys identical: the first 512 entries) or when the large scores sit
-    in one contiguous run (entries 5,000..7,499: the wave whose eighth holds them
-    has more candidates than room)"""
+    """the one-block-per-row selection over score rows (k_topk_row: few rows of more
+    than eight tokens a request, 16,384..131,072 cache rows; rows of up to eight
+    tokens take the selection without score rows) on its paths: a sampled threshold
+    (20,000 candidates), every score kept without a sample (3,000), and the exact
+    fallback when the sample cannot separate the scores (all 20,000 keys identical:
+    the first 512 entries) or when the large scores sit in one contiguous run
+    (entries 5,000..7,499: the wave whose eighth holds them has more candidates than
+    room)"""
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     rng = np.random.default_rng(71)
-    B, Tq, N = 4, 2, 20_000
+    B, Tq, N = 4, 9, 20_000
     kc = np.zeros((B, N, 64), np.uint8)
     ks = np.zeros((B, N, 4), np.uint8)
     for b in range(2):
