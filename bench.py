@@ -33,17 +33,17 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (2.0058e+10, {
-        "attention.hip": "25b23f3dcca9eb0e6553a89eaea860045d5ccaae5ef4d92fe31e2ca514720da9",
-        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
-    ("k_index_select", "prefill", 65536): (4.8099e+08, {
+    ("k_attn", "prefill", 65536): (2.0135e+10, {
+        "attention.hip": "7c7bc444a0a71829d15f7669a11be63b7a8fa1b049589b94f28b5bd6441dbeed",
+        "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
+    ("k_index_select", "prefill", 65536): (4.8140e+08, {
         "index_select.hip": "5fdd172ede2fae924619737dcf18698bfcc5853990b4fb175acce9ad3d8a7243",
-        "index_device.h": "199bc659f1aff50ef65e765600da6c8d7f8d1fabe7c79a5fe6da0f8fc9a7498a",
-        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
-    ("k_fs_scan", "decode", 131072): (5.8596e+08, {
-        "decode_select.hip": "96e381ce5df55e01d0a4b57aad26feb24b3bf3a3003ad4542bd8062b25ea7ec6",
-        "index_device.h": "199bc659f1aff50ef65e765600da6c8d7f8d1fabe7c79a5fe6da0f8fc9a7498a",
-        "csa2_device.h": "169a4cbc74701e3784cc4abf200aa8fe38764539d5817efc0b58142d69cecd76"}),
+        "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
+        "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
+    ("k_fs_scan", "decode", 131072): (5.8569e+08, {
+        "decode_select.hip": "a83429d46ec1808fcd1dc33f370106529af6560923cbedb547ae331c9705ce13",
+        "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
+        "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
 }
 
 
