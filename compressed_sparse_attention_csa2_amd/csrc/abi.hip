@@ -170,7 +170,10 @@ void* scratch_ptr() {
 // dequantising kernel (k_attn_dq, one block of four waves per unit) from 256.
 int attn_split(int64_t tokens, bool dq = false) {
     if (tokens >= (dq ? 256 : 128)) return 1;
-    const int ns = (int)cdiv(256, tokens > 0 ? tokens : 1);
+    // k_attn is persistent (one block per compute unit): no more units than
+    // blocks, so that no block takes two (96 verify rows: 2 splits, not 3)
+    const int64_t t1 = tokens > 0 ? tokens : 1;
+    const int ns = (int)(dq ? cdiv(256, t1) : 256 / t1);
     return ns > 8 ? 8 : ns;
 }
 
