@@ -307,7 +307,10 @@ def test_decode_over_prefill_caches(dev, synth, ratio, zf):
 
 def test_quant_index_query_bit_exact_full_size(dev, synth, orc):
     """the indexer's E4M3 query rows and folded weights for every (token, head) row of
-    the 65,536-token workload, plus edge rows (zero, tiny, huge, exact ties, saturation)"""
+    the 65,536-token workload, plus edge rows (zero, tiny, huge, exact ties, saturation),
+    and rows whose largest element is 448, so that the quotient is the value itself and
+    the hardware E4M3 conversion meets every rounding midpoint of the format (normal and
+    subnormal, both signs) and the values one bf16 step to either side"""
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     import tests.test_oracle_compress as tc
@@ -324,8 +327,18 @@ def test_quant_index_query_bit_exact_full_size(dev, synth, orc):
     edge[5] = np.ldexp(1.0, rng.integers(-20, 20, (32, 128))) * rng.choice([-1, 1], (32, 128))
     edge[6] = rng.choice([448.0, 464.0, 480.0, -448.0], (32, 128))
     edge[7] = np.exp(rng.standard_normal((32, 128)) * 4)
-    qI = np.concatenate([qI, tc.bf16(edge)])
-    wI = np.concatenate([wI, (rng.standard_normal((8, 32)) / 64).astype(np.float32)])
+    # E4M3 midpoints: (1 + (2m + 1)/16) 2^e for normal codes, (k + 1/2) 2^-9 below 2^-6
+    mids = [(1 + (2 * m + 1) / 16) * 2.0 ** e for e in range(-6, 9) for m in range(8)]
+    mids += [(k + 0.5) * 2.0 ** -9 for k in range(8)]
+    mids = np.array([v for v in mids if v < 464.0])
+    vals = np.concatenate([mids, mids * (1 + 2.0 ** -7), mids * (1 - 2.0 ** -7)])
+    vals = np.concatenate([vals, -vals])
+    ties = np.zeros((2, 32, 128), np.float32)
+    flat = np.resize(vals, 2 * 32 * 127).reshape(2, 32, 127)
+    ties[:, :, 0] = 448.0
+    ties[:, :, 1:] = flat
+    qI = np.concatenate([qI, tc.bf16(edge), tc.bf16(ties)])
+    wI = np.concatenate([wI, (rng.standard_normal((10, 32)) / 64).astype(np.float32)])
     rows = qI.shape[0] * 32
     log(f"csa2_quant_index_query: {rows} rows")
     q8 = torch.zeros(rows, 128, dtype=torch.uint8, device=dev)
