@@ -41,7 +41,7 @@ TRAFFIC = {
         "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
     ("k_fs_scan", "decode", 131072): (5.8569e+08, {
-        "decode_select.hip": "a83429d46ec1808fcd1dc33f370106529af6560923cbedb547ae331c9705ce13",
+        "decode_select.hip": "c540a14f8813d7e03290fe744d3637f0e16f4c3a89a7ae114331a0357ee79d74",
         "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
 }

@@ -11,9 +11,10 @@
 // stream; writing every fp32 score and reading it back for the selection cost
 // as much as a third of that stream again.  Three passes instead:
 //   k_fs_threshold  one block per row quantises the row's index query, scores
-//                   S = 1,024 .. 4,096 entries spread evenly over the row and
-//                   takes a key th that max(24, ceil(2,048 S / n)) of the sample
-//                   reach (about 2,048 of the row's n scores by the sample);
+//                   S = 1,024 .. 4,096 entries (runs of four spread evenly over
+//                   the row) and takes a threshold th that ks .. 1.25 ks of the
+//                   sample keys reach, ks = max(24, ceil(2,048 S / n)) (about
+//                   2,048 of the row's n scores by the sample);
 //   k_fs_scan       one wave per (row, chunk of IDX_CHUNK entries) scores the
 //                   chunk and keeps the keys >= th with their entries, in entry
 //                   order, in the chunk's own slots (no atomics, so the order
