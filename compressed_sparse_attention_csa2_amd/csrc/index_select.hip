@@ -52,9 +52,11 @@ template <int TOK> struct SelCfg {
     static constexpr int keep = cap - 192;
     static constexpr int waves = TOK == 1 ? 3 : (TOK == 4 ? 2 : 1);
 };
-// lists at least this long start from a sampled threshold (the four-token form,
-// and single-token rows up to 65,536 entries)
-constexpr int SAMPLE_MIN = 4096;
+// Lists at least this long start from a sampled threshold.  Four-token groups:
+// from 1,024 candidates (a shorter list is trimmed only once or twice).
+// Single-token rows: from 4,096 up to 65,536 entries.
+constexpr int SAMPLE_MIN = 1024;
+constexpr int ROW_SAMPLE_MIN = 4096;
 
 template <int TOK>
 struct SelBuf {
@@ -118,7 +120,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
 
     // the whole row of a single-token item (its segments' union), for the sampled start
     const int n_row = TOK == 1 ? (int)min(cand_count(qp, t0, ne, entry_stride, rsh), (int64_t)0x7FFFFFFF) : 0;
-    const bool row_sampled = TOK == 1 && n_row >= SAMPLE_MIN && n_row <= 65536;   // offsets fit 16 bits
+    const bool row_sampled = TOK == 1 && n_row >= ROW_SAMPLE_MIN && n_row <= 65536;   // offsets fit 16 bits
     const __amdgpu_buffer_rsrc_t krow = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(ki_codes + (int64_t)b * entry_stride * 64), (short)0, row_sampled ? n_row * 64 : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
@@ -334,8 +336,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         // entries every token of the group may select.  With p = 512 / n the
         // fraction of a token's n candidates in its top 512, about 256 p of the
         // sample's scores fall there; a threshold reached by r = 256 p + 3
-        // sqrt(256 p) + 1 of them (up to 1.5 r) leaves fewer than 512 scores
-        // above it only rarely, and then the token is scanned again from
+        // sqrt(256 p) + 1 of them (up to 1.5 r, within the 256 scores for
+        // n >= 1,024) leaves fewer than 512 scores above it only rarely, and
+        // then the token is scanned again from
         // minus infinity.  Without it a token's threshold starts at minus
         // infinity and rises only as its buffer fills, so a long list is
         // trimmed many more times.

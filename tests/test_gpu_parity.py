@@ -542,21 +542,27 @@ def test_fused_select_clustered_scores(dev, orc, Tq):
             assert gc_[b, i] == r_cnt and np.array_equal(gi[b, i], r_idx), (b, i)
 
 
-def test_fused_select_sampled_start(dev, orc):
-    """the four-token form of the fused kernel starts long lists (4,096 entries or
-    more) from a threshold taken on 16 tiles of 16 entries spread evenly over the
-    list, and scans a token again from minus infinity when fewer than 512 scores
-    pass it.  Here every large score sits in those tiles for the tokens whose query
-    follows the keys' common direction (tokens 0 and 1 of each group of four), and
-    ReLU zeroes every other score of theirs (a tie of 16,128 zeros at the cut): they
-    take the rescan.  Of the other tokens (random queries) some keep their sampled
+@pytest.mark.parametrize("N", [1024, 2048, 16384])
+def test_fused_select_sampled_start(dev, orc, N):
+    """the four-token form of the fused kernel starts lists of 1,024 entries or
+    more from a threshold taken on 16 tiles of 16 entries spread evenly over the
+    list (over each segment of a list cut into segments), and scans a token again
+    from minus infinity when fewer than 512 scores pass it.  The tokens whose query
+    follows the keys' common direction (tokens 0 and 1 of each group of four) have
+    large scores only in the 16 tiles the whole list's sample reads, and ReLU zeroes
+    every other score of theirs.  N <= 4096 (one segment, N=1024 the shortest list
+    that takes the sample): fewer than 512 of their scores pass the threshold and
+    they take the rescan, then cut a tie of zeros.  N=16384 (four 4,096-entry
+    segments, each sampling its own tiles, none of them large): they start from
+    a threshold below zero, keep every score and cut a tie of zeros in each segment
+    before the merge.  Of the other tokens (random queries) some keep their sampled
     start, some rescan.  All must give the exact top 512."""
     import math
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     import tests.test_oracle_compress as tc
     rng = np.random.default_rng(29)
-    N, Tq = 16384, 12
+    Tq = 12
     u = rng.standard_normal(128)
     u /= np.linalg.norm(u)
     starts = (((2 * np.arange(16) + 1) * N) // 32) & ~15
@@ -582,9 +588,16 @@ def test_fused_select_sampled_start(dev, orc):
         smp = np.sort(np.concatenate([S[s0:s0 + 16] for s0 in starts]))
         above.append(np.count_nonzero(S >= smp[-r]))
     # the construction does what it is for: the aligned tokens' sample has fewer than
-    # 512 scores above its r-th largest; some random token has more than enough
-    assert all(above[i] < 512 for i in range(Tq) if aligned[i])
-    assert any(above[i] >= 1024 for i in range(Tq) if not aligned[i])
+    # 512 scores above its r-th largest, or (segments) no segment's sample holds a
+    # large score; some random token has more than enough
+    if N <= 4096:
+        assert all(above[i] < 512 for i in range(Tq) if aligned[i])
+        assert any(above[i] >= 512 for i in range(Tq) if not aligned[i])
+    else:
+        seg_starts = [s0 + ((((2 * q + 1) * 4096) // 32) & ~15)
+                      for s0 in range(0, N, 4096) for q in range(16)]
+        assert not any(hot[s0:s0 + 16].any() for s0 in seg_starts)
+        assert any(above[i] >= 1024 for i in range(Tq) if not aligned[i])
     log(f"fused selection, sampled start and rescan: Tq={Tq} N={N}")
     idx = torch.full((1, Tq, 512), -7, dtype=torch.int32, device=dev)
     cnt = torch.full((1, Tq), -7, dtype=torch.int32, device=dev)
