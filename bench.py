@@ -36,8 +36,8 @@ TRAFFIC = {
     ("k_attn", "prefill", 65536): (2.0135e+10, {
         "attention.hip": "7c7bc444a0a71829d15f7669a11be63b7a8fa1b049589b94f28b5bd6441dbeed",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
-    ("k_index_select", "prefill", 65536): (4.8140e+08, {
-        "index_select.hip": "5fdd172ede2fae924619737dcf18698bfcc5853990b4fb175acce9ad3d8a7243",
+    ("k_index_select", "prefill", 65536): (4.8047e+08, {
+        "index_select.hip": "4babd359c70c06ae09f331536790e3e920365a8c0430b04291a78ceffae13161",
         "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
     ("k_fs_scan", "decode", 131072): (5.8569e+08, {
