@@ -199,16 +199,27 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(v), 63);
 }
 
+// How many of the buffered keys (R register rows of 64, 0 = no element) reach
+// x: a ballot and a scalar bit count per row, the same in every lane.
+template <int R>
+__device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&kr)[R], uint32_t x) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) c += (uint32_t)__popcll(__ballot(kr[r] >= x));
+    return c;
+}
+
 // A key theta that at least k and at most `limit` of the buffered keys (held in
 // registers as below, 0 = no element) reach, found by halving the interval
 // [smallest key, largest key]: each step counts the keys >= its middle.
 // Returns 0 when no such theta exists (so many keys equal one value that every
 // threshold leaves either fewer than k or more than `limit`; all keys equal
 // included).  The caller's buffer holds more than `limit` keys.
-__device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[16], uint32_t k, uint32_t limit) {
+template <int R>
+__device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[R], uint32_t k, uint32_t limit) {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < R; ++r) {
         if (kr[r] != 0u) lo = min(lo, kr[r]);
         hi = max(hi, kr[r]);
     }
@@ -218,10 +229,7 @@ __device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[1
     uint64_t b = (uint64_t)hi + 1u;         // fewer than k keys >= b
     while (b - a > 1u) {
         const uint32_t mid = (uint32_t)(a + ((b - a) >> 1));
-        uint32_t c = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) c += kr[r] >= mid ? 1u : 0u;
-        c = wave_sum(c);
+        const uint32_t c = wave_count_ge(kr, mid);
         if (c >= k) {
             a = mid;
             if (c <= limit) return a;
@@ -237,10 +245,11 @@ __device__ __forceinline__ uint32_t wave_threshold_bisect(const uint32_t (&kr)[1
 // the k largest (0xFFFFFFFF: all of them), by halving [smallest, largest key]:
 // each step counts the keys >= its middle.  Stops early when exactly k keys
 // reach the middle (the k-th largest is then their minimum).
-__device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[16], uint32_t k, uint32_t* krem_out) {
+template <int R>
+__device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[R], uint32_t k, uint32_t* krem_out) {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < R; ++r) {
         if (kr[r] != 0u) lo = min(lo, kr[r]);
         hi = max(hi, kr[r]);
     }
@@ -251,14 +260,11 @@ __device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[16], ui
     uint32_t cb = 0u;
     while (b - a > 1u) {
         const uint32_t mid = (uint32_t)(a + ((b - a) >> 1));
-        uint32_t c = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) c += kr[r] >= mid ? 1u : 0u;
-        c = wave_sum(c);
+        const uint32_t c = wave_count_ge(kr, mid);
         if (c == k) {
             uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < R; ++r)
                 if (kr[r] >= mid) m = min(m, kr[r]);
             *krem_out = 0xFFFFFFFFu;
             return wave_min(m);
@@ -276,17 +282,17 @@ __device__ __forceinline__ uint32_t wave_kth_bisect(const uint32_t (&kr)[16], ui
 
 // Keep, in order, the buffered elements above theta and the first krem equal to
 // it; the buffer (key, jb) holds keys, or with AS_SCORE the scores' bit patterns.
-template <bool AS_SCORE, typename JT>
-__device__ __forceinline__ int wave_keep_buf(uint32_t* key, JT* jb, int nc, const uint32_t (&kr)[16],
+template <bool AS_SCORE, typename JT, int R>
+__device__ __forceinline__ int wave_keep_buf(uint32_t* key, JT* jb, int nc, const uint32_t (&kr)[R],
                              uint32_t theta, uint32_t krem) {
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
-    int32_t jr[16];
+    int32_t jr[R];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) jr[r] = 64 * r + lane < nc ? (int32_t)jb[64 * r + lane] : 0;
+    for (int r = 0; r < R; ++r) jr[r] = 64 * r + lane < nc ? (int32_t)jb[64 * r + lane] : 0;
     uint32_t kept = 0, eq = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < R; ++r) {
         if (64 * r >= nc) break;
         const bool valid = 64 * r + lane < nc;
         const uint64_t meq = __ballot(valid && kr[r] == theta);

@@ -83,6 +83,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
     constexpr int CAP = SelCfg<TOK>::cap;
     constexpr int CHK = SelCfg<TOK>::tiles;
     constexpr int TRIGGER = CAP - 16 * (CHK + 1);
+    constexpr int KR = CAP / 64;                  // register rows of a buffer's keys
     __shared__ SelLds<TOK> L;
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
@@ -172,9 +173,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
     auto refill = [&](int r, int g) {      // r: a compile-time row set, g: the lane row
         const int tk = TOK == 1 ? 0 : 4 * r + g;
         const int nc = __builtin_amdgcn_readlane(fill[r], 16 * g);
-        uint32_t kr[16];
+        uint32_t kr[KR];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < KR; ++q) {
             const int i = 64 * q + lane;
             kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
         }
@@ -286,9 +287,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         scan(krow, srow, n_row);
         int nc = __builtin_amdgcn_readfirstlane(fill[0]);
         if (nc > TOPK) {
-            uint32_t kr[16];
+            uint32_t kr[KR];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
+            for (int q = 0; q < KR; ++q) {
                 const int i = 64 * q + lane;
                 kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[0][i])) : 0u;
             }
@@ -475,10 +476,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
         if (t >= Tq) break;
         const int64_t row = (int64_t)b * Tq + t;
         int nc = __builtin_amdgcn_readlane(fill[r], 16 * g);
-        uint32_t kr[16];
+        uint32_t kr[KR];
         if (nc > TOPK || nseg > 1) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
+            for (int q = 0; q < KR; ++q) {
                 const int i = 64 * q + lane;
                 kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
             }
@@ -487,10 +488,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SelCfg<
             uint32_t krem;
             const uint32_t kth = wave_kth_bisect(kr, TOPK, &krem);
             nc = wave_keep_buf<true>(L.b.key[tk], L.b.j[tk], nc, kr, kth, krem);
+            if (nseg > 1) {          // the segment's keys again, for its winners' bound
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int i = 64 * q + lane;
-                kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+                for (int q = 0; q < KR; ++q) {
+                    const int i = 64 * q + lane;
+                    kr[q] = i < nc ? score_key(__uint_as_float(L.b.key[tk][i])) : 0u;
+                }
             }
         }
         if (nseg == 1) {
