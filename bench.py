@@ -36,13 +36,13 @@ TRAFFIC = {
     ("k_attn", "prefill", 65536): (2.0135e+10, {
         "attention.hip": "7c7bc444a0a71829d15f7669a11be63b7a8fa1b049589b94f28b5bd6441dbeed",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
-    ("k_index_select", "prefill", 65536): (4.8047e+08, {
-        "index_select.hip": "4babd359c70c06ae09f331536790e3e920365a8c0430b04291a78ceffae13161",
-        "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
+    ("k_index_select", "prefill", 65536): (4.8043e+08, {
+        "index_select.hip": "379c201f58b7c75543d72111b0d9cfffd73f736db9747b93b3ccad3f49bf4ca7",
+        "index_device.h": "0acd7979927cedfd769d0d2bc055ab7118f0556847fcd84d3738b3b2a3260522",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
-    ("k_fs_scan", "decode", 131072): (5.8569e+08, {
+    ("k_fs_scan", "decode", 131072): (5.8564e+08, {
         "decode_select.hip": "c540a14f8813d7e03290fe744d3637f0e16f4c3a89a7ae114331a0357ee79d74",
-        "index_device.h": "429716c4f78a4dcc24276dc1b0df86f4cfa09cc0da05d214afb28928f6d0be5a",
+        "index_device.h": "0acd7979927cedfd769d0d2bc055ab7118f0556847fcd84d3738b3b2a3260522",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
 }
 
