@@ -79,7 +79,7 @@ template <int HG, bool ZF8>
 __global__ void k_attn(int, int, int, const int32_t*, const uint16_t*, const uint8_t*,
                        const float*, int, const uint8_t*, const uint8_t*, int64_t, const int32_t*,
                        const int32_t*, const float*, const float*, const float*, int64_t,
-                       uint16_t*, float*, int, float*, float*, const int32_t*);
+                       uint16_t*, float*, int, float*, float*, const int32_t*, int);
 __global__ void k_attn_combine(int, int, int, const int32_t*, const float*, const float*,
                                const float*, int64_t, int, const float*, const float*, uint16_t*,
                                float*);
@@ -318,15 +318,19 @@ bool attn_zf8(int B, int Tq, int64_t stride) {
 }
 
 struct AttnWs {
-    int nsplit, nsplit_dq;
+    int nsplit, nsplit_dq, hsplit;
     bool zf8;
     size_t pO, pml, zq, zs, total;
 };
 // (the partials are sized for the larger split count of the two kernels)
 AttnWs attn_ws(int B, int Tq, int H, int64_t stride) {
     AttnWs w;
-    w.nsplit = attn_split((int64_t)B * Tq);
-    w.nsplit_dq = attn_split((int64_t)B * Tq, true);
+    // k_attn: 65 to 128 query rows fill the GPU with two head groups a row (no
+    // merge: heads are independent) in place of row splits and their merge
+    const int64_t rows = (int64_t)B * Tq;
+    w.hsplit = (H % 32 == 0 && rows > 64 && rows <= 128) ? 2 : 1;
+    w.nsplit = w.hsplit > 1 ? 1 : attn_split(rows);
+    w.nsplit_dq = attn_split(rows, true);
     w.zf8 = attn_zf8(B, Tq, stride);
     w.pO = 0;
     w.pml = 0;
@@ -557,16 +561,16 @@ csa2_status launch_attn(int B, int Tq, int H, const int32_t* q_pos0, const uint1
         z_codes = zq;
         z_scales = (const uint8_t*)zsf;
     }
-    // persistent blocks (one per compute unit) walk the (row, split) units
-    const int64_t units = (int64_t)B * Tq * L.nsplit;
+    // persistent blocks (one per compute unit) walk the (row, split, head group) units
+    const int64_t units = (int64_t)B * Tq * L.nsplit * L.hsplit;
     if (units > (int64_t)0x7FFFFFFF) return fail(CSA2_ERR_SHAPE, "sparse_attn: too many rows");
     const int64_t nblk = units < device_cus() ? units : device_cus();
     const dim3 grid((unsigned)nblk);
-    const int ht = H / 16;   // head tiles of 16
+    const int ht = H / 16 / L.hsplit;   // head tiles of 16 a unit
 #define CSA2_ATTN(HTV, ZF)                                                                     \
     hipLaunchKernelGGL((k_attn<HTV, ZF>), grid, dim3(ATT_THREADS), 0, st, B, Tq, H, q_pos0, Q,     \
                        w_codes, w_scale, cap, z_codes, z_scales, stride, idx, cnt, sink, rc, rs,   \
-                       rope_rows, O, lse, L.nsplit, pO, pml, win_floor)
+                       rope_rows, O, lse, L.nsplit, pO, pml, win_floor, L.hsplit)
     if (L.zf8) {
         switch (ht) {
             case 1: CSA2_ATTN(1, true); break;

@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const float* __restrict__ sink, const float* __restrict__ rcos,
     const float* __restrict__ rsin, int64_t rope_rows, uint16_t* __restrict__ O,
     float* __restrict__ lse, int nsplit, float* __restrict__ part_O,
-    float* __restrict__ part_ml, const int32_t* __restrict__ win_floor) {
+    float* __restrict__ part_ml, const int32_t* __restrict__ win_floor, int hsplit) {
     __shared__ __attribute__((aligned(16))) uint8_t rawc[NRAW][CH * 512];
     __shared__ __attribute__((aligned(16))) uint32_t zsc[NRAW][CH][4];
     __shared__ __attribute__((aligned(16))) float rscl[NRAW][CH];
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     const int q4 = wave & 3;
     const bool qk_on = HT == 4 || q4 < HT;
     const float lscale = 0.044194173824159216f * LOG2E;   // log2(e) / sqrt(512)
-    const int nunits = B * Tq * nsplit;
+    const int nunits = B * Tq * nsplit * hsplit;
 
     if (wave == 0 && lane < H) dma4s(sink, 4u * (uint32_t)lane, lds_addr(&sinkl[0]));
 
@@ -164,15 +164,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     // come from LDS, copied 64 units at a time, so that no barrier waits on a
     // scalar load.
     struct Unit {
-        int row, split, b, t, nwin, slot0, ncmp, nwch, k_begin, k_end;
+        int row, split, h0, b, t, nwin, slot0, ncmp, nwch, k_begin, k_end;
         int64_t p, prow;
     };
     // u = unit_at(i): the block's i-th unit
     auto unit_of = [&](int u, int i) {
         const int32_t* inf = &uinfo[(i >> 6) & 1][0][i & 63];
         Unit U;
-        U.row = u / nsplit;
-        U.split = u - U.row * nsplit;
+        // a unit is (query row, split, head group): a head group's 16 HT heads
+        // start at h0; the groups of a row are adjacent units
+        const int uh = u / hsplit;
+        U.h0 = (u - uh * hsplit) * 16 * HT;
+        U.row = uh / nsplit;
+        U.split = uh - U.row * nsplit;
         U.b = U.row / Tq;
         U.t = U.row - U.b * Tq;
         int64_t p = (int64_t)inf[64] + U.t;
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
     auto info_issue = [&](int i0) {
         const int par = (i0 >> 6) & 1;
         const int uu = unit_at(i0 + lane);
-        const int row = uu < nunits ? uu / nsplit : 0;
+        const int row = uu < nunits ? uu / hsplit / nsplit : 0;
         const int b = row / Tq;
         dma4s(cnt, 4u * (uint32_t)row, lds_addr(&uinfo[par][0][0]));
         dma4s(q_pos0, 4u * (uint32_t)b, lds_addr(&uinfo[par][1][0]));
@@ -231,8 +235,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         // (a wave with no heads reads head H - 1 and discards it).  Issued
         // unconditionally, so the registers hold nothing across the chunk loop.
         uint4 qraw[4][4];
-        auto q_issue = [&](int b, int t) {
-            const int hq = h < H ? h : H - 1;
+        auto q_issue = [&](int b, int t, int h0) {
+            const int hq = h0 + h < H ? h0 + h : H - 1;
             const uint16_t* qrow = Q + (((int64_t)b * H + hq) * Tq + t) * D;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -290,7 +294,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         if (unit_at(0) < nunits) {
             const Unit U0 = unit_of(unit_at(0), 0);
             prefetch(U0, 0, 0);
-            q_issue(U0.b, U0.t);
+            q_issue(U0.b, U0.t, U0.h0);
         }
         for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
             const Unit U = unit_of(u, i);
@@ -567,7 +571,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 const bool more = un < nunits;
                 const Unit N = more ? unit_of(un, i + 1) : U;
                 if (more) prefetch(N, (rb0 + nch) % NRAW, up ^ 1);
-                q_issue(N.b, N.t);      // the last unit re-reads its own query
+                q_issue(N.b, N.t, N.h0);      // the last unit re-reads its own query
             }
             // final(u): this unit's per-head state for the PV waves: running
             // maximum and denominator (log2 units), and, for a whole row, the
@@ -577,12 +581,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                 mfin[up][h] = m_used;
                 lfin[up][h] = l_tot;
                 if (nsplit == 1) {
-                    const float shv = sinkl[h] * LOG2E;
+                    const float shv = sinkl[U.h0 + h] * LOG2E;
                     const float M = fmaxf(m_used, shv);
                     const float em = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - M);
                     const float den = l_tot * em + __builtin_amdgcn_exp2f(shv - M);
                     finf[up][h] = em / den;
-                    if (lse) lse[((int64_t)U.b * H + h) * Tq + U.t] = (M + log2f(den)) * 0.6931471805599453f;
+                    if (lse) lse[((int64_t)U.b * H + U.h0 + h) * Tq + U.t] = (M + log2f(den)) * 0.6931471805599453f;
                 }
             }
             barrier_lds();
@@ -601,7 +605,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
         // 128-byte head segments (8 lanes per head; the 16-byte unit u of head
         // h's segment sits at u ^ (h & 7)).  A split writes its unnormalised
         // partial and (m, l).
-        struct Done { int b, t, row, split; };      // a unit whose output is pending
+        struct Done { int b, t, row, split, h0; };  // a unit whose output is pending
         auto output = [&](const Done& P, int pp) {
             uint8_t* const stage = &Ost[p8][0];
             float rco[4][2], rsi[4][2];
@@ -644,10 +648,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
                     for (int i2 = 0; i2 < 2; ++i2) {
                         const int hr = hl + 8 * i2;
                         const uint4 v = *(const uint4*)(stage + hr * 128 + ((c8 ^ (hr & 7)) << 4));
-                        *(uint4*)(O + (((int64_t)P.b * H + 16 * ht + hr) * Tq + P.t) * D + 64 * p8 + 8 * c8) = v;
+                        *(uint4*)(O + (((int64_t)P.b * H + P.h0 + 16 * ht + hr) * Tq + P.t) * D + 64 * p8 + 8 * c8) = v;
                     }
                 } else {
-                    const int64_t pbase = ((int64_t)P.row * nsplit + P.split) * H + hh;
+                    const int64_t pbase = ((int64_t)P.row * nsplit + P.split) * H + P.h0 + hh;
                     float* po = part_O + pbase * D;
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) *(f4*)(po + 64 * p8 + 16 * ct + 4 * g) = oacc[ct][ht];
@@ -659,7 +663,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             }
         };
         int rb0 = 0;                    // raw buffer of the unit's first chunk
-        Done Uprev{0, 0, 0, 0};
+        Done Uprev{0, 0, 0, 0, 0};
         int nmine = 0;                  // units taken so far
         for (int i = 0, u = unit_at(0), up = 0; u < nunits; u = unit_at(++i), up ^= 1) {
             nmine = i + 1;
@@ -856,7 +860,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_attn(
             }
             if (k_end > k_begin) pv(k_end - 1, a1);
             barrier_lds();      // final(u): the QK waves' m, l and normalisation
-            Uprev = Done{U.b, U.t, U.row, U.split};
+            Uprev = Done{U.b, U.t, U.row, U.split, U.h0};
             rb0 = (rb0 + nch) % NRAW;
         }
         // the last unit's output
@@ -973,7 +977,7 @@ __global__ void __launch_bounds__(256) k_attn_combine(
                                          const uint8_t*, int64_t, const int32_t*,              \
                                          const int32_t*, const float*, const float*,           \
                                          const float*, int64_t, uint16_t*, float*, int, float*, \
-                                         float*, const int32_t*);
+                                         float*, const int32_t*, int);
 CSA2_ATTN_INST(1, false)
 CSA2_ATTN_INST(2, false)
 CSA2_ATTN_INST(3, false)

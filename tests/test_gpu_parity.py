@@ -260,22 +260,23 @@ def test_sparse_attn_given_oracle_selection(dev, synth):
     log(f"  max|dO|={mx:.2e} rel={rel:.2e}")
 
 
-@pytest.mark.parametrize("zf", [0, 1])
-def test_sparse_attn_bounded_replay_floor(dev, synth, zf):
+@pytest.mark.parametrize("zf,Tq,H", [(0, 5, 64), (1, 5, 64), (0, 30, 64), (0, 30, 32)])
+def test_sparse_attn_bounded_replay_floor(dev, synth, zf, Tq, H):
     """attention with a per-request replay start s: request 0 none, request 1 a start
     inside the 128-row window, request 2 a start past every query (one window row);
-    zf = 1: compressed rows in the pages' per-16 E4M3 format"""
+    zf = 1: compressed rows in the pages' per-16 E4M3 format.  Tq=30: 90 query rows,
+    which the attention kernel runs as two head groups a row (32 or 16 heads each)"""
     import torch
     import compressed_sparse_attention_csa2_amd as csa2
     import oracle
     from oracle.reference import DecodeReference
-    B, Tq, N, H = 3, 5, 2600, 64
+    B, N = 3, 2600
     wl = synth.decode_workload(B=B, Tq=Tq, n_entries=N, H=H, z_format=zf)
     p0 = wl.q_pos0
     floors = np.array([0, p0 - 40, p0 + 100], np.int32)
     log(f"csa2_sparse_attn with replay starts {floors.tolist()}: {wl.name}")
     g = np.random.default_rng(17)
-    cnts = np.array([[512, 300, 1, 0, 512]] * B, np.int32)
+    cnts = np.array([[512, 300, 1, 0, 512] * (Tq // 5)] * B, np.int32)
     idx = np.full((B, Tq, 512), -1, np.int32)
     refs = [DecodeReference(wl, b) for b in range(B)]
     for b in range(B):
