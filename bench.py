@@ -33,8 +33,8 @@ PEAK_HBM = 8.0e12       # HBM3E, B/s
 # a 1 GiB device copy; profiles/hbm_traffic_prefill_T65536_decode_B128.txt).  A figure is valid only
 # for the kernel sources it was taken on: reported as null once any listed file has changed.
 TRAFFIC = {
-    ("k_attn", "prefill", 65536): (2.0135e+10, {
-        "attention.hip": "7c7bc444a0a71829d15f7669a11be63b7a8fa1b049589b94f28b5bd6441dbeed",
+    ("k_attn", "prefill", 65536): (2.0005e+10, {
+        "attention.hip": "96b2726c8cfc0b9d54466acc24f2ec26fce49ee6639160644ca9c27364a87401",
         "csa2_device.h": "134fb61f73efbe5f457591414f833043a952f213f0ef3fd121a73d33f90c0881"}),
     ("k_index_select", "prefill", 65536): (4.8043e+08, {
         "index_select.hip": "379c201f58b7c75543d72111b0d9cfffd73f736db9747b93b3ccad3f49bf4ca7",
